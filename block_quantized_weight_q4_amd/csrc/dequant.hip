@@ -1,0 +1,152 @@
+// dequant.hip -- block bytes -> dense fp32 / fp16 / bf16 (kq_dequantize).
+//
+// mlx-kquant "bindings.cpp", dequantize; Ternary Bonsai
+// "ternel_packed_model.py", get_rows.  HBM-bound streaming: every thread
+// reads one aligned slice of a block and writes 8..32 contiguous outputs, so
+// reads and writes are coalesced across the wave.
+//
+// Exactness: every decoded weight is formed with one rounding in fp32.
+//   Q4_K: (d*sc) and (d*sc)*q are exact (<= 21 significant bits), dmin*m is
+//         exact (<= 17 bits); the final fused multiply-subtract rounds once.
+//   Q8_0: d*q is exact (<= 19 bits).
+//   TQ1:  (t-1)*s is exact.
+// fp16/bf16 outputs then round that fp32 value to nearest even.
+#include "kq_device.h"
+#include "kq_internal.h"
+
+namespace kq {
+
+template <int DT> struct Out8;  // 8 consecutive outputs
+template <> struct Out8<F32> {
+    static __device__ __forceinline__ void store(void* out, int64_t i, const float (&v)[8]) {
+        float4_t* p = (float4_t*)((float*)out + i);
+        p[0] = float4_t{v[0], v[1], v[2], v[3]};
+        p[1] = float4_t{v[4], v[5], v[6], v[7]};
+    }
+};
+template <> struct Out8<F16> {
+    static __device__ __forceinline__ void store(void* out, int64_t i, const float (&v)[8]) {
+        u32x4 r;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            r[j] = float_to_half_bits(v[2 * j]) | ((uint32_t)float_to_half_bits(v[2 * j + 1]) << 16);
+        *(u32x4*)((uint16_t*)out + i) = r;
+    }
+};
+template <> struct Out8<BF16> {
+    static __device__ __forceinline__ void store(void* out, int64_t i, const float (&v)[8]) {
+        u32x4 r;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            r[j] = float_to_bf16_bits(v[2 * j]) | ((uint32_t)float_to_bf16_bits(v[2 * j + 1]) << 16);
+        *(u32x4*)((uint16_t*)out + i) = r;
+    }
+};
+
+// Q4_K: 16 threads per super-block.  Thread (c, h) reads quant bytes
+// Q[32c+8h .. 32c+8h+8) and writes weights 64c+8h.. (low nibbles) and
+// 64c+32+8h.. (high nibbles).
+template <int DT>
+__global__ __launch_bounds__(256) void dequant_q4k_kernel(const uint8_t* __restrict__ w,
+                                                          void* __restrict__ out, int64_t nblocks) {
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t b = t >> 4;
+    if (b >= nblocks) return;
+    const int c = (t >> 2) & 3, h = t & 3;
+    const uint8_t* blk = w + b * 144;
+    const u32x4 hd = *(const u32x4*)blk;
+    const u32x2 q = *(const u32x2*)(blk + 16 + 32 * c + 8 * h);
+    int sc0, m0, sc1, m1;
+    q4k_scale_min(hd, 2 * c, sc0, m0);
+    q4k_scale_min(hd, 2 * c + 1, sc1, m1);
+    const float d = q4k_d(hd), dmin = q4k_dmin(hd);
+    const float s0 = d * (float)sc0, s1 = d * (float)sc1;
+    const float n0 = dmin * (float)m0, n1 = dmin * (float)m1;
+    float lo[8], hi[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t byte = (q[i >> 2] >> (8 * (i & 3))) & 0xffu;
+        lo[i] = __builtin_fmaf(s0, (float)(byte & 15u), -n0);
+        hi[i] = __builtin_fmaf(s1, (float)(byte >> 4), -n1);
+    }
+    const int64_t base = b * 256 + 64 * c + 8 * h;
+    Out8<DT>::store(out, base, lo);
+    Out8<DT>::store(out, base + 32, hi);
+}
+
+// Q8_0: 4 threads per 34-byte block, 8 weights each.  Blocks are only 2-byte
+// aligned, so quants are read as 16-bit words.
+template <int DT>
+__global__ __launch_bounds__(256) void dequant_q8_0_kernel(const uint8_t* __restrict__ w,
+                                                           void* __restrict__ out, int64_t nblocks) {
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t b = t >> 2;
+    if (b >= nblocks) return;
+    const int h = t & 3;
+    const uint16_t* blk = (const uint16_t*)(w + b * 34);
+    const float d = half_bits_to_float(blk[0]);
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t pair = blk[1 + 4 * h + i];
+        v[2 * i] = d * (float)(int8_t)(pair & 0xffu);
+        v[2 * i + 1] = d * (float)(int8_t)(pair >> 8);
+    }
+    Out8<DT>::store(out, b * 32 + 8 * h, v);
+}
+
+// TQ1_G128: 16 threads per 28-byte block, 8 columns each.  Column c < 125 is
+// digit c % 5 of code byte c / 5; columns 125..127 are digits 0..2 of the
+// tail byte; weight = (digit - 1) * scale.
+template <int DT>
+__global__ __launch_bounds__(256) void dequant_tq1_kernel(const uint8_t* __restrict__ w,
+                                                          void* __restrict__ out, int64_t nblocks) {
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t b = t >> 4;
+    if (b >= nblocks) return;
+    const int part = t & 15;
+    const uint8_t* blk = w + b * 28;
+    const float s = half_bits_to_float(*(const uint16_t*)(blk + 26));
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int col = 8 * part + i;
+        const int slot = col < 125 ? col / 5 : 25;
+        const int digit = col < 125 ? col - 5 * slot : col - 125;
+        v[i] = (float)tq1_trit(blk[slot], digit) * s;
+    }
+    Out8<DT>::store(out, b * 128 + 8 * part, v);
+}
+
+template <int DT>
+static hipError_t launch_dequant_dt(int codec, const void* w, int64_t nblocks, void* out,
+                                    hipStream_t s) {
+    const int tpb = codec == Q8_0 ? 4 : 16;
+    const int64_t threads = nblocks * tpb;
+    const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
+    switch (codec) {
+    case Q4_K:
+        hipLaunchKernelGGL(dequant_q4k_kernel<DT>, grid, block, 0, s, (const uint8_t*)w, out, nblocks);
+        break;
+    case Q8_0:
+        hipLaunchKernelGGL(dequant_q8_0_kernel<DT>, grid, block, 0, s, (const uint8_t*)w, out, nblocks);
+        break;
+    default:
+        hipLaunchKernelGGL(dequant_tq1_kernel<DT>, grid, block, 0, s, (const uint8_t*)w, out, nblocks);
+        break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_dequant(int codec, const void* w, int64_t rows, int64_t k, void* out, int out_dt,
+                          hipStream_t s) {
+    const int qk = codec == Q4_K ? 256 : codec == Q8_0 ? 32 : 128;
+    const int64_t nblocks = rows * (k / qk);
+    switch (out_dt) {
+    case F32: return launch_dequant_dt<F32>(codec, w, nblocks, out, s);
+    case F16: return launch_dequant_dt<F16>(codec, w, nblocks, out, s);
+    default: return launch_dequant_dt<BF16>(codec, w, nblocks, out, s);
+    }
+}
+
+}  // namespace kq

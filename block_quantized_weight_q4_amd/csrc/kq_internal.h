@@ -1,0 +1,58 @@
+// kq_internal.h -- host-side declarations shared by the libkq translation
+// units (launchers behind the C ABI).  Not part of the public interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kq {
+
+// Rows of a weight-streaming tile: one pass over a weight row serves up to
+// this many activation rows.
+constexpr int kMoeTileRows = 64;
+
+// Layout of the MoE workspace (int32 words); see include/kq.h.
+struct MoeLayout {
+    int64_t n_experts, rows, max_tiles;
+    int64_t counts_off, offsets_off, perm_off, tiles_off;  // word offsets
+    int64_t route_words;     // words used by the schedule
+    int64_t slot_off_bytes;  // start of the fp32 slot buffer
+    int64_t slot_bytes;      // rows * n_out * 4
+    int64_t total_bytes;
+};
+MoeLayout moe_layout(int64_t n_experts, int64_t n_tokens, int64_t top_k, int64_t n_out);
+
+// Arguments of the weight-streaming ("skinny") product kernels.
+struct SkinnyArgs {
+    const uint8_t* w;      // weights (gate for GLU)
+    const uint8_t* w2;     // up weights (GLU only)
+    int64_t row_bytes;     // bytes per weight row
+    int64_t expert_stride; // bytes between experts
+    int64_t n, k;          // weight rows, columns
+    const void* x;         // activations
+    int64_t x_row;         // elements between consecutive activation rows
+    int64_t top_k;         // routed: slots per token
+    int shared_x;          // routed: x row = r / top_k (else r)
+    const int32_t* ws;     // routed: workspace (schedule); null for dense
+    int64_t tiles_off, perm_off;
+    int64_t m;             // dense: activation rows
+    void* y;               // output
+    int y_dt;              // output dtype
+    int64_t y_row;         // elements between output rows
+};
+
+hipError_t launch_dequant(int codec, const void* w, int64_t rows, int64_t k, void* out, int out_dt,
+                          hipStream_t s);
+hipError_t launch_skinny(int codec, int x_dt, bool glu, const SkinnyArgs& a, int64_t grid_tiles,
+                         hipStream_t s);
+hipError_t launch_gemm(int codec, int x_dt, const void* w, int64_t n, int64_t k, const void* x,
+                       int64_t m, void* y, int y_dt, hipStream_t s);
+hipError_t launch_route(const uint32_t* ids, int64_t rows, int64_t n_experts, const MoeLayout& L,
+                        int32_t* ws, hipStream_t s);
+hipError_t launch_mix(const uint32_t* ids, const float* scores, int64_t n_tokens, int64_t top_k,
+                      int64_t n_experts, const float* slots, int64_t n, void* y, int y_dt,
+                      hipStream_t s);
+hipError_t launch_poison(const uint32_t* ids, int64_t rows, int64_t n_experts, void* y, int64_t n,
+                         int y_dt, hipStream_t s);
+
+}  // namespace kq

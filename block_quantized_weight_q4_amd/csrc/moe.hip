@@ -1,0 +1,174 @@
+// moe.hip -- expert routing schedule, slot-order mixing and invalid-id poison.
+//
+// mlx-kquant "bindings.cpp": expert_tile_map (64-row tiles per expert segment,
+// only the last partial, built on the GPU with no host sync),
+// gather_qmv_mix_ns_kq (each slot accumulated in f32 weighted by its score);
+// mlx-native "quantized_matmul_id_ggml.rs": map0 regroup with on-device id
+// validation, NaN poison for invalid routing metadata.
+#include "kq_device.h"
+#include "kq_internal.h"
+
+namespace kq {
+
+// One workgroup of 256 threads builds the whole schedule:
+//   1. histogram of ids into LDS counts (ids >= E counted as invalid)
+//   2. exclusive scans: row offsets per expert and tile offsets per expert
+//   3. stable scatter by one wave, 64 rows at a time in row order: each lane
+//      finds the lanes holding the same expert with ballots over the id bits,
+//      its rank among them, and the lowest such lane advances the cursor
+//   4. tile descriptors (expert, row_start, num_rows) in expert order
+__global__ __launch_bounds__(256) void route_kernel(const uint32_t* __restrict__ ids, int64_t rows,
+                                                    int64_t n_experts, int32_t* __restrict__ ws,
+                                                    int64_t counts_off, int64_t offsets_off,
+                                                    int64_t perm_off, int64_t tiles_off,
+                                                    int id_bits) {
+    extern __shared__ int32_t lds[];
+    int32_t* counts = lds;                  // [E]
+    int32_t* cursor = lds + n_experts;      // [E]
+    int32_t* tstart = lds + 2 * n_experts;  // [E]
+    __shared__ int32_t n_invalid, n_tiles;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+    for (int64_t e = tid; e < n_experts; e += 256) counts[e] = 0;
+    if (tid == 0) n_invalid = 0;
+    __syncthreads();
+    for (int64_t i = tid; i < rows; i += 256) {
+        const uint32_t e = ids[i];
+        if ((int64_t)e < n_experts) atomicAdd(&counts[e], 1);
+        else atomicAdd(&n_invalid, 1);
+    }
+    __syncthreads();
+
+    // exclusive scans over experts, by wave 0
+    if (wave == 0) {
+        int32_t run_rows = 0, run_tiles = 0;
+        for (int64_t base = 0; base < n_experts; base += 64) {
+            const int64_t e = base + lane;
+            const int32_t c = e < n_experts ? counts[e] : 0;
+            const int32_t t = (c + kMoeTileRows - 1) / kMoeTileRows;
+            int32_t ic = c, it = t;  // inclusive prefix within the 64
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const int32_t uc = __shfl_up(ic, off, 64), ut = __shfl_up(it, off, 64);
+                if (lane >= off) ic += uc, it += ut;
+            }
+            if (e < n_experts) {
+                cursor[e] = run_rows + ic - c;
+                tstart[e] = run_tiles + it - t;
+            }
+            run_rows += __shfl(ic, 63, 64);
+            run_tiles += __shfl(it, 63, 64);
+        }
+        if (lane == 0) n_tiles = run_tiles;
+    }
+    __syncthreads();
+
+    for (int64_t e = tid; e < n_experts; e += 256) {
+        ws[counts_off + e] = counts[e];
+        ws[offsets_off + e] = cursor[e];
+    }
+    if (tid == 0) {
+        ws[offsets_off + n_experts] = (int32_t)(rows - n_invalid);
+        ws[0] = n_tiles;
+        ws[1] = n_invalid;
+    }
+    // tile descriptors
+    for (int64_t e = tid; e < n_experts; e += 256) {
+        const int32_t c = counts[e], start = cursor[e];
+        int32_t t = tstart[e];
+        for (int32_t r0 = 0; r0 < c; r0 += kMoeTileRows, ++t) {
+            int32_t* d = ws + tiles_off + 3 * (int64_t)t;
+            d[0] = (int32_t)e;
+            d[1] = start + r0;
+            d[2] = c - r0 < kMoeTileRows ? c - r0 : kMoeTileRows;
+        }
+    }
+    __syncthreads();  // cursor[] is reused below after the reads above
+
+    if (wave == 0) {
+        for (int64_t base = 0; base < rows; base += 64) {
+            const int64_t i = base + lane;
+            const uint32_t e = i < rows ? ids[i] : 0xffffffffu;
+            const bool valid = (int64_t)e < n_experts;
+            uint64_t same = __ballot(valid);
+            for (int b = 0; b < id_bits; ++b) {
+                const bool bit = (e >> b) & 1u;
+                const uint64_t bal = __ballot(bit);
+                same &= bit ? bal : ~bal;
+            }
+            if (valid) {
+                const uint64_t below = same & ((1ull << lane) - 1ull);
+                const int32_t pos = cursor[e] + __popcll(below);
+                ws[perm_off + pos] = (int32_t)i;
+            }
+            __builtin_amdgcn_wave_barrier();
+            if (valid && (same & ((1ull << lane) - 1ull)) == 0ull)  // lowest lane of its expert
+                cursor[e] += __popcll(same);
+            __builtin_amdgcn_wave_barrier();
+        }
+    }
+}
+
+hipError_t launch_route(const uint32_t* ids, int64_t rows, int64_t n_experts, const MoeLayout& L,
+                        int32_t* ws, hipStream_t s) {
+    int bits = 1;
+    while ((1ll << bits) < n_experts) ++bits;
+    const size_t lds = (size_t)3 * n_experts * sizeof(int32_t);
+    hipLaunchKernelGGL(route_kernel, dim3(1), dim3(256), lds, s, ids, rows, n_experts, ws,
+                       L.counts_off, L.offsets_off, L.perm_off, L.tiles_off, bits);
+    return hipGetLastError();
+}
+
+// y[t, j] = sum over slots r = 0..top_k-1, in order, of scores[t,r] * slot[t*top_k+r, j]
+// in fp32; NaN if any of the token's ids is invalid.
+__global__ __launch_bounds__(256) void mix_kernel(const uint32_t* __restrict__ ids,
+                                                  const float* __restrict__ scores, int64_t top_k,
+                                                  int64_t n_experts, const float* __restrict__ slots,
+                                                  int64_t n, void* __restrict__ y, int y_dt) {
+    const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t t = blockIdx.y;
+    if (j >= n) return;
+    float acc = 0.f;
+    bool bad = false;
+    for (int64_t r = 0; r < top_k; ++r) {
+        const int64_t row = t * top_k + r;
+        bad |= (int64_t)ids[row] >= n_experts;
+        acc = __builtin_fmaf(scores[row], slots[row * n + j], acc);
+    }
+    const float v = bad ? __builtin_nanf("") : acc;
+    if (y_dt == F32) store_out<F32>(y, t * n + j, v);
+    else if (y_dt == F16) store_out<F16>(y, t * n + j, v);
+    else store_out<BF16>(y, t * n + j, v);
+}
+
+hipError_t launch_mix(const uint32_t* ids, const float* scores, int64_t n_tokens, int64_t top_k,
+                      int64_t n_experts, const float* slots, int64_t n, void* y, int y_dt,
+                      hipStream_t s) {
+    const dim3 grid((unsigned)((n + 255) / 256), (unsigned)n_tokens);
+    hipLaunchKernelGGL(mix_kernel, grid, dim3(256), 0, s, ids, scores, top_k, n_experts, slots, n,
+                       y, y_dt);
+    return hipGetLastError();
+}
+
+// Rows whose id is invalid: every output element NaN.
+__global__ __launch_bounds__(256) void poison_kernel(const uint32_t* __restrict__ ids,
+                                                     int64_t n_experts, void* __restrict__ y,
+                                                     int64_t n, int y_dt) {
+    const int64_t r = blockIdx.y;
+    if ((int64_t)ids[r] < n_experts) return;
+    const float v = __builtin_nanf("");
+    for (int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x; j < n; j += (int64_t)gridDim.x * 256) {
+        if (y_dt == F32) store_out<F32>(y, r * n + j, v);
+        else if (y_dt == F16) store_out<F16>(y, r * n + j, v);
+        else store_out<BF16>(y, r * n + j, v);
+    }
+}
+
+hipError_t launch_poison(const uint32_t* ids, int64_t rows, int64_t n_experts, void* y, int64_t n,
+                         int y_dt, hipStream_t s) {
+    const dim3 grid((unsigned)((n + 255) / 256 < 8 ? (n + 255) / 256 : 8), (unsigned)rows);
+    hipLaunchKernelGGL(poison_kernel, grid, dim3(256), 0, s, ids, n_experts, y, n, y_dt);
+    return hipGetLastError();
+}
+
+}  // namespace kq

@@ -1,0 +1,139 @@
+"""CPU checks of the C ABI: the library loads, exports every function the
+header declares, and its host-side logic (sizes, workspace layout, argument
+validation that rejects before any launch) behaves as documented.  No call
+here reaches a kernel."""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kq.h")
+
+
+@pytest.fixture(scope="module")
+def kq():
+    from block_quantized_weight_q4_amd import _build, kq as mod
+
+    _build.build_if_missing()
+    mod.lib()
+    return mod
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kq_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declarations_match_binding(kq):
+    assert _declared() == sorted(kq.SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol(kq):
+    from block_quantized_weight_q4_amd._build import LIB
+
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT (kq_[a-z_0-9]+)$", out, flags=re.M))
+    missing = [s for s in _declared() if s not in exported]
+    assert not missing
+    L = kq.lib()
+    for s in _declared():
+        assert getattr(L, s) is not None
+
+
+def test_block_geometry(kq):
+    assert (kq.kq_qk("q4_k"), kq.kq_block_bytes("q4_k")) == (256, 144)
+    assert (kq.kq_qk("q8_0"), kq.kq_block_bytes("q8_0")) == (32, 34)
+    assert (kq.kq_qk("tq1_g128"), kq.kq_block_bytes("tq1_g128")) == (128, 28)
+    assert kq.kq_row_bytes("q4_k", 4096) == 16 * 144
+    assert kq.kq_row_bytes("q8_0", 4096) == 128 * 34
+    assert kq.kq_row_bytes("tq1_g128", 5120) == 40 * 28
+    assert kq.kq_row_bytes("q4_k", 100) == -1
+    assert kq.kq_row_bytes("q4_k", 0) == -1
+    assert kq.lib().kq_qk(7) == 0
+
+
+def test_status_strings(kq):
+    assert kq.kq_status_string(0) == "ok"
+    for s in range(1, 5):
+        assert kq.kq_status_string(s) not in ("ok", "unknown status")
+
+
+def test_workspace_layout(kq):
+    E, T, top_k, n = 128, 256, 8, 7168
+    R = T * top_k
+    max_tiles = (R + 63) // 64 + E
+    route_words = 2 + E + (E + 1) + R + 3 * max_tiles
+    slot_off = (route_words * 4 + 255) // 256 * 256
+    assert kq.kq_moe_workspace_bytes(E, T, top_k, 0) == slot_off
+    assert kq.kq_moe_workspace_bytes(E, T, top_k, n) == slot_off + R * n * 4
+    assert kq.kq_moe_workspace_bytes(0, T, top_k, 0) == 0
+    assert kq.kq_moe_workspace_bytes(E, 2**31, 8, 0) == 0
+
+
+def _call_qmv(L, t=0, w=16, n=8, k=256, x=16, xdt=1, m=1, y=4096, ydt=1):
+    P = lambda v: C.c_void_p(v) if v else None  # noqa: E731  fake addresses, never dereferenced
+    return L.kq_qmv(t, P(w), n, k, P(x), xdt, m, P(y), ydt, None)
+
+
+def test_validation_rejects_before_launch(kq):
+    """Every rejected call returns before any HIP call, so fake addresses are safe."""
+    L = kq.lib()
+    base = 1 << 40
+    ok = dict(w=base, x=base + (1 << 30), y=base + (2 << 30))
+    assert _call_qmv(L, **{**ok, "k": 100}) == 1          # k % QK
+    assert _call_qmv(L, **{**ok, "n": 0}) == 1            # zero dim
+    assert _call_qmv(L, **{**ok, "m": 0}) == 1
+    assert _call_qmv(L, **{**ok, "m": 17}) == 1           # qmv takes <= 16 rows
+    assert _call_qmv(L, **{**ok, "w": 0}) == 1            # null
+    assert _call_qmv(L, **{**ok, "x": base + (1 << 30) + 2}) == 1  # misaligned
+    assert _call_qmv(L, **{**ok, "y": base + 16}) == 1    # y overlaps w
+    assert _call_qmv(L, **{**ok, "t": 9}) == 2            # unknown type
+    assert _call_qmv(L, **{**ok, "xdt": 7}) == 2          # unknown dtype
+    assert kq.kq_last_error() == "unknown dtype"
+
+
+def test_expert_validation(kq):
+    L = kq.lib()
+    P = C.c_void_p
+    base = 1 << 40
+    w, x, ids, y, ws = (P(base + (i << 32)) for i in range(5))
+
+    def call(**kw):
+        a = dict(t=0, w=w, E=8, n=64, k=256, stride=64 * 144, x=x, xdt=1, layout=0, ids=ids,
+                 T=4, top_k=2, scores=None, y=y, ydt=1, ws=ws, wsb=1 << 20)
+        a.update(kw)
+        return L.kq_qmm_id(a["t"], a["w"], a["E"], a["n"], a["k"], a["stride"], a["x"], a["xdt"],
+                           a["layout"], a["ids"], a["T"], a["top_k"], a["scores"], a["y"], a["ydt"],
+                           a["ws"], a["wsb"], None)
+
+    assert call(top_k=0) == 1
+    assert call(top_k=9) == 1                 # top_k > n_experts
+    assert call(E=0) == 1
+    assert call(stride=64 * 144 - 16) == 1    # stride below one expert
+    assert call(stride=64 * 144 + 8) == 1     # stride alignment
+    assert call(layout=5) == 1
+    assert call(wsb=16) == 3                  # workspace too small
+    assert call(T=2**31 // 2 + 1) == 1        # rows > INT32_MAX
+    assert call(y=P(base + (1 << 32) + 64)) == 1  # output overlaps x
+    assert L.kq_moe_glu(0, w, w, 8, 64, 256, 64 * 144, x, 1, ids, 4, 2, 9, y, 1, ws, 1 << 20,
+                        None) == 2            # unknown activation
+
+
+def test_product_path_has_no_fallback():
+    """The binding refuses to run without libkq.so instead of computing elsewhere."""
+    import block_quantized_weight_q4_amd.kq as mod
+
+    src = open(mod.__file__).read()
+    assert "oracle" not in src
+    for path in os.listdir(os.path.join(ROOT, "block_quantized_weight_q4_amd")):
+        if path.endswith(".py"):
+            text = open(os.path.join(ROOT, "block_quantized_weight_q4_amd", path)).read()
+            assert "import oracle" not in text and "from oracle" not in text

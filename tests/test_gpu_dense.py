@@ -1,0 +1,251 @@
+"""GPU parity of the dense entry points (kq_dequantize, kq_qmv, kq_qmm) against
+the CPU oracle, through the C ABI.
+
+Dequantization is compared bit for bit.  Products must satisfy
+|gpu - ref| <= tau * sum|w*x| with tau = 2e-3 for fp16/bf16 activations and
+1e-5 for fp32, ref and the sum both from the fp64 oracle.  Small shapes
+(several tiles plus ragged tails) are compared element by element; the full
+workload sizes are compared on sampled outputs that the oracle computes one
+by one, in the launch configuration the benchmark times.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from synth import workloads
+from tests.gpu_util import TAU, bits, check_tol, empty, to_dev, to_f64
+
+pytestmark = pytest.mark.gpu
+
+KINDS = ["q4_k", "q8_0", "tq1_g128"]
+QK = {"q4_k": 256, "q8_0": 32, "tq1_g128": 128}
+
+
+@pytest.fixture(scope="module")
+def kq():
+    from block_quantized_weight_q4_amd import _build, kq as mod
+
+    _build.build_if_missing()
+    mod.lib()
+    return mod
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+def _rng(seed):
+    return synth.rng_for(seed)
+
+
+def _gpu_dequant(kq, kind, w, rows, k, dt):
+    wd = to_dev(w)
+    out = empty((rows, k), dt)
+    kq.kq_dequantize(kind, wd, rows, k, out)
+    torch.cuda.synchronize()
+    return out
+
+
+# ---------------------------------------------------------------- dequantize
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("rows,nblk", [(1, 1), (7, 3), (129, 5)])
+def test_dequant_bit_exact(kq, kind, dt, rows, nblk):
+    k = QK[kind] * nblk
+    _say("dequant", kind, dt, rows, k)
+    w = synth.weight_blocks(kind, _rng(1000 + rows), rows, k)
+    got = _gpu_dequant(kq, kind, w, rows, k, dt)
+    ref = oracle.dequant_as(kind, w, rows, k, dt)
+    ref_bits = ref.view(np.uint32) if dt == "f32" else ref
+    assert np.array_equal(bits(got), ref_bits)
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+def test_dequant_q4k_full_range_scales(kq, dt):
+    """Arbitrary finite fp16 d/dmin (subnormal to 65504, both signs): still
+    one rounding of the exact value; fp16 outputs may overflow to inf."""
+    rng = _rng(7)
+    rows, k = 64, 1024
+    w = synth.q4k_blocks(rng, rows, k)
+    blocks = w.reshape(-1, 144)
+    h = rng.integers(0, 0x7C00, size=(blocks.shape[0], 2)).astype(np.uint16)
+    h |= (rng.integers(0, 2, size=h.shape).astype(np.uint16) << 15)
+    blocks[:, 0:4] = h.astype("<u2").view(np.uint8)
+    _say("dequant q4_k full-range scales", dt)
+    got = _gpu_dequant(kq, "q4_k", w, rows, k, dt)
+    ref = oracle.dequant_as("q4_k", w, rows, k, dt)
+    ref_bits = ref.view(np.uint32) if dt == "f32" else ref
+    assert np.array_equal(bits(got), ref_bits)
+
+
+def test_dequant_c1_full(kq):
+    """C1: Q4_K 2048x2048 -> fp32, bit exact over the whole matrix."""
+    c = workloads.c1()
+    for dt in ("f32", "f16", "bf16"):
+        _say("dequant C1", dt)
+        got = _gpu_dequant(kq, "q4_k", c["w"], c["n"], c["k"], dt)
+        ref = oracle.dequant_as("q4_k", c["w"], c["n"], c["k"], dt)
+        assert np.array_equal(bits(got), ref.view(np.uint32) if dt == "f32" else ref)
+
+
+@pytest.mark.parametrize("kind,shape", [("q4_k", (14336, 4096)), ("q8_0", (4096, 4096)),
+                                        ("tq1_g128", (5120, 17408))])
+def test_dequant_full_size_bit_exact(kq, kind, shape):
+    n, k = shape
+    _say("dequant full", kind, n, k)
+    w = synth.weight_blocks(kind, _rng(11), n, k)
+    got = _gpu_dequant(kq, kind, w, n, k, "bf16")
+    ref = oracle.dequant_as(kind, w, n, k, "bf16")
+    assert np.array_equal(bits(got), ref)
+
+
+# ---------------------------------------------------------------- products
+def _run(kq, fn, kind, w, n, k, x, x_dt, m, y_dt):
+    wd, xd = to_dev(w), to_dev(x, x_dt)
+    y = empty((m, n), y_dt)
+    getattr(kq, fn)(kind, wd, n, k, xd, m, y)
+    torch.cuda.synchronize()
+    return to_f64(y)
+
+
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("x_dt", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("m", [1, 3, 4, 8, 16])
+def test_qmv_small(kq, kind, x_dt, m):
+    n, k = 67, QK[kind] * 6
+    rng = _rng(2000 + m)
+    w = synth.weight_blocks(kind, rng, n, k)
+    x = synth.activations(rng, (m, k), x_dt)
+    for y_dt in ("f32", "f16", "bf16"):
+        _say("qmv", kind, x_dt, m, y_dt)
+        got = _run(kq, "kq_qmv", kind, w, n, k, x, x_dt, m, y_dt)
+        ref, s = oracle.qmm(kind, w, n, k, x, x_dt, m)
+        check_tol(got, ref, s, TAU[x_dt], f"qmv {kind} {x_dt} m={m} y={y_dt}",
+                  out_dt=y_dt if y_dt != "f32" and x_dt == "f32" else None)
+
+
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("x_dt", ["f16", "bf16"])
+@pytest.mark.parametrize("m,n,nblk", [(17, 64, 2), (130, 200, 3), (257, 131, 4)])
+def test_qmm_small(kq, kind, x_dt, m, n, nblk):
+    k = QK[kind] * nblk
+    if kind == "q8_0":
+        k = 32 * (2 * nblk + 1)  # odd block count: a half K step at the end
+    rng = _rng(3000 + m)
+    w = synth.weight_blocks(kind, rng, n, k)
+    x = synth.activations(rng, (m, k), x_dt)
+    for y_dt in ("f32", "bf16"):
+        _say("qmm", kind, x_dt, m, n, k, y_dt)
+        got = _run(kq, "kq_qmm", kind, w, n, k, x, x_dt, m, y_dt)
+        ref, s = oracle.qmm(kind, w, n, k, x, x_dt, m)
+        check_tol(got, ref, s, TAU[x_dt], f"qmm {kind} {x_dt} m={m} y={y_dt}")
+
+
+@pytest.mark.parametrize("kind", KINDS)
+def test_one_hot_columns_exact(kq, kind):
+    """x = e_c returns column c of the decoded weights, for every c."""
+    n, k = 40, QK[kind] * 2
+    w = synth.weight_blocks(kind, _rng(4), n, k)
+    W = oracle.dequant(kind, w, n, k)
+    for fn, m in (("kq_qmv", 16), ("kq_qmm", k)):
+        for c0 in range(0, k, m):
+            mm = min(m, k - c0)
+            x = np.zeros((mm, k), np.float32)
+            x[np.arange(mm), c0 + np.arange(mm)] = 1.0
+            _say("one-hot", kind, fn, c0)
+            if fn == "kq_qmm":
+                xb = x.astype(np.float16).view(np.uint16)
+                got = _run(kq, fn, kind, w, n, k, xb, "f16", mm, "f32")
+                # weights are rounded to the 16-bit MFMA type in the prefill path
+                ref = W[:, c0:c0 + mm].T
+                check_tol(got, ref, np.abs(ref), 0.0, "one-hot qmm", out_dt="f16")
+            else:
+                got = _run(kq, fn, kind, w, n, k, x, "f32", mm, "f32")
+                assert np.array_equal(got, W[:, c0:c0 + mm].T.astype(np.float32))
+
+
+def test_qmv_c1_full(kq):
+    """C1: Q4_K 2048x2048, fp32 activation vector, fp32 output, tau = 1e-5."""
+    c = workloads.c1()
+    _say("qmv C1")
+    got = _run(kq, "kq_qmv", "q4_k", c["w"], c["n"], c["k"], c["x"], "f32", 1, "f32")
+    ref, s = oracle.qmm("q4_k", c["w"], c["n"], c["k"], c["x"], "f32", 1)
+    check_tol(got, ref, s, 1e-5, "qmv C1")
+
+
+def _sampled(kq, fn, case, x, x_dt, m, y_dt, npts=384, seed=0):
+    kind, n, k, w = case["kind"], case["n"], case["k"], case["w"]
+    got = _run(kq, fn, kind, w, n, k, x[:m], x_dt, m, y_dt)
+    rng = np.random.default_rng(seed)
+    pm = np.concatenate([[0, m - 1, 0, m - 1], rng.integers(0, m, npts)])
+    pn = np.concatenate([[0, 0, n - 1, n - 1], rng.integers(0, n, npts)])
+    ref, s = oracle.qmm_points(kind, w, n, k, x[:m], x_dt, m, pm, pn)
+    assert not np.isnan(got).any()
+    return check_tol(got[pm, pn], ref, s, TAU[x_dt], f"{fn} {kind} {n}x{k} m={m}")
+
+
+@pytest.mark.parametrize("which", [0, 1])
+@pytest.mark.parametrize("b", [1, 4, 8])
+def test_qmv_c2_full_sampled(kq, which, b):
+    case = workloads.c2()[which]
+    _say("qmv C2", case["n"], case["k"], b)
+    _sampled(kq, "kq_qmv", case, case["x"], "f16", b, "f16")
+
+
+@pytest.mark.parametrize("which", [("q4_k", 4096), ("q4_k", 14336), ("q8_0", 4096),
+                                   ("q8_0", 14336)])
+@pytest.mark.parametrize("m", [512, 2048])
+def test_qmm_c3_full_sampled(kq, which, m):
+    cases, x = workloads.c3(which)
+    _say("qmm C3", which, m)
+    _sampled(kq, "kq_qmm", cases[0], x, "bf16", m, "bf16")
+
+
+@pytest.mark.parametrize("which", [0, 1])
+@pytest.mark.parametrize("m", [1, 512])
+def test_tq1_c5_full_sampled(kq, which, m):
+    case = workloads.c5()[which]
+    fn = "kq_qmv" if m == 1 else "kq_qmm"
+    _say("tq1 C5", case["n"], case["k"], m)
+    _sampled(kq, fn, case, case["x"], "f16", m, "f16")
+
+
+def test_qmm_small_m_matches_qmv(kq):
+    """qmm at m <= 16 and qmv agree within the tolerance of each."""
+    rng = _rng(5)
+    n, k = 300, 1024
+    w = synth.q4k_blocks(rng, n, k)
+    x = synth.activations(rng, (8, k), "f16")
+    a = _run(kq, "kq_qmv", "q4_k", w, n, k, x, "f16", 8, "f32")
+    b = _run(kq, "kq_qmm", "q4_k", w, n, k, x, "f16", 8, "f32")
+    ref, s = oracle.qmm("q4_k", w, n, k, x, "f16", 8)
+    check_tol(a, ref, s, 2e-3, "qmv")
+    check_tol(b, ref, s, 2e-3, "qmm")
+
+
+def test_zero_activations_give_zero(kq):
+    n, k = 64, 512
+    w = synth.q4k_blocks(_rng(6), n, k)
+    for fn, m in (("kq_qmv", 2), ("kq_qmm", 40)):
+        x = np.zeros((m, k), np.uint16)
+        got = _run(kq, fn, "q4_k", w, n, k, x, "f16", m, "f32")
+        assert np.all(got == 0.0)
+
+
+def test_errors_do_not_launch(kq):
+    from block_quantized_weight_q4_amd.kq import KQError
+
+    w = to_dev(synth.q4k_blocks(_rng(8), 4, 256))
+    x = empty((20, 256), "f16")
+    y = empty((20, 4), "f16")
+    with pytest.raises(KQError):
+        kq.kq_qmv("q4_k", w, 4, 256, x, 20, y)  # more than 16 rows
+    with pytest.raises(KQError):
+        kq.kq_qmm("q4_k", w, 4, 100, x, 1, y)   # k not a multiple of 256
+    with pytest.raises(KQError):
+        kq.kq_qmm("q4_k", w, 4, 256, x, 0, y)   # empty batch

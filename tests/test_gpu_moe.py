@@ -1,0 +1,203 @@
+"""GPU parity of the expert-routed entry points (kq_moe_route, kq_qmm_id,
+kq_moe_glu) against the CPU oracle, through the C ABI.
+
+The routing schedule is integer work and is compared exactly.  Products use
+the dense rule |gpu - ref| <= tau * S.  The GLU output h = silu(g) * u is
+checked against the bound that the gate and up tolerances imply:
+|h - h_ref| <= tau * (max|silu'| * |u| * S_g + |silu(g)| * S_u) + u_h * |h_ref|
+with max|silu'| < 1.1 and u_h the unit roundoff of h's storage type.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from synth import workloads
+from tests.gpu_util import TAU, UNIT, check_tol, device, empty, to_dev, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def kq():
+    from block_quantized_weight_q4_amd import _build, kq as mod
+
+    _build.build_if_missing()
+    mod.lib()
+    return mod
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+def _ws(kq, E, T, top_k, n_out=0):
+    nbytes = kq.kq_moe_workspace_bytes(E, T, top_k, n_out)
+    return torch.empty(nbytes, dtype=torch.uint8, device=device())
+
+
+def _ids(rng, T, E, top_k):
+    return np.stack([rng.choice(E, top_k, replace=False) for _ in range(T)]).astype(np.uint32)
+
+
+@pytest.mark.parametrize("E,T,top_k", [(1, 1, 1), (8, 1, 8), (128, 1, 8), (128, 256, 8),
+                                       (16, 300, 4), (5, 2000, 2), (4096, 64, 16)])
+def test_route_schedule_exact(kq, E, T, top_k):
+    rng = synth.rng_for(E * 1000 + T)
+    ids = _ids(rng, T, E, top_k)
+    if T * top_k > 8:
+        ids.ravel()[rng.integers(0, T * top_k, 3)] = [E, E + 1, 0xFFFFFFFF]
+    _say("route", E, T, top_k)
+    ws = _ws(kq, E, T, top_k)
+    kq.kq_moe_route(to_dev(ids), T, top_k, E, ws)
+    torch.cuda.synchronize()
+    got = kq.moe_schedule(ws, E, T, top_k)
+    ref = oracle.route(ids, E, kq.MOE_TILE_ROWS)
+    assert got["n_invalid"] == ref["n_invalid"]
+    for key in ("counts", "offsets", "perm", "tiles"):
+        assert np.array_equal(got[key], ref[key]), key
+
+
+def _moe_case(kind, E, n, k, T, top_k, seed):
+    rng = synth.rng_for(seed)
+    w = synth.weight_blocks(kind, rng, E * n, k)
+    stride = n * synth.row_bytes(kind, k)
+    ids = _ids(rng, T, E, top_k)
+    scores = rng.uniform(0.05, 1.0, size=(T, top_k)).astype(np.float32)
+    return rng, w, stride, ids, scores
+
+
+@pytest.mark.parametrize("kind", ["q4_k", "q8_0", "tq1_g128"])
+@pytest.mark.parametrize("layout", [0, 1])
+@pytest.mark.parametrize("mixed", [False, True])
+@pytest.mark.parametrize("E,T,top_k", [(8, 5, 3), (4, 70, 4)])
+def test_qmm_id_small(kq, kind, layout, mixed, E, T, top_k):
+    n, k = 96, {"q4_k": 512, "q8_0": 160, "tq1_g128": 384}[kind]
+    rng, w, stride, ids, scores = _moe_case(kind, E, n, k, T, top_k, 40 + T)
+    x_rows = T if layout == 0 else T * top_k
+    x = synth.activations(rng, (x_rows, k), "f16")
+    _say("qmm_id", kind, layout, mixed, E, T, top_k)
+    y = empty((T if mixed else T * top_k, n), "f32")
+    ws = _ws(kq, E, T, top_k, n if mixed else 0)
+    kq.kq_qmm_id(kind, to_dev(w), E, n, k, stride, to_dev(x, "f16"), layout, to_dev(ids), T,
+                 top_k, to_dev(scores) if mixed else None, y, ws)
+    torch.cuda.synchronize()
+    ref, s = oracle.qmm_id(kind, w, E, n, k, stride, x, "f16", layout == 1, ids, T, top_k,
+                           scores if mixed else None)
+    check_tol(to_f64(y), ref, s, TAU["f16"], f"qmm_id {kind}")
+
+
+def test_qmm_id_invalid_ids_poison(kq):
+    E, n, k, T, top_k = 6, 64, 256, 4, 2
+    rng, w, stride, ids, scores = _moe_case("q4_k", E, n, k, T, top_k, 77)
+    ids = ids.copy()
+    ids[1, 1] = E       # out of range
+    ids[3, 0] = 1 << 30
+    x = synth.activations(rng, (T, k), "f16")
+    for mixed in (False, True):
+        y = empty((T if mixed else T * top_k, n), "f16")
+        ws = _ws(kq, E, T, top_k, n if mixed else 0)
+        kq.kq_qmm_id("q4_k", to_dev(w), E, n, k, stride, to_dev(x, "f16"), 0, to_dev(ids), T,
+                     top_k, to_dev(scores) if mixed else None, y, ws)
+        torch.cuda.synchronize()
+        got = to_f64(y)
+        ref, s = oracle.qmm_id("q4_k", w, E, n, k, stride, x, "f16", False, ids, T, top_k,
+                               scores if mixed else None)
+        bad = np.isnan(ref).all(axis=1)
+        assert bad.sum() == 2
+        assert np.isnan(got[bad]).all()
+        check_tol(got[~bad], ref[~bad], s[~bad], TAU["f16"], "valid rows")
+
+
+def _check_glu(h, ref, tau, h_dt, what):
+    g, u, sg, su = ref["g"], ref["u"], ref["sg"], ref["su"]
+    assert not np.isnan(h).any(), what
+    if h_dt == "f16":
+        # values past the fp16 range must be stored as infinities of the right sign
+        over = np.abs(ref["h"]) >= 65520.0
+        assert np.array_equal(h[over], np.sign(ref["h"][over]) * np.inf), what
+        h, g, u, sg, su = h[~over], g[~over], u[~over], sg[~over], su[~over]
+        ref = {"h": ref["h"][~over]}
+    with np.errstate(over="ignore"):
+        sig = 1.0 / (1.0 + np.exp(-g))
+    bound = tau * (1.1 * np.abs(u) * sg + np.abs(g * sig) * su) + UNIT[h_dt] * np.abs(ref["h"])
+    err = np.abs(h - ref["h"])
+    bad = err > bound
+    assert not bad.any(), f"{what}: {bad.sum()} outside; worst {np.max(err - bound):.3e}"
+
+
+@pytest.mark.parametrize("kind", ["q4_k", "q8_0", "tq1_g128"])
+@pytest.mark.parametrize("h_dt", ["f16", "f32", "bf16"])
+def test_moe_glu_small(kq, kind, h_dt):
+    E, n, k, T, top_k = 6, 80, {"q4_k": 512, "q8_0": 96, "tq1_g128": 256}[kind], 9, 3
+    rng = synth.rng_for(90)
+    gate = synth.weight_blocks(kind, rng, E * n, k)
+    up = synth.weight_blocks(kind, rng, E * n, k)
+    stride = n * synth.row_bytes(kind, k)
+    ids = _ids(rng, T, E, top_k)
+    x = synth.activations(rng, (T, k), "f16")
+    _say("moe_glu", kind, h_dt)
+    h = empty((T, top_k, n), h_dt)
+    ws = _ws(kq, E, T, top_k)
+    kq.kq_moe_glu(kind, to_dev(gate), to_dev(up), E, n, k, stride, to_dev(x, "f16"), to_dev(ids),
+                  T, top_k, h, ws)
+    torch.cuda.synchronize()
+    ref = oracle.moe_glu(kind, gate, up, E, n, k, stride, x, "f16", ids, T, top_k)
+    _check_glu(to_f64(h), ref, TAU["f16"], h_dt, f"moe_glu {kind} {h_dt}")
+
+
+@pytest.fixture(scope="module")
+def c4_dev(kq):
+    c = workloads.c4()
+    d = {key: c[key] for key in c}
+    d["gate_d"], d["up_d"], d["down_d"] = to_dev(c["gate"]), to_dev(c["up"]), to_dev(c["down"])
+    return d
+
+
+def _moe_layer_gpu(kq, c, T):
+    E, H, F, top_k = c["n_experts"], c["hidden"], c["ffn"], c["top_k"]
+    x = to_dev(c["x"][:T], "f16")
+    ids = to_dev(c["ids"][:T])
+    scores = to_dev(c["scores"][:T])
+    # h and the layer output are fp32: with these unnormalised random weights
+    # h reaches ~5e5 and the output ~1e8, past the fp16 range
+    h = empty((T, top_k, F), "f32")
+    ws = _ws(kq, E, T, top_k, H)
+    kq.kq_moe_glu("q4_k", c["gate_d"], c["up_d"], E, F, H, c["gate_stride"], x, ids, T, top_k, h,
+                  ws)
+    out = empty((T, H), "f32")
+    kq.kq_qmm_id("q4_k", c["down_d"], E, H, F, c["down_stride"], h, kq.LAYOUT_SLOTTED, ids, T,
+                 top_k, scores, out, ws)
+    torch.cuda.synchronize()
+    return to_f64(h), to_f64(out)
+
+
+def test_moe_c4_decode_full(kq, c4_dev):
+    """C4 decode (1 token, top-8 of 128): every output of the layer."""
+    c = c4_dev
+    _say("moe C4 decode")
+    h, out = _moe_layer_gpu(kq, c, 1)
+    ref, s = oracle.moe_layer("q4_k", c["gate"], c["up"], c["down"], c["n_experts"], c["hidden"],
+                              c["ffn"], c["gate_stride"], c["down_stride"], c["x"][:1], "f16",
+                              c["ids"][:1], 1, c["top_k"], c["scores"][:1])
+    check_tol(out, ref, s, TAU["f16"], "moe C4 decode")
+    g = oracle.moe_glu("q4_k", c["gate"], c["up"], c["n_experts"], c["ffn"], c["hidden"],
+                       c["gate_stride"], c["x"][:1], "f16", c["ids"][:1], 1, c["top_k"])
+    _check_glu(h, g, TAU["f16"], "f32", "moe C4 decode h")
+
+
+def test_moe_c4_prefill_sampled_tokens(kq, c4_dev):
+    """C4 prefill (256 tokens): whole output rows of sampled tokens."""
+    c = c4_dev
+    _say("moe C4 prefill")
+    h, out = _moe_layer_gpu(kq, c, c["T"])
+    for t in (0, 97, 255):
+        ref, s = oracle.moe_layer("q4_k", c["gate"], c["up"], c["down"], c["n_experts"],
+                                  c["hidden"], c["ffn"], c["gate_stride"], c["down_stride"],
+                                  c["x"][t:t + 1], "f16", c["ids"][t:t + 1], 1, c["top_k"],
+                                  c["scores"][t:t + 1])
+        check_tol(out[t:t + 1], ref, s, TAU["f16"], f"moe C4 prefill token {t}")
