@@ -1,0 +1,369 @@
+"""Benchmark of the block-quantized product path on one MI355X.
+
+One step is one pass over every stage of the hot path on its synthetic
+workload:
+  dequant   Q4_K 2048x2048 -> fp32                         (2048x2048, seed 101)
+  qmv_c1    Q4_K 2048x2048 GEMV, fp32 x/y                  (seed 101)
+  qmv_c2    Q4_K 14336x4096 and 4096x14336 GEMV, fp16 x at batch 1/4/8, fp16 y  (seed 102)
+  qmm_c3    Q4_K and Q8_0 4096x4096 and 14336x4096, bf16 x at M=512/2048, bf16 y (seed 103)
+  moe_c4    128 experts, Q4_K gate/up 2048x7168, down 7168x2048, top-8;
+            fp16 x, fp32 h and output; 1 token (decode) and 256 tokens (seed 104)
+  tq1_c5    TQ1_G128 17408x5120 and 5120x17408, fp16 x at batch 1 and M=512 (seed 105)
+
+The headline value is the Q4_K decode GEMV (the six qmv_c2 calls): weight
+bytes streamed per second.  Every call reads weights from HBM: weight-bound
+stages rotate over >= 1 GiB of distinct weight copies (the 256 MB Infinity
+Cache would otherwise serve them), and MoE decode rotates over tokens, whose
+expert choices differ.  Each stage's calls run back to back between one pair
+of HIP events on the stream the kernels are launched on.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--stages a,b] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Q4_K GEMV weight-GB/s (% of HBM peak); prefill qmm TFLOP/s; MoE tokens/s"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFS = 2500.0
+GIB = 1 << 30
+STAGES = ("dequant", "qmv_c1", "qmv_c2", "qmm_c3", "moe_c4", "tq1_c5")
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--stages", default=",".join(STAGES))
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="only run a 256 MiB device copy (counter calibration)")
+    return p.parse_args()
+
+
+class Stage:
+    """A list of calls timed as one group; `work` gives the algorithmic
+    bytes and flops of one pass over `calls`."""
+
+    def __init__(self, name, calls, bytes_, flops, tokens=0, note=""):
+        self.name, self.calls, self.bytes, self.flops = name, calls, bytes_, flops
+        self.tokens, self.note = tokens, note
+        self.ms = []
+
+    def run(self):
+        for c in self.calls:
+            c()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; "
+                          f"--gpus {args.gpus} is not supported"}))
+        sys.exit(2)
+
+    import torch
+
+    from block_quantized_weight_q4_amd import _build, kq
+    import synth
+    from synth import workloads
+
+    _build.build_if_missing()
+    kq.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.calibrate_copy:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration_copy_bytes": 256 << 20}))
+        return
+
+    wanted = [s for s in args.stages.split(",") if s]
+
+    def d8(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    def d16(a, dt):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(dt).to(dev)
+
+    def copies(t, nbytes_each, min_total=GIB):
+        n = max(1, -(-min_total // nbytes_each))
+        return [t] + [t.clone() for _ in range(n - 1)]
+
+    stages = []
+    rot = {"i": 0}
+
+    def nxt(lst):
+        rot["i"] += 1
+        return lst[rot["i"] % len(lst)]
+
+    if "dequant" in wanted or "qmv_c1" in wanted:
+        c = workloads.c1()
+        w = d8(c["w"])
+        ws = copies(w, w.numel())
+        if "dequant" in wanted:
+            outs = [torch.empty((2048, 2048), dtype=torch.float32, device=dev) for _ in range(8)]
+            calls = [lambda ws=ws, outs=outs: kq.kq_dequantize("q4_k", nxt(ws), 2048, 2048,
+                                                                nxt(outs)) for _ in range(20)]
+            stages.append(Stage("dequant", calls, 20 * (w.numel() + 2048 * 2048 * 4), 0,
+                                note="Q4_K 2048x2048 -> fp32"))
+        if "qmv_c1" in wanted:
+            x = torch.from_numpy(c["x"]).to(dev)
+            y = torch.empty((1, 2048), dtype=torch.float32, device=dev)
+            calls = [lambda ws=ws, x=x, y=y: kq.kq_qmv("q4_k", nxt(ws), 2048, 2048, x, 1, y)
+                     for _ in range(40)]
+            stages.append(Stage("qmv_c1", calls, 40 * (w.numel() + 2 * 2048 * 4),
+                                40 * 2 * 2048 * 2048, note="Q4_K 2048x2048 GEMV fp32"))
+
+    c2_parts = []
+    if "qmv_c2" in wanted:
+        calls, nbytes, flops = [], 0, 0
+        for case in workloads.c2():
+            n, k = case["n"], case["k"]
+            w = d8(case["w"])
+            ws = copies(w, w.numel())
+            x = d16(case["x"], torch.float16)
+            for b in (1, 4, 8):
+                y = torch.empty((b, n), dtype=torch.float16, device=dev)
+                reps = len(ws)
+                part = [(lambda n=n, k=k, x=x, b=b, y=y, ws=ws:
+                         kq.kq_qmv("q4_k", nxt(ws), n, k, x, b, y)) for _ in range(reps)]
+                pbytes = reps * (w.numel() + b * (k + n) * 2)
+                c2_parts.append(Stage(f"qmv_c2_{n}x{k}_b{b}", part, pbytes, reps * 2 * b * n * k))
+                calls += part
+                nbytes += pbytes
+                flops += reps * 2 * b * n * k
+        stages.append(Stage("qmv_c2", calls, nbytes, flops,
+                            note="Q4_K 14336x4096 + 4096x14336, batch 1/4/8, fp16"))
+
+    c3_parts = []
+    if "qmm_c3" in wanted:
+        cases, xh = workloads.c3()
+        x = d16(xh, torch.bfloat16)
+        for case in cases:
+            kind, n, k = case["kind"], case["n"], case["k"]
+            w = d8(case["w"])
+            ws = copies(w, w.numel(), min_total=4 * w.numel())
+            for m in (512, 2048):
+                y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+                xm = x[:m]
+                part = [(lambda kind=kind, n=n, k=k, m=m, y=y, ws=ws, xm=xm:
+                         kq.kq_qmm(kind, nxt(ws), n, k, xm, m, y)) for _ in range(len(ws))]
+                c3_parts.append(Stage(f"qmm_c3_{kind}_{n}x{k}_m{m}", part,
+                                      len(part) * (w.numel() + m * (k + n) * 2),
+                                      len(part) * 2 * m * n * k))
+
+    if "tq1_c5" in wanted:
+        calls_v, calls_m, bv, bm, fv, fm = [], [], 0, 0, 0, 0
+        for case in workloads.c5():
+            n, k = case["n"], case["k"]
+            w = d8(case["w"])
+            ws = copies(w, w.numel())
+            x = d16(case["x"], torch.float16)
+            y1 = torch.empty((1, n), dtype=torch.float16, device=dev)
+            ym = torch.empty((512, n), dtype=torch.float16, device=dev)
+            for _ in range(len(ws)):
+                calls_v.append(lambda n=n, k=k, ws=ws, x=x, y1=y1:
+                               kq.kq_qmv("tq1_g128", nxt(ws), n, k, x[:1], 1, y1))
+                bv += w.numel() + (k + n) * 2
+                fv += 2 * n * k
+            for _ in range(4):
+                calls_m.append(lambda n=n, k=k, ws=ws, x=x, ym=ym:
+                               kq.kq_qmm("tq1_g128", nxt(ws), n, k, x, 512, ym))
+                bm += w.numel() + 512 * (k + n) * 2
+                fm += 2 * 512 * n * k
+        stages.append(Stage("tq1_c5_b1", calls_v, bv, fv, note="TQ1 GEMV batch 1, fp16"))
+        stages.append(Stage("tq1_c5_m512", calls_m, bm, fm, note="TQ1 qmm M=512, fp16"))
+
+    if "moe_c4" in wanted:
+        c = workloads.c4()
+        E, H, F, T, top_k = c["n_experts"], c["hidden"], c["ffn"], c["T"], c["top_k"]
+        gate, up, down = d8(c["gate"]), d8(c["up"]), d8(c["down"])
+        xall = d16(c["x"], torch.float16)
+        ids = torch.from_numpy(c["ids"].view(np.int32)).to(dev)
+        scores = torch.from_numpy(c["scores"]).to(dev)
+        mws = torch.empty(kq.kq_moe_workspace_bytes(E, T, top_k, H), dtype=torch.uint8, device=dev)
+        h = torch.empty((T, top_k, F), dtype=torch.float32, device=dev)
+        out = torch.empty((T, H), dtype=torch.float32, device=dev)
+        per_expert = 3 * F * synth.row_bytes("q4_k", H)
+
+        def layer(t0, nt):
+            kq.kq_moe_glu("q4_k", gate, up, E, F, H, c["gate_stride"], xall[t0:t0 + nt],
+                          ids[t0:t0 + nt], nt, top_k, h[:nt], mws)
+            kq.kq_qmm_id("q4_k", down, E, H, F, c["down_stride"], h[:nt], kq.LAYOUT_SLOTTED,
+                         ids[t0:t0 + nt], nt, top_k, scores[t0:t0 + nt], out[:nt], mws)
+
+        dec_calls = [lambda t=t, layer=layer: layer(t, 1) for t in range(0, 64)]
+        # every decode token reads its 8 experts' three matrices
+        stages.append(Stage("moe_c4_decode", dec_calls, len(dec_calls) * 8 * per_expert,
+                            len(dec_calls) * 8 * 3 * 2 * F * H, tokens=len(dec_calls),
+                            note="1 token, top-8 of 128"))
+        pre_calls = [lambda layer=layer, T=T: layer(0, T) for _ in range(2)]
+        used = len(np.unique(c["ids"]))
+        stages.append(Stage("moe_c4_prefill", pre_calls, 2 * used * per_expert,
+                            2 * T * top_k * 3 * 2 * F * H, tokens=2 * T,
+                            note=f"256 tokens, {used} experts hit"))
+
+    # ---------------------------------------------------------------- timing
+    # Each stage's calls are captured once into a HIP graph and replayed, so
+    # the kernels run back to back instead of waiting on Python launches.
+    timed = [s for s in stages if s.name not in ("qmv_c2",)] + c2_parts + c3_parts
+    graphs = {}
+    for s in timed:
+        s.run()  # eager pass: lazy initialisation outside the capture
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            s.run()
+        graphs[s.name] = g
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        for s in timed:
+            graphs[s.name].replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = {s.name: [] for s in timed}
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        for s in timed:
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            graphs[s.name].replay()
+            b.record(stream)
+            ev[s.name].append((a, b))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for s in timed:
+        s.ms = [a.elapsed_time(b) for a, b in ev[s.name]]
+
+    rows = {}
+    for s in timed:
+        ms = float(np.median(s.ms))
+        r = {"ms": round(ms, 4), "calls": len(s.calls), "us_per_call": round(1000 * ms / len(s.calls), 3)}
+        if s.bytes:
+            r["GB/s"] = round(s.bytes / (ms * 1e-3) / 1e9, 1)
+            r["frac_hbm"] = round(r["GB/s"] / HBM_PEAK_GBS, 4)
+        if s.flops:
+            r["TFLOP/s"] = round(s.flops / (ms * 1e-3) / 1e12, 2)
+        if s.tokens:
+            r["tokens/s"] = round(s.tokens / (ms * 1e-3), 1)
+        if s.note:
+            r["note"] = s.note
+        rows[s.name] = r
+    if c2_parts:
+        ms = sum(float(np.median(p.ms)) for p in c2_parts)
+        nbytes = sum(p.bytes for p in c2_parts)
+        rows["qmv_c2"] = {"ms": round(ms, 4), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                          "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    if c3_parts:
+        ms = sum(float(np.median(p.ms)) for p in c3_parts)
+        fl = sum(p.flops for p in c3_parts)
+        rows["qmm_c3"] = {"ms": round(ms, 4), "TFLOP/s": round(fl / (ms * 1e-3) / 1e12, 2),
+                          "frac_bf16_peak": round(fl / (ms * 1e-3) / 1e12 / BF16_PEAK_TFS, 4)}
+        for p in c3_parts:
+            rows[p.name]["frac_bf16_peak"] = round(rows[p.name]["TFLOP/s"] / BF16_PEAK_TFS, 4)
+
+    result = {
+        "metric": METRIC,
+        "value": rows.get("qmv_c2", {}).get("GB/s"),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(1000 * wall / args.steps, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "Q4_K decode GEMV 14336x4096 and 4096x14336, fp16 activations at "
+                               "batch 1/4/8, fp16 output, weights rotated over >=1 GiB of copies",
+                   "stages": wanted},
+        "roofline": roofline(rows),
+        "rows": rows,
+    }
+    if not args.no_cpu_baseline and "qmv_c2" in wanted:
+        result["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(result))
+
+
+def _kernel_sha():
+    h = hashlib.sha256()
+    src = os.path.join(ROOT, "block_quantized_weight_q4_amd", "csrc")
+    for f in sorted(os.listdir(src)):
+        if f.endswith((".hip", ".h")):
+            h.update(open(os.path.join(src, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def _traffic():
+    """HBM bytes per dispatch of the GEMV from the committed counter summary,
+    when it was taken on the current kernel sources; else None."""
+    path = os.path.join(PROFILE_DIR, "qmv_q4k_c2_counters.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path))
+    except ValueError:
+        return None
+    if d.get("kernel_sha") != _kernel_sha():
+        return None
+    return d.get("hbm_bytes_per_dispatch")
+
+
+def roofline(rows):
+    r = rows.get("qmv_c2")
+    if not r:
+        return None
+    return {"bound": "hbm", "achieved": r["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(r["GB/s"] / HBM_PEAK_GBS, 4), "traffic": _traffic(),
+            "kernel": "skinny Q4_K decode product (kq_qmv)"}
+
+
+def cpu_baseline():
+    """The fp64 CPU oracle on a bounded sample of the headline workload."""
+    import oracle
+    from synth import workloads
+
+    oracle.lib()
+    cases = workloads.c2()
+    threads = oracle.num_threads()
+    t_total, nbytes, calls = 0.0, 0, 0
+    deadline = 20.0
+    for case in cases:
+        for b in (1, 4, 8):
+            t0 = time.perf_counter()
+            oracle.qmm("q4_k", case["w"], case["n"], case["k"], case["x"][:b], "f16", b)
+            t_total += time.perf_counter() - t0
+            nbytes += case["w"].nbytes
+            calls += 1
+            if t_total > deadline:
+                break
+        if t_total > deadline:
+            break
+    return {"value": round(nbytes / t_total / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{calls} of the 6 Q4_K GEMV calls (14336x4096, 4096x14336 at batch "
+                      f"1/4/8), fp64, {t_total:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()
