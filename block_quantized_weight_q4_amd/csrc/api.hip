@@ -84,7 +84,10 @@ MoeLayout moe_layout(int64_t n_experts, int64_t n_tokens, int64_t top_k, int64_t
     MoeLayout L{};
     L.n_experts = n_experts;
     L.rows = n_tokens * top_k;
-    L.max_tiles = (L.rows + kMoeTileRows - 1) / kMoeTileRows + n_experts;
+    // every tile holds at least one row, and each expert has at most one
+    // partial tile
+    const int64_t bound = (L.rows + kMoeTileRows - 1) / kMoeTileRows + n_experts;
+    L.max_tiles = L.rows < bound ? L.rows : bound;
     L.counts_off = 2;
     L.offsets_off = L.counts_off + n_experts;
     L.perm_off = L.offsets_off + n_experts + 1;
@@ -277,6 +280,7 @@ kq_status kq_qmm_id(kq_type t, const void* w, int64_t n_experts, int64_t n, int6
     a.ws = ws;
     a.tiles_off = L.tiles_off;
     a.perm_off = L.perm_off;
+    a.rows_cap = L.rows;
     if (scores) {
         float* slots = (float*)((char*)workspace + L.slot_off_bytes);
         a.y = slots;
@@ -325,6 +329,7 @@ kq_status kq_moe_glu(kq_type t, const void* gate_w, const void* up_w, int64_t n_
     a.ws = ws;
     a.tiles_off = L.tiles_off;
     a.perm_off = L.perm_off;
+    a.rows_cap = L.rows;
     a.y = h;
     a.y_dt = h_dt;
     a.y_row = n;

@@ -9,7 +9,7 @@ namespace kq {
 
 // Rows of a weight-streaming tile: one pass over a weight row serves up to
 // this many activation rows.
-constexpr int kMoeTileRows = 64;
+constexpr int kMoeTileRows = 32;
 
 // Layout of the MoE workspace (int32 words); see include/kq.h.
 struct MoeLayout {
@@ -39,12 +39,19 @@ struct SkinnyArgs {
     void* y;               // output
     int y_dt;              // output dtype
     int64_t y_row;         // elements between output rows
+    int64_t rows_cap;      // routed: most rows any schedule tile can hold
+    // set by the launcher of the matrix-core kernels
+    int xch;               // super-blocks of activations staged per chunk
+    int xstride;           // halves between staged activation rows
+    int red_off;           // byte offset of the cross-wave reduction buffer
 };
 
 hipError_t launch_dequant(int codec, const void* w, int64_t rows, int64_t k, void* out, int out_dt,
                           hipStream_t s);
 hipError_t launch_skinny(int codec, int x_dt, bool glu, const SkinnyArgs& a, int64_t grid_tiles,
                          hipStream_t s);
+hipError_t launch_mmv_q4k(bool glu, const SkinnyArgs& a, int64_t grid_tiles, hipStream_t s);
+hipError_t launch_mmv2_q4k(bool glu, const SkinnyArgs& a, int64_t grid_tiles, hipStream_t s);
 hipError_t launch_gemm(int codec, int x_dt, const void* w, int64_t n, int64_t k, const void* x,
                        int64_t m, void* y, int y_dt, hipStream_t s);
 hipError_t launch_route(const uint32_t* ids, int64_t rows, int64_t n_experts, const MoeLayout& L,

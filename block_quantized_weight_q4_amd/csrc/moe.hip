@@ -1,6 +1,6 @@
 // moe.hip -- expert routing schedule, slot-order mixing and invalid-id poison.
 //
-// mlx-kquant "bindings.cpp": expert_tile_map (64-row tiles per expert segment,
+// mlx-kquant "bindings.cpp": expert_tile_map (fixed-size row tiles per expert segment,
 // only the last partial, built on the GPU with no host sync),
 // gather_qmv_mix_ns_kq (each slot accumulated in f32 weighted by its score);
 // mlx-native "quantized_matmul_id_ggml.rs": map0 regroup with on-device id

@@ -239,6 +239,12 @@ static void launch_x(int x_dt, const SkinnyArgs& a, int mb, dim3 grid, hipStream
 
 hipError_t launch_skinny(int codec, int x_dt, bool glu, const SkinnyArgs& a, int64_t grid_tiles,
                          hipStream_t s) {
+    if (codec == Q4_K && x_dt == F16) {
+        // decode shapes (at most 16 activation rows per tile): weights and
+        // activations streamed through LDS; wider routed tiles: mmv.hip
+        if (a.ws ? a.rows_cap <= 16 : a.m <= 16) return launch_mmv2_q4k(glu, a, grid_tiles, s);
+        return launch_mmv_q4k(glu, a, grid_tiles, s);
+    }
     int mb;
     int64_t tiles;
     if (a.ws) {

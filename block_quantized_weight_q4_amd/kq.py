@@ -28,7 +28,7 @@ TYPES = {"q4_k": 0, "q8_0": 1, "tq1_g128": 2}
 _DT = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 LAYOUT_SHARED, LAYOUT_SLOTTED = 0, 1
 ACT_SILU = 0
-MOE_TILE_ROWS = 64
+MOE_TILE_ROWS = 32
 
 # Every function include/kq.h declares.
 SYMBOLS = (
@@ -180,7 +180,7 @@ def moe_schedule(workspace, n_experts: int, n_tokens: int, top_k: int) -> dict:
     """Views of the schedule kq_moe_route leaves at the start of the workspace
     (layout documented in include/kq.h), copied to the host."""
     E, R = n_experts, n_tokens * top_k
-    max_tiles = (R + MOE_TILE_ROWS - 1) // MOE_TILE_ROWS + E
+    max_tiles = min(R, (R + MOE_TILE_ROWS - 1) // MOE_TILE_ROWS + E)
     words = 2 + E + (E + 1) + R + 3 * max_tiles
     w = workspace.view(torch.int32)[:words].cpu().numpy()
     n_tiles, n_invalid = int(w[0]), int(w[1])

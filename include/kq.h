@@ -139,16 +139,17 @@ size_t kq_moe_workspace_bytes(int64_t n_experts, int64_t n_tokens, int64_t top_k
  *   [3+2E+R .. +3*max_tiles)  tiles (expert, row_start, num_rows): each
  *                             expert's segment cut into KQ_MOE_TILE_ROWS-row
  *                             tiles, only the last of which may be partial
- * with R = n_tokens * top_k and max_tiles = ceil(R / KQ_MOE_TILE_ROWS) +
- * n_experts.  The fp32 slot buffer of kq_qmm_id follows at the next
+ * with R = n_tokens * top_k and max_tiles = min(R, ceil(R / KQ_MOE_TILE_ROWS)
+ * + n_experts).  The fp32 slot buffer of kq_qmm_id follows at the next
  * 256-byte boundary.
  */
-#define KQ_MOE_TILE_ROWS 64
+#define KQ_MOE_TILE_ROWS 32
 
 /*
  * kq_moe_route -- sort routed rows by expert and cut them into tiles.
- * mlx-kquant "bindings.cpp", expert_tile_map (64-row tiles, only the last tile
- * of a segment partial, built on the GPU with no host sync); mlx-native
+ * mlx-kquant "bindings.cpp", expert_tile_map (fixed-size row tiles, only the
+ * last tile of a segment partial, built on the GPU with no host sync; here
+ * KQ_MOE_TILE_ROWS = 32 rows, two 16-row MFMA sub-tiles); mlx-native
  * "quantized_matmul_id_ggml.rs", map0 regroup (ids validated on the device).
  *
  *   ids        [n_tokens, top_k] uint32 expert ids (device)
