@@ -4,204 +4,310 @@
 // "ternel_packed_model.py", tq1_gemm (decode a weight once and reuse it
 // across a whole block of activation rows on the matrix units).
 //
-// The contraction runs on MFMA in the activation's 16-bit type (bf16 or fp16)
-// with fp32 accumulation.  Each K step the workgroup decodes its weight tile
-// once into LDS (so every decoded weight feeds BM rows), stages the matching
-// activation tile, and four waves each multiply a 64x64 sub-tile with
-// 32x32x16 MFMAs.
+// The contraction runs on v_mfma_f32_32x32x16 in the activation's 16-bit
+// type (bf16 or fp16) with fp32 accumulation.  A workgroup of four waves owns
+// a BM x BN output tile; per K step of 64 it decodes its BN x 64 weight tile
+// once into LDS (so each decoded weight feeds BM rows) next to the BM x 64
+// activation tile.  The global loads of step k+1 are issued before the MFMAs
+// of step k and written to LDS after them, so memory latency overlaps the
+// matrix work.  Decoded weights are rounded once from fp32 to the 16-bit
+// operand type (round to nearest even).
 #include "kq_device.h"
 #include "kq_internal.h"
 
 namespace kq {
 
-constexpr int BM = 128, BN = 128, BK = 64, LDS_STRIDE = BK + 8;  // +8: bank spread
+constexpr int BK = 64, LDS_STRIDE = BK + 8;  // +8 halves: rows start in different banks
 
-template <int XDT> struct Mfma;
-template <> struct Mfma<BF16> {
-    typedef bf16x8 vec;
-    static __device__ __forceinline__ uint16_t cvt(float f) { return float_to_bf16_bits(f); }
-    static __device__ __forceinline__ float16_t mma(const short8& a, const short8& b, float16_t c) {
+typedef float float2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+
+template <int XDT> struct Op16;
+template <> struct Op16<BF16> {
+    static __device__ __forceinline__ uint32_t pack(float a, float b) {
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2_t{a, b}, bf16x2));
+    }
+    static __device__ __forceinline__ float16_t mma(const u32x4& a, const u32x4& b, float16_t c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                        __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
     }
 };
-template <> struct Mfma<F16> {
-    typedef half8 vec;
-    static __device__ __forceinline__ uint16_t cvt(float f) { return float_to_half_bits(f); }
-    static __device__ __forceinline__ float16_t mma(const short8& a, const short8& b, float16_t c) {
+template <> struct Op16<F16> {
+    static __device__ __forceinline__ uint32_t pack(float a, float b) {
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2_t{a, b}, half2v));
+    }
+    static __device__ __forceinline__ float16_t mma(const u32x4& a, const u32x4& b, float16_t c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, a),
                                                       __builtin_bit_cast(half8, b), c, 0, 0, 0);
     }
 };
 
-// Decode this thread's 32 weights of the BK=64 step `s` for weight row n into
-// v[0..31], destined for tile columns col0 .. col0+15 and col1 .. col1+15.
-template <int C> struct TileFill;
+// ---------------------------------------------------------------- weight tiles
+// One thread role = (tile row r, half h): 32 of the 64 weights of row r in a
+// K step.  Raw bytes are fetched into registers (Raw), then decoded into 32
+// floats and the tile columns they belong to.
+template <int C> struct WTile;
 
-// Q4_K: step s is chunk c = s%4 of super-block s/4 (sub-blocks 2c and 2c+1).
-// Thread half h takes quant bytes 32c+16h..+16: low nibbles -> columns 16h+i,
-// high nibbles -> 32+16h+i.
-template <> struct TileFill<Q4_K> {
-    static __device__ __forceinline__ bool fill(const uint8_t* row, int64_t k, int64_t s, int h,
-                                                float (&v)[32], int& col0, int& col1) {
-        const int64_t sb = s >> 2;
-        const int c = (int)s & 3;
-        const uint8_t* blk = row + sb * 144;
-        const u32x4 hd = *(const u32x4*)blk;
-        const u32x4 qb = *(const u32x4*)(blk + 16 + 32 * c + 16 * h);
+// Q4_K: step s is chunk c = s%4 of super-block s/4 (sub-blocks 2c, 2c+1).
+// Half h: quant bytes 32c+16h..+16 -> low nibbles to columns 16h+i, high
+// nibbles to 32+16h+i.
+template <> struct WTile<Q4_K> {
+    struct Raw { u32x4 hd, q; };
+    static __device__ __forceinline__ void fetch(const uint8_t* row, int s, int h, Raw& r, bool) {
+        const uint8_t* blk = row + (s >> 2) * 144;
+        r.hd = *(const u32x4*)blk;
+        r.q = *(const u32x4*)(blk + 16 + 32 * (s & 3) + 16 * h);
+    }
+    template <int XDT>
+    static __device__ __forceinline__ void decode(const Raw& r, int s, int h, uint32_t (&lo)[8],
+                                                  uint32_t (&hi)[8], int& col_lo, int& col_hi) {
+        const int c = s & 3;
         int sc0, m0, sc1, m1;
-        q4k_scale_min(hd, 2 * c, sc0, m0);
-        q4k_scale_min(hd, 2 * c + 1, sc1, m1);
-        const float d = q4k_d(hd), dmin = q4k_dmin(hd);
+        q4k_scale_min(r.hd, 2 * c, sc0, m0);
+        q4k_scale_min(r.hd, 2 * c + 1, sc1, m1);
+        const float d = q4k_d(r.hd), dmin = q4k_dmin(r.hd);
         const float s0 = d * (float)sc0, s1 = d * (float)sc1;
-        const float n0 = dmin * (float)m0, n1 = dmin * (float)m1;
+        const float n0 = -dmin * (float)m0, n1 = -dmin * (float)m1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t wd = r.q[i];
+#pragma unroll
+            for (int b = 0; b < 4; b += 2) {
+                const uint32_t b0 = (wd >> (8 * b)) & 0xffu, b1 = (wd >> (8 * b + 8)) & 0xffu;
+                lo[2 * i + b / 2] = Op16<XDT>::pack(__builtin_fmaf(s0, (float)(b0 & 15u), n0),
+                                                    __builtin_fmaf(s0, (float)(b1 & 15u), n0));
+                hi[2 * i + b / 2] = Op16<XDT>::pack(__builtin_fmaf(s1, (float)(b0 >> 4), n1),
+                                                    __builtin_fmaf(s1, (float)(b1 >> 4), n1));
+            }
+        }
+        col_lo = 16 * h;
+        col_hi = 32 + 16 * h;
+    }
+};
+
+// Q8_0: step s covers blocks 2s, 2s+1 (68 contiguous, 4-byte aligned bytes);
+// half h reads exactly its 34-byte block: h = 0 takes dwords 0..7 and the
+// 16-bit word at byte 32; h = 1 the 16-bit word at byte 34 (its scale) and
+// dwords 9..16 (its quants, dword aligned).
+template <> struct WTile<Q8_0> {
+    struct Raw { uint32_t w[8]; uint32_t tail; };
+    // Rows start on a 4-byte boundary only when the row size is a multiple of
+    // 4 bytes (an even number of blocks); otherwise the block is read as
+    // 16-bit words.
+    static __device__ __forceinline__ void fetch(const uint8_t* row, int s, int h, Raw& r,
+                                                 bool rows_4b_aligned) {
+        const uint8_t* base = row + 68 * s;
+        if (rows_4b_aligned) {
+            const uint32_t* p = (const uint32_t*)base + (h ? 9 : 0);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) r.w[i] = p[i];
+        } else {
+            const uint16_t* p = (const uint16_t*)base + (h ? 18 : 0);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) r.w[i] = (uint32_t)p[2 * i] | ((uint32_t)p[2 * i + 1] << 16);
+        }
+        r.tail = *(const uint16_t*)(base + (h ? 34 : 32));
+    }
+    template <int XDT>
+    static __device__ __forceinline__ void decode(const Raw& r, int s, int h, uint32_t (&lo)[8],
+                                                  uint32_t (&hi)[8], int& col_lo, int& col_hi) {
+        // quant i of the block and its scale
+        auto wbyte = [&](int i) -> uint32_t { return (r.w[i >> 2] >> (8 * (i & 3))) & 0xffu; };
+        float d;
+        uint32_t q[32];
+        if (h == 0) {
+            d = half_bits_to_float(r.w[0] & 0xffffu);
+#pragma unroll
+            for (int i = 0; i < 30; ++i) q[i] = wbyte(2 + i);
+            q[30] = r.tail & 0xffu;
+            q[31] = r.tail >> 8;
+        } else {
+            d = half_bits_to_float(r.tail);
+#pragma unroll
+            for (int i = 0; i < 32; ++i) q[i] = wbyte(i);
+        }
+        uint32_t v[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            v[i] = Op16<XDT>::pack(d * (float)(int8_t)q[2 * i], d * (float)(int8_t)q[2 * i + 1]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) lo[i] = v[i], hi[i] = v[8 + i];
+        col_lo = 32 * h;
+        col_hi = 32 * h + 16;
+    }
+};
+
+// TQ1_G128: step s is half s%2 of group s/2; half h takes the group's columns
+// 32*qi .. 32*qi+31 with qi = 2*(s%2) + h.  Column c < 125 is digit c%5 of
+// code byte c/5, columns 125..127 digits of the tail byte; w = (digit-1)*s.
+template <> struct WTile<TQ1> {
+    struct Raw { uint32_t w[7]; };
+    static __device__ __forceinline__ void fetch(const uint8_t* row, int s, int h, Raw& r, bool) {
+        const uint32_t* p = (const uint32_t*)(row + (s >> 1) * 28);
+#pragma unroll
+        for (int i = 0; i < 7; ++i) r.w[i] = p[i];
+    }
+    template <int XDT, int QI>
+    static __device__ __forceinline__ void quarter(const Raw& r, uint32_t (&v)[16]) {
+        const float sc = half_bits_to_float(r.w[6] >> 16);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const uint32_t byte = (qb[i >> 2] >> (8 * (i & 3))) & 0xffu;
-            v[i] = __builtin_fmaf(s0, (float)(byte & 15u), -n0);
-            v[16 + i] = __builtin_fmaf(s1, (float)(byte >> 4), -n1);
+            float t[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int col = 32 * QI + 2 * i + e;
+                const int slot = col < 125 ? col / 5 : 25;
+                const int digit = col < 125 ? col - 5 * slot : col - 125;
+                const uint32_t code = (r.w[slot >> 2] >> (8 * (slot & 3))) & 0xffu;
+                t[e] = (float)tq1_trit(code, digit) * sc;
+            }
+            v[i] = Op16<XDT>::pack(t[0], t[1]);
         }
-        col0 = 16 * h;
-        col1 = 32 + 16 * h;
-        return true;
+    }
+    template <int XDT>
+    static __device__ __forceinline__ void decode(const Raw& r, int s, int h, uint32_t (&lo)[8],
+                                                  uint32_t (&hi)[8], int& col_lo, int& col_hi) {
+        uint32_t v[16];
+        switch (2 * (s & 1) + h) {
+        case 0: quarter<XDT, 0>(r, v); break;
+        case 1: quarter<XDT, 1>(r, v); break;
+        case 2: quarter<XDT, 2>(r, v); break;
+        default: quarter<XDT, 3>(r, v); break;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) lo[i] = v[i], hi[i] = v[8 + i];
+        col_lo = 32 * h;
+        col_hi = 32 * h + 16;
     }
 };
 
-// Q8_0: step s covers blocks 2s and 2s+1; thread half h takes block 2s+h.
-template <> struct TileFill<Q8_0> {
-    static __device__ __forceinline__ bool fill(const uint8_t* row, int64_t k, int64_t s, int h,
-                                                float (&v)[32], int& col0, int& col1) {
-        const int64_t b = 2 * s + h;
-        col0 = 32 * h;
-        col1 = 32 * h + 16;
-        if (b * 32 >= k) return false;
-        const uint16_t* blk = (const uint16_t*)(row + b * 34);
-        const float d = half_bits_to_float(blk[0]);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const uint32_t pair = blk[1 + i];
-            v[2 * i] = d * (float)(int8_t)(pair & 0xffu);
-            v[2 * i + 1] = d * (float)(int8_t)(pair >> 8);
-        }
-        return true;
-    }
-};
-
-// TQ1: step s is half s%2 of group s/2; thread half h takes columns
-// 64*(s%2) + 32h .. +32 of the group.
-template <> struct TileFill<TQ1> {
-    static __device__ __forceinline__ bool fill(const uint8_t* row, int64_t k, int64_t s, int h,
-                                                float (&v)[32], int& col0, int& col1) {
-        const uint8_t* blk = row + (s >> 1) * 28;
-        const int base = 64 * ((int)s & 1) + 32 * h;
-        uint32_t words[7];
-#pragma unroll
-        for (int i = 0; i < 7; ++i) words[i] = ((const uint32_t*)blk)[i];
-        const float sc = half_bits_to_float(words[6] >> 16);
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-            const int col = base + i;
-            const int slot = col < 125 ? col / 5 : 25;
-            const int digit = col < 125 ? col - 5 * slot : col - 125;
-            const uint32_t code = (words[slot >> 2] >> (8 * (slot & 3))) & 0xffu;
-            v[i] = (float)tq1_trit(code, digit) * sc;
-        }
-        col0 = 32 * h;
-        col1 = 32 * h + 16;
-        return true;
-    }
-};
-
-template <int C, int XDT>
+// ---------------------------------------------------------------- kernel
+// BM x BN tile, four waves as 2 x 2, each a (BM/2) x (BN/2) sub-tile of
+// 32x32 MFMA blocks.
+template <int C, int XDT, int BM, int BN>
 __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ w, int64_t n,
                                                    int64_t k, const uint16_t* __restrict__ x,
                                                    int64_t m, void* __restrict__ y, int y_dt) {
-    __shared__ uint16_t As[BM * LDS_STRIDE];
-    __shared__ uint16_t Bs[BN * LDS_STRIDE];
+    constexpr int TM = BM / 2, TN = BN / 2, FM = TM / 32, FN = TN / 32;
+    constexpr int XP = BM * 8 / 256;  // 16-byte activation pieces per thread per step
+    constexpr int ASZ = BM * LDS_STRIDE, BSZ = BN * LDS_STRIDE;
+    using WT = WTile<C>;
+    // two stages of [activation tile | weight tile]
+    __shared__ __align__(16) uint16_t lds[2 * (ASZ + BSZ)];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const int64_t n0 = (int64_t)blockIdx.x * BN, m0 = (int64_t)blockIdx.y * BM;
     const int64_t row_bytes = (k / CodecInfo<C>::QK) * CodecInfo<C>::BYTES;
+    const int steps = (int)((k + BK - 1) / BK);
 
-    float16_t acc[2][2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = float16_t{};
-
-    // fill roles: tile row r = tid/2, half h = tid%2
-    const int fr = tid >> 1, fh = tid & 1;
-    const int64_t wrow_idx = n0 + fr;
+    // weight role: tile row wr = tid/2 (< BN), half wh = tid%2
+    const int wr = tid >> 1, wh = tid & 1;
+    const bool wrole = wr < BN;
+    const int64_t wrow_idx = n0 + wr;
     const uint8_t* wrow = w + (wrow_idx < n ? wrow_idx : n - 1) * row_bytes;
-    const int64_t xrow_idx = m0 + fr;
-    const uint16_t* xrow = x + (xrow_idx < m ? xrow_idx : 0) * k;
+    const bool wvalid = wrole && wrow_idx < n;
 
-    const int64_t steps = (k + BK - 1) / BK;
-    for (int64_t s = 0; s < steps; ++s) {
-        // activation tile: row fr, columns 32*fh .. +32
-        {
-            u32x4 v[4] = {};
-            const int64_t c0 = s * BK + 32 * fh;
-            if (xrow_idx < m && c0 < k) {
-                const u32x4* p = (const u32x4*)(xrow + c0);
+    float16_t acc[FM][FN];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) v[i] = p[i];
-            }
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) *(u32x4*)&As[fr * LDS_STRIDE + 32 * fh + 8 * i] = v[i];
+        for (int j = 0; j < FN; ++j) acc[i][j] = float16_t{};
+
+    u32x4 xr[XP];
+    typename WT::Raw raw;
+    auto fetch = [&](int s) {
+#pragma unroll
+        for (int i = 0; i < XP; ++i) {
+            const int p = tid + 256 * i, r = p >> 3, q = p & 7;
+            const int64_t gm = m0 + r;
+            const int64_t c0 = (int64_t)s * BK + 8 * q;
+            xr[i] = (gm < m && c0 < k) ? *(const u32x4*)(x + gm * k + c0) : u32x4{0u, 0u, 0u, 0u};
         }
-        // weight tile: decode once, round to the MFMA type
-        {
-            float v[32];
-            int col0 = C == Q4_K ? 16 * fh : 32 * fh;
-            int col1 = C == Q4_K ? 32 + 16 * fh : 32 * fh + 16;
-            const bool ok = wrow_idx < n && TileFill<C>::fill(wrow, k, s, fh, v, col0, col1);
-            if (!ok) {
+        if (wrole && ((C != Q8_0) || (int64_t)(2 * s + wh) * 32 < k))
+            WT::fetch(wrow, s, wh, raw, (row_bytes & 3) == 0);
+    };
+    // write the fetched step into stage st: activations as they are, weights
+    // decoded to the 16-bit operand type
+    auto stash = [&](int s, int st) {
+        uint16_t* As = lds + st * (ASZ + BSZ);
+        uint16_t* Bs = As + ASZ;
 #pragma unroll
-                for (int i = 0; i < 32; ++i) v[i] = 0.f;
-            }
-            u32x4 p0, p1, p2, p3;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                p0[i] = Mfma<XDT>::cvt(v[2 * i]) | ((uint32_t)Mfma<XDT>::cvt(v[2 * i + 1]) << 16);
-                p1[i] = Mfma<XDT>::cvt(v[8 + 2 * i]) | ((uint32_t)Mfma<XDT>::cvt(v[9 + 2 * i]) << 16);
-                p2[i] = Mfma<XDT>::cvt(v[16 + 2 * i]) | ((uint32_t)Mfma<XDT>::cvt(v[17 + 2 * i]) << 16);
-                p3[i] = Mfma<XDT>::cvt(v[24 + 2 * i]) | ((uint32_t)Mfma<XDT>::cvt(v[25 + 2 * i]) << 16);
-            }
-            *(u32x4*)&Bs[fr * LDS_STRIDE + col0] = p0;
-            *(u32x4*)&Bs[fr * LDS_STRIDE + col0 + 8] = p1;
-            *(u32x4*)&Bs[fr * LDS_STRIDE + col1] = p2;
-            *(u32x4*)&Bs[fr * LDS_STRIDE + col1 + 8] = p3;
+        for (int i = 0; i < XP; ++i) {
+            const int p = tid + 256 * i, r = p >> 3, q = p & 7;
+            *(u32x4*)&As[r * LDS_STRIDE + 8 * q] = xr[i];
         }
-        __syncthreads();
+        if (wrole) {
+            uint32_t lo[8], hi[8];
+            int cl, ch;
+            const bool live = wvalid && ((C != Q8_0) || (int64_t)(2 * s + wh) * 32 < k);
+            if (live) {
+                WT::template decode<XDT>(raw, s, wh, lo, hi, cl, ch);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) lo[i] = hi[i] = 0u;
+                cl = C == Q4_K ? 16 * wh : 32 * wh;
+                ch = C == Q4_K ? 32 + 16 * wh : 32 * wh + 16;
+            }
+            *(u32x4*)&Bs[wr * LDS_STRIDE + cl] = u32x4{lo[0], lo[1], lo[2], lo[3]};
+            *(u32x4*)&Bs[wr * LDS_STRIDE + cl + 8] = u32x4{lo[4], lo[5], lo[6], lo[7]};
+            *(u32x4*)&Bs[wr * LDS_STRIDE + ch] = u32x4{hi[0], hi[1], hi[2], hi[3]};
+            *(u32x4*)&Bs[wr * LDS_STRIDE + ch + 8] = u32x4{hi[4], hi[5], hi[6], hi[7]};
+        }
+    };
+    auto frags = [&](int st, int ks, u32x4 (&af)[FM], u32x4 (&bf)[FN]) {
+        const uint16_t* As = lds + st * (ASZ + BSZ);
+        const uint16_t* Bs = As + ASZ;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+            af[i] = *(const u32x4*)&As[(wm * TM + 32 * i + (lane & 31)) * LDS_STRIDE + 16 * ks + 8 * (lane >> 5)];
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+            bf[j] = *(const u32x4*)&Bs[(wn * TN + 32 * j + (lane & 31)) * LDS_STRIDE + 16 * ks + 8 * (lane >> 5)];
+    };
+
+    // Pipeline: stage s%2 holds step s; while the MFMAs of step s run, step
+    // s+1 (fetched an iteration earlier) is decoded into the other stage and
+    // step s+2 is fetched.  One barrier per step.
+    fetch(0);
+    stash(0, 0);
+    if (steps > 1) fetch(1);
+    __syncthreads();
+    for (int s = 0; s < steps; ++s) {
+        const int st = s & 1;
+        u32x4 af[FM], bf[FN];
+        frags(st, 0, af, bf);
 #pragma unroll
         for (int ks = 0; ks < BK / 16; ++ks) {
-            short8 af[2], bf[2];
+            u32x4 naf[FM], nbf[FN];
+            if (ks + 1 < BK / 16) frags(st, ks + 1, naf, nbf);
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int r = wm * 64 + 32 * i + (lane & 31);
-                af[i] = *(const short8*)&As[r * LDS_STRIDE + 16 * ks + 8 * (lane >> 5)];
-                const int c = wn * 64 + 32 * i + (lane & 31);
-                bf[i] = *(const short8*)&Bs[c * LDS_STRIDE + 16 * ks + 8 * (lane >> 5)];
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) acc[i][j] = Op16<XDT>::mma(af[i], bf[j], acc[i][j]);
+            if (ks == 0 && s + 1 < steps) stash(s + 1, st ^ 1);
+            if (ks + 1 < BK / 16) {
+#pragma unroll
+                for (int i = 0; i < FM; ++i) af[i] = naf[i];
+#pragma unroll
+                for (int j = 0; j < FN; ++j) bf[j] = nbf[j];
             }
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j) acc[i][j] = Mfma<XDT>::mma(af[i], bf[j], acc[i][j]);
         }
+        if (s + 2 < steps) fetch(s + 2);
         __syncthreads();
     }
 
     // epilogue: lane holds column l%32 and rows 8*(v/4) + 4*(l/32) + v%4
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int64_t col = n0 + wn * 64 + 32 * j + (lane & 31);
+        for (int j = 0; j < FN; ++j) {
+            const int64_t col = n0 + wn * TN + 32 * j + (lane & 31);
+            if (col >= n) continue;
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const int64_t row = m0 + wm * 64 + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-                if (row < m && col < n) {
+                const int64_t row = m0 + wm * TM + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                if (row < m) {
                     const float o = acc[i][j][v];
                     if (y_dt == F32) store_out<F32>(y, row * n + col, o);
                     else if (y_dt == F16) store_out<F16>(y, row * n + col, o);
@@ -211,24 +317,33 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ w
         }
 }
 
-template <int C>
-static void launch_c(int x_dt, const void* w, int64_t n, int64_t k, const void* x, int64_t m,
-                     void* y, int y_dt, hipStream_t s) {
+template <int C, int XDT, int BM, int BN>
+static void launch_tile(const void* w, int64_t n, int64_t k, const void* x, int64_t m, void* y,
+                        int y_dt, hipStream_t s) {
     const dim3 grid((unsigned)((n + BN - 1) / BN), (unsigned)((m + BM - 1) / BM)), block(256);
-    if (x_dt == BF16)
-        hipLaunchKernelGGL((gemm_kernel<C, BF16>), grid, block, 0, s, (const uint8_t*)w, n, k,
-                           (const uint16_t*)x, m, y, y_dt);
-    else
-        hipLaunchKernelGGL((gemm_kernel<C, F16>), grid, block, 0, s, (const uint8_t*)w, n, k,
-                           (const uint16_t*)x, m, y, y_dt);
+    hipLaunchKernelGGL((gemm_kernel<C, XDT, BM, BN>), grid, block, 0, s, (const uint8_t*)w, n, k,
+                       (const uint16_t*)x, m, y, y_dt);
+}
+
+// Tile choice: the largest tile whose grid still gives every compute unit a
+// workgroup (256 CUs), since a bigger tile reuses each decoded weight over
+// more rows and each activation over more columns.
+template <int C, int XDT>
+static void launch_c(const void* w, int64_t n, int64_t k, const void* x, int64_t m, void* y,
+                     int y_dt, hipStream_t s) {
+    auto tiles = [&](int64_t bm, int64_t bn) { return ((n + bn - 1) / bn) * ((m + bm - 1) / bm); };
+    if (tiles(256, 128) >= 256) launch_tile<C, XDT, 256, 128>(w, n, k, x, m, y, y_dt, s);
+    else if (tiles(128, 128) >= 256) launch_tile<C, XDT, 128, 128>(w, n, k, x, m, y, y_dt, s);
+    else launch_tile<C, XDT, 128, 64>(w, n, k, x, m, y, y_dt, s);
 }
 
 hipError_t launch_gemm(int codec, int x_dt, const void* w, int64_t n, int64_t k, const void* x,
                        int64_t m, void* y, int y_dt, hipStream_t s) {
+    const bool bf = x_dt == BF16;
     switch (codec) {
-    case Q4_K: launch_c<Q4_K>(x_dt, w, n, k, x, m, y, y_dt, s); break;
-    case Q8_0: launch_c<Q8_0>(x_dt, w, n, k, x, m, y, y_dt, s); break;
-    default: launch_c<TQ1>(x_dt, w, n, k, x, m, y, y_dt, s); break;
+    case Q4_K: bf ? launch_c<Q4_K, BF16>(w, n, k, x, m, y, y_dt, s) : launch_c<Q4_K, F16>(w, n, k, x, m, y, y_dt, s); break;
+    case Q8_0: bf ? launch_c<Q8_0, BF16>(w, n, k, x, m, y, y_dt, s) : launch_c<Q8_0, F16>(w, n, k, x, m, y, y_dt, s); break;
+    default: bf ? launch_c<TQ1, BF16>(w, n, k, x, m, y, y_dt, s) : launch_c<TQ1, F16>(w, n, k, x, m, y, y_dt, s); break;
     }
     return hipGetLastError();
 }
