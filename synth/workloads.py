@@ -13,7 +13,9 @@ Weight matrices are [N, K] (N output rows, K the reduction dimension).
   C4 seed 104  128 experts; Q4_K gate [128][2048 x 7168], up [128][2048 x
                7168], down [128][7168 x 2048]; x fp16 [256, 7168] (decode uses
                token 0); ids [256, 8] without replacement; softmax router
-               weights over 8 N(0,1) logits; out fp16.
+               weights over 8 N(0,1) logits.  h and the output are fp32:
+               with these weights |h| reaches ~5e5 and the output ~1e8,
+               past the fp16 range.
   C5 seed 105  TQ1 17408x5120 then 5120x17408; x fp16 [512, K] per shape
                (batch 1 uses row 0); y fp16.
 """
