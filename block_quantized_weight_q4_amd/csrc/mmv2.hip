@@ -39,8 +39,28 @@ __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
     return (uint32_t)(uintptr_t)(const lds_u8*)p;
 }
 
-// NM weight matrices (2: gate and up), C super-blocks per chunk, W waves.
-template <int NM, int C, int W>
+// Wait until at most n of this wave's vector-memory loads are outstanding
+// (n is wave-uniform).  Loads complete in issue order, so waiting down to the
+// number issued after a chunk's loads means that chunk has landed.  n is
+// rounded down to one of a few encodable counts, which only waits longer.
+#define KQ_VMCNT(N) __builtin_amdgcn_s_waitcnt(((N) & 15) | (7 << 4) | (15 << 8) | (((N) >> 4) << 14))
+__device__ __forceinline__ void wait_loads_le(int n) {
+    if (n >= 32) KQ_VMCNT(32);
+    else if (n >= 24) KQ_VMCNT(24);
+    else if (n >= 16) KQ_VMCNT(16);
+    else if (n >= 12) KQ_VMCNT(12);
+    else if (n >= 8) KQ_VMCNT(8);
+    else if (n >= 6) KQ_VMCNT(6);
+    else if (n >= 4) KQ_VMCNT(4);
+    else if (n >= 3) KQ_VMCNT(3);
+    else if (n >= 2) KQ_VMCNT(2);
+    else if (n >= 1) KQ_VMCNT(1);
+    else KQ_VMCNT(0);
+}
+
+// NM weight matrices (2: gate and up), C super-blocks per chunk, W waves,
+// S chunk buffers in LDS (S-1 chunks in flight while one is multiplied).
+template <int NM, int C, int W, int S>
 __global__ __launch_bounds__(64 * W) void mmv2_q4k_f16_kernel(SkinnyArgs a) {
     static_assert(C % 4 == 0, "a chunk of 16 rows x C super-blocks is whole 1 KB loads");
     constexpr int WPIECES = NM * 16 * 9 * C;   // 16-byte pieces of weights per chunk
@@ -69,10 +89,10 @@ __global__ __launch_bounds__(64 * W) void mmv2_q4k_f16_kernel(SkinnyArgs a) {
         nrows = a.m - row0 < 16 ? a.m - row0 : 16;
     }
 
-    // LDS: two buffers of [weights | activations]
+    // LDS: S buffers of [weights | activations]
     const int xstride = a.xstride;            // bytes between staged activation rows
     const int wbytes = WPIECES * 16;
-    const int bufbytes = a.red_off / 2;       // bytes of one buffer
+    const int bufbytes = a.red_off / S;       // bytes of one buffer
     float* red = (float*)(smem + a.red_off);
 
     // Per-lane byte offsets of this wave's weight pieces inside a chunk:
@@ -103,6 +123,15 @@ __global__ __launch_bounds__(64 * W) void mmv2_q4k_f16_kernel(SkinnyArgs a) {
         }
         return (const uint8_t*)a.x + xr * a.x_row * 2;
     };
+
+    // load instructions this wave issues per chunk (the same for every chunk)
+    int wave_loads = 0;
+#pragma unroll
+    for (int j = 0; j < WL_PER_WAVE; ++j) wave_loads += (wave + W * j < WLOADS) ? 1 : 0;
+    {
+        const int xl_total = (int)nrows * (XPIECES_ROW / 64);
+        wave_loads += xl_total > wave ? (xl_total - wave + W - 1) / W : 0;
+    }
 
     auto issue = [&](int chunk, int dst_off) {
         uint8_t* dst = smem + dst_off;
@@ -144,16 +173,17 @@ __global__ __launch_bounds__(64 * W) void mmv2_q4k_f16_kernel(SkinnyArgs a) {
     // the tile (its MFMA output row is never stored)
     const int xlane = wbytes + (n_l < nrows ? n_l : 0) * xstride + 128 * g;
 
-    // Order per chunk: wait for this wave's loads of chunk c, barrier (all
-    // of chunk c has landed and every wave is done with chunk c-1), then
-    // request chunk c+1 into the other buffer and multiply chunk c while it
-    // streams in.
-    issue(0, 0);
+    // Order per chunk: wait for this wave's loads of chunk c (those of the
+    // up to S-2 later chunks may stay in flight), barrier (all of chunk c has
+    // landed and every wave is done with chunk c-1), then request chunk
+    // c+S-1 into the buffer chunk c-1 used and multiply chunk c.
+    for (int c = 0; c < S - 1 && c < nchunks; ++c) issue(c, c * bufbytes);
     for (int c = 0; c < nchunks; ++c) {
-        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+        const int later = nchunks - 1 - c < S - 2 ? nchunks - 1 - c : S - 2;
+        wait_loads_le(wave_loads * later);
         __syncthreads();
-        if (c + 1 < nchunks) issue(c + 1, ((c + 1) & 1) * bufbytes);
-        const uint8_t* B = smem + (c & 1) * bufbytes;
+        if (c + S - 1 < nchunks) issue(c + S - 1, ((c + S - 1) % S) * bufbytes);
+        const uint8_t* B = smem + (c % S) * bufbytes;
         const int nsc = nsb - c * C < C ? nsb - c * C : C;
         for (int sb = wave; sb < nsc; sb += W) {
             u32x4 xa[8];
@@ -212,24 +242,39 @@ __global__ __launch_bounds__(64 * W) void mmv2_q4k_f16_kernel(SkinnyArgs a) {
     }
 }
 
-template <int NM, int C, int W>
+template <int NM, int C, int W, int S>
+static constexpr size_t lds_cfg2(int64_t rows_max) {
+    const int64_t wbytes = (int64_t)NM * 16 * 9 * C * 16;
+    const int64_t bufbytes = (wbytes + rows_max * (512 * C + 16) + 15) / 16 * 16;
+    return (size_t)(S * bufbytes + (int64_t)(W - 1) * NM * 4 * 64 * 4);
+}
+
+template <int NM, int C, int W, int S>
 static void launch_cfg2(SkinnyArgs a, int64_t rows_max, int64_t tiles_y, hipStream_t s) {
     const int64_t wbytes = (int64_t)NM * 16 * 9 * C * 16;
     a.xstride = 512 * C + 16;                      // padded staged activation row
     const int64_t bufbytes = (wbytes + rows_max * a.xstride + 15) / 16 * 16;
-    a.red_off = (int)(2 * bufbytes);
-    const size_t lds = (size_t)a.red_off + (size_t)(W - 1) * NM * 4 * 64 * 4;
+    a.red_off = (int)(S * bufbytes);
+    const size_t lds = lds_cfg2<NM, C, W, S>(rows_max);
     const dim3 grid((unsigned)((a.n + 15) / 16), (unsigned)tiles_y);
-    hipLaunchKernelGGL((mmv2_q4k_f16_kernel<NM, C, W>), grid, dim3(64 * W), lds, s, a);
+    hipLaunchKernelGGL((mmv2_q4k_f16_kernel<NM, C, W, S>), grid, dim3(64 * W), lds, s, a);
 }
+
+// LDS per workgroup is at most 160 KB; the staged activation rows grow with
+// the row count, so wide chunks are used only while they fit.  Measured on
+// the decode shapes: two buffers (one chunk in flight) beat deeper rings.
+constexpr size_t kLdsMax = 160 * 1024;
+static_assert(lds_cfg2<2, 4, 4, 2>(16) <= kLdsMax && lds_cfg2<1, 4, 4, 2>(16) <= kLdsMax,
+              "the fallback shapes hold 16 staged activation rows");
 
 hipError_t launch_mmv2_q4k(bool glu, const SkinnyArgs& a, int64_t grid_tiles, hipStream_t s) {
     const int64_t rows_max = a.ws ? (a.rows_cap < 16 ? a.rows_cap : 16) : a.m;
     const int64_t tiles = a.ws ? grid_tiles : (a.m + 15) / 16;
     const int64_t nsb = a.k / 256;
-    if (glu) launch_cfg2<2, 4, 4>(a, rows_max, tiles, s);
-    else if (nsb > 16) launch_cfg2<1, 8, 8>(a, rows_max, tiles, s);
-    else launch_cfg2<1, 4, 4>(a, rows_max, tiles, s);
+    if (glu) launch_cfg2<2, 4, 4, 2>(a, rows_max, tiles, s);
+    else if (nsb > 16 && lds_cfg2<1, 8, 8, 2>(rows_max) <= kLdsMax)
+        launch_cfg2<1, 8, 8, 2>(a, rows_max, tiles, s);
+    else launch_cfg2<1, 4, 4, 2>(a, rows_max, tiles, s);
     return hipGetLastError();
 }
 

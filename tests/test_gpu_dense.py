@@ -130,6 +130,21 @@ def test_qmv_small(kq, kind, x_dt, m):
 
 
 @pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("m", [14, 15, 16])
+def test_qmv_long_rows_many_activations(kq, kind, m):
+    # long rows (56 super-blocks of Q4_K) with up to 16 activation rows: the
+    # decode kernels pick narrower chunks when the staged rows would not fit
+    n, k = 37, 14336
+    rng = _rng(2500 + m)
+    w = synth.weight_blocks(kind, rng, n, k)
+    x = synth.activations(rng, (m, k), "f16")
+    _say("qmv long", kind, m)
+    got = _run(kq, "kq_qmv", kind, w, n, k, x, "f16", m, "f16")
+    ref, s = oracle.qmm(kind, w, n, k, x, "f16", m)
+    check_tol(got, ref, s, TAU["f16"], f"qmv long {kind} m={m}")
+
+
+@pytest.mark.parametrize("kind", KINDS)
 @pytest.mark.parametrize("x_dt", ["f16", "bf16"])
 @pytest.mark.parametrize("m,n,nblk", [(17, 64, 2), (130, 200, 3), (257, 131, 4)])
 def test_qmm_small(kq, kind, x_dt, m, n, nblk):
