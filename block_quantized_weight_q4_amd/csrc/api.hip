@@ -92,7 +92,8 @@ MoeLayout moe_layout(int64_t n_experts, int64_t n_tokens, int64_t top_k, int64_t
     L.offsets_off = L.counts_off + n_experts;
     L.perm_off = L.offsets_off + n_experts + 1;
     L.tiles_off = L.perm_off + L.rows;
-    L.route_words = L.tiles_off + 3 * L.max_tiles;
+    L.xexp_off = L.tiles_off + 3 * L.max_tiles;
+    L.route_words = L.xexp_off + L.rows;
     L.slot_off_bytes = (L.route_words * 4 + 255) / 256 * 256;
     L.slot_bytes = L.rows * n_out * 4;
     L.total_bytes = L.slot_off_bytes + L.slot_bytes;
@@ -280,6 +281,7 @@ kq_status kq_qmm_id(kq_type t, const void* w, int64_t n_experts, int64_t n, int6
     a.ws = ws;
     a.tiles_off = L.tiles_off;
     a.perm_off = L.perm_off;
+    a.xexp_off = L.xexp_off;
     a.rows_cap = L.rows;
     if (scores) {
         float* slots = (float*)((char*)workspace + L.slot_off_bytes);
@@ -329,6 +331,7 @@ kq_status kq_moe_glu(kq_type t, const void* gate_w, const void* up_w, int64_t n_
     a.ws = ws;
     a.tiles_off = L.tiles_off;
     a.perm_off = L.perm_off;
+    a.xexp_off = L.xexp_off;
     a.rows_cap = L.rows;
     a.y = h;
     a.y_dt = h_dt;

@@ -15,6 +15,7 @@ constexpr int kMoeTileRows = 32;
 struct MoeLayout {
     int64_t n_experts, rows, max_tiles;
     int64_t counts_off, offsets_off, perm_off, tiles_off;  // word offsets
+    int64_t xexp_off;        // word offset of the per-activation-row scale exponents
     int64_t route_words;     // words used by the schedule
     int64_t slot_off_bytes;  // start of the fp32 slot buffer
     int64_t slot_bytes;      // rows * n_out * 4
@@ -35,23 +36,26 @@ struct SkinnyArgs {
     int shared_x;          // routed: x row = r / top_k (else r)
     const int32_t* ws;     // routed: workspace (schedule); null for dense
     int64_t tiles_off, perm_off;
+    int64_t xexp_off;      // routed, fp32 activations: word offset of row exponents
     int64_t m;             // dense: activation rows
     void* y;               // output
     int y_dt;              // output dtype
     int64_t y_row;         // elements between output rows
     int64_t rows_cap;      // routed: most rows any schedule tile can hold
-    // set by the launcher of the matrix-core kernels
+    // set by the launchers of the matrix-core kernels
     int xch;               // super-blocks of activations staged per chunk
-    int xstride;           // halves between staged activation rows
-    int red_off;           // byte offset of the cross-wave reduction buffer
+    int xstride;           // elements (or bytes) between staged activation rows
+    int red_off;           // byte offset of a second LDS region
 };
 
 hipError_t launch_dequant(int codec, const void* w, int64_t rows, int64_t k, void* out, int out_dt,
                           hipStream_t s);
 hipError_t launch_skinny(int codec, int x_dt, bool glu, const SkinnyArgs& a, int64_t grid_tiles,
                          hipStream_t s);
-hipError_t launch_mmv_q4k(bool glu, const SkinnyArgs& a, int64_t grid_tiles, hipStream_t s);
 hipError_t launch_mmv2_q4k(bool glu, const SkinnyArgs& a, int64_t grid_tiles, hipStream_t s);
+hipError_t launch_moe_mm(bool glu, int x_dt, const SkinnyArgs& a, int64_t grid_tiles,
+                         hipStream_t s);
+hipError_t launch_row_exp(const float* x, int64_t rows, int64_t k, int32_t* e, hipStream_t s);
 hipError_t launch_gemm(int codec, int x_dt, const void* w, int64_t n, int64_t k, const void* x,
                        int64_t m, void* y, int y_dt, hipStream_t s);
 hipError_t launch_route(const uint32_t* ids, int64_t rows, int64_t n_experts, const MoeLayout& L,

@@ -13,9 +13,9 @@
 // global->LDS 16-byte loads, 64 consecutive pieces per instruction; the
 // activation rows of the tile are staged the same way.  Chunks are double
 // buffered: the loads of chunk j+1 are in flight while the waves multiply
-// chunk j.  The multiply is the exact-operand scheme of the routed kernel
-// (mmv.hip): sc*q as fp16 integers, the 6-bit min as a second MFMA chain,
-// d and dmin applied once per super-block in fp32.
+// chunk j.  The multiply is the exact-operand scheme of q4k_mfma.h: sc*q as
+// fp16 integers, the 6-bit min as a second MFMA chain, d and dmin applied
+// once per super-block in fp32.
 #include "kq_device.h"
 #include "kq_internal.h"
 #include "q4k_mfma.h"

@@ -239,12 +239,21 @@ static void launch_x(int x_dt, const SkinnyArgs& a, int mb, dim3 grid, hipStream
 
 hipError_t launch_skinny(int codec, int x_dt, bool glu, const SkinnyArgs& a, int64_t grid_tiles,
                          hipStream_t s) {
-    if (codec == Q4_K && x_dt == F16) {
-        // decode shapes (at most 16 activation rows per tile): weights and
-        // activations streamed through LDS; wider routed tiles: mmv.hip
-        if (a.ws ? a.rows_cap <= 16 : a.m <= 16) return launch_mmv2_q4k(glu, a, grid_tiles, s);
-        return launch_mmv_q4k(glu, a, grid_tiles, s);
+    // Q4_K on the matrix cores: routed fp32 activations and routed tiles of
+    // more than 16 rows take the grouped kernel (moe_mm.hip); decode shapes
+    // with fp16 activations stream weights and activations through LDS
+    // (mmv2.hip)
+    if (codec == Q4_K && a.ws && (x_dt == F32 || (x_dt == F16 && a.rows_cap > 16))) {
+        if (x_dt == F32) {
+            const int64_t x_rows = a.shared_x ? a.rows_cap / a.top_k : a.rows_cap;
+            const hipError_t e = launch_row_exp((const float*)a.x, x_rows, a.k,
+                                                const_cast<int32_t*>(a.ws) + a.xexp_off, s);
+            if (e != hipSuccess) return e;
+        }
+        return launch_moe_mm(glu, x_dt, a, grid_tiles, s);
     }
+    if (codec == Q4_K && x_dt == F16 && (a.ws ? a.rows_cap <= 16 : a.m <= 16))
+        return launch_mmv2_q4k(glu, a, grid_tiles, s);
     int mb;
     int64_t tiles;
     if (a.ws) {

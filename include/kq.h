@@ -139,6 +139,8 @@ size_t kq_moe_workspace_bytes(int64_t n_experts, int64_t n_tokens, int64_t top_k
  *   [3+2E+R .. +3*max_tiles)  tiles (expert, row_start, num_rows): each
  *                             expert's segment cut into KQ_MOE_TILE_ROWS-row
  *                             tiles, only the last of which may be partial
+ *   [.. +R)                   scratch: per-activation-row scale exponents
+ *                             (written by products with fp32 activations)
  * with R = n_tokens * top_k and max_tiles = min(R, ceil(R / KQ_MOE_TILE_ROWS)
  * + n_experts).  The fp32 slot buffer of kq_qmm_id follows at the next
  * 256-byte boundary.

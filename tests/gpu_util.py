@@ -9,6 +9,9 @@ TORCH_DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 TAU = {"f32": 1e-5, "f16": 2e-3, "bf16": 2e-3}
 # unit roundoff of the stored output format
 UNIT = {"f32": 2.0**-24, "f16": 2.0**-11, "bf16": 2.0**-8}
+# half the spacing of the format's subnormals: the absolute rounding error
+# of storing a value below the normal range
+ETA = {"f32": 2.0**-150, "f16": 2.0**-25, "bf16": 2.0**-134}
 
 
 def device():
@@ -56,7 +59,7 @@ def check_tol(got: np.ndarray, ref: np.ndarray, s: np.ndarray, tau: float, what:
     assert not np.isnan(got).any(), f"{what}: NaN in GPU output"
     bound = tau * s
     if out_dt is not None:
-        bound = bound + UNIT[out_dt] * np.abs(ref)
+        bound = bound + UNIT[out_dt] * np.abs(ref) + ETA[out_dt]
     err = np.abs(got - ref)
     bad = err > bound
     if bad.any():

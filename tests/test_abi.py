@@ -70,7 +70,7 @@ def test_workspace_layout(kq):
     E, T, top_k, n = 128, 256, 8, 7168
     R = T * top_k
     max_tiles = min(R, (R + 31) // 32 + E)
-    route_words = 2 + E + (E + 1) + R + 3 * max_tiles
+    route_words = 2 + E + (E + 1) + R + 3 * max_tiles + R
     slot_off = (route_words * 4 + 255) // 256 * 256
     assert kq.kq_moe_workspace_bytes(E, T, top_k, 0) == slot_off
     assert kq.kq_moe_workspace_bytes(E, T, top_k, n) == slot_off + R * n * 4

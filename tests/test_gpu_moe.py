@@ -4,8 +4,11 @@ kq_moe_glu) against the CPU oracle, through the C ABI.
 The routing schedule is integer work and is compared exactly.  Products use
 the dense rule |gpu - ref| <= tau * S.  The GLU output h = silu(g) * u is
 checked against the bound that the gate and up tolerances imply:
-|h - h_ref| <= tau * (max|silu'| * |u| * S_g + |silu(g)| * S_u) + u_h * |h_ref|
-with max|silu'| < 1.1 and u_h the unit roundoff of h's storage type.
+|h - h_ref| <= E * (1 + u_h) + u_h * |h_ref| + eta_h,
+E = tau * (max|silu'| * |u| * S_g + |silu(g)| * S_u)
+with max|silu'| < 1.1, u_h the unit roundoff of h's storage type and eta_h
+half its subnormal spacing (the stored value is the computed one, within E
+of h_ref, rounded once).
 """
 
 from __future__ import annotations
@@ -17,7 +20,7 @@ import torch
 import oracle
 import synth
 from synth import workloads
-from tests.gpu_util import TAU, UNIT, check_tol, device, empty, to_dev, to_f64
+from tests.gpu_util import ETA, TAU, UNIT, check_tol, device, empty, to_dev, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -91,6 +94,29 @@ def test_qmm_id_small(kq, kind, layout, mixed, E, T, top_k):
     check_tol(to_f64(y), ref, s, TAU["f16"], f"qmm_id {kind}")
 
 
+@pytest.mark.parametrize("kind", ["q4_k", "q8_0", "tq1_g128"])
+@pytest.mark.parametrize("layout", [0, 1])
+@pytest.mark.parametrize("mixed", [False, True])
+@pytest.mark.parametrize("E,T,top_k", [(8, 1, 8), (8, 5, 3), (4, 70, 4)])
+def test_qmm_id_f32_activations(kq, kind, layout, mixed, E, T, top_k):
+    # fp32 activations whose rows span 1e-3 .. 1e5 in magnitude (past the
+    # fp16 range), held to the fp32 tolerance
+    n, k = 80, {"q4_k": 768, "q8_0": 160, "tq1_g128": 384}[kind]
+    rng, w, stride, ids, scores = _moe_case(kind, E, n, k, T, top_k, 90 + T)
+    x_rows = T if layout == 0 else T * top_k
+    x = synth.activations(rng, (x_rows, k), "f32")
+    x *= (10.0 ** rng.uniform(-3, 5, size=(x_rows, 1))).astype(np.float32)
+    _say("qmm_id f32", kind, layout, mixed, E, T, top_k)
+    y = empty((T if mixed else T * top_k, n), "f32")
+    ws = _ws(kq, E, T, top_k, n if mixed else 0)
+    kq.kq_qmm_id(kind, to_dev(w), E, n, k, stride, to_dev(x), layout, to_dev(ids), T,
+                 top_k, to_dev(scores) if mixed else None, y, ws)
+    torch.cuda.synchronize()
+    ref, s = oracle.qmm_id(kind, w, E, n, k, stride, x, "f32", layout == 1, ids, T, top_k,
+                           scores if mixed else None)
+    check_tol(to_f64(y), ref, s, TAU["f32"], f"qmm_id f32 {kind}")
+
+
 def test_qmm_id_invalid_ids_poison(kq):
     E, n, k, T, top_k = 6, 64, 256, 4, 2
     rng, w, stride, ids, scores = _moe_case("q4_k", E, n, k, T, top_k, 77)
@@ -124,7 +150,10 @@ def _check_glu(h, ref, tau, h_dt, what):
         ref = {"h": ref["h"][~over]}
     with np.errstate(over="ignore"):
         sig = 1.0 / (1.0 + np.exp(-g))
-    bound = tau * (1.1 * np.abs(u) * sg + np.abs(g * sig) * su) + UNIT[h_dt] * np.abs(ref["h"])
+    # the computed h may be off by the product tolerance, and storing it
+    # rounds once more: relative UNIT of the stored value, |h_ref| + that error
+    comp = tau * (1.1 * np.abs(u) * sg + np.abs(g * sig) * su)
+    bound = comp * (1.0 + UNIT[h_dt]) + UNIT[h_dt] * np.abs(ref["h"]) + ETA[h_dt]
     err = np.abs(h - ref["h"])
     bad = err > bound
     assert not bad.any(), f"{what}: {bad.sum()} outside; worst {np.max(err - bound):.3e}"
@@ -132,22 +161,23 @@ def _check_glu(h, ref, tau, h_dt, what):
 
 @pytest.mark.parametrize("kind", ["q4_k", "q8_0", "tq1_g128"])
 @pytest.mark.parametrize("h_dt", ["f16", "f32", "bf16"])
-def test_moe_glu_small(kq, kind, h_dt):
+@pytest.mark.parametrize("x_dt", ["f16", "f32"])
+def test_moe_glu_small(kq, kind, h_dt, x_dt):
     E, n, k, T, top_k = 6, 80, {"q4_k": 512, "q8_0": 96, "tq1_g128": 256}[kind], 9, 3
     rng = synth.rng_for(90)
     gate = synth.weight_blocks(kind, rng, E * n, k)
     up = synth.weight_blocks(kind, rng, E * n, k)
     stride = n * synth.row_bytes(kind, k)
     ids = _ids(rng, T, E, top_k)
-    x = synth.activations(rng, (T, k), "f16")
-    _say("moe_glu", kind, h_dt)
+    x = synth.activations(rng, (T, k), x_dt)
+    _say("moe_glu", kind, h_dt, x_dt)
     h = empty((T, top_k, n), h_dt)
     ws = _ws(kq, E, T, top_k)
-    kq.kq_moe_glu(kind, to_dev(gate), to_dev(up), E, n, k, stride, to_dev(x, "f16"), to_dev(ids),
+    kq.kq_moe_glu(kind, to_dev(gate), to_dev(up), E, n, k, stride, to_dev(x, x_dt), to_dev(ids),
                   T, top_k, h, ws)
     torch.cuda.synchronize()
-    ref = oracle.moe_glu(kind, gate, up, E, n, k, stride, x, "f16", ids, T, top_k)
-    _check_glu(to_f64(h), ref, TAU["f16"], h_dt, f"moe_glu {kind} {h_dt}")
+    ref = oracle.moe_glu(kind, gate, up, E, n, k, stride, x, x_dt, ids, T, top_k)
+    _check_glu(to_f64(h), ref, TAU[x_dt], h_dt, f"moe_glu {kind} {h_dt} x={x_dt}")
 
 
 @pytest.fixture(scope="module")
