@@ -266,7 +266,10 @@ kq_status kq_qmm_id(kq_type t, const void* w, int64_t n_experts, int64_t n, int6
     hipStream_t s = (hipStream_t)stream;
     const kq::MoeLayout L = kq::moe_layout(n_experts, n_tokens, top_k, scores ? n : 0);
     int32_t* ws = (int32_t*)workspace;
-    hipError_t e = kq::launch_route(ids, L.rows, n_experts, L, ws, s);
+    // the unmixed form's rows with an invalid id are poisoned by the route;
+    // the mixed form's tokens by the mix
+    hipError_t e = scores ? kq::launch_route(ids, L.rows, n_experts, L, ws, s)
+                          : kq::launch_route(ids, L.rows, n_experts, L, ws, s, y, n, y_dt);
     if (e != hipSuccess) return launched(e);
     kq::SkinnyArgs a{};
     a.w = (const uint8_t*)w;
@@ -278,6 +281,7 @@ kq_status kq_qmm_id(kq_type t, const void* w, int64_t n_experts, int64_t n, int6
     a.x_row = k;
     a.top_k = top_k;
     a.shared_x = x_layout == KQ_LAYOUT_SHARED;
+    a.one_x_row = a.shared_x && n_tokens == 1;
     a.ws = ws;
     a.tiles_off = L.tiles_off;
     a.perm_off = L.perm_off;
@@ -295,9 +299,7 @@ kq_status kq_qmm_id(kq_type t, const void* w, int64_t n_experts, int64_t n, int6
     a.y = y;
     a.y_dt = y_dt;
     a.y_row = n;
-    e = kq::launch_skinny(t, x_dt, false, a, L.max_tiles, s);
-    if (e != hipSuccess) return launched(e);
-    return launched(kq::launch_poison(ids, L.rows, n_experts, y, n, y_dt, s));
+    return launched(kq::launch_skinny(t, x_dt, false, a, L.max_tiles, s));
 }
 
 kq_status kq_moe_glu(kq_type t, const void* gate_w, const void* up_w, int64_t n_experts,
@@ -315,7 +317,7 @@ kq_status kq_moe_glu(kq_type t, const void* gate_w, const void* up_w, int64_t n_
     hipStream_t s = (hipStream_t)stream;
     const kq::MoeLayout L = kq::moe_layout(n_experts, n_tokens, top_k, 0);
     int32_t* ws = (int32_t*)workspace;
-    hipError_t e = kq::launch_route(ids, L.rows, n_experts, L, ws, s);
+    hipError_t e = kq::launch_route(ids, L.rows, n_experts, L, ws, s, h, n, h_dt);
     if (e != hipSuccess) return launched(e);
     kq::SkinnyArgs a{};
     a.w = (const uint8_t*)gate_w;
@@ -328,6 +330,7 @@ kq_status kq_moe_glu(kq_type t, const void* gate_w, const void* up_w, int64_t n_
     a.x_row = k;
     a.top_k = top_k;
     a.shared_x = 1;
+    a.one_x_row = n_tokens == 1;
     a.ws = ws;
     a.tiles_off = L.tiles_off;
     a.perm_off = L.perm_off;
@@ -336,9 +339,7 @@ kq_status kq_moe_glu(kq_type t, const void* gate_w, const void* up_w, int64_t n_
     a.y = h;
     a.y_dt = h_dt;
     a.y_row = n;
-    e = kq::launch_skinny(t, x_dt, true, a, L.max_tiles, s);
-    if (e != hipSuccess) return launched(e);
-    return launched(kq::launch_poison(ids, L.rows, n_experts, h, n, h_dt, s));
+    return launched(kq::launch_skinny(t, x_dt, true, a, L.max_tiles, s));
 }
 
 }  // extern "C"

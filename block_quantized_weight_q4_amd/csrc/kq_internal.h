@@ -34,6 +34,7 @@ struct SkinnyArgs {
     int64_t x_row;         // elements between consecutive activation rows
     int64_t top_k;         // routed: slots per token
     int shared_x;          // routed: x row = r / top_k (else r)
+    int one_x_row;         // routed: all rows read one activation row (one token, shared x)
     const int32_t* ws;     // routed: workspace (schedule); null for dense
     int64_t tiles_off, perm_off;
     int64_t xexp_off;      // routed, fp32 activations: word offset of row exponents
@@ -58,12 +59,14 @@ hipError_t launch_moe_mm(bool glu, int x_dt, const SkinnyArgs& a, int64_t grid_t
 hipError_t launch_row_exp(const float* x, int64_t rows, int64_t k, int32_t* e, hipStream_t s);
 hipError_t launch_gemm(int codec, int x_dt, const void* w, int64_t n, int64_t k, const void* x,
                        int64_t m, void* y, int y_dt, hipStream_t s);
+// Builds the schedule; with poison_y, also writes NaN to the rows of
+// poison_y ([rows, poison_n] of poison_dt) whose id is invalid.
 hipError_t launch_route(const uint32_t* ids, int64_t rows, int64_t n_experts, const MoeLayout& L,
-                        int32_t* ws, hipStream_t s);
+                        int32_t* ws, hipStream_t s, void* poison_y = nullptr,
+                        int64_t poison_n = 0, int poison_dt = 0);
 hipError_t launch_mix(const uint32_t* ids, const float* scores, int64_t n_tokens, int64_t top_k,
                       int64_t n_experts, const float* slots, int64_t n, void* y, int y_dt,
                       hipStream_t s);
-hipError_t launch_poison(const uint32_t* ids, int64_t rows, int64_t n_experts, void* y, int64_t n,
-                         int y_dt, hipStream_t s);
+
 
 }  // namespace kq

@@ -58,11 +58,14 @@ __device__ __forceinline__ void wait_loads_le(int n) {
     else KQ_VMCNT(0);
 }
 
-// NM weight matrices (2: gate and up), C super-blocks per chunk, W waves,
-// S chunk buffers in LDS (S-1 chunks in flight while one is multiplied).
-template <int NM, int C, int W, int S>
+// NM sets of 16 weight rows: for the GLU the gate (set 0) and up (set 1)
+// rows of one 16-row block, otherwise NM consecutive 16-row blocks.  C
+// super-blocks per chunk, W waves, S chunk buffers in LDS (S-1 chunks in
+// flight while one is multiplied).
+template <int NM, bool GLU, int C, int W, int S>
 __global__ __launch_bounds__(64 * W) void mmv2_q4k_f16_kernel(SkinnyArgs a) {
-    static_assert(C % 4 == 0, "a chunk of 16 rows x C super-blocks is whole 1 KB loads");
+    static_assert(!GLU || NM == 2, "the GLU takes one gate and one up set");
+    static_assert((NM * 16 * 9 * C) % 64 == 0, "a chunk of weights is whole 1 KB loads");
     constexpr int WPIECES = NM * 16 * 9 * C;   // 16-byte pieces of weights per chunk
     constexpr int WLOADS = WPIECES / 64;       // load instructions per chunk
     constexpr int WL_PER_WAVE = (WLOADS + W - 1) / W;
@@ -70,7 +73,7 @@ __global__ __launch_bounds__(64 * W) void mmv2_q4k_f16_kernel(SkinnyArgs a) {
     extern __shared__ __align__(16) uint8_t smem[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n_l = lane & 15, g = lane >> 4;
-    const int64_t n0 = (int64_t)blockIdx.x * 16;
+    const int64_t n0 = (int64_t)blockIdx.x * (GLU ? 16 : 16 * NM);
     const int nsb = (int)(a.k / 256);
     const int nchunks = (nsb + C - 1) / C;
 
@@ -99,7 +102,7 @@ __global__ __launch_bounds__(64 * W) void mmv2_q4k_f16_kernel(SkinnyArgs a) {
     // piece p = 64*i + lane -> matrix m, row r, piece q of the row's chunk.
     const uint8_t* wbase[NM];
 #pragma unroll
-    for (int m = 0; m < NM; ++m) wbase[m] = (m ? a.w2 : a.w) + expert * a.expert_stride;
+    for (int m = 0; m < NM; ++m) wbase[m] = (GLU && m ? a.w2 : a.w) + expert * a.expert_stride;
     uint32_t woff[WL_PER_WAVE], wq16[WL_PER_WAVE];
     int wmat[WL_PER_WAVE];
 #pragma unroll
@@ -108,7 +111,7 @@ __global__ __launch_bounds__(64 * W) void mmv2_q4k_f16_kernel(SkinnyArgs a) {
         const int p = 64 * i + lane;
         const int m = p / (16 * 9 * C), rem = p - m * 16 * 9 * C;
         const int r = rem / (9 * C), q = rem - r * 9 * C;
-        int64_t n = n0 + r;
+        int64_t n = n0 + (GLU ? 0 : 16 * m) + r;
         if (n >= a.n) n = a.n - 1;
         wmat[j] = m < NM ? m : 0;
         wq16[j] = 16u * (uint32_t)q;
@@ -124,12 +127,16 @@ __global__ __launch_bounds__(64 * W) void mmv2_q4k_f16_kernel(SkinnyArgs a) {
         return (const uint8_t*)a.x + xr * a.x_row * 2;
     };
 
+    // activation rows staged per chunk: one when every routed row belongs to
+    // the same token (a single-token routing over shared activations)
+    const int xrows = a.one_x_row ? 1 : (int)nrows;
+
     // load instructions this wave issues per chunk (the same for every chunk)
     int wave_loads = 0;
 #pragma unroll
     for (int j = 0; j < WL_PER_WAVE; ++j) wave_loads += (wave + W * j < WLOADS) ? 1 : 0;
     {
-        const int xl_total = (int)nrows * (XPIECES_ROW / 64);
+        const int xl_total = xrows * (XPIECES_ROW / 64);
         wave_loads += xl_total > wave ? (xl_total - wave + W - 1) / W : 0;
     }
 
@@ -153,7 +160,7 @@ __global__ __launch_bounds__(64 * W) void mmv2_q4k_f16_kernel(SkinnyArgs a) {
         // activations: row r, pieces [0, 32*nsc); instruction k of a row
         // covers pieces [64k, 64k+64)
         const int xl_row = XPIECES_ROW / 64;
-        const int xl_total = (int)nrows * xl_row;
+        const int xl_total = xrows * xl_row;
         for (int i = wave; i < xl_total; i += W) {
             const int r = i / xl_row, k = i - r * xl_row;
             int piece = 64 * k + lane;
@@ -171,7 +178,7 @@ __global__ __launch_bounds__(64 * W) void mmv2_q4k_f16_kernel(SkinnyArgs a) {
     asm volatile("" : "+v"(magic_v));
     // A-operand LDS offset of this lane: staged row b, or row 0 for a lane past
     // the tile (its MFMA output row is never stored)
-    const int xlane = wbytes + (n_l < nrows ? n_l : 0) * xstride + 128 * g;
+    const int xlane = wbytes + (n_l < xrows ? n_l : 0) * xstride + 128 * g;
 
     // Order per chunk: wait for this wave's loads of chunk c (those of the
     // up to S-2 later chunks may stay in flight), barrier (all of chunk c has
@@ -229,16 +236,23 @@ __global__ __launch_bounds__(64 * W) void mmv2_q4k_f16_kernel(SkinnyArgs a) {
                 for (int v = 0; v < 4; ++v) acc[m][v] += red[(((w - 1) * NM + m) * 4 + v) * 64 + lane];
     }
 
-    // ---- store: lane holds activation rows b = 4g+v of weight row n_l
-    const int64_t n = n0 + n_l;
-    if (n >= a.n) return;
+    // ---- store: lane holds activation rows b = 4g+v of weight row n_l of
+    // each set
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
         const int64_t idx = 4 * g + v;
         if (idx >= nrows) continue;
         const int64_t orow = perm ? (int64_t)perm[row0 + idx] : row0 + idx;
-        const float val = NM == 2 ? silu_fast(acc[0][v]) * acc[NM - 1][v] : acc[0][v];
-        store_val(a.y, orow * a.y_row + n, a.y_dt, val);
+        if (GLU) {
+            const int64_t n = n0 + n_l;
+            if (n < a.n) store_val(a.y, orow * a.y_row + n, a.y_dt, silu_fast(acc[0][v]) * acc[1][v]);
+        } else {
+#pragma unroll
+            for (int m = 0; m < NM; ++m) {
+                const int64_t n = n0 + 16 * m + n_l;
+                if (n < a.n) store_val(a.y, orow * a.y_row + n, a.y_dt, acc[m][v]);
+            }
+        }
     }
 }
 
@@ -249,32 +263,33 @@ static constexpr size_t lds_cfg2(int64_t rows_max) {
     return (size_t)(S * bufbytes + (int64_t)(W - 1) * NM * 4 * 64 * 4);
 }
 
-template <int NM, int C, int W, int S>
+template <int NM, bool GLU, int C, int W, int S>
 static void launch_cfg2(SkinnyArgs a, int64_t rows_max, int64_t tiles_y, hipStream_t s) {
     const int64_t wbytes = (int64_t)NM * 16 * 9 * C * 16;
     a.xstride = 512 * C + 16;                      // padded staged activation row
     const int64_t bufbytes = (wbytes + rows_max * a.xstride + 15) / 16 * 16;
     a.red_off = (int)(S * bufbytes);
     const size_t lds = lds_cfg2<NM, C, W, S>(rows_max);
-    const dim3 grid((unsigned)((a.n + 15) / 16), (unsigned)tiles_y);
-    hipLaunchKernelGGL((mmv2_q4k_f16_kernel<NM, C, W, S>), grid, dim3(64 * W), lds, s, a);
+    const int64_t rows_wg = GLU ? 16 : 16 * NM;
+    const dim3 grid((unsigned)((a.n + rows_wg - 1) / rows_wg), (unsigned)tiles_y);
+    hipLaunchKernelGGL((mmv2_q4k_f16_kernel<NM, GLU, C, W, S>), grid, dim3(64 * W), lds, s, a);
 }
 
 // LDS per workgroup is at most 160 KB; the staged activation rows grow with
 // the row count, so wide chunks are used only while they fit.  Measured on
 // the decode shapes: two buffers (one chunk in flight) beat deeper rings.
 constexpr size_t kLdsMax = 160 * 1024;
-static_assert(lds_cfg2<2, 4, 4, 2>(16) <= kLdsMax && lds_cfg2<1, 4, 4, 2>(16) <= kLdsMax,
+static_assert(lds_cfg2<2, 2, 2, 2>(16) <= kLdsMax && lds_cfg2<1, 4, 4, 2>(16) <= kLdsMax,
               "the fallback shapes hold 16 staged activation rows");
 
 hipError_t launch_mmv2_q4k(bool glu, const SkinnyArgs& a, int64_t grid_tiles, hipStream_t s) {
-    const int64_t rows_max = a.ws ? (a.rows_cap < 16 ? a.rows_cap : 16) : a.m;
+    const int64_t rows_max = a.one_x_row ? 1 : a.ws ? (a.rows_cap < 16 ? a.rows_cap : 16) : a.m;
     const int64_t tiles = a.ws ? grid_tiles : (a.m + 15) / 16;
     const int64_t nsb = a.k / 256;
-    if (glu) launch_cfg2<2, 4, 4, 2>(a, rows_max, tiles, s);
+    if (glu) launch_cfg2<2, true, 2, 2, 2>(a, rows_max, tiles, s);
     else if (nsb > 16 && lds_cfg2<1, 8, 8, 2>(rows_max) <= kLdsMax)
-        launch_cfg2<1, 8, 8, 2>(a, rows_max, tiles, s);
-    else launch_cfg2<1, 4, 4, 2>(a, rows_max, tiles, s);
+        launch_cfg2<1, false, 8, 8, 2>(a, rows_max, tiles, s);
+    else launch_cfg2<1, false, 4, 4, 2>(a, rows_max, tiles, s);
     return hipGetLastError();
 }
 

@@ -1,4 +1,4 @@
-// moe.hip -- expert routing schedule, slot-order mixing and invalid-id poison.
+// moe.hip -- expert routing schedule (with NaN rows for invalid ids) and slot-order mixing.
 //
 // mlx-kquant "bindings.cpp": expert_tile_map (fixed-size row tiles per expert segment,
 // only the last partial, built on the GPU with no host sync),
@@ -17,11 +17,14 @@ namespace kq {
 //      finds the lanes holding the same expert with ballots over the id bits,
 //      its rank among them, and the lowest such lane advances the cursor
 //   4. tile descriptors (expert, row_start, num_rows) in expert order
+//   5. (when an output is given) rows with an invalid id are written as NaN
+//      in that output; the products never touch them
 __global__ __launch_bounds__(256) void route_kernel(const uint32_t* __restrict__ ids, int64_t rows,
                                                     int64_t n_experts, int32_t* __restrict__ ws,
                                                     int64_t counts_off, int64_t offsets_off,
                                                     int64_t perm_off, int64_t tiles_off,
-                                                    int id_bits) {
+                                                    int id_bits, void* __restrict__ poison_y,
+                                                    int64_t poison_n, int poison_dt) {
     extern __shared__ int32_t lds[];
     int32_t* counts = lds;                  // [E]
     int32_t* cursor = lds + n_experts;      // [E]
@@ -107,15 +110,29 @@ __global__ __launch_bounds__(256) void route_kernel(const uint32_t* __restrict__
             __builtin_amdgcn_wave_barrier();
         }
     }
+
+    if (poison_y && n_invalid > 0) {
+        const float v = __builtin_nanf("");
+        for (int64_t i = 0; i < rows; ++i) {
+            if ((int64_t)ids[i] < n_experts) continue;
+            for (int64_t j = tid; j < poison_n; j += 256) {
+                if (poison_dt == F32) store_out<F32>(poison_y, i * poison_n + j, v);
+                else if (poison_dt == F16) store_out<F16>(poison_y, i * poison_n + j, v);
+                else store_out<BF16>(poison_y, i * poison_n + j, v);
+            }
+        }
+    }
 }
 
 hipError_t launch_route(const uint32_t* ids, int64_t rows, int64_t n_experts, const MoeLayout& L,
-                        int32_t* ws, hipStream_t s) {
+                        int32_t* ws, hipStream_t s, void* poison_y, int64_t poison_n,
+                        int poison_dt) {
     int bits = 1;
     while ((1ll << bits) < n_experts) ++bits;
     const size_t lds = (size_t)3 * n_experts * sizeof(int32_t);
     hipLaunchKernelGGL(route_kernel, dim3(1), dim3(256), lds, s, ids, rows, n_experts, ws,
-                       L.counts_off, L.offsets_off, L.perm_off, L.tiles_off, bits);
+                       L.counts_off, L.offsets_off, L.perm_off, L.tiles_off, bits, poison_y,
+                       poison_n, poison_dt);
     return hipGetLastError();
 }
 
@@ -147,27 +164,6 @@ hipError_t launch_mix(const uint32_t* ids, const float* scores, int64_t n_tokens
     const dim3 grid((unsigned)((n + 255) / 256), (unsigned)n_tokens);
     hipLaunchKernelGGL(mix_kernel, grid, dim3(256), 0, s, ids, scores, top_k, n_experts, slots, n,
                        y, y_dt);
-    return hipGetLastError();
-}
-
-// Rows whose id is invalid: every output element NaN.
-__global__ __launch_bounds__(256) void poison_kernel(const uint32_t* __restrict__ ids,
-                                                     int64_t n_experts, void* __restrict__ y,
-                                                     int64_t n, int y_dt) {
-    const int64_t r = blockIdx.y;
-    if ((int64_t)ids[r] < n_experts) return;
-    const float v = __builtin_nanf("");
-    for (int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x; j < n; j += (int64_t)gridDim.x * 256) {
-        if (y_dt == F32) store_out<F32>(y, r * n + j, v);
-        else if (y_dt == F16) store_out<F16>(y, r * n + j, v);
-        else store_out<BF16>(y, r * n + j, v);
-    }
-}
-
-hipError_t launch_poison(const uint32_t* ids, int64_t rows, int64_t n_experts, void* y, int64_t n,
-                         int y_dt, hipStream_t s) {
-    const dim3 grid((unsigned)((n + 255) / 256 < 8 ? (n + 255) / 256 : 8), (unsigned)rows);
-    hipLaunchKernelGGL(poison_kernel, grid, dim3(256), 0, s, ids, n_experts, y, n, y_dt);
     return hipGetLastError();
 }
 
