@@ -207,8 +207,10 @@ def main():
         def layer(t0, nt):
             kq.kq_moe_glu("q4_k", gate, up, E, F, H, c["gate_stride"], xall[t0:t0 + nt],
                           ids[t0:t0 + nt], nt, top_k, h[:nt], mws)
-            kq.kq_qmm_id("q4_k", down, E, H, F, c["down_stride"], h[:nt], kq.LAYOUT_SLOTTED,
-                         ids[t0:t0 + nt], nt, top_k, scores[t0:t0 + nt], out[:nt], mws)
+            # the down projection keeps the schedule the gate/up call built
+            kq.kq_qmm_id("q4_k", down, E, H, F, c["down_stride"], h[:nt],
+                         kq.LAYOUT_SLOTTED | kq.REUSE_SCHEDULE, ids[t0:t0 + nt], nt, top_k,
+                         scores[t0:t0 + nt], out[:nt], mws)
 
         dec_calls = [lambda t=t, layer=layer: layer(t, 1) for t in range(0, 64)]
         # every decode token reads its 8 experts' three matrices

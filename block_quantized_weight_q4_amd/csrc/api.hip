@@ -253,6 +253,8 @@ kq_status kq_qmm_id(kq_type t, const void* w, int64_t n_experts, int64_t n, int6
                     const uint32_t* ids, int64_t n_tokens, int64_t top_k, const float* scores,
                     void* y, kq_dtype y_dt, void* workspace, size_t workspace_bytes,
                     void* stream) {
+    const bool reuse = (x_layout & KQ_REUSE_SCHEDULE) != 0 && scores;
+    x_layout &= ~KQ_REUSE_SCHEDULE;
     if (x_layout != KQ_LAYOUT_SHARED && x_layout != KQ_LAYOUT_SLOTTED)
         return fail(KQ_ERR_INVALID_ARG, "unknown x layout");
     const int64_t rows = (n_tokens > 0 && top_k > 0 && n_tokens <= INT32_MAX / top_k) ? n_tokens * top_k : 0;
@@ -268,8 +270,10 @@ kq_status kq_qmm_id(kq_type t, const void* w, int64_t n_experts, int64_t n, int6
     int32_t* ws = (int32_t*)workspace;
     // the unmixed form's rows with an invalid id are poisoned by the route;
     // the mixed form's tokens by the mix
-    hipError_t e = scores ? kq::launch_route(ids, L.rows, n_experts, L, ws, s)
-                          : kq::launch_route(ids, L.rows, n_experts, L, ws, s, y, n, y_dt);
+    hipError_t e = hipSuccess;
+    if (!reuse)
+        e = scores ? kq::launch_route(ids, L.rows, n_experts, L, ws, s)
+                   : kq::launch_route(ids, L.rows, n_experts, L, ws, s, y, n, y_dt);
     if (e != hipSuccess) return launched(e);
     kq::SkinnyArgs a{};
     a.w = (const uint8_t*)w;

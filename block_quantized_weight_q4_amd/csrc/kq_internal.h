@@ -38,6 +38,7 @@ struct SkinnyArgs {
     const int32_t* ws;     // routed: workspace (schedule); null for dense
     int64_t tiles_off, perm_off;
     int64_t xexp_off;      // routed, fp32 activations: word offset of row exponents
+    int xexp_local;        // ... or found by each workgroup for its own rows
     int64_t m;             // dense: activation rows
     void* y;               // output
     int y_dt;              // output dtype

@@ -17,8 +17,9 @@
 // q4k_mfma.h (sc*q as fp16 integers, 6-bit mins as a second MFMA chain, d and
 // dmin per super-block in fp32).
 //
-// fp32 activations: each activation row r is scaled by 2^-e_r (e_r from a
-// pre-pass, so the row's largest magnitude lies in [2^14, 2^15)) and split
+// fp32 activations: each activation row r is scaled by 2^-e_r (e_r such that
+// the row's largest magnitude lies in [2^14, 2^15): from a pre-pass over all
+// rows, or found by the workgroup itself when tiles hold few rows) and split
 // into fp16 hi + lo parts; both parts go through the MFMAs, and the row's
 // result is scaled back by 2^e_r.  hi + lo carries 22 significant bits of
 // each scaled element.
@@ -31,6 +32,15 @@ namespace kq {
 // ---------------------------------------------------------------- row scales
 // e[r] such that max_c |x[r,c]| * 2^-e[r] lies in [2^14, 2^15); 0 for a row
 // of zeros or with a non-finite maximum.
+__device__ __forceinline__ int row_exponent(float mx) {
+    int ex = 0;
+    if (mx > 0.f && mx <= 3.402823466e38f) {
+        frexpf(mx, &ex);  // mx = f * 2^ex, f in [0.5, 1)
+        ex -= 15;
+    }
+    return ex;
+}
+
 __global__ __launch_bounds__(256) void row_exp_kernel(const float* __restrict__ x, int64_t k,
                                                       int32_t* __restrict__ e) {
     __shared__ float part[4];
@@ -42,15 +52,7 @@ __global__ __launch_bounds__(256) void row_exp_kernel(const float* __restrict__ 
     for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
     if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = mx;
     __syncthreads();
-    if (threadIdx.x == 0) {
-        mx = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
-        int ex = 0;
-        if (mx > 0.f && mx <= 3.402823466e38f) {
-            frexpf(mx, &ex);  // mx = f * 2^ex, f in [0.5, 1)
-            ex -= 15;
-        }
-        e[r] = ex;
-    }
+    if (threadIdx.x == 0) e[r] = row_exponent(fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3])));
 }
 
 hipError_t launch_row_exp(const float* x, int64_t rows, int64_t k, int32_t* e, hipStream_t s) {
@@ -79,6 +81,27 @@ __global__ __launch_bounds__(64 * W) void moe_mm_kernel(SkinnyArgs a) {
     const int nrows = tile[2];
     const int32_t* perm = a.ws + a.perm_off;
     const int64_t n0 = (int64_t)blockIdx.x * ROWS;
+    auto x_row_of = [&](int r) -> int64_t {
+        int64_t xr = perm[row0 + r];
+        return a.shared_x ? xr / a.top_k : xr;
+    };
+
+    // fp32 activations of small tiles: each wave finds the scale exponent of
+    // some of the tile's rows (the first chunk's barrier publishes them)
+    __shared__ int sexp[kMoeTileRows];
+    if (XF32 && a.xexp_local) {
+        for (int r = wave; r < nrows; r += W) {
+            const float* row = (const float*)a.x + x_row_of(r) * a.x_row;
+            float mx = 0.f;
+            for (int64_t c = 4 * lane; c < a.k; c += 256) {
+                const float4_t v = *(const float4_t*)(row + c);
+                mx = fmaxf(fmaxf(mx, fmaxf(fabsf(v[0]), fabsf(v[1]))), fmaxf(fabsf(v[2]), fabsf(v[3])));
+            }
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+            if (lane == 0) sexp[r] = row_exponent(mx);
+        }
+    }
 
     const uint8_t* wrow[2];
 #pragma unroll
@@ -125,8 +148,7 @@ __global__ __launch_bounds__(64 * W) void moe_mm_kernel(SkinnyArgs a) {
             const int per_row = nch * 32;  // 16-byte pieces
             for (int i = tid; i < nrows * per_row; i += 64 * W) {
                 const int r = i / per_row, q = i - r * per_row;
-                int64_t xr = perm[row0 + r];
-                if (a.shared_x) xr /= a.top_k;
+                const int64_t xr = x_row_of(r);
                 const u32x4 v = *(const u32x4*)((const uint16_t*)a.x + xr * a.x_row + (int64_t)c0 * 256 + 8 * q);
                 *(u32x4*)&xh[r * XSTRIDE + 8 * q] = v;
             }
@@ -134,9 +156,8 @@ __global__ __launch_bounds__(64 * W) void moe_mm_kernel(SkinnyArgs a) {
             const int per_row = nch * 64;  // 4-float pieces
             for (int i = tid; i < nrows * per_row; i += 64 * W) {
                 const int r = i / per_row, q = i - r * per_row;
-                int64_t xr = perm[row0 + r];
-                if (a.shared_x) xr /= a.top_k;
-                const int ex = a.ws[a.xexp_off + xr];
+                const int64_t xr = x_row_of(r);
+                const int ex = a.xexp_local ? sexp[r] : a.ws[a.xexp_off + xr];
                 const float4_t v = *(const float4_t*)((const float*)a.x + xr * a.x_row + (int64_t)c0 * 256 + 4 * q);
                 uint32_t hi[2], lo[2];
 #pragma unroll
@@ -207,7 +228,7 @@ __global__ __launch_bounds__(64 * W) void moe_mm_kernel(SkinnyArgs a) {
             float sc = 1.f;
             if (XF32) {
                 const int64_t xr = a.shared_x ? orow / a.top_k : orow;
-                sc = ldexpf(1.f, a.ws[a.xexp_off + xr]);
+                sc = ldexpf(1.f, a.xexp_local ? sexp[idx] : a.ws[a.xexp_off + xr]);
             }
             if (GLU) {
                 const int64_t n = n0 + 16 * wave + n_l;
@@ -225,19 +246,21 @@ __global__ __launch_bounds__(64 * W) void moe_mm_kernel(SkinnyArgs a) {
     }
 }
 
-// Staged activations: 32 rows of XC super-blocks (fp16, plus the lo part
-// for fp32 activations) within 64 KB, so two workgroups share a CU.
+// Staged activations: up to 32 rows (no more than the routing holds) of XC
+// super-blocks, fp16 (plus the lo part for fp32 activations), within 64 KB so
+// that two workgroups share a CU.
 template <int W, bool GLU, bool XF32>
 static void launch_mm(SkinnyArgs a, int64_t grid_tiles, hipStream_t s) {
     constexpr int64_t kBudget = 64 * 1024;
     constexpr int ROWS = GLU ? 16 * W : 32 * W;
     const int64_t nsb = a.k / 256;
     const int64_t parts = XF32 ? 2 : 1;
-    int64_t xc = kBudget / (parts * kMoeTileRows * (256 * 2 + 16));
+    const int64_t rows = a.rows_cap < kMoeTileRows ? a.rows_cap : kMoeTileRows;
+    int64_t xc = kBudget / (parts * rows * (256 * 2 + 16));
     xc = xc < 1 ? 1 : xc > nsb ? nsb : xc;
     a.xch = (int)xc;
     a.xstride = (int)(xc * 256 + 8);
-    const int64_t part_bytes = ((int64_t)kMoeTileRows * a.xstride * 2 + 15) / 16 * 16;
+    const int64_t part_bytes = (rows * a.xstride * 2 + 15) / 16 * 16;
     a.red_off = (int)part_bytes;  // start of the lo part
     const size_t lds = (size_t)(parts * part_bytes);
     const dim3 grid((unsigned)((a.n + ROWS - 1) / ROWS), (unsigned)grid_tiles);

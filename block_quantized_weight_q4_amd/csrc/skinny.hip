@@ -244,13 +244,17 @@ hipError_t launch_skinny(int codec, int x_dt, bool glu, const SkinnyArgs& a, int
     // with fp16 activations stream weights and activations through LDS
     // (mmv2.hip)
     if (codec == Q4_K && a.ws && (x_dt == F32 || (x_dt == F16 && a.rows_cap > 16))) {
-        if (x_dt == F32) {
+        SkinnyArgs b = a;
+        // fp32 row scales: small routings find them per workgroup, larger
+        // ones in one pass over the activation rows
+        b.xexp_local = a.rows_cap <= 16;
+        if (x_dt == F32 && !b.xexp_local) {
             const int64_t x_rows = a.shared_x ? a.rows_cap / a.top_k : a.rows_cap;
             const hipError_t e = launch_row_exp((const float*)a.x, x_rows, a.k,
                                                 const_cast<int32_t*>(a.ws) + a.xexp_off, s);
             if (e != hipSuccess) return e;
         }
-        return launch_moe_mm(glu, x_dt, a, grid_tiles, s);
+        return launch_moe_mm(glu, x_dt, b, grid_tiles, s);
     }
     if (codec == Q4_K && x_dt == F16 && (a.ws ? a.rows_cap <= 16 : a.m <= 16))
         return launch_mmv2_q4k(glu, a, grid_tiles, s);

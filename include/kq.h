@@ -57,8 +57,17 @@ typedef enum kq_status {
 
 /* x layouts of kq_qmm_id: one activation row per token, shared by its
  * top_k slots ([T, k]), or one row per (token, slot) ([T, top_k, k]).
- * mlx-native "quantized_matmul_id_ggml.rs", IdMmInputLayout. */
-enum { KQ_LAYOUT_SHARED = 0, KQ_LAYOUT_SLOTTED = 1 };
+ * mlx-native "quantized_matmul_id_ggml.rs", IdMmInputLayout.
+ *
+ * KQ_REUSE_SCHEDULE, OR-ed into the layout of a kq_qmm_id call with scores,
+ * skips building the routing schedule: the workspace must then hold the
+ * schedule that the previous kq_moe_glu, kq_qmm_id or kq_moe_route call on
+ * the same stream built from the same ids, n_tokens, top_k and n_experts,
+ * unmodified since (the gate/up -> down sequence of one MoE layer).
+ * mlx-native "quantized_matmul_id_ggml.rs", the scratch reused across the
+ * expert dispatches of a layer.  Ignored when scores is NULL: that form's
+ * rows with an invalid id are written while the schedule is built. */
+enum { KQ_LAYOUT_SHARED = 0, KQ_LAYOUT_SLOTTED = 1, KQ_REUSE_SCHEDULE = 0x100 };
 
 /* GLU activations of kq_moe_glu: h = act(gate) * up.  silu(z) = z / (1 + e^-z).
  * mlx-kquant "bindings.cpp", moe_glu_gather_kq (act='silu', the default). */

@@ -117,6 +117,40 @@ def test_qmm_id_f32_activations(kq, kind, layout, mixed, E, T, top_k):
     check_tol(to_f64(y), ref, s, TAU["f32"], f"qmm_id f32 {kind}")
 
 
+@pytest.mark.parametrize("T", [1, 40])
+def test_reused_schedule_matches_rebuilt(kq, T):
+    # gate/up then down on one workspace: the down call that keeps the
+    # schedule built by the GLU gives the same bits as one that rebuilds it
+    E, F, H, top_k = 8, 256, 256, 4
+    rng = synth.rng_for(300 + T)
+    gate = synth.weight_blocks("q4_k", rng, E * F, H)
+    up = synth.weight_blocks("q4_k", rng, E * F, H)
+    down = synth.weight_blocks("q4_k", rng, E * H, F)
+    ids = _ids(rng, T, E, top_k)
+    if T > 1:
+        ids.ravel()[0] = E + 3  # an invalid id: token 0's output is NaN either way
+    scores = rng.uniform(0.05, 1.0, size=(T, top_k)).astype(np.float32)
+    x = synth.activations(rng, (T, H), "f16")
+    gs, ds = F * synth.row_bytes("q4_k", H), H * synth.row_bytes("q4_k", F)
+    dev = {k: to_dev(v) for k, v in (("gate", gate), ("up", up), ("down", down), ("ids", ids),
+                                     ("scores", scores))}
+    ws = _ws(kq, E, T, top_k, H)
+    h = empty((T, top_k, F), "f32")
+    outs = []
+    for flags in (0, kq.REUSE_SCHEDULE):
+        _say("reuse", T, flags)
+        kq.kq_moe_glu("q4_k", dev["gate"], dev["up"], E, F, H, gs, to_dev(x, "f16"), dev["ids"],
+                      T, top_k, h, ws)
+        out = empty((T, H), "f32")
+        kq.kq_qmm_id("q4_k", dev["down"], E, H, F, ds, h, kq.LAYOUT_SLOTTED | flags,
+                     dev["ids"], T, top_k, dev["scores"], out, ws)
+        torch.cuda.synchronize()
+        outs.append(out.cpu().numpy())
+    if T > 1:
+        assert np.isnan(outs[0][0]).all() and not np.isnan(outs[0][1:]).any()
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+
+
 def test_qmm_id_invalid_ids_poison(kq):
     E, n, k, T, top_k = 6, 64, 256, 4, 2
     rng, w, stride, ids, scores = _moe_case("q4_k", E, n, k, T, top_k, 77)
