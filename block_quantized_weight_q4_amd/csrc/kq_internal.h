@@ -58,6 +58,9 @@ hipError_t launch_mmv2_q4k(bool glu, const SkinnyArgs& a, int64_t grid_tiles, hi
 hipError_t launch_moe_mm(bool glu, int x_dt, const SkinnyArgs& a, int64_t grid_tiles,
                          hipStream_t s);
 hipError_t launch_row_exp(const float* x, int64_t rows, int64_t k, int32_t* e, hipStream_t s);
+bool tq1_mv_fits(int64_t k);
+hipError_t launch_tq1_mv(const uint8_t* w, int64_t n, int64_t k, const uint16_t* x, void* y,
+                         int y_dt, hipStream_t s);
 hipError_t launch_gemm(int codec, int x_dt, const void* w, int64_t n, int64_t k, const void* x,
                        int64_t m, void* y, int y_dt, hipStream_t s);
 // Builds the schedule; with poison_y, also writes NaN to the rows of
