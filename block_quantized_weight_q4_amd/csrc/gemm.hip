@@ -5,7 +5,7 @@
 // across a whole block of activation rows on the matrix units).
 //
 // The contraction runs on v_mfma_f32_32x32x16 in the activation's 16-bit
-// type (bf16 or fp16) with fp32 accumulation.  A workgroup of four waves owns
+// type (bf16 or fp16) with fp32 accumulation.  A workgroup of eight waves owns
 // a BM x BN output tile; per K step of 64 it decodes its BN x 64 weight tile
 // once into LDS (so each decoded weight feeds BM rows) next to the BM x 64
 // activation tile.  The global loads of step k+1 are issued before the MFMAs
@@ -183,20 +183,23 @@ template <> struct WTile<TQ1> {
 };
 
 // ---------------------------------------------------------------- kernel
-// BM x BN tile, four waves as 2 x 2, each a (BM/2) x (BN/2) sub-tile of
-// 32x32 MFMA blocks.
-template <int C, int XDT, int BM, int BN>
-__global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ w, int64_t n,
-                                                   int64_t k, const uint16_t* __restrict__ x,
-                                                   int64_t m, void* __restrict__ y, int y_dt) {
-    constexpr int TM = BM / 2, TN = BN / 2, FM = TM / 32, FN = TN / 32;
-    constexpr int XP = BM * 8 / 256;  // 16-byte activation pieces per thread per step
+// BM x BN tile, NW waves as 2 x (NW/2), each a (BM/2) x (2BN/NW) sub-tile of
+// 32x32 MFMA blocks.  With eight waves two share each SIMD, so one wave's
+// weight decoding overlaps the other's matrix work.
+template <int C, int XDT, int BM, int BN, int NW>
+__global__ __launch_bounds__(64 * NW) void gemm_kernel(const uint8_t* __restrict__ w, int64_t n,
+                                                       int64_t k, const uint16_t* __restrict__ x,
+                                                       int64_t m, void* __restrict__ y, int y_dt) {
+    constexpr int NT = 64 * NW, WN = NW / 2;
+    constexpr int TM = BM / 2, TN = BN / WN, FM = TM / 32, FN = TN / 32;
+    static_assert(FM >= 1 && FN >= 1 && 2 * BN <= NT, "tile shape");
+    constexpr int XP = BM * 8 / NT;  // 16-byte activation pieces per thread per step
     constexpr int ASZ = BM * LDS_STRIDE, BSZ = BN * LDS_STRIDE;
     using WT = WTile<C>;
     // two stages of [activation tile | weight tile]
     __shared__ __align__(16) uint16_t lds[2 * (ASZ + BSZ)];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WN, wn = wave % WN;
     const int64_t n0 = (int64_t)blockIdx.x * BN, m0 = (int64_t)blockIdx.y * BM;
     const int64_t row_bytes = (k / CodecInfo<C>::QK) * CodecInfo<C>::BYTES;
     const int steps = (int)((k + BK - 1) / BK);
@@ -219,7 +222,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ w
     auto fetch = [&](int s) {
 #pragma unroll
         for (int i = 0; i < XP; ++i) {
-            const int p = tid + 256 * i, r = p >> 3, q = p & 7;
+            const int p = tid + NT * i, r = p >> 3, q = p & 7;
             const int64_t gm = m0 + r;
             const int64_t c0 = (int64_t)s * BK + 8 * q;
             xr[i] = (gm < m && c0 < k) ? *(const u32x4*)(x + gm * k + c0) : u32x4{0u, 0u, 0u, 0u};
@@ -234,7 +237,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ w
         uint16_t* Bs = As + ASZ;
 #pragma unroll
         for (int i = 0; i < XP; ++i) {
-            const int p = tid + 256 * i, r = p >> 3, q = p & 7;
+            const int p = tid + NT * i, r = p >> 3, q = p & 7;
             *(u32x4*)&As[r * LDS_STRIDE + 8 * q] = xr[i];
         }
         if (wrole) {
@@ -317,24 +320,26 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ w
         }
 }
 
-template <int C, int XDT, int BM, int BN>
+template <int C, int XDT, int BM, int BN, int NW>
 static void launch_tile(const void* w, int64_t n, int64_t k, const void* x, int64_t m, void* y,
                         int y_dt, hipStream_t s) {
-    const dim3 grid((unsigned)((n + BN - 1) / BN), (unsigned)((m + BM - 1) / BM)), block(256);
-    hipLaunchKernelGGL((gemm_kernel<C, XDT, BM, BN>), grid, block, 0, s, (const uint8_t*)w, n, k,
-                       (const uint16_t*)x, m, y, y_dt);
+    const dim3 grid((unsigned)((n + BN - 1) / BN), (unsigned)((m + BM - 1) / BM)), block(64 * NW);
+    hipLaunchKernelGGL((gemm_kernel<C, XDT, BM, BN, NW>), grid, block, 0, s, (const uint8_t*)w, n,
+                       k, (const uint16_t*)x, m, y, y_dt);
 }
 
-// Tile choice: the largest tile whose grid still gives every compute unit a
-// workgroup (256 CUs), since a bigger tile reuses each decoded weight over
-// more rows and each activation over more columns.
+// Tile choice (eight waves, two per SIMD, measured on the prefill shapes):
+// 256 x 256 while the grid holds at least 1.5 workgroups per CU (256 CUs),
+// else 256 x 128 while it holds 0.75, else 128 x 128.  Larger tiles reuse
+// each decoded weight over more rows and each activation over more columns;
+// smaller ones keep the CUs busy when there are few tiles.
 template <int C, int XDT>
 static void launch_c(const void* w, int64_t n, int64_t k, const void* x, int64_t m, void* y,
                      int y_dt, hipStream_t s) {
     auto tiles = [&](int64_t bm, int64_t bn) { return ((n + bn - 1) / bn) * ((m + bm - 1) / bm); };
-    if (tiles(256, 128) >= 256) launch_tile<C, XDT, 256, 128>(w, n, k, x, m, y, y_dt, s);
-    else if (tiles(128, 128) >= 256) launch_tile<C, XDT, 128, 128>(w, n, k, x, m, y, y_dt, s);
-    else launch_tile<C, XDT, 128, 64>(w, n, k, x, m, y, y_dt, s);
+    if (tiles(256, 256) >= 384) launch_tile<C, XDT, 256, 256, 8>(w, n, k, x, m, y, y_dt, s);
+    else if (tiles(256, 128) >= 192) launch_tile<C, XDT, 256, 128, 8>(w, n, k, x, m, y, y_dt, s);
+    else launch_tile<C, XDT, 128, 128, 8>(w, n, k, x, m, y, y_dt, s);
 }
 
 hipError_t launch_gemm(int codec, int x_dt, const void* w, int64_t n, int64_t k, const void* x,
