@@ -217,35 +217,39 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const uint8_t* __restrict
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = float16_t{};
 
-    u32x4 xr[XP];
-    typename WT::Raw raw;
-    auto fetch = [&](int s) {
+    // registers holding the fetched-but-not-stashed step
+    struct Regs {
+        u32x4 xr[XP];
+        typename WT::Raw raw;
+    };
+    Regs ra;
+    auto fetch = [&](int s, Regs& R) {
 #pragma unroll
         for (int i = 0; i < XP; ++i) {
             const int p = tid + NT * i, r = p >> 3, q = p & 7;
             const int64_t gm = m0 + r;
             const int64_t c0 = (int64_t)s * BK + 8 * q;
-            xr[i] = (gm < m && c0 < k) ? *(const u32x4*)(x + gm * k + c0) : u32x4{0u, 0u, 0u, 0u};
+            R.xr[i] = (gm < m && c0 < k) ? *(const u32x4*)(x + gm * k + c0) : u32x4{0u, 0u, 0u, 0u};
         }
         if (wrole && ((C != Q8_0) || (int64_t)(2 * s + wh) * 32 < k))
-            WT::fetch(wrow, s, wh, raw, (row_bytes & 3) == 0);
+            WT::fetch(wrow, s, wh, R.raw, (row_bytes & 3) == 0);
     };
     // write the fetched step into stage st: activations as they are, weights
     // decoded to the 16-bit operand type
-    auto stash = [&](int s, int st) {
+    auto stash = [&](int s, int st, const Regs& R) {
         uint16_t* As = lds + st * (ASZ + BSZ);
         uint16_t* Bs = As + ASZ;
 #pragma unroll
         for (int i = 0; i < XP; ++i) {
             const int p = tid + NT * i, r = p >> 3, q = p & 7;
-            *(u32x4*)&As[r * LDS_STRIDE + 8 * q] = xr[i];
+            *(u32x4*)&As[r * LDS_STRIDE + 8 * q] = R.xr[i];
         }
         if (wrole) {
             uint32_t lo[8], hi[8];
             int cl, ch;
             const bool live = wvalid && ((C != Q8_0) || (int64_t)(2 * s + wh) * 32 < k);
             if (live) {
-                WT::template decode<XDT>(raw, s, wh, lo, hi, cl, ch);
+                WT::template decode<XDT>(R.raw, s, wh, lo, hi, cl, ch);
             } else {
 #pragma unroll
                 for (int i = 0; i < 8; ++i) lo[i] = hi[i] = 0u;
@@ -269,14 +273,11 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const uint8_t* __restrict
             bf[j] = *(const u32x4*)&Bs[(wn * TN + 32 * j + (lane & 31)) * LDS_STRIDE + 16 * ks + 8 * (lane >> 5)];
     };
 
-    // Pipeline: stage s%2 holds step s; while the MFMAs of step s run, step
-    // s+1 (fetched an iteration earlier) is decoded into the other stage and
-    // step s+2 is fetched.  One barrier per step.
-    fetch(0);
-    stash(0, 0);
-    if (steps > 1) fetch(1);
-    __syncthreads();
-    for (int s = 0; s < steps; ++s) {
+    // Pipeline: LDS stage s%2 holds step s; while the MFMAs of step s run,
+    // step s+1 (fetched an iteration earlier) is decoded into the other
+    // stage, and step s+2 is fetched into the freed registers.  One barrier
+    // per step.
+    auto step = [&](int s, Regs& R) {
         const int st = s & 1;
         u32x4 af[FM], bf[FN];
         frags(st, 0, af, bf);
@@ -288,7 +289,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const uint8_t* __restrict
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j) acc[i][j] = Op16<XDT>::mma(af[i], bf[j], acc[i][j]);
-            if (ks == 0 && s + 1 < steps) stash(s + 1, st ^ 1);
+            if (ks == 0 && s + 1 < steps) stash(s + 1, st ^ 1, R);
             if (ks + 1 < BK / 16) {
 #pragma unroll
                 for (int i = 0; i < FM; ++i) af[i] = naf[i];
@@ -296,9 +297,14 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const uint8_t* __restrict
                 for (int j = 0; j < FN; ++j) bf[j] = nbf[j];
             }
         }
-        if (s + 2 < steps) fetch(s + 2);
+        if (s + 2 < steps) fetch(s + 2, R);
         __syncthreads();
-    }
+    };
+    fetch(0, ra);
+    stash(0, 0, ra);
+    if (steps > 1) fetch(1, ra);
+    __syncthreads();
+    for (int s = 0; s < steps; ++s) step(s, ra);
 
     // epilogue: lane holds column l%32 and rows 8*(v/4) + 4*(l/32) + v%4
 #pragma unroll
