@@ -135,10 +135,12 @@ def main():
     c2_parts = []
     if "qmv_c2" in wanted:
         calls, nbytes, flops = [], 0, 0
+        c2_ws = {}
         for case in workloads.c2():
             n, k = case["n"], case["k"]
             w = d8(case["w"])
             ws = copies(w, w.numel())
+            c2_ws[(n, k)] = ws
             x = d16(case["x"], torch.float16)
             for b in (1, 4, 8):
                 y = torch.empty((b, n), dtype=torch.float16, device=dev)
@@ -152,6 +154,19 @@ def main():
                 flops += reps * 2 * b * n * k
         stages.append(Stage("qmv_c2", calls, nbytes, flops,
                             note="Q4_K 14336x4096 + 4096x14336, batch 1/4/8, fp16"))
+        # dependency chain at batch 1: each call's output row is the next
+        # call's activation row (14336x4096 then 4096x14336, alternating)
+        wa, wb = c2_ws[(14336, 4096)], c2_ws[(4096, 14336)]
+        va = d16(workloads.c2()[0]["x"][:1], torch.float16)
+        vb = torch.empty((1, 14336), dtype=torch.float16, device=dev)
+        chain = []
+        for _ in range(len(wa)):
+            chain.append(lambda: kq.kq_qmv("q4_k", nxt(wa), 14336, 4096, va, 1, vb))
+            chain.append(lambda: kq.kq_qmv("q4_k", nxt(wb), 4096, 14336, vb, 1, va))
+        cbytes = len(chain) * (wa[0].numel() + (4096 + 14336) * 2)
+        stages.append(Stage("qmv_c2_chain_b1", chain, cbytes, len(chain) * 2 * 4096 * 14336,
+                            note="batch 1, each output feeds the next call (values may overflow "
+                                 "fp16; the work is the same)"))
 
     c3_parts = []
     if "qmm_c3" in wanted:
@@ -369,10 +384,19 @@ def cpu_baseline():
                 nbytes += case["w"].nbytes
                 calls += 1
         passes += 1
+    cpu = "unknown CPU"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": round(nbytes / t_total / 1e9, 3), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
             "sample": f"{passes} passes over the 6 Q4_K GEMV calls (14336x4096 and 4096x14336 "
-                      f"at batch 1/4/8), {calls} calls, fp64 accumulation, {t_total:.1f} s"}
+                      f"at batch 1/4/8), {calls} calls, fp64 accumulation, {t_total:.1f} s, "
+                      f"{threads} threads on {cpu}"}
 
 
 if __name__ == "__main__":
