@@ -223,16 +223,32 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const uint8_t* __restrict
         typename WT::Raw raw;
     };
     Regs ra;
+    // With every thread owning a weight role (2 BN == threads) the step is
+    // branch-free: out-of-range pieces are read from a valid address and
+    // replaced by zeros with selects, so the whole K step is one scheduling
+    // region in which loads, decoding and MFMAs can interleave.
+    constexpr bool FULL = 2 * BN == NT;
     auto fetch = [&](int s, Regs& R) {
 #pragma unroll
         for (int i = 0; i < XP; ++i) {
             const int p = tid + NT * i, r = p >> 3, q = p & 7;
             const int64_t gm = m0 + r;
             const int64_t c0 = (int64_t)s * BK + 8 * q;
-            R.xr[i] = (gm < m && c0 < k) ? *(const u32x4*)(x + gm * k + c0) : u32x4{0u, 0u, 0u, 0u};
+            if (FULL) {
+                const bool ok = gm < m && c0 < k;
+                const u32x4 v = *(const u32x4*)(x + (ok ? gm * k + c0 : 0));
+                R.xr[i] = ok ? v : u32x4{0u, 0u, 0u, 0u};
+            } else {
+                R.xr[i] = (gm < m && c0 < k) ? *(const u32x4*)(x + gm * k + c0) : u32x4{0u, 0u, 0u, 0u};
+            }
         }
-        if (wrole && ((C != Q8_0) || (int64_t)(2 * s + wh) * 32 < k))
+        if (FULL) {
+            // a Q8_0 half past the row end reads the step's first block instead
+            const int hf = (C == Q8_0 && (int64_t)(2 * s + wh) * 32 >= k) ? 0 : wh;
+            WT::fetch(wrow, s, hf, R.raw, (row_bytes & 3) == 0);
+        } else if (wrole && ((C != Q8_0) || (int64_t)(2 * s + wh) * 32 < k)) {
             WT::fetch(wrow, s, wh, R.raw, (row_bytes & 3) == 0);
+        }
     };
     // write the fetched step into stage st: activations as they are, weights
     // decoded to the 16-bit operand type
@@ -244,11 +260,18 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const uint8_t* __restrict
             const int p = tid + NT * i, r = p >> 3, q = p & 7;
             *(u32x4*)&As[r * LDS_STRIDE + 8 * q] = R.xr[i];
         }
-        if (wrole) {
+        if (FULL || wrole) {
             uint32_t lo[8], hi[8];
             int cl, ch;
             const bool live = wvalid && ((C != Q8_0) || (int64_t)(2 * s + wh) * 32 < k);
-            if (live) {
+            if (FULL) {
+                WT::template decode<XDT>(R.raw, s, wh, lo, hi, cl, ch);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    lo[i] = live ? lo[i] : 0u;
+                    hi[i] = live ? hi[i] : 0u;
+                }
+            } else if (live) {
                 WT::template decode<XDT>(R.raw, s, wh, lo, hi, cl, ch);
             } else {
 #pragma unroll
@@ -289,7 +312,9 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const uint8_t* __restrict
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j) acc[i][j] = Op16<XDT>::mma(af[i], bf[j], acc[i][j]);
-            if (ks == 0 && s + 1 < steps) stash(s + 1, st ^ 1, R);
+            // (on the last step the stash fills the idle stage with data
+            // that is never read)
+            if (ks == 0 && (FULL || s + 1 < steps)) stash(s + 1, st ^ 1, R);
             if (ks + 1 < BK / 16) {
 #pragma unroll
                 for (int i = 0; i < FM; ++i) af[i] = naf[i];
@@ -297,7 +322,8 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const uint8_t* __restrict
                 for (int j = 0; j < FN; ++j) bf[j] = nbf[j];
             }
         }
-        if (s + 2 < steps) fetch(s + 2, R);
+        if (FULL) fetch(s + 2 < steps ? s + 2 : steps - 1, R);
+        else if (s + 2 < steps) fetch(s + 2, R);
         __syncthreads();
     };
     fetch(0, ra);
