@@ -16,12 +16,14 @@
 
 namespace kq {
 
-template <int DT> struct Out8;  // 8 consecutive outputs
+// 8 consecutive outputs.  Outputs are written once and not read back here,
+// so they are stored non-temporally (they need not stay in the caches).
+template <int DT> struct Out8;
 template <> struct Out8<F32> {
     static __device__ __forceinline__ void store(void* out, int64_t i, const float (&v)[8]) {
         float4_t* p = (float4_t*)((float*)out + i);
-        p[0] = float4_t{v[0], v[1], v[2], v[3]};
-        p[1] = float4_t{v[4], v[5], v[6], v[7]};
+        __builtin_nontemporal_store(float4_t{v[0], v[1], v[2], v[3]}, p);
+        __builtin_nontemporal_store(float4_t{v[4], v[5], v[6], v[7]}, p + 1);
     }
 };
 template <> struct Out8<F16> {
@@ -30,7 +32,7 @@ template <> struct Out8<F16> {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             r[j] = float_to_half_bits(v[2 * j]) | ((uint32_t)float_to_half_bits(v[2 * j + 1]) << 16);
-        *(u32x4*)((uint16_t*)out + i) = r;
+        __builtin_nontemporal_store(r, (u32x4*)((uint16_t*)out + i));
     }
 };
 template <> struct Out8<BF16> {
@@ -39,39 +41,48 @@ template <> struct Out8<BF16> {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             r[j] = float_to_bf16_bits(v[2 * j]) | ((uint32_t)float_to_bf16_bits(v[2 * j + 1]) << 16);
-        *(u32x4*)((uint16_t*)out + i) = r;
+        __builtin_nontemporal_store(r, (u32x4*)((uint16_t*)out + i));
     }
 };
 
-// Q4_K: 16 threads per super-block.  Thread (c, h) reads quant bytes
-// Q[32c+8h .. 32c+8h+8) and writes weights 64c+8h.. (low nibbles) and
-// 64c+32+8h.. (high nibbles).
+// Q4_K: each thread writes V consecutive weights of one sub-block (V = 4 for
+// fp32, 8 for 16-bit outputs: 16 bytes), so the lanes of a wave store
+// consecutive 16-byte pieces and every store instruction is one contiguous
+// 1 KB run.  Weight w of a super-block lies in chunk c = w / 64; its first 32
+// weights are the low nibbles of quant bytes 32c.., the next 32 the high
+// nibbles of the same bytes.
 template <int DT>
 __global__ __launch_bounds__(256) void dequant_q4k_kernel(const uint8_t* __restrict__ w,
                                                           void* __restrict__ out, int64_t nblocks) {
+    constexpr int V = DT == F32 ? 4 : 8, TPB = 256 / V;
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t b = t >> 4;
+    const int64_t b = t / TPB;
     if (b >= nblocks) return;
-    const int c = (t >> 2) & 3, h = t & 3;
+    const int w0 = V * (int)(t % TPB);
+    const int c = w0 >> 6, off = w0 & 63, hi = off >> 5, byte0 = 32 * c + (off & 31);
     const uint8_t* blk = w + b * 144;
     const u32x4 hd = *(const u32x4*)blk;
-    const u32x2 q = *(const u32x2*)(blk + 16 + 32 * c + 8 * h);
-    int sc0, m0, sc1, m1;
-    q4k_scale_min(hd, 2 * c, sc0, m0);
-    q4k_scale_min(hd, 2 * c + 1, sc1, m1);
-    const float d = q4k_d(hd), dmin = q4k_dmin(hd);
-    const float s0 = d * (float)sc0, s1 = d * (float)sc1;
-    const float n0 = dmin * (float)m0, n1 = dmin * (float)m1;
-    float lo[8], hi[8];
+    uint32_t q[V / 4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < V / 4; ++i) q[i] = *(const uint32_t*)(blk + 16 + byte0 + 4 * i);
+    int sc, m;
+    q4k_scale_min(hd, 2 * c + hi, sc, m);
+    const float sd = q4k_d(hd) * (float)sc, mn = q4k_dmin(hd) * (float)m;
+    float v[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
         const uint32_t byte = (q[i >> 2] >> (8 * (i & 3))) & 0xffu;
-        lo[i] = __builtin_fmaf(s0, (float)(byte & 15u), -n0);
-        hi[i] = __builtin_fmaf(s1, (float)(byte >> 4), -n1);
+        v[i] = __builtin_fmaf(sd, (float)((byte >> (4 * hi)) & 15u), -mn);
     }
-    const int64_t base = b * 256 + 64 * c + 8 * h;
-    Out8<DT>::store(out, base, lo);
-    Out8<DT>::store(out, base + 32, hi);
+    const int64_t base = b * 256 + w0;
+    if (DT == F32) {
+        __builtin_nontemporal_store(float4_t{v[0], v[1], v[2], v[3]}, (float4_t*)((float*)out + base));
+    } else {
+        float v8[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v8[i] = v[i % V];
+        Out8<DT>::store(out, base, v8);
+    }
 }
 
 // Q8_0: 4 threads per 34-byte block, 8 weights each.  Blocks are only 2-byte
@@ -121,7 +132,7 @@ __global__ __launch_bounds__(256) void dequant_tq1_kernel(const uint8_t* __restr
 template <int DT>
 static hipError_t launch_dequant_dt(int codec, const void* w, int64_t nblocks, void* out,
                                     hipStream_t s) {
-    const int tpb = codec == Q8_0 ? 4 : 16;
+    const int tpb = codec == Q8_0 ? 4 : codec == Q4_K ? (DT == F32 ? 64 : 32) : 16;
     const int64_t threads = nblocks * tpb;
     const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
     switch (codec) {
