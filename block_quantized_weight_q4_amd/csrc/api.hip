@@ -59,10 +59,22 @@ kq_status check_weights(int t, const void* w, int64_t n, int64_t k, int64_t& row
     return KQ_OK;
 }
 
+// Bounds of the product kernels: a dispatch counts its work-items per
+// dimension in 32 bits (at most 32 threads per weight row), and offsets inside
+// one weight row, or a few rows of one tile, are 32-bit.
+constexpr int64_t kMaxN = (int64_t)1 << 26, kMaxK = (int64_t)1 << 24;
+
+kq_status check_product_size(int64_t n, int64_t k) {
+    if (n > kMaxN) return fail(KQ_ERR_INVALID_ARG, "n exceeds 2^26 weight rows");
+    if (k > kMaxK) return fail(KQ_ERR_INVALID_ARG, "k exceeds 2^24 columns");
+    return KQ_OK;
+}
+
 kq_status check_product(kq_type t, const void* w, int64_t n, int64_t k, const void* x,
                         kq_dtype x_dt, int64_t m, void* y, kq_dtype y_dt, int64_t& row_bytes) {
     kq_status st = check_weights(t, w, n, k, row_bytes);
     if (st) return st;
+    if ((st = check_product_size(n, k))) return st;
     if (!valid_dt(x_dt) || !valid_dt(y_dt)) return fail(KQ_ERR_UNSUPPORTED, "unknown dtype");
     if (m <= 0) return fail(KQ_ERR_INVALID_ARG, "m must be positive");
     if (!x || !y) return fail(KQ_ERR_INVALID_ARG, "null activation or output pointer");
@@ -219,6 +231,7 @@ static kq_status check_expert_call(kq_type t, const void* w, const void* w2, int
                                    size_t workspace_bytes, int64_t n_out, int64_t& row_bytes) {
     kq_status st = check_weights(t, w, n, k, row_bytes);
     if (st) return st;
+    if ((st = check_product_size(n, k))) return st;
     if (w2 && !aligned(w2, 16)) return fail(KQ_ERR_INVALID_ARG, "weights must be 16-byte aligned");
     if (!valid_dt(x_dt) || !valid_dt(y_dt)) return fail(KQ_ERR_UNSUPPORTED, "unknown dtype");
     st = check_routing(ids, n_tokens, top_k, n_experts, workspace, workspace_bytes, n_out);

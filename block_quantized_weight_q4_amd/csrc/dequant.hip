@@ -133,20 +133,25 @@ template <int DT>
 static hipError_t launch_dequant_dt(int codec, const void* w, int64_t nblocks, void* out,
                                     hipStream_t s) {
     const int tpb = codec == Q8_0 ? 4 : codec == Q4_K ? (DT == F32 ? 64 : 32) : 16;
-    const int64_t threads = nblocks * tpb;
-    const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
-    switch (codec) {
-    case Q4_K:
-        hipLaunchKernelGGL(dequant_q4k_kernel<DT>, grid, block, 0, s, (const uint8_t*)w, out, nblocks);
-        break;
-    case Q8_0:
-        hipLaunchKernelGGL(dequant_q8_0_kernel<DT>, grid, block, 0, s, (const uint8_t*)w, out, nblocks);
-        break;
-    default:
-        hipLaunchKernelGGL(dequant_tq1_kernel<DT>, grid, block, 0, s, (const uint8_t*)w, out, nblocks);
-        break;
+    const int64_t bbytes = codec == Q8_0 ? 34 : codec == Q4_K ? 144 : 28;
+    const int64_t obytes = (codec == Q8_0 ? 32 : codec == Q4_K ? 256 : 128) * (DT == F32 ? 4 : 2);
+    // a dispatch counts its work-items in 32 bits: matrices past 2^31 threads
+    // go in pieces
+    const int64_t piece = ((int64_t)1 << 31) / tpb;
+    for (int64_t b0 = 0; b0 < nblocks; b0 += piece) {
+        const int64_t nb = nblocks - b0 < piece ? nblocks - b0 : piece;
+        const uint8_t* wp = (const uint8_t*)w + b0 * bbytes;
+        void* op = (uint8_t*)out + b0 * obytes;
+        const dim3 grid((unsigned)((nb * tpb + 255) / 256)), block(256);
+        switch (codec) {
+        case Q4_K: hipLaunchKernelGGL(dequant_q4k_kernel<DT>, grid, block, 0, s, wp, op, nb); break;
+        case Q8_0: hipLaunchKernelGGL(dequant_q8_0_kernel<DT>, grid, block, 0, s, wp, op, nb); break;
+        default: hipLaunchKernelGGL(dequant_tq1_kernel<DT>, grid, block, 0, s, wp, op, nb); break;
+        }
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
     }
-    return hipGetLastError();
+    return hipSuccess;
 }
 
 hipError_t launch_dequant(int codec, const void* w, int64_t rows, int64_t k, void* out, int out_dt,

@@ -98,11 +98,12 @@ __global__ __launch_bounds__(64 * W) void mmv2_q4k_f16_kernel(SkinnyArgs a) {
     const int bufbytes = a.red_off / S;       // bytes of one buffer
     float* red = (float*)(smem + a.red_off);
 
-    // Per-lane byte offsets of this wave's weight pieces inside a chunk:
-    // piece p = 64*i + lane -> matrix m, row r, piece q of the row's chunk.
+    // Per-lane byte offsets of this wave's weight pieces inside a chunk,
+    // counted from the tile's first row (so they stay small for any matrix
+    // size): piece p = 64*i + lane -> matrix m, row r, piece q of the row's chunk.
     const uint8_t* wbase[NM];
 #pragma unroll
-    for (int m = 0; m < NM; ++m) wbase[m] = (GLU && m ? a.w2 : a.w) + expert * a.expert_stride;
+    for (int m = 0; m < NM; ++m) wbase[m] = (GLU && m ? a.w2 : a.w) + expert * a.expert_stride + n0 * a.row_bytes;
     uint32_t woff[WL_PER_WAVE], wq16[WL_PER_WAVE];
     int wmat[WL_PER_WAVE];
 #pragma unroll
@@ -115,7 +116,7 @@ __global__ __launch_bounds__(64 * W) void mmv2_q4k_f16_kernel(SkinnyArgs a) {
         if (n >= a.n) n = a.n - 1;
         wmat[j] = m < NM ? m : 0;
         wq16[j] = 16u * (uint32_t)q;
-        woff[j] = (uint32_t)(n * a.row_bytes) + wq16[j];
+        woff[j] = (uint32_t)((n - n0) * a.row_bytes) + wq16[j];
     }
     // activation row pointers of the tile (scalar per row)
     auto xrow_ptr = [&](int r) -> const uint8_t* {

@@ -99,6 +99,8 @@ int64_t kq_row_bytes(kq_type t, int64_t k);
  *
  * Each value is the exact decoded weight rounded once to binary32 (ties to
  * even); fp16/bf16 outputs round that binary32 value again (ties to even).
+ * Any size that fits in memory is accepted (large matrices are decoded by
+ * several launches on the stream).
  * Errors: rows <= 0, k not a positive multiple of QK, null or misaligned
  * pointers, overlapping w/out -> KQ_ERR_INVALID_ARG.
  */
@@ -118,8 +120,8 @@ kq_status kq_dequantize(kq_type t, const void* w, int64_t rows, int64_t k, void*
  * y[i, j] = sum_c x[i, c] * w[j, c], accumulated in fp32 and rounded once to
  * y_dt.  kq_qmv is the decode form (1 <= m <= 16, weights streamed once);
  * kq_qmm takes any m >= 1 and picks the decode form itself for small m.
- * Errors: n, k or m <= 0, k % QK != 0, m > 16 for kq_qmv, null or misaligned
- * pointers, y overlapping w or x -> KQ_ERR_INVALID_ARG.
+ * Errors: n, k or m <= 0, k % QK != 0, n > 2^26, k > 2^24, m > 16 for kq_qmv,
+ * null or misaligned pointers, y overlapping w or x -> KQ_ERR_INVALID_ARG.
  */
 kq_status kq_qmv(kq_type t, const void* w, int64_t n, int64_t k, const void* x, kq_dtype x_dt,
                  int64_t m, void* y, kq_dtype y_dt, void* stream);
@@ -194,8 +196,8 @@ kq_status kq_moe_route(const uint32_t* ids, int64_t n_tokens, int64_t top_k, int
  * serves.  A row with an id >= n_experts reads no weights and is written as
  * NaN (for the mixed form: that token's output row).
  * Errors: zero or negative sizes, top_k outside 1..n_experts,
- * n_tokens*top_k > INT32_MAX, k % QK != 0, expert_stride smaller than one
- * expert's bytes, null/misaligned pointers, y overlapping its inputs or the
+ * n_tokens*top_k > INT32_MAX, k % QK != 0, n > 2^26, k > 2^24, expert_stride
+ * smaller than one expert's bytes, null/misaligned pointers, y overlapping its inputs or the
  * workspace -> KQ_ERR_INVALID_ARG; workspace too small -> KQ_ERR_WORKSPACE.
  */
 kq_status kq_qmm_id(kq_type t, const void* w, int64_t n_experts, int64_t n, int64_t k,

@@ -98,6 +98,11 @@ def test_validation_rejects_before_launch(kq):
     assert _call_qmv(L, **{**ok, "t": 9}) == 2            # unknown type
     assert _call_qmv(L, **{**ok, "xdt": 7}) == 2          # unknown dtype
     assert kq.kq_last_error() == "unknown dtype"
+    big = dict(w=base, x=base + (1 << 36), y=base + (2 << 36))
+    assert _call_qmv(L, **{**big, "n": 2**26 + 1}) == 1   # launch geometry bound on n
+    assert kq.kq_last_error() == "n exceeds 2^26 weight rows"
+    assert _call_qmv(L, **{**big, "k": 2**24 + 256}) == 1  # bound on k
+    assert kq.kq_last_error() == "k exceeds 2^24 columns"
 
 
 def test_expert_validation(kq):
@@ -122,6 +127,7 @@ def test_expert_validation(kq):
     assert call(layout=5) == 1
     assert call(wsb=16) == 3                  # workspace too small
     assert call(T=2**31 // 2 + 1) == 1        # rows > INT32_MAX
+    assert call(n=2**26 + 1, stride=(2**26 + 1) * 144) == 1  # launch geometry bound on n
     assert call(y=P(base + (1 << 32) + 64)) == 1  # output overlaps x
     assert L.kq_moe_glu(0, w, w, 8, 64, 256, 64 * 144, x, 1, ids, 4, 2, 9, y, 1, ws, 1 << 20,
                         None) == 2            # unknown activation

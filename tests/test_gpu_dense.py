@@ -264,3 +264,66 @@ def test_errors_do_not_launch(kq):
         kq.kq_qmm("q4_k", w, 4, 100, x, 1, y)   # k not a multiple of 256
     with pytest.raises(KQError):
         kq.kq_qmm("q4_k", w, 4, 256, x, 0, y)   # empty batch
+
+
+# ---------------------------------------------------------------- past 4 GiB
+def _big_rows(kind, k, seed, min_bytes=2**32 + 2**28, base_rows=4096):
+    """A weight matrix of more than min_bytes on the device whose row r is row
+    r % base_rows of a small seeded matrix, so that the oracle needs only the
+    small one.  Returns (small host matrix, device matrix, n)."""
+    rb = synth.row_bytes(kind, k)
+    reps = -(-min_bytes // (base_rows * rb))
+    w = synth.weight_blocks(kind, _rng(seed), base_rows, k)
+    wd = to_dev(w).reshape(-1).repeat(reps)
+    return w, wd, base_rows * reps
+
+
+def _far_rows(kind, k, n, npts, seed):
+    """Sampled weight rows, most of them past byte offset 2**32."""
+    first = -(-2**32 // synth.row_bytes(kind, k))
+    rng = np.random.default_rng(seed)
+    return np.concatenate([[n - 1, first, first - 1, 0], rng.integers(first, n, npts),
+                           rng.integers(0, n, 16)])
+
+
+@pytest.mark.parametrize("kind,fn,m,x_dt", [("q4_k", "kq_qmv", 1, "f16"),
+                                            ("q4_k", "kq_qmv", 5, "f32"),
+                                            ("q8_0", "kq_qmv", 1, "f16"),
+                                            ("tq1_g128", "kq_qmv", 1, "f16"),
+                                            ("q4_k", "kq_qmm", 64, "bf16"),
+                                            ("q8_0", "kq_qmm", 40, "f16"),
+                                            ("tq1_g128", "kq_qmm", 40, "f16")])
+def test_weights_past_4gib(kq, kind, fn, m, x_dt):
+    """Weight byte offsets beyond 32 bits: rows past 4 GiB are read where
+    they are by every product kernel."""
+    k = 2048
+    w, wd, n = _big_rows(kind, k, 40)
+    _say("past 4 GiB", kind, fn, m, x_dt, n, k)
+    x = synth.activations(_rng(41), (m, k), x_dt)
+    y = empty((m, n), "f32")
+    getattr(kq, fn)(kind, wd, n, k, to_dev(x, x_dt), m, y)
+    pn = _far_rows(kind, k, n, 200, 42)
+    pm = np.random.default_rng(43).integers(0, m, pn.size)
+    pm[:2] = [m - 1, 0]
+    got = to_f64(y[torch.from_numpy(pm).to(y.device), torch.from_numpy(pn).to(y.device)])
+    del y, wd
+    torch.cuda.empty_cache()
+    ref, s = oracle.qmm_points(kind, w, 4096, k, x, x_dt, m, pm, pn % 4096)
+    check_tol(got, ref, s, TAU[x_dt], f"{fn} {kind} past 4 GiB")
+
+
+@pytest.mark.parametrize("kind", ["q4_k", "tq1_g128"])
+def test_dequant_past_4gib(kq, kind):
+    """Dequantization of matrices past 4 GiB, bit-exact on sampled rows.  The
+    TQ1 matrix holds more than 2^27 blocks, so it takes more than one launch."""
+    k = 2048
+    w, wd, n = _big_rows(kind, k, 44)
+    _say("dequant past 4 GiB", kind, n, k)
+    out = empty((n, k), "f16")
+    kq.kq_dequantize(kind, wd, n, k, out)
+    pn = _far_rows(kind, k, n, 64, 45)
+    got = bits(out[torch.from_numpy(pn).to(out.device)])
+    del out, wd
+    torch.cuda.empty_cache()
+    ref = oracle.dequant_as(kind, w, 4096, k, "f16")
+    assert np.array_equal(got, ref[pn % 4096])
