@@ -57,6 +57,7 @@ hipError_t launch_skinny(int codec, int x_dt, bool glu, const SkinnyArgs& a, int
 hipError_t launch_mmv2_q4k(bool glu, const SkinnyArgs& a, int64_t grid_tiles, hipStream_t s);
 bool mmv3_fits(int64_t k);
 hipError_t launch_mmv3_q4k(const SkinnyArgs& a, hipStream_t s);
+hipError_t launch_mmv3m_q4k(const SkinnyArgs& a, hipStream_t s);
 hipError_t launch_moe_mm(bool glu, int x_dt, const SkinnyArgs& a, int64_t grid_tiles,
                          hipStream_t s);
 hipError_t launch_row_exp(const float* x, int64_t rows, int64_t k, int32_t* e, hipStream_t s);

@@ -256,10 +256,12 @@ hipError_t launch_skinny(int codec, int x_dt, bool glu, const SkinnyArgs& a, int
         }
         return launch_moe_mm(glu, x_dt, b, grid_tiles, s);
     }
-    // one dense fp16 activation row: unscaled nibbles on the matrix cores,
-    // scales applied to the fp32 sub-block sums (mmv3.hip)
+    // up to four dense fp16 activation rows: unscaled nibbles on the matrix
+    // cores, scales applied to the fp32 sub-block sums (mmv3.hip)
     if (codec == Q4_K && x_dt == F16 && !a.ws && !glu && a.m == 1 && mmv3_fits(a.k))
         return launch_mmv3_q4k(a, s);
+    if (codec == Q4_K && x_dt == F16 && !a.ws && !glu && a.m <= 4)
+        return launch_mmv3m_q4k(a, s);
     if (codec == Q4_K && x_dt == F16 && (a.ws ? a.rows_cap <= 16 : a.m <= 16))
         return launch_mmv2_q4k(glu, a, grid_tiles, s);
     // TQ1 decode GEMV of one fp16 activation row: table-decoded MFMA operands

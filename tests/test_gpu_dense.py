@@ -129,36 +129,38 @@ def test_qmv_small(kq, kind, x_dt, m):
                   out_dt=y_dt if y_dt != "f32" and x_dt == "f32" else None)
 
 
+@pytest.mark.parametrize("m", [1, 2, 3, 4])
 @pytest.mark.parametrize("n,nsb", [(1, 1), (67, 5), (200, 16), (33, 17), (48, 56), (17, 68)])
-def test_qmv_q4k_one_row_shapes(kq, n, nsb):
-    """One fp16 activation row against Q4_K (the unscaled-nibble kernel):
-    chunks of four and eight super-blocks with ragged last chunks, ragged
-    row tiles, and a row long enough to be rearranged in two passes."""
+def test_qmv_q4k_few_rows_shapes(kq, m, n, nsb):
+    """One to four fp16 activation rows against Q4_K (the unscaled-nibble
+    kernels): chunks of four and eight super-blocks with ragged last chunks,
+    ragged row tiles, and a row long enough to be rearranged in two passes."""
     k = 256 * nsb
-    rng = _rng(2600 + nsb)
+    rng = _rng(2600 + 10 * nsb + m)
     w = synth.q4k_blocks(rng, n, k)
-    x = synth.activations(rng, (1, k), "f16")
-    ref, s = oracle.qmm("q4_k", w, n, k, x, "f16", 1)
+    x = synth.activations(rng, (m, k), "f16")
+    ref, s = oracle.qmm("q4_k", w, n, k, x, "f16", m)
     for y_dt in ("f32", "f16", "bf16"):
-        _say("qmv q4k one row", n, k, y_dt)
-        got = _run(kq, "kq_qmv", "q4_k", w, n, k, x, "f16", 1, y_dt)
-        check_tol(got, ref, s, TAU["f16"], f"qmv q4k m=1 {n}x{k} y={y_dt}",
+        _say("qmv q4k few rows", m, n, k, y_dt)
+        got = _run(kq, "kq_qmv", "q4_k", w, n, k, x, "f16", m, y_dt)
+        check_tol(got, ref, s, TAU["f16"], f"qmv q4k m={m} {n}x{k} y={y_dt}",
                   out_dt=y_dt if y_dt != "f32" else None)
 
 
+@pytest.mark.parametrize("m", [1, 3])
 @pytest.mark.parametrize("scale", [2.0**-20, 1.0, 6.0e4])
-def test_qmv_q4k_one_row_activation_range(kq, scale):
+def test_qmv_q4k_few_rows_activation_range(kq, m, scale):
     """Activations from fp16 subnormals to near the fp16 maximum: the
     sub-block sums and the scaled products stay within the bound."""
     n, k = 96, 4096
-    rng = _rng(2700)
+    rng = _rng(2700 + m)
     w = synth.q4k_blocks(rng, n, k)
-    xf = rng.uniform(-1.0, 1.0, size=(1, k)).astype(np.float32) * np.float32(scale)
+    xf = rng.uniform(-1.0, 1.0, size=(m, k)).astype(np.float32) * np.float32(scale)
     x = xf.astype(np.float16).view(np.uint16)
-    _say("qmv q4k one row range", scale)
-    got = _run(kq, "kq_qmv", "q4_k", w, n, k, x, "f16", 1, "f32")
-    ref, s = oracle.qmm("q4_k", w, n, k, x, "f16", 1)
-    check_tol(got, ref, s, TAU["f16"], f"qmv q4k m=1 x scale {scale}")
+    _say("qmv q4k few rows range", m, scale)
+    got = _run(kq, "kq_qmv", "q4_k", w, n, k, x, "f16", m, "f32")
+    ref, s = oracle.qmm("q4_k", w, n, k, x, "f16", m)
+    check_tol(got, ref, s, TAU["f16"], f"qmv q4k m={m} x scale {scale}")
 
 
 @pytest.mark.parametrize("kind", KINDS)
