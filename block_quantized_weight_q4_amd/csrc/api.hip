@@ -266,7 +266,7 @@ kq_status kq_qmm_id(kq_type t, const void* w, int64_t n_experts, int64_t n, int6
                     const uint32_t* ids, int64_t n_tokens, int64_t top_k, const float* scores,
                     void* y, kq_dtype y_dt, void* workspace, size_t workspace_bytes,
                     void* stream) {
-    const bool reuse = (x_layout & KQ_REUSE_SCHEDULE) != 0 && scores;
+    const bool reuse = (x_layout & KQ_REUSE_SCHEDULE) != 0 && scores && n_tokens > 1;
     x_layout &= ~KQ_REUSE_SCHEDULE;
     if (x_layout != KQ_LAYOUT_SHARED && x_layout != KQ_LAYOUT_SLOTTED)
         return fail(KQ_ERR_INVALID_ARG, "unknown x layout");
@@ -279,6 +279,25 @@ kq_status kq_qmm_id(kq_type t, const void* w, int64_t n_experts, int64_t n, int6
                                      workspace_bytes, scores ? n : 0, row_bytes);
     if (st) return st;
     hipStream_t s = (hipStream_t)stream;
+    // one token, mixed: the slots are summed as their expert rows stream,
+    // with no schedule and no slot rows
+    if (scores && n_tokens == 1 && t == KQ_Q4_K && (x_dt == KQ_F16 || x_dt == KQ_F32)) {
+        kq::DownMixArgs d{};
+        d.w = (const uint8_t*)w;
+        d.expert_stride = expert_stride;
+        d.row_bytes = row_bytes;
+        d.n = n;
+        d.k = k;
+        d.x = x;
+        d.slotted = x_layout == KQ_LAYOUT_SLOTTED;
+        d.ids = ids;
+        d.scores = scores;
+        d.n_experts = n_experts;
+        d.top_k = top_k;
+        d.y = y;
+        d.y_dt = y_dt;
+        return launched(kq::launch_down_mix1(d, x_dt == KQ_F32, s));
+    }
     const kq::MoeLayout L = kq::moe_layout(n_experts, n_tokens, top_k, scores ? n : 0);
     int32_t* ws = (int32_t*)workspace;
     // the unmixed form's rows with an invalid id are poisoned by the route;
@@ -334,9 +353,20 @@ kq_status kq_moe_glu(kq_type t, const void* gate_w, const void* up_w, int64_t n_
     hipStream_t s = (hipStream_t)stream;
     const kq::MoeLayout L = kq::moe_layout(n_experts, n_tokens, top_k, 0);
     int32_t* ws = (int32_t*)workspace;
-    hipError_t e = kq::launch_route(ids, L.rows, n_experts, L, ws, s, h, n, h_dt);
-    if (e != hipSuccess) return launched(e);
     kq::SkinnyArgs a{};
+    // one token with fp16 activations: each grid row is one slot, whose
+    // expert id is read directly (no schedule)
+    const bool direct = n_tokens == 1 && t == KQ_Q4_K && x_dt == KQ_F16;
+    if (direct) {
+        a.direct = 1;
+        a.ids = ids;
+        a.n_experts = n_experts;
+        a.m = 1;
+    } else {
+        hipError_t e = kq::launch_route(ids, L.rows, n_experts, L, ws, s, h, n, h_dt);
+        if (e != hipSuccess) return launched(e);
+        a.ws = ws;
+    }
     a.w = (const uint8_t*)gate_w;
     a.w2 = (const uint8_t*)up_w;
     a.row_bytes = row_bytes;
@@ -348,7 +378,6 @@ kq_status kq_moe_glu(kq_type t, const void* gate_w, const void* up_w, int64_t n_
     a.top_k = top_k;
     a.shared_x = 1;
     a.one_x_row = n_tokens == 1;
-    a.ws = ws;
     a.tiles_off = L.tiles_off;
     a.perm_off = L.perm_off;
     a.xexp_off = L.xexp_off;
@@ -356,7 +385,7 @@ kq_status kq_moe_glu(kq_type t, const void* gate_w, const void* up_w, int64_t n_
     a.y = h;
     a.y_dt = h_dt;
     a.y_row = n;
-    return launched(kq::launch_skinny(t, x_dt, true, a, L.max_tiles, s));
+    return launched(kq::launch_skinny(t, x_dt, true, a, direct ? L.rows : L.max_tiles, s));
 }
 
 }  // extern "C"

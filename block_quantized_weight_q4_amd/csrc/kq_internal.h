@@ -36,6 +36,11 @@ struct SkinnyArgs {
     int shared_x;          // routed: x row = r / top_k (else r)
     int one_x_row;         // routed: all rows read one activation row (one token, shared x)
     const int32_t* ws;     // routed: workspace (schedule); null for dense
+    // single-token routing without a schedule: grid row y is slot y, whose
+    // expert is ids[y] (an id >= n_experts poisons the slot's output)
+    int direct;
+    const uint32_t* ids;
+    int64_t n_experts;
     int64_t tiles_off, perm_off;
     int64_t xexp_off;      // routed, fp32 activations: word offset of row exponents
     int xexp_local;        // ... or found by each workgroup for its own rows
@@ -49,6 +54,22 @@ struct SkinnyArgs {
     int xstride;           // elements (or bytes) between staged activation rows
     int red_off;           // byte offset of a second LDS region
 };
+
+// Single-token MoE down projection with the slot mix fused in (moe_dec.hip).
+struct DownMixArgs {
+    const uint8_t* w;       // experts' weights
+    int64_t expert_stride;  // bytes between experts
+    int64_t row_bytes;
+    int64_t n, k;
+    const void* x;          // activations: [k] (shared) or [top_k, k] (slotted)
+    int slotted;
+    const uint32_t* ids;    // [top_k]
+    const float* scores;    // [top_k]
+    int64_t n_experts, top_k;
+    void* y;                // [n]
+    int y_dt;
+};
+hipError_t launch_down_mix1(const DownMixArgs& a, bool x_f32, hipStream_t s);
 
 hipError_t launch_dequant(int codec, const void* w, int64_t rows, int64_t k, void* out, int out_dt,
                           hipStream_t s);

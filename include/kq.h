@@ -66,7 +66,9 @@ typedef enum kq_status {
  * unmodified since (the gate/up -> down sequence of one MoE layer).
  * mlx-native "quantized_matmul_id_ggml.rs", the scratch reused across the
  * expert dispatches of a layer.  Ignored when scores is NULL: that form's
- * rows with an invalid id are written while the schedule is built. */
+ * rows with an invalid id are written while the schedule is built.  Also
+ * ignored for a single token (n_tokens == 1): its calls read the ids
+ * directly, and a kq_moe_glu call for one token may leave no schedule. */
 enum { KQ_LAYOUT_SHARED = 0, KQ_LAYOUT_SLOTTED = 1, KQ_REUSE_SCHEDULE = 0x100 };
 
 /* GLU activations of kq_moe_glu: h = act(gate) * up.  silu(z) = z / (1 + e^-z).

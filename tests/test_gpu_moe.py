@@ -77,7 +77,7 @@ def _moe_case(kind, E, n, k, T, top_k, seed):
 @pytest.mark.parametrize("kind", ["q4_k", "q8_0", "tq1_g128"])
 @pytest.mark.parametrize("layout", [0, 1])
 @pytest.mark.parametrize("mixed", [False, True])
-@pytest.mark.parametrize("E,T,top_k", [(8, 5, 3), (4, 70, 4)])
+@pytest.mark.parametrize("E,T,top_k", [(8, 1, 8), (8, 5, 3), (4, 70, 4)])
 def test_qmm_id_small(kq, kind, layout, mixed, E, T, top_k):
     n, k = 96, {"q4_k": 512, "q8_0": 160, "tq1_g128": 384}[kind]
     rng, w, stride, ids, scores = _moe_case(kind, E, n, k, T, top_k, 40 + T)
@@ -151,26 +151,55 @@ def test_reused_schedule_matches_rebuilt(kq, T):
     assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
 
 
-def test_qmm_id_invalid_ids_poison(kq):
+@pytest.mark.parametrize("x_dt", ["f16", "f32"])
+def test_qmm_id_invalid_ids_poison(kq, x_dt):
     E, n, k, T, top_k = 6, 64, 256, 4, 2
     rng, w, stride, ids, scores = _moe_case("q4_k", E, n, k, T, top_k, 77)
     ids = ids.copy()
     ids[1, 1] = E       # out of range
     ids[3, 0] = 1 << 30
-    x = synth.activations(rng, (T, k), "f16")
+    x = synth.activations(rng, (T, k), x_dt)
     for mixed in (False, True):
         y = empty((T if mixed else T * top_k, n), "f16")
         ws = _ws(kq, E, T, top_k, n if mixed else 0)
-        kq.kq_qmm_id("q4_k", to_dev(w), E, n, k, stride, to_dev(x, "f16"), 0, to_dev(ids), T,
+        kq.kq_qmm_id("q4_k", to_dev(w), E, n, k, stride, to_dev(x, x_dt), 0, to_dev(ids), T,
                      top_k, to_dev(scores) if mixed else None, y, ws)
         torch.cuda.synchronize()
         got = to_f64(y)
-        ref, s = oracle.qmm_id("q4_k", w, E, n, k, stride, x, "f16", False, ids, T, top_k,
+        ref, s = oracle.qmm_id("q4_k", w, E, n, k, stride, x, x_dt, False, ids, T, top_k,
                                scores if mixed else None)
         bad = np.isnan(ref).all(axis=1)
         assert bad.sum() == 2
         assert np.isnan(got[bad]).all()
-        check_tol(got[~bad], ref[~bad], s[~bad], TAU["f16"], "valid rows")
+        check_tol(got[~bad], ref[~bad], s[~bad], TAU[x_dt], "valid rows",
+                  out_dt="f16" if x_dt == "f32" else None)
+
+
+@pytest.mark.parametrize("x_dt", ["f16", "f32"])
+@pytest.mark.parametrize("layout", [0, 1])
+def test_single_token_invalid_id_poisons(kq, x_dt, layout):
+    """One token with an invalid id among its slots: the mixed output is
+    NaN, the GLU slot row of that id is NaN and the other slots are valid."""
+    E, n, k, top_k = 6, 64, 512, 3
+    rng, w, stride, ids, scores = _moe_case("q4_k", E, n, k, 1, top_k, 78)
+    ids = ids.copy()
+    ids[0, 1] = E + 1
+    x_rows = 1 if layout == 0 else top_k
+    x = synth.activations(rng, (x_rows, k), x_dt)
+    _say("single token poison", x_dt, layout)
+    y = empty((1, n), "f32")
+    ws = _ws(kq, E, 1, top_k, n)
+    kq.kq_qmm_id("q4_k", to_dev(w), E, n, k, stride, to_dev(x, x_dt), layout, to_dev(ids), 1,
+                 top_k, to_dev(scores), y, ws)
+    torch.cuda.synchronize()
+    assert np.isnan(to_f64(y)).all()
+    if layout == 0:
+        h = empty((1, top_k, n), "f32")
+        kq.kq_moe_glu("q4_k", to_dev(w), to_dev(w), E, n, k, stride, to_dev(x, x_dt), to_dev(ids),
+                      1, top_k, h, ws)
+        torch.cuda.synchronize()
+        got = to_f64(h)[0]
+        assert np.isnan(got[1]).all() and not np.isnan(got[[0, 2]]).any()
 
 
 def _check_glu(h, ref, tau, h_dt, what):
@@ -196,8 +225,9 @@ def _check_glu(h, ref, tau, h_dt, what):
 @pytest.mark.parametrize("kind", ["q4_k", "q8_0", "tq1_g128"])
 @pytest.mark.parametrize("h_dt", ["f16", "f32", "bf16"])
 @pytest.mark.parametrize("x_dt", ["f16", "f32"])
-def test_moe_glu_small(kq, kind, h_dt, x_dt):
-    E, n, k, T, top_k = 6, 80, {"q4_k": 512, "q8_0": 96, "tq1_g128": 256}[kind], 9, 3
+@pytest.mark.parametrize("T", [1, 9])
+def test_moe_glu_small(kq, kind, h_dt, x_dt, T):
+    E, n, k, top_k = 6, 80, {"q4_k": 512, "q8_0": 96, "tq1_g128": 256}[kind], 3
     rng = synth.rng_for(90)
     gate = synth.weight_blocks(kind, rng, E * n, k)
     up = synth.weight_blocks(kind, rng, E * n, k)
