@@ -325,9 +325,10 @@ def main():
     print(json.dumps(result))
 
 
-# sources that define the decode GEMV kernel; the committed counter figures
-# hold only while these are unchanged
-GEMV_SOURCES = ("mmv2.hip", "q4k_mfma.h", "kq_device.h", "kq_internal.h")
+# sources that define the decode GEMV kernels and their dispatch; the
+# committed counter figures hold only while these are unchanged
+GEMV_SOURCES = ("mmv2.hip", "mmv3.hip", "skinny.hip", "lds_dma.h", "q4k_mfma.h", "kq_device.h",
+                "kq_internal.h")
 
 
 def _kernel_sha():
@@ -343,7 +344,7 @@ def _traffic():
     by its plain-copy calibration factor, averaged over the six launches) from
     the committed counter summary, when it was taken on the current kernel
     sources; else None."""
-    path = os.path.join(PROFILE_DIR, "mmv2_q4k_gemv_14336x4096_counters.json")
+    path = os.path.join(PROFILE_DIR, "q4k_decode_gemv_counters.json")
     if not os.path.exists(path):
         return None
     try:
@@ -361,7 +362,8 @@ def roofline(rows):
         return None
     return {"bound": "hbm", "achieved": r["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(r["GB/s"] / HBM_PEAK_GBS, 4), "traffic": _traffic(),
-            "kernel": "mmv2_q4k_f16_kernel (kq_qmv, Q4_K decode GEMV)",
+            "kernel": "kq_qmv Q4_K decode GEMV: mmv3_q4k_f16_kernel (batch 1), mmv3m_q4k_f16_kernel "
+                      "(batch 4), mmv2_q4k_f16_kernel (batch 8)",
             "bytes_per_launch": r.get("bytes_per_launch"), "us_per_launch": r.get("us_per_launch")}
 
 

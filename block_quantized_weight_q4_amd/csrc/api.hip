@@ -358,7 +358,6 @@ kq_status kq_moe_glu(kq_type t, const void* gate_w, const void* up_w, int64_t n_
     // expert id is read directly (no schedule)
     const bool direct = n_tokens == 1 && t == KQ_Q4_K && x_dt == KQ_F16;
     if (direct) {
-        a.direct = 1;
         a.ids = ids;
         a.n_experts = n_experts;
         a.m = 1;
@@ -385,7 +384,8 @@ kq_status kq_moe_glu(kq_type t, const void* gate_w, const void* up_w, int64_t n_
     a.y = h;
     a.y_dt = h_dt;
     a.y_row = n;
-    return launched(kq::launch_skinny(t, x_dt, true, a, direct ? L.rows : L.max_tiles, s));
+    if (direct) return launched(kq::launch_moe_glu1(a, s));
+    return launched(kq::launch_skinny(t, x_dt, true, a, L.max_tiles, s));
 }
 
 }  // extern "C"

@@ -36,9 +36,8 @@ struct SkinnyArgs {
     int shared_x;          // routed: x row = r / top_k (else r)
     int one_x_row;         // routed: all rows read one activation row (one token, shared x)
     const int32_t* ws;     // routed: workspace (schedule); null for dense
-    // single-token routing without a schedule: grid row y is slot y, whose
+    // single-token gate/up without a schedule: grid row y is slot y, whose
     // expert is ids[y] (an id >= n_experts poisons the slot's output)
-    int direct;
     const uint32_t* ids;
     int64_t n_experts;
     int64_t tiles_off, perm_off;
@@ -70,6 +69,8 @@ struct DownMixArgs {
     int y_dt;
 };
 hipError_t launch_down_mix1(const DownMixArgs& a, bool x_f32, hipStream_t s);
+// Single-token gate/up with SiLU, expert ids read directly (moe_dec.hip).
+hipError_t launch_moe_glu1(const SkinnyArgs& a, hipStream_t s);
 
 hipError_t launch_dequant(int codec, const void* w, int64_t rows, int64_t k, void* out, int out_dt,
                           hipStream_t s);

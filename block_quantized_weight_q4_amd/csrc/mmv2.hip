@@ -52,18 +52,6 @@ __global__ __launch_bounds__(64 * W) void mmv2_q4k_f16_kernel(SkinnyArgs a) {
         row0 = tile[1];
         nrows = tile[2];
         perm = a.ws + a.perm_off;
-    } else if (a.direct) {
-        // one token: grid row y is slot y; an invalid expert id poisons the
-        // slot's output row
-        const uint32_t e = a.ids[blockIdx.y];
-        row0 = blockIdx.y;
-        nrows = 1;
-        if (e >= (uint64_t)a.n_experts) {
-            const int64_t n = n0 + (GLU ? 0 : 16 * (tid >> 4)) + (tid & 15);
-            if (tid < (GLU ? 16 : 16 * NM) && n < a.n) store_val(a.y, row0 * a.y_row + n, a.y_dt, __builtin_nanf(""));
-            return;
-        }
-        expert = e;
     } else {
         row0 = (int64_t)blockIdx.y * 16;
         nrows = a.m - row0 < 16 ? a.m - row0 : 16;
@@ -260,7 +248,7 @@ static_assert(lds_cfg2<2, 2, 2, 2>(16) <= kLdsMax && lds_cfg2<1, 4, 4, 2>(16) <=
 
 hipError_t launch_mmv2_q4k(bool glu, const SkinnyArgs& a, int64_t grid_tiles, hipStream_t s) {
     const int64_t rows_max = a.one_x_row ? 1 : a.ws ? (a.rows_cap < 16 ? a.rows_cap : 16) : a.m;
-    const int64_t tiles = (a.ws || a.direct) ? grid_tiles : (a.m + 15) / 16;
+    const int64_t tiles = a.ws ? grid_tiles : (a.m + 15) / 16;
     const int64_t nsb = a.k / 256;
     if (glu) launch_cfg2<2, true, 2, 2, 2>(a, rows_max, tiles, s);
     else if (nsb > 16 && lds_cfg2<1, 8, 8, 2>(rows_max) <= kLdsMax)

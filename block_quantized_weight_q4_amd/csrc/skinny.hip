@@ -258,14 +258,14 @@ hipError_t launch_skinny(int codec, int x_dt, bool glu, const SkinnyArgs& a, int
     }
     // up to four dense fp16 activation rows: unscaled nibbles on the matrix
     // cores, scales applied to the fp32 sub-block sums (mmv3.hip)
-    if (codec == Q4_K && x_dt == F16 && !a.ws && !a.direct && !glu && a.m == 1 && mmv3_fits(a.k))
+    if (codec == Q4_K && x_dt == F16 && !a.ws && !glu && a.m == 1 && mmv3_fits(a.k))
         return launch_mmv3_q4k(a, s);
-    if (codec == Q4_K && x_dt == F16 && !a.ws && !a.direct && !glu && a.m <= 4)
+    if (codec == Q4_K && x_dt == F16 && !a.ws && !glu && a.m <= 4)
         return launch_mmv3m_q4k(a, s);
     if (codec == Q4_K && x_dt == F16 && (a.ws ? a.rows_cap <= 16 : a.m <= 16))
         return launch_mmv2_q4k(glu, a, grid_tiles, s);
     // TQ1 decode GEMV of one fp16 activation row: table-decoded MFMA operands
-    if (codec == TQ1 && x_dt == F16 && !a.ws && !a.direct && !glu && a.m == 1 && tq1_mv_fits(a.k))
+    if (codec == TQ1 && x_dt == F16 && !a.ws && !glu && a.m == 1 && tq1_mv_fits(a.k))
         return launch_tq1_mv(a.w, a.n, a.k, (const uint16_t*)a.x, a.y, a.y_dt, s);
     int mb;
     int64_t tiles;
