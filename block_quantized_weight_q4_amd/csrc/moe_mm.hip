@@ -86,20 +86,32 @@ __global__ __launch_bounds__(64 * W) void moe_mm_kernel(SkinnyArgs a) {
         return a.shared_x ? xr / a.top_k : xr;
     };
 
-    // fp32 activations of small tiles: each wave finds the scale exponent of
-    // some of the tile's rows (the first chunk's barrier publishes them)
+    // per tile row: the activation row's element offset and, for fp32
+    // activations, its scale exponent (found here for small tiles, else
+    // from the pre-pass); published by the first chunk's barrier
+    __shared__ int64_t xoffs[kMoeTileRows];
     __shared__ int sexp[kMoeTileRows];
-    if (XF32 && a.xexp_local) {
-        for (int r = wave; r < nrows; r += W) {
-            const float* row = (const float*)a.x + x_row_of(r) * a.x_row;
-            float mx = 0.f;
-            for (int64_t c = 4 * lane; c < a.k; c += 256) {
-                const float4_t v = *(const float4_t*)(row + c);
-                mx = fmaxf(fmaxf(mx, fmaxf(fabsf(v[0]), fabsf(v[1]))), fmaxf(fabsf(v[2]), fabsf(v[3])));
-            }
+    for (int r = wave; r < nrows; r += W) {
+        const int64_t xr = x_row_of(r);
+        int ex = 0;
+        if (XF32) {
+            if (a.xexp_local) {
+                const float* row = (const float*)a.x + xr * a.x_row;
+                float mx = 0.f;
+                for (int64_t c = 4 * lane; c < a.k; c += 256) {
+                    const float4_t v = *(const float4_t*)(row + c);
+                    mx = fmaxf(fmaxf(mx, fmaxf(fabsf(v[0]), fabsf(v[1]))), fmaxf(fabsf(v[2]), fabsf(v[3])));
+                }
 #pragma unroll
-            for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-            if (lane == 0) sexp[r] = row_exponent(mx);
+                for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+                ex = row_exponent(mx);
+            } else {
+                ex = a.ws[a.xexp_off + xr];
+            }
+        }
+        if (lane == 0) {
+            xoffs[r] = xr * a.x_row;
+            sexp[r] = ex;
         }
     }
 
@@ -143,34 +155,35 @@ __global__ __launch_bounds__(64 * W) void moe_mm_kernel(SkinnyArgs a) {
     for (int c0 = 0; c0 < nsb; c0 += XC) {
         const int nch = nsb - c0 < XC ? nsb - c0 : XC;
         __syncthreads();  // every wave is done with the previous chunk
-        // ---- stage activation rows [c0, c0+nch) super-blocks
+        // ---- stage activation rows [c0, c0+nch) super-blocks: a wave per
+        // row, consecutive lanes on consecutive 16-byte pieces
         if (!XF32) {
             const int per_row = nch * 32;  // 16-byte pieces
-            for (int i = tid; i < nrows * per_row; i += 64 * W) {
-                const int r = i / per_row, q = i - r * per_row;
-                const int64_t xr = x_row_of(r);
-                const u32x4 v = *(const u32x4*)((const uint16_t*)a.x + xr * a.x_row + (int64_t)c0 * 256 + 8 * q);
-                *(u32x4*)&xh[r * XSTRIDE + 8 * q] = v;
+            for (int r = wave; r < nrows; r += W) {
+                const uint16_t* src = (const uint16_t*)a.x + xoffs[r] + (int64_t)c0 * 256;
+                for (int q = lane; q < per_row; q += 64)
+                    *(u32x4*)&xh[r * XSTRIDE + 8 * q] = *(const u32x4*)(src + 8 * q);
             }
         } else {
             const int per_row = nch * 64;  // 4-float pieces
-            for (int i = tid; i < nrows * per_row; i += 64 * W) {
-                const int r = i / per_row, q = i - r * per_row;
-                const int64_t xr = x_row_of(r);
-                const int ex = a.xexp_local ? sexp[r] : a.ws[a.xexp_off + xr];
-                const float4_t v = *(const float4_t*)((const float*)a.x + xr * a.x_row + (int64_t)c0 * 256 + 4 * q);
-                uint32_t hi[2], lo[2];
+            for (int r = wave; r < nrows; r += W) {
+                const float* src = (const float*)a.x + xoffs[r] + (int64_t)c0 * 256;
+                const int nex = -sexp[r];
+                for (int q = lane; q < per_row; q += 64) {
+                    const float4_t v = *(const float4_t*)(src + 4 * q);
+                    uint32_t hi[2], lo[2];
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const float s0 = ldexpf(v[2 * j], -ex), s1 = ldexpf(v[2 * j + 1], -ex);
-                    const uint32_t h0 = float_to_half_bits(s0), h1 = float_to_half_bits(s1);
-                    const uint32_t l0 = float_to_half_bits(s0 - half_bits_to_float(h0));
-                    const uint32_t l1 = float_to_half_bits(s1 - half_bits_to_float(h1));
-                    hi[j] = h0 | (h1 << 16);
-                    lo[j] = l0 | (l1 << 16);
+                    for (int j = 0; j < 2; ++j) {
+                        const float s0 = ldexpf(v[2 * j], nex), s1 = ldexpf(v[2 * j + 1], nex);
+                        const uint32_t h0 = float_to_half_bits(s0), h1 = float_to_half_bits(s1);
+                        const uint32_t l0 = float_to_half_bits(s0 - half_bits_to_float(h0));
+                        const uint32_t l1 = float_to_half_bits(s1 - half_bits_to_float(h1));
+                        hi[j] = h0 | (h1 << 16);
+                        lo[j] = l0 | (l1 << 16);
+                    }
+                    *(uint2*)&xh[r * XSTRIDE + 4 * q] = uint2{hi[0], hi[1]};
+                    *(uint2*)&xl[r * XSTRIDE + 4 * q] = uint2{lo[0], lo[1]};
                 }
-                *(uint2*)&xh[r * XSTRIDE + 4 * q] = uint2{hi[0], hi[1]};
-                *(uint2*)&xl[r * XSTRIDE + 4 * q] = uint2{lo[0], lo[1]};
             }
         }
         __syncthreads();
@@ -225,21 +238,18 @@ __global__ __launch_bounds__(64 * W) void moe_mm_kernel(SkinnyArgs a) {
             const int idx = 16 * mt + 4 * g + v;
             if (idx >= nrows) continue;
             const int64_t orow = perm[row0 + idx];
-            float sc = 1.f;
-            if (XF32) {
-                const int64_t xr = a.shared_x ? orow / a.top_k : orow;
-                sc = ldexpf(1.f, a.xexp_local ? sexp[idx] : a.ws[a.xexp_off + xr]);
-            }
+            // fp32 activations: the row's result scaled back by 2^e exactly
+            auto back = [&](float v) { return XF32 ? ldexpf(v, sexp[idx]) : v; };
             if (GLU) {
                 const int64_t n = n0 + 16 * wave + n_l;
                 if (n < a.n)
                     store_val(a.y, orow * a.y_row + n, a.y_dt,
-                              silu_fast(sc * acc[0][mt][v]) * (sc * acc[1][mt][v]));
+                              silu_fast(back(acc[0][mt][v])) * back(acc[1][mt][v]));
             } else {
 #pragma unroll
                 for (int b = 0; b < 2; ++b) {
                     const int64_t n = n0 + 16 * (2 * wave + b) + n_l;
-                    if (n < a.n) store_val(a.y, orow * a.y_row + n, a.y_dt, sc * acc[b][mt][v]);
+                    if (n < a.n) store_val(a.y, orow * a.y_row + n, a.y_dt, back(acc[b][mt][v]));
                 }
             }
         }
@@ -247,11 +257,11 @@ __global__ __launch_bounds__(64 * W) void moe_mm_kernel(SkinnyArgs a) {
 }
 
 // Staged activations: up to 32 rows (no more than the routing holds) of XC
-// super-blocks, fp16 (plus the lo part for fp32 activations), within 64 KB so
+// super-blocks, fp16 (plus the lo part for fp32 activations), within 76 KB so
 // that two workgroups share a CU.
 template <int W, bool GLU, bool XF32>
 static void launch_mm(SkinnyArgs a, int64_t grid_tiles, hipStream_t s) {
-    constexpr int64_t kBudget = 64 * 1024;
+    constexpr int64_t kBudget = 76 * 1024;
     constexpr int ROWS = GLU ? 16 * W : 32 * W;
     const int64_t nsb = a.k / 256;
     const int64_t parts = XF32 ? 2 : 1;
