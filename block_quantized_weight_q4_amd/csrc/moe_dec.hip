@@ -48,10 +48,23 @@ struct DownMixLayout {
     static_assert(TOTAL <= 160 * 1024, "LDS budget");
 };
 
+// Largest value over the wave: within each row of 16 lanes by DPP moves,
+// then across the four rows by reading one lane of each.
+template <int CTRL>
+__device__ __forceinline__ float dpp_max(float v) {
+    return __builtin_fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false)));
+}
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, o));
-    return v;
+    v = dpp_max<0xb1>(v);   // quad_perm 1,0,3,2
+    v = dpp_max<0x4e>(v);   // quad_perm 2,3,0,1
+    v = dpp_max<0x141>(v);  // row_half_mirror
+    v = dpp_max<0x140>(v);  // row_mirror
+    const int b = __builtin_bit_cast(int, v);
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
+    return __builtin_fmaxf(__builtin_fmaxf(r0, r1), __builtin_fmaxf(r2, r3));
 }
 
 }  // namespace
