@@ -299,7 +299,8 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const uint8_t* __restrict
     // Pipeline: LDS stage s%2 holds step s; while the MFMAs of step s run,
     // step s+1 (fetched an iteration earlier) is decoded into the other
     // stage, and step s+2 is fetched into the freed registers.  One barrier
-    // per step.
+    // per step.  (Fetching two steps ahead was measured no faster, for
+    // small grids as well.)
     auto step = [&](int s, Regs& R) {
         const int st = s & 1;
         u32x4 af[FM], bf[FN];
@@ -362,16 +363,18 @@ static void launch_tile(const void* w, int64_t n, int64_t k, const void* x, int6
 
 // Tile choice (eight waves, two per SIMD, measured on the prefill shapes):
 // 256 x 256 while the grid holds at least 1.5 workgroups per CU (256 CUs),
-// else 256 x 128 while it holds 0.75, else 128 x 128.  Larger tiles reuse
-// each decoded weight over more rows and each activation over more columns;
-// smaller ones keep the CUs busy when there are few tiles.
+// else 256 x 128 or 128 x 128 while it holds 0.75, else 64 x 128 (not for
+// TQ1, whose per-weight decoding needs the 128 rows of reuse).  Larger tiles
+// reuse each decoded weight over more rows and each activation over more
+// columns; smaller ones keep the CUs busy when there are few tiles.
 template <int C, int XDT>
 static void launch_c(const void* w, int64_t n, int64_t k, const void* x, int64_t m, void* y,
                      int y_dt, hipStream_t s) {
     auto tiles = [&](int64_t bm, int64_t bn) { return ((n + bn - 1) / bn) * ((m + bm - 1) / bm); };
     if (tiles(256, 256) >= 384) launch_tile<C, XDT, 256, 256, 8>(w, n, k, x, m, y, y_dt, s);
     else if (tiles(256, 128) >= 192) launch_tile<C, XDT, 256, 128, 8>(w, n, k, x, m, y, y_dt, s);
-    else launch_tile<C, XDT, 128, 128, 8>(w, n, k, x, m, y, y_dt, s);
+    else if (C == TQ1 || tiles(128, 128) >= 192) launch_tile<C, XDT, 128, 128, 8>(w, n, k, x, m, y, y_dt, s);
+    else launch_tile<C, XDT, 64, 128, 8>(w, n, k, x, m, y, y_dt, s);
 }
 
 hipError_t launch_gemm(int codec, int x_dt, const void* w, int64_t n, int64_t k, const void* x,
