@@ -163,6 +163,23 @@ def test_qmv_q4k_few_rows_activation_range(kq, m, scale):
     check_tol(got, ref, s, TAU["f16"], f"qmv q4k m={m} x scale {scale}")
 
 
+@pytest.mark.parametrize("n,nblk", [(1, 4), (45, 20), (70, 36), (16, 68)])
+def test_qmv_tq1_one_row_shapes(kq, n, nblk):
+    """One fp16 activation row against TQ1 (the table-decoded kernel, rows of
+    a multiple of four blocks): ragged last chunks of 16 blocks and ragged
+    row tiles."""
+    k = 128 * nblk
+    rng = _rng(2800 + nblk)
+    w = synth.weight_blocks("tq1_g128", rng, n, k)
+    x = synth.activations(rng, (1, k), "f16")
+    ref, s = oracle.qmm("tq1_g128", w, n, k, x, "f16", 1)
+    for y_dt in ("f32", "f16"):
+        _say("qmv tq1 one row", n, k, y_dt)
+        got = _run(kq, "kq_qmv", "tq1_g128", w, n, k, x, "f16", 1, y_dt)
+        check_tol(got, ref, s, TAU["f16"], f"qmv tq1 m=1 {n}x{k} y={y_dt}",
+                  out_dt=y_dt if y_dt != "f32" else None)
+
+
 @pytest.mark.parametrize("kind", KINDS)
 @pytest.mark.parametrize("m", [14, 15, 16])
 def test_qmv_long_rows_many_activations(kq, kind, m):
