@@ -5,40 +5,44 @@
 // the LUT23 GEMV section (decoding through a table instead of dividing each
 // byte by powers of three).
 //
-// Here a code byte c = d0 + 3 d1 + 9 (d2 + 3 d3 + 9 d4) is decoded through two
-// small tables, as the page splits it: c mod 9 gives the trits (d0-1, d1-1)
-// as an fp16 pair, c div 9 the trits (d2-1, d3-1, d4-1); together with three
-// zeros they are eight fp16 values, exactly one 16x16x32 MFMA operand slice.
-// The tables are 9 and 27 entries long, so lanes that read different entries
-// never share an LDS bank and lanes that read the same entry are served by
-// one broadcast.  The contraction order is permuted so that each lane group's eight
-// MFMA k-slots are the five columns of one code byte: the activations are
-// staged in LDS once per workgroup in the same 8-wide "slot" layout (columns
-// 5s..5s+4 of byte s, then zeros; the tail byte's slot holds columns
-// 125..127).  A block of 128 weights is 28 slots (25 code bytes, the tail,
-// and the two scale bytes, whose activation slots are zero), i.e. seven
-// MFMAs; the fp16 scale multiplies each block's fp32 result.  All products
-// (+-x or 0) are exact; accumulation is fp32.
+// Here a code byte c = d0 + 3 d1 + 9 d2 + 27 (d3 + 3 d4) is decoded through
+// two small tables: c mod 27 gives the trits (d0-1, d1-1, d2-1), c div 27 the
+// trits (d3-1, d4-1), each as an 8-byte entry of fp16 values padded with
+// zeros, so that the two entries side by side are exactly one 16x16x32 MFMA
+// operand slice of eight fp16 values [d0 d1 d2 0 d3 d4 0 0] and both reads
+// land in aligned register pairs.  The tables are 27 and 10 entries long, so
+// lanes that read different entries never share an LDS bank and lanes that
+// read the same entry are served by one broadcast.  The contraction order is
+// permuted so that each lane group's eight MFMA k-slots are the five columns
+// of one code byte: the activations are staged in LDS once per workgroup in
+// the same 8-wide "slot" layout (columns 5s..5s+4 of byte s at positions
+// 0 1 2 4 5, zeros elsewhere; the tail byte's slot holds columns 125..127).
+// A block of 128 weights is 28 slots (25 code bytes, the tail, and the two
+// scale bytes, whose activation slots are zero), i.e. seven MFMAs; the fp16
+// scale multiplies each block's fp32 result.  All products (+-x or 0) are
+// exact; accumulation is fp32.
 //
 // A workgroup owns 16 weight rows.  Their weights stream through LDS in
-// chunks of 16 blocks (coalesced global->LDS copies, double buffered); the W
-// waves take the blocks of a chunk in turn and combine their partial sums
-// through LDS at the end.  Each block issues all of its table and activation
-// reads before its first MFMA, so their LDS latency overlaps.
+// chunks of 8 or 16 blocks (coalesced global->LDS copies, double buffered);
+// the W waves take the blocks of a chunk in turn and combine their partial
+// sums through LDS at the end.  Each half block issues all of its table and
+// activation reads before its first MFMA, so their LDS latency overlaps.
 #include "kq_device.h"
 #include "kq_internal.h"
 #include "lds_dma.h"
+
+#include <type_traits>
 
 namespace kq {
 
 namespace {
 
 constexpr int kSlots = 28;            // MFMA slots per 128-weight block
-// LDS tables: 9 dwords (two trits) then, from byte 64, 32 8-byte entries
-// (three trits; entries past 26 serve the scale bytes, whose activations are
-// zero)
-constexpr int kLut3Off = 64;
-constexpr int kLutBytes = kLut3Off + 32 * 8;
+// LDS tables of 8-byte entries: c mod 27 (27 entries), then from byte 256
+// c div 27 (16 entries; those past 8 serve the scale bytes, whose activations
+// are zero)
+constexpr int kHiOff = 256;
+constexpr int kLutBytes = kHiOff + 16 * 8;
 
 __device__ __forceinline__ float4_t mfma_h(const u32x4& a, const u32x4& b, const float4_t& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a),
@@ -47,26 +51,41 @@ __device__ __forceinline__ float4_t mfma_h(const u32x4& a, const u32x4& b, const
 
 }  // namespace
 
-// Weights stream through LDS: chunks of kCB blocks of the 16 rows, copied
-// with coalesced global->LDS 16-byte loads (each row's chunk is 448
-// contiguous bytes) and double buffered.  LDS rows are padded by one 16-byte
-// piece so that the 16 lanes reading one dword of 16 rows hit 16 banks.
-constexpr int kCB = 16;                       // blocks per chunk
-constexpr int kRowPieces = kCB * 28 / 16 + 1; // 16-byte pieces per LDS row (+1 pad)
-constexpr int kWBuf = 16 * kRowPieces * 16;   // bytes of one chunk buffer
+// Weights stream through LDS: chunks of CB blocks of the 16 rows, copied
+// with coalesced global->LDS 16-byte loads (each row's chunk is 28 CB
+// contiguous bytes) into NBUF buffers, up to NBUF - 1 chunks in flight.
+// LDS rows are padded by one 16-byte piece so that the 16 lanes reading one
+// dword of 16 rows hit 16 banks.  Four-wave workgroups (short rows) use small
+// chunks so that six workgroups fit in one compute unit's LDS: residency,
+// not bytes in flight, limits the short-row case.
+template <int W>
+struct TqCfg {
+    static constexpr int CB = W == 4 ? 8 : 16;                 // blocks per chunk
+    static constexpr int NBUF = 2;                             // chunk buffers
+    static constexpr int ROW_PIECES = CB * 28 / 16 + 1;        // 16-byte pieces per LDS row (+1 pad)
+    static constexpr int WBUF = 16 * ROW_PIECES * 16;          // bytes of one chunk buffer
+    static_assert(CB % 4 == 0, "a chunk row must be a whole number of 16-byte pieces");
+    // tables, chunk buffers, activation slots (3.5 bytes per column), reduction
+    static constexpr size_t lds_bytes(int64_t nblk) {
+        return (size_t)kLutBytes + NBUF * WBUF + (size_t)nblk * kSlots * 16 + (W - 1) * 16 * 4;
+    }
+};
 
 template <int W>
 __global__ __launch_bounds__(64 * W) void tq1_mv_kernel(const uint8_t* __restrict__ w, int64_t n,
                                                         int64_t k, const uint16_t* __restrict__ x,
                                                         void* __restrict__ y, int y_dt) {
+    using Cfg = TqCfg<W>;
+    constexpr int kCB = Cfg::CB, kNBuf = Cfg::NBUF, kRowPieces = Cfg::ROW_PIECES, kWBuf = Cfg::WBUF;
     constexpr int NPIECE = 16 * kRowPieces;
     constexpr int WLOADS = (NPIECE + 63) / 64;
     constexpr int WL_PER_WAVE = (WLOADS + W - 1) / W;
+    static_assert(WLOADS % W == 0, "every wave issues the same number of loads per chunk");
     extern __shared__ __align__(16) uint8_t smem[];
-    uint32_t* lut2 = (uint32_t*)smem;                            // [9]
-    u32x2* lut3 = (u32x2*)(smem + kLut3Off);                     // [32]
-    uint8_t* wbuf = smem + kLutBytes;                           // [2][kWBuf]
-    u32x4* xs = (u32x4*)(smem + kLutBytes + 2 * kWBuf);         // [nblk * 28] slots
+    u32x2* lut_lo = (u32x2*)smem;                                // [27]
+    u32x2* lut_hi = (u32x2*)(smem + kHiOff);                     // [16]
+    uint8_t* wbuf = smem + kLutBytes;                           // [kNBuf][kWBuf]
+    u32x4* xs = (u32x4*)(smem + kLutBytes + kNBuf * kWBuf);     // [nblk * 28] slots
     const int nblk = (int)(k / 128);
     float* red = (float*)((uint8_t*)xs + (size_t)nblk * kSlots * 16);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -77,32 +96,34 @@ __global__ __launch_bounds__(64 * W) void tq1_mv_kernel(const uint8_t* __restric
 
     // ---- tables of trits as fp16: -1, 0, +1 for digits 0, 1, 2
     auto trit = [](uint32_t d) -> uint32_t { return d == 0 ? 0xbc00u : d == 1 ? 0x0000u : 0x3c00u; };
-    if (tid < 9) lut2[tid] = trit(tid % 3) | (trit(tid / 3) << 16);
-    if (tid >= 64 && tid < 96) {
+    if (tid < 27) lut_lo[tid] = u32x2{trit(tid % 3) | (trit((tid / 3) % 3) << 16), trit(tid / 9)};
+    if (tid >= 64 && tid < 80) {
         const uint32_t j = tid - 64;
-        lut3[j] = u32x2{trit(j % 3) | (trit((j / 3) % 3) << 16), trit((j / 9) % 3)};
+        lut_hi[j] = u32x2{trit(j % 3) | (trit((j / 3) % 3) << 16), 0u};
     }
     // ---- activations in slot layout: slot s < 25 of block b holds columns
-    // 128b + 5s .. +4, slot 25 columns 128b + 125 .. 127, the rest zeros.
-    // Zero every slot, then scatter the columns read 8 at a time.
-    for (int i = tid; i < nblk * kSlots; i += 64 * W) xs[i] = u32x4{0u, 0u, 0u, 0u};
-    __syncthreads();
-    {
-        uint16_t* xh = (uint16_t*)xs;
-        for (int i = tid; i < nblk * 16; i += 64 * W) {
-            const u32x4 v = *(const u32x4*)(x + 8 * (int64_t)i);
-            const int b = i >> 4, c0 = 8 * (i & 15);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int c = c0 + j;
-                const int sl = c < 125 ? (c * 52429) >> 18 : 25;  // c / 5 for c < 128
-                const int pos = c - 5 * sl;
-                const uint32_t h = (v[j >> 1] >> (16 * (j & 1))) & 0xffffu;
-                xh[((b * kSlots + sl) << 3) + pos] = (uint16_t)h;
-            }
+    // 128b + 5s .. +4 at positions 0 1 2 4 5, slot 25 columns 128b + 125 .. 127
+    // at positions 0 1 2, the rest zeros.  Each thread builds whole slots from
+    // the (4-byte aligned) dwords that cover their columns.
+    for (int i = tid; i < nblk * kSlots; i += 64 * W) {
+        const int b = i / kSlots, sl = i - kSlots * b;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (sl < 26) {
+            const int64_t col = 128 * (int64_t)b + 5 * sl;
+            const uint32_t* p = (const uint32_t*)(x + (col & ~(int64_t)1));
+            // columns (col & ~1) .. +5; the tail slot needs only .. +3, and
+            // reading further would pass the end of the row
+            const uint32_t d0 = p[0], d1 = p[1], d2 = sl < 25 ? p[2] : 0u;
+            const bool odd = col & 1;
+            const uint32_t e0 = odd ? __builtin_amdgcn_alignbit(d1, d0, 16) : d0;  // columns 0, 1
+            const uint32_t e1 = odd ? __builtin_amdgcn_alignbit(d2, d1, 16) : d1;  // columns 2, 3
+            const uint32_t e2 = odd ? d2 >> 16 : d2 & 0xffffu;                      // column 4
+            v[0] = e0;
+            v[1] = e1 & 0xffffu;
+            v[2] = sl < 25 ? (e1 >> 16) | (e2 << 16) : 0u;
         }
+        xs[i] = v;
     }
-
     // ---- weight pieces of this lane: LDS slot p = 64 i + lane is piece
     // p % kRowPieces of row p / kRowPieces (the last piece of a row is
     // padding and is not loaded)
@@ -121,7 +142,7 @@ __global__ __launch_bounds__(64 * W) void tq1_mv_kernel(const uint8_t* __restric
         woff[j] = (uint32_t)((nr - n0) * row_bytes) + wq16[j];
     }
     auto issue = [&](int chunk) {
-        uint8_t* dst = wbuf + (chunk & 1) * kWBuf;
+        uint8_t* dst = wbuf + (chunk % kNBuf) * kWBuf;
         const uint32_t cbase = (uint32_t)chunk * (kCB * 28);
         const int ncb = nblk - chunk * kCB < kCB ? nblk - chunk * kCB : kCB;
         const uint32_t climit = (uint32_t)ncb * 28u;
@@ -140,36 +161,44 @@ __global__ __launch_bounds__(64 * W) void tq1_mv_kernel(const uint8_t* __restric
     const int sh = 8 * g;  // this lane group's byte within each dword
     auto block = [&](int b, const uint32_t (&dw)[7]) {
         const u32x4* xb = xs + (int64_t)b * kSlots + g;
-        // every table and activation read of the block is issued before the
-        // first MFMA waits on one
-        uint32_t t2[7];
-        u32x2 t3[7];
-        u32x4 xa[7];
-#pragma unroll
-        for (int i = 0; i < 7; ++i) {
-            // slot 4i + g: byte g of dword i
-            const uint32_t code = (dw[i] >> sh) & 0xffu;
-            const uint32_t hi9 = (code * 57u) >> 9;  // code / 9 for code <= 255
-            const uint32_t lo9 = code - 9u * hi9;
-            t2[i] = lut2[lo9];
-            t3[i] = lut3[hi9];
-            xa[i] = xb[4 * i];
-        }
-        __builtin_amdgcn_sched_barrier(0);
+        // the table and activation reads of each half block are issued
+        // before the first of its MFMAs waits on one
         float4_t c = {0.f, 0.f, 0.f, 0.f};
+        auto half = [&](auto I0, auto N) {
+            constexpr int i0 = decltype(I0)::value, nn = decltype(N)::value;
+            u32x2 tl[nn], th[nn];
+            u32x4 xa[nn];
 #pragma unroll
-        for (int i = 0; i < 7; ++i) c = mfma_h(xa[i], u32x4{t2[i], t3[i].x, t3[i].y, 0u}, c);
+            for (int t = 0; t < nn; ++t) {
+                // slot 4i + g: byte g of dword i
+                const uint32_t code = (dw[i0 + t] >> sh) & 0xffu;
+                const uint32_t hi = (code * 19u) >> 9;  // code / 27 for code <= 255
+                tl[t] = lut_lo[code - 27u * hi];
+                th[t] = lut_hi[hi];
+                xa[t] = xb[4 * (i0 + t)];
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int t = 0; t < nn; ++t) c = mfma_h(xa[t], u32x4{tl[t].x, tl[t].y, th[t].x, th[t].y}, c);
+        };
+        // two halves keep the live registers at or under 64, eight waves per SIMD
+        half(std::integral_constant<int, 0>{}, std::integral_constant<int, 4>{});
+        half(std::integral_constant<int, 4>{}, std::integral_constant<int, 3>{});
         const float s = half_bits_to_float(dw[6] >> 16);
 #pragma unroll
         for (int v = 0; v < 4; ++v) acc[v] = __builtin_fmaf(s, c[v], acc[v]);
     };
 
-    issue(0);
+    for (int c = 0; c < kNBuf - 1 && c < nchunks; ++c) issue(c);
     for (int c = 0; c < nchunks; ++c) {
-        wait_loads_le(0);
+        // chunks issued after chunk c so far: up to c + kNBuf - 2
+        const int later = (nchunks - 1 < c + kNBuf - 2 ? nchunks - 1 : c + kNBuf - 2) - c;
+        wait_loads_le(later * (WLOADS / W));
         __syncthreads();
-        if (c + 1 < nchunks) issue(c + 1);
-        const uint8_t* B = wbuf + (c & 1) * kWBuf + n_l * (kRowPieces * 16);
+        // the buffer refilled here was read in iteration c - 1, which every
+        // wave has finished at the barrier above
+        if (c + kNBuf - 1 < nchunks) issue(c + kNBuf - 1);
+        const uint8_t* B = wbuf + (c % kNBuf) * kWBuf + n_l * (kRowPieces * 16);
         const int ncb = nblk - c * kCB < kCB ? nblk - c * kCB : kCB;
         for (int bl = wave; bl < ncb; bl += W) {
             uint32_t dw[7];
@@ -195,22 +224,25 @@ __global__ __launch_bounds__(64 * W) void tq1_mv_kernel(const uint8_t* __restric
     }
 }
 
-// LDS: tables, two weight buffers, activation slots (3.5 bytes per column),
-// reduction.  Rows must start on 16-byte boundaries (a multiple of four
-// blocks per row) for the 16-byte copies.
+// Rows must start on 16-byte boundaries (a multiple of four blocks per row)
+// for the 16-byte copies, and the activation slots must fit in LDS.
+static int tq1_mv_waves(int64_t nblk) { return nblk >= 64 ? 8 : 4; }
+
 bool tq1_mv_fits(int64_t k) {
-    return (k / 128) % 4 == 0 && kLutBytes + 2 * kWBuf + (k / 128) * kSlots * 16 + 7 * 16 * 4 <= 160 * 1024;
+    const int64_t nblk = k / 128;
+    if (nblk % 4 != 0) return false;
+    const size_t lds = tq1_mv_waves(nblk) == 8 ? TqCfg<8>::lds_bytes(nblk) : TqCfg<4>::lds_bytes(nblk);
+    return lds <= 160 * 1024;
 }
 
 hipError_t launch_tq1_mv(const uint8_t* w, int64_t n, int64_t k, const uint16_t* x, void* y, int y_dt,
                          hipStream_t s) {
     const int64_t nblk = k / 128;
     const dim3 grid((unsigned)((n + 15) / 16));
-    const size_t base = (size_t)kLutBytes + 2 * kWBuf + (size_t)nblk * kSlots * 16;
-    if (nblk >= 64) {
-        hipLaunchKernelGGL(tq1_mv_kernel<8>, grid, dim3(512), base + 7 * 16 * 4, s, w, n, k, x, y, y_dt);
+    if (tq1_mv_waves(nblk) == 8) {
+        hipLaunchKernelGGL(tq1_mv_kernel<8>, grid, dim3(512), TqCfg<8>::lds_bytes(nblk), s, w, n, k, x, y, y_dt);
     } else {
-        hipLaunchKernelGGL(tq1_mv_kernel<4>, grid, dim3(256), base + 3 * 16 * 4, s, w, n, k, x, y, y_dt);
+        hipLaunchKernelGGL(tq1_mv_kernel<4>, grid, dim3(256), TqCfg<4>::lds_bytes(nblk), s, w, n, k, x, y, y_dt);
     }
     return hipGetLastError();
 }
