@@ -129,12 +129,13 @@ def test_qmv_small(kq, kind, x_dt, m):
                   out_dt=y_dt if y_dt != "f32" and x_dt == "f32" else None)
 
 
-@pytest.mark.parametrize("m", [1, 2, 3, 4])
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 7, 8])
 @pytest.mark.parametrize("n,nsb", [(1, 1), (67, 5), (200, 16), (33, 17), (48, 56), (17, 68)])
 def test_qmv_q4k_few_rows_shapes(kq, m, n, nsb):
-    """One to four fp16 activation rows against Q4_K (the unscaled-nibble
-    kernels): chunks of four and eight super-blocks with ragged last chunks,
-    ragged row tiles, and a row long enough to be rearranged in two passes."""
+    """One to eight fp16 activation rows against Q4_K (the unscaled-nibble
+    kernels up to four rows, the scaled-nibble one beyond): chunks of four
+    and eight super-blocks with ragged last chunks, ragged row tiles, and a
+    row long enough to be rearranged in two passes."""
     k = 256 * nsb
     rng = _rng(2600 + 10 * nsb + m)
     w = synth.q4k_blocks(rng, n, k)
@@ -147,7 +148,7 @@ def test_qmv_q4k_few_rows_shapes(kq, m, n, nsb):
                   out_dt=y_dt if y_dt != "f32" else None)
 
 
-@pytest.mark.parametrize("m", [1, 3])
+@pytest.mark.parametrize("m", [1, 3, 8])
 @pytest.mark.parametrize("scale", [2.0**-20, 1.0, 6.0e4])
 def test_qmv_q4k_few_rows_activation_range(kq, m, scale):
     """Activations from fp16 subnormals to near the fp16 maximum: the
