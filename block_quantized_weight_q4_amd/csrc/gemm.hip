@@ -148,21 +148,67 @@ template <> struct WTile<TQ1> {
 #pragma unroll
         for (int i = 0; i < 7; ++i) r.w[i] = p[i];
     }
-    template <int XDT, int QI>
-    static __device__ __forceinline__ void quarter(const Raw& r, uint32_t (&v)[16]) {
-        const float sc = half_bits_to_float(r.w[6] >> 16);
+    // fp16 activations: digits two at a time with packed 16-bit integer
+    // arithmetic.  A code byte c (<= 242) in fixed point, q = ceil(256 c /
+    // 243), holds its base-3 digits as a fraction: digit k is the integer part
+    // of 3 * ((q * 3^(4-k)) mod 256) / 256.  With the digit placed in the low
+    // byte of the fp16 1024 (0x6400 | d), subtracting 1025 gives d - 1 exactly,
+    // and the product with the fp16 scale is exact as well.
+    template <int QI>
+    static __device__ __forceinline__ void quarter_f16(const Raw& r, uint32_t (&v)[16]) {
+        typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+        typedef _Float16 h16x2 __attribute__((ext_vector_type(2)));
+        constexpr int B0 = (32 * QI) / 5, B1 = (32 * QI + 31) < 125 ? (32 * QI + 31) / 5 : 25;
+        uint32_t q[B1 - B0 + 1];
+#pragma unroll
+        for (int b = B0; b <= B1; ++b) {
+            const uint32_t c = (r.w[b >> 2] >> (8 * (b & 3))) & 0xffu;
+            q[b - B0] = (c * 17261u + 16240u) >> 14;  // ceil(256 c / 243) for c <= 255
+        }
+        const uint32_t scb = r.w[6] >> 16;
+        const h16x2 sc2 = __builtin_bit_cast(h16x2, scb | (scb << 16));
+        const h16x2 off = {(_Float16)-1025.0f, (_Float16)-1025.0f};
+        constexpr uint32_t kPow3[5] = {1u, 3u, 9u, 27u, 81u};
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            float t[2];
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const int col = 32 * QI + 2 * i + e;
-                const int slot = col < 125 ? col / 5 : 25;
-                const int digit = col < 125 ? col - 5 * slot : col - 125;
-                const uint32_t code = (r.w[slot >> 2] >> (8 * (slot & 3))) & 0xffu;
-                t[e] = (float)tq1_trit(code, digit) * sc;
+            const int col = 32 * QI + 2 * i;
+            const int b = col < 125 ? col / 5 : 25;
+            const int dg = col < 125 ? col - 5 * b : col - 125;
+            uint32_t qq, mm;
+            if (dg <= 3) {  // both columns in byte b: digits dg, dg + 1
+                qq = q[b - B0] * 0x10001u;
+                mm = kPow3[4 - dg] | (kPow3[3 - dg] << 16);
+            } else {        // digit 4 of byte b, digit 0 of byte b + 1
+                qq = q[b - B0] | (q[b + 1 - B0] << 16);
+                mm = 1u | (81u << 16);
             }
-            v[i] = Op16<XDT>::pack(t[0], t[1]);
+            u16x2 t = __builtin_bit_cast(u16x2, qq) * __builtin_bit_cast(u16x2, mm);
+            t = __builtin_bit_cast(u16x2, __builtin_bit_cast(uint32_t, t) & 0x00ff00ffu) * (u16x2){3, 3};
+            // [high byte of each half | 0x64]: 1024 + digit in fp16
+            const uint32_t h = __builtin_amdgcn_perm(0x64646464u, __builtin_bit_cast(uint32_t, t), 0x04030401u);
+            v[i] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(h16x2, h) + off) * sc2);
+        }
+    }
+    template <int XDT, int QI>
+    static __device__ __forceinline__ void quarter(const Raw& r, uint32_t (&v)[16]) {
+        if constexpr (XDT == F16) {
+            quarter_f16<QI>(r, v);
+        } else {
+            // bf16 activations: w = (digit - 1) * scale rounded to bf16
+            const float sc = half_bits_to_float(r.w[6] >> 16);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                float t[2];
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const int col = 32 * QI + 2 * i + e;
+                    const int slot = col < 125 ? col / 5 : 25;
+                    const int digit = col < 125 ? col - 5 * slot : col - 125;
+                    const uint32_t code = (r.w[slot >> 2] >> (8 * (slot & 3))) & 0xffu;
+                    t[e] = (float)tq1_trit(code, digit) * sc;
+                }
+                v[i] = Op16<XDT>::pack(t[0], t[1]);
+            }
         }
     }
     template <int XDT>
@@ -371,9 +417,17 @@ template <int C, int XDT>
 static void launch_c(const void* w, int64_t n, int64_t k, const void* x, int64_t m, void* y,
                      int y_dt, hipStream_t s) {
     auto tiles = [&](int64_t bm, int64_t bn) { return ((n + bn - 1) / bn) * ((m + bm - 1) / bm); };
+    if (C == TQ1) {
+        // TQ1 weights cost the most to decode, and a tile decodes its weights
+        // once for BM activation rows: the largest tile while it still gives
+        // half a workgroup per compute unit
+        if (tiles(256, 256) >= 128) launch_tile<C, XDT, 256, 256, 8>(w, n, k, x, m, y, y_dt, s);
+        else launch_tile<C, XDT, 128, 128, 8>(w, n, k, x, m, y, y_dt, s);
+        return;
+    }
     if (tiles(256, 256) >= 384) launch_tile<C, XDT, 256, 256, 8>(w, n, k, x, m, y, y_dt, s);
     else if (tiles(256, 128) >= 192) launch_tile<C, XDT, 256, 128, 8>(w, n, k, x, m, y, y_dt, s);
-    else if (C == TQ1 || tiles(128, 128) >= 192) launch_tile<C, XDT, 128, 128, 8>(w, n, k, x, m, y, y_dt, s);
+    else if (tiles(128, 128) >= 192) launch_tile<C, XDT, 128, 128, 8>(w, n, k, x, m, y, y_dt, s);
     else launch_tile<C, XDT, 64, 128, 8>(w, n, k, x, m, y, y_dt, s);
 }
 

@@ -273,6 +273,21 @@ def test_qmm_c3_full_sampled(kq, which, m):
     _sampled(kq, "kq_qmm", cases[0], x, "bf16", m, "bf16")
 
 
+@pytest.mark.parametrize("x_dt", ["f16", "bf16"])
+def test_qmm_tq1_large_tiles_ragged(kq, x_dt):
+    """TQ1 products with enough output tiles for the 256x256 tile, ragged in
+    both M and N, every output against the oracle (fp16 activations take the
+    packed digit decode, bf16 the per-digit one)."""
+    m, n, k = 300, 16400, 384
+    rng = _rng(3100)
+    w = synth.weight_blocks("tq1_g128", rng, n, k)
+    x = synth.activations(rng, (m, k), x_dt)
+    _say("qmm tq1 large tiles", x_dt, m, n, k)
+    got = _run(kq, "kq_qmm", "tq1_g128", w, n, k, x, x_dt, m, "f32")
+    ref, s = oracle.qmm("tq1_g128", w, n, k, x, x_dt, m)
+    check_tol(got, ref, s, TAU[x_dt], f"qmm tq1 {x_dt} {m}x{n}x{k}")
+
+
 @pytest.mark.parametrize("which", [0, 1])
 @pytest.mark.parametrize("m", [1, 512])
 def test_tq1_c5_full_sampled(kq, which, m):
