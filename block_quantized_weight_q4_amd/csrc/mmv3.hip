@@ -67,7 +67,17 @@ struct Mmv3Layout {
     // sub-block sums follow the rearranged activations, then the reduction
     __host__ __device__ static size_t xs_off(int nsb) { return XP_OFF + (size_t)nsb * XP_SB; }
     __host__ __device__ static size_t red_off(int nsb) { return xs_off(nsb) + (size_t)nsb * 32; }
-    __host__ __device__ static size_t total(int nsb) { return red_off(nsb) + (size_t)(W - 1) * 2 * 64 * 4; }
+    __host__ __device__ static size_t end_off(int nsb) { return red_off(nsb) + (size_t)(W - 1) * 2 * 64 * 4; }
+    // the activation row as loaded (whole 1 KB loads): in the second chunk
+    // buffer, idle until the main loop starts, when it fits; else past the end
+    __host__ __device__ static size_t raw_bytes(int nsb) { return (size_t)((nsb * 32 + 63) / 64) * 1024; }
+    __host__ __device__ static size_t raw_off(int nsb) {
+        return (S == 2 && raw_bytes(nsb) <= (size_t)WBYTES) ? (size_t)WBYTES : end_off(nsb);
+    }
+    __host__ __device__ static size_t total(int nsb) {
+        const size_t r = raw_off(nsb) + raw_bytes(nsb);
+        return r > end_off(nsb) ? r : end_off(nsb);
+    }
 };
 
 }  // namespace
@@ -118,37 +128,36 @@ __global__ __launch_bounds__(64 * W) void mmv3_q4k_f16_kernel(SkinnyArgs a) {
             }
         }
     };
-    // ---- the activation row, rearranged once for all of K before the
-    // first weights are requested (measured faster than overlapping the two,
-    // whose loads share one in-order completion counter): entry t of
+    // ---- the activation row: copied into LDS as loaded, issued just before
+    // the first weights so that it lands while they stream (loads complete
+    // in order, so waiting for the weights' count leaves only the weights
+    // outstanding), then rearranged once for all of K: entry t of
     // super-block s is [x(4t) x(4t+2) x(4t+1) x(4t+3) | 0 0 0 0] (t = 0..63,
     // 16 bytes).  The lanes of a wave take 64 consecutive entries (one
     // super-block), so each group of eight lanes holds one sub-block and
     // forms its sum.
+    uint8_t* xraw = smem + L::raw_off(nsb);
     {
-        constexpr int XB = 8;  // entries per thread whose loads are issued together
-        const uint16_t* xrow = (const uint16_t*)a.x;
-        for (int e0 = tid; e0 < nsb * 64; e0 += XB * 64 * W) {
-            u32x2 v[XB];
-#pragma unroll
-            for (int i = 0; i < XB; ++i) {
-                const int e = e0 + i * 64 * W;
-                v[i] = e < nsb * 64 ? *(const u32x2*)(xrow + 4 * (int64_t)e) : u32x2{0u, 0u};
-            }
-#pragma unroll
-            for (int i = 0; i < XB; ++i) {
-                const int e = e0 + i * 64 * W;
-                if (e >= nsb * 64) break;
-                const int sbg = e >> 6, t = e & 63;
-                const uint32_t p0 = __builtin_amdgcn_perm(v[i].y, v[i].x, 0x05040100u);  // x0 x2
-                const uint32_t p1 = __builtin_amdgcn_perm(v[i].y, v[i].x, 0x07060302u);  // x1 x3
-                *(u32x4*)(xp + sbg * L::XP_SB + 16 * t) = u32x4{p0, p1, 0u, 0u};
-                const float sum = sum8_lanes(sum4_h(v[i].x, v[i].y));
-                if ((t & 7) == 0) xs[8 * sbg + (t >> 3)] = sum;
-            }
+        const int xpieces = nsb * 32, xloads = (xpieces + 63) / 64;
+        const uint8_t* xsrc = (const uint8_t*)a.x;
+        for (int i = wave; i < xloads; i += W) {
+            // lanes past the row re-read its last piece into the padding
+            const int piece = 64 * i + lane < xpieces ? 64 * i + lane : xpieces - 1;
+            dma16(xsrc + 16 * piece, __builtin_amdgcn_readfirstlane(lds_addr(xraw + 1024 * i)));
         }
     }
     for (int c = 0; c < S - 1 && c < nchunks; ++c) issue(c, c * L::WBYTES);
+    wait_loads_le(wave_loads * (nchunks < S - 1 ? nchunks : S - 1));
+    __syncthreads();
+    for (int e0 = tid; e0 < nsb * 64; e0 += 64 * W) {
+        const int sbg = e0 >> 6, t = e0 & 63;
+        const u32x2 v = *(const u32x2*)(xraw + 8 * e0);
+        const uint32_t p0 = __builtin_amdgcn_perm(v.y, v.x, 0x05040100u);  // x0 x2
+        const uint32_t p1 = __builtin_amdgcn_perm(v.y, v.x, 0x07060302u);  // x1 x3
+        *(u32x4*)(xp + sbg * L::XP_SB + 16 * t) = u32x4{p0, p1, 0u, 0u};
+        const float sum = sum8_lanes(sum4_h(v.x, v.y));
+        if ((t & 7) == 0) xs[8 * sbg + (t >> 3)] = sum;
+    }
 
     // A operand: MFMA j takes from column group g the quant dword j of chunk
     // g (bytes 32g+4j..+3): low nibbles of sub-block 2g at columns 64g+4j..,
