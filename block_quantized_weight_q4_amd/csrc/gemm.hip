@@ -409,10 +409,11 @@ static void launch_tile(const void* w, int64_t n, int64_t k, const void* x, int6
 
 // Tile choice (eight waves, two per SIMD, measured on the prefill shapes):
 // 256 x 256 while the grid holds at least 1.5 workgroups per CU (256 CUs),
-// else 256 x 128 or 128 x 128 while it holds 0.75, else 64 x 128 (not for
-// TQ1, whose per-weight decoding needs the 128 rows of reuse).  Larger tiles
-// reuse each decoded weight over more rows and each activation over more
-// columns; smaller ones keep the CUs busy when there are few tiles.
+// else 256 x 128 or 128 x 128 while it holds 0.75, else 64 x 128.  TQ1,
+// whose weights cost the most to decode, takes 256 x 256 down to half a
+// workgroup per CU and 128 x 128 below that.  Larger tiles reuse each
+// decoded weight over more rows and each activation over more columns;
+// smaller ones keep the CUs busy when there are few tiles.
 template <int C, int XDT>
 static void launch_c(const void* w, int64_t n, int64_t k, const void* x, int64_t m, void* y,
                      int y_dt, hipStream_t s) {
