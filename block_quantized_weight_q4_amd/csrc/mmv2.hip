@@ -1,7 +1,8 @@
 // mmv2.hip -- decode-shaped Q4_K products on the matrix cores with fp16
-// activations: kq_qmv (m <= 16 rows), and the expert-routed forms when every
-// schedule tile holds at most 16 rows (decode batches): kq_qmm_id and the
-// fused gate/up SiLU of kq_moe_glu.
+// activations: kq_qmv and kq_qmm with 5 to 16 rows (fewer rows take the
+// unscaled-nibble kernels of mmv3.hip), and the expert-routed forms when
+// every schedule tile holds at most 16 rows (decode batches): kq_qmm_id and
+// the fused gate/up SiLU of kq_moe_glu.
 //
 // mlx-kquant "bindings.cpp": quantized_matmul, gather_qmv_kq,
 // moe_glu_gather_kq; mlx-native "quantized_matmul_id_ggml.rs": the
