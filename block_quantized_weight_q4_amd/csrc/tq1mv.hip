@@ -24,8 +24,8 @@
 //
 // A workgroup owns 16 weight rows.  Their weights stream through LDS in
 // chunks of 8 or 16 blocks (coalesced global->LDS copies, double buffered);
-// the W waves take the blocks of a chunk in turn and combine their partial
-// sums through LDS at the end.  Each half block issues all of its table and
+// the W waves (4 or 16) take the blocks of a chunk in turn and combine their
+// partial sums through LDS at the end.  Each half block issues all of its table and
 // activation reads before its first MFMA, so their LDS latency overlaps.
 #include "kq_device.h"
 #include "kq_internal.h"
@@ -55,12 +55,10 @@ __device__ __forceinline__ float4_t mfma_h(const u32x4& a, const u32x4& b, const
 // with coalesced global->LDS 16-byte loads (each row's chunk is 28 CB
 // contiguous bytes) into NBUF buffers, up to NBUF - 1 chunks in flight.
 // LDS rows are padded by one 16-byte piece so that the 16 lanes reading one
-// dword of 16 rows hit 16 banks.  Four-wave workgroups (short rows) use small
-// chunks so that six workgroups fit in one compute unit's LDS: residency,
-// not bytes in flight, limits the short-row case.
-template <int W>
+// dword of 16 rows hit 16 banks.
+template <int W, int CB_>
 struct TqCfg {
-    static constexpr int CB = W == 4 ? 8 : 16;                 // blocks per chunk
+    static constexpr int CB = CB_;                             // blocks per chunk
     static constexpr int NBUF = 2;                             // chunk buffers
     static constexpr int ROW_PIECES = CB * 28 / 16 + 1;        // 16-byte pieces per LDS row (+1 pad)
     static constexpr int WBUF = 16 * ROW_PIECES * 16;          // bytes of one chunk buffer
@@ -71,16 +69,15 @@ struct TqCfg {
     }
 };
 
-template <int W>
+template <int W, int CB>
 __global__ __launch_bounds__(64 * W) void tq1_mv_kernel(const uint8_t* __restrict__ w, int64_t n,
                                                         int64_t k, const uint16_t* __restrict__ x,
                                                         void* __restrict__ y, int y_dt) {
-    using Cfg = TqCfg<W>;
+    using Cfg = TqCfg<W, CB>;
     constexpr int kCB = Cfg::CB, kNBuf = Cfg::NBUF, kRowPieces = Cfg::ROW_PIECES, kWBuf = Cfg::WBUF;
     constexpr int NPIECE = 16 * kRowPieces;
     constexpr int WLOADS = (NPIECE + 63) / 64;
     constexpr int WL_PER_WAVE = (WLOADS + W - 1) / W;
-    static_assert(WLOADS % W == 0, "every wave issues the same number of loads per chunk");
     extern __shared__ __align__(16) uint8_t smem[];
     u32x2* lut_lo = (u32x2*)smem;                                // [27]
     u32x2* lut_hi = (u32x2*)(smem + kHiOff);                     // [16]
@@ -141,6 +138,11 @@ __global__ __launch_bounds__(64 * W) void tq1_mv_kernel(const uint8_t* __restric
         wq16[j] = 16u * (uint32_t)q;
         woff[j] = (uint32_t)((nr - n0) * row_bytes) + wq16[j];
     }
+    // load instructions this wave issues per chunk (every one of them has a
+    // live lane: each group of 64 pieces holds pieces of a row)
+    int wave_loads = 0;
+#pragma unroll
+    for (int j = 0; j < WL_PER_WAVE; ++j) wave_loads += (wave + W * j < WLOADS) ? 1 : 0;
     auto issue = [&](int chunk) {
         uint8_t* dst = wbuf + (chunk % kNBuf) * kWBuf;
         const uint32_t cbase = (uint32_t)chunk * (kCB * 28);
@@ -193,7 +195,7 @@ __global__ __launch_bounds__(64 * W) void tq1_mv_kernel(const uint8_t* __restric
     for (int c = 0; c < nchunks; ++c) {
         // chunks issued after chunk c so far: up to c + kNBuf - 2
         const int later = (nchunks - 1 < c + kNBuf - 2 ? nchunks - 1 : c + kNBuf - 2) - c;
-        wait_loads_le(later * (WLOADS / W));
+        wait_loads_le(later * wave_loads);
         __syncthreads();
         // the buffer refilled here was read in iteration c - 1, which every
         // wave has finished at the barrier above
@@ -226,12 +228,18 @@ __global__ __launch_bounds__(64 * W) void tq1_mv_kernel(const uint8_t* __restric
 
 // Rows must start on 16-byte boundaries (a multiple of four blocks per row)
 // for the 16-byte copies, and the activation slots must fit in LDS.
-static int tq1_mv_waves(int64_t nblk) { return nblk >= 64 ? 8 : 4; }
+// Short rows: four waves and 8-block chunks, so that six workgroups fit in
+// one compute unit's LDS and every workgroup of the short-row shapes is
+// resident at once.  Long rows: sixteen waves and 16-block chunks (two
+// workgroups per compute unit), so that a compute unit holding one of the
+// few workgroups still has four waves per SIMD.
+using TqShort = TqCfg<4, 8>;   // rows of fewer than 64 blocks
+using TqLong = TqCfg<16, 16>;
 
 bool tq1_mv_fits(int64_t k) {
     const int64_t nblk = k / 128;
     if (nblk % 4 != 0) return false;
-    const size_t lds = tq1_mv_waves(nblk) == 8 ? TqCfg<8>::lds_bytes(nblk) : TqCfg<4>::lds_bytes(nblk);
+    const size_t lds = nblk >= 64 ? TqLong::lds_bytes(nblk) : TqShort::lds_bytes(nblk);
     return lds <= 160 * 1024;
 }
 
@@ -239,10 +247,12 @@ hipError_t launch_tq1_mv(const uint8_t* w, int64_t n, int64_t k, const uint16_t*
                          hipStream_t s) {
     const int64_t nblk = k / 128;
     const dim3 grid((unsigned)((n + 15) / 16));
-    if (tq1_mv_waves(nblk) == 8) {
-        hipLaunchKernelGGL(tq1_mv_kernel<8>, grid, dim3(512), TqCfg<8>::lds_bytes(nblk), s, w, n, k, x, y, y_dt);
+    if (nblk >= 64) {
+        hipLaunchKernelGGL((tq1_mv_kernel<16, 16>), grid, dim3(64 * 16),
+                           TqLong::lds_bytes(nblk), s, w, n, k, x, y, y_dt);
     } else {
-        hipLaunchKernelGGL(tq1_mv_kernel<4>, grid, dim3(256), TqCfg<4>::lds_bytes(nblk), s, w, n, k, x, y, y_dt);
+        hipLaunchKernelGGL((tq1_mv_kernel<4, 8>), grid, dim3(64 * 4),
+                           TqShort::lds_bytes(nblk), s, w, n, k, x, y, y_dt);
     }
     return hipGetLastError();
 }
