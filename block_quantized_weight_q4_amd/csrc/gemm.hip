@@ -69,16 +69,19 @@ template <> struct WTile<Q4_K> {
         const float d = q4k_d(r.hd), dmin = q4k_dmin(r.hd);
         const float s0 = d * (float)sc0, s1 = d * (float)sc1;
         const float n0 = -dmin * (float)m0, n1 = -dmin * (float)m1;
+        // high nibbles are converted in place (16 q) against s1 / 16: the
+        // product is the same, and each byte converts in one instruction
+        const float s1h = s1 * 0.0625f;
+        auto byte = [](uint32_t v, int j) { return (float)((v >> (8 * j)) & 0xffu); };
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const uint32_t wd = r.q[i];
+            const uint32_t ml = r.q[i] & 0x0f0f0f0fu, mh = r.q[i] & 0xf0f0f0f0u;
 #pragma unroll
             for (int b = 0; b < 4; b += 2) {
-                const uint32_t b0 = (wd >> (8 * b)) & 0xffu, b1 = (wd >> (8 * b + 8)) & 0xffu;
-                lo[2 * i + b / 2] = Op16<XDT>::pack(__builtin_fmaf(s0, (float)(b0 & 15u), n0),
-                                                    __builtin_fmaf(s0, (float)(b1 & 15u), n0));
-                hi[2 * i + b / 2] = Op16<XDT>::pack(__builtin_fmaf(s1, (float)(b0 >> 4), n1),
-                                                    __builtin_fmaf(s1, (float)(b1 >> 4), n1));
+                lo[2 * i + b / 2] = Op16<XDT>::pack(__builtin_fmaf(s0, byte(ml, b), n0),
+                                                    __builtin_fmaf(s0, byte(ml, b + 1), n0));
+                hi[2 * i + b / 2] = Op16<XDT>::pack(__builtin_fmaf(s1h, byte(mh, b), n1),
+                                                    __builtin_fmaf(s1h, byte(mh, b + 1), n1));
             }
         }
         col_lo = 16 * h;
@@ -250,12 +253,17 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const uint8_t* __restrict
     const int64_t row_bytes = (k / CodecInfo<C>::QK) * CodecInfo<C>::BYTES;
     const int steps = (int)((k + BK - 1) / BK);
 
-    // weight role: tile row wr = tid/2 (< BN), half wh = tid%2
-    const int wr = tid >> 1, wh = tid & 1;
-    const bool wrole = wr < BN;
+    // weight role: tile row wr and half wh (< 2) of each step.  Neighbouring
+    // threads read the two halves of one row (contiguous bytes), except for
+    // TQ1, whose decoding branches on the half: there each wave holds one
+    // half, so it runs one branch (measured faster for TQ1, slower for the
+    // others).
+    constexpr bool kWaveHalves = C == TQ1;
+    const int wr = kWaveHalves ? tid % BN : tid >> 1, wh = kWaveHalves ? tid / BN : tid & 1;
+    const bool wrole = tid < 2 * BN;
     const int64_t wrow_idx = n0 + wr;
+    const bool wr_valid = wrole && wrow_idx < n;
     const uint8_t* wrow = w + (wrow_idx < n ? wrow_idx : n - 1) * row_bytes;
-    const bool wvalid = wrole && wrow_idx < n;
 
     float16_t acc[FM][FN];
 #pragma unroll
@@ -281,9 +289,14 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const uint8_t* __restrict
             const int64_t gm = m0 + r;
             const int64_t c0 = (int64_t)s * BK + 8 * q;
             if (FULL) {
+                // rows past m read row 0; for Q4_K and TQ1 (K a multiple of
+                // the step) they are left as read, since they only reach
+                // output rows that are not stored.  Q8_0 zeroes them and the
+                // columns past k (rows of an odd block count), which keeps
+                // its scheduling measured faster.
                 const bool ok = gm < m && c0 < k;
                 const u32x4 v = *(const u32x4*)(x + (ok ? gm * k + c0 : 0));
-                R.xr[i] = ok ? v : u32x4{0u, 0u, 0u, 0u};
+                R.xr[i] = (C != Q8_0 || ok) ? v : u32x4{0u, 0u, 0u, 0u};
             } else {
                 R.xr[i] = (gm < m && c0 < k) ? *(const u32x4*)(x + gm * k + c0) : u32x4{0u, 0u, 0u, 0u};
             }
@@ -309,7 +322,11 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const uint8_t* __restrict
         if (FULL || wrole) {
             uint32_t lo[8], hi[8];
             int cl, ch;
-            const bool live = wvalid && ((C != Q8_0) || (int64_t)(2 * s + wh) * 32 < k);
+            // weight rows past n (read from row n-1) only reach output
+            // columns that are not stored and are left as decoded, except
+            // for Q8_0, which also zeroes a half past the row end (that one
+            // would reach stored outputs)
+            const bool live = (C != Q8_0) || (wr_valid && (int64_t)(2 * s + wh) * 32 < k);
             if (FULL) {
                 WT::template decode<XDT>(R.raw, s, wh, lo, hi, cl, ch);
 #pragma unroll
