@@ -112,28 +112,27 @@ template <> struct WTile<Q8_0> {
         }
         r.tail = *(const uint16_t*)(base + (h ? 34 : 32));
     }
+    // Both halves decode with the same instructions (the half differs per
+    // lane): the words [w0..w7, tail] shifted right by 16 bits (h = 0, whose
+    // quants start at byte 2) or not at all (h = 1) give the 32 quants in
+    // order.  A quant byte xor 0x80 is q + 128, converted in one instruction,
+    // and fma(d, q + 128, -128 d) is d q exactly (a zero weight comes out as
+    // +0 whatever the sign of d).
     template <int XDT>
     static __device__ __forceinline__ void decode(const Raw& r, int s, int h, uint32_t (&lo)[8],
                                                   uint32_t (&hi)[8], int& col_lo, int& col_hi) {
-        // quant i of the block and its scale
-        auto wbyte = [&](int i) -> uint32_t { return (r.w[i >> 2] >> (8 * (i & 3))) & 0xffu; };
-        float d;
-        uint32_t q[32];
-        if (h == 0) {
-            d = half_bits_to_float(r.w[0] & 0xffffu);
-#pragma unroll
-            for (int i = 0; i < 30; ++i) q[i] = wbyte(2 + i);
-            q[30] = r.tail & 0xffu;
-            q[31] = r.tail >> 8;
-        } else {
-            d = half_bits_to_float(r.tail);
-#pragma unroll
-            for (int i = 0; i < 32; ++i) q[i] = wbyte(i);
-        }
+        const uint32_t sh = h ? 0u : 16u;
+        const float d = half_bits_to_float(h ? r.tail : (r.w[0] & 0xffffu));
+        const float nd = -128.0f * d;
+        auto byte = [](uint32_t v, int j) { return (float)((v >> (8 * j)) & 0xffu); };
         uint32_t v[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-            v[i] = Op16<XDT>::pack(d * (float)(int8_t)q[2 * i], d * (float)(int8_t)q[2 * i + 1]);
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t next = j < 7 ? r.w[j + 1] : r.tail;
+            const uint32_t u = __builtin_amdgcn_alignbit(next, r.w[j], sh) ^ 0x80808080u;
+            v[2 * j] = Op16<XDT>::pack(__builtin_fmaf(d, byte(u, 0), nd), __builtin_fmaf(d, byte(u, 1), nd));
+            v[2 * j + 1] = Op16<XDT>::pack(__builtin_fmaf(d, byte(u, 2), nd), __builtin_fmaf(d, byte(u, 3), nd));
+        }
 #pragma unroll
         for (int i = 0; i < 8; ++i) lo[i] = v[i], hi[i] = v[8 + i];
         col_lo = 32 * h;
