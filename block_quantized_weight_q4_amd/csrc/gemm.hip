@@ -75,7 +75,10 @@ template <> struct WTile<Q4_K> {
         auto byte = [](uint32_t v, int j) { return (float)((v >> (8 * j)) & 0xffu); };
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const uint32_t ml = r.q[i] & 0x0f0f0f0fu, mh = r.q[i] & 0xf0f0f0f0u;
+            uint32_t ml = r.q[i] & 0x0f0f0f0fu, mh = r.q[i] & 0xf0f0f0f0u;
+            // opaque to the compiler, which would otherwise fold the masks
+            // into one bit-field extract per nibble
+            asm("" : "+v"(ml), "+v"(mh));
 #pragma unroll
             for (int b = 0; b < 4; b += 2) {
                 lo[2 * i + b / 2] = Op16<XDT>::pack(__builtin_fmaf(s0, byte(ml, b), n0),
@@ -121,7 +124,8 @@ template <> struct WTile<Q8_0> {
     template <int XDT>
     static __device__ __forceinline__ void decode(const Raw& r, int s, int h, uint32_t (&lo)[8],
                                                   uint32_t (&hi)[8], int& col_lo, int& col_hi) {
-        const uint32_t sh = h ? 0u : 16u;
+        uint32_t sh = h ? 0u : 16u;
+        asm("" : "+v"(sh));  // one funnel shift by a register, not two selected
         const float d = half_bits_to_float(h ? r.tail : (r.w[0] & 0xffffu));
         const float nd = -128.0f * d;
         auto byte = [](uint32_t v, int j) { return (float)((v >> (8 * j)) & 0xffu); };
