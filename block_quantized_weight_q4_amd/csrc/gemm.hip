@@ -365,8 +365,11 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const uint8_t* __restrict
     // Pipeline: LDS stage s%2 holds step s; while the MFMAs of step s run,
     // step s+1 (fetched an iteration earlier) is decoded into the other
     // stage, and step s+2 is fetched into the freed registers.  One barrier
-    // per step.  (Fetching two steps ahead was measured no faster, for
-    // small grids as well.)
+    // per step.  The decode is placed after the last MFMAs of the step are
+    // issued, so the loads it consumes have a whole step of matrix work to
+    // land (5-9 % faster than decoding after the first MFMAs at M = 512).
+    // (Fetching a further step ahead, with a second register set, was
+    // measured no faster.)
     auto step = [&](int s, Regs& R) {
         const int st = s & 1;
         u32x4 af[FM], bf[FN];
@@ -381,7 +384,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const uint8_t* __restrict
                 for (int j = 0; j < FN; ++j) acc[i][j] = Op16<XDT>::mma(af[i], bf[j], acc[i][j]);
             // (on the last step the stash fills the idle stage with data
             // that is never read)
-            if (ks == 0 && (FULL || s + 1 < steps)) stash(s + 1, st ^ 1, R);
+            if (ks == BK / 16 - 1 && (FULL || s + 1 < steps)) stash(s + 1, st ^ 1, R);
             if (ks + 1 < BK / 16) {
 #pragma unroll
                 for (int i = 0; i < FM; ++i) af[i] = naf[i];
