@@ -90,6 +90,40 @@ template <> struct WTile<Q4_K> {
         col_lo = 16 * h;
         col_hi = 32 + 16 * h;
     }
+    // Quarter q of step s: quant bytes 32c+8q..+8 -> low nibbles to columns
+    // 8q+i, high nibbles to 32+8q+i.
+    struct RawQ { u32x4 hd; u32x2 q; };
+    static __device__ __forceinline__ void fetch_q(const uint8_t* row, int s, int q, RawQ& r) {
+        const uint8_t* blk = row + (s >> 2) * 144;
+        r.hd = *(const u32x4*)blk;
+        r.q = *(const u32x2*)(blk + 16 + 32 * (s & 3) + 8 * q);
+    }
+    template <int XDT>
+    static __device__ __forceinline__ void decode_q(const RawQ& r, int s, int q, uint32_t (&lo)[4],
+                                                    uint32_t (&hi)[4], int& col_lo, int& col_hi) {
+        const int c = s & 3;
+        int sc0, m0, sc1, m1;
+        q4k_scale_min(r.hd, 2 * c, sc0, m0);
+        q4k_scale_min(r.hd, 2 * c + 1, sc1, m1);
+        const float d = q4k_d(r.hd), dmin = q4k_dmin(r.hd);
+        const float s0 = d * (float)sc0, s1h = d * (float)sc1 * 0.0625f;
+        const float n0 = -dmin * (float)m0, n1 = -dmin * (float)m1;
+        auto byte = [](uint32_t v, int j) { return (float)((v >> (8 * j)) & 0xffu); };
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            uint32_t ml = r.q[i] & 0x0f0f0f0fu, mh = r.q[i] & 0xf0f0f0f0u;
+            asm("" : "+v"(ml), "+v"(mh));
+#pragma unroll
+            for (int b = 0; b < 4; b += 2) {
+                lo[2 * i + b / 2] = Op16<XDT>::pack(__builtin_fmaf(s0, byte(ml, b), n0),
+                                                    __builtin_fmaf(s0, byte(ml, b + 1), n0));
+                hi[2 * i + b / 2] = Op16<XDT>::pack(__builtin_fmaf(s1h, byte(mh, b), n1),
+                                                    __builtin_fmaf(s1h, byte(mh, b + 1), n1));
+            }
+        }
+        col_lo = 8 * q;
+        col_hi = 32 + 8 * q;
+    }
 };
 
 // Q8_0: step s covers blocks 2s, 2s+1 (68 contiguous, 4-byte aligned bytes);
@@ -160,11 +194,13 @@ template <> struct WTile<TQ1> {
     // of 3 * ((q * 3^(4-k)) mod 256) / 256.  With the digit placed in the low
     // byte of the fp16 1024 (0x6400 | d), subtracting 1025 gives d - 1 exactly,
     // and the product with the fp16 scale is exact as well.
-    template <int QI>
-    static __device__ __forceinline__ void quarter_f16(const Raw& r, uint32_t (&v)[16]) {
+    // Column pairs C0 + 2i, C0 + 2i + 1 (i < NP) of the block.
+    template <int C0, int NP>
+    static __device__ __forceinline__ void cols_f16(const Raw& r, uint32_t (&v)[NP]) {
         typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
         typedef _Float16 h16x2 __attribute__((ext_vector_type(2)));
-        constexpr int B0 = (32 * QI) / 5, B1 = (32 * QI + 31) < 125 ? (32 * QI + 31) / 5 : 25;
+        constexpr int CL = C0 + 2 * NP - 1;  // last column
+        constexpr int B0 = C0 / 5, B1 = CL < 125 ? CL / 5 : 25;
         uint32_t q[B1 - B0 + 1];
 #pragma unroll
         for (int b = B0; b <= B1; ++b) {
@@ -176,8 +212,8 @@ template <> struct WTile<TQ1> {
         const h16x2 off = {(_Float16)-1025.0f, (_Float16)-1025.0f};
         constexpr uint32_t kPow3[5] = {1u, 3u, 9u, 27u, 81u};
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int col = 32 * QI + 2 * i;
+        for (int i = 0; i < NP; ++i) {
+            const int col = C0 + 2 * i;
             const int b = col < 125 ? col / 5 : 25;
             const int dg = col < 125 ? col - 5 * b : col - 125;
             uint32_t qq, mm;
@@ -195,19 +231,19 @@ template <> struct WTile<TQ1> {
             v[i] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(h16x2, h) + off) * sc2);
         }
     }
-    template <int XDT, int QI>
-    static __device__ __forceinline__ void quarter(const Raw& r, uint32_t (&v)[16]) {
+    template <int XDT, int C0, int NP>
+    static __device__ __forceinline__ void cols(const Raw& r, uint32_t (&v)[NP]) {
         if constexpr (XDT == F16) {
-            quarter_f16<QI>(r, v);
+            cols_f16<C0, NP>(r, v);
         } else {
             // bf16 activations: w = (digit - 1) * scale rounded to bf16
             const float sc = half_bits_to_float(r.w[6] >> 16);
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
+            for (int i = 0; i < NP; ++i) {
                 float t[2];
 #pragma unroll
                 for (int e = 0; e < 2; ++e) {
-                    const int col = 32 * QI + 2 * i + e;
+                    const int col = C0 + 2 * i + e;
                     const int slot = col < 125 ? col / 5 : 25;
                     const int digit = col < 125 ? col - 5 * slot : col - 125;
                     const uint32_t code = (r.w[slot >> 2] >> (8 * (slot & 3))) & 0xffu;
@@ -222,17 +258,45 @@ template <> struct WTile<TQ1> {
                                                   uint32_t (&hi)[8], int& col_lo, int& col_hi) {
         uint32_t v[16];
         switch (2 * (s & 1) + h) {
-        case 0: quarter<XDT, 0>(r, v); break;
-        case 1: quarter<XDT, 1>(r, v); break;
-        case 2: quarter<XDT, 2>(r, v); break;
-        default: quarter<XDT, 3>(r, v); break;
+        case 0: cols<XDT, 0, 16>(r, v); break;
+        case 1: cols<XDT, 32, 16>(r, v); break;
+        case 2: cols<XDT, 64, 16>(r, v); break;
+        default: cols<XDT, 96, 16>(r, v); break;
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) lo[i] = v[i], hi[i] = v[8 + i];
         col_lo = 32 * h;
         col_hi = 32 * h + 16;
     }
+    // Quarter q of step s: columns 16e..16e+15 of the block, e = 4 (s%2) + q.
+    using RawQ = Raw;
+    static __device__ __forceinline__ void fetch_q(const uint8_t* row, int s, int, RawQ& r) {
+        fetch(row, s, 0, r, true);
+    }
+    template <int XDT>
+    static __device__ __forceinline__ void decode_q(const RawQ& r, int s, int q, uint32_t (&lo)[4],
+                                                    uint32_t (&hi)[4], int& col_lo, int& col_hi) {
+        uint32_t v[8];
+        switch (4 * (s & 1) + q) {
+        case 0: cols<XDT, 0, 8>(r, v); break;
+        case 1: cols<XDT, 16, 8>(r, v); break;
+        case 2: cols<XDT, 32, 8>(r, v); break;
+        case 3: cols<XDT, 48, 8>(r, v); break;
+        case 4: cols<XDT, 64, 8>(r, v); break;
+        case 5: cols<XDT, 80, 8>(r, v); break;
+        case 6: cols<XDT, 96, 8>(r, v); break;
+        default: cols<XDT, 112, 8>(r, v); break;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lo[i] = v[i], hi[i] = v[4 + i];
+        col_lo = 16 * q;
+        col_hi = 16 * q + 8;
+    }
 };
+
+// The per-step weight registers: halves (Raw) or quarters (RawQ).
+template <bool Q, class WT> struct RawSel { using type = typename WT::Raw; };
+template <class WT> struct RawSel<true, WT> { using type = typename WT::RawQ; };
 
 // ---------------------------------------------------------------- kernel
 // BM x BN tile, NW waves as 2 x (NW/2), each a (BM/2) x (2BN/NW) sub-tile of
@@ -256,14 +320,17 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const uint8_t* __restrict
     const int64_t row_bytes = (k / CodecInfo<C>::QK) * CodecInfo<C>::BYTES;
     const int steps = (int)((k + BK - 1) / BK);
 
-    // weight role: tile row wr and half wh (< 2) of each step.  Neighbouring
-    // threads read the two halves of one row (contiguous bytes), except for
-    // TQ1, whose decoding branches on the half: there each wave holds one
-    // half, so it runs one branch (measured faster for TQ1, slower for the
-    // others).
-    constexpr bool kWaveHalves = C == TQ1;
-    const int wr = kWaveHalves ? tid % BN : tid >> 1, wh = kWaveHalves ? tid / BN : tid & 1;
-    const bool wrole = tid < 2 * BN;
+    // weight role: tile row wr and part wh of each step, a half (wh < 2) or,
+    // when the threads are four times the tile's rows (Q4_K and TQ1), a
+    // quarter (wh < 4), so that every wave shares the decoding.  Neighbouring
+    // threads read the parts of one row (contiguous bytes), except for TQ1,
+    // whose decoding branches on the part: there each wave holds one part,
+    // so it runs one branch (measured faster for TQ1, slower for the others).
+    constexpr bool QM = 4 * BN == NT && C != Q8_0;
+    constexpr int NPART = QM ? 4 : 2;
+    constexpr bool kWaveParts = C == TQ1;
+    const int wr = kWaveParts ? tid % BN : tid / NPART, wh = kWaveParts ? tid / BN : tid % NPART;
+    const bool wrole = tid < NPART * BN;
     const int64_t wrow_idx = n0 + wr;
     const bool wr_valid = wrole && wrow_idx < n;
     const uint8_t* wrow = w + (wrow_idx < n ? wrow_idx : n - 1) * row_bytes;
@@ -277,14 +344,15 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const uint8_t* __restrict
     // registers holding the fetched-but-not-stashed step
     struct Regs {
         u32x4 xr[XP];
-        typename WT::Raw raw;
+        typename RawSel<QM, WT>::type raw;
     };
     Regs ra;
-    // With every thread owning a weight role (2 BN == threads) the step is
-    // branch-free: out-of-range pieces are read from a valid address and
-    // replaced by zeros with selects, so the whole K step is one scheduling
-    // region in which loads, decoding and MFMAs can interleave.
-    constexpr bool FULL = 2 * BN == NT;
+    // With every thread owning a weight role (2 BN, or 4 BN in quarters, ==
+    // threads) the step is branch-free: out-of-range pieces are read from a
+    // valid address and replaced by zeros with selects, so the whole K step
+    // is one scheduling region in which loads, decoding and MFMAs can
+    // interleave.
+    constexpr bool FULL = 2 * BN == NT || QM;
     auto fetch = [&](int s, Regs& R) {
 #pragma unroll
         for (int i = 0; i < XP; ++i) {
@@ -304,7 +372,9 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const uint8_t* __restrict
                 R.xr[i] = (gm < m && c0 < k) ? *(const u32x4*)(x + gm * k + c0) : u32x4{0u, 0u, 0u, 0u};
             }
         }
-        if (FULL) {
+        if constexpr (QM) {
+            WT::fetch_q(wrow, s, wh, R.raw);
+        } else if (FULL) {
             // a Q8_0 half past the row end reads the step's first block instead
             const int hf = (C == Q8_0 && (int64_t)(2 * s + wh) * 32 >= k) ? 0 : wh;
             WT::fetch(wrow, s, hf, R.raw, (row_bytes & 3) == 0);
@@ -322,7 +392,14 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const uint8_t* __restrict
             const int p = tid + NT * i, r = p >> 3, q = p & 7;
             *(u32x4*)&As[r * LDS_STRIDE + 8 * q] = R.xr[i];
         }
-        if (FULL || wrole) {
+        if constexpr (QM) {
+            // rows past n are left as decoded (see below)
+            uint32_t lo[4], hi[4];
+            int cl, ch;
+            WT::template decode_q<XDT>(R.raw, s, wh, lo, hi, cl, ch);
+            *(u32x4*)&Bs[wr * LDS_STRIDE + cl] = u32x4{lo[0], lo[1], lo[2], lo[3]};
+            *(u32x4*)&Bs[wr * LDS_STRIDE + ch] = u32x4{hi[0], hi[1], hi[2], hi[3]};
+        } else if (FULL || wrole) {
             uint32_t lo[8], hi[8];
             int cl, ch;
             // weight rows past n (read from row n-1) only reach output
