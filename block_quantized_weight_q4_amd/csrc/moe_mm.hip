@@ -26,6 +26,7 @@
 #include "kq_device.h"
 #include "kq_internal.h"
 #include "q4k_mfma.h"
+#include "lds_dma.h"
 
 namespace kq {
 
@@ -68,8 +69,10 @@ template <int W, bool GLU, bool XF32>
 __global__ __launch_bounds__(64 * W) void moe_mm_kernel(SkinnyArgs a) {
     constexpr int ROWS = GLU ? 16 * W : 32 * W;  // output columns of the workgroup
     extern __shared__ __align__(16) uint8_t smem[];
-    uint16_t* xh = (uint16_t*)smem;                        // [32][xstride] hi (or fp16 x)
-    uint16_t* xl = (uint16_t*)(smem + a.red_off);          // [32][xstride] lo (fp32 x only)
+    // fp32 x: [32][xstride] hi and lo parts; fp16 x: two [32][xstride]
+    // chunk buffers, filled alternately
+    uint16_t* xh = (uint16_t*)smem;
+    uint16_t* xl = (uint16_t*)(smem + a.red_off);
     const int XC = a.xch, XSTRIDE = a.xstride;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n_l = lane & 15, g = lane >> 4;
@@ -152,19 +155,42 @@ __global__ __launch_bounds__(64 * W) void moe_mm_kernel(SkinnyArgs a) {
     };
     load_w(0, hd, q0, q1);
 
-    for (int c0 = 0; c0 < nsb; c0 += XC) {
+    // fp16 activations: the rows of chunk [c0, c0 + XC) are copied straight
+    // into LDS one chunk ahead (a 1 KB load per row: XC = 2, rows of at
+    // least 1 KB), so their latency overlaps the previous chunk's work.
+    // Loads complete in order, so the compiler's own waits on the weight
+    // registers stay correct (and only wait longer).
+    auto issue_x = [&](int c0, uint16_t* dst) {
         const int nch = nsb - c0 < XC ? nsb - c0 : XC;
-        __syncthreads();  // every wave is done with the previous chunk
-        // ---- stage activation rows [c0, c0+nch) super-blocks: a wave per
-        // row, consecutive lanes on consecutive 16-byte pieces
-        if (!XF32) {
-            const int per_row = nch * 32;  // 16-byte pieces
-            for (int r = wave; r < nrows; r += W) {
-                const uint16_t* src = (const uint16_t*)a.x + xoffs[r] + (int64_t)c0 * 256;
-                for (int q = lane; q < per_row; q += 64)
-                    *(u32x4*)&xh[r * XSTRIDE + 8 * q] = *(const u32x4*)(src + 8 * q);
+        const int pieces = nch * 32, loads = (pieces + 63) / 64;
+        for (int r = wave; r < nrows; r += W) {
+            const uint8_t* src = (const uint8_t*)((const uint16_t*)a.x + xoffs[r] + (int64_t)c0 * 256);
+            for (int i = 0; i < loads; ++i) {
+                // lanes past the chunk re-read its first piece into the row's padding
+                const int piece = 64 * i + lane < pieces ? 64 * i + lane : 0;
+                dma16(src + 16 * piece,
+                      __builtin_amdgcn_readfirstlane(lds_addr((const uint8_t*)(dst + r * XSTRIDE) + 1024 * i)));
             }
+        }
+    };
+    if (!XF32) {
+        __syncthreads();  // the row offsets
+        issue_x(0, xh);
+    }
+    const uint16_t* xcur = xh;
+
+    int ci = 0;
+    for (int c0 = 0; c0 < nsb; c0 += XC, ++ci) {
+        const int nch = nsb - c0 < XC ? nsb - c0 : XC;
+        if (!XF32) {
+            wait_loads_le(0);  // this wave's copies of chunk ci have landed
+            __syncthreads();   // every wave's, and every wave is done with chunk ci - 1
+            if (c0 + XC < nsb) issue_x(c0 + XC, (ci & 1) ? xh : xl);
+            xcur = (ci & 1) ? xl : xh;
         } else {
+            __syncthreads();  // every wave is done with the previous chunk
+            // ---- stage activation rows [c0, c0+nch) super-blocks: a wave
+            // per row, consecutive lanes on consecutive 4-float pieces
             const int per_row = nch * 64;  // 4-float pieces
             for (int r = wave; r < nrows; r += W) {
                 const float* src = (const float*)a.x + xoffs[r] + (int64_t)c0 * 256;
@@ -185,8 +211,8 @@ __global__ __launch_bounds__(64 * W) void moe_mm_kernel(SkinnyArgs a) {
                     *(uint2*)&xl[r * XSTRIDE + 4 * q] = uint2{lo[0], lo[1]};
                 }
             }
+            __syncthreads();
         }
-        __syncthreads();
 
         for (int sb = c0; sb < c0 + nch; ++sb) {
             u32x4 nhd[2], nq0[2], nq1[2];
@@ -202,7 +228,7 @@ __global__ __launch_bounds__(64 * W) void moe_mm_kernel(SkinnyArgs a) {
 #pragma unroll
                     for (int i = 0; i < 8; ++i) {
                         const int o = xoff[mt] + sl + 32 * (i >> 2) + 8 * (i & 3);
-                        xa[i] = *(const u32x4*)&xh[o];
+                        xa[i] = *(const u32x4*)&xcur[o];
                         if (XF32) xb[i] = *(const u32x4*)&xl[o];
                     }
 #pragma unroll
@@ -257,8 +283,9 @@ __global__ __launch_bounds__(64 * W) void moe_mm_kernel(SkinnyArgs a) {
 }
 
 // Staged activations: up to 32 rows (no more than the routing holds) of XC
-// super-blocks, fp16 (plus the lo part for fp32 activations), within 76 KB so
-// that two workgroups share a CU.
+// super-blocks, fp16 hi and lo parts for fp32 activations (within 76 KB so
+// that two workgroups share a CU), or two chunk buffers of two super-blocks
+// for fp16 activations.
 template <int W, bool GLU, bool XF32>
 static void launch_mm(SkinnyArgs a, int64_t grid_tiles, hipStream_t s) {
     constexpr int64_t kBudget = 76 * 1024;
@@ -268,11 +295,13 @@ static void launch_mm(SkinnyArgs a, int64_t grid_tiles, hipStream_t s) {
     const int64_t rows = a.rows_cap < kMoeTileRows ? a.rows_cap : kMoeTileRows;
     int64_t xc = kBudget / (parts * rows * (256 * 2 + 16));
     xc = xc < 1 ? 1 : xc > nsb ? nsb : xc;
+    // fp16: two buffers of two super-blocks per row (whole 1 KB copies)
+    if (!XF32) xc = 2;
     a.xch = (int)xc;
     a.xstride = (int)(xc * 256 + 8);
     const int64_t part_bytes = (rows * a.xstride * 2 + 15) / 16 * 16;
-    a.red_off = (int)part_bytes;  // start of the lo part
-    const size_t lds = (size_t)(parts * part_bytes);
+    a.red_off = (int)part_bytes;  // start of the lo part, or of the second buffer
+    const size_t lds = (size_t)(2 * part_bytes);
     const dim3 grid((unsigned)((a.n + ROWS - 1) / ROWS), (unsigned)grid_tiles);
     hipLaunchKernelGGL((moe_mm_kernel<W, GLU, XF32>), grid, dim3(64 * W), lds, s, a);
 }
