@@ -69,8 +69,8 @@ template <int W, bool GLU, bool XF32>
 __global__ __launch_bounds__(64 * W) void moe_mm_kernel(SkinnyArgs a) {
     constexpr int ROWS = GLU ? 16 * W : 32 * W;  // output columns of the workgroup
     extern __shared__ __align__(16) uint8_t smem[];
-    // fp32 x: [32][xstride] hi and lo parts; fp16 x: two [32][xstride]
-    // chunk buffers, filled alternately
+    // fp32 x: [32][xstride] hi and lo parts (then the raw rows); fp16 x:
+    // two [32][xstride] chunk buffers, filled alternately
     uint16_t* xh = (uint16_t*)smem;
     uint16_t* xl = (uint16_t*)(smem + a.red_off);
     const int XC = a.xch, XSTRIDE = a.xstride;
@@ -173,10 +173,19 @@ __global__ __launch_bounds__(64 * W) void moe_mm_kernel(SkinnyArgs a) {
             }
         }
     };
-    if (!XF32) {
-        __syncthreads();  // the row offsets
-        issue_x(0, xh);
-    }
+    // fp32 activations: each chunk (one super-block) of the rows is copied
+    // as loaded into a raw buffer one chunk ahead, then split into the hi
+    // and lo rows in LDS.
+    uint8_t* xraw = smem + 2 * a.red_off;  // [32][1 KB]
+    auto issue_raw = [&](int c0) {
+        for (int r = wave; r < nrows; r += W) {
+            const uint8_t* src = (const uint8_t*)((const float*)a.x + xoffs[r] + (int64_t)c0 * 256);
+            dma16(src + 16 * lane, __builtin_amdgcn_readfirstlane(lds_addr(xraw + 1024 * r)));
+        }
+    };
+    __syncthreads();  // the row offsets and exponents
+    if (!XF32) issue_x(0, xh);
+    else issue_raw(0);
     const uint16_t* xcur = xh;
 
     int ci = 0;
@@ -188,14 +197,15 @@ __global__ __launch_bounds__(64 * W) void moe_mm_kernel(SkinnyArgs a) {
             if (c0 + XC < nsb) issue_x(c0 + XC, (ci & 1) ? xh : xl);
             xcur = (ci & 1) ? xl : xh;
         } else {
-            __syncthreads();  // every wave is done with the previous chunk
-            // ---- stage activation rows [c0, c0+nch) super-blocks: a wave
-            // per row, consecutive lanes on consecutive 4-float pieces
-            const int per_row = nch * 64;  // 4-float pieces
+            wait_loads_le(0);  // this wave's copies of the chunk have landed
+            __syncthreads();   // every wave's, and every wave is done with the previous chunk
+            // ---- split activation rows of super-block c0 (XC = 1): a wave
+            // per row, lane q on columns 4q..4q+3
             for (int r = wave; r < nrows; r += W) {
-                const float* src = (const float*)a.x + xoffs[r] + (int64_t)c0 * 256;
+                const float* src = (const float*)(xraw + 1024 * r);
                 const int nex = -sexp[r];
-                for (int q = lane; q < per_row; q += 64) {
+                {
+                    const int q = lane;
                     const float4_t v = *(const float4_t*)(src + 4 * q);
                     uint32_t hi[2], lo[2];
 #pragma unroll
@@ -211,7 +221,8 @@ __global__ __launch_bounds__(64 * W) void moe_mm_kernel(SkinnyArgs a) {
                     *(uint2*)&xl[r * XSTRIDE + 4 * q] = uint2{lo[0], lo[1]};
                 }
             }
-            __syncthreads();
+            __syncthreads();  // hi and lo rows ready, raw buffer free
+            if (c0 + 1 < nsb) issue_raw(c0 + 1);
         }
 
         for (int sb = c0; sb < c0 + nch; ++sb) {
@@ -282,26 +293,21 @@ __global__ __launch_bounds__(64 * W) void moe_mm_kernel(SkinnyArgs a) {
     }
 }
 
-// Staged activations: up to 32 rows (no more than the routing holds) of XC
-// super-blocks, fp16 hi and lo parts for fp32 activations (within 76 KB so
-// that two workgroups share a CU), or two chunk buffers of two super-blocks
-// for fp16 activations.
+// Staged activations, up to 32 rows (no more than the routing holds), each
+// filled by direct-to-LDS copies one chunk ahead: fp16 activations in two
+// buffers of two super-blocks per row (whole 1 KB copies); fp32 activations
+// as hi and lo rows of one super-block beside a raw 1 KB row buffer.  About
+// 66 KB for 32 rows, so two workgroups share a CU.
 template <int W, bool GLU, bool XF32>
 static void launch_mm(SkinnyArgs a, int64_t grid_tiles, hipStream_t s) {
-    constexpr int64_t kBudget = 76 * 1024;
     constexpr int ROWS = GLU ? 16 * W : 32 * W;
-    const int64_t nsb = a.k / 256;
-    const int64_t parts = XF32 ? 2 : 1;
     const int64_t rows = a.rows_cap < kMoeTileRows ? a.rows_cap : kMoeTileRows;
-    int64_t xc = kBudget / (parts * rows * (256 * 2 + 16));
-    xc = xc < 1 ? 1 : xc > nsb ? nsb : xc;
-    // fp16: two buffers of two super-blocks per row (whole 1 KB copies)
-    if (!XF32) xc = 2;
+    const int64_t xc = XF32 ? 1 : 2;
     a.xch = (int)xc;
     a.xstride = (int)(xc * 256 + 8);
     const int64_t part_bytes = (rows * a.xstride * 2 + 15) / 16 * 16;
     a.red_off = (int)part_bytes;  // start of the lo part, or of the second buffer
-    const size_t lds = (size_t)(2 * part_bytes);
+    const size_t lds = (size_t)(2 * part_bytes + (XF32 ? rows * 1024 : 0));
     const dim3 grid((unsigned)((a.n + ROWS - 1) / ROWS), (unsigned)grid_tiles);
     hipLaunchKernelGGL((moe_mm_kernel<W, GLU, XF32>), grid, dim3(64 * W), lds, s, a);
 }
