@@ -117,6 +117,27 @@ def test_qmm_id_f32_activations(kq, kind, layout, mixed, E, T, top_k):
     check_tol(to_f64(y), ref, s, TAU["f32"], f"qmm_id f32 {kind}")
 
 
+@pytest.mark.parametrize("x_dt", ["f16", "f32"])
+@pytest.mark.parametrize("layout", [0, 1])
+def test_qmm_id_tiles_over_16_rows_long_k(kq, x_dt, layout):
+    """Q4_K routed product with tiles of more than 16 rows over five
+    super-blocks of K: the activation rows go through LDS in several
+    one-chunk-ahead copies (fp16: chunks of two super-blocks, the last of
+    one; fp32: one super-block at a time), every output against the oracle."""
+    E, T, top_k, n, k = 4, 70, 4, 96, 1280
+    rng, w, stride, ids, scores = _moe_case("q4_k", E, n, k, T, top_k, 60 + layout)
+    x_rows = T if layout == 0 else T * top_k
+    x = synth.activations(rng, (x_rows, k), x_dt)
+    _say("qmm_id long k", x_dt, layout)
+    y = empty((T, n), "f32")
+    ws = _ws(kq, E, T, top_k, n)
+    kq.kq_qmm_id("q4_k", to_dev(w), E, n, k, stride, to_dev(x, x_dt), layout, to_dev(ids), T,
+                 top_k, to_dev(scores), y, ws)
+    torch.cuda.synchronize()
+    ref, s = oracle.qmm_id("q4_k", w, E, n, k, stride, x, x_dt, layout == 1, ids, T, top_k, scores)
+    check_tol(to_f64(y), ref, s, TAU[x_dt], f"qmm_id long k {x_dt}")
+
+
 @pytest.mark.parametrize("T", [1, 40])
 def test_reused_schedule_matches_rebuilt(kq, T):
     # gate/up then down on one workspace: the down call that keeps the
