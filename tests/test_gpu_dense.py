@@ -273,6 +273,22 @@ def test_qmm_c3_full_sampled(kq, which, m):
     _sampled(kq, "kq_qmm", cases[0], x, "bf16", m, "bf16")
 
 
+@pytest.mark.parametrize("kind", ["q4_k", "q8_0"])
+@pytest.mark.parametrize("m,n", [(600, 8242), (2100, 11015)])
+def test_qmm_large_tiles_ragged(kq, kind, m, n):
+    """Grids large enough for the 256x128 (first shape) and 256x256 tiles,
+    ragged in M and N, every output against the oracle; Q8_0 rows of an odd
+    block count end in half a K step."""
+    k = 256 if kind == "q4_k" else 288
+    rng = _rng(3200 + m)
+    w = synth.weight_blocks(kind, rng, n, k)
+    x = synth.activations(rng, (m, k), "bf16")
+    _say("qmm large tiles", kind, m, n, k)
+    got = _run(kq, "kq_qmm", kind, w, n, k, x, "bf16", m, "f32")
+    ref, s = oracle.qmm(kind, w, n, k, x, "bf16", m)
+    check_tol(got, ref, s, TAU["bf16"], f"qmm {kind} {m}x{n}x{k}")
+
+
 @pytest.mark.parametrize("x_dt", ["f16", "bf16"])
 def test_qmm_tq1_large_tiles_ragged(kq, x_dt):
     """TQ1 products with enough output tiles for the 256x256 tile, ragged in

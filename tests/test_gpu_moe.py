@@ -119,16 +119,17 @@ def test_qmm_id_f32_activations(kq, kind, layout, mixed, E, T, top_k):
 
 @pytest.mark.parametrize("x_dt", ["f16", "f32"])
 @pytest.mark.parametrize("layout", [0, 1])
-def test_qmm_id_tiles_over_16_rows_long_k(kq, x_dt, layout):
-    """Q4_K routed product with tiles of more than 16 rows over five
-    super-blocks of K: the activation rows go through LDS in several
-    one-chunk-ahead copies (fp16: chunks of two super-blocks, the last of
-    one; fp32: one super-block at a time), every output against the oracle."""
-    E, T, top_k, n, k = 4, 70, 4, 96, 1280
-    rng, w, stride, ids, scores = _moe_case("q4_k", E, n, k, T, top_k, 60 + layout)
+@pytest.mark.parametrize("nsb", [1, 5])
+def test_qmm_id_tiles_over_16_rows_long_k(kq, x_dt, layout, nsb):
+    """Q4_K routed product with tiles of more than 16 rows over one and five
+    super-blocks of K: the activation rows go through LDS in one-chunk-ahead
+    copies (fp16: chunks of two super-blocks, the last possibly of one; fp32:
+    one super-block at a time), every output against the oracle."""
+    E, T, top_k, n, k = 4, 70, 4, 96, 256 * nsb
+    rng, w, stride, ids, scores = _moe_case("q4_k", E, n, k, T, top_k, 60 + layout + 2 * nsb)
     x_rows = T if layout == 0 else T * top_k
     x = synth.activations(rng, (x_rows, k), x_dt)
-    _say("qmm_id long k", x_dt, layout)
+    _say("qmm_id long k", x_dt, layout, nsb)
     y = empty((T, n), "f32")
     ws = _ws(kq, E, T, top_k, n)
     kq.kq_qmm_id("q4_k", to_dev(w), E, n, k, stride, to_dev(x, x_dt), layout, to_dev(ids), T,
