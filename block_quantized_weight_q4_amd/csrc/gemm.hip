@@ -440,13 +440,17 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const uint8_t* __restrict
     };
 
     // Pipeline: LDS stage s%2 holds step s; while the MFMAs of step s run,
-    // step s+1 (fetched an iteration earlier) is decoded into the other
-    // stage, and step s+2 is fetched into the freed registers.  One barrier
-    // per step.  The decode is placed after the last MFMAs of the step are
-    // issued, so the loads it consumes have a whole step of matrix work to
-    // land (5-9 % faster than decoding after the first MFMAs at M = 512).
-    // (Fetching a further step ahead, with a second register set, was
-    // measured no faster.)
+    // step s+1 (fetched earlier) is decoded into the other stage, and the
+    // freed registers take the fetch of a later step.  One barrier per step,
+    // which keeps the waves in phase, so a decode overlaps matrix work only
+    // if it sits among the step's MFMAs.  Measured per codec:
+    //  - Q4_K and TQ1: two register sets, fetching three steps ahead, and the
+    //    decode after the second of the four MFMA sub-steps (loads have over
+    //    a step to land, and the decode runs under the remaining MFMAs);
+    //  - Q8_0: one register set, fetching two steps ahead, and the decode
+    //    after the last sub-step (the loads have a whole step to land).
+    constexpr int kAhead = C == Q8_0 ? 2 : 3;              // steps fetched ahead
+    constexpr int kStashKs = C == Q8_0 ? BK / 16 - 1 : 1;  // sub-step the decode follows
     auto step = [&](int s, Regs& R) {
         const int st = s & 1;
         u32x4 af[FM], bf[FN];
@@ -461,7 +465,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const uint8_t* __restrict
                 for (int j = 0; j < FN; ++j) acc[i][j] = Op16<XDT>::mma(af[i], bf[j], acc[i][j]);
             // (on the last step the stash fills the idle stage with data
             // that is never read)
-            if (ks == BK / 16 - 1 && (FULL || s + 1 < steps)) stash(s + 1, st ^ 1, R);
+            if (ks == kStashKs && (FULL || s + 1 < steps)) stash(s + 1, st ^ 1, R);
             if (ks + 1 < BK / 16) {
 #pragma unroll
                 for (int i = 0; i < FM; ++i) af[i] = naf[i];
@@ -469,15 +473,28 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const uint8_t* __restrict
                 for (int j = 0; j < FN; ++j) bf[j] = nbf[j];
             }
         }
-        if (FULL) fetch(s + 2 < steps ? s + 2 : steps - 1, R);
-        else if (s + 2 < steps) fetch(s + 2, R);
+        if (FULL) fetch(s + kAhead < steps ? s + kAhead : steps - 1, R);
+        else if (s + kAhead < steps) fetch(s + kAhead, R);
         __syncthreads();
     };
     fetch(0, ra);
     stash(0, 0, ra);
-    if (steps > 1) fetch(1, ra);
-    __syncthreads();
-    for (int s = 0; s < steps; ++s) step(s, ra);
+    if constexpr (kAhead == 3) {
+        // step j's fetch lives in rb for odd j, in ra for even j
+        Regs rb;
+        if (steps > 1) fetch(1, rb);
+        if (FULL) fetch(steps > 2 ? 2 : steps - 1, ra);
+        else if (steps > 2) fetch(2, ra);
+        __syncthreads();
+        for (int s = 0; s < steps; s += 2) {
+            step(s, rb);
+            if (s + 1 < steps) step(s + 1, ra);
+        }
+    } else {
+        if (steps > 1) fetch(1, ra);
+        __syncthreads();
+        for (int s = 0; s < steps; ++s) step(s, ra);
+    }
 
     // epilogue: lane holds column l%32 and rows 8*(v/4) + 4*(l/32) + v%4
 #pragma unroll
