@@ -242,9 +242,12 @@ static void launch_cfg2(SkinnyArgs a, int64_t rows_max, int64_t tiles_y, hipStre
 
 // LDS per workgroup is at most 160 KB; the staged activation rows grow with
 // the row count, so wide chunks are used only while they fit.  Measured on
-// the decode shapes: two buffers (one chunk in flight) beat deeper rings.
+// the decode shapes (batch 8): two buffers (one chunk in flight) beat deeper
+// rings; sixteen waves on 8-block chunks for long rows, eight waves on
+// 4-block chunks otherwise (the spare waves hide latency: only two to four
+// workgroups fit per CU); pairs of 16-row tiles per workgroup were slower.
 constexpr size_t kLdsMax = 160 * 1024;
-static_assert(lds_cfg2<2, 2, 2, 2>(16) <= kLdsMax && lds_cfg2<1, 4, 4, 2>(16) <= kLdsMax,
+static_assert(lds_cfg2<2, 2, 2, 2>(16) <= kLdsMax && lds_cfg2<1, 4, 8, 2>(16) <= kLdsMax,
               "the fallback shapes hold 16 staged activation rows");
 
 hipError_t launch_mmv2_q4k(bool glu, const SkinnyArgs& a, int64_t grid_tiles, hipStream_t s) {
@@ -252,9 +255,9 @@ hipError_t launch_mmv2_q4k(bool glu, const SkinnyArgs& a, int64_t grid_tiles, hi
     const int64_t tiles = a.ws ? grid_tiles : (a.m + 15) / 16;
     const int64_t nsb = a.k / 256;
     if (glu) launch_cfg2<2, true, 2, 2, 2>(a, rows_max, tiles, s);
-    else if (nsb > 16 && lds_cfg2<1, 8, 8, 2>(rows_max) <= kLdsMax)
-        launch_cfg2<1, false, 8, 8, 2>(a, rows_max, tiles, s);
-    else launch_cfg2<1, false, 4, 4, 2>(a, rows_max, tiles, s);
+    else if (nsb > 16 && lds_cfg2<1, 8, 16, 2>(rows_max) <= kLdsMax)
+        launch_cfg2<1, false, 8, 16, 2>(a, rows_max, tiles, s);
+    else launch_cfg2<1, false, 4, 8, 2>(a, rows_max, tiles, s);
     return hipGetLastError();
 }
 
