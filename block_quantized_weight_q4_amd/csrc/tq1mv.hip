@@ -23,8 +23,8 @@
 // exact; accumulation is fp32.
 //
 // A workgroup owns 16 weight rows.  Their weights stream through LDS in
-// chunks of 8 or 16 blocks (coalesced global->LDS copies, double buffered);
-// the W waves (4 or 16) take the blocks of a chunk in turn and combine their
+// chunks of 16 blocks (coalesced global->LDS copies, double buffered);
+// the W waves (8 or 16) take the blocks of a chunk in turn and combine their
 // partial sums through LDS at the end.  Each half block issues all of its table and
 // activation reads before its first MFMA, so their LDS latency overlaps.
 #include "kq_device.h"
@@ -228,12 +228,14 @@ __global__ __launch_bounds__(64 * W) void tq1_mv_kernel(const uint8_t* __restric
 
 // Rows must start on 16-byte boundaries (a multiple of four blocks per row)
 // for the 16-byte copies, and the activation slots must fit in LDS.
-// Short rows: four waves and 8-block chunks, so that six workgroups fit in
-// one compute unit's LDS and every workgroup of the short-row shapes is
-// resident at once.  Long rows: sixteen waves and 16-block chunks (two
-// workgroups per compute unit), so that a compute unit holding one of the
-// few workgroups still has four waves per SIMD.
-using TqShort = TqCfg<4, 8>;   // rows of fewer than 64 blocks
+// Chunks of 16 blocks (448 bytes of a row) keep every chunk of a row on the
+// row's own 64-byte alignment; measured, chunks whose copies start on odd
+// 16-byte boundaries (4, 12 or 20 blocks) stream 30-130 % slower.
+// Short rows: eight waves (four workgroups per compute unit at 40 blocks).
+// Long rows: sixteen waves (two workgroups per compute unit), so that a
+// compute unit holding one of the few workgroups still has four waves per
+// SIMD.
+using TqShort = TqCfg<8, 16>;  // rows of fewer than 64 blocks
 using TqLong = TqCfg<16, 16>;
 
 bool tq1_mv_fits(int64_t k) {
@@ -251,7 +253,7 @@ hipError_t launch_tq1_mv(const uint8_t* w, int64_t n, int64_t k, const uint16_t*
         hipLaunchKernelGGL((tq1_mv_kernel<16, 16>), grid, dim3(64 * 16),
                            TqLong::lds_bytes(nblk), s, w, n, k, x, y, y_dt);
     } else {
-        hipLaunchKernelGGL((tq1_mv_kernel<4, 8>), grid, dim3(64 * 4),
+        hipLaunchKernelGGL((tq1_mv_kernel<8, 16>), grid, dim3(64 * 8),
                            TqShort::lds_bytes(nblk), s, w, n, k, x, y, y_dt);
     }
     return hipGetLastError();
