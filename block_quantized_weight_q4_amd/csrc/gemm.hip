@@ -93,7 +93,7 @@ template <> struct WTile<Q4_K> {
     // Quarter q of step s: quant bytes 32c+8q..+8 -> low nibbles to columns
     // 8q+i, high nibbles to 32+8q+i.
     struct RawQ { u32x4 hd; u32x2 q; };
-    static __device__ __forceinline__ void fetch_q(const uint8_t* row, int s, int q, RawQ& r) {
+    static __device__ __forceinline__ void fetch_q(const uint8_t* row, int s, int q, RawQ& r, bool) {
         const uint8_t* blk = row + (s >> 2) * 144;
         r.hd = *(const u32x4*)blk;
         r.q = *(const u32x2*)(blk + 16 + 32 * (s & 3) + 8 * q);
@@ -175,6 +175,49 @@ template <> struct WTile<Q8_0> {
         for (int i = 0; i < 8; ++i) lo[i] = v[i], hi[i] = v[8 + i];
         col_lo = 32 * h;
         col_hi = 32 * h + 16;
+    }
+    // Quarter q of step s: quants 16 (q%2) .. +15 of block q/2, i.e. columns
+    // 16q .. 16q+15.  Block 0's quants start 2 bytes past a word, so its four
+    // words are shifted by 16 bits with the first half-word after them;
+    // block 1's quants start on a word.
+    struct RawQ { uint32_t w[4]; uint32_t next; uint32_t sc; };
+    static __device__ __forceinline__ void fetch_q(const uint8_t* row, int s, int q, RawQ& r,
+                                                   bool rows_4b_aligned) {
+        const int h = q >> 1, hh = q & 1;
+        const uint8_t* blk = row + 68 * s + 34 * h;
+        const uint8_t* qb = blk + 16 * hh + (h ? 2 : 0);
+        if (rows_4b_aligned) {
+            const uint32_t* p = (const uint32_t*)qb;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) r.w[i] = p[i];
+        } else {
+            const uint16_t* p = (const uint16_t*)qb;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) r.w[i] = (uint32_t)p[2 * i] | ((uint32_t)p[2 * i + 1] << 16);
+        }
+        r.next = *(const uint16_t*)(blk + 16 + 16 * hh);
+        r.sc = *(const uint16_t*)blk;
+    }
+    template <int XDT>
+    static __device__ __forceinline__ void decode_q(const RawQ& r, int s, int q, uint32_t (&lo)[4],
+                                                    uint32_t (&hi)[4], int& col_lo, int& col_hi) {
+        uint32_t sh = (q >> 1) ? 0u : 16u;
+        asm("" : "+v"(sh));
+        const float d = half_bits_to_float(r.sc);
+        const float nd = -128.0f * d;
+        auto byte = [](uint32_t v, int j) { return (float)((v >> (8 * j)) & 0xffu); };
+        uint32_t v[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t next = j < 3 ? r.w[j + 1] : r.next;
+            const uint32_t u = __builtin_amdgcn_alignbit(next, r.w[j], sh) ^ 0x80808080u;
+            v[2 * j] = Op16<XDT>::pack(__builtin_fmaf(d, byte(u, 0), nd), __builtin_fmaf(d, byte(u, 1), nd));
+            v[2 * j + 1] = Op16<XDT>::pack(__builtin_fmaf(d, byte(u, 2), nd), __builtin_fmaf(d, byte(u, 3), nd));
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lo[i] = v[i], hi[i] = v[4 + i];
+        col_lo = 16 * q;
+        col_hi = 16 * q + 8;
     }
 };
 
@@ -270,7 +313,7 @@ template <> struct WTile<TQ1> {
     }
     // Quarter q of step s: columns 16e..16e+15 of the block, e = 4 (s%2) + q.
     using RawQ = Raw;
-    static __device__ __forceinline__ void fetch_q(const uint8_t* row, int s, int, RawQ& r) {
+    static __device__ __forceinline__ void fetch_q(const uint8_t* row, int s, int, RawQ& r, bool) {
         fetch(row, s, 0, r, true);
     }
     template <int XDT>
@@ -321,12 +364,15 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const uint8_t* __restrict
     const int steps = (int)((k + BK - 1) / BK);
 
     // weight role: tile row wr and part wh of each step, a half (wh < 2) or,
-    // when the threads are four times the tile's rows (Q4_K and TQ1), a
-    // quarter (wh < 4), so that every wave shares the decoding.  Neighbouring
-    // threads read the parts of one row (contiguous bytes), except for TQ1,
-    // whose decoding branches on the part: there each wave holds one part,
-    // so it runs one branch (measured faster for TQ1, slower for the others).
-    constexpr bool QM = 4 * BN == NT && C != Q8_0;
+    // when the threads are four times the tile's rows, a quarter (wh < 4), so
+    // that every wave shares the decoding.  Q8_0 takes quarters only in
+    // tiles of at most 128 activation rows (7-8 % faster there, 3-6 %
+    // slower in the 256-row tiles, where half the threads decoding keeps the
+    // rest on matrix work).  Neighbouring threads read the parts of one row
+    // (contiguous bytes), except for TQ1, whose decoding branches on the
+    // part: there each wave holds one part, so it runs one branch (measured
+    // faster for TQ1, slower for the others).
+    constexpr bool QM = 4 * BN == NT && (C != Q8_0 || BM <= 128);
     constexpr int NPART = QM ? 4 : 2;
     constexpr bool kWaveParts = C == TQ1;
     const int wr = kWaveParts ? tid % BN : tid / NPART, wh = kWaveParts ? tid / BN : tid % NPART;
@@ -373,7 +419,9 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const uint8_t* __restrict
             }
         }
         if constexpr (QM) {
-            WT::fetch_q(wrow, s, wh, R.raw);
+            // a Q8_0 quarter past the row end reads block 0 of the step instead
+            const int qf = (C == Q8_0 && (int64_t)(2 * s + (wh >> 1)) * 32 >= k) ? (wh & 1) : wh;
+            WT::fetch_q(wrow, s, qf, R.raw, (row_bytes & 3) == 0);
         } else if (FULL) {
             // a Q8_0 half past the row end reads the step's first block instead
             const int hf = (C == Q8_0 && (int64_t)(2 * s + wh) * 32 >= k) ? 0 : wh;
@@ -397,6 +445,11 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const uint8_t* __restrict
             uint32_t lo[4], hi[4];
             int cl, ch;
             WT::template decode_q<XDT>(R.raw, s, wh, lo, hi, cl, ch);
+            if (C == Q8_0 && (int64_t)(2 * s + (wh >> 1)) * 32 >= k) {
+                // a quarter past the row end (odd block count) would reach stored outputs
+#pragma unroll
+                for (int i = 0; i < 4; ++i) lo[i] = hi[i] = 0u;
+            }
             *(u32x4*)&Bs[wr * LDS_STRIDE + cl] = u32x4{lo[0], lo[1], lo[2], lo[3]};
             *(u32x4*)&Bs[wr * LDS_STRIDE + ch] = u32x4{hi[0], hi[1], hi[2], hi[3]};
         } else if (FULL || wrole) {

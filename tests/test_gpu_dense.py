@@ -274,11 +274,11 @@ def test_qmm_c3_full_sampled(kq, which, m):
 
 
 @pytest.mark.parametrize("kind", ["q4_k", "q8_0"])
-@pytest.mark.parametrize("m,n", [(600, 8242), (2100, 11015)])
+@pytest.mark.parametrize("m,n", [(300, 8242), (600, 8242), (2100, 11015)])
 def test_qmm_large_tiles_ragged(kq, kind, m, n):
-    """Grids large enough for the 256x128 (first shape) and 256x256 tiles,
-    ragged in M and N, every output against the oracle; Q8_0 rows of an odd
-    block count end in half a K step."""
+    """Grids large enough for the 128x128, 256x128 and 256x256 tiles (in
+    that order), ragged in M and N, every output against the oracle; Q8_0
+    rows of an odd block count end in half a K step."""
     k = 256 if kind == "q4_k" else 288
     rng = _rng(3200 + m)
     w = synth.weight_blocks(kind, rng, n, k)
