@@ -232,6 +232,23 @@ def main():
         stages.append(Stage("moe_c4_decode", dec_calls, len(dec_calls) * 8 * per_expert,
                             len(dec_calls) * 8 * 3 * 2 * F * H, tokens=len(dec_calls),
                             note="1 token, top-8 of 128"))
+        # decode as a dependency chain: each token's mixed output (fp16) is the
+        # next token's activation row, so no layer overlaps the one before it
+        cx = [d16(c["x"][:1], torch.float16), torch.empty((1, H), dtype=torch.float16, device=dev)]
+
+        def chain_layer(t):
+            src, dst = cx[t % 2], cx[(t + 1) % 2]
+            kq.kq_moe_glu("q4_k", gate, up, E, F, H, c["gate_stride"], src, ids[t:t + 1], 1, top_k,
+                          h[:1], mws)
+            kq.kq_qmm_id("q4_k", down, E, H, F, c["down_stride"], h[:1],
+                         kq.LAYOUT_SLOTTED | kq.REUSE_SCHEDULE, ids[t:t + 1], 1, top_k,
+                         scores[t:t + 1], dst, mws)
+
+        chain_calls = [lambda t=t: chain_layer(t) for t in range(0, 64)]
+        stages.append(Stage("moe_c4_decode_chain", chain_calls, len(chain_calls) * 8 * per_expert,
+                            len(chain_calls) * 8 * 3 * 2 * F * H, tokens=len(chain_calls),
+                            note="1 token, top-8 of 128, each token's fp16 output feeds the next "
+                                 "(values may overflow fp16; the work is the same)"))
         pre_calls = [lambda layer=layer, T=T: layer(0, T) for _ in range(2)]
         used = len(np.unique(c["ids"]))
         stages.append(Stage("moe_c4_prefill", pre_calls, 2 * used * per_expert,
