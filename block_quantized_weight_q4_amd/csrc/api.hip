@@ -342,7 +342,7 @@ kq_status kq_moe_glu(kq_type t, const void* gate_w, const void* up_w, int64_t n_
                      int64_t n, int64_t k, int64_t expert_stride, const void* x, kq_dtype x_dt,
                      const uint32_t* ids, int64_t n_tokens, int64_t top_k, int act, void* h,
                      kq_dtype h_dt, void* workspace, size_t workspace_bytes, void* stream) {
-    if (act != KQ_ACT_SILU) return fail(KQ_ERR_UNSUPPORTED, "unknown GLU activation");
+    if (act != KQ_ACT_SILU && act != KQ_ACT_GELU_TANH) return fail(KQ_ERR_UNSUPPORTED, "unknown GLU activation");
     if (!up_w) return fail(KQ_ERR_INVALID_ARG, "null up weights");
     const int64_t rows = (n_tokens > 0 && top_k > 0 && n_tokens <= INT32_MAX / top_k) ? n_tokens * top_k : 0;
     int64_t row_bytes;
@@ -384,6 +384,7 @@ kq_status kq_moe_glu(kq_type t, const void* gate_w, const void* up_w, int64_t n_
     a.y = h;
     a.y_dt = h_dt;
     a.y_row = n;
+    a.act = act;
     if (direct) return launched(kq::launch_moe_glu1(a, s));
     return launched(kq::launch_skinny(t, x_dt, true, a, L.max_tiles, s));
 }

@@ -127,4 +127,18 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
+// GLU activations (h = act(g) * u), kq_moe_glu's KQ_ACT_SILU and
+// KQ_ACT_GELU_TANH
+__device__ __forceinline__ float silu_fast(float z) { return z / (1.0f + __expf(-z)); }
+// gelu with the tanh approximation, z/2 (1 + tanh(y)) with y = sqrt(2/pi)
+// (z + 0.044715 z^3), written as z / (1 + e^(-2y)) (the same function)
+__device__ __forceinline__ float gelu_tanh_fast(float z) {
+    const float y2 = 1.5957691216057308f * z * (1.0f + 0.044715f * z * z);  // 2y
+    return z / (1.0f + __expf(-y2));
+}
+// h = act(g) * u for the GLU epilogues; act is uniform over the launch
+__device__ __forceinline__ float glu_act(int act, float g, float u) {
+    return (act == 1 ? gelu_tanh_fast(g) : silu_fast(g)) * u;
+}
+
 }  // namespace kq

@@ -48,6 +48,7 @@ struct SkinnyArgs {
     int y_dt;              // output dtype
     int64_t y_row;         // elements between output rows
     int64_t rows_cap;      // routed: most rows any schedule tile can hold
+    int act;               // GLU: KQ_ACT_SILU or KQ_ACT_GELU_TANH
     // set by the launchers of the matrix-core kernels
     int xch;               // super-blocks of activations staged per chunk
     int xstride;           // elements (or bytes) between staged activation rows

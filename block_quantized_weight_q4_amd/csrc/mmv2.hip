@@ -210,7 +210,7 @@ __global__ __launch_bounds__(64 * W) void mmv2_q4k_f16_kernel(SkinnyArgs a) {
         const int64_t orow = perm ? (int64_t)perm[row0 + idx] : row0 + idx;
         if (GLU) {
             const int64_t n = n0 + n_l;
-            if (n < a.n) store_val(a.y, orow * a.y_row + n, a.y_dt, silu_fast(acc[0][v]) * acc[1][v]);
+            if (n < a.n) store_val(a.y, orow * a.y_row + n, a.y_dt, glu_act(a.act, acc[0][v], acc[1][v]));
         } else {
 #pragma unroll
             for (int m = 0; m < NM; ++m) {

@@ -383,7 +383,7 @@ __global__ __launch_bounds__(64 * W) void moe_glu1_kernel(SkinnyArgs a) {
         acc[st] += __shfl_xor(acc[st], 32);
     }
     const int64_t n = n0 + n_l;
-    if (g == 0 && n < a.n) store_val(a.y, slot * a.y_row + n, a.y_dt, silu_fast(acc[0]) * acc[1]);
+    if (g == 0 && n < a.n) store_val(a.y, slot * a.y_row + n, a.y_dt, glu_act(a.act, acc[0], acc[1]));
 }
 
 template <int C, int W>

@@ -281,7 +281,7 @@ __global__ __launch_bounds__(64 * W) void moe_mm_kernel(SkinnyArgs a) {
                 const int64_t n = n0 + 16 * wave + n_l;
                 if (n < a.n)
                     store_val(a.y, orow * a.y_row + n, a.y_dt,
-                              silu_fast(back(acc[0][mt][v])) * back(acc[1][mt][v]));
+                              glu_act(a.act, back(acc[0][mt][v]), back(acc[1][mt][v])));
             } else {
 #pragma unroll
                 for (int b = 0; b < 2; ++b) {

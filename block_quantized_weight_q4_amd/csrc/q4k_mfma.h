@@ -114,7 +114,6 @@ __device__ __forceinline__ void q4k_operands(const u32x4& hd, const u32x4& q0, c
     }
 }
 
-__device__ __forceinline__ float silu_fast(float z) { return z / (1.0f + __expf(-z)); }
 
 __device__ __forceinline__ void store_val(void* y, int64_t i, int dt, float v) {
     if (dt == F32) store_out<F32>(y, i, v);

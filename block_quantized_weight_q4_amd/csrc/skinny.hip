@@ -129,7 +129,6 @@ template <> struct Chunk<TQ1> {
     }
 };
 
-__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
 
 __device__ __forceinline__ void store_any(void* y, int64_t i, int dt, float v) {
     if (dt == F32) store_out<F32>(y, i, v);
@@ -211,7 +210,7 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs a) {
             if (i < cnt) {
                 const float g = wave_sum(acc[i]);
                 float v = g;
-                if (GLU) v = silu_f(g) * wave_sum(acc2[i]);
+                if (GLU) v = glu_act(a.act, g, wave_sum(acc2[i]));
                 if (lane == 0) store_any(a.y, orow[i] * a.y_row + j, a.y_dt, v);
             }
         }

@@ -21,7 +21,7 @@ __all__ = [
     "KQError", "TYPES", "lib", "kq_status_string", "kq_last_error", "kq_qk", "kq_block_bytes",
     "kq_row_bytes", "kq_dequantize", "kq_qmv", "kq_qmm", "kq_moe_workspace_bytes", "kq_moe_route",
     "kq_qmm_id", "kq_moe_glu", "moe_schedule", "SYMBOLS", "LAYOUT_SHARED", "LAYOUT_SLOTTED", "REUSE_SCHEDULE",
-    "ACT_SILU", "MOE_TILE_ROWS",
+    "ACT_SILU", "ACT_GELU_TANH", "MOE_TILE_ROWS",
 ]
 
 TYPES = {"q4_k": 0, "q8_0": 1, "tq1_g128": 2}
@@ -29,6 +29,7 @@ _DT = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 LAYOUT_SHARED, LAYOUT_SLOTTED = 0, 1
 REUSE_SCHEDULE = 0x100  # OR into the layout of a mixed kq_qmm_id: keep the workspace schedule
 ACT_SILU = 0
+ACT_GELU_TANH = 1
 MOE_TILE_ROWS = 32
 
 # Every function include/kq.h declares.

@@ -71,9 +71,13 @@ typedef enum kq_status {
  * directly, and a kq_moe_glu call for one token may leave no schedule. */
 enum { KQ_LAYOUT_SHARED = 0, KQ_LAYOUT_SLOTTED = 1, KQ_REUSE_SCHEDULE = 0x100 };
 
-/* GLU activations of kq_moe_glu: h = act(gate) * up.  silu(z) = z / (1 + e^-z).
- * mlx-kquant "bindings.cpp", moe_glu_gather_kq (act='silu', the default). */
-enum { KQ_ACT_SILU = 0 };
+/* GLU activations of kq_moe_glu: h = act(gate) * up.
+ * mlx-kquant "bindings.cpp", moe_glu_gather_kq: act='silu' (the default) or
+ * 'gelu' (the tanh approximation).
+ *   KQ_ACT_SILU       silu(z) = z / (1 + e^-z)
+ *   KQ_ACT_GELU_TANH  gelu(z) = z/2 * (1 + tanh(sqrt(2/pi) * (z + 0.044715 z^3)))
+ * Any other value -> KQ_ERR_UNSUPPORTED. */
+enum { KQ_ACT_SILU = 0, KQ_ACT_GELU_TANH = 1 };
 
 /* Human-readable name of a status code (static storage). */
 const char* kq_status_string(kq_status s);

@@ -407,14 +407,23 @@ int or_qmm_id(int type, const uint8_t* w, int64_t n_experts, int64_t n, int64_t 
 /* SiLU as defined: z / (1 + e^-z). */
 double or_silu(double z) { return z / (1.0 + exp(-z)); }
 
-/* [KQ] moe_glu_gather_kq with act='silu': for each token t and slot r with
- * e = ids[t,r]: g = W_gate[e] x_t, u = W_up[e] x_t, h = silu(g) * u, giving
- * h[T, top_k, n].  Also returns g, u and their |.|-sums sg, su (any of the
- * extra outputs may be NULL).  An invalid id poisons its h row with NaN. */
+/* [KQ] moe_glu_gather_kq, act='gelu': GELU by its tanh approximation,
+ * z/2 * (1 + tanh(sqrt(2/pi) * (z + 0.044715 z^3))). */
+double or_gelu_tanh(double z) {
+    const double c = sqrt(2.0 / 3.14159265358979323846);
+    return 0.5 * z * (1.0 + tanh(c * (z + 0.044715 * z * z * z)));
+}
+
+/* [KQ] moe_glu_gather_kq with act = 0 ('silu') or 1 ('gelu', tanh
+ * approximation): for each token t and slot r with e = ids[t,r]:
+ * g = W_gate[e] x_t, u = W_up[e] x_t, h = act(g) * u, giving h[T, top_k, n].
+ * Also returns g, u and their |.|-sums sg, su (any of the extra outputs may
+ * be NULL).  An invalid id poisons its h row with NaN. */
 int or_moe_glu(int type, const uint8_t* gate_w, const uint8_t* up_w, int64_t n_experts,
                int64_t n, int64_t k, int64_t expert_stride, const void* x, int x_dt,
-               const uint32_t* ids, int64_t T, int64_t top_k, double* h, double* g, double* u,
-               double* sg, double* su) {
+               const uint32_t* ids, int64_t T, int64_t top_k, int act, double* h, double* g,
+               double* u, double* sg, double* su) {
+    if (act != 0 && act != 1) return -3;
     int qk = or_qk(type);
     if (!qk || k % qk) return -1;
 #pragma omp parallel
@@ -445,7 +454,7 @@ int or_moe_glu(int type, const uint8_t* gate_w, const uint8_t* up_w, int64_t n_e
                     au += xv * ru[c];
                     mu += fabs(xv * ru[c]);
                 }
-                h[o] = or_silu(ag) * au;
+                h[o] = (act == 1 ? or_gelu_tanh(ag) : or_silu(ag)) * au;
                 if (g) g[o] = ag;
                 if (u) u[o] = au;
                 if (sg) sg[o] = mg;
@@ -468,7 +477,7 @@ int or_moe_layer(int type, const uint8_t* gate_w, const uint8_t* up_w, const uin
     double* h = (double*)malloc(sizeof(double) * T * top_k * ffn);
     if (!h) return -2;
     int rc = or_moe_glu(type, gate_w, up_w, n_experts, ffn, hidden, gate_stride, x, x_dt, ids,
-                        T, top_k, h, NULL, NULL, NULL, NULL);
+                        T, top_k, 0, h, NULL, NULL, NULL, NULL);
     if (rc) {
         free(h);
         return rc;

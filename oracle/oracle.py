@@ -17,7 +17,7 @@ from .build import build_oracle
 __all__ = [
     "TYPES", "DTYPES", "lib", "half_to_double", "bf16_to_double", "float_to_half_rne",
     "float_to_bf16_rne", "q4k_scale_min", "dequant", "dequant_as", "qmm", "qmm_points",
-    "qmm_id", "moe_glu", "moe_layer", "route", "silu", "num_threads",
+    "qmm_id", "moe_glu", "moe_layer", "route", "silu", "gelu_tanh", "num_threads",
 ]
 
 TYPES = {"q4_k": 0, "q8_0": 1, "tq1_g128": 2}
@@ -45,6 +45,8 @@ def lib():
         L.or_round_f32.argtypes = [C.c_double]
         L.or_silu.restype = C.c_double
         L.or_silu.argtypes = [C.c_double]
+        L.or_gelu_tanh.restype = C.c_double
+        L.or_gelu_tanh.argtypes = [C.c_double]
         L.or_q4k_scale_min.restype = None
         L.or_q4k_scale_min.argtypes = [P, C.c_int, C.POINTER(C.c_int), C.POINTER(C.c_int)]
         L.or_dequant.restype = C.c_int
@@ -60,7 +62,7 @@ def lib():
                                 i64, P, P, P]
         L.or_moe_glu.restype = C.c_int
         L.or_moe_glu.argtypes = [C.c_int, P, P, i64, i64, i64, i64, P, C.c_int, P, i64, i64,
-                                 P, P, P, P, P]
+                                 C.c_int, P, P, P, P, P]
         L.or_moe_layer.restype = C.c_int
         L.or_moe_layer.argtypes = [C.c_int, P, P, P, i64, i64, i64, i64, i64, P, C.c_int, P,
                                    i64, i64, P, P, P]
@@ -104,6 +106,10 @@ def float_to_bf16_rne(f: float) -> int:
 
 def silu(z: float) -> float:
     return lib().or_silu(float(z))
+
+
+def gelu_tanh(z: float) -> float:
+    return lib().or_gelu_tanh(float(z))
 
 
 def q4k_scale_min(scale_bytes, j: int):
@@ -177,15 +183,16 @@ def qmm_id(kind, w, n_experts, n, k, expert_stride, x, x_dt, slotted, ids, T, to
     return y, s
 
 
-def moe_glu(kind, gate_w, up_w, n_experts, n, k, expert_stride, x, x_dt, ids, T, top_k):
-    """dict of h, g, u, sg, su, each [T, top_k, n] float64."""
+def moe_glu(kind, gate_w, up_w, n_experts, n, k, expert_stride, x, x_dt, ids, T, top_k, act=0):
+    """dict of h, g, u, sg, su, each [T, top_k, n] float64; act 0 is silu,
+    1 gelu (tanh approximation)."""
     gate_w = _c(gate_w, np.uint8)
     up_w = _c(up_w, np.uint8)
     x = _c(x, np.float32 if x_dt == "f32" else np.uint16)
     ids = _c(ids, np.uint32)
     out = {key: np.empty((T, top_k, n), dtype=np.float64) for key in ("h", "g", "u", "sg", "su")}
     rc = lib().or_moe_glu(TYPES[kind], _p(gate_w), _p(up_w), n_experts, n, k, expert_stride,
-                          _p(x), DTYPES[x_dt], _p(ids), T, top_k, _p(out["h"]), _p(out["g"]),
+                          _p(x), DTYPES[x_dt], _p(ids), T, top_k, act, _p(out["h"]), _p(out["g"]),
                           _p(out["u"]), _p(out["sg"]), _p(out["su"]))
     if rc:
         raise ValueError(f"or_moe_glu failed ({rc})")

@@ -6,7 +6,8 @@ the dense rule |gpu - ref| <= tau * S.  The GLU output h = silu(g) * u is
 checked against the bound that the gate and up tolerances imply:
 |h - h_ref| <= E * (1 + u_h) + u_h * |h_ref| + eta_h,
 E = tau * (max|silu'| * |u| * S_g + |silu(g)| * S_u)
-with max|silu'| < 1.1, u_h the unit roundoff of h's storage type and eta_h
+with max|silu'| < 1.1 (for the tanh-approximated GELU: gelu and 1.13),
+u_h the unit roundoff of h's storage type and eta_h
 half its subnormal spacing (the stored value is the computed one, within E
 of h_ref, rounded once).
 """
@@ -224,7 +225,9 @@ def test_single_token_invalid_id_poisons(kq, x_dt, layout):
         assert np.isnan(got[1]).all() and not np.isnan(got[[0, 2]]).any()
 
 
-def _check_glu(h, ref, tau, h_dt, what):
+def _check_glu(h, ref, tau, h_dt, what, act=0):
+    """act 0: silu (|silu'| < 1.1); act 1: gelu, tanh approximation
+    (|gelu'| < 1.13)."""
     g, u, sg, su = ref["g"], ref["u"], ref["sg"], ref["su"]
     assert not np.isnan(h).any(), what
     if h_dt == "f16":
@@ -234,10 +237,13 @@ def _check_glu(h, ref, tau, h_dt, what):
         h, g, u, sg, su = h[~over], g[~over], u[~over], sg[~over], su[~over]
         ref = {"h": ref["h"][~over]}
     with np.errstate(over="ignore"):
-        sig = 1.0 / (1.0 + np.exp(-g))
+        if act == 1:
+            a_g, dmax = 0.5 * g * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (g + 0.044715 * g ** 3))), 1.13
+        else:
+            a_g, dmax = g / (1.0 + np.exp(-g)), 1.1
     # the computed h may be off by the product tolerance, and storing it
     # rounds once more: relative UNIT of the stored value, |h_ref| + that error
-    comp = tau * (1.1 * np.abs(u) * sg + np.abs(g * sig) * su)
+    comp = tau * (dmax * np.abs(u) * sg + np.abs(a_g) * su)
     bound = comp * (1.0 + UNIT[h_dt]) + UNIT[h_dt] * np.abs(ref["h"]) + ETA[h_dt]
     err = np.abs(h - ref["h"])
     bad = err > bound
@@ -264,6 +270,31 @@ def test_moe_glu_small(kq, kind, h_dt, x_dt, T):
     torch.cuda.synchronize()
     ref = oracle.moe_glu(kind, gate, up, E, n, k, stride, x, x_dt, ids, T, top_k)
     _check_glu(to_f64(h), ref, TAU[x_dt], h_dt, f"moe_glu {kind} {h_dt} x={x_dt}")
+
+
+@pytest.mark.parametrize("kind", ["q4_k", "q8_0", "tq1_g128"])
+@pytest.mark.parametrize("x_dt", ["f16", "f32"])
+@pytest.mark.parametrize("T", [1, 9, 40])
+def test_moe_glu_gelu(kq, kind, x_dt, T):
+    """act = GELU (tanh approximation) through every GLU kernel: one token
+    (read ids directly for Q4_K with fp16 x), tiles of <= 16 rows, and a
+    routing with tiles of more than 16 rows (T = 40, top-3 of 6)."""
+    E, n, k, top_k = 6, 80, {"q4_k": 512, "q8_0": 96, "tq1_g128": 256}[kind], 3
+    rng = synth.rng_for(95)
+    gate = synth.weight_blocks(kind, rng, E * n, k)
+    up = synth.weight_blocks(kind, rng, E * n, k)
+    stride = n * synth.row_bytes(kind, k)
+    ids = _ids(rng, T, E, top_k)
+    x = synth.activations(rng, (T, k), x_dt)
+    ref = oracle.moe_glu(kind, gate, up, E, n, k, stride, x, x_dt, ids, T, top_k, act=1)
+    for h_dt in ("f32", "f16"):
+        _say("moe_glu gelu", kind, x_dt, T, h_dt)
+        h = empty((T, top_k, n), h_dt)
+        ws = _ws(kq, E, T, top_k)
+        kq.kq_moe_glu(kind, to_dev(gate), to_dev(up), E, n, k, stride, to_dev(x, x_dt), to_dev(ids),
+                      T, top_k, h, ws, act=kq.ACT_GELU_TANH)
+        torch.cuda.synchronize()
+        _check_glu(to_f64(h), ref, TAU[x_dt], h_dt, f"moe_glu gelu {kind} {h_dt} x={x_dt} T={T}", act=1)
 
 
 @pytest.fixture(scope="module")

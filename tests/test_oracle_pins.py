@@ -425,6 +425,45 @@ def test_silu_definition(orc):
     assert orc.silu(0.0) == 0.0
 
 
+def test_gelu_tanh_pins(orc):
+    """GELU's tanh approximation (mlx-kquant "bindings.cpp", moe_glu_gather_kq,
+    act='gelu') against facts that do not restate its formula: the identity
+    gelu(z) - gelu(-z) = z (1/2 (1 + tanh y) + 1/2 (1 - tanh y) = 1), slope 1/2
+    at 0 and the limits z and 0, and the known closeness of the approximation to
+    the exact GELU z * Phi(z) (a dropped cubic term is off by 0.03 at z = 2)."""
+    from scipy.special import erf
+
+    zs = np.linspace(-12.0, 12.0, 961)
+    for z in zs:
+        assert orc.gelu_tanh(z) - orc.gelu_tanh(-z) == pytest.approx(z, rel=1e-14, abs=1e-14)
+    assert orc.gelu_tanh(0.0) == 0.0
+    assert orc.gelu_tanh(1e-8) / 1e-8 == pytest.approx(0.5, abs=1e-7)
+    assert orc.gelu_tanh(40.0) == 40.0 and abs(orc.gelu_tanh(-40.0)) < 1e-300
+    exact = 0.5 * zs * (1.0 + erf(zs / np.sqrt(2.0)))
+    diff = np.abs(np.array([orc.gelu_tanh(z) for z in zs]) - exact)
+    assert diff.max() < 1e-3 and diff.max() > 1e-5  # the approximation, not the exact function
+
+
+def test_moe_glu_act_selects_the_activation(orc):
+    """h = act(g) * u with the g and u the oracle returns: act 0 silu, act 1
+    gelu (tanh approximation); an unknown act is rejected."""
+    import synth
+
+    rng = _rng(31)
+    E, n, k, T, top_k = 3, 24, 256, 2, 2
+    gate = synth.weight_blocks("q4_k", rng, E * n, k)
+    up = synth.weight_blocks("q4_k", rng, E * n, k)
+    stride = n * synth.row_bytes("q4_k", k)
+    x = synth.activations(rng, (T, k), "f16")
+    ids = np.array([[0, 2], [1, 0]], np.uint32)
+    for act, fn in ((0, orc.silu), (1, orc.gelu_tanh)):
+        r = orc.moe_glu("q4_k", gate, up, E, n, k, stride, x, "f16", ids, T, top_k, act)
+        want = np.vectorize(fn)(r["g"]) * r["u"]
+        assert np.allclose(r["h"], want, rtol=1e-14, atol=0.0)
+    with pytest.raises(ValueError):
+        orc.moe_glu("q4_k", gate, up, E, n, k, stride, x, "f16", ids, T, top_k, 7)
+
+
 def test_moe_layer_one_expert_is_dense_composition(orc):
     import synth
 
