@@ -35,6 +35,23 @@ def test_header_declarations_match_binding(kq):
     assert _declared() == sorted(kq.SYMBOLS)
 
 
+def test_binding_constants_match_header():
+    """Every enum constant KQ_X of the header that the binding also names (X)
+    has the same value there."""
+    import block_quantized_weight_q4_amd.kq as mod
+
+    text = open(HEADER).read()
+    consts = {}
+    for body in re.findall(r"enum\s*\w*\s*\{([^}]*)\}", text):
+        for name, val in re.findall(r"\bKQ_(\w+)\s*=\s*(0x[0-9a-fA-F]+|\d+)", body):
+            consts[name] = int(val, 0)
+    assert "ACT_GELU_TANH" in consts
+    shared = [n for n in consts if hasattr(mod, n)]
+    assert {"ACT_SILU", "ACT_GELU_TANH"} <= set(shared)
+    for n in shared:
+        assert getattr(mod, n) == consts[n], n
+
+
 def test_library_exports_every_declared_symbol(kq):
     from block_quantized_weight_q4_amd._build import LIB
 
@@ -129,8 +146,9 @@ def test_expert_validation(kq):
     assert call(T=2**31 // 2 + 1) == 1        # rows > INT32_MAX
     assert call(n=2**26 + 1, stride=(2**26 + 1) * 144) == 1  # launch geometry bound on n
     assert call(y=P(base + (1 << 32) + 64)) == 1  # output overlaps x
-    assert L.kq_moe_glu(0, w, w, 8, 64, 256, 64 * 144, x, 1, ids, 4, 2, 9, y, 1, ws, 1 << 20,
-                        None) == 2            # unknown activation
+    for act in (2, 9, -1):
+        assert L.kq_moe_glu(0, w, w, 8, 64, 256, 64 * 144, x, 1, ids, 4, 2, act, y, 1, ws, 1 << 20,
+                            None) == 2        # unknown activation
 
 
 def test_product_path_has_no_fallback():
