@@ -62,7 +62,7 @@ __global__ __launch_bounds__(64 * W) void mmv2_q4k_f16_kernel(SkinnyArgs a) {
     const int xstride = a.xstride;            // bytes between staged activation rows
     const int wbytes = WPIECES * 16;
     const int bufbytes = a.red_off / S;       // bytes of one buffer
-    float* red = (float*)(smem + a.red_off);
+    float* red = (float*)smem;                // over buffer 0, used after the last chunk
 
     // Per-lane byte offsets of this wave's weight pieces inside a chunk,
     // counted from the tile's first row (so they stay small for any matrix
@@ -221,11 +221,14 @@ __global__ __launch_bounds__(64 * W) void mmv2_q4k_f16_kernel(SkinnyArgs a) {
     }
 }
 
+// The reduction area is only used after the last chunk's barrier, when every
+// chunk buffer is idle and no copy is in flight, so it overlays buffer 0.
 template <int NM, int C, int W, int S>
 static constexpr size_t lds_cfg2(int64_t rows_max) {
     const int64_t wbytes = (int64_t)NM * 16 * 9 * C * 16;
     const int64_t bufbytes = (wbytes + rows_max * (512 * C + 16) + 15) / 16 * 16;
-    return (size_t)(S * bufbytes + (int64_t)(W - 1) * NM * 4 * 64 * 4);
+    const int64_t red = (int64_t)(W - 1) * NM * 4 * 64 * 4;
+    return (size_t)(S * bufbytes > red ? S * bufbytes : red);
 }
 
 template <int NM, bool GLU, int C, int W, int S>
@@ -233,7 +236,7 @@ static void launch_cfg2(SkinnyArgs a, int64_t rows_max, int64_t tiles_y, hipStre
     const int64_t wbytes = (int64_t)NM * 16 * 9 * C * 16;
     a.xstride = 512 * C + 16;                      // padded staged activation row
     const int64_t bufbytes = (wbytes + rows_max * a.xstride + 15) / 16 * 16;
-    a.red_off = (int)(S * bufbytes);
+    a.red_off = (int)(S * bufbytes);  // bytes of the chunk buffers
     const size_t lds = lds_cfg2<NM, C, W, S>(rows_max);
     const int64_t rows_wg = GLU ? 16 : 16 * NM;
     const dim3 grid((unsigned)((a.n + rows_wg - 1) / rows_wg), (unsigned)tiles_y);
