@@ -60,9 +60,10 @@ kq_status check_weights(int t, const void* w, int64_t n, int64_t k, int64_t& row
 }
 
 // Bounds of the product kernels: a dispatch counts its work-items per
-// dimension in 32 bits (at most 32 threads per weight row), and offsets inside
-// one weight row, or a few rows of one tile, are 32-bit.
-constexpr int64_t kMaxN = (int64_t)1 << 26, kMaxK = (int64_t)1 << 24;
+// dimension in 32 bits (at most 32 threads per weight row), offsets inside
+// one weight row, or a few rows of one tile, are 32-bit, and grid.y (tiles of
+// activation rows, at least 16 rows each) stays below 65536.
+constexpr int64_t kMaxN = (int64_t)1 << 26, kMaxK = (int64_t)1 << 24, kMaxM = (int64_t)1 << 19;
 
 kq_status check_product_size(int64_t n, int64_t k) {
     if (n > kMaxN) return fail(KQ_ERR_INVALID_ARG, "n exceeds 2^26 weight rows");
@@ -77,6 +78,7 @@ kq_status check_product(kq_type t, const void* w, int64_t n, int64_t k, const vo
     if ((st = check_product_size(n, k))) return st;
     if (!valid_dt(x_dt) || !valid_dt(y_dt)) return fail(KQ_ERR_UNSUPPORTED, "unknown dtype");
     if (m <= 0) return fail(KQ_ERR_INVALID_ARG, "m must be positive");
+    if (m > kMaxM) return fail(KQ_ERR_INVALID_ARG, "m exceeds 2^19 activation rows");
     if (!x || !y) return fail(KQ_ERR_INVALID_ARG, "null activation or output pointer");
     if (!aligned(x, 16) || !aligned(y, 16)) return fail(KQ_ERR_INVALID_ARG, "x and y must be 16-byte aligned");
     int64_t wb, xb, yb;
@@ -194,6 +196,7 @@ size_t kq_moe_workspace_bytes(int64_t n_experts, int64_t n_tokens, int64_t top_k
 }
 
 static const int64_t kMaxExperts = 4096;
+static const int64_t kMaxGridY = 65535;
 
 static kq_status check_routing(const uint32_t* ids, int64_t n_tokens, int64_t top_k,
                                int64_t n_experts, void* workspace, size_t workspace_bytes,
@@ -205,6 +208,9 @@ static kq_status check_routing(const uint32_t* ids, int64_t n_tokens, int64_t to
     if (n_tokens > INT32_MAX / top_k) return fail(KQ_ERR_INVALID_ARG, "n_tokens * top_k exceeds INT32_MAX");
     if (!ids || !aligned(ids, 4)) return fail(KQ_ERR_INVALID_ARG, "ids must be non-null and 4-byte aligned");
     const kq::MoeLayout L = kq::moe_layout(n_experts, n_tokens, top_k, n_out);
+    // the routed products put the schedule's tile slots on grid.y
+    if (L.max_tiles > kMaxGridY)
+        return fail(KQ_ERR_INVALID_ARG, "routing exceeds 65535 schedule tiles (n_tokens * top_k too large)");
     if (!workspace || !aligned(workspace, 256))
         return fail(KQ_ERR_WORKSPACE, "workspace must be non-null and 256-byte aligned");
     if ((int64_t)workspace_bytes < L.total_bytes)
@@ -219,7 +225,8 @@ kq_status kq_moe_route(const uint32_t* ids, int64_t n_tokens, int64_t top_k, int
     kq_status st = check_routing(ids, n_tokens, top_k, n_experts, workspace, workspace_bytes, 0);
     if (st) return st;
     const kq::MoeLayout L = kq::moe_layout(n_experts, n_tokens, top_k, 0);
-    return launched(kq::launch_route(ids, L.rows, n_experts, L, (int32_t*)workspace, (hipStream_t)stream));
+    return launched(kq::launch_route(ids, L.rows, top_k, n_experts, L, (int32_t*)workspace,
+                                     (hipStream_t)stream));
 }
 
 // Shared validation of the expert-routed calls.
@@ -304,8 +311,8 @@ kq_status kq_qmm_id(kq_type t, const void* w, int64_t n_experts, int64_t n, int6
     // the mixed form's tokens by the mix
     hipError_t e = hipSuccess;
     if (!reuse)
-        e = scores ? kq::launch_route(ids, L.rows, n_experts, L, ws, s)
-                   : kq::launch_route(ids, L.rows, n_experts, L, ws, s, y, n, y_dt);
+        e = scores ? kq::launch_route(ids, L.rows, top_k, n_experts, L, ws, s)
+                   : kq::launch_route(ids, L.rows, top_k, n_experts, L, ws, s, y, n, y_dt);
     if (e != hipSuccess) return launched(e);
     kq::SkinnyArgs a{};
     a.w = (const uint8_t*)w;
@@ -330,7 +337,8 @@ kq_status kq_qmm_id(kq_type t, const void* w, int64_t n_experts, int64_t n, int6
         a.y_row = n;
         e = kq::launch_skinny(t, x_dt, false, a, L.max_tiles, s);
         if (e != hipSuccess) return launched(e);
-        return launched(kq::launch_mix(ids, scores, n_tokens, top_k, n_experts, slots, n, y, y_dt, s));
+        return launched(kq::launch_mix(ids, scores, n_tokens, top_k, n_experts, ws, slots, n, y,
+                                       y_dt, s));
     }
     a.y = y;
     a.y_dt = y_dt;
@@ -362,7 +370,7 @@ kq_status kq_moe_glu(kq_type t, const void* gate_w, const void* up_w, int64_t n_
         a.n_experts = n_experts;
         a.m = 1;
     } else {
-        hipError_t e = kq::launch_route(ids, L.rows, n_experts, L, ws, s, h, n, h_dt);
+        hipError_t e = kq::launch_route(ids, L.rows, top_k, n_experts, L, ws, s, h, n, h_dt);
         if (e != hipSuccess) return launched(e);
         a.ws = ws;
     }

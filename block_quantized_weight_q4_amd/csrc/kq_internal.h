@@ -89,14 +89,17 @@ hipError_t launch_tq1_mv(const uint8_t* w, int64_t n, int64_t k, const uint16_t*
                          int y_dt, hipStream_t s);
 hipError_t launch_gemm(int codec, int x_dt, const void* w, int64_t n, int64_t k, const void* x,
                        int64_t m, void* y, int y_dt, hipStream_t s);
-// Builds the schedule; with poison_y, also writes NaN to the rows of
-// poison_y ([rows, poison_n] of poison_dt) whose id is invalid.
-hipError_t launch_route(const uint32_t* ids, int64_t rows, int64_t n_experts, const MoeLayout& L,
-                        int32_t* ws, hipStream_t s, void* poison_y = nullptr,
+// Builds the schedule; with poison_y, also writes NaN to the poisoned rows
+// of poison_y ([rows, poison_n] of poison_dt).
+// Rows of poison_y are NaN-ed by the routing rule: below 32 tokens those with
+// an id >= n_experts, from 32 tokens on all of them if any id is out of range
+// or repeated within a token (then the schedule has no tiles).
+hipError_t launch_route(const uint32_t* ids, int64_t rows, int64_t top_k, int64_t n_experts,
+                        const MoeLayout& L, int32_t* ws, hipStream_t s, void* poison_y = nullptr,
                         int64_t poison_n = 0, int poison_dt = 0);
 hipError_t launch_mix(const uint32_t* ids, const float* scores, int64_t n_tokens, int64_t top_k,
-                      int64_t n_experts, const float* slots, int64_t n, void* y, int y_dt,
-                      hipStream_t s);
+                      int64_t n_experts, const int32_t* ws, const float* slots, int64_t n,
+                      void* y, int y_dt, hipStream_t s);
 
 
 }  // namespace kq

@@ -10,6 +10,15 @@
 
 namespace kq {
 
+// Invalid routing metadata (mlx-native "quantized_matmul_id_ggml.rs", the
+// id contract of quantized_matmul_id_ggml and the map0 comment of its
+// matrix-matrix dispatch): below kMmIdMinTokens tokens (the matrix-vector
+// rule) an id >= E poisons the rows it touches; from kMmIdMinTokens tokens on
+// (the matrix-matrix rule) an out-of-range id or an id repeated within a
+// token poisons the entire output and the schedule gets no tiles, so no
+// weight is read.
+constexpr int64_t kMmIdMinTokens = 32;
+
 // One workgroup of 256 threads builds the whole schedule:
 //   1. histogram of ids into LDS counts (ids >= E counted as invalid)
 //   2. exclusive scans: row offsets per expert and tile offsets per expert
@@ -17,10 +26,15 @@ namespace kq {
 //      finds the lanes holding the same expert with ballots over the id bits,
 //      its rank among them, and the lowest such lane advances the cursor
 //   4. tile descriptors (expert, row_start, num_rows) in expert order
-//   5. (when an output is given) rows with an invalid id are written as NaN
-//      in that output; the products never touch them
+//   5. matrix-matrix rule: a repeated id within a token shows up as two
+//      neighbours of one expert's segment of the (stable) permutation that
+//      belong to the same token; any defect then empties the tile list
+//   6. (when an output is given) the poisoned rows -- those with an id >= E,
+//      or every row under the matrix-matrix rule -- are written as NaN in that
+//      output; the products never touch them
 __global__ __launch_bounds__(256) void route_kernel(const uint32_t* __restrict__ ids, int64_t rows,
-                                                    int64_t n_experts, int32_t* __restrict__ ws,
+                                                    int64_t top_k, int64_t n_experts,
+                                                    int32_t* __restrict__ ws,
                                                     int64_t counts_off, int64_t offsets_off,
                                                     int64_t perm_off, int64_t tiles_off,
                                                     int id_bits, void* __restrict__ poison_y,
@@ -29,11 +43,12 @@ __global__ __launch_bounds__(256) void route_kernel(const uint32_t* __restrict__
     int32_t* counts = lds;                  // [E]
     int32_t* cursor = lds + n_experts;      // [E]
     int32_t* tstart = lds + 2 * n_experts;  // [E]
-    __shared__ int32_t n_invalid, n_tiles;
+    __shared__ int32_t n_invalid, n_tiles, n_repeat;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const bool mm_rule = rows / top_k >= kMmIdMinTokens;
 
     for (int64_t e = tid; e < n_experts; e += 256) counts[e] = 0;
-    if (tid == 0) n_invalid = 0;
+    if (tid == 0) n_invalid = 0, n_repeat = 0;
     __syncthreads();
     for (int64_t i = tid; i < rows; i += 256) {
         const uint32_t e = ids[i];
@@ -70,11 +85,7 @@ __global__ __launch_bounds__(256) void route_kernel(const uint32_t* __restrict__
         ws[counts_off + e] = counts[e];
         ws[offsets_off + e] = cursor[e];
     }
-    if (tid == 0) {
-        ws[offsets_off + n_experts] = (int32_t)(rows - n_invalid);
-        ws[0] = n_tiles;
-        ws[1] = n_invalid;
-    }
+    if (tid == 0) ws[offsets_off + n_experts] = (int32_t)(rows - n_invalid);
     // tile descriptors
     for (int64_t e = tid; e < n_experts; e += 256) {
         const int32_t c = counts[e], start = cursor[e];
@@ -111,10 +122,28 @@ __global__ __launch_bounds__(256) void route_kernel(const uint32_t* __restrict__
         }
     }
 
-    if (poison_y && n_invalid > 0) {
+    if (mm_rule) {
+        // the scatter's global writes of perm are visible to the whole
+        // workgroup after the barrier
+        __syncthreads();
+        const int64_t valid = rows - n_invalid;
+        int32_t rep = 0;
+        for (int64_t p = tid; p + 1 < valid; p += 256) {
+            const int32_t a = ws[perm_off + p], b = ws[perm_off + p + 1];
+            rep += ids[a] == ids[b] && a / top_k == b / top_k;
+        }
+        if (rep) atomicAdd(&n_repeat, rep);
+    }
+    __syncthreads();
+    const bool poison_all = mm_rule && n_invalid + n_repeat > 0;
+    if (tid == 0) {
+        ws[0] = poison_all ? 0 : n_tiles;
+        ws[1] = n_invalid + n_repeat;
+    }
+    if (poison_y && n_invalid + n_repeat > 0) {
         const float v = __builtin_nanf("");
         for (int64_t i = 0; i < rows; ++i) {
-            if ((int64_t)ids[i] < n_experts) continue;
+            if (!poison_all && (int64_t)ids[i] < n_experts) continue;
             for (int64_t j = tid; j < poison_n; j += 256) {
                 if (poison_dt == F32) store_out<F32>(poison_y, i * poison_n + j, v);
                 else if (poison_dt == F16) store_out<F16>(poison_y, i * poison_n + j, v);
@@ -124,46 +153,54 @@ __global__ __launch_bounds__(256) void route_kernel(const uint32_t* __restrict__
     }
 }
 
-hipError_t launch_route(const uint32_t* ids, int64_t rows, int64_t n_experts, const MoeLayout& L,
-                        int32_t* ws, hipStream_t s, void* poison_y, int64_t poison_n,
-                        int poison_dt) {
+hipError_t launch_route(const uint32_t* ids, int64_t rows, int64_t top_k, int64_t n_experts,
+                        const MoeLayout& L, int32_t* ws, hipStream_t s, void* poison_y,
+                        int64_t poison_n, int poison_dt) {
     int bits = 1;
     while ((1ll << bits) < n_experts) ++bits;
     const size_t lds = (size_t)3 * n_experts * sizeof(int32_t);
-    hipLaunchKernelGGL(route_kernel, dim3(1), dim3(256), lds, s, ids, rows, n_experts, ws,
+    hipLaunchKernelGGL(route_kernel, dim3(1), dim3(256), lds, s, ids, rows, top_k, n_experts, ws,
                        L.counts_off, L.offsets_off, L.perm_off, L.tiles_off, bits, poison_y,
                        poison_n, poison_dt);
     return hipGetLastError();
 }
 
 // y[t, j] = sum over slots r = 0..top_k-1, in order, of scores[t,r] * slot[t*top_k+r, j]
-// in fp32; NaN if any of the token's ids is invalid.
+// in fp32.  Poison: below kMmIdMinTokens tokens, NaN for a token with an id
+// >= E; from kMmIdMinTokens tokens on, NaN everywhere when the schedule
+// counted any defect (*n_defects, word 1 of the workspace).  Tokens are
+// walked with a grid-sized stride, so any token count fits the grid.
 __global__ __launch_bounds__(256) void mix_kernel(const uint32_t* __restrict__ ids,
-                                                  const float* __restrict__ scores, int64_t top_k,
-                                                  int64_t n_experts, const float* __restrict__ slots,
+                                                  const float* __restrict__ scores,
+                                                  int64_t n_tokens, int64_t top_k,
+                                                  int64_t n_experts, const int32_t* __restrict__ n_defects,
+                                                  const float* __restrict__ slots,
                                                   int64_t n, void* __restrict__ y, int y_dt) {
     const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t t = blockIdx.y;
     if (j >= n) return;
-    float acc = 0.f;
-    bool bad = false;
-    for (int64_t r = 0; r < top_k; ++r) {
-        const int64_t row = t * top_k + r;
-        bad |= (int64_t)ids[row] >= n_experts;
-        acc = __builtin_fmaf(scores[row], slots[row * n + j], acc);
+    const bool all_bad = n_tokens >= kMmIdMinTokens && *n_defects > 0;
+    for (int64_t t = blockIdx.y; t < n_tokens; t += gridDim.y) {
+        float acc = 0.f;
+        bool bad = all_bad;
+        for (int64_t r = 0; r < top_k; ++r) {
+            const int64_t row = t * top_k + r;
+            bad |= (int64_t)ids[row] >= n_experts;
+            acc = __builtin_fmaf(scores[row], slots[row * n + j], acc);
+        }
+        const float v = bad ? __builtin_nanf("") : acc;
+        if (y_dt == F32) store_out<F32>(y, t * n + j, v);
+        else if (y_dt == F16) store_out<F16>(y, t * n + j, v);
+        else store_out<BF16>(y, t * n + j, v);
     }
-    const float v = bad ? __builtin_nanf("") : acc;
-    if (y_dt == F32) store_out<F32>(y, t * n + j, v);
-    else if (y_dt == F16) store_out<F16>(y, t * n + j, v);
-    else store_out<BF16>(y, t * n + j, v);
 }
 
 hipError_t launch_mix(const uint32_t* ids, const float* scores, int64_t n_tokens, int64_t top_k,
-                      int64_t n_experts, const float* slots, int64_t n, void* y, int y_dt,
-                      hipStream_t s) {
-    const dim3 grid((unsigned)((n + 255) / 256), (unsigned)n_tokens);
-    hipLaunchKernelGGL(mix_kernel, grid, dim3(256), 0, s, ids, scores, top_k, n_experts, slots, n,
-                       y, y_dt);
+                      int64_t n_experts, const int32_t* ws, const float* slots, int64_t n,
+                      void* y, int y_dt, hipStream_t s) {
+    const int64_t gy = n_tokens < 65535 ? n_tokens : 65535;
+    const dim3 grid((unsigned)((n + 255) / 256), (unsigned)gy);
+    hipLaunchKernelGGL(mix_kernel, grid, dim3(256), 0, s, ids, scores, n_tokens, top_k, n_experts,
+                       ws + 1, slots, n, y, y_dt);
     return hipGetLastError();
 }
 

@@ -98,11 +98,6 @@ def kq_last_error() -> str:
     return lib().kq_last_error().decode()
 
 
-def _check(status: int):
-    if status != 0:
-        raise KQError(status, kq_last_error())
-
-
 def _ptr(t):
     return None if t is None else C.c_void_p(t.data_ptr())
 
@@ -112,6 +107,40 @@ def _stream(*tensors):
         if t is not None and t.is_cuda:
             return C.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
     return None
+
+
+def _check(status: int):
+    if status != 0:
+        raise KQError(status, kq_last_error())
+
+
+def _tensors(*specs):
+    """Marshalling checks before a call: each (name, tensor, bytes the call
+    reads or writes through it) must be contiguous, on the device of the first
+    tensor, and at least that large.  A size the C side will reject (None or
+    negative) is left to it."""
+    dev = None
+    for name, t, need in specs:
+        if t is None:
+            continue
+        if not t.is_contiguous():
+            raise KQError(1, f"{name} must be contiguous")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise KQError(1, f"{name} is on device {t.device}; the call's other tensors are on {dev}")
+        have = t.numel() * t.element_size()
+        if need is not None and need > 0 and have < need:
+            raise KQError(1, f"{name} holds {have} bytes; the call uses {need}")
+
+
+def _rows_bytes(kind: str, rows: int, k: int):
+    rb = lib().kq_row_bytes(TYPES[kind], int(k)) if kind in TYPES else -1
+    return rows * rb if rb > 0 and rows > 0 else None
+
+
+def _esz(t):
+    return None if t is None else t.element_size()
 
 
 def _dt(t) -> int:
@@ -134,17 +163,22 @@ def kq_row_bytes(kind: str, k: int) -> int:
 
 
 def kq_dequantize(kind: str, w, rows: int, k: int, out):
+    _tensors(("w", w, _rows_bytes(kind, rows, k)), ("out", out, rows * k * out.element_size()))
     _check(lib().kq_dequantize(TYPES[kind], _ptr(w), rows, k, _ptr(out), _dt(out), _stream(w, out)))
     return out
 
 
 def kq_qmv(kind: str, w, n: int, k: int, x, m: int, y):
+    _tensors(("w", w, _rows_bytes(kind, n, k)), ("x", x, m * k * x.element_size()),
+             ("y", y, m * n * y.element_size()))
     _check(lib().kq_qmv(TYPES[kind], _ptr(w), n, k, _ptr(x), _dt(x), m, _ptr(y), _dt(y),
                         _stream(w, x, y)))
     return y
 
 
 def kq_qmm(kind: str, w, n: int, k: int, x, m: int, y):
+    _tensors(("w", w, _rows_bytes(kind, n, k)), ("x", x, m * k * x.element_size()),
+             ("y", y, m * n * y.element_size()))
     _check(lib().kq_qmm(TYPES[kind], _ptr(w), n, k, _ptr(x), _dt(x), m, _ptr(y), _dt(y),
                         _stream(w, x, y)))
     return y
@@ -155,6 +189,7 @@ def kq_moe_workspace_bytes(n_experts: int, n_tokens: int, top_k: int, n_out: int
 
 
 def kq_moe_route(ids, n_tokens: int, top_k: int, n_experts: int, workspace):
+    _tensors(("ids", ids, n_tokens * top_k * 4), ("workspace", workspace, None))
     _check(lib().kq_moe_route(_ptr(ids), n_tokens, top_k, n_experts, _ptr(workspace),
                               workspace.numel() * workspace.element_size(), _stream(ids, workspace)))
     return workspace
@@ -162,6 +197,14 @@ def kq_moe_route(ids, n_tokens: int, top_k: int, n_experts: int, workspace):
 
 def kq_qmm_id(kind: str, w, n_experts: int, n: int, k: int, expert_stride: int, x, layout: int,
               ids, n_tokens: int, top_k: int, scores, y, workspace):
+    rows = n_tokens * top_k
+    x_rows = n_tokens if (layout & ~REUSE_SCHEDULE) == LAYOUT_SHARED else rows
+    one = _rows_bytes(kind, n, k)
+    _tensors(("w", w, None if one is None else (n_experts - 1) * expert_stride + one),
+             ("x", x, x_rows * k * x.element_size()), ("ids", ids, rows * 4),
+             ("scores", scores, rows * 4),
+             ("y", y, (n_tokens if scores is not None else rows) * n * y.element_size()),
+             ("workspace", workspace, None))
     _check(lib().kq_qmm_id(TYPES[kind], _ptr(w), n_experts, n, k, expert_stride, _ptr(x), _dt(x),
                            layout, _ptr(ids), n_tokens, top_k, _ptr(scores), _ptr(y), _dt(y),
                            _ptr(workspace), workspace.numel() * workspace.element_size(),
@@ -171,6 +214,11 @@ def kq_qmm_id(kind: str, w, n_experts: int, n: int, k: int, expert_stride: int, 
 
 def kq_moe_glu(kind: str, gate_w, up_w, n_experts: int, n: int, k: int, expert_stride: int, x,
                ids, n_tokens: int, top_k: int, h, workspace, act: int = ACT_SILU):
+    one = _rows_bytes(kind, n, k)
+    wneed = None if one is None else (n_experts - 1) * expert_stride + one
+    _tensors(("gate_w", gate_w, wneed), ("up_w", up_w, wneed),
+             ("x", x, n_tokens * k * x.element_size()), ("ids", ids, n_tokens * top_k * 4),
+             ("h", h, n_tokens * top_k * n * h.element_size()), ("workspace", workspace, None))
     _check(lib().kq_moe_glu(TYPES[kind], _ptr(gate_w), _ptr(up_w), n_experts, n, k, expert_stride,
                             _ptr(x), _dt(x), _ptr(ids), n_tokens, top_k, act, _ptr(h), _dt(h),
                             _ptr(workspace), workspace.numel() * workspace.element_size(),

@@ -126,8 +126,9 @@ kq_status kq_dequantize(kq_type t, const void* w, int64_t rows, int64_t k, void*
  * y[i, j] = sum_c x[i, c] * w[j, c], accumulated in fp32 and rounded once to
  * y_dt.  kq_qmv is the decode form (1 <= m <= 16, weights streamed once);
  * kq_qmm takes any m >= 1 and picks the decode form itself for small m.
- * Errors: n, k or m <= 0, k % QK != 0, n > 2^26, k > 2^24, m > 16 for kq_qmv,
- * null or misaligned pointers, y overlapping w or x -> KQ_ERR_INVALID_ARG.
+ * Errors: n, k or m <= 0, k % QK != 0, n > 2^26, k > 2^24, m > 2^19 (m > 16
+ * for kq_qmv), null or misaligned pointers, y overlapping w or x ->
+ * KQ_ERR_INVALID_ARG.
  */
 kq_status kq_qmv(kq_type t, const void* w, int64_t n, int64_t k, const void* x, kq_dtype x_dt,
                  int64_t m, void* y, kq_dtype y_dt, void* stream);
@@ -147,8 +148,11 @@ size_t kq_moe_workspace_bytes(int64_t n_experts, int64_t n_tokens, int64_t top_k
 
 /*
  * Workspace layout written by kq_moe_route (int32 words, from the start):
- *   [0]                       number of tiles
- *   [1]                       number of rows with an invalid id (>= n_experts)
+ *   [0]                       number of tiles (0 when the matrix-matrix
+ *                             rule poisons the whole operation)
+ *   [1]                       number of rows with an id >= n_experts, plus,
+ *                             from 32 tokens on, rows whose id repeats an
+ *                             earlier slot of the same token
  *   [2 .. 2+E)                counts[e]: rows routed to expert e
  *   [2+E .. 3+2E)             offsets[e]: exclusive prefix sum of counts
  *   [3+2E .. 3+2E+R)          perm: routed-row indices t*top_k+slot grouped by
@@ -175,8 +179,10 @@ size_t kq_moe_workspace_bytes(int64_t n_experts, int64_t n_tokens, int64_t top_k
  *   workspace  at least kq_moe_workspace_bytes(n_experts, n_tokens, top_k, 0)
  *
  * The ids are never read on the host.  An id >= n_experts is counted as
- * invalid and left out of the schedule.  kq_qmm_id and kq_moe_glu call this
- * themselves; it is exported so the schedule can be inspected.
+ * invalid and left out of the schedule; from 32 tokens on, repeated ids are
+ * counted too and any defect leaves the schedule with no tiles (the rule of
+ * kq_qmm_id).  kq_qmm_id and kq_moe_glu call this themselves; it is exported
+ * so the schedule can be inspected.
  */
 kq_status kq_moe_route(const uint32_t* ids, int64_t n_tokens, int64_t top_k, int64_t n_experts,
                        void* workspace, size_t workspace_bytes, void* stream);
@@ -199,10 +205,23 @@ kq_status kq_moe_route(const uint32_t* ids, int64_t n_tokens, int64_t top_k, int
  *   workspace  kq_moe_workspace_bytes(n_experts, n_tokens, top_k, n) bytes
  *
  * Each expert's weights are streamed once per call however many rows it
- * serves.  A row with an id >= n_experts reads no weights and is written as
- * NaN (for the mixed form: that token's output row).
+ * serves.
+ *
+ * Invalid ids are data, not host errors (the ids are never read on the
+ * host).  mlx-native "quantized_matmul_id_ggml.rs", the id contract of
+ * quantized_matmul_id_ggml and the map0 comment of its matrix-matrix
+ * dispatch, whose route threshold is 32 tokens:
+ *   n_tokens < 32   (matrix-vector rule) a row with an id >= n_experts reads
+ *                   no weights and is written as NaN (for the mixed form:
+ *                   that token's output row); an id repeated within a token
+ *                   is computed as written.
+ *   n_tokens >= 32  (matrix-matrix rule) the top_k ids of a token must be
+ *                   distinct and in range; otherwise the ENTIRE output is
+ *                   NaN and no weights are read.
  * Errors: zero or negative sizes, top_k outside 1..n_experts,
- * n_tokens*top_k > INT32_MAX, k % QK != 0, n > 2^26, k > 2^24, expert_stride
+ * n_tokens*top_k > INT32_MAX, more than 65535 schedule tiles
+ * (min(R, ceil(R / KQ_MOE_TILE_ROWS) + n_experts) with R = n_tokens * top_k),
+ * k % QK != 0, n > 2^26, k > 2^24, expert_stride
  * smaller than one expert's bytes, null/misaligned pointers, y overlapping its inputs or the
  * workspace -> KQ_ERR_INVALID_ARG; workspace too small -> KQ_ERR_WORKSPACE.
  */
@@ -226,8 +245,10 @@ kq_status kq_qmm_id(kq_type t, const void* w, int64_t n_experts, int64_t n, int6
  *                 h = silu(W_gate[e] x_t) * (W_up[e] x_t), fp32 inside
  *   workspace     kq_moe_workspace_bytes(n_experts, n_tokens, top_k, 0)
  *
- * Rows with an invalid id are written as NaN.  Errors as kq_qmm_id; an
- * unknown act -> KQ_ERR_UNSUPPORTED.
+ * Invalid ids poison h by the rule of kq_qmm_id (below 32 tokens the h row
+ * of an out-of-range id; from 32 tokens on all of h if any id is out of range
+ * or repeated within a token).  Errors as kq_qmm_id; an unknown act ->
+ * KQ_ERR_UNSUPPORTED.
  */
 kq_status kq_moe_glu(kq_type t, const void* gate_w, const void* up_w, int64_t n_experts,
                      int64_t n, int64_t k, int64_t expert_stride, const void* x, kq_dtype x_dt,

@@ -351,19 +351,57 @@ int or_qmm_points(int type, const uint8_t* w, int64_t n, int64_t k, const void* 
     return 0;
 }
 
+/* [MID] quantized_matmul_id_ggml doc comment ("Errors") and the map0
+ * comment of its matrix-matrix dispatch: device-produced ids are checked on
+ * the device.  The matrix-vector route only bounds-checks: an out-of-range id
+ * poisons the output row(s) it touches and repeated ids are computed as
+ * written.  The matrix-matrix route, which the page takes from
+ * MM_ID_ROUTING_THRESHOLD = 32 tokens on, also requires the top_k ids of each
+ * token to be distinct, and any out-of-range or repeated id there poisons the
+ * entire output, with no weight read.  The reading here: a call of n_tokens
+ * >= 32 follows the matrix-matrix rule, a smaller one the matrix-vector
+ * rule, whichever kernels compute it. */
+#define OR_MM_ID_MIN_TOKENS 32
+
+/* 1 when a routing of T tokens follows the matrix-matrix rule and holds an
+ * out-of-range id or a token with a repeated id (the whole output is NaN). */
+int or_routing_poisons_all(const uint32_t* ids, int64_t T, int64_t top_k, int64_t n_experts) {
+    if (T < OR_MM_ID_MIN_TOKENS) return 0;
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t r = 0; r < top_k; ++r) {
+            uint32_t e = ids[t * top_k + r];
+            if ((int64_t)e >= n_experts) return 1;
+            for (int64_t q = 0; q < r; ++q)
+                if (ids[t * top_k + q] == e) return 1;
+        }
+    return 0;
+}
+
+static void fill_nan(double* a, int64_t count) {
+    if (!a) return;
+    for (int64_t i = 0; i < count; ++i) a[i] = NAN;
+}
+
 /* [MID] module comment + [KQ] gather_qmm / gather_qmv_kq /
  * gather_qmv_mix_ns_kq.  For each token t and slot r: e = ids[t,r];
  * row = W[e] (experts are expert_stride bytes apart) applied to x[t] (shared
  * layout, x is [T,k]) or x[t,r] (slotted layout, x is [T,top_k,k]).
  * Without scores: y[(t*top_k + r), n].  With scores: y[t, n] =
- * sum_r scores[t,r] * (W[e] x)[n], accumulated in slot order.  An id outside
- * [0, n_experts) poisons the rows it touches with NaN ([MID] contract). */
+ * sum_r scores[t,r] * (W[e] x)[n], accumulated in slot order.  Invalid ids
+ * poison the output as or_routing_poisons_all describes: below 32 tokens an
+ * id outside [0, n_experts) poisons the rows it touches with NaN, from 32
+ * tokens on an out-of-range or repeated id poisons the whole output. */
 int or_qmm_id(int type, const uint8_t* w, int64_t n_experts, int64_t n, int64_t k,
               int64_t expert_stride, const void* x, int x_dt, int slotted, const uint32_t* ids,
               int64_t T, int64_t top_k, const float* scores, double* y, double* s) {
     int qk = or_qk(type);
     if (!qk || k % qk) return -1;
     int64_t out_rows = scores ? T : T * top_k;
+    if (or_routing_poisons_all(ids, T, top_k, n_experts)) {
+        fill_nan(y, out_rows * n);
+        fill_nan(s, out_rows * n);
+        return 0;
+    }
     for (int64_t i = 0; i < out_rows * n; ++i) {
         y[i] = 0.0;
         if (s) s[i] = 0.0;
@@ -418,7 +456,8 @@ double or_gelu_tanh(double z) {
  * approximation): for each token t and slot r with e = ids[t,r]:
  * g = W_gate[e] x_t, u = W_up[e] x_t, h = act(g) * u, giving h[T, top_k, n].
  * Also returns g, u and their |.|-sums sg, su (any of the extra outputs may
- * be NULL).  An invalid id poisons its h row with NaN. */
+ * be NULL).  Invalid ids poison h as or_routing_poisons_all describes (below
+ * 32 tokens only the h row of an out-of-range id). */
 int or_moe_glu(int type, const uint8_t* gate_w, const uint8_t* up_w, int64_t n_experts,
                int64_t n, int64_t k, int64_t expert_stride, const void* x, int x_dt,
                const uint32_t* ids, int64_t T, int64_t top_k, int act, double* h, double* g,
@@ -426,6 +465,14 @@ int or_moe_glu(int type, const uint8_t* gate_w, const uint8_t* up_w, int64_t n_e
     if (act != 0 && act != 1) return -3;
     int qk = or_qk(type);
     if (!qk || k % qk) return -1;
+    if (or_routing_poisons_all(ids, T, top_k, n_experts)) {
+        fill_nan(h, T * top_k * n);
+        fill_nan(g, T * top_k * n);
+        fill_nan(u, T * top_k * n);
+        fill_nan(sg, T * top_k * n);
+        fill_nan(su, T * top_k * n);
+        return 0;
+    }
 #pragma omp parallel
     {
         double* rg = (double*)malloc(sizeof(double) * k);
@@ -474,6 +521,11 @@ int or_moe_layer(int type, const uint8_t* gate_w, const uint8_t* up_w, const uin
                  int64_t n_experts, int64_t hidden, int64_t ffn, int64_t gate_stride,
                  int64_t down_stride, const void* x, int x_dt, const uint32_t* ids, int64_t T,
                  int64_t top_k, const float* scores, double* out, double* s_out) {
+    if (or_routing_poisons_all(ids, T, top_k, n_experts)) {
+        fill_nan(out, T * hidden);
+        fill_nan(s_out, T * hidden);
+        return 0;
+    }
     double* h = (double*)malloc(sizeof(double) * T * top_k * ffn);
     if (!h) return -2;
     int rc = or_moe_glu(type, gate_w, up_w, n_experts, ffn, hidden, gate_stride, x, x_dt, ids,
@@ -530,18 +582,22 @@ int or_moe_layer(int type, const uint8_t* gate_w, const uint8_t* up_w, const uin
 /* ------------------------------------------------------------------ */
 
 /* [KQ] expert_tile_map / [MID] expert regroup.  Routed rows are the flat
- * (token, slot) indices i = t*top_k + r.  counts[e] is the number of rows
- * with ids[i] == e; offsets is its exclusive prefix sum (offsets[E] = number
- * of valid rows); perm lists the rows grouped by expert in ascending expert
- * order, and in ascending i within an expert (a stable sort).  Rows with an
- * id >= E are not placed; their number is returned in *n_invalid.  The tile
- * map cuts each expert's segment into tiles of at most tile_rows rows, only
- * the last of which may be partial: (expert, row_start, num_rows), in
- * expert order.  Returns the number of tiles, or -1 if max_tiles is too
- * small. */
-int64_t or_route(const uint32_t* ids, int64_t n_rows, int64_t n_experts, int64_t tile_rows,
-                 int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* tiles,
-                 int64_t max_tiles, int64_t* n_invalid) {
+ * (token, slot) indices i = t*top_k + r of n_tokens x top_k ids.  counts[e]
+ * is the number of rows with ids[i] == e; offsets is its exclusive prefix sum
+ * (offsets[E] = number of rows with an in-range id); perm lists those rows
+ * grouped by expert in ascending expert order, and in ascending i within an
+ * expert (a stable sort).  Rows with an id >= E are not placed.  *n_invalid
+ * counts them, plus (from 32 tokens on, the matrix-matrix rule of
+ * or_routing_poisons_all) every row whose id repeats an earlier slot of the
+ * same token.  The tile map cuts each expert's segment into tiles of at most
+ * tile_rows rows, only the last of which may be partial: (expert, row_start,
+ * num_rows), in expert order -- and is empty when the matrix-matrix rule
+ * poisons the whole operation (no weights are read).  Returns the number of
+ * tiles, or -1 if max_tiles is too small. */
+int64_t or_route(const uint32_t* ids, int64_t n_tokens, int64_t top_k, int64_t n_experts,
+                 int64_t tile_rows, int32_t* counts, int32_t* offsets, int32_t* perm,
+                 int32_t* tiles, int64_t max_tiles, int64_t* n_invalid) {
+    int64_t n_rows = n_tokens * top_k;
     int64_t bad = 0;
     for (int64_t e = 0; e < n_experts; ++e) counts[e] = 0;
     for (int64_t i = 0; i < n_rows; ++i) {
@@ -550,12 +606,26 @@ int64_t or_route(const uint32_t* ids, int64_t n_rows, int64_t n_experts, int64_t
         else
             bad++;
     }
+    if (n_tokens >= OR_MM_ID_MIN_TOKENS) {
+        for (int64_t t = 0; t < n_tokens; ++t)
+            for (int64_t r = 0; r < top_k; ++r) {
+                uint32_t e = ids[t * top_k + r];
+                if ((int64_t)e >= n_experts) continue;
+                for (int64_t q = 0; q < r; ++q)
+                    if (ids[t * top_k + q] == e) {
+                        bad++;
+                        break;
+                    }
+            }
+    }
     offsets[0] = 0;
     for (int64_t e = 0; e < n_experts; ++e) offsets[e + 1] = offsets[e] + counts[e];
     int64_t pos = 0;
     for (int64_t e = 0; e < n_experts; ++e)
         for (int64_t i = 0; i < n_rows; ++i)
             if ((int64_t)ids[i] == e) perm[pos++] = (int32_t)i;
+    if (n_invalid) *n_invalid = bad;
+    if (n_tokens >= OR_MM_ID_MIN_TOKENS && bad > 0) return 0;
     int64_t nt = 0;
     for (int64_t e = 0; e < n_experts; ++e) {
         for (int64_t start = 0; start < counts[e]; start += tile_rows) {
@@ -567,6 +637,5 @@ int64_t or_route(const uint32_t* ids, int64_t n_rows, int64_t n_experts, int64_t
             nt++;
         }
     }
-    if (n_invalid) *n_invalid = bad;
     return nt;
 }

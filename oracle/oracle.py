@@ -17,7 +17,7 @@ from .build import build_oracle
 __all__ = [
     "TYPES", "DTYPES", "lib", "half_to_double", "bf16_to_double", "float_to_half_rne",
     "float_to_bf16_rne", "q4k_scale_min", "dequant", "dequant_as", "qmm", "qmm_points",
-    "qmm_id", "moe_glu", "moe_layer", "route", "silu", "gelu_tanh", "num_threads",
+    "qmm_id", "moe_glu", "moe_layer", "route", "routing_poisons_all", "silu", "gelu_tanh", "num_threads",
 ]
 
 TYPES = {"q4_k": 0, "q8_0": 1, "tq1_g128": 2}
@@ -67,7 +67,9 @@ def lib():
         L.or_moe_layer.argtypes = [C.c_int, P, P, P, i64, i64, i64, i64, i64, P, C.c_int, P,
                                    i64, i64, P, P, P]
         L.or_route.restype = C.c_int64
-        L.or_route.argtypes = [P, i64, i64, i64, P, P, P, P, i64, P]
+        L.or_route.argtypes = [P, i64, i64, i64, i64, P, P, P, P, i64, P]
+        L.or_routing_poisons_all.restype = C.c_int
+        L.or_routing_poisons_all.argtypes = [P, i64, i64, i64]
         _lib = L
     return _lib
 
@@ -218,9 +220,21 @@ def moe_layer(kind, gate_w, up_w, down_w, n_experts, hidden, ffn, gate_stride, d
     return out, s
 
 
+def routing_poisons_all(ids, n_experts) -> bool:
+    """ids [T, top_k]: True when the matrix-matrix rule (32 tokens or more)
+    poisons the whole output (an out-of-range or a repeated id in a token)."""
+    ids = np.atleast_2d(_c(ids, np.uint32))
+    T, top_k = ids.shape
+    return bool(lib().or_routing_poisons_all(_p(ids), T, top_k, n_experts))
+
+
 def route(ids, n_experts, tile_rows):
-    """dict(counts, offsets, perm, tiles[n_tiles,3], n_invalid) from flat ids."""
-    ids = _c(ids, np.uint32).ravel()
+    """dict(counts, offsets, perm, tiles[n_tiles,3], n_invalid) from ids
+    [n_tokens, top_k] (a 1-D array is one slot per token)."""
+    ids = _c(ids, np.uint32)
+    if ids.ndim == 1:
+        ids = ids.reshape(-1, 1)
+    T, top_k = ids.shape
     n = ids.size
     counts = np.zeros(n_experts, dtype=np.int32)
     offsets = np.zeros(n_experts + 1, dtype=np.int32)
@@ -228,8 +242,8 @@ def route(ids, n_experts, tile_rows):
     max_tiles = n + n_experts
     tiles = np.zeros((max_tiles, 3), dtype=np.int32)
     bad = np.zeros(1, dtype=np.int64)
-    nt = lib().or_route(_p(ids), n, n_experts, tile_rows, _p(counts), _p(offsets), _p(perm),
-                        _p(tiles), max_tiles, _p(bad))
+    nt = lib().or_route(_p(ids), T, top_k, n_experts, tile_rows, _p(counts), _p(offsets),
+                        _p(perm), _p(tiles), max_tiles, _p(bad))
     if nt < 0:
         raise ValueError("or_route: tile capacity exceeded")
     valid = int(offsets[-1])

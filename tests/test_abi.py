@@ -146,9 +146,38 @@ def test_expert_validation(kq):
     assert call(T=2**31 // 2 + 1) == 1        # rows > INT32_MAX
     assert call(n=2**26 + 1, stride=(2**26 + 1) * 144) == 1  # launch geometry bound on n
     assert call(y=P(base + (1 << 32) + 64)) == 1  # output overlaps x
+    assert call(T=1_100_000) == 1              # more than 65535 schedule tiles
+    assert "65535" in kq.kq_last_error()
     for act in (2, 9, -1):
         assert L.kq_moe_glu(0, w, w, 8, 64, 256, 64 * 144, x, 1, ids, 4, 2, act, y, 1, ws, 1 << 20,
                             None) == 2        # unknown activation
+
+
+def test_qmm_row_bound(kq):
+    L = kq.lib()
+    P = C.c_void_p
+    base = 1 << 40
+    m = 2**19 + 1
+    rc = L.kq_qmm(0, P(base), 8, 256, P(base + (1 << 36)), 2, m, P(base + (2 << 36)), 2, None)
+    assert rc == 1 and kq.kq_last_error() == "m exceeds 2^19 activation rows"
+
+
+def test_binding_checks_tensors_before_calling(kq):
+    """The binding refuses strided, short or mixed-device tensors before any C
+    call (host tensors here: nothing reaches a kernel)."""
+    import torch
+
+    w = torch.zeros(8 * 144, dtype=torch.uint8)
+    x = torch.zeros((2, 512), dtype=torch.float16)
+    y = torch.zeros((1, 8), dtype=torch.float16)
+    with pytest.raises(kq.KQError, match="contiguous"):
+        kq.kq_qmv("q4_k", w, 8, 256, x[:, ::2], 1, y)
+    with pytest.raises(kq.KQError, match="bytes"):
+        kq.kq_qmv("q4_k", w[:100], 8, 256, x, 1, y)
+    with pytest.raises(kq.KQError, match="bytes"):
+        kq.kq_qmv("q4_k", w, 8, 256, x, 1, y[:, :4])
+    with pytest.raises(kq.KQError, match="device"):
+        kq.kq_qmv("q4_k", w, 8, 256, x.to("meta"), 1, y)
 
 
 def test_product_path_has_no_fallback():

@@ -49,13 +49,24 @@ def _ids(rng, T, E, top_k):
 
 
 @pytest.mark.parametrize("E,T,top_k", [(1, 1, 1), (8, 1, 8), (128, 1, 8), (128, 256, 8),
-                                       (16, 300, 4), (5, 2000, 2), (4096, 64, 16)])
-def test_route_schedule_exact(kq, E, T, top_k):
+                                       (16, 300, 4), (5, 2000, 2), (4096, 64, 16), (32, 31, 4),
+                                       (32, 32, 4)])
+@pytest.mark.parametrize("defect", ["none", "range", "repeat"])
+def test_route_schedule_exact(kq, E, T, top_k, defect):
+    """The schedule bit for bit against the oracle's, with out-of-range ids
+    (three of them) or one id repeated within a token: below 32 tokens the
+    matrix-vector rule (schedule of the valid rows), from 32 on the
+    matrix-matrix rule (no tiles)."""
     rng = synth.rng_for(E * 1000 + T)
     ids = _ids(rng, T, E, top_k)
-    if T * top_k > 8:
+    if defect == "range" and T * top_k > 8:
         ids.ravel()[rng.integers(0, T * top_k, 3)] = [E, E + 1, 0xFFFFFFFF]
-    _say("route", E, T, top_k)
+    elif defect == "repeat" and top_k > 1:
+        t = int(rng.integers(0, T))
+        ids[t, top_k - 1] = ids[t, 0]
+    elif defect != "none":
+        pytest.skip("no such defect at this shape")
+    _say("route", E, T, top_k, defect)
     ws = _ws(kq, E, T, top_k)
     kq.kq_moe_route(to_dev(ids), T, top_k, E, ws)
     torch.cuda.synchronize()
@@ -140,8 +151,8 @@ def test_qmm_id_tiles_over_16_rows_long_k(kq, x_dt, layout, nsb):
     check_tol(to_f64(y), ref, s, TAU[x_dt], f"qmm_id long k {x_dt}")
 
 
-@pytest.mark.parametrize("T", [1, 40])
-def test_reused_schedule_matches_rebuilt(kq, T):
+@pytest.mark.parametrize("T,defect", [(1, False), (20, True), (40, False), (40, True)])
+def test_reused_schedule_matches_rebuilt(kq, T, defect):
     # gate/up then down on one workspace: the down call that keeps the
     # schedule built by the GLU gives the same bits as one that rebuilds it
     E, F, H, top_k = 8, 256, 256, 4
@@ -150,8 +161,10 @@ def test_reused_schedule_matches_rebuilt(kq, T):
     up = synth.weight_blocks("q4_k", rng, E * F, H)
     down = synth.weight_blocks("q4_k", rng, E * H, F)
     ids = _ids(rng, T, E, top_k)
-    if T > 1:
-        ids.ravel()[0] = E + 3  # an invalid id: token 0's output is NaN either way
+    if defect:
+        # an out-of-range id: token 0's output is NaN below 32 tokens, the
+        # whole output from 32 tokens on
+        ids.ravel()[0] = E + 3
     scores = rng.uniform(0.05, 1.0, size=(T, top_k)).astype(np.float32)
     x = synth.activations(rng, (T, H), "f16")
     gs, ds = F * synth.row_bytes("q4_k", H), H * synth.row_bytes("q4_k", F)
@@ -169,9 +182,71 @@ def test_reused_schedule_matches_rebuilt(kq, T):
                      dev["ids"], T, top_k, dev["scores"], out, ws)
         torch.cuda.synchronize()
         outs.append(out.cpu().numpy())
-    if T > 1:
+    if defect and T < 32:
         assert np.isnan(outs[0][0]).all() and not np.isnan(outs[0][1:]).any()
+    elif defect:
+        assert np.isnan(outs[0]).all()
+    else:
+        assert not np.isnan(outs[0]).any()
     assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+
+
+@pytest.mark.parametrize("defect", ["repeat", "range"])
+@pytest.mark.parametrize("T", [31, 32, 70])
+def test_routing_rule_matrix_matrix(kq, defect, T):
+    """mlx-native "quantized_matmul_id_ggml.rs" id contract: from 32 tokens on
+    a repeated or out-of-range id makes the entire output NaN (unmixed, mixed
+    and GLU forms, and a down projection that reuses the poisoned schedule);
+    below 32 tokens only an out-of-range id's rows are NaN and a repeated id
+    is computed as written, compared with the oracle."""
+    E, n, k, top_k = 8, 64, 512, 4
+    rng, w, stride, ids, scores = _moe_case("q4_k", E, n, k, T, top_k, 500 + T)
+    ids = ids.copy()
+    if defect == "repeat":
+        ids[T // 2, 3] = ids[T // 2, 1]
+    else:
+        ids[T // 2, 2] = E + 7
+    x = synth.activations(rng, (T, k), "f16")
+    wd, idd, xd, scd = to_dev(w), to_dev(ids), to_dev(x, "f16"), to_dev(scores)
+    _say("routing rule", defect, T)
+    for mixed in (False, True):
+        y = empty((T if mixed else T * top_k, n), "f32")
+        ws = _ws(kq, E, T, top_k, n if mixed else 0)
+        kq.kq_qmm_id("q4_k", wd, E, n, k, stride, xd, 0, idd, T, top_k, scd if mixed else None,
+                     y, ws)
+        torch.cuda.synchronize()
+        got = to_f64(y)
+        ref, s = oracle.qmm_id("q4_k", w, E, n, k, stride, x, "f16", False, ids, T, top_k,
+                               scores if mixed else None)
+        bad = np.isnan(ref).all(axis=1)
+        assert np.array_equal(np.isnan(got).all(axis=1), bad)
+        assert not np.isnan(got[~bad]).any()
+        if T >= 32:
+            assert bad.all()
+        else:
+            assert bad.sum() == (0 if defect == "repeat" else 1)
+            check_tol(got[~bad], ref[~bad], s[~bad], TAU["f16"], f"rule {defect} T={T}")
+    # GLU h [T, top_k, 256], then a down projection (64 rows of 256 columns
+    # per expert) that keeps the GLU's schedule
+    F, H = 256, 64
+    gate = synth.weight_blocks("q4_k", rng, E * F, k)
+    down = synth.weight_blocks("q4_k", rng, E * H, F)
+    gs, ds = F * synth.row_bytes("q4_k", k), H * synth.row_bytes("q4_k", F)
+    ws = _ws(kq, E, T, top_k, H)
+    h = empty((T, top_k, F), "f32")
+    gd = to_dev(gate)
+    kq.kq_moe_glu("q4_k", gd, gd, E, F, k, gs, xd, idd, T, top_k, h, ws)
+    out = empty((T, H), "f32")
+    kq.kq_qmm_id("q4_k", to_dev(down), E, H, F, ds, h, kq.LAYOUT_SLOTTED | kq.REUSE_SCHEDULE,
+                 idd, T, top_k, scd, out, ws)
+    torch.cuda.synchronize()
+    hg, og = to_f64(h), to_f64(out)
+    if T >= 32:
+        assert np.isnan(hg).all() and np.isnan(og).all()
+    else:
+        rows_bad = np.isnan(hg).all(axis=2)
+        assert rows_bad.sum() == (0 if defect == "repeat" else 1)
+        assert not np.isnan(hg[~rows_bad]).any()
 
 
 @pytest.mark.parametrize("x_dt", ["f16", "f32"])
@@ -306,6 +381,8 @@ def c4_dev(kq):
 
 
 def _moe_layer_gpu(kq, c, T):
+    """The layer as the benchmark times it: gate/up with the GLU, then the
+    mixed down projection over the slotted h that keeps the GLU's schedule."""
     E, H, F, top_k = c["n_experts"], c["hidden"], c["ffn"], c["top_k"]
     x = to_dev(c["x"][:T], "f16")
     ids = to_dev(c["ids"][:T])
@@ -317,8 +394,8 @@ def _moe_layer_gpu(kq, c, T):
     kq.kq_moe_glu("q4_k", c["gate_d"], c["up_d"], E, F, H, c["gate_stride"], x, ids, T, top_k, h,
                   ws)
     out = empty((T, H), "f32")
-    kq.kq_qmm_id("q4_k", c["down_d"], E, H, F, c["down_stride"], h, kq.LAYOUT_SLOTTED, ids, T,
-                 top_k, scores, out, ws)
+    kq.kq_qmm_id("q4_k", c["down_d"], E, H, F, c["down_stride"], h,
+                 kq.LAYOUT_SLOTTED | kq.REUSE_SCHEDULE, ids, T, top_k, scores, out, ws)
     torch.cuda.synchronize()
     return to_f64(h), to_f64(out)
 
@@ -337,14 +414,38 @@ def test_moe_c4_decode_full(kq, c4_dev):
     _check_glu(h, g, TAU["f16"], "f32", "moe C4 decode h")
 
 
+def _c4_prefill_tokens(ids, E, tile_rows=32):
+    """Tokens whose routed rows open the first tile or sit in the partial last
+    tile of several experts' segments (the schedule sorts each expert's rows by
+    token), plus the first and last token."""
+    flat = ids.ravel()
+    picked = {0, ids.shape[0] - 1}
+    for e in (0, 1, 37, 64, 100, E - 1):
+        rows = np.nonzero(flat == e)[0]  # ascending: the expert's segment order
+        if rows.size:
+            picked.add(int(rows[0] // ids.shape[1]))       # first row of the first tile
+            last_tile = (rows.size - 1) // tile_rows * tile_rows
+            picked.add(int(rows[last_tile] // ids.shape[1]))  # first row of the last tile
+            picked.add(int(rows[-1] // ids.shape[1]))       # last row of the segment
+    return sorted(picked)
+
+
 def test_moe_c4_prefill_sampled_tokens(kq, c4_dev):
-    """C4 prefill (256 tokens): whole output rows of sampled tokens."""
+    """C4 prefill (256 tokens) in the launch sequence the benchmark times:
+    whole output rows and h rows of at least 16 tokens, chosen to hit the
+    first and the partial last schedule tile of several experts."""
     c = c4_dev
     _say("moe C4 prefill")
     h, out = _moe_layer_gpu(kq, c, c["T"])
-    for t in (0, 97, 255):
-        ref, s = oracle.moe_layer("q4_k", c["gate"], c["up"], c["down"], c["n_experts"],
-                                  c["hidden"], c["ffn"], c["gate_stride"], c["down_stride"],
-                                  c["x"][t:t + 1], "f16", c["ids"][t:t + 1], 1, c["top_k"],
-                                  c["scores"][t:t + 1])
-        check_tol(out[t:t + 1], ref, s, TAU["f16"], f"moe C4 prefill token {t}")
+    toks = _c4_prefill_tokens(c["ids"], c["n_experts"], kq.MOE_TILE_ROWS)
+    extra = [t for t in range(c["T"]) if t not in toks]
+    toks = sorted(toks + extra[:max(0, 16 - len(toks))])
+    assert len(toks) >= 16
+    sel = np.array(toks)
+    ref, s = oracle.moe_layer("q4_k", c["gate"], c["up"], c["down"], c["n_experts"], c["hidden"],
+                              c["ffn"], c["gate_stride"], c["down_stride"], c["x"][sel], "f16",
+                              c["ids"][sel], len(sel), c["top_k"], c["scores"][sel])
+    check_tol(out[sel], ref, s, TAU["f16"], f"moe C4 prefill tokens {toks}")
+    g = oracle.moe_glu("q4_k", c["gate"], c["up"], c["n_experts"], c["ffn"], c["hidden"],
+                       c["gate_stride"], c["x"][sel], "f16", c["ids"][sel], len(sel), c["top_k"])
+    _check_glu(h[sel], g, TAU["f16"], "f32", "moe C4 prefill h")

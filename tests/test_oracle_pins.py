@@ -418,6 +418,67 @@ def test_qmm_id_invalid_id_poisons_its_row(orc):
     assert np.all(np.isnan(ym[1])) and np.all(np.isfinite(ym[[0, 2]]))
 
 
+def _dup_case(T, seed):
+    import synth
+
+    E, n, k, top_k = 6, 32, 256, 3
+    rng, w, stride, ids, scores = _moe_small(E=E, n=n, k=k, T=T, top_k=top_k, seed=seed)
+    x = synth.activations(rng, (T, k), "f16")
+    return E, n, k, top_k, w, stride, ids.copy(), scores, x
+
+
+def test_routing_rule_below_32_tokens(orc):
+    """mlx-native "quantized_matmul_id_ggml.rs": the matrix-vector route only
+    bounds-checks.  Below 32 tokens a repeated id is computed as written (its
+    slot equals the first slot with that id) and an out-of-range id poisons
+    only the rows it touches."""
+    T = 31
+    E, n, k, top_k, w, stride, ids, scores, x = _dup_case(T, 61)
+    ids[4, 2] = ids[4, 0]
+    ids[9, 1] = E
+    assert not orc.routing_poisons_all(ids, E)
+    y, _ = orc.qmm_id("q4_k", w, E, n, k, stride, x, "f16", False, ids, T, top_k)
+    assert np.array_equal(y[4 * top_k + 2], y[4 * top_k + 0])
+    bad = 9 * top_k + 1
+    assert np.all(np.isnan(y[bad])) and np.all(np.isfinite(np.delete(y, bad, axis=0)))
+    ym, _ = orc.qmm_id("q4_k", w, E, n, k, stride, x, "f16", False, ids, T, top_k, scores)
+    assert np.all(np.isnan(ym[9])) and np.all(np.isfinite(np.delete(ym, 9, axis=0)))
+    want4 = sum(float(scores[4, r]) * y[4 * top_k + r] for r in range(top_k))
+    assert np.allclose(ym[4], want4, rtol=1e-13, atol=0)
+    r = orc.route(ids, E, 32)
+    assert r["n_invalid"] == 1 and len(r["tiles"]) > 0
+
+
+@pytest.mark.parametrize("defect", ["repeat", "range"])
+def test_routing_rule_from_32_tokens(orc, defect):
+    """mlx-native "quantized_matmul_id_ggml.rs": the matrix-matrix route (from
+    32 tokens on) requires distinct ids per token, and any out-of-range or
+    repeated id writes NaN to the entire output and leaves the schedule with
+    no tiles (no weight is read)."""
+    T = 32
+    E, n, k, top_k, w, stride, ids, scores, x = _dup_case(T, 62)
+    good = ids.copy()
+    assert not orc.routing_poisons_all(good, E)
+    y0, _ = orc.qmm_id("q4_k", w, E, n, k, stride, x, "f16", False, good, T, top_k)
+    assert np.all(np.isfinite(y0))
+    if defect == "repeat":
+        ids[17, 1] = ids[17, 2]
+    else:
+        ids[17, 1] = E + 100
+    assert orc.routing_poisons_all(ids, E)
+    for sc in (None, scores):
+        y, s = orc.qmm_id("q4_k", w, E, n, k, stride, x, "f16", False, ids, T, top_k, sc)
+        assert np.all(np.isnan(y)) and np.all(np.isnan(s))
+    glu = orc.moe_glu("q4_k", w, w, E, n, k, stride, x, "f16", ids, T, top_k)
+    assert all(np.all(np.isnan(glu[key])) for key in glu)
+    r = orc.route(ids, E, 32)
+    assert r["n_invalid"] == 1 and len(r["tiles"]) == 0
+    flat = ids.ravel()
+    assert np.array_equal(r["counts"], np.bincount(flat[flat < E], minlength=E))
+    # the same defect in a 31-token call follows the matrix-vector rule
+    assert not orc.routing_poisons_all(ids[1:], E)
+
+
 def test_silu_definition(orc):
     from scipy.special import expit
 
@@ -445,6 +506,19 @@ def test_gelu_tanh_pins(orc):
     assert diff.max() < 1e-3 and diff.max() > 1e-5  # the approximation, not the exact function
 
 
+def test_gelu_tanh_against_torch(orc):
+    """The same function from an independent implementation: torch's GELU with
+    approximate='tanh', evaluated in float64.  A mistyped cubic coefficient
+    (0.0447 for 0.044715) moves the result by ~1e-5 and fails here."""
+    import torch
+
+    zs = np.concatenate([np.linspace(-12.0, 12.0, 2401), np.geomspace(1e-6, 12.0, 200),
+                         -np.geomspace(1e-6, 12.0, 200)])
+    ref = torch.nn.functional.gelu(torch.from_numpy(zs), approximate="tanh").numpy()
+    got = np.array([orc.gelu_tanh(z) for z in zs])
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-15)
+
+
 def test_moe_glu_act_selects_the_activation(orc):
     """h = act(g) * u with the g and u the oracle returns: act 0 silu, act 1
     gelu (tanh approximation); an unknown act is rejected."""
@@ -457,10 +531,15 @@ def test_moe_glu_act_selects_the_activation(orc):
     stride = n * synth.row_bytes("q4_k", k)
     x = synth.activations(rng, (T, k), "f16")
     ids = np.array([[0, 2], [1, 0]], np.uint32)
-    for act, fn in ((0, orc.silu), (1, orc.gelu_tanh)):
+    import torch
+
+    # the activations from torch (float64), not from the oracle itself
+    acts = ((0, lambda g: torch.nn.functional.silu(torch.from_numpy(g)).numpy()),
+            (1, lambda g: torch.nn.functional.gelu(torch.from_numpy(g), approximate="tanh").numpy()))
+    for act, fn in acts:
         r = orc.moe_glu("q4_k", gate, up, E, n, k, stride, x, "f16", ids, T, top_k, act)
-        want = np.vectorize(fn)(r["g"]) * r["u"]
-        assert np.allclose(r["h"], want, rtol=1e-14, atol=0.0)
+        want = fn(r["g"]) * r["u"]
+        assert np.allclose(r["h"], want, rtol=1e-12, atol=0.0)
     with pytest.raises(ValueError):
         orc.moe_glu("q4_k", gate, up, E, n, k, stride, x, "f16", ids, T, top_k, 7)
 
@@ -526,15 +605,17 @@ def test_moe_layer_brute_force_small(orc):
 
 # ------------------------------------------------------------------ routing schedule
 @pytest.mark.parametrize("tile_rows", [1, 4, 16, 64])
-def test_route_schedule_invariants(orc, tile_rows):
+@pytest.mark.parametrize("T,n_bad", [(20, 2), (50, 0)])
+def test_route_schedule_invariants(orc, tile_rows, T, n_bad):
     rng = _rng(14)
-    E, T, top_k = 16, 50, 4
+    E, top_k = 16, 4
     ids = np.stack([rng.choice(E, top_k, replace=False) for _ in range(T)]).astype(np.uint32)
-    ids.ravel()[[5, 77]] = [E, E + 9]  # two invalid ids
+    if n_bad:
+        ids.ravel()[[5, 77]] = [E, E + 9]  # two out-of-range ids (matrix-vector rule)
     r = orc.route(ids, E, tile_rows)
     flat = ids.ravel()
     valid = flat < E
-    assert r["n_invalid"] == 2
+    assert r["n_invalid"] == n_bad
     assert np.array_equal(r["counts"], np.bincount(flat[valid], minlength=E))
     assert np.array_equal(r["offsets"], np.concatenate([[0], np.cumsum(r["counts"])]))
     perm = r["perm"]
