@@ -168,22 +168,33 @@ def main():
                             note="batch 1, each output feeds the next call (values may overflow "
                                  "fp16; the work is the same)"))
 
-    c3_parts = []
+    def scratch(kind, n, k, m, dt):
+        nb = kq.kq_qmm_workspace_bytes(kind, n, k, m, dt)
+        return torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
+
+    c3_parts, extra_parts = [], []
     if "qmm_c3" in wanted:
         cases, xh = workloads.c3()
         x = d16(xh, torch.bfloat16)
         for case in cases:
             kind, n, k = case["kind"], case["n"], case["k"]
             w = d8(case["w"])
-            ws = copies(w, w.numel(), min_total=4 * w.numel())
+            ws = copies(w, w.numel())  # >= 1 GiB of distinct weight copies
             for m in (512, 2048):
                 y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
                 xm = x[:m]
-                part = [(lambda kind=kind, n=n, k=k, m=m, y=y, ws=ws, xm=xm:
-                         kq.kq_qmm(kind, nxt(ws), n, k, xm, m, y)) for _ in range(len(ws))]
+                sc = scratch(kind, n, k, m, torch.bfloat16)
+                part = [(lambda kind=kind, n=n, k=k, m=m, y=y, ws=ws, xm=xm, sc=sc:
+                         kq.kq_qmm_ws(kind, nxt(ws), n, k, xm, m, y, sc)) for _ in range(len(ws))]
                 c3_parts.append(Stage(f"qmm_c3_{kind}_{n}x{k}_m{m}", part,
                                       len(part) * (w.numel() + m * (k + n) * 2),
-                                      len(part) * 2 * m * n * k))
+                                      len(part) * 2 * m * n * k, note="kq_qmm_ws"))
+                # the same product without a workspace (bf16 rows scaled per tile column)
+                part = [(lambda kind=kind, n=n, k=k, m=m, y=y, ws=ws, xm=xm:
+                         kq.kq_qmm(kind, nxt(ws), n, k, xm, m, y)) for _ in range(8)]
+                extra_parts.append(Stage(f"qmm_c3_noworkspace_{kind}_{n}x{k}_m{m}", part,
+                                         len(part) * (w.numel() + m * (k + n) * 2),
+                                         len(part) * 2 * m * n * k, note="kq_qmm"))
 
     if "tq1_c5" in wanted:
         calls_v, calls_m, bv, bm, fv, fm = [], [], 0, 0, 0, 0
@@ -199,13 +210,14 @@ def main():
                                kq.kq_qmv("tq1_g128", nxt(ws), n, k, x[:1], 1, y1))
                 bv += w.numel() + (k + n) * 2
                 fv += 2 * n * k
-            for _ in range(4):
-                calls_m.append(lambda n=n, k=k, ws=ws, x=x, ym=ym:
-                               kq.kq_qmm("tq1_g128", nxt(ws), n, k, x, 512, ym))
+            sc = scratch("tq1_g128", n, k, 512, torch.float16)
+            for _ in range(len(ws)):
+                calls_m.append(lambda n=n, k=k, ws=ws, x=x, ym=ym, sc=sc:
+                               kq.kq_qmm_ws("tq1_g128", nxt(ws), n, k, x, 512, ym, sc))
                 bm += w.numel() + 512 * (k + n) * 2
                 fm += 2 * 512 * n * k
         stages.append(Stage("tq1_c5_b1", calls_v, bv, fv, note="TQ1 GEMV batch 1, fp16"))
-        stages.append(Stage("tq1_c5_m512", calls_m, bm, fm, note="TQ1 qmm M=512, fp16"))
+        stages.append(Stage("tq1_c5_m512", calls_m, bm, fm, note="TQ1 qmm M=512, fp16 (kq_qmm_ws)"))
 
     if "moe_c4" in wanted:
         c = workloads.c4()
@@ -258,7 +270,7 @@ def main():
     # ---------------------------------------------------------------- timing
     # Each stage's calls are captured once into a HIP graph and replayed, so
     # the kernels run back to back instead of waiting on Python launches.
-    timed = [s for s in stages if s.name not in ("qmv_c2",)] + c2_parts + c3_parts
+    timed = [s for s in stages if s.name not in ("qmv_c2",)] + c2_parts + c3_parts + extra_parts
     graphs = {}
     for s in timed:
         s.run()  # eager pass: lazy initialisation outside the capture

@@ -186,7 +186,40 @@ kq_status kq_qmm(kq_type t, const void* w, int64_t n, int64_t k, const void* x, 
     if (st) return st;
     if (m <= 16 || x_dt == KQ_F32)
         return dense_skinny(t, w, n, k, row_bytes, x, x_dt, m, y, y_dt, (hipStream_t)stream);
-    return launched(kq::launch_gemm(t, x_dt, w, n, k, x, m, y, y_dt, (hipStream_t)stream));
+    return launched(kq::launch_gemm(t, x_dt, w, n, k, x, m, y, y_dt, nullptr, (hipStream_t)stream));
+}
+
+// The products that take the decode kernels (m <= 16) or the fp32 path need
+// no scratch; the prefill GEMM takes the layout of kq::gemm_workspace.
+static bool qmm_uses_workspace(int64_t m, kq_dtype x_dt) { return m > 16 && x_dt != KQ_F32; }
+
+size_t kq_qmm_workspace_bytes(kq_type t, int64_t n, int64_t k, int64_t m, kq_dtype x_dt) {
+    if (!qk_of(t) || n <= 0 || k <= 0 || m <= 0 || k % qk_of(t) || !valid_dt(x_dt)) return 0;
+    if (n > kMaxN || k > kMaxK || m > kMaxM || !qmm_uses_workspace(m, x_dt)) return 0;
+    return (size_t)kq::gemm_workspace(t, n, k, m, x_dt).bytes;
+}
+
+kq_status kq_qmm_ws(kq_type t, const void* w, int64_t n, int64_t k, const void* x, kq_dtype x_dt,
+                    int64_t m, void* y, kq_dtype y_dt, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+    int64_t row_bytes;
+    kq_status st = check_product(t, w, n, k, x, x_dt, m, y, y_dt, row_bytes);
+    if (st) return st;
+    hipStream_t s = (hipStream_t)stream;
+    if (!qmm_uses_workspace(m, x_dt))
+        return dense_skinny(t, w, n, k, row_bytes, x, x_dt, m, y, y_dt, s);
+    const int64_t need = kq::gemm_workspace(t, n, k, m, x_dt).bytes;
+    if (need > 0) {
+        if (!workspace || !aligned(workspace, 256))
+            return fail(KQ_ERR_WORKSPACE, "workspace must be non-null and 256-byte aligned");
+        if ((int64_t)workspace_bytes < need)
+            return fail(KQ_ERR_WORKSPACE, "workspace smaller than kq_qmm_workspace_bytes()");
+        const int64_t xb = m * k * elem_size(x_dt), yb = m * n * elem_size(y_dt);
+        if (overlap({workspace, need}, {w, n * row_bytes}) || overlap({workspace, need}, {x, xb}) ||
+            overlap({workspace, need}, {y, yb}))
+            return fail(KQ_ERR_INVALID_ARG, "workspace overlaps an input or the output");
+    }
+    return launched(kq::launch_gemm(t, x_dt, w, n, k, x, m, y, y_dt, need > 0 ? workspace : nullptr, s));
 }
 
 size_t kq_moe_workspace_bytes(int64_t n_experts, int64_t n_tokens, int64_t top_k, int64_t n_out) {

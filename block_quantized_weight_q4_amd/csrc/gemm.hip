@@ -4,14 +4,30 @@
 // "ternel_packed_model.py", tq1_gemm (decode a weight once and reuse it
 // across a whole block of activation rows on the matrix units).
 //
-// The contraction runs on v_mfma_f32_32x32x16 in the activation's 16-bit
-// type (bf16 or fp16) with fp32 accumulation.  A workgroup of eight waves owns
-// a BM x BN output tile; per K step of 64 it decodes its BN x 64 weight tile
-// once into LDS (so each decoded weight feeds BM rows) next to the BM x 64
-// activation tile.  The global loads of step k+1 are issued before the MFMAs
-// of step k and written to LDS after them, so memory latency overlaps the
-// matrix work.  Decoded weights are rounded once from fp32 to the 16-bit
-// operand type (round to nearest even).
+// The contraction runs on v_mfma_f32_32x32x16_f16 with fp32 accumulation.  A
+// workgroup of eight waves owns a BM x BN output tile; per K step of 64 it
+// decodes its BN x 64 weight tile once into LDS (so each decoded weight feeds
+// BM rows) next to the BM x 64 activation tile.  The global loads of step k+1
+// are issued before the MFMAs of step k and written to LDS after them, so
+// memory latency overlaps the matrix work.
+//
+// Operand precision (the product must stay within 2e-3 * sum|x*w| of the
+// exact one for 16-bit activations):
+//  - Weights are decoded exactly in fp32 and rounded once to fp16.  Q4_K and
+//    Q8_0 weights are integer multiples of 2^-24 (d and dmin are fp16), so a
+//    weight below 2^-14 is an exact fp16 subnormal and any other keeps 11
+//    significant bits: relative error <= 2^-11 for every block whose weights
+//    stay below 65520.  TQ1 weights (digit - 1) * scale are exact.
+//  - fp16 activations are used as they are.  bf16 activations carry 8
+//    significant bits, which fp16 holds exactly within a window of 2^31: each
+//    workgroup first finds, per activation row, the largest and smallest
+//    nonzero magnitude over all of K, scales the row by 2^-e so that its
+//    largest magnitude lies in [2^14, 2^15), and multiplies the row's results
+//    by 2^e at the store (both exact).
+//  - A tile with a weight that could reach 65520 (|d| or |dmin| too large,
+//    Inf or NaN) or with an activation row outside the window (a nonzero
+//    range above 2^31, bf16 subnormals, Inf or NaN) is recomputed by an exact
+//    fp32 path instead, so no legal input loses precision silently.
 #include "kq_device.h"
 #include "kq_internal.h"
 
@@ -20,28 +36,19 @@ namespace kq {
 constexpr int BK = 64, LDS_STRIDE = BK + 8;  // +8 halves: rows start in different banks
 
 typedef float float2_t __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
-template <int XDT> struct Op16;
-template <> struct Op16<BF16> {
-    static __device__ __forceinline__ uint32_t pack(float a, float b) {
-        return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2_t{a, b}, bf16x2));
-    }
-    static __device__ __forceinline__ float16_t mma(const u32x4& a, const u32x4& b, float16_t c) {
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-    }
-};
-template <> struct Op16<F16> {
-    static __device__ __forceinline__ uint32_t pack(float a, float b) {
-        return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2_t{a, b}, half2v));
-    }
-    static __device__ __forceinline__ float16_t mma(const u32x4& a, const u32x4& b, float16_t c) {
-        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, a),
-                                                      __builtin_bit_cast(half8, b), c, 0, 0, 0);
-    }
-};
+// two fp32 values -> one dword of fp16 (round to nearest even)
+__device__ __forceinline__ uint32_t pack_h(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2_t{a, b}, half2v));
+}
+__device__ __forceinline__ float16_t mma_h(const u32x4& a, const u32x4& b, float16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, a),
+                                                  __builtin_bit_cast(half8, b), c, 0, 0, 0);
+}
+// fp16 overflows at 65520 (round to nearest even); NaN compares false
+__device__ __forceinline__ bool f16_safe(float bound) { return bound < 65520.0f; }
 
 // ---------------------------------------------------------------- weight tiles
 // One thread role = (tile row r, half h): 32 of the 64 weights of row r in a
@@ -59,9 +66,9 @@ template <> struct WTile<Q4_K> {
         r.hd = *(const u32x4*)blk;
         r.q = *(const u32x4*)(blk + 16 + 32 * (s & 3) + 16 * h);
     }
-    template <int XDT>
     static __device__ __forceinline__ void decode(const Raw& r, int s, int h, uint32_t (&lo)[8],
-                                                  uint32_t (&hi)[8], int& col_lo, int& col_hi) {
+                                                  uint32_t (&hi)[8], int& col_lo, int& col_hi,
+                                                  bool& big) {
         const int c = s & 3;
         int sc0, m0, sc1, m1;
         q4k_scale_min(r.hd, 2 * c, sc0, m0);
@@ -72,6 +79,8 @@ template <> struct WTile<Q4_K> {
         // high nibbles are converted in place (16 q) against s1 / 16: the
         // product is the same, and each byte converts in one instruction
         const float s1h = s1 * 0.0625f;
+        big |= !f16_safe(__builtin_fabsf(s0) * 15.0f + __builtin_fabsf(n0)) ||
+               !f16_safe(__builtin_fabsf(s1h) * 240.0f + __builtin_fabsf(n1));
         auto byte = [](uint32_t v, int j) { return (float)((v >> (8 * j)) & 0xffu); };
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -81,10 +90,10 @@ template <> struct WTile<Q4_K> {
             asm("" : "+v"(ml), "+v"(mh));
 #pragma unroll
             for (int b = 0; b < 4; b += 2) {
-                lo[2 * i + b / 2] = Op16<XDT>::pack(__builtin_fmaf(s0, byte(ml, b), n0),
-                                                    __builtin_fmaf(s0, byte(ml, b + 1), n0));
-                hi[2 * i + b / 2] = Op16<XDT>::pack(__builtin_fmaf(s1h, byte(mh, b), n1),
-                                                    __builtin_fmaf(s1h, byte(mh, b + 1), n1));
+                lo[2 * i + b / 2] = pack_h(__builtin_fmaf(s0, byte(ml, b), n0),
+                                           __builtin_fmaf(s0, byte(ml, b + 1), n0));
+                hi[2 * i + b / 2] = pack_h(__builtin_fmaf(s1h, byte(mh, b), n1),
+                                           __builtin_fmaf(s1h, byte(mh, b + 1), n1));
             }
         }
         col_lo = 16 * h;
@@ -98,9 +107,9 @@ template <> struct WTile<Q4_K> {
         r.hd = *(const u32x4*)blk;
         r.q = *(const u32x2*)(blk + 16 + 32 * (s & 3) + 8 * q);
     }
-    template <int XDT>
     static __device__ __forceinline__ void decode_q(const RawQ& r, int s, int q, uint32_t (&lo)[4],
-                                                    uint32_t (&hi)[4], int& col_lo, int& col_hi) {
+                                                    uint32_t (&hi)[4], int& col_lo, int& col_hi,
+                                                    bool& big) {
         const int c = s & 3;
         int sc0, m0, sc1, m1;
         q4k_scale_min(r.hd, 2 * c, sc0, m0);
@@ -108,6 +117,8 @@ template <> struct WTile<Q4_K> {
         const float d = q4k_d(r.hd), dmin = q4k_dmin(r.hd);
         const float s0 = d * (float)sc0, s1h = d * (float)sc1 * 0.0625f;
         const float n0 = -dmin * (float)m0, n1 = -dmin * (float)m1;
+        big |= !f16_safe(__builtin_fabsf(s0) * 15.0f + __builtin_fabsf(n0)) ||
+               !f16_safe(__builtin_fabsf(s1h) * 240.0f + __builtin_fabsf(n1));
         auto byte = [](uint32_t v, int j) { return (float)((v >> (8 * j)) & 0xffu); };
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
@@ -115,10 +126,10 @@ template <> struct WTile<Q4_K> {
             asm("" : "+v"(ml), "+v"(mh));
 #pragma unroll
             for (int b = 0; b < 4; b += 2) {
-                lo[2 * i + b / 2] = Op16<XDT>::pack(__builtin_fmaf(s0, byte(ml, b), n0),
-                                                    __builtin_fmaf(s0, byte(ml, b + 1), n0));
-                hi[2 * i + b / 2] = Op16<XDT>::pack(__builtin_fmaf(s1h, byte(mh, b), n1),
-                                                    __builtin_fmaf(s1h, byte(mh, b + 1), n1));
+                lo[2 * i + b / 2] = pack_h(__builtin_fmaf(s0, byte(ml, b), n0),
+                                           __builtin_fmaf(s0, byte(ml, b + 1), n0));
+                hi[2 * i + b / 2] = pack_h(__builtin_fmaf(s1h, byte(mh, b), n1),
+                                           __builtin_fmaf(s1h, byte(mh, b + 1), n1));
             }
         }
         col_lo = 8 * q;
@@ -155,21 +166,22 @@ template <> struct WTile<Q8_0> {
     // order.  A quant byte xor 0x80 is q + 128, converted in one instruction,
     // and fma(d, q + 128, -128 d) is d q exactly (a zero weight comes out as
     // +0 whatever the sign of d).
-    template <int XDT>
     static __device__ __forceinline__ void decode(const Raw& r, int s, int h, uint32_t (&lo)[8],
-                                                  uint32_t (&hi)[8], int& col_lo, int& col_hi) {
+                                                  uint32_t (&hi)[8], int& col_lo, int& col_hi,
+                                                  bool& big) {
         uint32_t sh = h ? 0u : 16u;
         asm("" : "+v"(sh));  // one funnel shift by a register, not two selected
         const float d = half_bits_to_float(h ? r.tail : (r.w[0] & 0xffffu));
         const float nd = -128.0f * d;
+        big |= !f16_safe(__builtin_fabsf(nd));
         auto byte = [](uint32_t v, int j) { return (float)((v >> (8 * j)) & 0xffu); };
         uint32_t v[16];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const uint32_t next = j < 7 ? r.w[j + 1] : r.tail;
             const uint32_t u = __builtin_amdgcn_alignbit(next, r.w[j], sh) ^ 0x80808080u;
-            v[2 * j] = Op16<XDT>::pack(__builtin_fmaf(d, byte(u, 0), nd), __builtin_fmaf(d, byte(u, 1), nd));
-            v[2 * j + 1] = Op16<XDT>::pack(__builtin_fmaf(d, byte(u, 2), nd), __builtin_fmaf(d, byte(u, 3), nd));
+            v[2 * j] = pack_h(__builtin_fmaf(d, byte(u, 0), nd), __builtin_fmaf(d, byte(u, 1), nd));
+            v[2 * j + 1] = pack_h(__builtin_fmaf(d, byte(u, 2), nd), __builtin_fmaf(d, byte(u, 3), nd));
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) lo[i] = v[i], hi[i] = v[8 + i];
@@ -198,21 +210,22 @@ template <> struct WTile<Q8_0> {
         r.next = *(const uint16_t*)(blk + 16 + 16 * hh);
         r.sc = *(const uint16_t*)blk;
     }
-    template <int XDT>
     static __device__ __forceinline__ void decode_q(const RawQ& r, int s, int q, uint32_t (&lo)[4],
-                                                    uint32_t (&hi)[4], int& col_lo, int& col_hi) {
+                                                    uint32_t (&hi)[4], int& col_lo, int& col_hi,
+                                                    bool& big) {
         uint32_t sh = (q >> 1) ? 0u : 16u;
         asm("" : "+v"(sh));
         const float d = half_bits_to_float(r.sc);
         const float nd = -128.0f * d;
+        big |= !f16_safe(__builtin_fabsf(nd));
         auto byte = [](uint32_t v, int j) { return (float)((v >> (8 * j)) & 0xffu); };
         uint32_t v[8];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const uint32_t next = j < 3 ? r.w[j + 1] : r.next;
             const uint32_t u = __builtin_amdgcn_alignbit(next, r.w[j], sh) ^ 0x80808080u;
-            v[2 * j] = Op16<XDT>::pack(__builtin_fmaf(d, byte(u, 0), nd), __builtin_fmaf(d, byte(u, 1), nd));
-            v[2 * j + 1] = Op16<XDT>::pack(__builtin_fmaf(d, byte(u, 2), nd), __builtin_fmaf(d, byte(u, 3), nd));
+            v[2 * j] = pack_h(__builtin_fmaf(d, byte(u, 0), nd), __builtin_fmaf(d, byte(u, 1), nd));
+            v[2 * j + 1] = pack_h(__builtin_fmaf(d, byte(u, 2), nd), __builtin_fmaf(d, byte(u, 3), nd));
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) lo[i] = v[i], hi[i] = v[4 + i];
@@ -231,8 +244,7 @@ template <> struct WTile<TQ1> {
 #pragma unroll
         for (int i = 0; i < 7; ++i) r.w[i] = p[i];
     }
-    // fp16 activations: digits two at a time with packed 16-bit integer
-    // arithmetic.  A code byte c (<= 242) in fixed point, q = ceil(256 c /
+    // Digits two at a time with packed 16-bit integer arithmetic.  A code byte c (<= 242) in fixed point, q = ceil(256 c /
     // 243), holds its base-3 digits as a fraction: digit k is the integer part
     // of 3 * ((q * 3^(4-k)) mod 256) / 256.  With the digit placed in the low
     // byte of the fp16 1024 (0x6400 | d), subtracting 1025 gives d - 1 exactly,
@@ -274,37 +286,17 @@ template <> struct WTile<TQ1> {
             v[i] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(h16x2, h) + off) * sc2);
         }
     }
-    template <int XDT, int C0, int NP>
-    static __device__ __forceinline__ void cols(const Raw& r, uint32_t (&v)[NP]) {
-        if constexpr (XDT == F16) {
-            cols_f16<C0, NP>(r, v);
-        } else {
-            // bf16 activations: w = (digit - 1) * scale rounded to bf16
-            const float sc = half_bits_to_float(r.w[6] >> 16);
-#pragma unroll
-            for (int i = 0; i < NP; ++i) {
-                float t[2];
-#pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    const int col = C0 + 2 * i + e;
-                    const int slot = col < 125 ? col / 5 : 25;
-                    const int digit = col < 125 ? col - 5 * slot : col - 125;
-                    const uint32_t code = (r.w[slot >> 2] >> (8 * (slot & 3))) & 0xffu;
-                    t[e] = (float)tq1_trit(code, digit) * sc;
-                }
-                v[i] = Op16<XDT>::pack(t[0], t[1]);
-            }
-        }
-    }
-    template <int XDT>
+    // (weights are at most |scale| and never overflow fp16; Inf and NaN scales
+    // give the same Inf and NaN products as the exact values)
     static __device__ __forceinline__ void decode(const Raw& r, int s, int h, uint32_t (&lo)[8],
-                                                  uint32_t (&hi)[8], int& col_lo, int& col_hi) {
+                                                  uint32_t (&hi)[8], int& col_lo, int& col_hi,
+                                                  bool&) {
         uint32_t v[16];
         switch (2 * (s & 1) + h) {
-        case 0: cols<XDT, 0, 16>(r, v); break;
-        case 1: cols<XDT, 32, 16>(r, v); break;
-        case 2: cols<XDT, 64, 16>(r, v); break;
-        default: cols<XDT, 96, 16>(r, v); break;
+        case 0: cols_f16<0, 16>(r, v); break;
+        case 1: cols_f16<32, 16>(r, v); break;
+        case 2: cols_f16<64, 16>(r, v); break;
+        default: cols_f16<96, 16>(r, v); break;
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) lo[i] = v[i], hi[i] = v[8 + i];
@@ -316,19 +308,19 @@ template <> struct WTile<TQ1> {
     static __device__ __forceinline__ void fetch_q(const uint8_t* row, int s, int, RawQ& r, bool) {
         fetch(row, s, 0, r, true);
     }
-    template <int XDT>
     static __device__ __forceinline__ void decode_q(const RawQ& r, int s, int q, uint32_t (&lo)[4],
-                                                    uint32_t (&hi)[4], int& col_lo, int& col_hi) {
+                                                    uint32_t (&hi)[4], int& col_lo, int& col_hi,
+                                                    bool&) {
         uint32_t v[8];
         switch (4 * (s & 1) + q) {
-        case 0: cols<XDT, 0, 8>(r, v); break;
-        case 1: cols<XDT, 16, 8>(r, v); break;
-        case 2: cols<XDT, 32, 8>(r, v); break;
-        case 3: cols<XDT, 48, 8>(r, v); break;
-        case 4: cols<XDT, 64, 8>(r, v); break;
-        case 5: cols<XDT, 80, 8>(r, v); break;
-        case 6: cols<XDT, 96, 8>(r, v); break;
-        default: cols<XDT, 112, 8>(r, v); break;
+        case 0: cols_f16<0, 8>(r, v); break;
+        case 1: cols_f16<16, 8>(r, v); break;
+        case 2: cols_f16<32, 8>(r, v); break;
+        case 3: cols_f16<48, 8>(r, v); break;
+        case 4: cols_f16<64, 8>(r, v); break;
+        case 5: cols_f16<80, 8>(r, v); break;
+        case 6: cols_f16<96, 8>(r, v); break;
+        default: cols_f16<112, 8>(r, v); break;
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) lo[i] = v[i], hi[i] = v[4 + i];
@@ -341,27 +333,83 @@ template <> struct WTile<TQ1> {
 template <bool Q, class WT> struct RawSel { using type = typename WT::Raw; };
 template <class WT> struct RawSel<true, WT> { using type = typename WT::RawQ; };
 
-// ---------------------------------------------------------------- kernel
-// BM x BN tile, NW waves as 2 x (NW/2), each a (BM/2) x (2BN/NW) sub-tile of
-// 32x32 MFMA blocks.  With eight waves two share each SIMD, so one wave's
-// weight decoding overlaps the other's matrix work.
-template <int C, int XDT, int BM, int BN, int NW>
-__global__ __launch_bounds__(64 * NW) void gemm_kernel(const uint8_t* __restrict__ w, int64_t n,
-                                                       int64_t k, const uint16_t* __restrict__ x,
-                                                       int64_t m, void* __restrict__ y, int y_dt) {
+// Activation modes of the GEMM kernel.
+enum XMode {
+    XM_F16 = 0,     // fp16 activations, used as they are
+    XM_BF16 = 1,    // bf16 activations, row exponents found by each workgroup
+    XM_SCALED = 2,  // fp16 rows pre-scaled by 2^-e, exponents in GemmArgs::xexp
+};
+constexpr int32_t kBadRow = INT32_MIN;  // an activation row outside the fp16 window
+
+// The exact path of one tile: every output is the fp32 sum, in column
+// order, of the exact activation (fp32) times the weight decoded exactly to
+// fp32, with no fp16 operand.  Slow (each thread decodes its weight row once
+// per group of eight activation rows); taken only by tiles whose weights or
+// activations do not fit the fp16 operands.  Covers columns [c0, c1) of K
+// (the workgroup's share when K is split).
+template <int C, int BM, int BN, int NT>
+__device__ __forceinline__ void gemm_tile_exact(const GemmArgs& a, int64_t row_bytes, int64_t m0,
+                                                int64_t n0, int64_t c0, int64_t c1, int tid) {
+    constexpr int RS = NT / BN;  // threads per weight row
+    static_assert(RS >= 1 && NT % BN == 0, "tile shape");
+    const int64_t gn = n0 + tid % BN;
+    if (gn >= a.n) return;
+    const uint8_t* wr = a.w + gn * row_bytes;
+    float* part = a.part && gridDim.z > 1 ? a.part + (int64_t)blockIdx.z * a.m * a.n : nullptr;
+    for (int r0 = tid / BN; r0 < BM; r0 += 8 * RS) {
+        float acc[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
+        for (int64_t c = c0; c < c1; ++c) {
+            const float wv = weight_exact<C>(wr, c);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int64_t gm = m0 + r0 + RS * j;
+                if (r0 + RS * j < BM && gm < a.m) {
+                    const float xv = a.x_src_dt == BF16 ? load_act<BF16>(a.x_src, gm * a.k + c)
+                                                        : load_act<F16>(a.x_src, gm * a.k + c);
+                    acc[j] = __builtin_fmaf(xv, wv, acc[j]);
+                }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int64_t gm = m0 + r0 + RS * j;
+            if (r0 + RS * j >= BM || gm >= a.m) continue;
+            if (part) part[gm * a.n + gn] = acc[j];
+            else if (a.y_dt == F32) store_out<F32>(a.y, gm * a.n + gn, acc[j]);
+            else if (a.y_dt == F16) store_out<F16>(a.y, gm * a.n + gn, acc[j]);
+            else store_out<BF16>(a.y, gm * a.n + gn, acc[j]);
+        }
+    }
+}
+
+template <int C, int XM, int BM, int BN, int NW, bool SPLIT>
+__global__ __launch_bounds__(64 * NW) void gemm_kernel(const GemmArgs a) {
     constexpr int NT = 64 * NW, WN = NW / 2;
     constexpr int TM = BM / 2, TN = BN / WN, FM = TM / 32, FN = TN / 32;
     static_assert(FM >= 1 && FN >= 1 && 2 * BN <= NT, "tile shape");
     constexpr int XP = BM * 8 / NT;  // 16-byte activation pieces per thread per step
     constexpr int ASZ = BM * LDS_STRIDE, BSZ = BN * LDS_STRIDE;
+    constexpr bool ROWEXP = XM != XM_F16;  // results are scaled by 2^e per row
     using WT = WTile<C>;
     // two stages of [activation tile | weight tile]
     __shared__ __align__(16) uint16_t lds[2 * (ASZ + BSZ)];
+    // scaled activations: each tile row's exponent e (results x 2^e)
+    __shared__ int32_t xe_lds[ROWEXP ? BM : 1];
+    __shared__ int32_t exact_flag;  // the tile takes the exact path
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
+    const int64_t n = a.n, k = a.k, m = a.m;
+    const uint16_t* __restrict__ x = a.x;
+    const uint8_t* __restrict__ w = a.w;
     const int64_t n0 = (int64_t)blockIdx.x * BN, m0 = (int64_t)blockIdx.y * BM;
     const int64_t row_bytes = (k / CodecInfo<C>::QK) * CodecInfo<C>::BYTES;
-    const int steps = (int)((k + BK - 1) / BK);
+    // this workgroup's K steps: [sb, sb + steps) of the whole product's
+    const int total_steps = (int)((k + BK - 1) / BK);
+    const int sb = SPLIT ? (int)blockIdx.z * a.split_steps : 0;
+    const int steps = !SPLIT ? total_steps
+                      : total_steps - sb < a.split_steps ? total_steps - sb : a.split_steps;
 
     // weight role: tile row wr and part wh of each step, a half (wh < 2) or,
     // when the threads are four times the tile's rows, a quarter (wh < 4), so
@@ -387,6 +435,68 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const uint8_t* __restrict
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = float16_t{};
 
+    // A thread stages 16-byte pieces p = tid + NT i (i < XP) of each step:
+    // tile row p / 8, columns 8 (p % 8) .. +7.  The eight threads of one row
+    // are eight neighbouring lanes of one wave.
+    if (tid == 0) exact_flag = 0;
+    __syncthreads();  // before any thread may raise it
+    if constexpr (XM == XM_SCALED) {
+        for (int r = tid; r < BM; r += NT) {
+            const int32_t e = m0 + r < m ? a.xexp[m0 + r] : 0;
+            xe_lds[r] = e == kBadRow ? 0 : e;
+            if (e == kBadRow) exact_flag = 1;
+        }
+        __syncthreads();
+    }
+    if constexpr (XM == XM_BF16) {
+        // Per row: the largest and the smallest nonzero magnitude over all of
+        // K, as bf16 bit patterns without the sign (ordered like the values).
+        // Packed 16-bit max/min over both halves of each dword; the minimum
+        // runs over magnitude - 1, so a zero wraps to 0xffff and is ignored.
+        u16x2 mx[XP], mn[XP];
+#pragma unroll
+        for (int i = 0; i < XP; ++i) mx[i] = u16x2{0, 0}, mn[i] = u16x2{0xffff, 0xffff};
+        for (int s = 0; s < steps; ++s) {
+#pragma unroll
+            for (int i = 0; i < XP; ++i) {
+                const int p = tid + NT * i, r = p >> 3, q = p & 7;
+                const int64_t gm = m0 + r, c0 = (int64_t)s * BK + 8 * q;
+                if (gm < m && c0 < k) {
+                    const u32x4 v = *(const u32x4*)(x + gm * k + c0);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const u16x2 mag = __builtin_bit_cast(u16x2, v[j] & 0x7fff7fffu);
+                        mx[i] = __builtin_elementwise_max(mx[i], mag);
+                        mn[i] = __builtin_elementwise_min(mn[i], mag - u16x2{1, 1});
+                    }
+                }
+            }
+        }
+        bool bad = false;
+#pragma unroll
+        for (int i = 0; i < XP; ++i) {
+            uint32_t hi = mx[i][0] > mx[i][1] ? mx[i][0] : mx[i][1];
+            uint32_t lo = mn[i][0] < mn[i][1] ? mn[i][0] : mn[i][1];
+#pragma unroll
+            for (int off = 1; off < 8; off <<= 1) {
+                const uint32_t h2 = __shfl_xor(hi, off, 64), l2 = __shfl_xor(lo, off, 64);
+                hi = h2 > hi ? h2 : hi;
+                lo = l2 < lo ? l2 : lo;
+            }
+            // exponent fields of the largest and smallest nonzero magnitudes
+            const int emax = (int)(hi >> 7), emin = (int)((lo + 1u) >> 7);
+            const bool any = hi != 0u;
+            const bool row_bad = any && (emax == 255 || emin == 0 || emax - emin > 31);
+            const int e = any ? emax - 127 - 14 : 0;
+            const int p = tid + NT * i;
+            if ((p & 7) == 0) xe_lds[p >> 3] = e;
+            bad |= row_bad;
+        }
+        if (bad) exact_flag = 1;
+        __syncthreads();
+    }
+    bool wbig = false;  // a decoded weight could overflow fp16
+
     // registers holding the fetched-but-not-stashed step
     struct Regs {
         u32x4 xr[XP];
@@ -399,7 +509,8 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const uint8_t* __restrict
     // is one scheduling region in which loads, decoding and MFMAs can
     // interleave.
     constexpr bool FULL = 2 * BN == NT || QM;
-    auto fetch = [&](int s, Regs& R) {
+    auto fetch = [&](int sr, Regs& R) {
+        const int s = sb + sr;  // step of the whole product
 #pragma unroll
         for (int i = 0; i < XP; ++i) {
             const int p = tid + NT * i, r = p >> 3, q = p & 7;
@@ -432,19 +543,31 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const uint8_t* __restrict
     };
     // write the fetched step into stage st: activations as they are, weights
     // decoded to the 16-bit operand type
-    auto stash = [&](int s, int st, const Regs& R) {
+    auto stash = [&](int sr, int st, const Regs& R) {
+        const int s = sb + sr;  // step of the whole product
         uint16_t* As = lds + st * (ASZ + BSZ);
         uint16_t* Bs = As + ASZ;
 #pragma unroll
         for (int i = 0; i < XP; ++i) {
             const int p = tid + NT * i, r = p >> 3, q = p & 7;
-            *(u32x4*)&As[r * LDS_STRIDE + 8 * q] = R.xr[i];
+            u32x4 v = R.xr[i];
+            if constexpr (XM == XM_BF16) {
+                // bf16 -> fp32 is a shift; the power-of-two scale (ldexp: the
+                // factor itself may lie outside fp32) and the conversion to
+                // fp16 are exact inside the row's window
+                const int ne = -xe_lds[r];
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    v[j] = pack_h(__builtin_ldexpf(__builtin_bit_cast(float, v[j] << 16), ne),
+                                  __builtin_ldexpf(__builtin_bit_cast(float, v[j] & 0xffff0000u), ne));
+            }
+            *(u32x4*)&As[r * LDS_STRIDE + 8 * q] = v;
         }
         if constexpr (QM) {
             // rows past n are left as decoded (see below)
             uint32_t lo[4], hi[4];
             int cl, ch;
-            WT::template decode_q<XDT>(R.raw, s, wh, lo, hi, cl, ch);
+            WT::decode_q(R.raw, s, wh, lo, hi, cl, ch, wbig);
             if (C == Q8_0 && (int64_t)(2 * s + (wh >> 1)) * 32 >= k) {
                 // a quarter past the row end (odd block count) would reach stored outputs
 #pragma unroll
@@ -461,14 +584,14 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const uint8_t* __restrict
             // would reach stored outputs)
             const bool live = (C != Q8_0) || (wr_valid && (int64_t)(2 * s + wh) * 32 < k);
             if (FULL) {
-                WT::template decode<XDT>(R.raw, s, wh, lo, hi, cl, ch);
+                WT::decode(R.raw, s, wh, lo, hi, cl, ch, wbig);
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     lo[i] = live ? lo[i] : 0u;
                     hi[i] = live ? hi[i] : 0u;
                 }
             } else if (live) {
-                WT::template decode<XDT>(R.raw, s, wh, lo, hi, cl, ch);
+                WT::decode(R.raw, s, wh, lo, hi, cl, ch, wbig);
             } else {
 #pragma unroll
                 for (int i = 0; i < 8; ++i) lo[i] = hi[i] = 0u;
@@ -515,7 +638,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const uint8_t* __restrict
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
-                for (int j = 0; j < FN; ++j) acc[i][j] = Op16<XDT>::mma(af[i], bf[j], acc[i][j]);
+                for (int j = 0; j < FN; ++j) acc[i][j] = mma_h(af[i], bf[j], acc[i][j]);
             // (on the last step the stash fills the idle stage with data
             // that is never read)
             if (ks == kStashKs && (FULL || s + 1 < steps)) stash(s + 1, st ^ 1, R);
@@ -549,6 +672,17 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const uint8_t* __restrict
         for (int s = 0; s < steps; ++s) step(s, ra);
     }
 
+    // a weight that could overflow fp16, or an activation row outside the
+    // window: the whole tile is recomputed exactly
+    if (wbig) exact_flag = 1;
+    __syncthreads();
+    if (exact_flag) {
+        const int64_t c0 = (int64_t)sb * BK, c1 = c0 + (int64_t)steps * BK < k ? c0 + (int64_t)steps * BK : k;
+        gemm_tile_exact<C, BM, BN, NT>(a, row_bytes, m0, n0, c0, c1, tid);
+        return;
+    }
+    float* part = SPLIT ? a.part + (int64_t)blockIdx.z * m * n : nullptr;
+
     // epilogue: lane holds column l%32 and rows 8*(v/4) + 4*(l/32) + v%4
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -558,23 +692,102 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const uint8_t* __restrict
             if (col >= n) continue;
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const int64_t row = m0 + wm * TM + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                const int lr = wm * TM + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                const int64_t row = m0 + lr;
                 if (row < m) {
-                    const float o = acc[i][j][v];
-                    if (y_dt == F32) store_out<F32>(y, row * n + col, o);
-                    else if (y_dt == F16) store_out<F16>(y, row * n + col, o);
-                    else store_out<BF16>(y, row * n + col, o);
+                    float o = acc[i][j][v];
+                    if constexpr (ROWEXP) o = __builtin_ldexpf(o, xe_lds[lr]);
+                    if (SPLIT) part[row * n + col] = o;
+                    else if (a.y_dt == F32) store_out<F32>(a.y, row * n + col, o);
+                    else if (a.y_dt == F16) store_out<F16>(a.y, row * n + col, o);
+                    else store_out<BF16>(a.y, row * n + col, o);
                 }
             }
         }
 }
 
-template <int C, int XDT, int BM, int BN, int NW>
-static void launch_tile(const void* w, int64_t n, int64_t k, const void* x, int64_t m, void* y,
-                        int y_dt, hipStream_t s) {
-    const dim3 grid((unsigned)((n + BN - 1) / BN), (unsigned)((m + BM - 1) / BM)), block(64 * NW);
-    hipLaunchKernelGGL((gemm_kernel<C, XDT, BM, BN, NW>), grid, block, 0, s, (const uint8_t*)w, n,
-                       k, (const uint16_t*)x, m, y, y_dt);
+// y = sum over the K splits, in split order, of the fp32 partial sums
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part,
+                                                            int splits, int64_t mn,
+                                                            void* __restrict__ y, int y_dt) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < mn; i += (int64_t)gridDim.x * 256) {
+        float acc = part[i];
+        for (int z = 1; z < splits; ++z) acc += part[(int64_t)z * mn + i];
+        if (y_dt == F32) store_out<F32>(y, i, acc);
+        else if (y_dt == F16) store_out<F16>(y, i, acc);
+        else store_out<BF16>(y, i, acc);
+    }
+}
+
+// bf16 activation rows -> fp16 rows scaled by 2^-e, one workgroup per row:
+// e puts the row's largest magnitude in [2^14, 2^15), which keeps every
+// element whose magnitude is within 2^31 of it exact.  A row with a larger
+// range, bf16 subnormals, Inf or NaN gets e = kBadRow (and zeros): the GEMM
+// tiles holding it take the exact path.
+__global__ __launch_bounds__(256) void x16_kernel(const uint16_t* __restrict__ x, int64_t k,
+                                                  uint16_t* __restrict__ x16,
+                                                  int32_t* __restrict__ xexp) {
+    __shared__ uint32_t red_hi[4], red_lo[4];
+    const int64_t row = blockIdx.x;
+    const uint16_t* xr = x + row * k;
+    uint16_t* outr = x16 + row * k;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    uint32_t hi = 0u, lo = 0xffffu;
+    // k is a multiple of 32: whole 16-byte pieces of 8 values
+    for (int64_t c = 8 * (int64_t)tid; c < k; c += 8 * 256) {
+        const u32x4 v = *(const u32x4*)(xr + c);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const uint32_t mag = (v[j] >> (16 * h)) & 0x7fffu;
+                hi = mag > hi ? mag : hi;
+                const uint32_t m1 = (mag - 1u) & 0xffffu;  // a zero wraps to 0xffff
+                lo = m1 < lo ? m1 : lo;
+            }
+        }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const uint32_t h2 = __shfl_xor(hi, off, 64), l2 = __shfl_xor(lo, off, 64);
+        hi = h2 > hi ? h2 : hi;
+        lo = l2 < lo ? l2 : lo;
+    }
+    if (lane == 0) red_hi[wave] = hi, red_lo[wave] = lo;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        hi = red_hi[i] > hi ? red_hi[i] : hi;
+        lo = red_lo[i] < lo ? red_lo[i] : lo;
+    }
+    const int emax = (int)(hi >> 7), emin = (int)((lo + 1u) >> 7);
+    const bool any = hi != 0u;
+    const bool bad = any && (emax == 255 || emin == 0 || emax - emin > 31);
+    const int e = any ? emax - 127 - 14 : 0;
+    if (tid == 0) xexp[row] = bad ? kBadRow : e;
+    for (int64_t c = 8 * (int64_t)tid; c < k; c += 8 * 256) {
+        u32x4 v = *(const u32x4*)(xr + c);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            v[j] = bad ? 0u
+                       : pack_h(__builtin_ldexpf(__builtin_bit_cast(float, v[j] << 16), -e),
+                                __builtin_ldexpf(__builtin_bit_cast(float, v[j] & 0xffff0000u), -e));
+        *(u32x4*)(outr + c) = v;
+    }
+}
+
+template <int C, int XM, int BM, int BN, int NW, bool SPLIT = true>
+static void launch_tile(const GemmArgs& a, int splits, hipStream_t s) {
+    const dim3 grid((unsigned)((a.n + BN - 1) / BN), (unsigned)((a.m + BM - 1) / BM),
+                    (unsigned)splits),
+        block(64 * NW);
+    if constexpr (SPLIT) {
+        if (splits > 1) {
+            hipLaunchKernelGGL((gemm_kernel<C, XM, BM, BN, NW, true>), grid, block, 0, s, a);
+            return;
+        }
+    }
+    hipLaunchKernelGGL((gemm_kernel<C, XM, BM, BN, NW, false>), grid, block, 0, s, a);
 }
 
 // Tile choice (eight waves, two per SIMD, measured on the prefill shapes):
@@ -584,36 +797,117 @@ static void launch_tile(const void* w, int64_t n, int64_t k, const void* x, int6
 // workgroup per CU and 128 x 128 below that.  Larger tiles reuse each
 // decoded weight over more rows and each activation over more columns;
 // smaller ones keep the CUs busy when there are few tiles.
-template <int C, int XDT>
-static void launch_c(const void* w, int64_t n, int64_t k, const void* x, int64_t m, void* y,
-                     int y_dt, hipStream_t s) {
+GemmPlan gemm_plan(int codec, int64_t n, int64_t k, int64_t m, bool may_split) {
     auto tiles = [&](int64_t bm, int64_t bn) { return ((n + bn - 1) / bn) * ((m + bm - 1) / bm); };
-    if (C == TQ1) {
+    GemmPlan p{};
+    p.splits = 1;
+    if (codec == TQ1) {
         // TQ1 weights cost the most to decode, and a tile decodes its weights
         // once for BM activation rows: the largest tile while it still gives
         // half a workgroup per compute unit
-        if (tiles(256, 256) >= 128) launch_tile<C, XDT, 256, 256, 8>(w, n, k, x, m, y, y_dt, s);
-        else launch_tile<C, XDT, 128, 128, 8>(w, n, k, x, m, y, y_dt, s);
-        return;
+        if (tiles(256, 256) >= 128) p.bm = 256, p.bn = 256;
+        else p.bm = 128, p.bn = 128;
+    } else if (tiles(256, 256) >= 384) p.bm = 256, p.bn = 256;
+    else if (tiles(256, 128) >= 192) p.bm = 256, p.bn = 128;
+    else if (tiles(128, 128) >= 192) p.bm = 128, p.bn = 128;
+    else p.bm = 64, p.bn = 128;
+    p.tiles = tiles(p.bm, p.bn);
+    const int64_t steps = (k + BK - 1) / BK;
+    if (may_split && p.tiles < 256) {
+        // too few tiles to fill the CUs: split K into pieces of whole
+        // super-blocks (4 steps) of at least 16 steps each, until the grid
+        // holds about two workgroups per CU
+        int64_t sp = (512 + p.tiles - 1) / p.tiles;
+        const int64_t cap = steps / 16;
+        if (sp > cap) sp = cap;
+        if (sp > 1) {
+            int64_t per = (steps + sp - 1) / sp;
+            per = (per + 3) / 4 * 4;
+            p.split_steps = (int)per;
+            p.splits = (int)((steps + per - 1) / per);
+        }
     }
-    if (tiles(256, 256) >= 384) {
+    if (p.splits == 1) p.split_steps = (int)steps;
+    return p;
+}
+
+template <int C, int XM>
+static void launch_c(const GemmArgs& a, const GemmPlan& p, hipStream_t s) {
+    constexpr bool SP = XM != XM_BF16;  // (no workspace, so never split)
+    if (p.bm == 256 && p.bn == 256) {
         // Q8_0 runs its 256 x 256 tiles with sixteen waves: half of them
         // decode, and the spare ones hide latency (10 % faster; Q4_K would
-        // spill registers)
-        if (C == Q8_0) launch_tile<C, XDT, 256, 256, 16>(w, n, k, x, m, y, y_dt, s);
-        else launch_tile<C, XDT, 256, 256, 8>(w, n, k, x, m, y, y_dt, s);
-    } else if (tiles(256, 128) >= 192) launch_tile<C, XDT, 256, 128, 8>(w, n, k, x, m, y, y_dt, s);
-    else if (tiles(128, 128) >= 192) launch_tile<C, XDT, 128, 128, 8>(w, n, k, x, m, y, y_dt, s);
-    else launch_tile<C, XDT, 64, 128, 8>(w, n, k, x, m, y, y_dt, s);
+        // spill registers); only for grids of 384 tiles or more, which are
+        // never split
+        if constexpr (C == Q8_0) launch_tile<C, XM, 256, 256, 16, false>(a, 1, s);
+        else launch_tile<C, XM, 256, 256, 8, SP>(a, p.splits, s);
+    } else if (p.bm == 256) launch_tile<C, XM, 256, 128, 8, SP>(a, p.splits, s);
+    else if (p.bm == 128) launch_tile<C, XM, 128, 128, 8, SP>(a, p.splits, s);
+    else launch_tile<C, XM, 64, 128, 8, SP>(a, p.splits, s);
+}
+
+template <int XM>
+static void launch_xm(int codec, const GemmArgs& a, const GemmPlan& p, hipStream_t s) {
+    switch (codec) {
+    case Q4_K: launch_c<Q4_K, XM>(a, p, s); break;
+    case Q8_0: launch_c<Q8_0, XM>(a, p, s); break;
+    default: launch_c<TQ1, XM>(a, p, s); break;
+    }
+}
+
+GemmWorkspace gemm_workspace(int codec, int64_t n, int64_t k, int64_t m, int x_dt) {
+    const GemmPlan p = gemm_plan(codec, n, k, m, true);
+    GemmWorkspace L{};
+    auto up = [](int64_t b) { return (b + 255) / 256 * 256; };
+    int64_t off = 0;
+    if (x_dt == BF16) {
+        L.xexp_off = off;
+        off += up(m * 4);
+        L.x16_off = off;
+        off += up(m * k * 2);
+    }
+    L.part_off = off;
+    if (p.splits > 1) off += up((int64_t)p.splits * m * n * 4);
+    L.bytes = off;
+    return L;
 }
 
 hipError_t launch_gemm(int codec, int x_dt, const void* w, int64_t n, int64_t k, const void* x,
-                       int64_t m, void* y, int y_dt, hipStream_t s) {
-    const bool bf = x_dt == BF16;
-    switch (codec) {
-    case Q4_K: bf ? launch_c<Q4_K, BF16>(w, n, k, x, m, y, y_dt, s) : launch_c<Q4_K, F16>(w, n, k, x, m, y, y_dt, s); break;
-    case Q8_0: bf ? launch_c<Q8_0, BF16>(w, n, k, x, m, y, y_dt, s) : launch_c<Q8_0, F16>(w, n, k, x, m, y, y_dt, s); break;
-    default: bf ? launch_c<TQ1, BF16>(w, n, k, x, m, y, y_dt, s) : launch_c<TQ1, F16>(w, n, k, x, m, y, y_dt, s); break;
+                       int64_t m, void* y, int y_dt, void* ws, hipStream_t s) {
+    GemmArgs a{};
+    a.w = (const uint8_t*)w;
+    a.n = n, a.k = k, a.m = m;
+    a.x = (const uint16_t*)x;
+    a.x_src = (const uint16_t*)x;
+    a.x_src_dt = x_dt;
+    a.y = y;
+    a.y_dt = y_dt;
+    const GemmPlan p = gemm_plan(codec, n, k, m, ws != nullptr);
+    a.split_steps = p.split_steps;
+    if (!ws) {
+        // no workspace: bf16 rows are scaled inside each workgroup
+        if (x_dt == BF16) launch_xm<XM_BF16>(codec, a, p, s);
+        else launch_xm<XM_F16>(codec, a, p, s);
+        return hipGetLastError();
+    }
+    const GemmWorkspace L = gemm_workspace(codec, n, k, m, x_dt);
+    char* base = (char*)ws;
+    if (x_dt == BF16) {
+        int32_t* xexp = (int32_t*)(base + L.xexp_off);
+        uint16_t* x16 = (uint16_t*)(base + L.x16_off);
+        hipLaunchKernelGGL(x16_kernel, dim3((unsigned)m), dim3(256), 0, s, (const uint16_t*)x, k,
+                           x16, xexp);
+        a.x = x16;
+        a.xexp = xexp;
+    }
+    if (p.splits > 1) a.part = (float*)(base + L.part_off);
+    if (x_dt == BF16) launch_xm<XM_SCALED>(codec, a, p, s);
+    else launch_xm<XM_F16>(codec, a, p, s);
+    if (p.splits > 1) {
+        const int64_t mn = m * n;
+        const int64_t blocks = (mn + 255) / 256 < 4096 ? (mn + 255) / 256 : 4096;
+        hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                           (const float*)a.part, p.splits, mn, y, y_dt);
     }
     return hipGetLastError();
 }

@@ -120,6 +120,39 @@ __device__ __forceinline__ int tq1_trit(uint32_t code, int d) {
     return (int)r - 1;
 }
 
+// ---------------------------------------------------------------- exact scalar decode
+// Weight c of a weight row, rounded once to fp32 (Q4_K: fused multiply-add of
+// the exact d*sc*q and dmin*m; Q8_0 and TQ1: exact).  Slow (reads the block
+// header per weight): for the rare exact fallback paths only.
+template <int C> __device__ __forceinline__ float weight_exact(const uint8_t* row, int64_t c);
+template <> __device__ __forceinline__ float weight_exact<Q4_K>(const uint8_t* row, int64_t c) {
+    const uint8_t* blk = row + (c >> 8) * 144;
+    const int w = (int)(c & 255), ch = w >> 6, hi = (w >> 5) & 1;
+    u32x4 h;
+    const uint16_t* p16 = (const uint16_t*)blk;
+    h.x = p16[0] | ((uint32_t)p16[1] << 16);
+    h.y = p16[2] | ((uint32_t)p16[3] << 16);
+    h.z = p16[4] | ((uint32_t)p16[5] << 16);
+    h.w = p16[6] | ((uint32_t)p16[7] << 16);
+    int sc, m;
+    q4k_scale_min(h, 2 * ch + hi, sc, m);
+    const uint32_t q = (blk[16 + 32 * ch + (w & 31)] >> (4 * hi)) & 15u;
+    return __builtin_fmaf(q4k_d(h) * (float)sc, (float)q, -(q4k_dmin(h) * (float)m));
+}
+template <> __device__ __forceinline__ float weight_exact<Q8_0>(const uint8_t* row, int64_t c) {
+    const uint8_t* blk = row + (c >> 5) * 34;
+    const uint32_t d = blk[0] | ((uint32_t)blk[1] << 8);
+    return half_bits_to_float(d) * (float)(int8_t)blk[2 + (c & 31)];
+}
+template <> __device__ __forceinline__ float weight_exact<TQ1>(const uint8_t* row, int64_t c) {
+    const uint8_t* blk = row + (c >> 7) * 28;
+    const int col = (int)(c & 127);
+    const int slot = col < 125 ? col / 5 : 25;
+    const int digit = col < 125 ? col - 5 * slot : col - 125;
+    const uint32_t s = blk[26] | ((uint32_t)blk[27] << 8);
+    return (float)tq1_trit(blk[slot], digit) * half_bits_to_float(s);
+}
+
 // ---------------------------------------------------------------- wave helpers
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

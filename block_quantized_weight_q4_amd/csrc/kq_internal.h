@@ -87,8 +87,33 @@ hipError_t launch_row_exp(const float* x, int64_t rows, int64_t k, int32_t* e, h
 bool tq1_mv_fits(int64_t k);
 hipError_t launch_tq1_mv(const uint8_t* w, int64_t n, int64_t k, const uint16_t* x, void* y,
                          int y_dt, hipStream_t s);
+// Prefill GEMM (gemm.hip).
+struct GemmArgs {
+    const uint8_t* w;
+    int64_t n, k, m;
+    const uint16_t* x;      // activations the matrix cores read (fp16 or bf16)
+    const uint16_t* x_src;  // the caller's activations (exact path)
+    int x_src_dt;           // F16 or BF16
+    const int32_t* xexp;    // pre-scaled fp16 rows: exponent per row
+    void* y;
+    int y_dt;
+    float* part;            // split K: fp32 partial sums [splits][m][n], else null
+    int split_steps;        // K steps (of 64) per split
+};
+struct GemmPlan {
+    int bm, bn, splits, split_steps;
+    int64_t tiles;
+};
+// Caller-owned scratch of kq_qmm_ws (byte offsets, 256-aligned).
+struct GemmWorkspace {
+    int64_t xexp_off, x16_off, part_off, bytes;
+};
+GemmPlan gemm_plan(int codec, int64_t n, int64_t k, int64_t m, bool may_split);
+GemmWorkspace gemm_workspace(int codec, int64_t n, int64_t k, int64_t m, int x_dt);
+// ws null: no workspace (bf16 rows are scaled inside each workgroup, no
+// split); else the layout of gemm_workspace.
 hipError_t launch_gemm(int codec, int x_dt, const void* w, int64_t n, int64_t k, const void* x,
-                       int64_t m, void* y, int y_dt, hipStream_t s);
+                       int64_t m, void* y, int y_dt, void* ws, hipStream_t s);
 // Builds the schedule; with poison_y, also writes NaN to the poisoned rows
 // of poison_y ([rows, poison_n] of poison_dt).
 // Rows of poison_y are NaN-ed by the routing rule: below 32 tokens those with

@@ -19,7 +19,8 @@ from ._build import LIB
 
 __all__ = [
     "KQError", "TYPES", "lib", "kq_status_string", "kq_last_error", "kq_qk", "kq_block_bytes",
-    "kq_row_bytes", "kq_dequantize", "kq_qmv", "kq_qmm", "kq_moe_workspace_bytes", "kq_moe_route",
+    "kq_row_bytes", "kq_dequantize", "kq_qmv", "kq_qmm", "kq_qmm_workspace_bytes", "kq_qmm_ws",
+    "kq_moe_workspace_bytes", "kq_moe_route",
     "kq_qmm_id", "kq_moe_glu", "moe_schedule", "SYMBOLS", "LAYOUT_SHARED", "LAYOUT_SLOTTED", "REUSE_SCHEDULE",
     "ACT_SILU", "ACT_GELU_TANH", "MOE_TILE_ROWS",
 ]
@@ -35,8 +36,8 @@ MOE_TILE_ROWS = 32
 # Every function include/kq.h declares.
 SYMBOLS = (
     "kq_status_string", "kq_last_error", "kq_qk", "kq_block_bytes", "kq_row_bytes",
-    "kq_dequantize", "kq_qmv", "kq_qmm", "kq_moe_workspace_bytes", "kq_moe_route", "kq_qmm_id",
-    "kq_moe_glu",
+    "kq_dequantize", "kq_qmv", "kq_qmm", "kq_qmm_workspace_bytes", "kq_qmm_ws",
+    "kq_moe_workspace_bytes", "kq_moe_route", "kq_qmm_id", "kq_moe_glu",
 )
 
 
@@ -76,6 +77,10 @@ def lib():
         f = getattr(L, name)
         f.restype = i32
         f.argtypes = [i32, P, i64, i64, P, i32, i64, P, i32, P]
+    L.kq_qmm_workspace_bytes.restype = C.c_size_t
+    L.kq_qmm_workspace_bytes.argtypes = [i32, i64, i64, i64, i32]
+    L.kq_qmm_ws.restype = i32
+    L.kq_qmm_ws.argtypes = [i32, P, i64, i64, P, i32, i64, P, i32, P, C.c_size_t, P]
     L.kq_moe_workspace_bytes.restype = C.c_size_t
     L.kq_moe_workspace_bytes.argtypes = [i64, i64, i64, i64]
     L.kq_moe_route.restype = i32
@@ -181,6 +186,20 @@ def kq_qmm(kind: str, w, n: int, k: int, x, m: int, y):
              ("y", y, m * n * y.element_size()))
     _check(lib().kq_qmm(TYPES[kind], _ptr(w), n, k, _ptr(x), _dt(x), m, _ptr(y), _dt(y),
                         _stream(w, x, y)))
+    return y
+
+
+def kq_qmm_workspace_bytes(kind: str, n: int, k: int, m: int, x_dtype) -> int:
+    """Scratch bytes kq_qmm_ws needs; x_dtype is a torch dtype."""
+    return int(lib().kq_qmm_workspace_bytes(TYPES[kind], n, k, m, _DT[x_dtype]))
+
+
+def kq_qmm_ws(kind: str, w, n: int, k: int, x, m: int, y, workspace):
+    _tensors(("w", w, _rows_bytes(kind, n, k)), ("x", x, m * k * x.element_size()),
+             ("y", y, m * n * y.element_size()), ("workspace", workspace, None))
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().kq_qmm_ws(TYPES[kind], _ptr(w), n, k, _ptr(x), _dt(x), m, _ptr(y), _dt(y),
+                           _ptr(workspace), nbytes, _stream(w, x, y)))
     return y
 
 

@@ -136,6 +136,37 @@ kq_status kq_qmm(kq_type t, const void* w, int64_t n, int64_t k, const void* x, 
                  int64_t m, void* y, kq_dtype y_dt, void* stream);
 
 /*
+ * kq_qmm_workspace_bytes / kq_qmm_ws -- kq_qmm with caller-owned scratch.
+ * mlx-kquant "bindings.cpp", quantized_matmul (the same product); Ternary
+ * Bonsai "ternel_packed_model.py", tq1_matmul (k_split: fp32 partial sums
+ * over pieces of K, added in a second pass, for products whose output alone
+ * does not fill the GPU); mlx-native "quantized_matmul_id_ggml.rs",
+ * IdMmScratch (reusable caller-owned scratch, no allocation per call).
+ *
+ * y = x @ dequant(w)^T exactly as kq_qmm computes it (same arguments and
+ * layouts, same error bound).  With the workspace:
+ *   - bf16 activations are converted once per call to fp16 rows scaled by a
+ *     power of two (without it, each output tile column converts its own
+ *     copy of the activation rows);
+ *   - a product with fewer output tiles than the GPU has compute units splits
+ *     K across workgroups; the fp32 partial sums are added in a fixed order,
+ *     so results are deterministic.
+ *
+ * kq_qmm_workspace_bytes returns the bytes kq_qmm_ws needs for these sizes
+ * (0: none needed -- m <= 16 or fp32 activations -- or invalid arguments).
+ * workspace: device memory, 256-byte aligned, at least that many bytes,
+ * overlapping neither the inputs nor y; its contents on entry are ignored
+ * and on return unspecified.  Calls that share a workspace must not overlap
+ * in time (use one stream, or one workspace per stream).
+ * Errors: as kq_qmm; a missing, misaligned or too small workspace ->
+ * KQ_ERR_WORKSPACE; a workspace overlapping w, x or y -> KQ_ERR_INVALID_ARG.
+ */
+size_t kq_qmm_workspace_bytes(kq_type t, int64_t n, int64_t k, int64_t m, kq_dtype x_dt);
+kq_status kq_qmm_ws(kq_type t, const void* w, int64_t n, int64_t k, const void* x, kq_dtype x_dt,
+                    int64_t m, void* y, kq_dtype y_dt, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/*
  * kq_moe_workspace_bytes -- size of the caller-owned scratch that
  * kq_moe_route, kq_qmm_id and kq_moe_glu need for a routing of n_tokens x
  * top_k rows over n_experts experts, where n_out is the widest output row

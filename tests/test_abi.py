@@ -162,6 +162,32 @@ def test_qmm_row_bound(kq):
     assert rc == 1 and kq.kq_last_error() == "m exceeds 2^19 activation rows"
 
 
+def test_qmm_workspace_sizes_and_validation(kq):
+    """kq_qmm_workspace_bytes: none for decode shapes or fp32 activations, the
+    converted activation rows (m*k fp16 + m exponents) for bf16, fp32 partial
+    sums when K is split; kq_qmm_ws rejects a small or missing workspace
+    before launching (fake addresses are never dereferenced)."""
+    import torch
+
+    bf, f16, f32 = torch.bfloat16, torch.float16, torch.float32
+    assert kq.kq_qmm_workspace_bytes("q4_k", 4096, 4096, 16, bf) == 0
+    assert kq.kq_qmm_workspace_bytes("q4_k", 4096, 4096, 512, f32) == 0
+    assert kq.kq_qmm_workspace_bytes("q4_k", 4096, 100, 512, bf) == 0   # k % QK
+    big = kq.kq_qmm_workspace_bytes("q4_k", 14336, 4096, 2048, bf)
+    assert big >= 2048 * 4096 * 2 + 2048 * 4
+    assert kq.kq_qmm_workspace_bytes("q4_k", 14336, 4096, 2048, f16) == 0  # many tiles: no split
+    few = kq.kq_qmm_workspace_bytes("q4_k", 512, 4096, 200, f16)         # few tiles: split K
+    assert few >= 2 * 200 * 512 * 4
+    L = kq.lib()
+    P = C.c_void_p
+    base = 1 << 40
+    args = (0, P(base), 14336, 4096, P(base + (1 << 36)), 2, 2048, P(base + (2 << 36)), 2)
+    assert L.kq_qmm_ws(*args, P(base + (3 << 36)), big - 256, None) == 3
+    assert L.kq_qmm_ws(*args, None, 0, None) == 3
+    assert L.kq_qmm_ws(*args, P(base + (3 << 36) + 16), big, None) == 3  # misaligned
+    assert L.kq_qmm_ws(*args, P(base + (1 << 36)), big, None) == 1       # overlaps x
+
+
 def test_binding_checks_tensors_before_calling(kq):
     """The binding refuses strided, short or mixed-device tensors before any C
     call (host tensors here: nothing reaches a kernel)."""

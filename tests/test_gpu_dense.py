@@ -108,7 +108,12 @@ def test_dequant_full_size_bit_exact(kq, kind, shape):
 def _run(kq, fn, kind, w, n, k, x, x_dt, m, y_dt):
     wd, xd = to_dev(w), to_dev(x, x_dt)
     y = empty((m, n), y_dt)
-    getattr(kq, fn)(kind, wd, n, k, xd, m, y)
+    if fn == "kq_qmm_ws":
+        nb = kq.kq_qmm_workspace_bytes(kind, n, k, m, xd.dtype)
+        ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=xd.device)
+        kq.kq_qmm_ws(kind, wd, n, k, xd, m, y, ws)
+    else:
+        getattr(kq, fn)(kind, wd, n, k, xd, m, y)
     torch.cuda.synchronize()
     return to_f64(y)
 
@@ -267,15 +272,37 @@ def test_qmv_c2_full_sampled(kq, which, b):
 @pytest.mark.parametrize("which", [("q4_k", 4096), ("q4_k", 14336), ("q8_0", 4096),
                                    ("q8_0", 14336)])
 @pytest.mark.parametrize("m", [512, 2048])
-def test_qmm_c3_full_sampled(kq, which, m):
+@pytest.mark.parametrize("fn", ["kq_qmm", "kq_qmm_ws"])
+def test_qmm_c3_full_sampled(kq, which, m, fn):
     cases, x = workloads.c3(which)
-    _say("qmm C3", which, m)
-    _sampled(kq, "kq_qmm", cases[0], x, "bf16", m, "bf16")
+    _say("qmm C3", which, m, fn)
+    _sampled(kq, fn, cases[0], x, "bf16", m, "bf16")
+
+
+@pytest.mark.parametrize("kind", ["q4_k", "q8_0", "tq1_g128"])
+@pytest.mark.parametrize("x_dt", ["f16", "bf16"])
+@pytest.mark.parametrize("m,n,k", [(300, 700, 2048), (200, 512, 4096), (33, 130, 1536)])
+def test_qmm_split_k(kq, kind, x_dt, m, n, k):
+    """Products with fewer output tiles than compute units: kq_qmm_ws splits
+    K (fp32 partial sums added in a fixed order); every output against the
+    oracle, and the result bit-identical from call to call."""
+    if kind == "q8_0":
+        k -= 32  # an odd block count: the last K step is half a step
+    rng = _rng(3300 + m + n)
+    w = synth.weight_blocks(kind, rng, n, k)
+    x = synth.activations(rng, (m, k), x_dt)
+    _say("qmm split k", kind, x_dt, m, n, k)
+    got = _run(kq, "kq_qmm_ws", kind, w, n, k, x, x_dt, m, "f32")
+    again = _run(kq, "kq_qmm_ws", kind, w, n, k, x, x_dt, m, "f32")
+    assert np.array_equal(got, again)
+    ref, s = oracle.qmm(kind, w, n, k, x, x_dt, m)
+    check_tol(got, ref, s, TAU[x_dt], f"split k {kind} {x_dt} {m}x{n}x{k}")
 
 
 @pytest.mark.parametrize("kind", ["q4_k", "q8_0"])
 @pytest.mark.parametrize("m,n", [(300, 8242), (600, 8242), (2100, 11015)])
-def test_qmm_large_tiles_ragged(kq, kind, m, n):
+@pytest.mark.parametrize("fn", ["kq_qmm", "kq_qmm_ws"])
+def test_qmm_large_tiles_ragged(kq, kind, m, n, fn):
     """Grids large enough for the 128x128, 256x128 and 256x256 tiles (in
     that order), ragged in M and N, every output against the oracle; Q8_0
     rows of an odd block count end in half a K step."""
@@ -283,33 +310,32 @@ def test_qmm_large_tiles_ragged(kq, kind, m, n):
     rng = _rng(3200 + m)
     w = synth.weight_blocks(kind, rng, n, k)
     x = synth.activations(rng, (m, k), "bf16")
-    _say("qmm large tiles", kind, m, n, k)
-    got = _run(kq, "kq_qmm", kind, w, n, k, x, "bf16", m, "f32")
+    _say("qmm large tiles", kind, m, n, k, fn)
+    got = _run(kq, fn, kind, w, n, k, x, "bf16", m, "f32")
     ref, s = oracle.qmm(kind, w, n, k, x, "bf16", m)
     check_tol(got, ref, s, TAU["bf16"], f"qmm {kind} {m}x{n}x{k}")
 
 
 @pytest.mark.parametrize("x_dt", ["f16", "bf16"])
-def test_qmm_tq1_large_tiles_ragged(kq, x_dt):
+@pytest.mark.parametrize("fn", ["kq_qmm", "kq_qmm_ws"])
+def test_qmm_tq1_large_tiles_ragged(kq, x_dt, fn):
     """TQ1 products with enough output tiles for the 256x256 tile, ragged in
-    both M and N, every output against the oracle (fp16 activations take the
-    packed digit decode, bf16 the per-digit one)."""
+    both M and N, every output against the oracle."""
     m, n, k = 300, 16400, 384
     rng = _rng(3100)
     w = synth.weight_blocks("tq1_g128", rng, n, k)
     x = synth.activations(rng, (m, k), x_dt)
-    _say("qmm tq1 large tiles", x_dt, m, n, k)
-    got = _run(kq, "kq_qmm", "tq1_g128", w, n, k, x, x_dt, m, "f32")
+    _say("qmm tq1 large tiles", x_dt, m, n, k, fn)
+    got = _run(kq, fn, "tq1_g128", w, n, k, x, x_dt, m, "f32")
     ref, s = oracle.qmm("tq1_g128", w, n, k, x, x_dt, m)
     check_tol(got, ref, s, TAU[x_dt], f"qmm tq1 {x_dt} {m}x{n}x{k}")
 
 
 @pytest.mark.parametrize("which", [0, 1])
-@pytest.mark.parametrize("m", [1, 512])
-def test_tq1_c5_full_sampled(kq, which, m):
+@pytest.mark.parametrize("m,fn", [(1, "kq_qmv"), (512, "kq_qmm"), (512, "kq_qmm_ws")])
+def test_tq1_c5_full_sampled(kq, which, m, fn):
     case = workloads.c5()[which]
-    fn = "kq_qmv" if m == 1 else "kq_qmm"
-    _say("tq1 C5", case["n"], case["k"], m)
+    _say("tq1 C5", case["n"], case["k"], m, fn)
     _sampled(kq, fn, case, case["x"], "f16", m, "f16")
 
 
