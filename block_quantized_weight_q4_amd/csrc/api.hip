@@ -3,6 +3,7 @@
 // (mlx-native "quantized_matmul_id_ggml.rs", validate_id_call and the pooled
 // pair variant: sizes, top_k range, K % QK, row-count limit, overlapping
 // ranges); nothing here allocates, frees or synchronizes.
+#include <mutex>
 #include <string>
 
 #include "../../include/kq.h"
@@ -220,6 +221,54 @@ kq_status kq_qmm_ws(kq_type t, const void* w, int64_t n, int64_t k, const void* 
             return fail(KQ_ERR_INVALID_ARG, "workspace overlaps an input or the output");
     }
     return launched(kq::launch_gemm(t, x_dt, w, n, k, x, m, y, y_dt, need > 0 ? workspace : nullptr, s));
+}
+
+// ---------------------------------------------------------------- kq_qmm_noalloc
+// The scratch of kq_qmm_noalloc: one fixed array per GPU, held until the
+// process ends.  Host code never uses the array's name as an address (on the
+// host it is only a stand-in for the symbol): the device address comes from
+// hipGetSymbolAddress, once per device with that device current, and is kept
+// per device.
+static constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+static constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+static kq_status scratch_address(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(KQ_ERR_DEVICE, std::string("hipGetDevice: ") + hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(KQ_ERR_DEVICE, "device index out of range");
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(KQ_ERR_DEVICE, std::string("hipGetSymbolAddress: ") + hipGetErrorString(e));
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return KQ_OK;
+}
+
+size_t kq_qmm_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
+
+kq_status kq_qmm_noalloc(kq_type t, const void* w, int64_t n, int64_t k, const void* x,
+                         kq_dtype x_dt, int64_t m, void* y, kq_dtype y_dt, void* stream) {
+    int64_t row_bytes;
+    kq_status st = check_product(t, w, n, k, x, x_dt, m, y, y_dt, row_bytes);
+    if (st) return st;
+    hipStream_t s = (hipStream_t)stream;
+    if (!qmm_uses_workspace(m, x_dt))
+        return dense_skinny(t, w, n, k, row_bytes, x, x_dt, m, y, y_dt, s);
+    const int64_t need = kq::gemm_workspace(t, n, k, m, x_dt).bytes;
+    if (need > (int64_t)kNoAllocScratchBytes)
+        return fail(KQ_ERR_WORKSPACE, "product needs more scratch than kq_qmm_noalloc holds "
+                                      "(kq_qmm_workspace_bytes() > kq_qmm_noalloc_max_bytes())");
+    void* ws = nullptr;
+    if (need > 0 && (st = scratch_address(&ws))) return st;
+    return launched(kq::launch_gemm(t, x_dt, w, n, k, x, m, y, y_dt, need > 0 ? ws : nullptr, s));
 }
 
 size_t kq_moe_workspace_bytes(int64_t n_experts, int64_t n_tokens, int64_t top_k, int64_t n_out) {

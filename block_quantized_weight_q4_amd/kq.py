@@ -20,7 +20,7 @@ from ._build import LIB
 __all__ = [
     "KQError", "TYPES", "lib", "kq_status_string", "kq_last_error", "kq_qk", "kq_block_bytes",
     "kq_row_bytes", "kq_dequantize", "kq_qmv", "kq_qmm", "kq_qmm_workspace_bytes", "kq_qmm_ws",
-    "kq_moe_workspace_bytes", "kq_moe_route",
+    "kq_qmm_noalloc_max_bytes", "kq_qmm_noalloc", "kq_moe_workspace_bytes", "kq_moe_route",
     "kq_qmm_id", "kq_moe_glu", "moe_schedule", "SYMBOLS", "LAYOUT_SHARED", "LAYOUT_SLOTTED", "REUSE_SCHEDULE",
     "ACT_SILU", "ACT_GELU_TANH", "MOE_TILE_ROWS",
 ]
@@ -37,7 +37,8 @@ MOE_TILE_ROWS = 32
 SYMBOLS = (
     "kq_status_string", "kq_last_error", "kq_qk", "kq_block_bytes", "kq_row_bytes",
     "kq_dequantize", "kq_qmv", "kq_qmm", "kq_qmm_workspace_bytes", "kq_qmm_ws",
-    "kq_moe_workspace_bytes", "kq_moe_route", "kq_qmm_id", "kq_moe_glu",
+    "kq_qmm_noalloc_max_bytes", "kq_qmm_noalloc", "kq_moe_workspace_bytes", "kq_moe_route",
+    "kq_qmm_id", "kq_moe_glu",
 )
 
 
@@ -81,6 +82,10 @@ def lib():
     L.kq_qmm_workspace_bytes.argtypes = [i32, i64, i64, i64, i32]
     L.kq_qmm_ws.restype = i32
     L.kq_qmm_ws.argtypes = [i32, P, i64, i64, P, i32, i64, P, i32, P, C.c_size_t, P]
+    L.kq_qmm_noalloc_max_bytes.restype = C.c_size_t
+    L.kq_qmm_noalloc_max_bytes.argtypes = []
+    L.kq_qmm_noalloc.restype = i32
+    L.kq_qmm_noalloc.argtypes = [i32, P, i64, i64, P, i32, i64, P, i32, P]
     L.kq_moe_workspace_bytes.restype = C.c_size_t
     L.kq_moe_workspace_bytes.argtypes = [i64, i64, i64, i64]
     L.kq_moe_route.restype = i32
@@ -200,6 +205,18 @@ def kq_qmm_ws(kind: str, w, n: int, k: int, x, m: int, y, workspace):
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().kq_qmm_ws(TYPES[kind], _ptr(w), n, k, _ptr(x), _dt(x), m, _ptr(y), _dt(y),
                            _ptr(workspace), nbytes, _stream(w, x, y)))
+    return y
+
+
+def kq_qmm_noalloc_max_bytes() -> int:
+    return int(lib().kq_qmm_noalloc_max_bytes())
+
+
+def kq_qmm_noalloc(kind: str, w, n: int, k: int, x, m: int, y):
+    _tensors(("w", w, _rows_bytes(kind, n, k)), ("x", x, m * k * x.element_size()),
+             ("y", y, m * n * y.element_size()))
+    _check(lib().kq_qmm_noalloc(TYPES[kind], _ptr(w), n, k, _ptr(x), _dt(x), m, _ptr(y), _dt(y),
+                                _stream(w, x, y)))
     return y
 
 

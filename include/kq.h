@@ -167,6 +167,24 @@ kq_status kq_qmm_ws(kq_type t, const void* w, int64_t n, int64_t k, const void* 
                     void* stream);
 
 /*
+ * kq_qmm_noalloc -- kq_qmm_ws for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments as kq_qmm, same result as kq_qmm_ws (the same
+ * kernels), with the scratch in a fixed array inside the library: one per
+ * GPU, kq_qmm_noalloc_max_bytes() = 64 MiB, held until the process ends.
+ * Nothing is allocated or freed by the call.
+ *
+ * Every call on one GPU shares that GPU's array: calls that overlap in time
+ * on one GPU (concurrent streams or threads) race and give undefined results.
+ * Serialize them (one stream), or use kq_qmm_ws with a workspace per stream.
+ * Errors: as kq_qmm; a product whose kq_qmm_workspace_bytes() exceeds
+ * kq_qmm_noalloc_max_bytes() -> KQ_ERR_WORKSPACE (nothing is launched).
+ */
+size_t kq_qmm_noalloc_max_bytes(void);
+kq_status kq_qmm_noalloc(kq_type t, const void* w, int64_t n, int64_t k, const void* x,
+                         kq_dtype x_dt, int64_t m, void* y, kq_dtype y_dt, void* stream);
+
+/*
  * kq_moe_workspace_bytes -- size of the caller-owned scratch that
  * kq_moe_route, kq_qmm_id and kq_moe_glu need for a routing of n_tokens x
  * top_k rows over n_experts experts, where n_out is the widest output row
