@@ -219,6 +219,18 @@ def main():
         stages.append(Stage("tq1_c5_b1", calls_v, bv, fv, note="TQ1 GEMV batch 1, fp16"))
         stages.append(Stage("tq1_c5_m512", calls_m, bm, fm, note="TQ1 qmm M=512, fp16 (kq_qmm_ws)"))
 
+    # Streaming-read ceiling: a plain device reduction (torch) over the same
+    # number of bytes as one C2 / C5 weight matrix, rotated over >= 1 GiB of
+    # copies like the GEMVs; reported beside the 8 TB/s figure
+    ceil_parts = []
+    if "qmv_c2" in wanted or "tq1_c5" in wanted:
+        for nbytes, tag in ((33030144, "33MB"), (19496960, "19.5MB")):
+            base = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+            bufs = copies(base, nbytes)
+            part = [(lambda bufs=bufs: torch.sum(nxt(bufs))) for _ in range(len(bufs))]
+            ceil_parts.append(Stage(f"hbm_read_ceiling_{tag}", part, len(part) * nbytes, 0,
+                                    note="torch.sum over rotated copies: a plain streaming read"))
+
     if "moe_c4" in wanted:
         c = workloads.c4()
         E, H, F, T, top_k = c["n_experts"], c["hidden"], c["ffn"], c["T"], c["top_k"]
@@ -270,7 +282,8 @@ def main():
     # ---------------------------------------------------------------- timing
     # Each stage's calls are captured once into a HIP graph and replayed, so
     # the kernels run back to back instead of waiting on Python launches.
-    timed = [s for s in stages if s.name not in ("qmv_c2",)] + c2_parts + c3_parts + extra_parts
+    timed = ([s for s in stages if s.name not in ("qmv_c2",)] + c2_parts + c3_parts + extra_parts
+             + ceil_parts)
     graphs = {}
     for s in timed:
         s.run()  # eager pass: lazy initialisation outside the capture
@@ -303,7 +316,9 @@ def main():
     rows = {}
     for s in timed:
         ms = float(np.median(s.ms))
-        r = {"ms": round(ms, 4), "calls": len(s.calls), "us_per_call": round(1000 * ms / len(s.calls), 3)}
+        r = {"ms": round(ms, 4), "calls": len(s.calls), "us_per_call": round(1000 * ms / len(s.calls), 3),
+             "us_per_call_min": round(1000 * min(s.ms) / len(s.calls), 3),
+             "us_per_call_max": round(1000 * max(s.ms) / len(s.calls), 3)}
         if s.bytes:
             r["GB/s"] = round(s.bytes / (ms * 1e-3) / 1e9, 1)
             r["frac_hbm"] = round(r["GB/s"] / HBM_PEAK_GBS, 4)
@@ -314,6 +329,12 @@ def main():
         if s.note:
             r["note"] = s.note
         rows[s.name] = r
+    ceil = {p.name: rows[p.name]["GB/s"] for p in ceil_parts}
+    for name, r in rows.items():
+        c = ceil.get("hbm_read_ceiling_33MB") if name.startswith("qmv_c2") else (
+            ceil.get("hbm_read_ceiling_19.5MB") if name == "tq1_c5_b1" else None)
+        if c and "GB/s" in r:
+            r["frac_read_ceiling"] = round(r["GB/s"] / c, 4)
     if c2_parts:
         ms = sum(float(np.median(p.ms)) for p in c2_parts)
         nbytes = sum(p.bytes for p in c2_parts)
@@ -322,6 +343,10 @@ def main():
                           "bytes_per_launch": round(nbytes / launches),
                           "us_per_launch": round(1000 * ms / launches, 3),
                           "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        if ceil.get("hbm_read_ceiling_33MB"):
+            rows["qmv_c2"]["read_ceiling_GB/s"] = ceil["hbm_read_ceiling_33MB"]
+            rows["qmv_c2"]["frac_read_ceiling"] = round(rows["qmv_c2"]["GB/s"] /
+                                                        ceil["hbm_read_ceiling_33MB"], 4)
     if c3_parts:
         ms = sum(float(np.median(p.ms)) for p in c3_parts)
         fl = sum(p.flops for p in c3_parts)
@@ -351,6 +376,7 @@ def main():
     }
     if not args.no_cpu_baseline and "qmv_c2" in wanted:
         result["cpu_baseline"] = cpu_baseline()
+        result["cpu_baseline_rows"] = cpu_baseline_rows()
     print(json.dumps(result))
 
 
@@ -385,12 +411,101 @@ def _traffic():
     return d.get("hbm_bytes_per_dispatch")
 
 
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
+
+
+def cpu_baseline_rows():
+    """The fp64 CPU oracle on a bounded sample of every other workload: whole
+    calls where they take a few seconds at most, else a contiguous slice of
+    the output rows (weight rows, or tokens for the MoE layer) timed and
+    scaled linearly to the whole call."""
+    import oracle
+    from synth import workloads
+
+    oracle.lib()
+    threads, cpu = oracle.num_threads(), _cpu_model()
+    out = {}
+
+    def timed(fn, budget=1.5):
+        if budget >= 1.0:
+            fn()  # untimed run (the slices of the largest calls are timed once, cold)
+        t0, n = time.perf_counter(), 0
+        while True:
+            fn()
+            n += 1
+            if time.perf_counter() - t0 >= budget:
+                return (time.perf_counter() - t0) / n
+
+    c = workloads.c1()
+    t = timed(lambda: oracle.qmm("q4_k", c["w"], 2048, 2048, c["x"], "f32", 1))
+    out["qmv_c1"] = {"us_per_call": round(t * 1e6, 1), "GB/s": round(c["w"].nbytes / t / 1e9, 3),
+                     "sample": "whole Q4_K 2048x2048 GEMV, fp32 x"}
+    t = timed(lambda: oracle.dequant_as("q4_k", c["w"], 2048, 2048, "f32"))
+    out["dequant"] = {"us_per_call": round(t * 1e6, 1),
+                      "GB/s": round((c["w"].nbytes + 2048 * 2048 * 4) / t / 1e9, 3),
+                      "sample": "whole Q4_K 2048x2048 -> fp32"}
+
+    cases, x = workloads.c3(("q4_k", 14336))
+    w, n, k, m = cases[0]["w"], 14336, 4096, 2048
+    ns = 717  # 5 % of the weight rows
+    t = timed(lambda: oracle.qmm("q4_k", w[:ns], ns, k, x[:m], "bf16", m), budget=0.1)
+    full = t * n / ns
+    out["qmm_c3_q4_k_14336x4096_m2048"] = {
+        "us_per_call": round(full * 1e6, 1), "TFLOP/s": round(2 * m * n * k / full / 1e12, 5),
+        "sample": f"first {ns} of {n} weight rows (5 %), M=2048, timed once and scaled x{n / ns:.1f}"}
+
+    c4 = workloads.c4()
+    E, H, F, top_k = c4["n_experts"], c4["hidden"], c4["ffn"], c4["top_k"]
+
+    def layer(t0, nt):
+        return oracle.moe_layer("q4_k", c4["gate"], c4["up"], c4["down"], E, H, F,
+                                c4["gate_stride"], c4["down_stride"], c4["x"][t0:t0 + nt], "f16",
+                                c4["ids"][t0:t0 + nt], nt, top_k, c4["scores"][t0:t0 + nt])
+
+    t = timed(lambda: layer(0, 1), budget=0.1)
+    out["moe_c4_decode"] = {"us_per_call": round(t * 1e6, 1), "tokens/s": round(1 / t, 2),
+                            "sample": "one token, whole layer (8 experts x 3 matrices)"}
+    nt = 13  # 5 % of the 256 tokens
+    t = timed(lambda: layer(0, nt), budget=0.1)
+    full = t * 256 / nt
+    out["moe_c4_prefill"] = {"us_per_call": round(full * 1e6, 1), "tokens/s": round(256 / full, 2),
+                             "sample": f"first {nt} of 256 tokens (5 %), timed once and scaled "
+                                       f"x{256 / nt:.1f}"}
+
+    c5 = workloads.c5()[0]
+    t = timed(lambda: oracle.qmm("tq1_g128", c5["w"], c5["n"], c5["k"], c5["x"][:1], "f16", 1))
+    out["tq1_c5_b1"] = {"us_per_call": round(t * 1e6, 1), "GB/s": round(c5["w"].nbytes / t / 1e9, 3),
+                        "sample": "whole TQ1 17408x5120 GEMV, fp16 x"}
+    ns = 871  # 5 % of 17408
+    rb = c5["w"].shape[1]
+    t = timed(lambda: oracle.qmm("tq1_g128", c5["w"][:ns], ns, c5["k"], c5["x"], "f16", 512),
+              budget=0.1)
+    full = t * c5["n"] / ns
+    out["tq1_c5_m512"] = {"us_per_call": round(full * 1e6, 1),
+                          "TFLOP/s": round(2 * 512 * c5["n"] * c5["k"] / full / 1e12, 5),
+                          "sample": f"first {ns} of {c5['n']} weight rows (5 %), M=512, scaled "
+                                    f"x{c5['n'] / ns:.1f} (row bytes {rb})"}
+    for r in out.values():
+        r["cores"] = threads
+        r["kind"] = "oracle"
+        r["cpu"] = cpu
+    return out
+
+
 def roofline(rows):
     r = rows.get("qmv_c2")
     if not r:
         return None
     return {"bound": "hbm", "achieved": r["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(r["GB/s"] / HBM_PEAK_GBS, 4), "traffic": _traffic(),
+            "read_ceiling": r.get("read_ceiling_GB/s"), "frac_read_ceiling": r.get("frac_read_ceiling"),
             "kernel": "kq_qmv Q4_K decode GEMV: mmv3_q4k_f16_kernel (batch 1), mmv3m_q4k_f16_kernel "
                       "(batch 4), mmv2_q4k_f16_kernel (batch 8)",
             "bytes_per_launch": r.get("bytes_per_launch"), "us_per_launch": r.get("us_per_launch")}
