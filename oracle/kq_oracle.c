@@ -578,6 +578,199 @@ int or_moe_layer(int type, const uint8_t* gate_w, const uint8_t* up_w, const uin
 }
 
 /* ------------------------------------------------------------------ */
+/* Encoders: float weights -> block bytes                              */
+/* ------------------------------------------------------------------ */
+/* [KQ] quantize encodes float weights [rows, k] (k a multiple of the block
+ * size) into the wire bytes of a codec, with an optional importance vector
+ * of length k that steers the K-quant encoder; [TQ1] "Bounds safety": code
+ * legality is established at conversion.  The pages fix the contract, not an
+ * encoder; the encoders below are the plain readings stated with each.  All
+ * arithmetic is binary32 (float variables, this file is compiled without
+ * contraction into fused multiply-adds), divisions and square-free products
+ * correctly rounded, rintf rounds to nearest even, and every sum runs in
+ * index order, so a faithful implementation elsewhere produces the same
+ * bytes.  Weights and importances must be finite (importances >= 0). */
+
+static float act_f32(const void* x, int dt, int64_t i) { return (float)act_value(x, dt, i); }
+
+/* binary32 -> fp16 bits, round to nearest even, with magnitudes past the
+ * fp16 range clamped to 65504 (scales are never infinite). */
+static uint16_t scale_to_half(float v) {
+    if (v > 65504.0f) v = 65504.0f;
+    return or_float_to_half_rne(v);
+}
+
+static float clampf(float v, float lo, float hi) { return v < lo ? lo : v > hi ? hi : v; }
+
+/* Q8_0: d = fp16(max|w| / 127); q = clamp(rint(w * (1/d)), -127, 127). */
+static void encode_q8_0(const float* w, uint8_t* blk) {
+    float amax = 0.0f;
+    for (int i = 0; i < 32; ++i) {
+        float a = fabsf(w[i]);
+        if (a > amax) amax = a;
+    }
+    uint16_t dh = scale_to_half(amax / 127.0f);
+    float d = (float)or_half_to_double(dh);
+    float inv = d > 0.0f ? 1.0f / d : 0.0f;
+    blk[0] = (uint8_t)(dh & 0xff);
+    blk[1] = (uint8_t)(dh >> 8);
+    for (int i = 0; i < 32; ++i) {
+        float q = clampf(rintf(w[i] * inv), -127.0f, 127.0f);
+        blk[2 + i] = (uint8_t)(int8_t)q;
+    }
+}
+
+/* TQ1_G128: s = fp16(max|w|) over the 128 weights (absmax, so a decoded block
+ * encodes back to its own bytes); trit t = clamp(rint(w * (1/s)), -1, 1),
+ * stored as the base-3 digit t + 1: column c < 125 is digit c mod 5 of code
+ * byte c / 5, columns 125..127 digits 0..2 of the tail byte (place values 1,
+ * 3, 9, 27, 81); the scale's fp16 bits follow. */
+static void encode_tq1(const float* w, uint8_t* blk) {
+    float amax = 0.0f;
+    for (int i = 0; i < 128; ++i) {
+        float a = fabsf(w[i]);
+        if (a > amax) amax = a;
+    }
+    uint16_t sh = scale_to_half(amax);
+    float sv = (float)or_half_to_double(sh);
+    float inv = sv > 0.0f ? 1.0f / sv : 0.0f;
+    for (int b = 0; b < 26; ++b) blk[b] = 0;
+    for (int c = 0; c < 128; ++c) {
+        int t = (int)clampf(rintf(w[c] * inv), -1.0f, 1.0f);
+        int slot = c < 125 ? c / 5 : 25;
+        int digit = c < 125 ? c - 5 * slot : c - 125;
+        int p = 1;
+        for (int i = 0; i < digit; ++i) p *= 3;
+        blk[slot] = (uint8_t)(blk[slot] + (t + 1) * p);
+    }
+    blk[26] = (uint8_t)(sh & 0xff);
+    blk[27] = (uint8_t)(sh >> 8);
+}
+
+/* Q4_K.  Per sub-block j of 32 weights: lo = min(0, min w), hi = max w,
+ * range scale r_j = (hi - lo) / 15 and min mn_j = -lo, so that the 16 levels
+ * lo + r_j q (q = 0..15) span [lo, hi].  With an importance vector the range
+ * is the best of eight shrunk candidates r_j (16 - t) / 16 (t = 0..7, the
+ * levels anchored at lo): the one with the smallest importance-weighted sum
+ * of squared errors sum_i imp_i (w_i - (lo + s q_i))^2, q_i the nearest level
+ * clamped to 0..15, ties to the smaller t.  Then d = fp16(max_j r_j / 63),
+ * dmin = fp16(max_j mn_j / 63), sc_j = clamp(rint(r_j / d), 0, 63), m_j =
+ * clamp(rint(mn_j / dmin), 0, 63), and each weight takes q = clamp(rint((w +
+ * dmin m_j) / (d sc_j)), 0, 15) -- the nearest point of the grid the block
+ * decodes to (0 where d sc_j = 0). */
+static float q4k_level_err(const float* w, const float* imp, float lo, float s) {
+    float e = 0.0f;
+    for (int i = 0; i < 32; ++i) {
+        float q = s > 0.0f ? clampf(rintf((w[i] - lo) / s), 0.0f, 15.0f) : 0.0f;
+        float r = w[i] - (lo + s * q);
+        e = e + imp[i] * (r * r);
+    }
+    return e;
+}
+
+static void encode_q4k(const float* w, const float* imp, uint8_t* blk) {
+    float rng[8], mn[8];
+    for (int j = 0; j < 8; ++j) {
+        const float* x = w + 32 * j;
+        float lo = 0.0f, hi = x[0];
+        for (int i = 0; i < 32; ++i) {
+            if (x[i] < lo) lo = x[i];
+            if (x[i] > hi) hi = x[i];
+        }
+        float r = (hi - lo) / 15.0f;
+        if (imp) {
+            float best = 0.0f;
+            int best_t = 0;
+            for (int t = 0; t < 8; ++t) {
+                float s = (r * (float)(16 - t)) * 0.0625f;
+                float e = q4k_level_err(x, imp + 32 * j, lo, s);
+                if (t == 0 || e < best) {
+                    best = e;
+                    best_t = t;
+                }
+            }
+            r = (r * (float)(16 - best_t)) * 0.0625f;
+        }
+        rng[j] = r;
+        mn[j] = -lo;
+    }
+    float rmax = 0.0f, mmax = 0.0f;
+    for (int j = 0; j < 8; ++j) {
+        if (rng[j] > rmax) rmax = rng[j];
+        if (mn[j] > mmax) mmax = mn[j];
+    }
+    uint16_t dh = scale_to_half(rmax / 63.0f), mh = scale_to_half(mmax / 63.0f);
+    float d = (float)or_half_to_double(dh), dmin = (float)or_half_to_double(mh);
+    int sc[8], m[8];
+    for (int j = 0; j < 8; ++j) {
+        sc[j] = d > 0.0f ? (int)clampf(rintf(rng[j] / d), 0.0f, 63.0f) : 0;
+        m[j] = dmin > 0.0f ? (int)clampf(rintf(mn[j] / dmin), 0.0f, 63.0f) : 0;
+    }
+    blk[0] = (uint8_t)(dh & 0xff);
+    blk[1] = (uint8_t)(dh >> 8);
+    blk[2] = (uint8_t)(mh & 0xff);
+    blk[3] = (uint8_t)(mh >> 8);
+    /* the 6-bit packing that or_q4k_scale_min reads */
+    uint8_t* S = blk + 4;
+    for (int j = 0; j < 4; ++j) {
+        S[j] = (uint8_t)((sc[j] & 63) | ((sc[j + 4] >> 4) << 6));
+        S[j + 4] = (uint8_t)((m[j] & 63) | ((m[j + 4] >> 4) << 6));
+        S[j + 8] = (uint8_t)((sc[j + 4] & 15) | ((m[j + 4] & 15) << 4));
+    }
+    uint8_t* Q = blk + 16;
+    for (int c = 0; c < 4; ++c) {
+        for (int l = 0; l < 32; ++l) {
+            int qq[2];
+            for (int h = 0; h < 2; ++h) {
+                int j = 2 * c + h;
+                float step = d * (float)sc[j];
+                float off = dmin * (float)m[j];
+                float x = w[64 * c + 32 * h + l];
+                qq[h] = step > 0.0f ? (int)clampf(rintf((x + off) / step), 0.0f, 15.0f) : 0;
+            }
+            Q[32 * c + l] = (uint8_t)(qq[0] | (qq[1] << 4));
+        }
+    }
+}
+
+/* Encode rows x k weights of dtype w_dt (f32, f16 bits or bf16 bits) into
+ * out (rows x k/QK blocks).  imatrix: NULL or k floats (Q4_K only). */
+int or_quantize(int type, const void* w, int w_dt, int64_t rows, int64_t k, const float* imatrix,
+                uint8_t* out) {
+    int qk = or_qk(type), bb = or_block_bytes(type);
+    if (!qk || k % qk) return -1;
+    int64_t nb = k / qk;
+#pragma omp parallel
+    {
+        float* blockw = (float*)malloc(sizeof(float) * qk);
+#pragma omp for schedule(static)
+        for (int64_t r = 0; r < rows; ++r) {
+            for (int64_t b = 0; b < nb; ++b) {
+                for (int i = 0; i < qk; ++i) blockw[i] = act_f32(w, w_dt, r * k + b * qk + i);
+                uint8_t* blk = out + (r * nb + b) * bb;
+                if (type == OR_Q4_K) encode_q4k(blockw, imatrix ? imatrix + b * qk : NULL, blk);
+                else if (type == OR_Q8_0) encode_q8_0(blockw, blk);
+                else encode_tq1(blockw, blk);
+            }
+        }
+        free(blockw);
+    }
+    return 0;
+}
+
+/* [TQ1] "Bounds safety": number of illegal code bytes (a full slot above 242,
+ * a tail above 26) in rows x k/128 blocks. */
+int64_t or_tq1_illegal(const uint8_t* w, int64_t rows, int64_t k) {
+    int64_t nb = rows * (k / 128), bad = 0;
+    for (int64_t b = 0; b < nb; ++b) {
+        const uint8_t* blk = w + b * 28;
+        for (int s = 0; s < 25; ++s) bad += blk[s] > 242;
+        bad += blk[25] > 26;
+    }
+    return bad;
+}
+
+/* ------------------------------------------------------------------ */
 /* Expert routing schedule (integer work)                              */
 /* ------------------------------------------------------------------ */
 

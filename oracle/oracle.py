@@ -17,7 +17,7 @@ from .build import build_oracle
 __all__ = [
     "TYPES", "DTYPES", "lib", "half_to_double", "bf16_to_double", "float_to_half_rne",
     "float_to_bf16_rne", "q4k_scale_min", "dequant", "dequant_as", "qmm", "qmm_points",
-    "qmm_id", "moe_glu", "moe_layer", "route", "routing_poisons_all", "silu", "gelu_tanh", "num_threads",
+    "qmm_id", "moe_glu", "moe_layer", "route", "routing_poisons_all", "quantize", "tq1_illegal", "silu", "gelu_tanh", "num_threads",
 ]
 
 TYPES = {"q4_k": 0, "q8_0": 1, "tq1_g128": 2}
@@ -66,6 +66,10 @@ def lib():
         L.or_moe_layer.restype = C.c_int
         L.or_moe_layer.argtypes = [C.c_int, P, P, P, i64, i64, i64, i64, i64, P, C.c_int, P,
                                    i64, i64, P, P, P]
+        L.or_quantize.restype = C.c_int
+        L.or_quantize.argtypes = [C.c_int, P, C.c_int, i64, i64, P, P]
+        L.or_tq1_illegal.restype = C.c_int64
+        L.or_tq1_illegal.argtypes = [P, i64, i64]
         L.or_route.restype = C.c_int64
         L.or_route.argtypes = [P, i64, i64, i64, i64, P, P, P, P, i64, P]
         L.or_routing_poisons_all.restype = C.c_int
@@ -249,3 +253,22 @@ def route(ids, n_experts, tile_rows):
     valid = int(offsets[-1])
     return {"counts": counts, "offsets": offsets, "perm": perm[:valid], "tiles": tiles[:nt],
             "n_invalid": int(bad[0])}
+
+
+def quantize(kind, w, w_dt, rows, k, imatrix=None):
+    """uint8 [rows, row_bytes]: the encoder's bytes for float weights w
+    [rows, k] (float32, or the uint16 bits of fp16/bf16)."""
+    w = _c(w, np.float32 if w_dt == "f32" else np.uint16)
+    imp = None if imatrix is None else _c(imatrix, np.float32)
+    qk = {"q4_k": 256, "q8_0": 32, "tq1_g128": 128}[kind]
+    bb = {"q4_k": 144, "q8_0": 34, "tq1_g128": 28}[kind]
+    out = np.zeros((rows, (k // qk) * bb), dtype=np.uint8)
+    rc = lib().or_quantize(TYPES[kind], _p(w), DTYPES[w_dt], rows, k, _p(imp), _p(out))
+    if rc:
+        raise ValueError(f"or_quantize failed ({rc})")
+    return out
+
+
+def tq1_illegal(w, rows, k) -> int:
+    w = _c(w, np.uint8)
+    return int(lib().or_tq1_illegal(_p(w), rows, k))

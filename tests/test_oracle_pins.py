@@ -633,3 +633,162 @@ def test_route_schedule_invariants(orc, tile_rows, T, n_bad):
             assert nrows == tile_rows  # only the last tile of an expert is partial
         covered[start:end] += 1
     assert np.all(covered == 1)
+
+
+# ------------------------------------------------------------------ encoders
+def _q4k_grid_blocks(rng, rows, k):
+    """Q4_K blocks whose every sub-block holds both q = 0 and q = 15, with one
+    sub-block at sc = 63 and one at m = 63 (positive normal d, dmin): the
+    grid points that the min-max encoder must reproduce byte for byte."""
+    from tests.test_gpu_precision import _pack_q4k_scales
+
+    nb = rows * (k // 256)
+    out = np.zeros((nb, 144), np.uint8)
+    for b in range(nb):
+        sc = rng.integers(1, 64, 8)
+        m = rng.integers(0, 64, 8)
+        sc[rng.integers(0, 8)] = 63
+        m[rng.integers(0, 8)] = 63
+        d = np.float16(rng.uniform(1e-3, 2e-2))
+        dmin = np.float16(rng.uniform(1e-3, 2e-2))
+        out[b, 0:2] = np.array([d]).view(np.uint8)
+        out[b, 2:4] = np.array([dmin]).view(np.uint8)
+        out[b, 4:16] = _pack_q4k_scales(sc, m)
+        q = rng.integers(0, 16, 256)
+        for j in range(8):
+            q[32 * j] = 0
+            q[32 * j + 1] = 15
+        rng.shuffle(q.reshape(8, 32), axis=1)
+        for c in range(4):
+            lo, hi = q[64 * c:64 * c + 32], q[64 * c + 32:64 * c + 64]
+            out[b, 16 + 32 * c:48 + 32 * c] = lo | (hi << 4)
+    return out.reshape(rows, -1)
+
+
+def test_encoders_reproduce_decoded_blocks(orc):
+    """A block the encoder could have produced decodes to values that encode
+    back to the same bytes: Q8_0 with d > 0 and some |q| = 127, TQ1 with s > 0
+    and some nonzero trit, Q4_K grid blocks."""
+    import synth
+
+    rng = _rng(40)
+    rows = 20
+    q8 = synth.q8_0_blocks(rng, rows, 320).reshape(-1, 34)
+    q8[:, 2] = 127  # one |q| = 127 per block
+    q8 = q8.reshape(rows, -1)
+    tq = synth.tq1_blocks(rng, rows, 384).reshape(-1, 28)
+    tq[:, 0] = 242  # some nonzero trits
+    tq = tq.reshape(rows, -1)
+    q4 = _q4k_grid_blocks(rng, rows, 512)
+    for kind, b, k in (("q8_0", q8, 320), ("tq1_g128", tq, 384), ("q4_k", q4, 512)):
+        w = orc.dequant(kind, b, rows, k).astype(np.float32)
+        assert np.array_equal(w.astype(np.float64), orc.dequant(kind, b, rows, k)), kind
+        again = orc.quantize(kind, w, "f32", rows, k)
+        assert np.array_equal(again, b), kind
+
+
+def test_q4k_encoder_picks_nearest_levels(orc):
+    """Whatever scales the encoder chose, every weight decodes to a level of
+    its sub-block's grid nearest to it (levels from the independent numpy
+    decoder), and the error stays within half the largest step plus the
+    6-bit scale rounding."""
+    rng = _rng(41)
+    rows, k = 16, 1024
+    w = (rng.standard_normal((rows, k)) * rng.uniform(0.01, 3.0, (rows, 1))).astype(np.float32)
+    w[3] = np.abs(w[3])          # all positive rows (min 0)
+    w[4] = -np.abs(w[4])         # all negative rows
+    for imp in (None, rng.uniform(0.0, 2.0, k).astype(np.float32)):
+        b = orc.quantize("q4_k", w, "f32", rows, k, imp)
+        dec = npd.decode_matrix("q4_k", b, rows, k)
+        # the 16 levels of each sub-block: decode blocks with every nibble q
+        blocks = b.reshape(-1, 144)
+        lv = np.empty((blocks.shape[0], 8, 16))
+        for q in range(16):
+            bq = blocks.copy()
+            bq[:, 16:] = q | (q << 4)
+            lv[:, :, q] = npd.decode_matrix("q4_k", bq, blocks.shape[0], 256)[:, ::32]
+        lv = lv.reshape(rows, k // 256, 8, 1, 16)
+        ww = w.astype(np.float64).reshape(rows, k // 256, 8, 32, 1)
+        best = np.abs(ww - lv).min(axis=-1).reshape(rows, k)
+        err = np.abs(dec - w)
+        assert np.all(err <= best + 1e-6 * np.abs(w).max()), np.max(err - best)
+        if imp is not None:
+            continue  # a shrunk range may clip weights of low importance
+        # inside its grid a weight is within half a step; the plain min-max
+        # grid misses the sub-block's range by at most the 6-bit rounding of
+        # its scale (d / 2 per step, 15 steps) and of its min (dmin / 2)
+        hd = blocks[:, 0:4].copy().view(np.float16).astype(np.float64).reshape(rows, k // 256, 2)
+        step = (lv[..., 1] - lv[..., 0]).reshape(rows, k // 256, 8, 1)
+        bound = 0.5 * step + 7.5 * hd[..., 0, None, None] + 0.5 * hd[..., 1, None, None]
+        assert np.all(err.reshape(rows, k // 256, 8, 32) <= bound * (1 + 1e-6) + 1e-7)
+
+
+def test_q8_0_and_tq1_encoder_bounds(orc):
+    rng = _rng(42)
+    rows = 12
+    w = (rng.standard_normal((rows, 384)) * rng.uniform(1e-3, 50.0, (rows, 1))).astype(np.float32)
+    b = orc.quantize("q8_0", w, "f32", rows, 384)
+    d = b.reshape(-1, 34)[:, 0:2].copy().view(np.float16).astype(np.float64).reshape(rows, -1)
+    amax = np.abs(w.reshape(rows, -1, 32)).max(axis=2)
+    assert np.all(np.abs(d - amax / 127) <= 2.0**-11 * amax / 127)  # one fp16 rounding
+    err = np.abs(orc.dequant("q8_0", b, rows, 384) - w).reshape(rows, -1, 32)
+    assert np.all(err <= 0.5 * d[..., None] * (1 + 2.0**-10) + 1e-12)
+    assert (b.reshape(-1, 34)[:, 2:] == 0x80).sum() == 0  # never -128
+    t = orc.quantize("tq1_g128", w, "f32", rows, 384)
+    assert orc.tq1_illegal(t, rows, 384) == 0
+    s = t.reshape(-1, 28)[:, 26:28].copy().view(np.float16).astype(np.float64).reshape(rows, -1)
+    err = np.abs(orc.dequant("tq1_g128", t, rows, 384) - w).reshape(rows, -1, 128)
+    assert np.all(err <= 0.5 * s[..., None] * (1 + 2.0**-10) + 1e-12)
+
+
+def test_encoders_zero_blocks_and_dtypes(orc):
+    z = np.zeros((2, 256), np.float32)
+    assert np.all(orc.quantize("q8_0", z, "f32", 2, 256) == 0)
+    assert np.all(orc.quantize("q4_k", z, "f32", 2, 256) == 0)
+    t = orc.quantize("tq1_g128", z, "f32", 2, 256).reshape(-1, 28)
+    assert np.all(t[:, :25] == 1 + 3 + 9 + 27 + 81) and np.all(t[:, 25] == 1 + 3 + 9)
+    assert np.all(t[:, 26:] == 0)
+    # fp16 / bf16 inputs are the same values as their fp32 conversion
+    import torch
+
+    rng = _rng(43)
+    w = rng.standard_normal((4, 512)).astype(np.float32)
+    h = w.astype(np.float16)
+    bf = torch.from_numpy(w).to(torch.bfloat16)
+    for kind in ("q4_k", "q8_0", "tq1_g128"):
+        a = orc.quantize(kind, h.view(np.uint16), "f16", 4, 512)
+        assert np.array_equal(a, orc.quantize(kind, h.astype(np.float32), "f32", 4, 512))
+        a = orc.quantize(kind, bf.view(torch.int16).numpy().view(np.uint16), "bf16", 4, 512)
+        assert np.array_equal(a, orc.quantize(kind, bf.float().numpy(), "f32", 4, 512))
+
+
+def test_q4k_importance_vector(orc):
+    """Scaling the importances by a power of two changes nothing; an importance
+    on one weight only never makes that weight worse than the plain min-max
+    range of its sub-block would (the unshrunk range is a candidate)."""
+    rng = _rng(44)
+    rows, k = 6, 512
+    w = rng.standard_normal((rows, k)).astype(np.float32)
+    imp = rng.uniform(0.0, 3.0, k).astype(np.float32)
+    a = orc.quantize("q4_k", w, "f32", rows, k, imp)
+    assert np.array_equal(a, orc.quantize("q4_k", w, "f32", rows, k, imp * 4.0))
+    assert not np.array_equal(a, orc.quantize("q4_k", w, "f32", rows, k, None))
+    plain = npd.decode_matrix("q4_k", orc.quantize("q4_k", w, "f32", rows, k, None), rows, k)
+    for col in (5, 100, 300):
+        one = np.zeros(k, np.float32)
+        one[col] = 1.0
+        got = npd.decode_matrix("q4_k", orc.quantize("q4_k", w, "f32", rows, k, one), rows, k)
+        # same d/dmin rounding effects aside, the focused weight does not get worse
+        assert np.all(np.abs(got[:, col] - w[:, col]) <= np.abs(plain[:, col] - w[:, col]) + 0.05)
+
+
+def test_tq1_illegal_count(orc):
+    import synth
+
+    w = synth.tq1_blocks(_rng(45), 3, 256)
+    assert orc.tq1_illegal(w, 3, 256) == 0
+    bad = w.copy().reshape(-1, 28)
+    bad[0, 3] = 243
+    bad[1, 25] = 27
+    bad[5, 24] = 255
+    assert orc.tq1_illegal(bad.reshape(3, -1), 3, 256) == 3
