@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libkq.so")
-SOURCES = ["api.hip", "dequant.hip", "skinny.hip", "mmv2.hip", "mmv3.hip", "gemm.hip", "moe.hip", "moe_dec.hip", "moe_mm.hip", "tq1mv.hip"]
+SOURCES = ["api.hip", "dequant.hip", "skinny.hip", "mmv2.hip", "mmv3.hip", "gemm.hip", "moe.hip", "moe_dec.hip", "moe_mm.hip", "tq1mv.hip", "quantize.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -154,6 +154,39 @@ kq_status kq_dequantize(kq_type t, const void* w, int64_t rows, int64_t k, void*
     return launched(kq::launch_dequant(t, w, rows, k, out, out_dt, (hipStream_t)stream));
 }
 
+kq_status kq_quantize(kq_type t, const void* w, kq_dtype w_dt, int64_t rows, int64_t k,
+                      const float* imatrix, void* out, void* stream) {
+    if (!qk_of(t)) return fail(KQ_ERR_UNSUPPORTED, "unknown weight type");
+    if (!valid_dt(w_dt)) return fail(KQ_ERR_UNSUPPORTED, "unknown dtype");
+    if (imatrix && t != KQ_Q4_K)
+        return fail(KQ_ERR_UNSUPPORTED, "an importance vector steers the Q4_K encoder only");
+    if (rows <= 0 || k <= 0) return fail(KQ_ERR_INVALID_ARG, "rows and k must be positive");
+    if (k % qk_of(t)) return fail(KQ_ERR_INVALID_ARG, "k must be a multiple of the block size");
+    if (!w || !out) return fail(KQ_ERR_INVALID_ARG, "null weight or output pointer");
+    if (!aligned(w, (uintptr_t)elem_size(w_dt)) || !aligned(out, 16) || (imatrix && !aligned(imatrix, 4)))
+        return fail(KQ_ERR_INVALID_ARG, "misaligned pointer (out: 16 bytes, w and imatrix: their element)");
+    int64_t wb, ob;
+    if (!mul_ok(rows, k, wb) || !mul_ok(wb, elem_size(w_dt), wb) ||
+        !mul_ok(rows, (k / qk_of(t)) * bb_of(t), ob))
+        return fail(KQ_ERR_INVALID_ARG, "size overflow");
+    if (overlap({out, ob}, {w, wb}) || (imatrix && overlap({out, ob}, {imatrix, k * 4})))
+        return fail(KQ_ERR_INVALID_ARG, "output overlaps an input");
+    return launched(kq::launch_quantize(t, w, w_dt, rows, k, imatrix, out, (hipStream_t)stream));
+}
+
+kq_status kq_validate_tq1(const void* w, int64_t rows, int64_t k, uint64_t* n_illegal,
+                          void* stream) {
+    if (rows <= 0 || k <= 0) return fail(KQ_ERR_INVALID_ARG, "rows and k must be positive");
+    if (k % 128) return fail(KQ_ERR_INVALID_ARG, "k must be a multiple of 128");
+    if (!w || !n_illegal) return fail(KQ_ERR_INVALID_ARG, "null pointer");
+    if (!aligned(w, 4) || !aligned(n_illegal, 8)) return fail(KQ_ERR_INVALID_ARG, "misaligned pointer");
+    int64_t wb;
+    if (!mul_ok(rows, (k / 128) * 28, wb)) return fail(KQ_ERR_INVALID_ARG, "size overflow");
+    if (overlap({n_illegal, 8}, {w, wb})) return fail(KQ_ERR_INVALID_ARG, "count overlaps the weights");
+    return launched(kq::launch_tq1_illegal(w, rows, k, (unsigned long long*)n_illegal,
+                                           (hipStream_t)stream));
+}
+
 static kq_status dense_skinny(kq_type t, const void* w, int64_t n, int64_t k, int64_t row_bytes,
                               const void* x, kq_dtype x_dt, int64_t m, void* y, kq_dtype y_dt,
                               hipStream_t s) {

@@ -73,6 +73,11 @@ hipError_t launch_down_mix1(const DownMixArgs& a, bool x_f32, hipStream_t s);
 // Single-token gate/up with SiLU, expert ids read directly (moe_dec.hip).
 hipError_t launch_moe_glu1(const SkinnyArgs& a, hipStream_t s);
 
+// Encoders and the TQ1 legality scan (quantize.hip).
+hipError_t launch_quantize(int codec, const void* w, int w_dt, int64_t rows, int64_t k,
+                           const float* imatrix, void* out, hipStream_t s);
+hipError_t launch_tq1_illegal(const void* w, int64_t rows, int64_t k, unsigned long long* count,
+                              hipStream_t s);
 hipError_t launch_dequant(int codec, const void* w, int64_t rows, int64_t k, void* out, int out_dt,
                           hipStream_t s);
 hipError_t launch_skinny(int codec, int x_dt, bool glu, const SkinnyArgs& a, int64_t grid_tiles,

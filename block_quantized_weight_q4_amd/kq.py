@@ -19,7 +19,7 @@ from ._build import LIB
 
 __all__ = [
     "KQError", "TYPES", "lib", "kq_status_string", "kq_last_error", "kq_qk", "kq_block_bytes",
-    "kq_row_bytes", "kq_dequantize", "kq_qmv", "kq_qmm", "kq_qmm_workspace_bytes", "kq_qmm_ws",
+    "kq_row_bytes", "kq_dequantize", "kq_quantize", "kq_validate_tq1", "kq_qmv", "kq_qmm", "kq_qmm_workspace_bytes", "kq_qmm_ws",
     "kq_qmm_noalloc_max_bytes", "kq_qmm_noalloc", "kq_moe_workspace_bytes", "kq_moe_route",
     "kq_qmm_id", "kq_moe_glu", "moe_schedule", "SYMBOLS", "LAYOUT_SHARED", "LAYOUT_SLOTTED", "REUSE_SCHEDULE",
     "ACT_SILU", "ACT_GELU_TANH", "MOE_TILE_ROWS",
@@ -36,8 +36,8 @@ MOE_TILE_ROWS = 32
 # Every function include/kq.h declares.
 SYMBOLS = (
     "kq_status_string", "kq_last_error", "kq_qk", "kq_block_bytes", "kq_row_bytes",
-    "kq_dequantize", "kq_qmv", "kq_qmm", "kq_qmm_workspace_bytes", "kq_qmm_ws",
-    "kq_qmm_noalloc_max_bytes", "kq_qmm_noalloc", "kq_moe_workspace_bytes", "kq_moe_route",
+    "kq_dequantize", "kq_quantize", "kq_validate_tq1", "kq_qmv", "kq_qmm",
+    "kq_qmm_workspace_bytes", "kq_qmm_ws", "kq_qmm_noalloc_max_bytes", "kq_qmm_noalloc", "kq_moe_workspace_bytes", "kq_moe_route",
     "kq_qmm_id", "kq_moe_glu",
 )
 
@@ -74,6 +74,10 @@ def lib():
     L.kq_row_bytes.argtypes = [i32, i64]
     L.kq_dequantize.restype = i32
     L.kq_dequantize.argtypes = [i32, P, i64, i64, P, i32, P]
+    L.kq_quantize.restype = i32
+    L.kq_quantize.argtypes = [i32, P, i32, i64, i64, P, P, P]
+    L.kq_validate_tq1.restype = i32
+    L.kq_validate_tq1.argtypes = [P, i64, i64, P, P]
     for name in ("kq_qmv", "kq_qmm"):
         f = getattr(L, name)
         f.restype = i32
@@ -176,6 +180,23 @@ def kq_dequantize(kind: str, w, rows: int, k: int, out):
     _tensors(("w", w, _rows_bytes(kind, rows, k)), ("out", out, rows * k * out.element_size()))
     _check(lib().kq_dequantize(TYPES[kind], _ptr(w), rows, k, _ptr(out), _dt(out), _stream(w, out)))
     return out
+
+
+def kq_quantize(kind: str, w, rows: int, k: int, out, imatrix=None):
+    """Encode float weights w [rows, k] into out (uint8 block bytes)."""
+    _tensors(("w", w, rows * k * w.element_size()), ("imatrix", imatrix, k * 4),
+             ("out", out, _rows_bytes(kind, rows, k)))
+    _check(lib().kq_quantize(TYPES[kind], _ptr(w), _dt(w), rows, k, _ptr(imatrix), _ptr(out),
+                             _stream(w, out)))
+    return out
+
+
+def kq_validate_tq1(w, rows: int, k: int, count):
+    """count: a device int64 tensor of one element that receives the number
+    of illegal code bytes."""
+    _tensors(("w", w, _rows_bytes("tq1_g128", rows, k)), ("count", count, 8))
+    _check(lib().kq_validate_tq1(_ptr(w), rows, k, _ptr(count), _stream(w, count)))
+    return count
 
 
 def kq_qmv(kind: str, w, n: int, k: int, x, m: int, y):

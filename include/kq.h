@@ -114,6 +114,51 @@ kq_status kq_dequantize(kq_type t, const void* w, int64_t rows, int64_t k, void*
                         kq_dtype out_dt, void* stream);
 
 /*
+ * kq_quantize -- encode float weights into block bytes.
+ * mlx-kquant "bindings.cpp", quantize (float weights whose last dimension is
+ * a multiple of the codec's block size -> the codec's wire bytes; an optional
+ * 1-D float32 importance vector of length K steers the K-quant encoder).
+ *
+ *   w        [rows, k]            w_dt (f32, f16 or bf16), row-major, finite
+ *   imatrix  [k] float32 >= 0, or NULL; Q4_K only (else KQ_ERR_UNSUPPORTED)
+ *   out      [rows, k/QK blocks]  block bytes, 16-byte aligned
+ *
+ * The pages fix the contract, not an encoder; the encoders (binary32 steps in
+ * a fixed order, so the bytes are reproducible bit for bit):
+ *   Q8_0   d = fp16(max|w| / 127), q = clamp(rint(w * (1/d)), -127, 127).
+ *   TQ1    s = fp16(max|w|) per 128 weights, trit = clamp(rint(w * (1/s)),
+ *          -1, 1); every code byte is legal.
+ *   Q4_K   per 32-weight sub-block, the min-max range [min(0, min w), max w]
+ *          (with imatrix: the best of eight ranges shrunk towards the
+ *          minimum, by importance-weighted squared error); d and dmin are
+ *          the largest scale and min over 63 in fp16, the 6-bit sc and m the
+ *          nearest multiples, q the nearest level clamped to 0..15.
+ * Scales past 65504 are clamped to it.  A block decoded from the encoders'
+ * output range (Q8_0 with a |q| of 127, TQ1 with a nonzero trit, Q4_K whose
+ * sub-blocks use levels 0 and 15 and whose largest sc and m are 63) encodes
+ * back to its own bytes.
+ * Errors: rows or k <= 0, k % QK != 0, null or misaligned pointers, out
+ * overlapping an input -> KQ_ERR_INVALID_ARG.
+ */
+kq_status kq_quantize(kq_type t, const void* w, kq_dtype w_dt, int64_t rows, int64_t k,
+                      const float* imatrix, void* out, void* stream);
+
+/*
+ * kq_validate_tq1 -- count illegal TQ1_G128 code bytes (a full code byte
+ * above 242, a tail byte above 26) in rows x k/128 blocks.  Ternary Bonsai
+ * "ternel_packed_model.py", kernels section ("Bounds safety": legality is
+ * enforced outside the product kernels, at conversion and at load).
+ *
+ *   w          [rows, k/128 blocks], 4-byte aligned (device)
+ *   n_illegal  one uint64 in device memory, 8-byte aligned: the count
+ *
+ * The count is written on the stream (no host synchronization).  The product
+ * kernels' outputs for weights with a nonzero count are unspecified.
+ */
+kq_status kq_validate_tq1(const void* w, int64_t rows, int64_t k, uint64_t* n_illegal,
+                          void* stream);
+
+/*
  * kq_qmv / kq_qmm -- y = x @ dequant(w)^T.
  * mlx-kquant "bindings.cpp", quantized_matmul (x @ dequant(w), w laid out
  * [N, K] when transpose=True); Ternary Bonsai "ternel_packed_model.py",
