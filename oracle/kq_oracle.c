@@ -452,25 +452,53 @@ double or_gelu_tanh(double z) {
     return 0.5 * z * (1.0 + tanh(c * (z + 0.044715 * z * z * z)));
 }
 
+/* [KQ] moe_glu_gather_kq, act='silu_limit' (deepseek-v4 LimitedSwiGLU):
+ * silu(min(g, limit)) * clip(u, -limit, limit), limit > 0. */
+double or_silu_limit(double g, double u, double limit) {
+    double gc = g < limit ? g : limit;
+    double uc = u < -limit ? -limit : u > limit ? limit : u;
+    return or_silu(gc) * uc;
+}
+
+static double glu_value(int act, double g, double u, double limit) {
+    if (act == 1) return or_gelu_tanh(g) * u;
+    if (act == 2) return or_silu_limit(g, u, limit);
+    return or_silu(g) * u;
+}
+
 /* [KQ] moe_glu_gather_kq with act = 0 ('silu') or 1 ('gelu', tanh
  * approximation): for each token t and slot r with e = ids[t,r]:
  * g = W_gate[e] x_t, u = W_up[e] x_t, h = act(g) * u, giving h[T, top_k, n].
  * Also returns g, u and their |.|-sums sg, su (any of the extra outputs may
  * be NULL).  Invalid ids poison h as or_routing_poisons_all describes (below
  * 32 tokens only the h row of an out-of-range id). */
-int or_moe_glu(int type, const uint8_t* gate_w, const uint8_t* up_w, int64_t n_experts,
-               int64_t n, int64_t k, int64_t expert_stride, const void* x, int x_dt,
-               const uint32_t* ids, int64_t T, int64_t top_k, int act, double* h, double* g,
-               double* u, double* sg, double* su) {
-    if (act != 0 && act != 1) return -3;
+/* [KQ] moe_glu_gather_kq (act 0 'silu', 1 'gelu', 2 'silu_limit' with
+ * limit > 0) and moe_glu_gather_shexp_kq: for each token t and slot r,
+ * g = W_gate[e] x_t, u = W_up[e] x_t, h = act(g, u), giving h[T, S, n].
+ * Without a shared expert S = top_k and e = ids[t, r]; with one (shexp_gate
+ * and shexp_up non-NULL, single-expert matrices [n, k/QK blocks]) S = top_k
+ * + 1 and the last slot of every token uses the shared expert's weights.
+ * Also returns g, u and their |.|-sums sg, su (any extra output may be NULL).
+ * Invalid routed ids poison h by the rule of or_routing_poisons_all (the
+ * shared slot is never invalid; below 32 tokens only an out-of-range routed
+ * id's row is NaN). */
+int or_moe_glu_ex(int type, const uint8_t* gate_w, const uint8_t* up_w, int64_t n_experts,
+                  int64_t n, int64_t k, int64_t expert_stride, const uint8_t* shexp_gate,
+                  const uint8_t* shexp_up, const void* x, int x_dt, const uint32_t* ids, int64_t T,
+                  int64_t top_k, int act, double limit, double* h, double* g, double* u,
+                  double* sg, double* su) {
+    if (act < 0 || act > 2) return -3;
+    if (act == 2 && !(limit > 0.0)) return -4;
     int qk = or_qk(type);
     if (!qk || k % qk) return -1;
+    int shexp = shexp_gate && shexp_up;
+    int64_t S = top_k + shexp;
     if (or_routing_poisons_all(ids, T, top_k, n_experts)) {
-        fill_nan(h, T * top_k * n);
-        fill_nan(g, T * top_k * n);
-        fill_nan(u, T * top_k * n);
-        fill_nan(sg, T * top_k * n);
-        fill_nan(su, T * top_k * n);
+        fill_nan(h, T * S * n);
+        fill_nan(g, T * S * n);
+        fill_nan(u, T * S * n);
+        fill_nan(sg, T * S * n);
+        fill_nan(su, T * S * n);
         return 0;
     }
 #pragma omp parallel
@@ -478,12 +506,15 @@ int or_moe_glu(int type, const uint8_t* gate_w, const uint8_t* up_w, int64_t n_e
         double* rg = (double*)malloc(sizeof(double) * k);
         double* ru = (double*)malloc(sizeof(double) * k);
 #pragma omp for schedule(static)
-        for (int64_t tr = 0; tr < T * top_k; ++tr) {
-            int64_t t = tr / top_k;
-            uint32_t e = ids[tr];
+        for (int64_t ts = 0; ts < T * S; ++ts) {
+            int64_t t = ts / S, r = ts % S;
+            int shared = shexp && r == top_k;
+            uint32_t e = shared ? 0u : ids[t * top_k + r];
+            const uint8_t* wg = shared ? shexp_gate : gate_w + (int64_t)e * expert_stride;
+            const uint8_t* wu = shared ? shexp_up : up_w + (int64_t)e * expert_stride;
             for (int64_t j = 0; j < n; ++j) {
-                int64_t o = tr * n + j;
-                if ((int64_t)e >= n_experts) {
+                int64_t o = ts * n + j;
+                if (!shared && (int64_t)e >= n_experts) {
                     h[o] = NAN;
                     if (g) g[o] = NAN;
                     if (u) u[o] = NAN;
@@ -491,8 +522,8 @@ int or_moe_glu(int type, const uint8_t* gate_w, const uint8_t* up_w, int64_t n_e
                     if (su) su[o] = NAN;
                     continue;
                 }
-                decode_row(type, gate_w + (int64_t)e * expert_stride, j, k, rg);
-                decode_row(type, up_w + (int64_t)e * expert_stride, j, k, ru);
+                decode_row(type, wg, j, k, rg);
+                decode_row(type, wu, j, k, ru);
                 double ag = 0, au = 0, mg = 0, mu = 0;
                 for (int64_t c = 0; c < k; ++c) {
                     double xv = act_value(x, x_dt, t * k + c);
@@ -501,7 +532,7 @@ int or_moe_glu(int type, const uint8_t* gate_w, const uint8_t* up_w, int64_t n_e
                     au += xv * ru[c];
                     mu += fabs(xv * ru[c]);
                 }
-                h[o] = (act == 1 ? or_gelu_tanh(ag) : or_silu(ag)) * au;
+                h[o] = glu_value(act, ag, au, limit);
                 if (g) g[o] = ag;
                 if (u) u[o] = au;
                 if (sg) sg[o] = mg;
@@ -510,6 +541,67 @@ int or_moe_glu(int type, const uint8_t* gate_w, const uint8_t* up_w, int64_t n_e
         }
         free(rg);
         free(ru);
+    }
+    return 0;
+}
+
+/* The same without a shared expert or a limit (act 0 or 1). */
+int or_moe_glu(int type, const uint8_t* gate_w, const uint8_t* up_w, int64_t n_experts,
+               int64_t n, int64_t k, int64_t expert_stride, const void* x, int x_dt,
+               const uint32_t* ids, int64_t T, int64_t top_k, int act, double* h, double* g,
+               double* u, double* sg, double* su) {
+    if (act != 0 && act != 1) return -3;
+    return or_moe_glu_ex(type, gate_w, up_w, n_experts, n, k, expert_stride, NULL, NULL, x, x_dt,
+                         ids, T, top_k, act, 0.0, h, g, u, sg, su);
+}
+
+/* [KQ] gather_qmv_mix_kq: the mixed down projection with the shared expert
+ * as the last of S = top_k + 1 slots: x is [T, S, k], scores [T, S] and
+ * y[t] = sum over slots r in order of scores[t,r] * (W_r x[t,r]) with W_r =
+ * W[ids[t,r]] for r < top_k and the shared matrix shexp_w ([n, k/QK
+ * blocks]) for r = top_k.  s[t] = sum_r |scores| * sum_c |W_r x|.  Invalid
+ * routed ids poison as in or_qmm_id. */
+int or_qmm_id_mix_shexp(int type, const uint8_t* w, int64_t n_experts, int64_t n, int64_t k,
+                        int64_t expert_stride, const uint8_t* shexp_w, const void* x, int x_dt,
+                        const uint32_t* ids, int64_t T, int64_t top_k, const float* scores,
+                        double* y, double* s) {
+    int qk = or_qk(type);
+    if (!qk || k % qk) return -1;
+    int64_t S = top_k + 1;
+    if (or_routing_poisons_all(ids, T, top_k, n_experts)) {
+        fill_nan(y, T * n);
+        fill_nan(s, T * n);
+        return 0;
+    }
+#pragma omp parallel
+    {
+        double* row = (double*)malloc(sizeof(double) * k);
+#pragma omp for schedule(static)
+        for (int64_t t = 0; t < T; ++t) {
+            int bad = 0;
+            for (int64_t r = 0; r < top_k; ++r) bad |= (int64_t)ids[t * top_k + r] >= n_experts;
+            for (int64_t j = 0; j < n; ++j) {
+                y[t * n + j] = bad ? NAN : 0.0;
+                if (s) s[t * n + j] = bad ? NAN : 0.0;
+            }
+            if (bad) continue;
+            for (int64_t r = 0; r < S; ++r) {
+                const uint8_t* wr = r == top_k ? shexp_w : w + (int64_t)ids[t * top_k + r] * expert_stride;
+                double wt = (double)scores[t * S + r];
+                for (int64_t j = 0; j < n; ++j) {
+                    decode_row(type, wr, j, k, row);
+                    double acc = 0.0, mag = 0.0;
+                    for (int64_t c = 0; c < k; ++c) {
+                        double tv = act_value(x, x_dt, (t * S + r) * k + c) * row[c];
+                        acc += tv;
+                        mag += fabs(tv);
+                    }
+                    y[t * n + j] += wt * acc;
+                    if (s) s[t * n + j] += fabs(wt) * mag;
+                }
+            }
+        }
+        free(row);
     }
     return 0;
 }

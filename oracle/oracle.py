@@ -17,7 +17,7 @@ from .build import build_oracle
 __all__ = [
     "TYPES", "DTYPES", "lib", "half_to_double", "bf16_to_double", "float_to_half_rne",
     "float_to_bf16_rne", "q4k_scale_min", "dequant", "dequant_as", "qmm", "qmm_points",
-    "qmm_id", "moe_glu", "moe_layer", "route", "routing_poisons_all", "quantize", "tq1_illegal", "silu", "gelu_tanh", "num_threads",
+    "qmm_id", "moe_glu", "moe_layer", "route", "routing_poisons_all", "quantize", "tq1_illegal", "silu_limit", "moe_glu_ex", "qmm_id_mix_shexp", "silu", "gelu_tanh", "num_threads",
 ]
 
 TYPES = {"q4_k": 0, "q8_0": 1, "tq1_g128": 2}
@@ -63,6 +63,14 @@ def lib():
         L.or_moe_glu.restype = C.c_int
         L.or_moe_glu.argtypes = [C.c_int, P, P, i64, i64, i64, i64, P, C.c_int, P, i64, i64,
                                  C.c_int, P, P, P, P, P]
+        L.or_silu_limit.restype = C.c_double
+        L.or_silu_limit.argtypes = [C.c_double, C.c_double, C.c_double]
+        L.or_moe_glu_ex.restype = C.c_int
+        L.or_moe_glu_ex.argtypes = [C.c_int, P, P, i64, i64, i64, i64, P, P, P, C.c_int, P, i64,
+                                    i64, C.c_int, C.c_double, P, P, P, P, P]
+        L.or_qmm_id_mix_shexp.restype = C.c_int
+        L.or_qmm_id_mix_shexp.argtypes = [C.c_int, P, i64, i64, i64, i64, P, P, C.c_int, P, i64,
+                                          i64, P, P, P]
         L.or_moe_layer.restype = C.c_int
         L.or_moe_layer.argtypes = [C.c_int, P, P, P, i64, i64, i64, i64, i64, P, C.c_int, P,
                                    i64, i64, P, P, P]
@@ -272,3 +280,46 @@ def quantize(kind, w, w_dt, rows, k, imatrix=None):
 def tq1_illegal(w, rows, k) -> int:
     w = _c(w, np.uint8)
     return int(lib().or_tq1_illegal(_p(w), rows, k))
+
+
+def silu_limit(g: float, u: float, limit: float) -> float:
+    return lib().or_silu_limit(float(g), float(u), float(limit))
+
+
+def moe_glu_ex(kind, gate_w, up_w, n_experts, n, k, expert_stride, x, x_dt, ids, T, top_k,
+               act=0, limit=0.0, shexp_gate=None, shexp_up=None):
+    """dict of h, g, u, sg, su, each [T, S, n] float64 with S = top_k (+1 with
+    a shared expert, its slot last); act 0 silu, 1 gelu (tanh), 2 silu_limit."""
+    gate_w = _c(gate_w, np.uint8)
+    up_w = _c(up_w, np.uint8)
+    sg_ = None if shexp_gate is None else _c(shexp_gate, np.uint8)
+    su_ = None if shexp_up is None else _c(shexp_up, np.uint8)
+    x = _c(x, np.float32 if x_dt == "f32" else np.uint16)
+    ids = _c(ids, np.uint32)
+    S = top_k + (1 if sg_ is not None else 0)
+    out = {key: np.empty((T, S, n), dtype=np.float64) for key in ("h", "g", "u", "sg", "su")}
+    rc = lib().or_moe_glu_ex(TYPES[kind], _p(gate_w), _p(up_w), n_experts, n, k, expert_stride,
+                             _p(sg_), _p(su_), _p(x), DTYPES[x_dt], _p(ids), T, top_k, act,
+                             float(limit), _p(out["h"]), _p(out["g"]), _p(out["u"]),
+                             _p(out["sg"]), _p(out["su"]))
+    if rc:
+        raise ValueError(f"or_moe_glu_ex failed ({rc})")
+    return out
+
+
+def qmm_id_mix_shexp(kind, w, n_experts, n, k, expert_stride, shexp_w, x, x_dt, ids, T, top_k,
+                     scores):
+    """(y, s), each [T, n]: the mixed down projection over T x (top_k + 1)
+    slotted rows, the shared expert last."""
+    w = _c(w, np.uint8)
+    sw = _c(shexp_w, np.uint8)
+    x = _c(x, np.float32 if x_dt == "f32" else np.uint16)
+    ids = _c(ids, np.uint32)
+    scores = _c(scores, np.float32)
+    y = np.empty((T, n), dtype=np.float64)
+    s = np.empty((T, n), dtype=np.float64)
+    rc = lib().or_qmm_id_mix_shexp(TYPES[kind], _p(w), n_experts, n, k, expert_stride, _p(sw),
+                                   _p(x), DTYPES[x_dt], _p(ids), T, top_k, _p(scores), _p(y), _p(s))
+    if rc:
+        raise ValueError(f"or_qmm_id_mix_shexp failed ({rc})")
+    return y, s

@@ -792,3 +792,103 @@ def test_tq1_illegal_count(orc):
     bad[1, 25] = 27
     bad[5, 24] = 255
     assert orc.tq1_illegal(bad.reshape(3, -1), 3, 256) == 3
+
+
+# ------------------------------------------------------------------ silu_limit, shared expert
+def test_silu_limit_against_torch(orc):
+    """mlx-kquant moe_glu_gather_kq act='silu_limit': silu(min(g, limit)) *
+    clip(u, -limit, limit), checked against torch's silu and clamp (float64)."""
+    import torch
+
+    rng = _rng(50)
+    g = rng.uniform(-40, 40, 500)
+    u = rng.uniform(-40, 40, 500)
+    for limit in (0.5, 7.0, 1e6):
+        ref = (torch.nn.functional.silu(torch.clamp(torch.from_numpy(g), max=limit)) *
+               torch.clamp(torch.from_numpy(u), -limit, limit)).numpy()
+        got = np.array([orc.silu_limit(a, b, limit) for a, b in zip(g, u)])
+        assert np.allclose(got, ref, rtol=1e-13, atol=1e-300)
+    # a limit past every value is plain silu(g) * u
+    assert orc.silu_limit(3.0, -2.0, 1e9) == pytest.approx(orc.silu(3.0) * -2.0, rel=1e-15)
+
+
+def _shexp_case(seed, E=5, n=64, k=512, T=4, top_k=2):
+    import synth
+
+    rng = _rng(seed)
+    gate = synth.weight_blocks("q4_k", rng, E * n, k)
+    up = synth.weight_blocks("q4_k", rng, E * n, k)
+    sg = synth.weight_blocks("q4_k", rng, n, k)
+    su = synth.weight_blocks("q4_k", rng, n, k)
+    stride = n * synth.row_bytes("q4_k", k)
+    x = synth.activations(rng, (T, k), "f16")
+    ids = np.stack([rng.choice(E, top_k, replace=False) for _ in range(T)]).astype(np.uint32)
+    return rng, E, n, k, T, top_k, gate, up, sg, su, stride, x, ids
+
+
+def test_moe_glu_shared_expert_slot(orc):
+    """mlx-kquant moe_glu_gather_shexp_kq: the shared expert is one extra,
+    last slot computed with its own matrices; the routed slots are unchanged.
+    Checked with the independent numpy decoder, for silu, gelu and silu_limit."""
+    import torch
+
+    rng, E, n, k, T, top_k, gate, up, sg, su, stride, x, ids = _shexp_case(51)
+    X = npd.act_f64(x, "f16")
+    Gs = X @ npd.decode_matrix("q4_k", sg, n, k).T
+    Us = X @ npd.decode_matrix("q4_k", su, n, k).T
+    acts = {0: lambda g, u: torch.nn.functional.silu(g) * u,
+            1: lambda g, u: torch.nn.functional.gelu(g, approximate="tanh") * u,
+            2: lambda g, u: torch.nn.functional.silu(torch.clamp(g, max=3.0)) * torch.clamp(u, -3.0, 3.0)}
+    for act, fn in acts.items():
+        r = orc.moe_glu_ex("q4_k", gate, up, E, n, k, stride, x, "f16", ids, T, top_k, act, 3.0,
+                           sg, su)
+        assert r["h"].shape == (T, top_k + 1, n)
+        want = fn(torch.from_numpy(Gs), torch.from_numpy(Us)).numpy()
+        assert np.allclose(r["h"][:, top_k], want, rtol=1e-11, atol=1e-11 * np.abs(want).max())
+        routed = orc.moe_glu_ex("q4_k", gate, up, E, n, k, stride, x, "f16", ids, T, top_k, act, 3.0)
+        assert np.array_equal(r["h"][:, :top_k], routed["h"])
+
+
+def test_mix_with_shared_expert_brute_force(orc):
+    """mlx-kquant gather_qmv_mix_kq: y[t] = sum over routed slots of score *
+    W[e] x[t, r] plus the last score times the shared matrix applied to the
+    last slot's row, against numpy with the independent decoder."""
+    import synth
+
+    rng, E, n, k, T, top_k, gate, up, sg, su, stride, x, ids = _shexp_case(52, n=64, k=256)
+    H = 96
+    down = synth.weight_blocks("q4_k", rng, E * H, n * 4)
+    dsh = synth.weight_blocks("q4_k", rng, H, n * 4)
+    kk = n * 4
+    xs = synth.activations(rng, (T, top_k + 1, kk), "f16")
+    scores = rng.uniform(0.05, 1.0, (T, top_k + 1)).astype(np.float32)
+    dstride = H * synth.row_bytes("q4_k", kk)
+    y, s = orc.qmm_id_mix_shexp("q4_k", down, E, H, kk, dstride, dsh, xs, "f16", ids, T, top_k,
+                                scores)
+    Wd = npd.decode_matrix("q4_k", down, E * H, kk).reshape(E, H, kk)
+    Ws = npd.decode_matrix("q4_k", dsh, H, kk)
+    X = npd.act_f64(xs.reshape(-1, kk), "f16").reshape(T, top_k + 1, kk)
+    for t in range(T):
+        ref = sum(float(scores[t, r]) * (Wd[ids[t, r]] @ X[t, r]) for r in range(top_k))
+        ref = ref + float(scores[t, top_k]) * (Ws @ X[t, top_k])
+        assert np.allclose(y[t], ref, rtol=0, atol=1e-11 * np.abs(ref).max())
+        sref = sum(abs(float(scores[t, r])) * (np.abs(Wd[ids[t, r]]) @ np.abs(X[t, r]))
+                   for r in range(top_k)) + abs(float(scores[t, top_k])) * (np.abs(Ws) @ np.abs(X[t, top_k]))
+        assert np.allclose(s[t], sref, rtol=1e-12)
+
+
+def test_shared_expert_poison_rules(orc):
+    """The shared slot is never invalid; routed ids poison as without it."""
+    import synth
+
+    rng, E, n, k, T, top_k, gate, up, sg, su, stride, x, ids = _shexp_case(53, T=40)
+    bad = ids.copy()
+    bad[7, 1] = bad[7, 0]  # a repeat, 40 tokens: matrix-matrix rule
+    r = orc.moe_glu_ex("q4_k", gate, up, E, n, k, stride, x, "f16", bad, 40, top_k, 0, 0.0, sg, su)
+    assert np.all(np.isnan(r["h"]))
+    small = ids[:10].copy()
+    small[3, 0] = E + 2    # out of range, 10 tokens: only that routed row
+    r = orc.moe_glu_ex("q4_k", gate, up, E, n, k, stride, x[:10], "f16", small, 10, top_k, 0, 0.0,
+                       sg, su)
+    nanrows = np.isnan(r["h"]).all(axis=2)
+    assert nanrows.sum() == 1 and nanrows[3, 0] and np.all(np.isfinite(r["h"][:, top_k]))
