@@ -313,9 +313,12 @@ size_t kq_moe_workspace_bytes(int64_t n_experts, int64_t n_tokens, int64_t top_k
 static const int64_t kMaxExperts = 4096;
 static const int64_t kMaxGridY = 65535;
 
+// top_k and n_experts count a shared expert's slot when there is one;
+// ids_per_token (0: top_k) is the number of ids per token the caller holds.
 static kq_status check_routing(const uint32_t* ids, int64_t n_tokens, int64_t top_k,
                                int64_t n_experts, void* workspace, size_t workspace_bytes,
-                               int64_t n_out) {
+                               int64_t n_out, int64_t ids_per_token = 0) {
+    if (!ids_per_token) ids_per_token = top_k;
     if (n_experts <= 0 || n_experts > kMaxExperts)
         return fail(KQ_ERR_INVALID_ARG, "n_experts must be in 1..4096");
     if (n_tokens <= 0) return fail(KQ_ERR_INVALID_ARG, "n_tokens must be positive");
@@ -330,7 +333,7 @@ static kq_status check_routing(const uint32_t* ids, int64_t n_tokens, int64_t to
         return fail(KQ_ERR_WORKSPACE, "workspace must be non-null and 256-byte aligned");
     if ((int64_t)workspace_bytes < L.total_bytes)
         return fail(KQ_ERR_WORKSPACE, "workspace smaller than kq_moe_workspace_bytes()");
-    if (overlap({workspace, L.total_bytes}, {ids, n_tokens * top_k * 4}))
+    if (overlap({workspace, L.total_bytes}, {ids, n_tokens * ids_per_token * 4}))
         return fail(KQ_ERR_INVALID_ARG, "workspace overlaps ids");
     return KQ_OK;
 }
@@ -345,18 +348,31 @@ kq_status kq_moe_route(const uint32_t* ids, int64_t n_tokens, int64_t top_k, int
 }
 
 // Shared validation of the expert-routed calls.
+// With a shared expert (shexp = 1; w_sh, and w2_sh for the GLU, are its
+// matrices of n rows) the routing has top_k + 1 slots per token over
+// n_experts + 1 experts, and scores / outputs count top_k + 1 slots.
 static kq_status check_expert_call(kq_type t, const void* w, const void* w2, int64_t n_experts,
                                    int64_t n, int64_t k, int64_t expert_stride, const void* x,
                                    kq_dtype x_dt, int64_t x_rows, const uint32_t* ids,
                                    int64_t n_tokens, int64_t top_k, const float* scores, void* y,
                                    kq_dtype y_dt, int64_t y_rows, void* workspace,
-                                   size_t workspace_bytes, int64_t n_out, int64_t& row_bytes) {
+                                   size_t workspace_bytes, int64_t n_out, int64_t& row_bytes,
+                                   int shexp = 0, const void* w_sh = nullptr,
+                                   const void* w2_sh = nullptr) {
     kq_status st = check_weights(t, w, n, k, row_bytes);
     if (st) return st;
     if ((st = check_product_size(n, k))) return st;
     if (w2 && !aligned(w2, 16)) return fail(KQ_ERR_INVALID_ARG, "weights must be 16-byte aligned");
+    if (shexp && (!w_sh || (w2 && !w2_sh)))
+        return fail(KQ_ERR_INVALID_ARG, "null shared-expert weights");
+    if ((w_sh && !aligned(w_sh, 16)) || (w2_sh && !aligned(w2_sh, 16)))
+        return fail(KQ_ERR_INVALID_ARG, "shared-expert weights must be 16-byte aligned");
     if (!valid_dt(x_dt) || !valid_dt(y_dt)) return fail(KQ_ERR_UNSUPPORTED, "unknown dtype");
-    st = check_routing(ids, n_tokens, top_k, n_experts, workspace, workspace_bytes, n_out);
+    if (top_k <= 0 || top_k > n_experts) return fail(KQ_ERR_INVALID_ARG, "top_k must be in 1..n_experts");
+    if (n_experts <= 0 || n_experts > kMaxExperts - shexp)
+        return fail(KQ_ERR_INVALID_ARG, "n_experts out of range");
+    st = check_routing(ids, n_tokens, top_k + shexp, n_experts + shexp, workspace, workspace_bytes,
+                       n_out, top_k);
     if (st) return st;
     int64_t one;
     if (!mul_ok(n, row_bytes, one)) return fail(KQ_ERR_INVALID_ARG, "size overflow");
@@ -371,34 +387,40 @@ static kq_status check_expert_call(kq_type t, const void* w, const void* w2, int
     if (!mul_ok(x_rows, k, xb) || !mul_ok(xb, elem_size(x_dt), xb) || !mul_ok(y_rows, n, yb) ||
         !mul_ok(yb, elem_size(y_dt), yb))
         return fail(KQ_ERR_INVALID_ARG, "size overflow");
-    const kq::MoeLayout L = kq::moe_layout(n_experts, n_tokens, top_k, n_out);
+    const kq::MoeLayout L = kq::moe_layout(n_experts + shexp, n_tokens, top_k + shexp, n_out);
     const Range ry{y, yb};
     if (overlap(ry, {w, wb}) || (w2 && overlap(ry, {w2, wb})) || overlap(ry, {x, xb}) ||
         overlap(ry, {ids, n_tokens * top_k * 4}) ||
-        (scores && overlap(ry, {scores, n_tokens * top_k * 4})) ||
-        overlap(ry, {workspace, L.total_bytes}))
+        (scores && overlap(ry, {scores, n_tokens * (top_k + shexp) * 4})) ||
+        overlap(ry, {workspace, L.total_bytes}) || overlap(ry, {w_sh, one}) ||
+        overlap(ry, {w2_sh, one}))
         return fail(KQ_ERR_INVALID_ARG, "output overlaps an input or the workspace");
-    if (overlap({workspace, L.total_bytes}, {x, xb}) || overlap({workspace, L.total_bytes}, {w, wb}))
+    if (overlap({workspace, L.total_bytes}, {x, xb}) || overlap({workspace, L.total_bytes}, {w, wb}) ||
+        overlap({workspace, L.total_bytes}, {w_sh, one}) || overlap({workspace, L.total_bytes}, {w2_sh, one}))
         return fail(KQ_ERR_INVALID_ARG, "workspace overlaps an input");
     return KQ_OK;
 }
 
-kq_status kq_qmm_id(kq_type t, const void* w, int64_t n_experts, int64_t n, int64_t k,
-                    int64_t expert_stride, const void* x, kq_dtype x_dt, int x_layout,
-                    const uint32_t* ids, int64_t n_tokens, int64_t top_k, const float* scores,
-                    void* y, kq_dtype y_dt, void* workspace, size_t workspace_bytes,
-                    void* stream) {
+// The routed product; with shexp (mixed and slotted only) the last of top_k
+// + 1 slots per token is the shared expert w_sh.
+static kq_status qmm_id_impl(kq_type t, const void* w, int64_t n_experts, int64_t n, int64_t k,
+                             int64_t expert_stride, const void* w_sh, const void* x, kq_dtype x_dt,
+                             int x_layout, const uint32_t* ids, int64_t n_tokens, int64_t top_k,
+                             const float* scores, void* y, kq_dtype y_dt, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+    const int shexp = w_sh ? 1 : 0;
     const bool reuse = (x_layout & KQ_REUSE_SCHEDULE) != 0 && scores && n_tokens > 1;
     x_layout &= ~KQ_REUSE_SCHEDULE;
     if (x_layout != KQ_LAYOUT_SHARED && x_layout != KQ_LAYOUT_SLOTTED)
         return fail(KQ_ERR_INVALID_ARG, "unknown x layout");
-    const int64_t rows = (n_tokens > 0 && top_k > 0 && n_tokens <= INT32_MAX / top_k) ? n_tokens * top_k : 0;
+    const int64_t S = top_k + shexp;  // slots per token
+    const int64_t rows = (n_tokens > 0 && S > 0 && n_tokens <= INT32_MAX / S) ? n_tokens * S : 0;
     const int64_t x_rows = x_layout == KQ_LAYOUT_SHARED ? n_tokens : rows;
     const int64_t y_rows = scores ? n_tokens : rows;
     int64_t row_bytes;
     kq_status st = check_expert_call(t, w, nullptr, n_experts, n, k, expert_stride, x, x_dt, x_rows,
                                      ids, n_tokens, top_k, scores, y, y_dt, y_rows, workspace,
-                                     workspace_bytes, scores ? n : 0, row_bytes);
+                                     workspace_bytes, scores ? n : 0, row_bytes, shexp, w_sh);
     if (st) return st;
     hipStream_t s = (hipStream_t)stream;
     // one token, mixed: the slots are summed as their expert rows stream,
@@ -415,29 +437,34 @@ kq_status kq_qmm_id(kq_type t, const void* w, int64_t n_experts, int64_t n, int6
         d.ids = ids;
         d.scores = scores;
         d.n_experts = n_experts;
-        d.top_k = top_k;
+        d.top_k = S;
         d.y = y;
         d.y_dt = y_dt;
+        d.shexp = shexp;
+        d.w_sh = (const uint8_t*)w_sh;
         return launched(kq::launch_down_mix1(d, x_dt == KQ_F32, s));
     }
-    const kq::MoeLayout L = kq::moe_layout(n_experts, n_tokens, top_k, scores ? n : 0);
+    const kq::MoeLayout L = kq::moe_layout(n_experts + shexp, n_tokens, S, scores ? n : 0);
     int32_t* ws = (int32_t*)workspace;
     // the unmixed form's rows with an invalid id are poisoned by the route;
     // the mixed form's tokens by the mix
     hipError_t e = hipSuccess;
     if (!reuse)
-        e = scores ? kq::launch_route(ids, L.rows, top_k, n_experts, L, ws, s)
-                   : kq::launch_route(ids, L.rows, top_k, n_experts, L, ws, s, y, n, y_dt);
+        e = scores ? kq::launch_route(ids, L.rows, S, n_experts + shexp, L, ws, s, nullptr, 0, 0, shexp)
+                   : kq::launch_route(ids, L.rows, S, n_experts + shexp, L, ws, s, y, n, y_dt, shexp);
     if (e != hipSuccess) return launched(e);
     kq::SkinnyArgs a{};
     a.w = (const uint8_t*)w;
+    a.w_sh = (const uint8_t*)w_sh;
+    a.shexp = shexp;
+    a.n_experts = n_experts;
     a.row_bytes = row_bytes;
     a.expert_stride = expert_stride;
     a.n = n;
     a.k = k;
     a.x = x;
     a.x_row = k;
-    a.top_k = top_k;
+    a.top_k = S;
     a.shared_x = x_layout == KQ_LAYOUT_SHARED;
     a.one_x_row = a.shared_x && n_tokens == 1;
     a.ws = ws;
@@ -452,8 +479,8 @@ kq_status kq_qmm_id(kq_type t, const void* w, int64_t n_experts, int64_t n, int6
         a.y_row = n;
         e = kq::launch_skinny(t, x_dt, false, a, L.max_tiles, s);
         if (e != hipSuccess) return launched(e);
-        return launched(kq::launch_mix(ids, scores, n_tokens, top_k, n_experts, ws, slots, n, y,
-                                       y_dt, s));
+        return launched(kq::launch_mix(ids, scores, n_tokens, S, n_experts + shexp, ws, slots, n, y,
+                                       y_dt, s, shexp));
     }
     a.y = y;
     a.y_dt = y_dt;
@@ -461,20 +488,52 @@ kq_status kq_qmm_id(kq_type t, const void* w, int64_t n_experts, int64_t n, int6
     return launched(kq::launch_skinny(t, x_dt, false, a, L.max_tiles, s));
 }
 
-kq_status kq_moe_glu(kq_type t, const void* gate_w, const void* up_w, int64_t n_experts,
-                     int64_t n, int64_t k, int64_t expert_stride, const void* x, kq_dtype x_dt,
-                     const uint32_t* ids, int64_t n_tokens, int64_t top_k, int act, void* h,
-                     kq_dtype h_dt, void* workspace, size_t workspace_bytes, void* stream) {
-    if (act != KQ_ACT_SILU && act != KQ_ACT_GELU_TANH) return fail(KQ_ERR_UNSUPPORTED, "unknown GLU activation");
+kq_status kq_qmm_id(kq_type t, const void* w, int64_t n_experts, int64_t n, int64_t k,
+                    int64_t expert_stride, const void* x, kq_dtype x_dt, int x_layout,
+                    const uint32_t* ids, int64_t n_tokens, int64_t top_k, const float* scores,
+                    void* y, kq_dtype y_dt, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+    return qmm_id_impl(t, w, n_experts, n, k, expert_stride, nullptr, x, x_dt, x_layout, ids,
+                       n_tokens, top_k, scores, y, y_dt, workspace, workspace_bytes, stream);
+}
+
+kq_status kq_qmm_id_mix_shexp(kq_type t, const void* w, int64_t n_experts, int64_t n, int64_t k,
+                              int64_t expert_stride, const void* shexp_w, const void* x,
+                              kq_dtype x_dt, int flags, const uint32_t* ids, int64_t n_tokens,
+                              int64_t top_k, const float* scores, void* y, kq_dtype y_dt,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+    if (flags & ~KQ_REUSE_SCHEDULE) return fail(KQ_ERR_INVALID_ARG, "unknown flags");
+    if (!shexp_w) return fail(KQ_ERR_INVALID_ARG, "null shared-expert weights");
+    if (!scores) return fail(KQ_ERR_INVALID_ARG, "null scores");
+    return qmm_id_impl(t, w, n_experts, n, k, expert_stride, shexp_w, x, x_dt,
+                       KQ_LAYOUT_SLOTTED | flags, ids, n_tokens, top_k, scores, y, y_dt, workspace,
+                       workspace_bytes, stream);
+}
+
+static kq_status moe_glu_impl(kq_type t, const void* gate_w, const void* up_w, int64_t n_experts,
+                              int64_t n, int64_t k, int64_t expert_stride, const void* shexp_gate_w,
+                              const void* shexp_up_w, const void* x, kq_dtype x_dt,
+                              const uint32_t* ids, int64_t n_tokens, int64_t top_k, int act,
+                              float limit, void* h, kq_dtype h_dt, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+    if (act != KQ_ACT_SILU && act != KQ_ACT_GELU_TANH && act != KQ_ACT_SILU_LIMIT)
+        return fail(KQ_ERR_UNSUPPORTED, "unknown GLU activation");
+    if (act == KQ_ACT_SILU_LIMIT && !(limit > 0.0f && limit < __builtin_inff()))
+        return fail(KQ_ERR_INVALID_ARG, "silu_limit needs a finite limit > 0");
     if (!up_w) return fail(KQ_ERR_INVALID_ARG, "null up weights");
-    const int64_t rows = (n_tokens > 0 && top_k > 0 && n_tokens <= INT32_MAX / top_k) ? n_tokens * top_k : 0;
+    if ((shexp_gate_w == nullptr) != (shexp_up_w == nullptr))
+        return fail(KQ_ERR_INVALID_ARG, "shared-expert gate and up weights go together");
+    const int shexp = shexp_gate_w ? 1 : 0;
+    const int64_t S = top_k + shexp;
+    const int64_t rows = (n_tokens > 0 && S > 0 && n_tokens <= INT32_MAX / S) ? n_tokens * S : 0;
     int64_t row_bytes;
     kq_status st = check_expert_call(t, gate_w, up_w, n_experts, n, k, expert_stride, x, x_dt,
                                      n_tokens, ids, n_tokens, top_k, nullptr, h, h_dt, rows,
-                                     workspace, workspace_bytes, 0, row_bytes);
+                                     workspace, workspace_bytes, 0, row_bytes, shexp, shexp_gate_w,
+                                     shexp_up_w);
     if (st) return st;
     hipStream_t s = (hipStream_t)stream;
-    const kq::MoeLayout L = kq::moe_layout(n_experts, n_tokens, top_k, 0);
+    const kq::MoeLayout L = kq::moe_layout(n_experts + shexp, n_tokens, S, 0);
     int32_t* ws = (int32_t*)workspace;
     kq::SkinnyArgs a{};
     // one token with fp16 activations: each grid row is one slot, whose
@@ -482,22 +541,25 @@ kq_status kq_moe_glu(kq_type t, const void* gate_w, const void* up_w, int64_t n_
     const bool direct = n_tokens == 1 && t == KQ_Q4_K && x_dt == KQ_F16;
     if (direct) {
         a.ids = ids;
-        a.n_experts = n_experts;
         a.m = 1;
     } else {
-        hipError_t e = kq::launch_route(ids, L.rows, top_k, n_experts, L, ws, s, h, n, h_dt);
+        hipError_t e = kq::launch_route(ids, L.rows, S, n_experts + shexp, L, ws, s, h, n, h_dt, shexp);
         if (e != hipSuccess) return launched(e);
         a.ws = ws;
     }
+    a.n_experts = n_experts;
+    a.shexp = shexp;
     a.w = (const uint8_t*)gate_w;
     a.w2 = (const uint8_t*)up_w;
+    a.w_sh = (const uint8_t*)shexp_gate_w;
+    a.w2_sh = (const uint8_t*)shexp_up_w;
     a.row_bytes = row_bytes;
     a.expert_stride = expert_stride;
     a.n = n;
     a.k = k;
     a.x = x;
     a.x_row = k;
-    a.top_k = top_k;
+    a.top_k = S;
     a.shared_x = 1;
     a.one_x_row = n_tokens == 1;
     a.tiles_off = L.tiles_off;
@@ -508,8 +570,30 @@ kq_status kq_moe_glu(kq_type t, const void* gate_w, const void* up_w, int64_t n_
     a.y_dt = h_dt;
     a.y_row = n;
     a.act = act;
+    a.limit = limit;
     if (direct) return launched(kq::launch_moe_glu1(a, s));
     return launched(kq::launch_skinny(t, x_dt, true, a, L.max_tiles, s));
+}
+
+kq_status kq_moe_glu(kq_type t, const void* gate_w, const void* up_w, int64_t n_experts,
+                     int64_t n, int64_t k, int64_t expert_stride, const void* x, kq_dtype x_dt,
+                     const uint32_t* ids, int64_t n_tokens, int64_t top_k, int act, void* h,
+                     kq_dtype h_dt, void* workspace, size_t workspace_bytes, void* stream) {
+    if (act != KQ_ACT_SILU && act != KQ_ACT_GELU_TANH)
+        return fail(KQ_ERR_UNSUPPORTED, "unknown GLU activation (silu_limit: kq_moe_glu_ex)");
+    return moe_glu_impl(t, gate_w, up_w, n_experts, n, k, expert_stride, nullptr, nullptr, x, x_dt,
+                        ids, n_tokens, top_k, act, 0.0f, h, h_dt, workspace, workspace_bytes,
+                        stream);
+}
+
+kq_status kq_moe_glu_ex(kq_type t, const void* gate_w, const void* up_w, int64_t n_experts,
+                        int64_t n, int64_t k, int64_t expert_stride, const void* shexp_gate_w,
+                        const void* shexp_up_w, const void* x, kq_dtype x_dt, const uint32_t* ids,
+                        int64_t n_tokens, int64_t top_k, int act, float limit, void* h,
+                        kq_dtype h_dt, void* workspace, size_t workspace_bytes, void* stream) {
+    return moe_glu_impl(t, gate_w, up_w, n_experts, n, k, expert_stride, shexp_gate_w, shexp_up_w,
+                        x, x_dt, ids, n_tokens, top_k, act, limit, h, h_dt, workspace,
+                        workspace_bytes, stream);
 }
 
 }  // extern "C"

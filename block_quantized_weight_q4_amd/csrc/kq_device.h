@@ -169,9 +169,37 @@ __device__ __forceinline__ float gelu_tanh_fast(float z) {
     const float y2 = 1.5957691216057308f * z * (1.0f + 0.044715f * z * z);  // 2y
     return z / (1.0f + __expf(-y2));
 }
-// h = act(g) * u for the GLU epilogues; act is uniform over the launch
-__device__ __forceinline__ float glu_act(int act, float g, float u) {
+// h = act(g, u) for the GLU epilogues; act is uniform over the launch:
+// 0 silu(g) u, 1 gelu(g) u, 2 silu(min(g, limit)) clip(u, -limit, limit)
+// (mlx-kquant "bindings.cpp", moe_glu_gather_kq act='silu_limit'; the
+// comparisons keep a NaN u as NaN, and a NaN g takes the limit)
+__device__ __forceinline__ float glu_act(int act, float g, float u, float limit) {
+    if (act == 2) {
+        const float gc = g < limit ? g : limit;
+        const float uc = u < -limit ? -limit : (u > limit ? limit : u);
+        return silu_fast(gc) * uc;
+    }
     return (act == 1 ? gelu_tanh_fast(g) : silu_fast(g)) * u;
+}
+
+// ---------------------------------------------------------------- routing
+// Expert of routed row i of a routing with S slots per token.  With a shared
+// expert (shexp) the last slot of every token is expert n_experts (the shared
+// expert's own matrices) and ids holds the S - 1 routed ids per token; a
+// routed id >= n_experts is returned as 0xffffffff (out of range either way).
+__device__ __forceinline__ uint32_t slot_expert(const uint32_t* ids, int64_t i, int64_t S,
+                                                int shexp, int64_t n_experts) {
+    if (!shexp) return ids[i];
+    const int64_t t = i / S, r = i - t * S;
+    if (r == S - 1) return (uint32_t)n_experts;
+    const uint32_t e = ids[t * (S - 1) + r];
+    return (int64_t)e < n_experts ? e : 0xffffffffu;
+}
+// Weights of expert e: the stacked experts, or the shared expert's matrix
+// for e == n_experts.
+__device__ __forceinline__ const uint8_t* expert_base(const uint8_t* w, const uint8_t* w_sh,
+                                                      int64_t e, int64_t n_experts, int64_t stride) {
+    return (w_sh && e == n_experts) ? w_sh : w + e * stride;
 }
 
 }  // namespace kq

@@ -48,7 +48,13 @@ struct SkinnyArgs {
     int y_dt;              // output dtype
     int64_t y_row;         // elements between output rows
     int64_t rows_cap;      // routed: most rows any schedule tile can hold
-    int act;               // GLU: KQ_ACT_SILU or KQ_ACT_GELU_TANH
+    int act;               // GLU: KQ_ACT_SILU, KQ_ACT_GELU_TANH or KQ_ACT_SILU_LIMIT
+    float limit;           // GLU: the bound of KQ_ACT_SILU_LIMIT
+    // shared expert: the last of top_k slots per token is expert n_experts,
+    // whose matrices are w_sh (and w2_sh for the GLU's up projection)
+    int shexp;
+    const uint8_t* w_sh;
+    const uint8_t* w2_sh;
     // set by the launchers of the matrix-core kernels
     int xch;               // super-blocks of activations staged per chunk
     int xstride;           // elements (or bytes) between staged activation rows
@@ -68,6 +74,8 @@ struct DownMixArgs {
     int64_t n_experts, top_k;
     void* y;                // [n]
     int y_dt;
+    int shexp;              // the last of top_k slots is the shared expert w_sh
+    const uint8_t* w_sh;
 };
 hipError_t launch_down_mix1(const DownMixArgs& a, bool x_f32, hipStream_t s);
 // Single-token gate/up with SiLU, expert ids read directly (moe_dec.hip).
@@ -124,12 +132,14 @@ hipError_t launch_gemm(int codec, int x_dt, const void* w, int64_t n, int64_t k,
 // Rows of poison_y are NaN-ed by the routing rule: below 32 tokens those with
 // an id >= n_experts, from 32 tokens on all of them if any id is out of range
 // or repeated within a token (then the schedule has no tiles).
+// With shexp, rows counts top_k slots per token of which the last is the
+// shared expert (routed ids: top_k - 1 per token) and n_experts counts it.
 hipError_t launch_route(const uint32_t* ids, int64_t rows, int64_t top_k, int64_t n_experts,
                         const MoeLayout& L, int32_t* ws, hipStream_t s, void* poison_y = nullptr,
-                        int64_t poison_n = 0, int poison_dt = 0);
+                        int64_t poison_n = 0, int poison_dt = 0, int shexp = 0);
 hipError_t launch_mix(const uint32_t* ids, const float* scores, int64_t n_tokens, int64_t top_k,
                       int64_t n_experts, const int32_t* ws, const float* slots, int64_t n,
-                      void* y, int y_dt, hipStream_t s);
+                      void* y, int y_dt, hipStream_t s, int shexp = 0);
 
 
 }  // namespace kq

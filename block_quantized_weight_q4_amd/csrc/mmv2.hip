@@ -69,7 +69,9 @@ __global__ __launch_bounds__(64 * W) void mmv2_q4k_f16_kernel(SkinnyArgs a) {
     // size): piece p = 64*i + lane -> matrix m, row r, piece q of the row's chunk.
     const uint8_t* wbase[NM];
 #pragma unroll
-    for (int m = 0; m < NM; ++m) wbase[m] = (GLU && m ? a.w2 : a.w) + expert * a.expert_stride + n0 * a.row_bytes;
+    for (int m = 0; m < NM; ++m)
+        wbase[m] = expert_base(GLU && m ? a.w2 : a.w, GLU && m ? a.w2_sh : a.w_sh, expert,
+                               a.n_experts, a.expert_stride) + n0 * a.row_bytes;
     uint32_t woff[WL_PER_WAVE], wq16[WL_PER_WAVE];
     int wmat[WL_PER_WAVE];
 #pragma unroll
@@ -210,7 +212,7 @@ __global__ __launch_bounds__(64 * W) void mmv2_q4k_f16_kernel(SkinnyArgs a) {
         const int64_t orow = perm ? (int64_t)perm[row0 + idx] : row0 + idx;
         if (GLU) {
             const int64_t n = n0 + n_l;
-            if (n < a.n) store_val(a.y, orow * a.y_row + n, a.y_dt, glu_act(a.act, acc[0][v], acc[1][v]));
+            if (n < a.n) store_val(a.y, orow * a.y_row + n, a.y_dt, glu_act(a.act, acc[0][v], acc[1][v], a.limit));
         } else {
 #pragma unroll
             for (int m = 0; m < NM; ++m) {

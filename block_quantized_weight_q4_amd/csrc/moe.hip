@@ -38,7 +38,7 @@ __global__ __launch_bounds__(256) void route_kernel(const uint32_t* __restrict__
                                                     int64_t counts_off, int64_t offsets_off,
                                                     int64_t perm_off, int64_t tiles_off,
                                                     int id_bits, void* __restrict__ poison_y,
-                                                    int64_t poison_n, int poison_dt) {
+                                                    int64_t poison_n, int poison_dt, int shexp) {
     extern __shared__ int32_t lds[];
     int32_t* counts = lds;                  // [E]
     int32_t* cursor = lds + n_experts;      // [E]
@@ -46,12 +46,16 @@ __global__ __launch_bounds__(256) void route_kernel(const uint32_t* __restrict__
     __shared__ int32_t n_invalid, n_tiles, n_repeat;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const bool mm_rule = rows / top_k >= kMmIdMinTokens;
+    // expert of routed row i: with a shared expert it is the last slot of
+    // each token (expert n_experts - 1), the ids hold the others
+    const int64_t real_e = n_experts - shexp;
+    auto expert_of = [&](int64_t i) { return slot_expert(ids, i, top_k, shexp, real_e); };
 
     for (int64_t e = tid; e < n_experts; e += 256) counts[e] = 0;
     if (tid == 0) n_invalid = 0, n_repeat = 0;
     __syncthreads();
     for (int64_t i = tid; i < rows; i += 256) {
-        const uint32_t e = ids[i];
+        const uint32_t e = expert_of(i);
         if ((int64_t)e < n_experts) atomicAdd(&counts[e], 1);
         else atomicAdd(&n_invalid, 1);
     }
@@ -102,7 +106,7 @@ __global__ __launch_bounds__(256) void route_kernel(const uint32_t* __restrict__
     if (wave == 0) {
         for (int64_t base = 0; base < rows; base += 64) {
             const int64_t i = base + lane;
-            const uint32_t e = i < rows ? ids[i] : 0xffffffffu;
+            const uint32_t e = i < rows ? expert_of(i) : 0xffffffffu;
             const bool valid = (int64_t)e < n_experts;
             uint64_t same = __ballot(valid);
             for (int b = 0; b < id_bits; ++b) {
@@ -130,7 +134,7 @@ __global__ __launch_bounds__(256) void route_kernel(const uint32_t* __restrict__
         int32_t rep = 0;
         for (int64_t p = tid; p + 1 < valid; p += 256) {
             const int32_t a = ws[perm_off + p], b = ws[perm_off + p + 1];
-            rep += ids[a] == ids[b] && a / top_k == b / top_k;
+            rep += expert_of(a) == expert_of(b) && a / top_k == b / top_k;
         }
         if (rep) atomicAdd(&n_repeat, rep);
     }
@@ -143,7 +147,7 @@ __global__ __launch_bounds__(256) void route_kernel(const uint32_t* __restrict__
     if (poison_y && n_invalid + n_repeat > 0) {
         const float v = __builtin_nanf("");
         for (int64_t i = 0; i < rows; ++i) {
-            if (!poison_all && (int64_t)ids[i] < n_experts) continue;
+            if (!poison_all && (int64_t)expert_of(i) < n_experts) continue;
             for (int64_t j = tid; j < poison_n; j += 256) {
                 if (poison_dt == F32) store_out<F32>(poison_y, i * poison_n + j, v);
                 else if (poison_dt == F16) store_out<F16>(poison_y, i * poison_n + j, v);
@@ -155,13 +159,13 @@ __global__ __launch_bounds__(256) void route_kernel(const uint32_t* __restrict__
 
 hipError_t launch_route(const uint32_t* ids, int64_t rows, int64_t top_k, int64_t n_experts,
                         const MoeLayout& L, int32_t* ws, hipStream_t s, void* poison_y,
-                        int64_t poison_n, int poison_dt) {
+                        int64_t poison_n, int poison_dt, int shexp) {
     int bits = 1;
     while ((1ll << bits) < n_experts) ++bits;
     const size_t lds = (size_t)3 * n_experts * sizeof(int32_t);
     hipLaunchKernelGGL(route_kernel, dim3(1), dim3(256), lds, s, ids, rows, top_k, n_experts, ws,
                        L.counts_off, L.offsets_off, L.perm_off, L.tiles_off, bits, poison_y,
-                       poison_n, poison_dt);
+                       poison_n, poison_dt, shexp);
     return hipGetLastError();
 }
 
@@ -175,7 +179,8 @@ __global__ __launch_bounds__(256) void mix_kernel(const uint32_t* __restrict__ i
                                                   int64_t n_tokens, int64_t top_k,
                                                   int64_t n_experts, const int32_t* __restrict__ n_defects,
                                                   const float* __restrict__ slots,
-                                                  int64_t n, void* __restrict__ y, int y_dt) {
+                                                  int64_t n, void* __restrict__ y, int y_dt,
+                                                  int shexp) {
     const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (j >= n) return;
     const bool all_bad = n_tokens >= kMmIdMinTokens && *n_defects > 0;
@@ -184,7 +189,7 @@ __global__ __launch_bounds__(256) void mix_kernel(const uint32_t* __restrict__ i
         bool bad = all_bad;
         for (int64_t r = 0; r < top_k; ++r) {
             const int64_t row = t * top_k + r;
-            bad |= (int64_t)ids[row] >= n_experts;
+            bad |= (int64_t)slot_expert(ids, row, top_k, shexp, n_experts - shexp) >= n_experts;
             acc = __builtin_fmaf(scores[row], slots[row * n + j], acc);
         }
         const float v = bad ? __builtin_nanf("") : acc;
@@ -196,11 +201,11 @@ __global__ __launch_bounds__(256) void mix_kernel(const uint32_t* __restrict__ i
 
 hipError_t launch_mix(const uint32_t* ids, const float* scores, int64_t n_tokens, int64_t top_k,
                       int64_t n_experts, const int32_t* ws, const float* slots, int64_t n,
-                      void* y, int y_dt, hipStream_t s) {
+                      void* y, int y_dt, hipStream_t s, int shexp) {
     const int64_t gy = n_tokens < 65535 ? n_tokens : 65535;
     const dim3 grid((unsigned)((n + 255) / 256), (unsigned)gy);
     hipLaunchKernelGGL(mix_kernel, grid, dim3(256), 0, s, ids, scores, n_tokens, top_k, n_experts,
-                       ws + 1, slots, n, y, y_dt);
+                       ws + 1, slots, n, y, y_dt, shexp);
     return hipGetLastError();
 }
 

@@ -84,9 +84,11 @@ __global__ __launch_bounds__(64 * W) void moe_down_mix1_kernel(DownMixArgs a) {
     const int nch = (nsb + C - 1) / C;         // chunks per slot
     const int nq = (int)a.top_k * nch;         // chunks of the whole token
 
-    // a token with an invalid expert id has NaN outputs
+    // a token with an invalid expert id has NaN outputs (with a shared
+    // expert, slot top_k - 1 is expert n_experts)
     bool bad = false;
-    for (int r = 0; r < a.top_k; ++r) bad |= a.ids[r] >= (uint64_t)a.n_experts;
+    for (int r = 0; r < a.top_k; ++r)
+        bad |= (int64_t)slot_expert(a.ids, r, a.top_k, a.shexp, a.n_experts) >= a.n_experts + a.shexp;
     if (bad) {
         if (tid < 16 && n0 + tid < a.n) store_val(a.y, n0 + tid, a.y_dt, __builtin_nanf(""));
         return;
@@ -107,7 +109,9 @@ __global__ __launch_bounds__(64 * W) void moe_down_mix1_kernel(DownMixArgs a) {
         uint8_t* dst = smem + (qc & 1) * L::BUF;
         const int r = qc / nch, s0 = (qc - r * nch) * C;
         const int nsc = nsb - s0 < C ? nsb - s0 : C;
-        const uint8_t* wbase = a.w + (int64_t)a.ids[r] * a.expert_stride + n0 * a.row_bytes + (uint32_t)s0 * 144u;
+        const uint8_t* wbase = expert_base(a.w, a.w_sh, slot_expert(a.ids, r, a.top_k, a.shexp, a.n_experts),
+                                           a.n_experts, a.expert_stride) +
+                               n0 * a.row_bytes + (uint32_t)s0 * 144u;
         const uint32_t climit = (uint32_t)nsc * 144u;
 #pragma unroll
         for (int j = 0; j < WL_PER_WAVE; ++j) {
@@ -262,13 +266,13 @@ __global__ __launch_bounds__(64 * W) void moe_glu1_kernel(SkinnyArgs a) {
     const int nsb = (int)(a.k / 256);
     const int nchunks = (nsb + C - 1) / C;
 
-    const uint32_t e = a.ids[slot];
-    if (e >= (uint64_t)a.n_experts) {
+    const uint32_t e = slot_expert(a.ids, slot, a.top_k, a.shexp, a.n_experts);
+    if ((int64_t)e >= a.n_experts + a.shexp) {
         if (tid < 16 && n0 + tid < a.n) store_val(a.y, slot * a.y_row + n0 + tid, a.y_dt, __builtin_nanf(""));
         return;
     }
-    const uint8_t* wb[2] = {a.w + (int64_t)e * a.expert_stride + n0 * a.row_bytes,
-                            a.w2 + (int64_t)e * a.expert_stride + n0 * a.row_bytes};
+    const uint8_t* wb[2] = {expert_base(a.w, a.w_sh, e, a.n_experts, a.expert_stride) + n0 * a.row_bytes,
+                            expert_base(a.w2, a.w2_sh, e, a.n_experts, a.expert_stride) + n0 * a.row_bytes};
     uint32_t woff[WL_PER_WAVE], wq16[WL_PER_WAVE];
     int wset[WL_PER_WAVE];
 #pragma unroll
@@ -383,7 +387,7 @@ __global__ __launch_bounds__(64 * W) void moe_glu1_kernel(SkinnyArgs a) {
         acc[st] += __shfl_xor(acc[st], 32);
     }
     const int64_t n = n0 + n_l;
-    if (g == 0 && n < a.n) store_val(a.y, slot * a.y_row + n, a.y_dt, glu_act(a.act, acc[0], acc[1]));
+    if (g == 0 && n < a.n) store_val(a.y, slot * a.y_row + n, a.y_dt, glu_act(a.act, acc[0], acc[1], a.limit));
 }
 
 template <int C, int W>

@@ -121,10 +121,11 @@ __global__ __launch_bounds__(64 * W) void moe_mm_kernel(SkinnyArgs a) {
     const uint8_t* wrow[2];
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-        const uint8_t* base = (GLU && b == 1) ? a.w2 : a.w;
+        const uint8_t* base = expert_base((GLU && b == 1) ? a.w2 : a.w, (GLU && b == 1) ? a.w2_sh : a.w_sh,
+                                          expert, a.n_experts, a.expert_stride);
         int64_t n = n0 + (GLU ? 16 * wave : 16 * (2 * wave + b)) + n_l;
         if (n >= a.n) n = a.n - 1;
-        wrow[b] = base + expert * a.expert_stride + n * a.row_bytes;
+        wrow[b] = base + n * a.row_bytes;
     }
 
     float4_t acc[2][2];
@@ -281,7 +282,7 @@ __global__ __launch_bounds__(64 * W) void moe_mm_kernel(SkinnyArgs a) {
                 const int64_t n = n0 + 16 * wave + n_l;
                 if (n < a.n)
                     store_val(a.y, orow * a.y_row + n, a.y_dt,
-                              glu_act(a.act, back(acc[0][mt][v]), back(acc[1][mt][v])));
+                              glu_act(a.act, back(acc[0][mt][v]), back(acc[1][mt][v]), a.limit));
             } else {
 #pragma unroll
                 for (int b = 0; b < 2; ++b) {

@@ -160,8 +160,9 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs a) {
         nrows = a.m - row0 < MB ? a.m - row0 : MB;
     }
 
-    const uint8_t* wrow = a.w + expert * a.expert_stride + j * a.row_bytes;
-    const uint8_t* wrow2 = GLU ? a.w2 + expert * a.expert_stride + j * a.row_bytes : nullptr;
+    const uint8_t* wrow = expert_base(a.w, a.w_sh, expert, a.n_experts, a.expert_stride) + j * a.row_bytes;
+    const uint8_t* wrow2 =
+        GLU ? expert_base(a.w2, a.w2_sh, expert, a.n_experts, a.expert_stride) + j * a.row_bytes : nullptr;
     const int64_t nchunks = a.k / 32;
 
     for (int64_t sub = 0; sub < nrows; sub += MB) {
@@ -210,7 +211,7 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs a) {
             if (i < cnt) {
                 const float g = wave_sum(acc[i]);
                 float v = g;
-                if (GLU) v = glu_act(a.act, g, wave_sum(acc2[i]));
+                if (GLU) v = glu_act(a.act, g, wave_sum(acc2[i]), a.limit);
                 if (lane == 0) store_any(a.y, orow[i] * a.y_row + j, a.y_dt, v);
             }
         }

@@ -21,8 +21,9 @@ __all__ = [
     "KQError", "TYPES", "lib", "kq_status_string", "kq_last_error", "kq_qk", "kq_block_bytes",
     "kq_row_bytes", "kq_dequantize", "kq_quantize", "kq_validate_tq1", "kq_qmv", "kq_qmm", "kq_qmm_workspace_bytes", "kq_qmm_ws",
     "kq_qmm_noalloc_max_bytes", "kq_qmm_noalloc", "kq_moe_workspace_bytes", "kq_moe_route",
-    "kq_qmm_id", "kq_moe_glu", "moe_schedule", "SYMBOLS", "LAYOUT_SHARED", "LAYOUT_SLOTTED", "REUSE_SCHEDULE",
-    "ACT_SILU", "ACT_GELU_TANH", "MOE_TILE_ROWS",
+    "kq_qmm_id", "kq_moe_glu", "kq_moe_glu_ex", "kq_qmm_id_mix_shexp", "moe_schedule", "SYMBOLS",
+    "LAYOUT_SHARED", "LAYOUT_SLOTTED", "REUSE_SCHEDULE", "ACT_SILU", "ACT_GELU_TANH",
+    "ACT_SILU_LIMIT", "MOE_TILE_ROWS",
 ]
 
 TYPES = {"q4_k": 0, "q8_0": 1, "tq1_g128": 2}
@@ -31,6 +32,7 @@ LAYOUT_SHARED, LAYOUT_SLOTTED = 0, 1
 REUSE_SCHEDULE = 0x100  # OR into the layout of a mixed kq_qmm_id: keep the workspace schedule
 ACT_SILU = 0
 ACT_GELU_TANH = 1
+ACT_SILU_LIMIT = 2
 MOE_TILE_ROWS = 32
 
 # Every function include/kq.h declares.
@@ -38,7 +40,7 @@ SYMBOLS = (
     "kq_status_string", "kq_last_error", "kq_qk", "kq_block_bytes", "kq_row_bytes",
     "kq_dequantize", "kq_quantize", "kq_validate_tq1", "kq_qmv", "kq_qmm",
     "kq_qmm_workspace_bytes", "kq_qmm_ws", "kq_qmm_noalloc_max_bytes", "kq_qmm_noalloc", "kq_moe_workspace_bytes", "kq_moe_route",
-    "kq_qmm_id", "kq_moe_glu",
+    "kq_qmm_id", "kq_moe_glu", "kq_moe_glu_ex", "kq_qmm_id_mix_shexp",
 )
 
 
@@ -100,6 +102,12 @@ def lib():
     L.kq_moe_glu.restype = i32
     L.kq_moe_glu.argtypes = [i32, P, P, i64, i64, i64, i64, P, i32, P, i64, i64, i32, P, i32, P,
                              C.c_size_t, P]
+    L.kq_moe_glu_ex.restype = i32
+    L.kq_moe_glu_ex.argtypes = [i32, P, P, i64, i64, i64, i64, P, P, P, i32, P, i64, i64, i32,
+                                C.c_float, P, i32, P, C.c_size_t, P]
+    L.kq_qmm_id_mix_shexp.restype = i32
+    L.kq_qmm_id_mix_shexp.argtypes = [i32, P, i64, i64, i64, i64, P, P, i32, i32, P, i64, i64, P,
+                                      P, i32, P, C.c_size_t, P]
     _lib = L
     return L
 
@@ -281,6 +289,40 @@ def kq_moe_glu(kind: str, gate_w, up_w, n_experts: int, n: int, k: int, expert_s
                             _ptr(workspace), workspace.numel() * workspace.element_size(),
                             _stream(gate_w, x, h)))
     return h
+
+
+def kq_moe_glu_ex(kind: str, gate_w, up_w, n_experts: int, n: int, k: int, expert_stride: int,
+                  x, ids, n_tokens: int, top_k: int, h, workspace, act: int = ACT_SILU,
+                  limit: float = 0.0, shexp_gate_w=None, shexp_up_w=None):
+    one = _rows_bytes(kind, n, k)
+    wneed = None if one is None else (n_experts - 1) * expert_stride + one
+    S = top_k + (1 if shexp_gate_w is not None else 0)
+    _tensors(("gate_w", gate_w, wneed), ("up_w", up_w, wneed), ("shexp_gate_w", shexp_gate_w, one),
+             ("shexp_up_w", shexp_up_w, one), ("x", x, n_tokens * k * x.element_size()),
+             ("ids", ids, n_tokens * top_k * 4), ("h", h, n_tokens * S * n * h.element_size()),
+             ("workspace", workspace, None))
+    _check(lib().kq_moe_glu_ex(TYPES[kind], _ptr(gate_w), _ptr(up_w), n_experts, n, k,
+                               expert_stride, _ptr(shexp_gate_w), _ptr(shexp_up_w), _ptr(x), _dt(x),
+                               _ptr(ids), n_tokens, top_k, act, float(limit), _ptr(h), _dt(h),
+                               _ptr(workspace), workspace.numel() * workspace.element_size(),
+                               _stream(gate_w, x, h)))
+    return h
+
+
+def kq_qmm_id_mix_shexp(kind: str, w, n_experts: int, n: int, k: int, expert_stride: int,
+                        shexp_w, x, ids, n_tokens: int, top_k: int, scores, y, workspace,
+                        flags: int = 0):
+    one = _rows_bytes(kind, n, k)
+    _tensors(("w", w, None if one is None else (n_experts - 1) * expert_stride + one),
+             ("shexp_w", shexp_w, one), ("x", x, n_tokens * (top_k + 1) * k * x.element_size()),
+             ("ids", ids, n_tokens * top_k * 4), ("scores", scores, n_tokens * (top_k + 1) * 4),
+             ("y", y, n_tokens * n * y.element_size()), ("workspace", workspace, None))
+    _check(lib().kq_qmm_id_mix_shexp(TYPES[kind], _ptr(w), n_experts, n, k, expert_stride,
+                                     _ptr(shexp_w), _ptr(x), _dt(x), flags, _ptr(ids), n_tokens,
+                                     top_k, _ptr(scores), _ptr(y), _dt(y), _ptr(workspace),
+                                     workspace.numel() * workspace.element_size(),
+                                     _stream(w, x, y)))
+    return y
 
 
 def moe_schedule(workspace, n_experts: int, n_tokens: int, top_k: int) -> dict:

@@ -76,8 +76,12 @@ enum { KQ_LAYOUT_SHARED = 0, KQ_LAYOUT_SLOTTED = 1, KQ_REUSE_SCHEDULE = 0x100 };
  * 'gelu' (the tanh approximation).
  *   KQ_ACT_SILU       silu(z) = z / (1 + e^-z)
  *   KQ_ACT_GELU_TANH  gelu(z) = z/2 * (1 + tanh(sqrt(2/pi) * (z + 0.044715 z^3)))
- * Any other value -> KQ_ERR_UNSUPPORTED. */
-enum { KQ_ACT_SILU = 0, KQ_ACT_GELU_TANH = 1 };
+ *   KQ_ACT_SILU_LIMIT h = silu(min(g, limit)) * clip(u, -limit, limit)
+ *                     (act='silu_limit', deepseek-v4 LimitedSwiGLU; limit > 0;
+ *                     kq_moe_glu_ex only, as it takes the limit)
+ * The page's 'swiglu_clamp' (gpt-oss) is for mxfp4/nvfp4 weights only and is
+ * not offered for these codecs.  Any other value -> KQ_ERR_UNSUPPORTED. */
+enum { KQ_ACT_SILU = 0, KQ_ACT_GELU_TANH = 1, KQ_ACT_SILU_LIMIT = 2 };
 
 /* Human-readable name of a status code (static storage). */
 const char* kq_status_string(kq_status s);
@@ -348,6 +352,54 @@ kq_status kq_moe_glu(kq_type t, const void* gate_w, const void* up_w, int64_t n_
                      int64_t n, int64_t k, int64_t expert_stride, const void* x, kq_dtype x_dt,
                      const uint32_t* ids, int64_t n_tokens, int64_t top_k, int act, void* h,
                      kq_dtype h_dt, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kq_moe_glu_ex -- kq_moe_glu with every activation (KQ_ACT_SILU_LIMIT takes
+ * `limit`) and an optional shared expert folded in as one extra, last slot.
+ * mlx-kquant "bindings.cpp", moe_glu_gather_kq (act, limit) and
+ * moe_glu_gather_shexp_kq (the block's shared expert as slot top_k, fed by
+ * single-expert matrices row-shape-matched to the expert stack).
+ *
+ *   shexp_gate_w, shexp_up_w  [n, k/QK blocks] of type t (both, or both NULL)
+ *   h   [n_tokens, top_k, n] without a shared expert, [n_tokens, top_k + 1, n]
+ *       with one (slot top_k: act(W_sg x_t, W_su x_t))
+ *   workspace  kq_moe_workspace_bytes(n_experts + 1, n_tokens, top_k + 1, 0)
+ *       with a shared expert (it is routed as one more expert and slot)
+ * The shared slot is never invalid; routed ids poison h by the rule of
+ * kq_qmm_id.  Errors as kq_moe_glu; KQ_ACT_SILU_LIMIT with a limit that is
+ * not a finite value > 0, or one of the two shared matrices NULL ->
+ * KQ_ERR_INVALID_ARG.
+ */
+kq_status kq_moe_glu_ex(kq_type t, const void* gate_w, const void* up_w, int64_t n_experts,
+                        int64_t n, int64_t k, int64_t expert_stride, const void* shexp_gate_w,
+                        const void* shexp_up_w, const void* x, kq_dtype x_dt, const uint32_t* ids,
+                        int64_t n_tokens, int64_t top_k, int act, float limit, void* h,
+                        kq_dtype h_dt, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kq_qmm_id_mix_shexp -- the mixed down projection with the shared expert
+ * as the last slot.  mlx-kquant "bindings.cpp", gather_qmv_mix_kq (every
+ * slot, the last being the shared expert, accumulated in f32 weighted by its
+ * score, replacing gather + weighted sum + shared add).
+ *
+ *   w        [n_experts][n, k/QK blocks], experts expert_stride apart
+ *   shexp_w  [n, k/QK blocks] of type t
+ *   x        [n_tokens, top_k + 1, k] (slotted; slot top_k feeds shexp_w)
+ *   ids      [n_tokens, top_k] uint32 (the routed slots)
+ *   scores   [n_tokens, top_k + 1] float32 (the last: the shared expert's)
+ *   y        [n_tokens, n]: y[t] = sum over slots r in order of
+ *            scores[t,r] * (W_r x[t,r]), W_r = W[ids[t,r]] or shexp_w
+ *   flags    0 or KQ_REUSE_SCHEDULE (after a kq_moe_glu_ex call with the
+ *            same shared-expert layout, ids, n_tokens and top_k)
+ *   workspace  kq_moe_workspace_bytes(n_experts + 1, n_tokens, top_k + 1, n)
+ * Invalid routed ids poison as in kq_qmm_id's mixed form.  Errors as
+ * kq_qmm_id; NULL shexp_w or scores, unknown flags -> KQ_ERR_INVALID_ARG.
+ */
+kq_status kq_qmm_id_mix_shexp(kq_type t, const void* w, int64_t n_experts, int64_t n, int64_t k,
+                              int64_t expert_stride, const void* shexp_w, const void* x,
+                              kq_dtype x_dt, int flags, const uint32_t* ids, int64_t n_tokens,
+                              int64_t top_k, const float* scores, void* y, kq_dtype y_dt,
+                              void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -300,9 +300,11 @@ def test_single_token_invalid_id_poisons(kq, x_dt, layout):
         assert np.isnan(got[1]).all() and not np.isnan(got[[0, 2]]).any()
 
 
-def _check_glu(h, ref, tau, h_dt, what, act=0):
+def _check_glu(h, ref, tau, h_dt, what, act=0, limit=0.0):
     """act 0: silu (|silu'| < 1.1); act 1: gelu, tanh approximation
-    (|gelu'| < 1.13)."""
+    (|gelu'| < 1.13); act 2: silu(min(g, limit)) * clip(u, -limit, limit),
+    whose derivatives are bounded by those of silu(g) * u (min and clip are
+    1-Lipschitz)."""
     g, u, sg, su = ref["g"], ref["u"], ref["sg"], ref["su"]
     assert not np.isnan(h).any(), what
     if h_dt == "f16":
@@ -314,6 +316,9 @@ def _check_glu(h, ref, tau, h_dt, what, act=0):
     with np.errstate(over="ignore"):
         if act == 1:
             a_g, dmax = 0.5 * g * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (g + 0.044715 * g ** 3))), 1.13
+        elif act == 2:
+            gc = np.minimum(g, limit)
+            a_g, dmax = gc / (1.0 + np.exp(-gc)), 1.1
         else:
             a_g, dmax = g / (1.0 + np.exp(-g)), 1.1
     # the computed h may be off by the product tolerance, and storing it
@@ -449,3 +454,110 @@ def test_moe_c4_prefill_sampled_tokens(kq, c4_dev):
     g = oracle.moe_glu("q4_k", c["gate"], c["up"], c["n_experts"], c["ffn"], c["hidden"],
                        c["gate_stride"], c["x"][sel], "f16", c["ids"][sel], len(sel), c["top_k"])
     _check_glu(h[sel], g, TAU["f16"], "f32", "moe C4 prefill h")
+
+
+# ---------------------------------------------------------------- silu_limit, shared expert
+def _shexp_inputs(kind, E, n, k, T, top_k, seed, x_dt="f16"):
+    rng = synth.rng_for(seed)
+    gate = synth.weight_blocks(kind, rng, E * n, k)
+    up = synth.weight_blocks(kind, rng, E * n, k)
+    sg = synth.weight_blocks(kind, rng, n, k)
+    su = synth.weight_blocks(kind, rng, n, k)
+    stride = n * synth.row_bytes(kind, k)
+    ids = _ids(rng, T, E, top_k)
+    x = synth.activations(rng, (T, k), x_dt)
+    return rng, gate, up, sg, su, stride, ids, x
+
+
+@pytest.mark.parametrize("kind", ["q4_k", "q8_0", "tq1_g128"])
+@pytest.mark.parametrize("x_dt", ["f16", "f32"])
+@pytest.mark.parametrize("T", [1, 9, 40])
+@pytest.mark.parametrize("shexp,act,limit", [(False, 2, 5.0), (True, 2, 5.0), (True, 0, 0.0)])
+def test_moe_glu_ex(kq, kind, x_dt, T, shexp, act, limit):
+    """kq_moe_glu_ex: silu_limit (mlx-kquant moe_glu_gather_kq act='silu_limit')
+    and the shared expert as the last slot (moe_glu_gather_shexp_kq), against
+    the oracle; one token takes the direct single-token kernels for Q4_K with
+    fp16 activations."""
+    E, top_k = 6, 3
+    n, k = 80, {"q4_k": 512, "q8_0": 96, "tq1_g128": 256}[kind]
+    rng, gate, up, sg, su, stride, ids, x = _shexp_inputs(kind, E, n, k, T, top_k, 600 + T, x_dt)
+    S = top_k + (1 if shexp else 0)
+    _say("moe_glu_ex", kind, x_dt, T, shexp, act)
+    ws = _ws(kq, E + (1 if shexp else 0), T, S)
+    h = empty((T, S, n), "f32")
+    kq.kq_moe_glu_ex(kind, to_dev(gate), to_dev(up), E, n, k, stride, to_dev(x, x_dt), to_dev(ids),
+                     T, top_k, h, ws, act, limit, to_dev(sg) if shexp else None,
+                     to_dev(su) if shexp else None)
+    torch.cuda.synchronize()
+    ref = oracle.moe_glu_ex(kind, gate, up, E, n, k, stride, x, x_dt, ids, T, top_k, act, limit,
+                            sg if shexp else None, su if shexp else None)
+    _check_glu(to_f64(h), ref, TAU[x_dt], "f32", f"glu_ex {kind} {x_dt} T={T}", act=act, limit=limit)
+
+
+@pytest.mark.parametrize("kind", ["q4_k", "q8_0", "tq1_g128"])
+@pytest.mark.parametrize("x_dt", ["f16", "f32"])
+@pytest.mark.parametrize("T", [1, 5, 40])
+def test_qmm_id_mix_shexp(kq, kind, x_dt, T):
+    """kq_qmm_id_mix_shexp (mlx-kquant gather_qmv_mix_kq): the routed slots and
+    the shared expert's last slot mixed by score, against the oracle."""
+    E, top_k, n = 6, 3, 72
+    k = {"q4_k": 512, "q8_0": 160, "tq1_g128": 256}[kind]
+    rng = synth.rng_for(700 + T)
+    w = synth.weight_blocks(kind, rng, E * n, k)
+    wsh = synth.weight_blocks(kind, rng, n, k)
+    stride = n * synth.row_bytes(kind, k)
+    ids = _ids(rng, T, E, top_k)
+    x = synth.activations(rng, (T * (top_k + 1), k), x_dt)
+    scores = rng.uniform(0.05, 1.0, size=(T, top_k + 1)).astype(np.float32)
+    _say("mix shexp", kind, x_dt, T)
+    y = empty((T, n), "f32")
+    ws = _ws(kq, E + 1, T, top_k + 1, n)
+    kq.kq_qmm_id_mix_shexp(kind, to_dev(w), E, n, k, stride, to_dev(wsh), to_dev(x, x_dt),
+                           to_dev(ids), T, top_k, to_dev(scores), y, ws)
+    torch.cuda.synchronize()
+    ref, s = oracle.qmm_id_mix_shexp(kind, w, E, n, k, stride, wsh, x, x_dt, ids, T, top_k, scores)
+    check_tol(to_f64(y), ref, s, TAU[x_dt], f"mix shexp {kind} {x_dt} T={T}")
+
+
+@pytest.mark.parametrize("T", [1, 20, 40])
+def test_shexp_layer_reuses_schedule(kq, T):
+    """A layer with a shared expert as the benchmark would run it: the GLU
+    builds the schedule (one more expert and slot), the down projection keeps
+    it; the down output equals a rebuilt-schedule call bit for bit and the
+    oracle on the GPU's h.  From 32 tokens on a repeated routed id makes both
+    outputs NaN; the shared slot itself never poisons."""
+    E, F, H, top_k = 8, 256, 256, 2
+    rng, gate, up, sg, su, stride, ids, x = _shexp_inputs("q4_k", E, F, H, T, top_k, 800 + T)
+    down = synth.weight_blocks("q4_k", rng, E * H, F)
+    dsh = synth.weight_blocks("q4_k", rng, H, F)
+    ds = H * synth.row_bytes("q4_k", F)
+    scores = rng.uniform(0.05, 1.0, size=(T, top_k + 1)).astype(np.float32)
+    dev = {k_: to_dev(v) for k_, v in (("gate", gate), ("up", up), ("sg", sg), ("su", su),
+                                       ("down", down), ("dsh", dsh), ("ids", ids), ("sc", scores))}
+    ws = _ws(kq, E + 1, T, top_k + 1, H)
+    outs = []
+    for flags in (0, kq.REUSE_SCHEDULE):
+        h = empty((T, top_k + 1, F), "f32")
+        kq.kq_moe_glu_ex("q4_k", dev["gate"], dev["up"], E, F, H, stride, to_dev(x, "f16"),
+                         dev["ids"], T, top_k, h, ws, kq.ACT_SILU, 0.0, dev["sg"], dev["su"])
+        out = empty((T, H), "f32")
+        kq.kq_qmm_id_mix_shexp("q4_k", dev["down"], E, H, F, ds, dev["dsh"], h, dev["ids"], T,
+                               top_k, dev["sc"], out, ws, flags)
+        torch.cuda.synchronize()
+        outs.append((to_f64(h), out.cpu().numpy()))
+    assert np.array_equal(outs[0][1].view(np.uint32), outs[1][1].view(np.uint32))
+    hg = outs[0][0].astype(np.float32)
+    ref, s = oracle.qmm_id_mix_shexp("q4_k", down, E, H, F, ds, dsh, hg.reshape(-1, F), "f32",
+                                     ids, T, top_k, scores)
+    check_tol(outs[0][1].astype(np.float64), ref, s, TAU["f32"], f"shexp layer T={T}")
+    if T >= 32:
+        bad = ids.copy()
+        bad[5, 1] = bad[5, 0]
+        h = empty((T, top_k + 1, F), "f32")
+        kq.kq_moe_glu_ex("q4_k", dev["gate"], dev["up"], E, F, H, stride, to_dev(x, "f16"),
+                         to_dev(bad), T, top_k, h, ws, kq.ACT_SILU, 0.0, dev["sg"], dev["su"])
+        out = empty((T, H), "f32")
+        kq.kq_qmm_id_mix_shexp("q4_k", dev["down"], E, H, F, ds, dev["dsh"], h, to_dev(bad), T,
+                               top_k, dev["sc"], out, ws, kq.REUSE_SCHEDULE)
+        torch.cuda.synchronize()
+        assert np.isnan(to_f64(h)).all() and np.isnan(to_f64(out)).all()
