@@ -1,7 +1,9 @@
 """Compile libkq.so (all HIP kernels + the C ABI) for gfx950, in-tree.
 
 Each .hip source is compiled to an object in ``_build/`` in parallel, then
-linked into ``block_quantized_weight_q4_amd/libkq.so``.  Always recompiles
+linked into ``block_quantized_weight_q4_amd/libkq.so``.  The streaming-read
+measuring stick (``csrc/hbm_read.hip``) goes into its own
+``libkq_hbmread.so``, which only the benchmark loads.  Always recompiles
 (the caller asked for a build); ``build_if_missing`` only builds when the
 library is absent.
 """
@@ -17,6 +19,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libkq.so")
+READ_LIB = os.path.join(PKG, "libkq_hbmread.so")
+READ_SOURCES = ["hbm_read.hip"]
 SOURCES = ["api.hip", "dequant.hip", "skinny.hip", "mmv2.hip", "mmv3.hip", "gemm.hip", "moe.hip", "moe_dec.hip", "moe_mm.hip", "tq1mv.hip", "quantize.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -39,24 +43,30 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    workers = min(len(SOURCES), max(1, min(8, os.cpu_count() or 1)))
-    with cf.ThreadPoolExecutor(workers) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _link(objs, lib):
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + READ_SOURCES
+    workers = min(len(srcs), max(1, min(8, os.cpu_count() or 1)))
+    with cf.ThreadPoolExecutor(workers) as ex:
+        objs = list(ex.map(_compile, srcs))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], READ_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {READ_LIB}")
     return LIB
 
 
 def build_if_missing() -> str:
-    if not os.path.exists(LIB):
+    if not (os.path.exists(LIB) and os.path.exists(READ_LIB)):
         build()
     return LIB
 

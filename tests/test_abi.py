@@ -65,6 +65,28 @@ def test_library_exports_every_declared_symbol(kq):
         assert getattr(L, s) is not None
 
 
+def test_read_ceiling_library_is_separate(kq):
+    """The benchmark's streaming-read measuring stick lives in its own
+    library: libkq.so does not export it, libkq_hbmread.so does, and its
+    host-side argument check rejects bad input before any launch."""
+    from block_quantized_weight_q4_amd._build import LIB, READ_LIB
+
+    main = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True,
+                          check=True).stdout
+    assert "kq_hbm_read" not in main
+    out = subprocess.run(["nm", "-D", "--defined-only", READ_LIB], capture_output=True, text=True,
+                         check=True).stdout
+    assert re.search(r"\bT kq_hbm_read$", out, flags=re.M)
+    rd = C.CDLL(READ_LIB)
+    rd.kq_hbm_read.restype = C.c_int
+    rd.kq_hbm_read.argtypes = [C.c_void_p, C.c_size_t, C.c_int, C.c_int, C.c_uint32, C.c_void_p,
+                               C.c_void_p]
+    assert rd.kq_hbm_read(None, 16, 1, 4, 0, 16, None) == -1
+    assert rd.kq_hbm_read(16, 15, 1, 4, 0, 16, None) == -1
+    assert rd.kq_hbm_read(16, 16, 0, 4, 0, 16, None) == -1
+    assert rd.kq_hbm_read(16, 16, 1, 3, 0, 16, None) == -1
+
+
 def test_block_geometry(kq):
     assert (kq.kq_qk("q4_k"), kq.kq_block_bytes("q4_k")) == (256, 144)
     assert (kq.kq_qk("q8_0"), kq.kq_block_bytes("q8_0")) == (32, 34)
