@@ -145,6 +145,8 @@ __global__ __launch_bounds__(64 * W) void moe_mm_kernel(SkinnyArgs a) {
     }
 
     u32x4 hd[2], q0[2], q1[2];
+    // the weights of one super-block: kWLoads 16-byte loads per lane
+    constexpr int kWLoads = 6;
     auto load_w = [&](int sb, u32x4 (&h)[2], u32x4 (&w0)[2], u32x4 (&w1)[2]) {
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
@@ -154,7 +156,6 @@ __global__ __launch_bounds__(64 * W) void moe_mm_kernel(SkinnyArgs a) {
             w1[b] = *(const u32x4*)(p + 32 + 32 * g);
         }
     };
-    load_w(0, hd, q0, q1);
 
     // fp16 activations: the rows of chunk [c0, c0 + XC) are copied straight
     // into LDS one chunk ahead (a 1 KB load per row: XC = 2, rows of at
@@ -187,18 +188,34 @@ __global__ __launch_bounds__(64 * W) void moe_mm_kernel(SkinnyArgs a) {
     __syncthreads();  // the row offsets and exponents
     if (!XF32) issue_x(0, xh);
     else issue_raw(0);
+    // the first weights are requested after the first activation copies, so
+    // that at every chunk boundary the loads issued after a chunk's copies
+    // are exactly the kWLoads of the next super-block's weights, which stay
+    // in flight across the wait
+    load_w(0, hd, q0, q1);
+    // The compiler waits for a weight register by counting only the loads it
+    // issued itself, so a wait placed after the next chunk's copies would wait
+    // for those copies too.  Taking the current weights before issuing the
+    // copies keeps the copies' latency under this chunk's matrix work.
+    auto weights_ready = [&]() {
+#pragma unroll
+        for (int b = 0; b < 2; ++b) asm volatile("" : "+v"(hd[b]), "+v"(q0[b]), "+v"(q1[b]));
+    };
     const uint16_t* xcur = xh;
 
     int ci = 0;
     for (int c0 = 0; c0 < nsb; c0 += XC, ++ci) {
         const int nch = nsb - c0 < XC ? nsb - c0 : XC;
         if (!XF32) {
-            wait_loads_le(0);  // this wave's copies of chunk ci have landed
+            // this wave's copies of chunk ci have landed (loads complete in
+            // issue order; only the prefetched weights may be outstanding)
+            wait_loads_le(kWLoads);
             __syncthreads();   // every wave's, and every wave is done with chunk ci - 1
+            weights_ready();
             if (c0 + XC < nsb) issue_x(c0 + XC, (ci & 1) ? xh : xl);
             xcur = (ci & 1) ? xl : xh;
         } else {
-            wait_loads_le(0);  // this wave's copies of the chunk have landed
+            wait_loads_le(kWLoads);  // this wave's copies of the chunk have landed
             __syncthreads();   // every wave's, and every wave is done with the previous chunk
             // ---- split activation rows of super-block c0 (XC = 1): a wave
             // per row, lane q on columns 4q..4q+3
@@ -223,12 +240,15 @@ __global__ __launch_bounds__(64 * W) void moe_mm_kernel(SkinnyArgs a) {
                 }
             }
             __syncthreads();  // hi and lo rows ready, raw buffer free
+            weights_ready();
             if (c0 + 1 < nsb) issue_raw(c0 + 1);
         }
 
         for (int sb = c0; sb < c0 + nch; ++sb) {
             u32x4 nhd[2], nq0[2], nq1[2];
             load_w(sb + 1 < nsb ? sb + 1 : sb, nhd, nq0, nq1);
+            // the next super-block's loads go out before this one's decode
+            __builtin_amdgcn_sched_barrier(0);
             Q4Operands op[2];
 #pragma unroll
             for (int b = 0; b < 2; ++b) q4k_operands(hd[b], q0[b], q1[b], ls, magic_v, op[b]);
