@@ -40,7 +40,7 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFS = 2500.0
 GIB = 1 << 30
 # (workgroups, loads in flight per lane) of the streaming-read ceiling
-READ_SHAPES = ((1024, 4), (2048, 4), (4096, 2), (2048, 8))
+READ_SHAPES = ((1024, 4), (2048, 4), (4096, 2), (4096, 4), (1024, 8), (2048, 8), (4096, 8))
 STAGES = ("dequant", "qmv_c1", "qmv_c2", "qmm_c3", "moe_c4", "tq1_c5")
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 

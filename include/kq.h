@@ -202,7 +202,8 @@ kq_status kq_qmm(kq_type t, const void* w, int64_t n, int64_t k, const void* x, 
  *     so results are deterministic.
  *
  * kq_qmm_workspace_bytes returns the bytes kq_qmm_ws needs for these sizes
- * (0: none needed -- m <= 16 or fp32 activations -- or invalid arguments).
+ * (0: none needed -- m <= 16, fp32 activations, or fp16 activations on a
+ * grid that is not split -- or invalid arguments).
  * workspace: device memory, 256-byte aligned, at least that many bytes,
  * overlapping neither the inputs nor y; its contents on entry are ignored
  * and on return unspecified.  Calls that share a workspace must not overlap
