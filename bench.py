@@ -201,6 +201,7 @@ def main():
 
     if "tq1_c5" in wanted:
         calls_v, calls_m, bv, bm, fv, fm = [], [], 0, 0, 0, 0
+        calls_q, bq = [], 0
         for case in workloads.c5():
             n, k = case["n"], case["k"]
             w = d8(case["w"])
@@ -208,18 +209,32 @@ def main():
             x = d16(case["x"], torch.float16)
             y1 = torch.empty((1, n), dtype=torch.float16, device=dev)
             ym = torch.empty((512, n), dtype=torch.float16, device=dev)
+            # batch 1 through the workspace form: K split for the 5120-row
+            # shape; also the no-workspace GEMV (kq_qmv) beside it
+            s1 = scratch("tq1_g128", n, k, 1, torch.float16)
+            part, pb = [], 0
             for _ in range(len(ws)):
-                calls_v.append(lambda n=n, k=k, ws=ws, x=x, y1=y1:
+                part.append(lambda n=n, k=k, ws=ws, x=x, y1=y1, s1=s1:
+                            kq.kq_qmm_ws("tq1_g128", nxt(ws), n, k, x[:1], 1, y1, s1))
+                pb += w.numel() + (k + n) * 2
+                calls_q.append(lambda n=n, k=k, ws=ws, x=x, y1=y1:
                                kq.kq_qmv("tq1_g128", nxt(ws), n, k, x[:1], 1, y1))
-                bv += w.numel() + (k + n) * 2
                 fv += 2 * n * k
+            calls_v += part
+            bv += pb
+            bq += pb
+            extra_parts.append(Stage(f"tq1_c5_b1_{n}x{k}", part, pb, len(part) * 2 * n * k,
+                                     note="TQ1 GEMV batch 1, fp16 (kq_qmm_ws)"))
             sc = scratch("tq1_g128", n, k, 512, torch.float16)
             for _ in range(len(ws)):
                 calls_m.append(lambda n=n, k=k, ws=ws, x=x, ym=ym, sc=sc:
                                kq.kq_qmm_ws("tq1_g128", nxt(ws), n, k, x, 512, ym, sc))
                 bm += w.numel() + 512 * (k + n) * 2
                 fm += 2 * 512 * n * k
-        stages.append(Stage("tq1_c5_b1", calls_v, bv, fv, note="TQ1 GEMV batch 1, fp16"))
+        stages.append(Stage("tq1_c5_b1", calls_v, bv, fv,
+                            note="TQ1 GEMV batch 1, fp16 (kq_qmm_ws: K split on the 5120-row shape)"))
+        extra_parts.append(Stage("tq1_c5_b1_noworkspace", calls_q, bq, fv,
+                                 note="TQ1 GEMV batch 1, fp16 (kq_qmv, no workspace)"))
         stages.append(Stage("tq1_c5_m512", calls_m, bm, fm, note="TQ1 qmm M=512, fp16 (kq_qmm_ws)"))
 
     # Streaming-read ceiling: a plain 16-byte-load read of the same number of
@@ -358,7 +373,7 @@ def main():
                      "note": "best launch shape of the plain streaming read"}
     for name, r in rows.items():
         c = ceil.get("hbm_read_ceiling_33MB") if name.startswith("qmv_c2") else (
-            ceil.get("hbm_read_ceiling_19.5MB") if name == "tq1_c5_b1" else None)
+            ceil.get("hbm_read_ceiling_19.5MB") if name.startswith("tq1_c5_b1") else None)
         if c and "GB/s" in r:
             r["frac_read_ceiling"] = round(r["GB/s"] / c, 4)
     if c2_parts:

@@ -223,14 +223,49 @@ kq_status kq_qmm(kq_type t, const void* w, int64_t n, int64_t k, const void* x, 
     return launched(kq::launch_gemm(t, x_dt, w, n, k, x, m, y, y_dt, nullptr, (hipStream_t)stream));
 }
 
-// The products that take the decode kernels (m <= 16) or the fp32 path need
-// no scratch; the prefill GEMM takes the layout of kq::gemm_workspace.
-static bool qmm_uses_workspace(int64_t m, kq_dtype x_dt) { return m > 16 && x_dt != KQ_F32; }
+// Scratch of the workspace forms.  The prefill GEMM (m > 16, 16-bit
+// activations) takes the layout of kq::gemm_workspace.  Of the decode shapes,
+// the TQ1 GEMV of one fp16 row splits K when its rows fill few workgroups,
+// with fp32 partials [pieces][n]; the other decode products and the fp32
+// path need no scratch.
+static bool qmm_uses_gemm(int64_t m, kq_dtype x_dt) { return m > 16 && x_dt != KQ_F32; }
+
+static int64_t decode_split_bytes(kq_type t, int64_t n, int64_t k, int64_t m, kq_dtype x_dt,
+                                  int* pnb) {
+    *pnb = 0;
+    if (t != KQ_TQ1_G128 || x_dt != KQ_F16 || m != 1) return 0;
+    const int pieces = kq::tq1_mv_pieces(n, k, pnb);
+    if (pieces < 2) return 0;
+    return ((int64_t)pieces * n * 4 + 255) / 256 * 256;
+}
+
+static int64_t qmm_scratch_bytes(kq_type t, int64_t n, int64_t k, int64_t m, kq_dtype x_dt,
+                                 int* pnb) {
+    *pnb = 0;
+    if (qmm_uses_gemm(m, x_dt)) return kq::gemm_workspace(t, n, k, m, x_dt).bytes;
+    return decode_split_bytes(t, n, k, m, x_dt, pnb);
+}
+
+// The product of the workspace forms on scratch of `need` bytes at ws (or
+// none when need is 0).
+static kq_status qmm_with_scratch(kq_type t, const void* w, int64_t n, int64_t k, int64_t row_bytes,
+                                  const void* x, kq_dtype x_dt, int64_t m, void* y, kq_dtype y_dt,
+                                  int64_t need, int pnb, void* ws, hipStream_t s) {
+    if (qmm_uses_gemm(m, x_dt))
+        return launched(kq::launch_gemm(t, x_dt, w, n, k, x, m, y, y_dt, need > 0 ? ws : nullptr, s));
+    if (need == 0) return dense_skinny(t, w, n, k, row_bytes, x, x_dt, m, y, y_dt, s);
+    const int pieces = (int)((k / 128 + pnb - 1) / pnb);
+    hipError_t e = kq::launch_tq1_mv((const uint8_t*)w, n, k, (const uint16_t*)x, y, y_dt, s, pnb,
+                                     (float*)ws);
+    if (e == hipSuccess) e = kq::launch_splitk_reduce((const float*)ws, pieces, n, y, y_dt, s);
+    return launched(e);
+}
 
 size_t kq_qmm_workspace_bytes(kq_type t, int64_t n, int64_t k, int64_t m, kq_dtype x_dt) {
     if (!qk_of(t) || n <= 0 || k <= 0 || m <= 0 || k % qk_of(t) || !valid_dt(x_dt)) return 0;
-    if (n > kMaxN || k > kMaxK || m > kMaxM || !qmm_uses_workspace(m, x_dt)) return 0;
-    return (size_t)kq::gemm_workspace(t, n, k, m, x_dt).bytes;
+    if (n > kMaxN || k > kMaxK || m > kMaxM) return 0;
+    int pnb;
+    return (size_t)qmm_scratch_bytes(t, n, k, m, x_dt, &pnb);
 }
 
 kq_status kq_qmm_ws(kq_type t, const void* w, int64_t n, int64_t k, const void* x, kq_dtype x_dt,
@@ -240,9 +275,8 @@ kq_status kq_qmm_ws(kq_type t, const void* w, int64_t n, int64_t k, const void* 
     kq_status st = check_product(t, w, n, k, x, x_dt, m, y, y_dt, row_bytes);
     if (st) return st;
     hipStream_t s = (hipStream_t)stream;
-    if (!qmm_uses_workspace(m, x_dt))
-        return dense_skinny(t, w, n, k, row_bytes, x, x_dt, m, y, y_dt, s);
-    const int64_t need = kq::gemm_workspace(t, n, k, m, x_dt).bytes;
+    int pnb;
+    const int64_t need = qmm_scratch_bytes(t, n, k, m, x_dt, &pnb);
     if (need > 0) {
         if (!workspace || !aligned(workspace, 256))
             return fail(KQ_ERR_WORKSPACE, "workspace must be non-null and 256-byte aligned");
@@ -253,7 +287,7 @@ kq_status kq_qmm_ws(kq_type t, const void* w, int64_t n, int64_t k, const void* 
             overlap({workspace, need}, {y, yb}))
             return fail(KQ_ERR_INVALID_ARG, "workspace overlaps an input or the output");
     }
-    return launched(kq::launch_gemm(t, x_dt, w, n, k, x, m, y, y_dt, need > 0 ? workspace : nullptr, s));
+    return qmm_with_scratch(t, w, n, k, row_bytes, x, x_dt, m, y, y_dt, need, pnb, workspace, s);
 }
 
 // ---------------------------------------------------------------- kq_qmm_noalloc
@@ -293,15 +327,14 @@ kq_status kq_qmm_noalloc(kq_type t, const void* w, int64_t n, int64_t k, const v
     kq_status st = check_product(t, w, n, k, x, x_dt, m, y, y_dt, row_bytes);
     if (st) return st;
     hipStream_t s = (hipStream_t)stream;
-    if (!qmm_uses_workspace(m, x_dt))
-        return dense_skinny(t, w, n, k, row_bytes, x, x_dt, m, y, y_dt, s);
-    const int64_t need = kq::gemm_workspace(t, n, k, m, x_dt).bytes;
+    int pnb;
+    const int64_t need = qmm_scratch_bytes(t, n, k, m, x_dt, &pnb);
     if (need > (int64_t)kNoAllocScratchBytes)
         return fail(KQ_ERR_WORKSPACE, "product needs more scratch than kq_qmm_noalloc holds "
                                       "(kq_qmm_workspace_bytes() > kq_qmm_noalloc_max_bytes())");
     void* ws = nullptr;
     if (need > 0 && (st = scratch_address(&ws))) return st;
-    return launched(kq::launch_gemm(t, x_dt, w, n, k, x, m, y, y_dt, need > 0 ? ws : nullptr, s));
+    return qmm_with_scratch(t, w, n, k, row_bytes, x, x_dt, m, y, y_dt, need, pnb, ws, s);
 }
 
 size_t kq_moe_workspace_bytes(int64_t n_experts, int64_t n_tokens, int64_t top_k, int64_t n_out) {

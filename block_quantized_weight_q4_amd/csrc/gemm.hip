@@ -911,12 +911,15 @@ hipError_t launch_gemm(int codec, int x_dt, const void* w, int64_t n, int64_t k,
     if (p.splits > 1) a.part = (float*)(base + L.part_off);
     if (x_dt == BF16) launch_xm<XM_SCALED>(codec, a, p, s);
     else launch_xm<XM_F16>(codec, a, p, s);
-    if (p.splits > 1) {
-        const int64_t mn = m * n;
-        const int64_t blocks = (mn + 255) / 256 < 4096 ? (mn + 255) / 256 : 4096;
-        hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
-                           (const float*)a.part, p.splits, mn, y, y_dt);
-    }
+    if (p.splits > 1) return launch_splitk_reduce(a.part, p.splits, m * n, y, y_dt, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_splitk_reduce(const float* part, int pieces, int64_t count, void* y, int y_dt,
+                                hipStream_t s) {
+    const int64_t blocks = (count + 255) / 256 < 4096 ? (count + 255) / 256 : 4096;
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, s, part, pieces,
+                       count, y, y_dt);
     return hipGetLastError();
 }
 

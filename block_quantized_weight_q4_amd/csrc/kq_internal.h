@@ -98,8 +98,14 @@ hipError_t launch_moe_mm(bool glu, int x_dt, const SkinnyArgs& a, int64_t grid_t
                          hipStream_t s);
 hipError_t launch_row_exp(const float* x, int64_t rows, int64_t k, int32_t* e, hipStream_t s);
 bool tq1_mv_fits(int64_t k);
+// pieces of K for the TQ1 GEMV of n rows (1: no split); *pnb = blocks per piece
+int tq1_mv_pieces(int64_t n, int64_t k, int* pnb);
+// pnb > 0: K in pieces of pnb blocks, fp32 partials to part [pieces][n]
 hipError_t launch_tq1_mv(const uint8_t* w, int64_t n, int64_t k, const uint16_t* x, void* y,
-                         int y_dt, hipStream_t s);
+                         int y_dt, hipStream_t s, int pnb = 0, float* part = nullptr);
+// y[i] = sum over pieces p in order of part[p * count + i], stored as y_dt
+hipError_t launch_splitk_reduce(const float* part, int pieces, int64_t count, void* y, int y_dt,
+                                hipStream_t s);
 // Prefill GEMM (gemm.hip).
 struct GemmArgs {
     const uint8_t* w;

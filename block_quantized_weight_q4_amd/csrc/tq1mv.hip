@@ -69,10 +69,14 @@ struct TqCfg {
     }
 };
 
+// K pieces (split-K): with pnb > 0, workgroup (tile, piece) covers blocks
+// [piece * pnb, piece * pnb + pnb) of its rows and stores its fp32 partial
+// sums to part[piece * n + row] instead of y.
 template <int W, int CB>
 __global__ __launch_bounds__(64 * W) void tq1_mv_kernel(const uint8_t* __restrict__ w, int64_t n,
                                                         int64_t k, const uint16_t* __restrict__ x,
-                                                        void* __restrict__ y, int y_dt) {
+                                                        void* __restrict__ y, int y_dt, int pnb,
+                                                        float* __restrict__ part) {
     using Cfg = TqCfg<W, CB>;
     constexpr int kCB = Cfg::CB, kNBuf = Cfg::NBUF, kRowPieces = Cfg::ROW_PIECES, kWBuf = Cfg::WBUF;
     constexpr int NPIECE = 16 * kRowPieces;
@@ -83,12 +87,16 @@ __global__ __launch_bounds__(64 * W) void tq1_mv_kernel(const uint8_t* __restric
     u32x2* lut_hi = (u32x2*)(smem + kHiOff);                     // [16]
     uint8_t* wbuf = smem + kLutBytes;                           // [kNBuf][kWBuf]
     u32x4* xs = (u32x4*)(smem + kLutBytes + kNBuf * kWBuf);     // [nblk * 28] slots
-    const int nblk = (int)(k / 128);
+    const int nblk_row = (int)(k / 128);
+    const int piece = (int)blockIdx.y;
+    // blocks of this workgroup's piece of K (all of K without a split)
+    const int nblk = pnb ? (nblk_row - piece * pnb < pnb ? nblk_row - piece * pnb : pnb) : nblk_row;
+    x += (int64_t)piece * pnb * 128;
     float* red = (float*)((uint8_t*)xs + (size_t)nblk * kSlots * 16);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n_l = lane & 15, g = lane >> 4;
     const int64_t n0 = (int64_t)blockIdx.x * 16;
-    const int64_t row_bytes = (int64_t)nblk * 28;
+    const int64_t row_bytes = (int64_t)nblk_row * 28;
     const int nchunks = (nblk + kCB - 1) / kCB;
 
     // ---- tables of trits as fp16: -1, 0, +1 for digits 0, 1, 2
@@ -124,7 +132,7 @@ __global__ __launch_bounds__(64 * W) void tq1_mv_kernel(const uint8_t* __restric
     // ---- weight pieces of this lane: LDS slot p = 64 i + lane is piece
     // p % kRowPieces of row p / kRowPieces (the last piece of a row is
     // padding and is not loaded)
-    const uint8_t* wbase = w + n0 * row_bytes;
+    const uint8_t* wbase = w + n0 * row_bytes + (int64_t)piece * pnb * 28;
     uint32_t woff[WL_PER_WAVE], wq16[WL_PER_WAVE];
     bool wact[WL_PER_WAVE];
 #pragma unroll
@@ -218,6 +226,10 @@ __global__ __launch_bounds__(64 * W) void tq1_mv_kernel(const uint8_t* __restric
         if (wave > 0) return;
         for (int ww = 1; ww < W; ++ww) acc[0] += red[(ww - 1) * 16 + n_l];
     }
+    if (part) {
+        if (g == 0 && n0 + n_l < n) part[(int64_t)piece * n + n0 + n_l] = acc[0];
+        return;
+    }
     if (g == 0 && n0 + n_l < n) {
         const int64_t o = n0 + n_l;
         if (y_dt == F32) store_out<F32>(y, o, acc[0]);
@@ -245,16 +257,39 @@ bool tq1_mv_fits(int64_t k) {
     return lds <= 160 * 1024;
 }
 
+// Split-K for rows that fill few workgroups (Ternary Bonsai
+// "ternel_packed_model.py", the split-K budget of its decode dispatches: a
+// tensor whose rows yield few tiles runs one short chain on an idle GPU).
+// Fewer than 512 row tiles of 16 are split into ceil(1024 / tiles) pieces of
+// at least 16 blocks, each a whole number of four blocks (16-byte aligned
+// copies).  Measured on 5120x17408: 17.2 -> 13.9 us with four pieces,
+// reduction included; the 17408-row shape (1088 tiles) is not split.
+int tq1_mv_pieces(int64_t n, int64_t k, int* pnb_out) {
+    const int64_t tiles = (n + 15) / 16, nblk = k / 128;
+    *pnb_out = 0;
+    if (!tq1_mv_fits(k) || tiles >= 512) return 1;
+    int64_t pieces = (1024 + tiles - 1) / tiles;
+    if (pieces > nblk / 16) pieces = nblk / 16;
+    if (pieces < 2) return 1;
+    int64_t pnb = (nblk + pieces - 1) / pieces;
+    pnb = (pnb + 3) / 4 * 4;
+    pieces = (nblk + pnb - 1) / pnb;
+    if (pieces < 2) return 1;
+    *pnb_out = (int)pnb;
+    return (int)pieces;
+}
+
 hipError_t launch_tq1_mv(const uint8_t* w, int64_t n, int64_t k, const uint16_t* x, void* y, int y_dt,
-                         hipStream_t s) {
-    const int64_t nblk = k / 128;
-    const dim3 grid((unsigned)((n + 15) / 16));
+                         hipStream_t s, int pnb, float* part) {
+    const int64_t nblk = pnb ? pnb : k / 128;  // blocks per workgroup
+    const int pieces = pnb ? (int)((k / 128 + pnb - 1) / pnb) : 1;
+    const dim3 grid((unsigned)((n + 15) / 16), (unsigned)pieces);
     if (nblk >= 64) {
-        hipLaunchKernelGGL((tq1_mv_kernel<16, 16>), grid, dim3(64 * 16),
-                           TqLong::lds_bytes(nblk), s, w, n, k, x, y, y_dt);
+        hipLaunchKernelGGL((tq1_mv_kernel<16, 16>), grid, dim3(64 * 16), TqLong::lds_bytes(nblk), s, w,
+                           n, k, x, y, y_dt, pnb, part);
     } else {
-        hipLaunchKernelGGL((tq1_mv_kernel<8, 16>), grid, dim3(64 * 8),
-                           TqShort::lds_bytes(nblk), s, w, n, k, x, y, y_dt);
+        hipLaunchKernelGGL((tq1_mv_kernel<8, 16>), grid, dim3(64 * 8), TqShort::lds_bytes(nblk), s, w,
+                           n, k, x, y, y_dt, pnb, part);
     }
     return hipGetLastError();
 }

@@ -199,11 +199,15 @@ kq_status kq_qmm(kq_type t, const void* w, int64_t n, int64_t k, const void* x, 
  *     copy of the activation rows);
  *   - a product with fewer output tiles than the GPU has compute units splits
  *     K across workgroups; the fp32 partial sums are added in a fixed order,
- *     so results are deterministic.
+ *     so results are deterministic;
+ *   - the TQ1_G128 decode product of one fp16 activation row (m = 1) whose
+ *     rows fill fewer than 512 workgroups of 16 rows splits K the same way
+ *     (Ternary Bonsai "ternel_packed_model.py", the split-K budget of its
+ *     decode dispatches).
  *
  * kq_qmm_workspace_bytes returns the bytes kq_qmm_ws needs for these sizes
- * (0: none needed -- m <= 16, fp32 activations, or fp16 activations on a
- * grid that is not split -- or invalid arguments).
+ * (0: none needed -- any other m <= 16 product, fp32 activations, or fp16
+ * activations on a grid that is not split -- or invalid arguments).
  * workspace: device memory, 256-byte aligned, at least that many bytes,
  * overlapping neither the inputs nor y; its contents on entry are ignored
  * and on return unspecified.  Calls that share a workspace must not overlap

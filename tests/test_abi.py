@@ -200,6 +200,14 @@ def test_qmm_workspace_sizes_and_validation(kq):
     assert kq.kq_qmm_workspace_bytes("q4_k", 14336, 4096, 2048, f16) == 0  # many tiles: no split
     few = kq.kq_qmm_workspace_bytes("q4_k", 512, 4096, 200, f16)         # few tiles: split K
     assert few >= 2 * 200 * 512 * 4
+    # the TQ1 decode product of one fp16 row: split K when its 16-row tiles
+    # are fewer than 512 (5120 rows: 320 tiles, four pieces of 36 blocks)
+    assert kq.kq_qmm_workspace_bytes("tq1_g128", 5120, 17408, 1, f16) == 4 * 5120 * 4
+    assert kq.kq_qmm_workspace_bytes("tq1_g128", 17408, 5120, 1, f16) == 0   # 1088 tiles
+    assert kq.kq_qmm_workspace_bytes("tq1_g128", 5120, 17408, 2, f16) == 0   # m > 1
+    assert kq.kq_qmm_workspace_bytes("tq1_g128", 5120, 17408, 1, bf) == 0    # bf16 x
+    assert kq.kq_qmm_workspace_bytes("tq1_g128", 300, 1536, 1, f16) == 0     # 12 blocks: too short
+    assert kq.kq_qmm_workspace_bytes("q4_k", 4096, 14336, 1, f16) == 0
     L = kq.lib()
     P = C.c_void_p
     base = 1 << 40

@@ -186,6 +186,28 @@ def test_qmv_tq1_one_row_shapes(kq, n, nblk):
                   out_dt=y_dt if y_dt != "f32" else None)
 
 
+@pytest.mark.parametrize("n,nblk", [(300, 64), (1000, 72), (4099, 36), (16, 68)])
+def test_qmv_tq1_split_k(kq, n, nblk):
+    """The TQ1 decode product of one fp16 row through kq_qmm_ws: rows that
+    fill few workgroups split K into pieces (fp32 partials added in piece
+    order).  Pieces: 4 x 16 blocks; 20+20+20+12 (a short last piece); 20+16
+    with a ragged last row tile; and a single tile.  Every output against the
+    oracle, bit-identical from call to call."""
+    k = 128 * nblk
+    rng = _rng(2900 + nblk)
+    w = synth.weight_blocks("tq1_g128", rng, n, k)
+    x = synth.activations(rng, (1, k), "f16")
+    assert kq.kq_qmm_workspace_bytes("tq1_g128", n, k, 1, torch.float16) > 0
+    ref, s = oracle.qmm("tq1_g128", w, n, k, x, "f16", 1)
+    for y_dt in ("f32", "f16", "bf16"):
+        _say("qmv tq1 split k", n, k, y_dt)
+        got = _run(kq, "kq_qmm_ws", "tq1_g128", w, n, k, x, "f16", 1, y_dt)
+        check_tol(got, ref, s, TAU["f16"], f"qmv tq1 split {n}x{k} y={y_dt}",
+                  out_dt=y_dt if y_dt != "f32" else None)
+        again = _run(kq, "kq_qmm_ws", "tq1_g128", w, n, k, x, "f16", 1, y_dt)
+        assert np.array_equal(got, again)
+
+
 @pytest.mark.parametrize("kind", KINDS)
 @pytest.mark.parametrize("m", [14, 15, 16])
 def test_qmv_long_rows_many_activations(kq, kind, m):
@@ -332,7 +354,7 @@ def test_qmm_tq1_large_tiles_ragged(kq, x_dt, fn):
 
 
 @pytest.mark.parametrize("which", [0, 1])
-@pytest.mark.parametrize("m,fn", [(1, "kq_qmv"), (512, "kq_qmm"), (512, "kq_qmm_ws")])
+@pytest.mark.parametrize("m,fn", [(1, "kq_qmv"), (1, "kq_qmm_ws"), (512, "kq_qmm"), (512, "kq_qmm_ws")])
 def test_tq1_c5_full_sampled(kq, which, m, fn):
     case = workloads.c5()[which]
     _say("tq1 C5", case["n"], case["k"], m, fn)

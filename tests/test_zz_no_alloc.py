@@ -38,8 +38,10 @@ def _ws_result(kq, kind, w, n, k, x, m, y_dt):
 
 
 # (kind, n, k, m, x dtype): the first uses the activation pre-pass and eight
-# K splits (about 20 MB of scratch), the second two splits and fp16 rows
-CASES = [("q4_k", 1024, 4096, 512, "bf16"), ("q8_0", 300, 1024, 40, "f16")]
+# K splits (about 20 MB of scratch), the second two splits and fp16 rows, the
+# third the split-K TQ1 decode product of one row (four pieces, 4.8 KB)
+CASES = [("q4_k", 1024, 4096, 512, "bf16"), ("q8_0", 300, 1024, 40, "f16"),
+         ("tq1_g128", 300, 8192, 1, "f16")]
 
 
 def test_noalloc_matches_workspace_twice(kq):
@@ -58,10 +60,11 @@ def test_noalloc_matches_workspace_twice(kq):
         torch.cuda.synchronize()
         assert np.array_equal(y.cpu().numpy().view(np.uint32), ref_y.cpu().numpy().view(np.uint32))
         outs.append((kind, w, n, k, x, x_dt, m, to_f64(y)))
-    # both against the oracle (the first on sampled outputs)
-    kind, w, n, k, x, x_dt, m, got = outs[1]
-    ref, s = oracle.qmm(kind, w, n, k, x, x_dt, m)
-    check_tol(got, ref, s, TAU[x_dt], "noalloc second call")
+    # all against the oracle (the first on sampled outputs)
+    for i in (1, 2):
+        kind, w, n, k, x, x_dt, m, got = outs[i]
+        ref, s = oracle.qmm(kind, w, n, k, x, x_dt, m)
+        check_tol(got, ref, s, TAU[x_dt], f"noalloc call {i + 1}")
     kind, w, n, k, x, x_dt, m, got = outs[0]
     rng = np.random.default_rng(1)
     pm, pn = rng.integers(0, m, 500), rng.integers(0, n, 500)
