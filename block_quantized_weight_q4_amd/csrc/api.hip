@@ -235,7 +235,10 @@ static int64_t decode_split_bytes(kq_type t, int64_t n, int64_t k, int64_t m, kq
     *pnb = 0;
     if (t != KQ_TQ1_G128 || x_dt != KQ_F16 || m != 1) return 0;
     const int pieces = kq::tq1_mv_pieces(n, k, pnb);
-    if (pieces < 2) return 0;
+    if (pieces < 2) {
+        *pnb = 0;
+        return 0;
+    }
     return ((int64_t)pieces * n * 4 + 255) / 256 * 256;
 }
 
@@ -254,6 +257,7 @@ static kq_status qmm_with_scratch(kq_type t, const void* w, int64_t n, int64_t k
     if (qmm_uses_gemm(m, x_dt))
         return launched(kq::launch_gemm(t, x_dt, w, n, k, x, m, y, y_dt, need > 0 ? ws : nullptr, s));
     if (need == 0) return dense_skinny(t, w, n, k, row_bytes, x, x_dt, m, y, y_dt, s);
+    // the split TQ1 decode product (the only decode shape that takes scratch)
     const int pieces = (int)((k / 128 + pnb - 1) / pnb);
     hipError_t e = kq::launch_tq1_mv((const uint8_t*)w, n, k, (const uint16_t*)x, y, y_dt, s, pnb,
                                      (float*)ws);

@@ -207,7 +207,8 @@ def test_qmm_workspace_sizes_and_validation(kq):
     assert kq.kq_qmm_workspace_bytes("tq1_g128", 5120, 17408, 2, f16) == 0   # m > 1
     assert kq.kq_qmm_workspace_bytes("tq1_g128", 5120, 17408, 1, bf) == 0    # bf16 x
     assert kq.kq_qmm_workspace_bytes("tq1_g128", 300, 1536, 1, f16) == 0     # 12 blocks: too short
-    assert kq.kq_qmm_workspace_bytes("q4_k", 4096, 14336, 1, f16) == 0
+    for m in (1, 4, 8, 16):                                                 # Q4_K decode: no split
+        assert kq.kq_qmm_workspace_bytes("q4_k", 4096, 14336, m, f16) == 0
     L = kq.lib()
     P = C.c_void_p
     base = 1 << 40
