@@ -27,6 +27,11 @@
  *  the [KQ] and [MID] pages name ("q4_k", GgmlType::Q4_K).  The pages never
  *  print its bit packing; the packing used here is the GGUF convention and is
  *  a documented reading, pinned by hand-built blocks in the tests.
+ *  Q4_0, Q5_0, Q5_1 and Q6_K are the further GGUF blocks of the [MID] page's
+ *  codec table (GgmlType::Q4_0, Q5_0, Q5_1, Q6_K and their mv_id / mm_id
+ *  kernel names); the page names them without printing a layout, so their
+ *  layouts below are the GGUF convention as well -- readings, pinned by
+ *  hand-built blocks and an independent decoder in the tests.
  *
  * Parity status: every function below has pins in tests/test_oracle_pins.py.
  */
@@ -35,7 +40,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { OR_Q4_K = 0, OR_Q8_0 = 1, OR_TQ1 = 2 };
+enum { OR_Q4_K = 0, OR_Q8_0 = 1, OR_TQ1 = 2, OR_Q4_0 = 3, OR_Q5_0 = 4, OR_Q5_1 = 5, OR_Q6_K = 6 };
 enum { OR_F32 = 0, OR_F16 = 1, OR_BF16 = 2 };
 
 /* ------------------------------------------------------------------ */
@@ -214,11 +219,83 @@ void or_decode_tq1(const uint8_t* blk, double* out) {
     }
 }
 
+/* Q4_0 block (32 weights, 18 bytes): fp16 d, then 16 bytes of nibbles; the
+ * low nibble of byte j is weight j and the high nibble weight j + 16, and a
+ * weight is d * (q - 8). */
+void or_decode_q4_0(const uint8_t* blk, double* out) {
+    double d = or_half_to_double(le16(blk));
+    for (int j = 0; j < 16; ++j) {
+        out[j] = d * ((blk[2 + j] & 15) - 8);
+        out[j + 16] = d * ((blk[2 + j] >> 4) - 8);
+    }
+}
+
+/* The fifth bit of weight i (0..31) of a Q5_0 / Q5_1 block: bit i of the
+ * 32-bit little-endian word qh. */
+static int q5_high_bit(const uint8_t* qh, int i) { return (qh[i >> 3] >> (i & 7)) & 1; }
+
+/* Q5_0 block (32 weights, 22 bytes): fp16 d, 4 bytes qh, 16 bytes of nibbles
+ * laid out as in Q4_0; the 5-bit quant of weight i is its nibble plus 16
+ * times bit i of qh, and the weight is d * (q - 16). */
+void or_decode_q5_0(const uint8_t* blk, double* out) {
+    double d = or_half_to_double(le16(blk));
+    const uint8_t* qh = blk + 2;
+    const uint8_t* qs = blk + 6;
+    for (int j = 0; j < 16; ++j) {
+        int q0 = (qs[j] & 15) | (q5_high_bit(qh, j) << 4);
+        int q1 = (qs[j] >> 4) | (q5_high_bit(qh, j + 16) << 4);
+        out[j] = d * (q0 - 16);
+        out[j + 16] = d * (q1 - 16);
+    }
+}
+
+/* Q5_1 block (32 weights, 24 bytes): fp16 d, fp16 m, 4 bytes qh, 16 bytes of
+ * nibbles; quants as in Q5_0, and the weight is d * q + m. */
+void or_decode_q5_1(const uint8_t* blk, double* out) {
+    double d = or_half_to_double(le16(blk));
+    double m = or_half_to_double(le16(blk + 2));
+    const uint8_t* qh = blk + 4;
+    const uint8_t* qs = blk + 8;
+    for (int j = 0; j < 16; ++j) {
+        int q0 = (qs[j] & 15) | (q5_high_bit(qh, j) << 4);
+        int q1 = (qs[j] >> 4) | (q5_high_bit(qh, j + 16) << 4);
+        out[j] = d * q0 + m;
+        out[j + 16] = d * q1 + m;
+    }
+}
+
+/* Q6_K super-block (256 weights, 210 bytes): ql[128] (low four bits), qh[64]
+ * (high two bits), 16 signed 8-bit scales, fp16 d.  The block is two halves
+ * of 128 weights; half h uses ql[64h..], qh[32h..] and scales[8h..].  Weight
+ * 128h + 32u + l (u = 0..3, l = 0..31) has the low bits of byte
+ * ql[64h + l + 32 (u % 2)] (the low nibble for u < 2, the high nibble for
+ * u >= 2), the high bits (qh[32h + l] >> 2u) & 3, the scale
+ * scales[8h + l / 16 + 2u], and the value d * scale * (q - 32). */
+void or_decode_q6_k(const uint8_t* blk, double* out) {
+    const uint8_t* ql = blk;
+    const uint8_t* qh = blk + 128;
+    const int8_t* sc = (const int8_t*)(blk + 192);
+    double d = or_half_to_double(le16(blk + 208));
+    for (int h = 0; h < 2; ++h)
+        for (int u = 0; u < 4; ++u)
+            for (int l = 0; l < 32; ++l) {
+                int lowb = ql[64 * h + l + 32 * (u & 1)];
+                int lo4 = u < 2 ? (lowb & 15) : (lowb >> 4);
+                int hi2 = (qh[32 * h + l] >> (2 * u)) & 3;
+                int q = lo4 | (hi2 << 4);
+                out[128 * h + 32 * u + l] = d * (double)sc[8 * h + l / 16 + 2 * u] * (q - 32);
+            }
+}
+
 int or_qk(int type) {
     switch (type) {
     case OR_Q4_K: return 256;
     case OR_Q8_0: return 32;
     case OR_TQ1: return 128;
+    case OR_Q4_0: return 32;
+    case OR_Q5_0: return 32;
+    case OR_Q5_1: return 32;
+    case OR_Q6_K: return 256;
     }
     return 0;
 }
@@ -228,6 +305,10 @@ int or_block_bytes(int type) {
     case OR_Q4_K: return 144;
     case OR_Q8_0: return 34;
     case OR_TQ1: return 28;
+    case OR_Q4_0: return 18;
+    case OR_Q5_0: return 22;
+    case OR_Q5_1: return 24;
+    case OR_Q6_K: return 210;
     }
     return 0;
 }
@@ -237,6 +318,10 @@ static void decode_block(int type, const uint8_t* blk, double* out) {
     case OR_Q4_K: or_decode_q4k(blk, out); break;
     case OR_Q8_0: or_decode_q8_0(blk, out); break;
     case OR_TQ1: or_decode_tq1(blk, out); break;
+    case OR_Q4_0: or_decode_q4_0(blk, out); break;
+    case OR_Q5_0: or_decode_q5_0(blk, out); break;
+    case OR_Q5_1: or_decode_q5_1(blk, out); break;
+    case OR_Q6_K: or_decode_q6_k(blk, out); break;
     }
 }
 
@@ -831,6 +916,7 @@ int or_quantize(int type, const void* w, int w_dt, int64_t rows, int64_t k, cons
                 uint8_t* out) {
     int qk = or_qk(type), bb = or_block_bytes(type);
     if (!qk || k % qk) return -1;
+    if (type != OR_Q4_K && type != OR_Q8_0 && type != OR_TQ1) return -1;  /* no encoder */
     int64_t nb = k / qk;
 #pragma omp parallel
     {

@@ -20,7 +20,7 @@ __all__ = [
     "qmm_id", "moe_glu", "moe_layer", "route", "routing_poisons_all", "quantize", "tq1_illegal", "silu_limit", "moe_glu_ex", "qmm_id_mix_shexp", "silu", "gelu_tanh", "num_threads",
 ]
 
-TYPES = {"q4_k": 0, "q8_0": 1, "tq1_g128": 2}
+TYPES = {"q4_k": 0, "q8_0": 1, "tq1_g128": 2, "q4_0": 3, "q5_0": 4, "q5_1": 5, "q6_k": 6}
 DTYPES = {"f32": 0, "f16": 1, "bf16": 2}
 
 _lib = None

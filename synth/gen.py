@@ -28,12 +28,14 @@ import numpy as np
 
 __all__ = [
     "QK", "BLOCK_BYTES", "TYPE_NAMES", "rng_for", "q4k_blocks", "q8_0_blocks",
-    "tq1_blocks", "weight_blocks", "activations", "moe_routing", "row_bytes",
+    "tq1_blocks", "legacy_blocks", "q6k_blocks", "weight_blocks", "activations", "moe_routing",
+    "row_bytes",
 ]
 
-TYPE_NAMES = ("q4_k", "q8_0", "tq1_g128")
-QK = {"q4_k": 256, "q8_0": 32, "tq1_g128": 128}
-BLOCK_BYTES = {"q4_k": 144, "q8_0": 34, "tq1_g128": 28}
+TYPE_NAMES = ("q4_k", "q8_0", "tq1_g128", "q4_0", "q5_0", "q5_1", "q6_k")
+QK = {"q4_k": 256, "q8_0": 32, "tq1_g128": 128, "q4_0": 32, "q5_0": 32, "q5_1": 32, "q6_k": 256}
+BLOCK_BYTES = {"q4_k": 144, "q8_0": 34, "tq1_g128": 28, "q4_0": 18, "q5_0": 22, "q5_1": 24,
+               "q6_k": 210}
 
 SCALE_LO = 1e-3
 SCALE_HI = 2e-2
@@ -83,7 +85,33 @@ def tq1_blocks(rng: np.random.Generator, rows: int, k: int) -> np.ndarray:
     return blk.reshape(rows, row_bytes("tq1_g128", k))
 
 
-_GEN = {"q4_k": q4k_blocks, "q8_0": q8_0_blocks, "tq1_g128": tq1_blocks}
+def legacy_blocks(kind: str, rng: np.random.Generator, rows: int, k: int) -> np.ndarray:
+    """uint8 [rows, row_bytes]: random Q4_0 / Q5_0 / Q5_1 blocks: random quant
+    bytes, fp16 d in [1e-3, 2e-2] and (Q5_1) an fp16 offset m in [-0.3, 0.3]."""
+    bb = BLOCK_BYTES[kind]
+    nb = rows * (k // 32)
+    blk = rng.integers(0, 256, size=(nb, bb), dtype=np.uint8)
+    blk[:, 0:2] = _fp16_scales(rng, nb)
+    if kind == "q5_1":
+        m = rng.uniform(-0.3, 0.3, size=nb).astype(np.float16)
+        blk[:, 2:4] = m.view(np.uint16).astype("<u2").view(np.uint8).reshape(nb, 2)
+    return blk.reshape(rows, row_bytes(kind, k))
+
+
+def q6k_blocks(rng: np.random.Generator, rows: int, k: int) -> np.ndarray:
+    """uint8 [rows, row_bytes]: random Q6_K super-blocks: random quant bytes,
+    int8 scales in [-64, 64], fp16 d in [1e-3, 2e-2]."""
+    nb = rows * (k // 256)
+    blk = rng.integers(0, 256, size=(nb, 210), dtype=np.uint8)
+    blk[:, 192:208] = rng.integers(-64, 65, size=(nb, 16), dtype=np.int8).view(np.uint8)
+    blk[:, 208:210] = _fp16_scales(rng, nb)
+    return blk.reshape(rows, row_bytes("q6_k", k))
+
+
+_GEN = {"q4_k": q4k_blocks, "q8_0": q8_0_blocks, "tq1_g128": tq1_blocks, "q6_k": q6k_blocks,
+        "q4_0": lambda rng, r, k: legacy_blocks("q4_0", rng, r, k),
+        "q5_0": lambda rng, r, k: legacy_blocks("q5_0", rng, r, k),
+        "q5_1": lambda rng, r, k: legacy_blocks("q5_1", rng, r, k)}
 
 
 def weight_blocks(kind: str, rng: np.random.Generator, rows: int, k: int) -> np.ndarray:

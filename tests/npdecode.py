@@ -104,10 +104,100 @@ def tq1_pack(trits: np.ndarray, scale16: np.ndarray) -> np.ndarray:
     return out
 
 
+# ---------------------------------------------------------------- GGUF legacy 32-weight blocks
+def _f16_bytes(v16: np.ndarray) -> np.ndarray:
+    v = np.asarray(v16, dtype=np.float16).view(np.uint16).astype("<u2")
+    return v[:, None].view(np.uint8).reshape(len(v), 2)
+
+
+def _nibbles(qs: np.ndarray) -> np.ndarray:
+    """qs uint8 [nb,16] -> [nb,32]: low nibbles are weights 0..15, high 16..31."""
+    q = qs.astype(np.int64)
+    return np.concatenate([q & 15, q >> 4], axis=1)
+
+
+def _q5_high(qh: np.ndarray) -> np.ndarray:
+    """qh uint8 [nb,4] -> the fifth bit of each of the 32 weights [nb,32]."""
+    word = qh.copy().view("<u4")[:, 0].astype(np.int64)
+    return (word[:, None] >> np.arange(32)) & 1
+
+
+def q4_0_decode(blocks: np.ndarray) -> np.ndarray:
+    b = np.asarray(blocks, dtype=np.uint8).reshape(-1, 18)
+    d = f16_bits_to_f64(b[:, 0:2].copy().view("<u2")[:, 0])
+    return d[:, None] * (_nibbles(b[:, 2:18]) - 8)
+
+
+def q5_0_decode(blocks: np.ndarray) -> np.ndarray:
+    b = np.asarray(blocks, dtype=np.uint8).reshape(-1, 22)
+    d = f16_bits_to_f64(b[:, 0:2].copy().view("<u2")[:, 0])
+    q = _nibbles(b[:, 6:22]) + 16 * _q5_high(b[:, 2:6])
+    return d[:, None] * (q - 16)
+
+
+def q5_1_decode(blocks: np.ndarray) -> np.ndarray:
+    b = np.asarray(blocks, dtype=np.uint8).reshape(-1, 24)
+    d = f16_bits_to_f64(b[:, 0:2].copy().view("<u2")[:, 0])
+    m = f16_bits_to_f64(b[:, 2:4].copy().view("<u2")[:, 0])
+    q = _nibbles(b[:, 8:24]) + 16 * _q5_high(b[:, 4:8])
+    return d[:, None] * q + m[:, None]
+
+
+def legacy_pack(kind: str, q: np.ndarray, d16: np.ndarray, m16=None) -> np.ndarray:
+    """Blocks of Q4_0 / Q5_0 / Q5_1 from quants q [nb,32] (0..15 or 0..31)."""
+    q = np.asarray(q, dtype=np.int64)
+    nb = q.shape[0]
+    lo = q & 15
+    qs = (lo[:, :16] | (lo[:, 16:] << 4)).astype(np.uint8)
+    if kind == "q4_0":
+        return np.concatenate([_f16_bytes(d16), qs], axis=1)
+    word = ((q >> 4) << np.arange(32)).sum(axis=1).astype("<u4")
+    qh = word[:, None].view(np.uint8).reshape(nb, 4)
+    if kind == "q5_0":
+        return np.concatenate([_f16_bytes(d16), qh, qs], axis=1)
+    return np.concatenate([_f16_bytes(d16), _f16_bytes(m16), qh, qs], axis=1)
+
+
+# ---------------------------------------------------------------- Q6_K
+def _q6k_maps():
+    """Per weight position e of a super-block: the ql byte, its nibble shift,
+    the qh byte, its 2-bit shift and the scale index (GGUF Q6_K layout:
+    halves of 128 weights, each four runs of 32)."""
+    e = np.arange(256)
+    h, r = e // 128, e % 128
+    u, l = r // 32, r % 32
+    return (64 * h + l + 32 * (u % 2), 4 * (u // 2), 32 * h + l, 2 * u, 8 * h + l // 16 + 2 * u)
+
+
+def q6k_decode(blocks: np.ndarray) -> np.ndarray:
+    b = np.asarray(blocks, dtype=np.uint8).reshape(-1, 210)
+    ql, qh = b[:, 0:128].astype(np.int64), b[:, 128:192].astype(np.int64)
+    sc = b[:, 192:208].view(np.int8).astype(np.int64)
+    d = f16_bits_to_f64(b[:, 208:210].copy().view("<u2")[:, 0])
+    qli, qls, qhi, qhs, sci = _q6k_maps()
+    q = ((ql[:, qli] >> qls) & 15) | (((qh[:, qhi] >> qhs) & 3) << 4)
+    return d[:, None] * sc[:, sci] * (q - 32)
+
+
+def q6k_pack(q: np.ndarray, sc: np.ndarray, d16: np.ndarray) -> np.ndarray:
+    """Q6_K blocks from quants q [nb,256] in 0..63, int8 scales [nb,16], fp16 d [nb]."""
+    q = np.asarray(q, dtype=np.int64)
+    nb = q.shape[0]
+    qli, qls, qhi, qhs, _ = _q6k_maps()
+    ql = np.zeros((nb, 128), dtype=np.int64)
+    qh = np.zeros((nb, 64), dtype=np.int64)
+    for e in range(256):
+        ql[:, qli[e]] |= (q[:, e] & 15) << qls[e]
+        qh[:, qhi[e]] |= (q[:, e] >> 4) << qhs[e]
+    return np.concatenate([ql.astype(np.uint8), qh.astype(np.uint8),
+                           np.asarray(sc, dtype=np.int8).view(np.uint8), _f16_bytes(d16)], axis=1)
+
+
 # ---------------------------------------------------------------- helpers
-QK = {"q4_k": 256, "q8_0": 32, "tq1_g128": 128}
-BB = {"q4_k": 144, "q8_0": 34, "tq1_g128": 28}
-_DEC = {"q4_k": q4k_decode, "q8_0": q8_0_decode, "tq1_g128": tq1_decode}
+QK = {"q4_k": 256, "q8_0": 32, "tq1_g128": 128, "q4_0": 32, "q5_0": 32, "q5_1": 32, "q6_k": 256}
+BB = {"q4_k": 144, "q8_0": 34, "tq1_g128": 28, "q4_0": 18, "q5_0": 22, "q5_1": 24, "q6_k": 210}
+_DEC = {"q4_k": q4k_decode, "q8_0": q8_0_decode, "tq1_g128": tq1_decode, "q4_0": q4_0_decode,
+        "q5_0": q5_0_decode, "q5_1": q5_1_decode, "q6_k": q6k_decode}
 
 
 def decode_matrix(kind: str, w: np.ndarray, rows: int, k: int) -> np.ndarray:

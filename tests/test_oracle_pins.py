@@ -157,7 +157,7 @@ def test_q4k_round_trip_tiny_matrix(orc):
             assert w[b, i] == want
 
 
-@pytest.mark.parametrize("kind", ["q4_k", "q8_0", "tq1_g128"])
+@pytest.mark.parametrize("kind", ["q4_k", "q8_0", "tq1_g128", "q4_0", "q5_0", "q5_1", "q6_k"])
 def test_independent_decoders_agree(orc, kind):
     """C oracle and the vectorised numpy decoder agree bit for bit on random
     blocks (Q4_K with arbitrary fp16 d/dmin bit patterns, not just the
@@ -166,7 +166,8 @@ def test_independent_decoders_agree(orc, kind):
 
     rng = _rng(4)
     rows, k = 400, 256 * 1  # 400 Q4_K blocks; more for the smaller formats
-    k = {"q4_k": 256 * 250, "q8_0": 32 * 250, "tq1_g128": 128 * 250}[kind]
+    k = {"q4_k": 256 * 250, "q8_0": 32 * 250, "tq1_g128": 128 * 250, "q4_0": 32 * 250,
+         "q5_0": 32 * 250, "q5_1": 32 * 250, "q6_k": 256 * 250}[kind]
     w = synth.weight_blocks(kind, rng, rows, k)
     if kind == "q4_k":
         # also cover arbitrary finite fp16 d/dmin (exponents across the range)
@@ -177,6 +178,99 @@ def test_independent_decoders_agree(orc, kind):
     got = orc.dequant(kind, w, rows, k)
     ref = npd.decode_matrix(kind, w, rows, k)
     assert np.array_equal(got, ref)
+
+
+# ------------------------------------------------------------------ GGUF Q4_0 / Q5_0 / Q5_1 / Q6_K
+# The [MID] page's codec table names these blocks; their layouts are the GGUF
+# convention (a reading).  Pins: hand-built blocks whose every weight is known
+# from its fields, single-bit and single-weight probes of the bit maps, and
+# the independent numpy decoder above.
+@pytest.mark.parametrize("kind", ["q4_0", "q5_0", "q5_1"])
+def test_legacy_blocks_from_fields(orc, kind):
+    """Blocks packed from chosen quants decode to d*(q - 8) (Q4_0), d*(q - 16)
+    (Q5_0) and d*q + m (Q5_1), weight i from quant i."""
+    rng = _rng(60)
+    nb = 64
+    qmax = 16 if kind == "q4_0" else 32
+    q = rng.integers(0, qmax, size=(nb, 32))
+    d16 = rng.uniform(-2.0, 2.0, nb).astype(np.float16)
+    m16 = rng.uniform(-3.0, 3.0, nb).astype(np.float16)
+    blocks = npd.legacy_pack(kind, q, d16, m16)
+    got = orc.dequant(kind, blocks, nb, 32)
+    d, m = d16.astype(np.float64)[:, None], m16.astype(np.float64)[:, None]
+    want = {"q4_0": d * (q - 8), "q5_0": d * (q - 16), "q5_1": d * q + m}[kind]
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("kind", ["q5_0", "q5_1"])
+def test_q5_high_bit_map(orc, kind):
+    """All nibbles zero and a single high bit i set: weight i alone carries the
+    extra 16 (bit i of the little-endian qh word is weight i's fifth bit)."""
+    for i in range(32):
+        q = np.zeros((1, 32), np.int64)
+        q[0, i] = 16
+        blk = npd.legacy_pack(kind, q, np.array([1.0], np.float16), np.array([0.0], np.float16))
+        # the bit sits in qh byte i // 8, bit i % 8
+        qh = blk[0, 2:6] if kind == "q5_0" else blk[0, 4:8]
+        assert qh[i // 8] == 1 << (i % 8) and qh.sum() == qh[i // 8]
+        got = orc.dequant(kind, blk, 1, 32)[0]
+        base = -16.0 if kind == "q5_0" else 0.0
+        want = np.full(32, base)
+        want[i] = base + 16.0
+        assert np.array_equal(got, want)
+
+
+def test_q6k_blocks_from_fields(orc):
+    """Q6_K packed from chosen 6-bit quants and int8 scales decodes to
+    d * scale[j] * (q - 32), scale j for weights 16j..16j+15."""
+    rng = _rng(61)
+    nb = 40
+    q = rng.integers(0, 64, size=(nb, 256))
+    sc = rng.integers(-128, 128, size=(nb, 16))
+    d16 = rng.uniform(-0.5, 0.5, nb).astype(np.float16)
+    blocks = npd.q6k_pack(q, sc, d16)
+    got = orc.dequant("q6_k", blocks, nb, 256)
+    want = d16.astype(np.float64)[:, None] * np.repeat(sc, 16, axis=1) * (q - 32)
+    assert np.array_equal(got, want)
+
+
+def test_q6k_single_weight_probes(orc):
+    """One weight at 32 + v, every other at 32 (zero): exactly that weight is
+    nonzero, for every position, so no two positions share low or high bits."""
+    for e in range(256):
+        q = np.full((1, 256), 32)
+        q[0, e] = 32 + 1 + (e % 31)
+        blk = npd.q6k_pack(q, np.ones((1, 16), np.int64), np.array([1.0], np.float16))
+        got = orc.dequant("q6_k", blk, 1, 256)[0]
+        nz = np.flatnonzero(got)
+        assert list(nz) == [e] and got[e] == 1 + (e % 31)
+
+
+def test_q6k_layout_bytes(orc):
+    """The byte layout: ql[128], qh[64], 16 int8 scales, fp16 d (210 bytes).
+    Raising ql byte 0's low nibble by one raises weight 0 by d*scale[0];
+    its high nibble, weight 64; qh byte 0's bits 2-3 by one, weight 32 by
+    16*d*scale[2]; scale byte 192+5 scales weights 80..95; the last two
+    bytes are d."""
+    blk = np.zeros((1, 210), np.uint8)
+    blk[0, 192:208] = np.arange(1, 17, dtype=np.int8).view(np.uint8)
+    blk[0, 208:210] = np.array([1.0], np.float16).view(np.uint8)
+    base = orc.dequant("q6_k", blk, 1, 256)[0]  # every q = 0: -32 * scale
+    assert np.array_equal(base, -32.0 * np.repeat(np.arange(1, 17), 16))
+    b = blk.copy()
+    b[0, 0] = 0x01
+    assert np.flatnonzero(orc.dequant("q6_k", b, 1, 256)[0] - base).tolist() == [0]
+    b = blk.copy()
+    b[0, 0] = 0x10
+    diff = orc.dequant("q6_k", b, 1, 256)[0] - base
+    assert np.flatnonzero(diff).tolist() == [64] and diff[64] == 1.0 * 5
+    b = blk.copy()
+    b[0, 128] = 0x04
+    diff = orc.dequant("q6_k", b, 1, 256)[0] - base
+    assert np.flatnonzero(diff).tolist() == [32] and diff[32] == 16.0 * 3
+    b = blk.copy()
+    b[0, 197] = 0  # scale 5 -> 0
+    assert np.array_equal(np.flatnonzero(orc.dequant("q6_k", b, 1, 256)[0] - base), np.arange(80, 96))
 
 
 # ------------------------------------------------------------------ Q8_0
@@ -297,7 +391,7 @@ def test_dequant_store_is_rounded_exact_value(orc, kind, dt):
 
 
 # ------------------------------------------------------------------ products
-@pytest.mark.parametrize("kind", ["q4_k", "q8_0", "tq1_g128"])
+@pytest.mark.parametrize("kind", ["q4_k", "q8_0", "tq1_g128", "q4_0", "q5_0", "q5_1", "q6_k"])
 def test_qmm_one_hot_columns(orc, kind):
     """x = e_c gives y[., n] = w[n, c] exactly, for every c."""
     import synth
@@ -324,7 +418,7 @@ def test_qmm_integer_case(orc):
     assert np.array_equal(y[0], nib.reshape(n, -1).sum(axis=1).astype(np.float64))
 
 
-@pytest.mark.parametrize("kind", ["q4_k", "q8_0", "tq1_g128"])
+@pytest.mark.parametrize("kind", ["q4_k", "q8_0", "tq1_g128", "q4_0", "q5_0", "q5_1", "q6_k"])
 @pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
 def test_qmm_brute_force_vs_numpy(orc, kind, dt):
     import synth
