@@ -19,8 +19,29 @@ kq_status fail(kq_status st, const std::string& msg) {
     return st;
 }
 
-int qk_of(int t) { return t == KQ_Q4_K ? 256 : t == KQ_Q8_0 ? 32 : t == KQ_TQ1_G128 ? 128 : 0; }
-int bb_of(int t) { return t == KQ_Q4_K ? 144 : t == KQ_Q8_0 ? 34 : t == KQ_TQ1_G128 ? 28 : 0; }
+int qk_of(int t) {
+    switch (t) {
+    case KQ_Q4_K: case KQ_Q6_K: return 256;
+    case KQ_TQ1_G128: return 128;
+    case KQ_Q8_0: case KQ_Q4_0: case KQ_Q5_0: case KQ_Q5_1: return 32;
+    default: return 0;
+    }
+}
+int bb_of(int t) {
+    switch (t) {
+    case KQ_Q4_K: return 144;
+    case KQ_Q8_0: return 34;
+    case KQ_TQ1_G128: return 28;
+    case KQ_Q4_0: return 18;
+    case KQ_Q5_0: return 22;
+    case KQ_Q5_1: return 24;
+    case KQ_Q6_K: return 210;
+    default: return 0;
+    }
+}
+// the codecs with matrix-core GEMM kernels (and encoders); the other GGUF
+// blocks run every product on the chunk-decoding vector kernel
+static bool mfma_codec(int t) { return t == KQ_Q4_K || t == KQ_Q8_0 || t == KQ_TQ1_G128; }
 int64_t elem_size(int dt) { return dt == KQ_F32 ? 4 : 2; }
 bool valid_dt(int dt) { return dt == KQ_F32 || dt == KQ_F16 || dt == KQ_BF16; }
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
@@ -157,6 +178,7 @@ kq_status kq_dequantize(kq_type t, const void* w, int64_t rows, int64_t k, void*
 kq_status kq_quantize(kq_type t, const void* w, kq_dtype w_dt, int64_t rows, int64_t k,
                       const float* imatrix, void* out, void* stream) {
     if (!qk_of(t)) return fail(KQ_ERR_UNSUPPORTED, "unknown weight type");
+    if (!mfma_codec(t)) return fail(KQ_ERR_UNSUPPORTED, "no encoder for this weight type");
     if (!valid_dt(w_dt)) return fail(KQ_ERR_UNSUPPORTED, "unknown dtype");
     if (imatrix && t != KQ_Q4_K)
         return fail(KQ_ERR_UNSUPPORTED, "an importance vector steers the Q4_K encoder only");
@@ -218,7 +240,7 @@ kq_status kq_qmm(kq_type t, const void* w, int64_t n, int64_t k, const void* x, 
     int64_t row_bytes;
     kq_status st = check_product(t, w, n, k, x, x_dt, m, y, y_dt, row_bytes);
     if (st) return st;
-    if (m <= 16 || x_dt == KQ_F32)
+    if (m <= 16 || x_dt == KQ_F32 || !mfma_codec(t))
         return dense_skinny(t, w, n, k, row_bytes, x, x_dt, m, y, y_dt, (hipStream_t)stream);
     return launched(kq::launch_gemm(t, x_dt, w, n, k, x, m, y, y_dt, nullptr, (hipStream_t)stream));
 }
@@ -228,7 +250,9 @@ kq_status kq_qmm(kq_type t, const void* w, int64_t n, int64_t k, const void* x, 
 // the TQ1 GEMV of one fp16 row splits K when its rows fill few workgroups,
 // with fp32 partials [pieces][n]; the other decode products and the fp32
 // path need no scratch.
-static bool qmm_uses_gemm(int64_t m, kq_dtype x_dt) { return m > 16 && x_dt != KQ_F32; }
+static bool qmm_uses_gemm(kq_type t, int64_t m, kq_dtype x_dt) {
+    return m > 16 && x_dt != KQ_F32 && mfma_codec(t);
+}
 
 static int64_t decode_split_bytes(kq_type t, int64_t n, int64_t k, int64_t m, kq_dtype x_dt,
                                   int* pnb) {
@@ -245,7 +269,7 @@ static int64_t decode_split_bytes(kq_type t, int64_t n, int64_t k, int64_t m, kq
 static int64_t qmm_scratch_bytes(kq_type t, int64_t n, int64_t k, int64_t m, kq_dtype x_dt,
                                  int* pnb) {
     *pnb = 0;
-    if (qmm_uses_gemm(m, x_dt)) return kq::gemm_workspace(t, n, k, m, x_dt).bytes;
+    if (qmm_uses_gemm(t, m, x_dt)) return kq::gemm_workspace(t, n, k, m, x_dt).bytes;
     return decode_split_bytes(t, n, k, m, x_dt, pnb);
 }
 
@@ -254,7 +278,7 @@ static int64_t qmm_scratch_bytes(kq_type t, int64_t n, int64_t k, int64_t m, kq_
 static kq_status qmm_with_scratch(kq_type t, const void* w, int64_t n, int64_t k, int64_t row_bytes,
                                   const void* x, kq_dtype x_dt, int64_t m, void* y, kq_dtype y_dt,
                                   int64_t need, int pnb, void* ws, hipStream_t s) {
-    if (qmm_uses_gemm(m, x_dt))
+    if (qmm_uses_gemm(t, m, x_dt))
         return launched(kq::launch_gemm(t, x_dt, w, n, k, x, m, y, y_dt, need > 0 ? ws : nullptr, s));
     if (need == 0) return dense_skinny(t, w, n, k, row_bytes, x, x_dt, m, y, y_dt, s);
     // the split TQ1 decode product (the only decode shape that takes scratch)

@@ -10,6 +10,8 @@
 //         exact (<= 17 bits); the final fused multiply-subtract rounds once.
 //   Q8_0: d*q is exact (<= 19 bits).
 //   TQ1:  (t-1)*s is exact.
+//   Q4_0 / Q5_0: d*(q-8), d*(q-16) are exact; Q5_1: d*q+m fused, one
+//         rounding; Q6_K: d*sc is exact, (d*sc)*(q-32) rounds once.
 // fp16/bf16 outputs then round that fp32 value to nearest even.
 #include "kq_device.h"
 #include "kq_internal.h"
@@ -129,6 +131,54 @@ __global__ __launch_bounds__(256) void dequant_tq1_kernel(const uint8_t* __restr
     Out8<DT>::store(out, b * 128 + 8 * part, v);
 }
 
+// GGUF Q4_0 / Q5_0 / Q5_1 / Q6_K: one thread per 32-weight chunk, decoded
+// by the shared chunk decoders (kq_device.h); the chunk's 32 outputs are
+// contiguous.  Rows are contiguous in both the blocks and the output, so
+// chunk g of the whole matrix is chunk g of one long row.
+template <int C, int DT>
+__global__ __launch_bounds__(256) void dequant_chunk32_kernel(const uint8_t* __restrict__ w,
+                                                              void* __restrict__ out, int64_t nchunks) {
+    const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (g >= nchunks) return;
+    float v[32];
+    int64_t xa, xb;
+    Chunk32<C>::decode(w, g, v, xa, xb);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        float a[8], b[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) a[i] = v[16 * h + i], b[i] = v[16 * h + 8 + i];
+        const int64_t base = h ? xb : xa;
+        Out8<DT>::store(out, base, a);
+        Out8<DT>::store(out, base + 8, b);
+    }
+}
+
+template <int DT>
+static hipError_t launch_chunk32_dt(int codec, const void* w, int64_t nchunks, void* out,
+                                    hipStream_t s) {
+    // chunks of one launch: a multiple of 8 (Q6_K super-blocks hold 8), and
+    // fewer than 2^31 work-items
+    const int64_t piece = (int64_t)1 << 30;
+    const int64_t bbytes = codec == Q4_0 ? 18 : codec == Q5_0 ? 22 : codec == Q5_1 ? 24 : 210;
+    const int64_t per = codec == Q6_K ? 8 : 1;  // chunks per block
+    for (int64_t c0 = 0; c0 < nchunks; c0 += piece) {
+        const int64_t nc = nchunks - c0 < piece ? nchunks - c0 : piece;
+        const uint8_t* wp = (const uint8_t*)w + c0 / per * bbytes;
+        void* op = (uint8_t*)out + c0 * 32 * (DT == F32 ? 4 : 2);
+        const dim3 grid((unsigned)((nc + 255) / 256)), block(256);
+        switch (codec) {
+        case Q4_0: hipLaunchKernelGGL((dequant_chunk32_kernel<Q4_0, DT>), grid, block, 0, s, wp, op, nc); break;
+        case Q5_0: hipLaunchKernelGGL((dequant_chunk32_kernel<Q5_0, DT>), grid, block, 0, s, wp, op, nc); break;
+        case Q5_1: hipLaunchKernelGGL((dequant_chunk32_kernel<Q5_1, DT>), grid, block, 0, s, wp, op, nc); break;
+        default: hipLaunchKernelGGL((dequant_chunk32_kernel<Q6_K, DT>), grid, block, 0, s, wp, op, nc); break;
+        }
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 template <int DT>
 static hipError_t launch_dequant_dt(int codec, const void* w, int64_t nblocks, void* out,
                                     hipStream_t s) {
@@ -156,6 +206,14 @@ static hipError_t launch_dequant_dt(int codec, const void* w, int64_t nblocks, v
 
 hipError_t launch_dequant(int codec, const void* w, int64_t rows, int64_t k, void* out, int out_dt,
                           hipStream_t s) {
+    if (codec >= Q4_0) {
+        const int64_t nchunks = rows * (k / 32);
+        switch (out_dt) {
+        case F32: return launch_chunk32_dt<F32>(codec, w, nchunks, out, s);
+        case F16: return launch_chunk32_dt<F16>(codec, w, nchunks, out, s);
+        default: return launch_chunk32_dt<BF16>(codec, w, nchunks, out, s);
+        }
+    }
     const int qk = codec == Q4_K ? 256 : codec == Q8_0 ? 32 : 128;
     const int64_t nblocks = rows * (k / qk);
     switch (out_dt) {

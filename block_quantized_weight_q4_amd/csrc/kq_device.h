@@ -19,13 +19,17 @@ typedef float float16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-enum Codec { Q4_K = 0, Q8_0 = 1, TQ1 = 2 };
+enum Codec { Q4_K = 0, Q8_0 = 1, TQ1 = 2, Q4_0 = 3, Q5_0 = 4, Q5_1 = 5, Q6_K = 6 };
 enum DType { F32 = 0, F16 = 1, BF16 = 2 };
 
 template <int C> struct CodecInfo;
 template <> struct CodecInfo<Q4_K> { static constexpr int QK = 256, BYTES = 144; };
 template <> struct CodecInfo<Q8_0> { static constexpr int QK = 32, BYTES = 34; };
 template <> struct CodecInfo<TQ1> { static constexpr int QK = 128, BYTES = 28; };
+template <> struct CodecInfo<Q4_0> { static constexpr int QK = 32, BYTES = 18; };
+template <> struct CodecInfo<Q5_0> { static constexpr int QK = 32, BYTES = 22; };
+template <> struct CodecInfo<Q5_1> { static constexpr int QK = 32, BYTES = 24; };
+template <> struct CodecInfo<Q6_K> { static constexpr int QK = 256, BYTES = 210; };
 
 // ---------------------------------------------------------------- scalars
 __device__ __forceinline__ float half_bits_to_float(uint32_t bits16) {
@@ -152,6 +156,123 @@ template <> __device__ __forceinline__ float weight_exact<TQ1>(const uint8_t* ro
     const uint32_t s = blk[26] | ((uint32_t)blk[27] << 8);
     return (float)tq1_trit(blk[slot], digit) * half_bits_to_float(s);
 }
+
+// ---------------------------------------------------------------- GGUF Q4_0 / Q5_0 / Q5_1 / Q6_K
+// The further GGUF blocks of mlx-native's codec table (GgmlType::Q4_0, Q5_0,
+// Q5_1, Q6_K), in the GGUF layouts (see include/kq.h).  Chunk32<C>::decode
+// gives the 32 weights of chunk q of a row, each the exact value rounded
+// once to fp32: w[0..15] are the weights at columns xa.., w[16..31] at xb..
+// Blocks of 18, 22 and 210 bytes are only 2-byte aligned (read as 16-bit
+// words); Q5_1 blocks are 8-byte aligned.
+template <int C> struct Chunk32;
+
+// Q4_0 chunk q = block q: low nibble of quant byte i is weight i, the high
+// nibble weight i + 16; weight d (q - 8) (exact: 11 + 4 bits).
+template <> struct Chunk32<Q4_0> {
+    static __device__ __forceinline__ void decode(const uint8_t* row, int64_t q, float (&w)[32],
+                                                  int64_t& xa, int64_t& xb) {
+        const uint16_t* blk = (const uint16_t*)(row + q * 18);
+        const float d = half_bits_to_float(blk[0]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t pair = blk[1 + i];  // quant bytes 2i, 2i + 1
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const uint32_t b = (pair >> (8 * h)) & 0xffu;
+                w[2 * i + h] = d * (float)((int)(b & 15u) - 8);
+                w[16 + 2 * i + h] = d * (float)((int)(b >> 4) - 8);
+            }
+        }
+        xa = q * 32;
+        xb = xa + 16;
+    }
+};
+
+// Q5_0 chunk q = block q: fp16 d, qh (32 bits: bit i is weight i's fifth
+// bit), nibbles as in Q4_0; weight d (q - 16) (exact).
+template <> struct Chunk32<Q5_0> {
+    static __device__ __forceinline__ void decode(const uint8_t* row, int64_t q, float (&w)[32],
+                                                  int64_t& xa, int64_t& xb) {
+        const uint16_t* blk = (const uint16_t*)(row + q * 22);
+        const float d = half_bits_to_float(blk[0]);
+        const uint32_t qh = blk[1] | ((uint32_t)blk[2] << 16);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t pair = blk[3 + i];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int j = 2 * i + h;
+                const uint32_t b = (pair >> (8 * h)) & 0xffu;
+                const int q0 = (int)((b & 15u) | (((qh >> j) & 1u) << 4));
+                const int q1 = (int)((b >> 4) | (((qh >> (j + 16)) & 1u) << 4));
+                w[j] = d * (float)(q0 - 16);
+                w[16 + j] = d * (float)(q1 - 16);
+            }
+        }
+        xa = q * 32;
+        xb = xa + 16;
+    }
+};
+
+// Q5_1 chunk q = block q: fp16 d, fp16 m, qh, nibbles; weight d q + m with
+// one rounding (fused).
+template <> struct Chunk32<Q5_1> {
+    static __device__ __forceinline__ void decode(const uint8_t* row, int64_t q, float (&w)[32],
+                                                  int64_t& xa, int64_t& xb) {
+        const uint32_t* blk = (const uint32_t*)(row + q * 24);
+        const float d = half_bits_to_float(blk[0] & 0xffffu), m = half_bits_to_float(blk[0] >> 16);
+        const uint32_t qh = blk[1];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t word = blk[2 + i];  // quant bytes 4i .. 4i + 3
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                const int j = 4 * i + h;
+                const uint32_t b = (word >> (8 * h)) & 0xffu;
+                const uint32_t q0 = (b & 15u) | (((qh >> j) & 1u) << 4);
+                const uint32_t q1 = (b >> 4) | (((qh >> (j + 16)) & 1u) << 4);
+                w[j] = __builtin_fmaf(d, (float)q0, m);
+                w[16 + j] = __builtin_fmaf(d, (float)q1, m);
+            }
+        }
+        xa = q * 32;
+        xb = xa + 16;
+    }
+};
+
+// Q6_K chunk q: super-block q / 8, weights 32p .. 32p + 31 (p = q % 8), i.e.
+// half h = p / 4 and run u = p % 4 of it: weight l of the run takes the low
+// bits of ql[64h + l + 32 (u % 2)] (low nibble for u < 2, high for u >= 2),
+// the high bits (qh[32h + l] >> 2u) & 3 and the scale scales[8h + 2u + l/16];
+// value (d scale) (q - 32): d * scale is exact, the product rounds once.
+template <> struct Chunk32<Q6_K> {
+    static __device__ __forceinline__ void decode(const uint8_t* row, int64_t q, float (&w)[32],
+                                                  int64_t& xa, int64_t& xb) {
+        const int64_t sb = q >> 3;
+        const int p = (int)q & 7, h = p >> 2, u = p & 3;
+        const uint8_t* blk = row + sb * 210;
+        const uint16_t* ql = (const uint16_t*)(blk + 64 * h + 32 * (u & 1));
+        const uint16_t* qh = (const uint16_t*)(blk + 128 + 32 * h);
+        const float d = half_bits_to_float(*(const uint16_t*)(blk + 208));
+        const uint16_t scw = *(const uint16_t*)(blk + 192 + 8 * h + 2 * u);  // scales l/16 = 0, 1
+        const float s0 = d * (float)(int8_t)(scw & 0xffu), s1 = d * (float)(int8_t)(scw >> 8);
+        const int lsh = 4 * (u >> 1), hsh = 2 * u;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const uint32_t lw = ql[i], hw = qh[i];  // bytes 2i, 2i + 1 of the run
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int l = 2 * i + e;
+                const uint32_t lo4 = ((lw >> (8 * e)) >> lsh) & 15u;
+                const uint32_t hi2 = ((hw >> (8 * e)) >> hsh) & 3u;
+                const int qv = (int)(lo4 | (hi2 << 4)) - 32;
+                w[l] = (l < 16 ? s0 : s1) * (float)qv;
+            }
+        }
+        xa = sb * 256 + 32 * p;
+        xb = xa + 16;
+    }
+};
 
 // ---------------------------------------------------------------- wave helpers
 __device__ __forceinline__ float wave_sum(float v) {

@@ -129,6 +129,11 @@ template <> struct Chunk<TQ1> {
     }
 };
 
+// the further GGUF codecs: the shared chunk decoders of kq_device.h
+template <> struct Chunk<Q4_0> : Chunk32<Q4_0> {};
+template <> struct Chunk<Q5_0> : Chunk32<Q5_0> {};
+template <> struct Chunk<Q5_1> : Chunk32<Q5_1> {};
+template <> struct Chunk<Q6_K> : Chunk32<Q6_K> {};
 
 __device__ __forceinline__ void store_any(void* y, int64_t i, int dt, float v) {
     if (dt == F32) store_out<F32>(y, i, v);
@@ -280,6 +285,10 @@ hipError_t launch_skinny(int codec, int x_dt, bool glu, const SkinnyArgs& a, int
     switch (codec) {
     case Q4_K: glu ? launch_x<Q4_K, true>(x_dt, a, mb, grid, s) : launch_x<Q4_K, false>(x_dt, a, mb, grid, s); break;
     case Q8_0: glu ? launch_x<Q8_0, true>(x_dt, a, mb, grid, s) : launch_x<Q8_0, false>(x_dt, a, mb, grid, s); break;
+    case Q4_0: glu ? launch_x<Q4_0, true>(x_dt, a, mb, grid, s) : launch_x<Q4_0, false>(x_dt, a, mb, grid, s); break;
+    case Q5_0: glu ? launch_x<Q5_0, true>(x_dt, a, mb, grid, s) : launch_x<Q5_0, false>(x_dt, a, mb, grid, s); break;
+    case Q5_1: glu ? launch_x<Q5_1, true>(x_dt, a, mb, grid, s) : launch_x<Q5_1, false>(x_dt, a, mb, grid, s); break;
+    case Q6_K: glu ? launch_x<Q6_K, true>(x_dt, a, mb, grid, s) : launch_x<Q6_K, false>(x_dt, a, mb, grid, s); break;
     default: glu ? launch_x<TQ1, true>(x_dt, a, mb, grid, s) : launch_x<TQ1, false>(x_dt, a, mb, grid, s); break;
     }
     return hipGetLastError();

@@ -30,6 +30,29 @@
  *                above 26) are not valid input; legality is checked when
  *                weights are produced, not by these kernels.
  *
+ * The further GGUF blocks that mlx-native "quantized_matmul_id_ggml.rs"
+ * dispatches (GgmlType::Q4_0, Q5_0, Q5_1 and Q6_K in its mv_id / mm_id kernel
+ * tables).  The page names them without printing a layout; these are the
+ * GGUF layouts:
+ *   KQ_Q4_0      32 weights in 18 bytes: fp16 d, 16 bytes of nibbles (low
+ *                nibble of byte i is weight i, high nibble weight i + 16);
+ *                w = d * (q - 8).
+ *   KQ_Q5_0      32 weights in 22 bytes: fp16 d, uint32 qh (bit i is weight
+ *                i's fifth bit), 16 bytes of nibbles as in Q4_0;
+ *                w = d * (q - 16).
+ *   KQ_Q5_1      32 weights in 24 bytes: fp16 d, fp16 m, uint32 qh, 16 bytes
+ *                of nibbles; w = d * q + m.
+ *   KQ_Q6_K      256 weights in 210 bytes: ql[128] (low four bits), qh[64]
+ *                (high two bits), int8 scales[16], fp16 d.  Weight
+ *                128h + 32u + l (h < 2, u < 4, l < 32) takes the low (u < 2)
+ *                or high nibble of ql[64h + 32(u % 2) + l], bits 2u..2u+1 of
+ *                qh[32h + l] and scales[8h + 2u + l / 16];
+ *                w = d * scale * (q - 32).
+ * These four are decoded and multiplied (kq_dequantize, the products and the
+ * expert-routed forms) but not encoded (kq_quantize -> KQ_ERR_UNSUPPORTED);
+ * their products run on the vector units (no matrix-core kernel is built for
+ * them), for every m.
+ *
  * All multi-byte fields are little-endian.  fp16 is IEEE binary16; bf16 is
  * the upper half of an IEEE binary32.
  */
@@ -43,7 +66,15 @@
 extern "C" {
 #endif
 
-typedef enum kq_type { KQ_Q4_K = 0, KQ_Q8_0 = 1, KQ_TQ1_G128 = 2 } kq_type;
+typedef enum kq_type {
+    KQ_Q4_K = 0,
+    KQ_Q8_0 = 1,
+    KQ_TQ1_G128 = 2,
+    KQ_Q4_0 = 3,
+    KQ_Q5_0 = 4,
+    KQ_Q5_1 = 5,
+    KQ_Q6_K = 6
+} kq_type;
 
 typedef enum kq_dtype { KQ_F32 = 0, KQ_F16 = 1, KQ_BF16 = 2 } kq_dtype;
 
@@ -142,7 +173,8 @@ kq_status kq_dequantize(kq_type t, const void* w, int64_t rows, int64_t k, void*
  * sub-blocks use levels 0 and 15 and whose largest sc and m are 63) encodes
  * back to its own bytes.
  * Errors: rows or k <= 0, k % QK != 0, null or misaligned pointers, out
- * overlapping an input -> KQ_ERR_INVALID_ARG.
+ * overlapping an input -> KQ_ERR_INVALID_ARG; Q4_0, Q5_0, Q5_1 and Q6_K ->
+ * KQ_ERR_UNSUPPORTED (no encoder is built for them).
  */
 kq_status kq_quantize(kq_type t, const void* w, kq_dtype w_dt, int64_t rows, int64_t k,
                       const float* imatrix, void* out, void* stream);

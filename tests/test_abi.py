@@ -99,6 +99,32 @@ def test_block_geometry(kq):
     assert kq.lib().kq_qk(7) == 0
 
 
+def test_ggml_block_geometry(kq):
+    """The further GGUF blocks: QK and block bytes of the GGUF layouts, and
+    their row strides."""
+    for kind, qk, bb in (("q4_0", 32, 18), ("q5_0", 32, 22), ("q5_1", 32, 24), ("q6_k", 256, 210)):
+        assert (kq.kq_qk(kind), kq.kq_block_bytes(kind)) == (qk, bb), kind
+        assert kq.kq_row_bytes(kind, 4096) == 4096 // qk * bb, kind
+    assert kq.kq_row_bytes("q6_k", 4096 + 32) == -1
+
+
+def test_ggml_codecs_take_no_scratch_and_no_encoder(kq):
+    """Their products run on the vector kernel for every m: no workspace for
+    any shape; kq_quantize rejects them before touching memory."""
+    import torch
+
+    for kind in ("q4_0", "q5_0", "q5_1", "q6_k"):
+        for m, dt in ((1, torch.float16), (16, torch.bfloat16), (512, torch.float16),
+                      (2048, torch.bfloat16)):
+            assert kq.kq_qmm_workspace_bytes(kind, 512, 4096, m, dt) == 0, (kind, m)
+    L = kq.lib()
+    P = C.c_void_p
+    base = 1 << 40
+    for t in (3, 4, 5, 6):
+        assert L.kq_quantize(t, P(base), 0, 4, 256, None, P(base + (1 << 30)), None) == 2
+        assert kq.kq_last_error() == "no encoder for this weight type"
+
+
 def test_status_strings(kq):
     assert kq.kq_status_string(0) == "ok"
     for s in range(1, 5):

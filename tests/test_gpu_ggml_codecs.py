@@ -1,0 +1,246 @@
+"""GPU parity of the further GGUF blocks (Q4_0, Q5_0, Q5_1, Q6_K) against the
+CPU oracle, through the C ABI, over every entry point that takes them.
+
+mlx-native "quantized_matmul_id_ggml.rs" dispatches these four types
+(GgmlType::Q4_0, Q5_0, Q5_1, Q6_K) to its mv_id / mm_id kernels.  Here they
+decode chunk by chunk on the vector units for every product shape, so the
+weights enter the products as exact fp32 values: dequantization is compared
+bit for bit, products with |gpu - ref| <= tau * sum|w*x| as for the other
+codecs, and a one-hot activation returns the decoded column exactly.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests.gpu_util import TAU, bits, check_tol, device, empty, to_dev, to_f64
+
+pytestmark = pytest.mark.gpu
+
+KINDS = ["q4_0", "q5_0", "q5_1", "q6_k"]
+QK = {"q4_0": 32, "q5_0": 32, "q5_1": 32, "q6_k": 256}
+
+
+@pytest.fixture(scope="module")
+def kq():
+    from block_quantized_weight_q4_amd import _build, kq as mod
+
+    _build.build_if_missing()
+    mod.lib()
+    return mod
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+def _ids(rng, T, E, top_k):
+    return np.stack([rng.choice(E, top_k, replace=False) for _ in range(T)]).astype(np.uint32)
+
+
+def _moe_ws(kq, E, T, top_k, n_out=0):
+    return torch.empty(kq.kq_moe_workspace_bytes(E, T, top_k, n_out), dtype=torch.uint8,
+                       device=device())
+
+
+# ---------------------------------------------------------------- dequantize
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("rows,nblk", [(1, 1), (7, 3), (129, 5), (300, 48)])
+def test_dequant_bit_exact(kq, kind, dt, rows, nblk):
+    k = QK[kind] * nblk
+    _say("dequant", kind, dt, rows, k)
+    w = synth.weight_blocks(kind, synth.rng_for(5000 + rows), rows, k)
+    out = empty((rows, k), dt)
+    kq.kq_dequantize(kind, to_dev(w), rows, k, out)
+    torch.cuda.synchronize()
+    ref = oracle.dequant_as(kind, w, rows, k, dt)
+    assert np.array_equal(bits(out), ref.view(np.uint32) if dt == "f32" else ref)
+
+
+# ---------------------------------------------------------------- products
+def _run(kq, fn, kind, w, n, k, x, x_dt, m, y_dt):
+    wd, xd = to_dev(w), to_dev(x, x_dt)
+    y = empty((m, n), y_dt)
+    if fn == "kq_qmm_ws":
+        assert kq.kq_qmm_workspace_bytes(kind, n, k, m, xd.dtype) == 0
+        ws = torch.empty(256, dtype=torch.uint8, device=xd.device)
+        kq.kq_qmm_ws(kind, wd, n, k, xd, m, y, ws)
+    else:
+        getattr(kq, fn)(kind, wd, n, k, xd, m, y)
+    torch.cuda.synchronize()
+    return to_f64(y)
+
+
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("x_dt", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("m", [1, 4, 16])
+@pytest.mark.parametrize("n,nblk", [(67, 6), (130, 150)])
+def test_qmv(kq, kind, x_dt, m, n, nblk):
+    # 150 blocks of 32 (or 19 super-blocks of Q6_K, 152 chunks): each lane
+    # of a wave takes two or three chunks, the last pass ragged
+    if kind == "q6_k":
+        nblk = max(1, nblk * 32 // 256)
+    k = QK[kind] * nblk
+    rng = synth.rng_for(5100 + m + n)
+    w = synth.weight_blocks(kind, rng, n, k)
+    x = synth.activations(rng, (m, k), x_dt)
+    for y_dt in ("f32", "f16", "bf16"):
+        _say("qmv", kind, x_dt, m, n, k, y_dt)
+        got = _run(kq, "kq_qmv", kind, w, n, k, x, x_dt, m, y_dt)
+        ref, s = oracle.qmm(kind, w, n, k, x, x_dt, m)
+        check_tol(got, ref, s, TAU[x_dt], f"qmv {kind} {x_dt} m={m} y={y_dt}",
+                  out_dt=y_dt if y_dt != "f32" else None)
+
+
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("x_dt", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("m", [17, 40, 130])
+@pytest.mark.parametrize("fn", ["kq_qmm", "kq_qmm_ws", "kq_qmm_noalloc"])
+def test_qmm(kq, kind, x_dt, m, fn):
+    """m > 16: tiles of 16 activation rows plus a ragged one, through the
+    three prefill entry points (none of which takes scratch here)."""
+    n, k = 75, QK[kind] * (9 if kind == "q6_k" else 70)
+    rng = synth.rng_for(5200 + m)
+    w = synth.weight_blocks(kind, rng, n, k)
+    x = synth.activations(rng, (m, k), x_dt)
+    _say("qmm", kind, x_dt, m, fn)
+    got = _run(kq, fn, kind, w, n, k, x, x_dt, m, "f32")
+    ref, s = oracle.qmm(kind, w, n, k, x, x_dt, m)
+    check_tol(got, ref, s, TAU[x_dt], f"{fn} {kind} {x_dt} m={m}")
+
+
+@pytest.mark.parametrize("kind", KINDS)
+def test_one_hot_columns_exact(kq, kind):
+    """x = e_c returns column c of the decoded weights exactly, for every c,
+    in the decode (m <= 16) and the prefill (m = k) forms and with fp32 and
+    fp16 activations: the weights are never rounded below fp32."""
+    n, k = 40, QK[kind] * (2 if kind == "q6_k" else 8)
+    w = synth.weight_blocks(kind, synth.rng_for(5300), n, k)
+    W = oracle.dequant(kind, w, n, k).astype(np.float32)
+    for fn, m, x_dt in (("kq_qmv", 16, "f32"), ("kq_qmm", k, "f32"), ("kq_qmm", k, "f16")):
+        for c0 in range(0, k, m):
+            mm = min(m, k - c0)
+            x = np.zeros((mm, k), np.float32)
+            x[np.arange(mm), c0 + np.arange(mm)] = 1.0
+            _say("one-hot", kind, fn, x_dt, c0)
+            xa = x if x_dt == "f32" else x.astype(np.float16).view(np.uint16)
+            got = _run(kq, fn, kind, w, n, k, xa, x_dt, mm, "f32")
+            assert np.array_equal(got, W[:, c0:c0 + mm].T), (fn, x_dt, c0)
+
+
+# ---------------------------------------------------------------- expert-routed forms
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("x_dt", ["f16", "f32"])
+@pytest.mark.parametrize("layout", [0, 1])
+@pytest.mark.parametrize("mixed", [False, True])
+@pytest.mark.parametrize("E,T,top_k", [(8, 1, 8), (8, 5, 3), (4, 70, 4)])
+def test_qmm_id(kq, kind, x_dt, layout, mixed, E, T, top_k):
+    n, k = 96, QK[kind] * (2 if kind == "q6_k" else 12)
+    rng = synth.rng_for(5400 + T)
+    w = synth.weight_blocks(kind, rng, E * n, k)
+    stride = n * synth.row_bytes(kind, k)
+    ids = _ids(rng, T, E, top_k)
+    scores = rng.uniform(0.05, 1.0, size=(T, top_k)).astype(np.float32)
+    x_rows = T if layout == 0 else T * top_k
+    x = synth.activations(rng, (x_rows, k), x_dt)
+    _say("qmm_id", kind, x_dt, layout, mixed, E, T, top_k)
+    y = empty((T if mixed else T * top_k, n), "f32")
+    ws = _moe_ws(kq, E, T, top_k, n if mixed else 0)
+    kq.kq_qmm_id(kind, to_dev(w), E, n, k, stride, to_dev(x, x_dt), layout, to_dev(ids), T,
+                 top_k, to_dev(scores) if mixed else None, y, ws)
+    torch.cuda.synchronize()
+    ref, s = oracle.qmm_id(kind, w, E, n, k, stride, x, x_dt, layout == 1, ids, T, top_k,
+                           scores if mixed else None)
+    check_tol(to_f64(y), ref, s, TAU[x_dt], f"qmm_id {kind} {x_dt}")
+
+
+def _glu_bound_ok(h, ref, tau, act, limit):
+    """The GLU bound of the other codecs' tests (fp32 outputs): the gate and
+    up products within tau of the oracle's, through max|act'| <= 1.13 and
+    |act(g)|, plus one rounding of the stored value."""
+    g, u, sg, su = ref["g"], ref["u"], ref["sg"], ref["su"]
+    with np.errstate(over="ignore"):
+        if act == 1:
+            a_g = 0.5 * g * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (g + 0.044715 * g ** 3)))
+        else:
+            gc = np.minimum(g, limit) if act == 2 else g
+            a_g = gc / (1.0 + np.exp(-gc))
+    comp = tau * (1.13 * np.abs(u) * sg + np.abs(a_g) * su)
+    bound = comp * (1.0 + 2.0**-24) + 2.0**-24 * np.abs(ref["h"]) + 2.0**-150
+    return not np.isnan(h).any() and bool((np.abs(h - ref["h"]) <= bound).all())
+
+
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("x_dt", ["f16", "f32"])
+@pytest.mark.parametrize("T", [1, 9, 40])
+@pytest.mark.parametrize("act", [0, 1])
+def test_moe_glu(kq, kind, x_dt, T, act):
+    E, n, top_k = 6, 80, 3
+    k = QK[kind] * (2 if kind == "q6_k" else 10)
+    rng = synth.rng_for(5500 + T)
+    gate = synth.weight_blocks(kind, rng, E * n, k)
+    up = synth.weight_blocks(kind, rng, E * n, k)
+    stride = n * synth.row_bytes(kind, k)
+    ids = _ids(rng, T, E, top_k)
+    x = synth.activations(rng, (T, k), x_dt)
+    _say("moe_glu", kind, x_dt, T, act)
+    h = empty((T, top_k, n), "f32")
+    ws = _moe_ws(kq, E, T, top_k)
+    kq.kq_moe_glu(kind, to_dev(gate), to_dev(up), E, n, k, stride, to_dev(x, x_dt), to_dev(ids),
+                  T, top_k, h, ws, act)
+    torch.cuda.synchronize()
+    ref = oracle.moe_glu(kind, gate, up, E, n, k, stride, x, x_dt, ids, T, top_k, act)
+    assert _glu_bound_ok(to_f64(h), ref, TAU[x_dt], act, 0.0), f"moe_glu {kind} {x_dt} T={T}"
+
+
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("T", [1, 40])
+def test_moe_glu_ex_shexp_silu_limit(kq, kind, T):
+    """silu_limit and a shared expert in the last slot (kq_moe_glu_ex)."""
+    E, n, top_k, limit = 6, 80, 3, 5.0
+    k = QK[kind] * (2 if kind == "q6_k" else 10)
+    rng = synth.rng_for(5600 + T)
+    gate = synth.weight_blocks(kind, rng, E * n, k)
+    up = synth.weight_blocks(kind, rng, E * n, k)
+    sg = synth.weight_blocks(kind, rng, n, k)
+    su = synth.weight_blocks(kind, rng, n, k)
+    stride = n * synth.row_bytes(kind, k)
+    ids = _ids(rng, T, E, top_k)
+    x = synth.activations(rng, (T, k), "f16")
+    _say("moe_glu_ex", kind, T)
+    h = empty((T, top_k + 1, n), "f32")
+    ws = _moe_ws(kq, E + 1, T, top_k + 1)
+    kq.kq_moe_glu_ex(kind, to_dev(gate), to_dev(up), E, n, k, stride, to_dev(x, "f16"),
+                     to_dev(ids), T, top_k, h, ws, 2, limit, to_dev(sg), to_dev(su))
+    torch.cuda.synchronize()
+    ref = oracle.moe_glu_ex(kind, gate, up, E, n, k, stride, x, "f16", ids, T, top_k, 2, limit,
+                            sg, su)
+    assert _glu_bound_ok(to_f64(h), ref, TAU["f16"], 2, limit), f"glu_ex {kind} T={T}"
+
+
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("x_dt", ["f16", "f32"])
+@pytest.mark.parametrize("T", [1, 5, 40])
+def test_qmm_id_mix_shexp(kq, kind, x_dt, T):
+    E, top_k, n = 6, 3, 72
+    k = QK[kind] * (2 if kind == "q6_k" else 10)
+    rng = synth.rng_for(5700 + T)
+    w = synth.weight_blocks(kind, rng, E * n, k)
+    wsh = synth.weight_blocks(kind, rng, n, k)
+    stride = n * synth.row_bytes(kind, k)
+    ids = _ids(rng, T, E, top_k)
+    x = synth.activations(rng, (T * (top_k + 1), k), x_dt)
+    scores = rng.uniform(0.05, 1.0, size=(T, top_k + 1)).astype(np.float32)
+    _say("mix shexp", kind, x_dt, T)
+    y = empty((T, n), "f32")
+    ws = _moe_ws(kq, E + 1, T, top_k + 1, n)
+    kq.kq_qmm_id_mix_shexp(kind, to_dev(w), E, n, k, stride, to_dev(wsh), to_dev(x, x_dt),
+                           to_dev(ids), T, top_k, to_dev(scores), y, ws)
+    torch.cuda.synchronize()
+    ref, s = oracle.qmm_id_mix_shexp(kind, w, E, n, k, stride, wsh, x, x_dt, ids, T, top_k, scores)
+    check_tol(to_f64(y), ref, s, TAU[x_dt], f"mix shexp {kind} {x_dt} T={T}")
