@@ -27,8 +27,8 @@
  *  the [KQ] and [MID] pages name ("q4_k", GgmlType::Q4_K).  The pages never
  *  print its bit packing; the packing used here is the GGUF convention and is
  *  a documented reading, pinned by hand-built blocks in the tests.
- *  Q4_0, Q5_0, Q5_1 and Q6_K are the further GGUF blocks of the [MID] page's
- *  codec table (GgmlType::Q4_0, Q5_0, Q5_1, Q6_K and their mv_id / mm_id
+ *  Q4_0, Q5_0, Q5_1, Q6_K, Q2_K, Q3_K and Q5_K are the further GGUF blocks of
+ *  the [MID] page's codec table (GgmlType::Q4_0 ... Q5_K and their mv_id / mm_id
  *  kernel names); the page names them without printing a layout, so their
  *  layouts below are the GGUF convention as well -- readings, pinned by
  *  hand-built blocks and an independent decoder in the tests.
@@ -40,7 +40,10 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { OR_Q4_K = 0, OR_Q8_0 = 1, OR_TQ1 = 2, OR_Q4_0 = 3, OR_Q5_0 = 4, OR_Q5_1 = 5, OR_Q6_K = 6 };
+enum {
+    OR_Q4_K = 0, OR_Q8_0 = 1, OR_TQ1 = 2, OR_Q4_0 = 3, OR_Q5_0 = 4, OR_Q5_1 = 5, OR_Q6_K = 6,
+    OR_Q2_K = 7, OR_Q3_K = 8, OR_Q5_K = 9
+};
 enum { OR_F32 = 0, OR_F16 = 1, OR_BF16 = 2 };
 
 /* ------------------------------------------------------------------ */
@@ -287,6 +290,79 @@ void or_decode_q6_k(const uint8_t* blk, double* out) {
             }
 }
 
+/* Q2_K super-block (256 weights, 84 bytes): 16 scale bytes (low nibble the
+ * scale, high nibble the min of 16 weights), qs[64] of 2-bit quants, fp16 d,
+ * fp16 dmin.  Like Q6_K it is two halves of 128 weights, each four runs of
+ * 32: weight 128h + 32u + l takes bits 2u..2u+1 of qs[32h + l] and scale
+ * byte 8h + 2u + l / 16, and is d * scale * q - dmin * min. */
+void or_decode_q2_k(const uint8_t* blk, double* out) {
+    const uint8_t* sc = blk;
+    const uint8_t* qs = blk + 16;
+    double d = or_half_to_double(le16(blk + 80));
+    double dmin = or_half_to_double(le16(blk + 82));
+    for (int h = 0; h < 2; ++h)
+        for (int u = 0; u < 4; ++u)
+            for (int l = 0; l < 32; ++l) {
+                int q = (qs[32 * h + l] >> (2 * u)) & 3;
+                int s = sc[8 * h + 2 * u + l / 16];
+                out[128 * h + 32 * u + l] = d * (s & 15) * q - dmin * (s >> 4);
+            }
+}
+
+/* The 6-bit scale i (0..15) of a Q3_K super-block from its 12 packed bytes
+ * S: the low four bits are the low nibble of S[i] for i < 8 and the high
+ * nibble of S[i - 8] for i >= 8; the top two bits are bits 2 (i / 4) and
+ * 2 (i / 4) + 1 of S[8 + i % 4].  The stored value is offset by 32. */
+int or_q3k_scale(const uint8_t* S, int i) {
+    int low = i < 8 ? (S[i] & 15) : (S[i - 8] >> 4);
+    int top = (S[8 + i % 4] >> (2 * (i / 4))) & 3;
+    return (low | (top << 4)) - 32;
+}
+
+/* Q3_K super-block (256 weights, 110 bytes): hmask[32], qs[64] of 2-bit
+ * quants, 12 bytes of packed 6-bit scales, fp16 d.  Weight 128h + 32u + l
+ * takes bits 2u..2u+1 of qs[32h + l] as its low bits and bit 4h + u of
+ * hmask[l] as its third bit; a clear third bit subtracts 4, so the quant
+ * lies in -4..3.  Its scale is scale 8h + 2u + l / 16, and the weight is
+ * d * scale * q. */
+void or_decode_q3_k(const uint8_t* blk, double* out) {
+    const uint8_t* hm = blk;
+    const uint8_t* qs = blk + 32;
+    const uint8_t* S = blk + 96;
+    double d = or_half_to_double(le16(blk + 108));
+    for (int h = 0; h < 2; ++h)
+        for (int u = 0; u < 4; ++u)
+            for (int l = 0; l < 32; ++l) {
+                int low = (qs[32 * h + l] >> (2 * u)) & 3;
+                int third = (hm[l] >> (4 * h + u)) & 1;
+                int q = low - (third ? 0 : 4);
+                out[128 * h + 32 * u + l] = d * or_q3k_scale(S, 8 * h + 2 * u + l / 16) * q;
+            }
+}
+
+/* Q5_K super-block (256 weights, 176 bytes): fp16 d, fp16 dmin, the 12 scale
+ * and min bytes of Q4_K, qh[32], qs[128] of nibbles laid out as in Q4_K.
+ * Weight 32j + l of sub-block j (0..7) has the nibble Q4_K gives it as its
+ * low four bits and bit j of qh[l] as its fifth, and is
+ * d * sc_j * q - dmin * m_j. */
+void or_decode_q5_k(const uint8_t* blk, double* out) {
+    double d = or_half_to_double(le16(blk));
+    double dmin = or_half_to_double(le16(blk + 2));
+    const uint8_t* S = blk + 4;
+    const uint8_t* qh = blk + 16;
+    const uint8_t* qs = blk + 48;
+    for (int j = 0; j < 8; ++j) {
+        int sc, m;
+        or_q4k_scale_min(S, j, &sc, &m);
+        for (int l = 0; l < 32; ++l) {
+            int byte = qs[32 * (j / 2) + l];
+            int nib = (j % 2) ? (byte >> 4) : (byte & 15);
+            int q = nib | (((qh[l] >> j) & 1) << 4);
+            out[32 * j + l] = d * sc * q - dmin * m;
+        }
+    }
+}
+
 int or_qk(int type) {
     switch (type) {
     case OR_Q4_K: return 256;
@@ -296,6 +372,9 @@ int or_qk(int type) {
     case OR_Q5_0: return 32;
     case OR_Q5_1: return 32;
     case OR_Q6_K: return 256;
+    case OR_Q2_K: return 256;
+    case OR_Q3_K: return 256;
+    case OR_Q5_K: return 256;
     }
     return 0;
 }
@@ -309,6 +388,9 @@ int or_block_bytes(int type) {
     case OR_Q5_0: return 22;
     case OR_Q5_1: return 24;
     case OR_Q6_K: return 210;
+    case OR_Q2_K: return 84;
+    case OR_Q3_K: return 110;
+    case OR_Q5_K: return 176;
     }
     return 0;
 }
@@ -322,6 +404,9 @@ static void decode_block(int type, const uint8_t* blk, double* out) {
     case OR_Q5_0: or_decode_q5_0(blk, out); break;
     case OR_Q5_1: or_decode_q5_1(blk, out); break;
     case OR_Q6_K: or_decode_q6_k(blk, out); break;
+    case OR_Q2_K: or_decode_q2_k(blk, out); break;
+    case OR_Q3_K: or_decode_q3_k(blk, out); break;
+    case OR_Q5_K: or_decode_q5_k(blk, out); break;
     }
 }
 

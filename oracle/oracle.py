@@ -17,10 +17,11 @@ from .build import build_oracle
 __all__ = [
     "TYPES", "DTYPES", "lib", "half_to_double", "bf16_to_double", "float_to_half_rne",
     "float_to_bf16_rne", "q4k_scale_min", "dequant", "dequant_as", "qmm", "qmm_points",
-    "qmm_id", "moe_glu", "moe_layer", "route", "routing_poisons_all", "quantize", "tq1_illegal", "silu_limit", "moe_glu_ex", "qmm_id_mix_shexp", "silu", "gelu_tanh", "num_threads",
+    "qmm_id", "moe_glu", "moe_layer", "route", "routing_poisons_all", "quantize", "tq1_illegal", "silu_limit", "moe_glu_ex", "qmm_id_mix_shexp", "silu", "gelu_tanh", "num_threads", "q3k_scale",
 ]
 
-TYPES = {"q4_k": 0, "q8_0": 1, "tq1_g128": 2, "q4_0": 3, "q5_0": 4, "q5_1": 5, "q6_k": 6}
+TYPES = {"q4_k": 0, "q8_0": 1, "tq1_g128": 2, "q4_0": 3, "q5_0": 4, "q5_1": 5, "q6_k": 6,
+         "q2_k": 7, "q3_k": 8, "q5_k": 9}
 DTYPES = {"f32": 0, "f16": 1, "bf16": 2}
 
 _lib = None
@@ -49,6 +50,8 @@ def lib():
         L.or_gelu_tanh.argtypes = [C.c_double]
         L.or_q4k_scale_min.restype = None
         L.or_q4k_scale_min.argtypes = [P, C.c_int, C.POINTER(C.c_int), C.POINTER(C.c_int)]
+        L.or_q3k_scale.restype = C.c_int
+        L.or_q3k_scale.argtypes = [P, C.c_int]
         L.or_dequant.restype = C.c_int
         L.or_dequant.argtypes = [C.c_int, P, i64, i64, P]
         L.or_dequant_store.restype = C.c_int
@@ -132,6 +135,13 @@ def q4k_scale_min(scale_bytes, j: int):
     sc, m = C.c_int(), C.c_int()
     lib().or_q4k_scale_min(_p(s), int(j), C.byref(sc), C.byref(m))
     return sc.value, m.value
+
+
+def q3k_scale(scale_bytes, i: int) -> int:
+    """Signed scale i (0..15) of a Q3_K super-block's 12 packed scale bytes."""
+    s = _c(scale_bytes, np.uint8)
+    assert s.size == 12
+    return int(lib().or_q3k_scale(_p(s), int(i)))
 
 
 def dequant(kind: str, w: np.ndarray, rows: int, k: int) -> np.ndarray:

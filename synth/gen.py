@@ -28,14 +28,16 @@ import numpy as np
 
 __all__ = [
     "QK", "BLOCK_BYTES", "TYPE_NAMES", "rng_for", "q4k_blocks", "q8_0_blocks",
-    "tq1_blocks", "legacy_blocks", "q6k_blocks", "weight_blocks", "activations", "moe_routing",
+    "tq1_blocks", "legacy_blocks", "q6k_blocks", "kquant_blocks", "weight_blocks", "activations",
+    "moe_routing",
     "row_bytes",
 ]
 
-TYPE_NAMES = ("q4_k", "q8_0", "tq1_g128", "q4_0", "q5_0", "q5_1", "q6_k")
-QK = {"q4_k": 256, "q8_0": 32, "tq1_g128": 128, "q4_0": 32, "q5_0": 32, "q5_1": 32, "q6_k": 256}
+TYPE_NAMES = ("q4_k", "q8_0", "tq1_g128", "q4_0", "q5_0", "q5_1", "q6_k", "q2_k", "q3_k", "q5_k")
+QK = {"q4_k": 256, "q8_0": 32, "tq1_g128": 128, "q4_0": 32, "q5_0": 32, "q5_1": 32, "q6_k": 256,
+      "q2_k": 256, "q3_k": 256, "q5_k": 256}
 BLOCK_BYTES = {"q4_k": 144, "q8_0": 34, "tq1_g128": 28, "q4_0": 18, "q5_0": 22, "q5_1": 24,
-               "q6_k": 210}
+               "q6_k": 210, "q2_k": 84, "q3_k": 110, "q5_k": 176}
 
 SCALE_LO = 1e-3
 SCALE_HI = 2e-2
@@ -108,10 +110,30 @@ def q6k_blocks(rng: np.random.Generator, rows: int, k: int) -> np.ndarray:
     return blk.reshape(rows, row_bytes("q6_k", k))
 
 
+def kquant_blocks(kind: str, rng: np.random.Generator, rows: int, k: int) -> np.ndarray:
+    """uint8 [rows, row_bytes]: random Q2_K / Q3_K / Q5_K super-blocks: random
+    quant and scale bytes, fp16 d (and dmin) in [1e-3, 2e-2]."""
+    bb = BLOCK_BYTES[kind]
+    nb = rows * (k // 256)
+    blk = rng.integers(0, 256, size=(nb, bb), dtype=np.uint8)
+    if kind == "q2_k":
+        blk[:, 80:82] = _fp16_scales(rng, nb)
+        blk[:, 82:84] = _fp16_scales(rng, nb)
+    elif kind == "q3_k":
+        blk[:, 108:110] = _fp16_scales(rng, nb)
+    else:
+        blk[:, 0:2] = _fp16_scales(rng, nb)
+        blk[:, 2:4] = _fp16_scales(rng, nb)
+    return blk.reshape(rows, row_bytes(kind, k))
+
+
 _GEN = {"q4_k": q4k_blocks, "q8_0": q8_0_blocks, "tq1_g128": tq1_blocks, "q6_k": q6k_blocks,
         "q4_0": lambda rng, r, k: legacy_blocks("q4_0", rng, r, k),
         "q5_0": lambda rng, r, k: legacy_blocks("q5_0", rng, r, k),
-        "q5_1": lambda rng, r, k: legacy_blocks("q5_1", rng, r, k)}
+        "q5_1": lambda rng, r, k: legacy_blocks("q5_1", rng, r, k),
+        "q2_k": lambda rng, r, k: kquant_blocks("q2_k", rng, r, k),
+        "q3_k": lambda rng, r, k: kquant_blocks("q3_k", rng, r, k),
+        "q5_k": lambda rng, r, k: kquant_blocks("q5_k", rng, r, k)}
 
 
 def weight_blocks(kind: str, rng: np.random.Generator, rows: int, k: int) -> np.ndarray:

@@ -193,11 +193,115 @@ def q6k_pack(q: np.ndarray, sc: np.ndarray, d16: np.ndarray) -> np.ndarray:
                            np.asarray(sc, dtype=np.int8).view(np.uint8), _f16_bytes(d16)], axis=1)
 
 
+# ---------------------------------------------------------------- GGUF Q2_K / Q3_K / Q5_K
+def _run_maps():
+    """Per weight position e of a 256-weight super-block laid out as two
+    halves of four 32-weight runs: the quant byte (32h + l), the 2-bit shift
+    within it (2u), the 16-weight scale index (8h + 2u + l // 16) and the
+    plane of the third bit (4h + u) for Q3_K."""
+    e = np.arange(256)
+    h, u, l = e // 128, (e % 128) // 32, e % 32
+    return 32 * h + l, 2 * u, 8 * h + 2 * u + l // 16, 4 * h + u
+
+
+def q2k_decode(blocks: np.ndarray) -> np.ndarray:
+    b = np.asarray(blocks, dtype=np.uint8).reshape(-1, 84)
+    scb, qs = b[:, 0:16].astype(np.int64), b[:, 16:80].astype(np.int64)
+    d = f16_bits_to_f64(b[:, 80:82].copy().view("<u2")[:, 0])
+    dmin = f16_bits_to_f64(b[:, 82:84].copy().view("<u2")[:, 0])
+    qb, qsh, si, _ = _run_maps()
+    q = (qs[:, qb] >> qsh) & 3
+    sc = scb[:, si]
+    return d[:, None] * (sc & 15) * q - dmin[:, None] * (sc >> 4)
+
+
+def q2k_pack(q, sc, mn, d16, dmin16) -> np.ndarray:
+    """Q2_K blocks from quants q [nb,256] in 0..3, scales and mins [nb,16] in
+    0..15, fp16 d and dmin [nb]."""
+    q = np.asarray(q, dtype=np.int64)
+    nb = q.shape[0]
+    qb, qsh, _, _ = _run_maps()
+    qs = np.zeros((nb, 64), dtype=np.int64)
+    for e in range(256):
+        qs[:, qb[e]] |= q[:, e] << qsh[e]
+    scb = (np.asarray(sc, np.int64) & 15) | ((np.asarray(mn, np.int64) & 15) << 4)
+    return np.concatenate([scb.astype(np.uint8), qs.astype(np.uint8), _f16_bytes(d16),
+                           _f16_bytes(dmin16)], axis=1)
+
+
+def q3k_scales(S: np.ndarray) -> np.ndarray:
+    """12 packed bytes [nb,12] -> the 16 signed scales [nb,16] (stored + 32):
+    nibble planes from bytes 0..7 (low nibbles first, then high nibbles),
+    2-bit planes from bytes 8..11 (bit pair p of byte 8 + r is scale 4p + r)."""
+    S = np.asarray(S, dtype=np.int64)
+    low = np.concatenate([S[:, 0:8] & 15, S[:, 0:8] >> 4], axis=1)
+    top = np.stack([(S[:, 8:12] >> (2 * p)) & 3 for p in range(4)], axis=1).reshape(-1, 16)
+    return (low | (top << 4)) - 32
+
+
+def q3k_decode(blocks: np.ndarray) -> np.ndarray:
+    b = np.asarray(blocks, dtype=np.uint8).reshape(-1, 110)
+    hm, qs = b[:, 0:32].astype(np.int64), b[:, 32:96].astype(np.int64)
+    sc = q3k_scales(b[:, 96:108])
+    d = f16_bits_to_f64(b[:, 108:110].copy().view("<u2")[:, 0])
+    qb, qsh, si, plane = _run_maps()
+    l = np.arange(256) % 32
+    third = (hm[:, l] >> plane) & 1
+    q = ((qs[:, qb] >> qsh) & 3) + 4 * third - 4
+    return d[:, None] * sc[:, si] * q
+
+
+def q3k_pack(q, sc, d16) -> np.ndarray:
+    """Q3_K blocks from quants q [nb,256] in -4..3, scales [nb,16] in -32..31
+    and fp16 d [nb]."""
+    q = np.asarray(q, dtype=np.int64) + 4
+    nb = q.shape[0]
+    qb, qsh, _, plane = _run_maps()
+    hm = np.zeros((nb, 32), dtype=np.int64)
+    qs = np.zeros((nb, 64), dtype=np.int64)
+    for e in range(256):
+        qs[:, qb[e]] |= (q[:, e] & 3) << qsh[e]
+        hm[:, e % 32] |= (q[:, e] >> 2) << plane[e]
+    u = np.asarray(sc, dtype=np.int64) + 32
+    S = np.zeros((nb, 12), dtype=np.int64)
+    S[:, 0:8] = (u[:, 0:8] & 15) | ((u[:, 8:16] & 15) << 4)
+    for r in range(4):
+        S[:, 8 + r] = sum(((u[:, 4 * p + r] >> 4) & 3) << (2 * p) for p in range(4))
+    return np.concatenate([hm.astype(np.uint8), qs.astype(np.uint8), S.astype(np.uint8),
+                           _f16_bytes(d16)], axis=1)
+
+
+def q5k_decode(blocks: np.ndarray) -> np.ndarray:
+    b = np.asarray(blocks, dtype=np.uint8).reshape(-1, 176)
+    # the Q4_K fields from a Q4_K-shaped view (head + scales + nibbles)
+    view = np.concatenate([b[:, 0:16], b[:, 48:176]], axis=1)
+    d, dmin, sc, m, q4 = q4k_fields(view)
+    qh = b[:, 16:48].astype(np.int64)
+    e = np.arange(256)
+    fifth = (qh[:, e % 32] >> (e // 32)) & 1
+    sub = e // 32
+    return d[:, None] * sc[:, sub] * (q4 + 16 * fifth) - dmin[:, None] * m[:, sub]
+
+
+def q5k_pack(d16, dmin16, sc, m, q) -> np.ndarray:
+    """Q5_K blocks from the Q4_K fields with quants q [nb,256] in 0..31."""
+    q = np.asarray(q, dtype=np.int64)
+    head = q4k_pack(d16, dmin16, sc, m, q & 15)
+    nb = q.shape[0]
+    qh = np.zeros((nb, 32), dtype=np.int64)
+    for j in range(8):
+        qh |= (q[:, 32 * j:32 * j + 32] >> 4) << j
+    return np.concatenate([head[:, 0:16], qh.astype(np.uint8), head[:, 16:144]], axis=1)
+
+
 # ---------------------------------------------------------------- helpers
-QK = {"q4_k": 256, "q8_0": 32, "tq1_g128": 128, "q4_0": 32, "q5_0": 32, "q5_1": 32, "q6_k": 256}
-BB = {"q4_k": 144, "q8_0": 34, "tq1_g128": 28, "q4_0": 18, "q5_0": 22, "q5_1": 24, "q6_k": 210}
+QK = {"q4_k": 256, "q8_0": 32, "tq1_g128": 128, "q4_0": 32, "q5_0": 32, "q5_1": 32, "q6_k": 256,
+      "q2_k": 256, "q3_k": 256, "q5_k": 256}
+BB = {"q4_k": 144, "q8_0": 34, "tq1_g128": 28, "q4_0": 18, "q5_0": 22, "q5_1": 24, "q6_k": 210,
+      "q2_k": 84, "q3_k": 110, "q5_k": 176}
 _DEC = {"q4_k": q4k_decode, "q8_0": q8_0_decode, "tq1_g128": tq1_decode, "q4_0": q4_0_decode,
-        "q5_0": q5_0_decode, "q5_1": q5_1_decode, "q6_k": q6k_decode}
+        "q5_0": q5_0_decode, "q5_1": q5_1_decode, "q6_k": q6k_decode, "q2_k": q2k_decode,
+        "q3_k": q3k_decode, "q5_k": q5k_decode}
 
 
 def decode_matrix(kind: str, w: np.ndarray, rows: int, k: int) -> np.ndarray:

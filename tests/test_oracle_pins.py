@@ -157,7 +157,8 @@ def test_q4k_round_trip_tiny_matrix(orc):
             assert w[b, i] == want
 
 
-@pytest.mark.parametrize("kind", ["q4_k", "q8_0", "tq1_g128", "q4_0", "q5_0", "q5_1", "q6_k"])
+@pytest.mark.parametrize("kind", ["q4_k", "q8_0", "tq1_g128", "q4_0", "q5_0", "q5_1", "q6_k",
+                                  "q2_k", "q3_k", "q5_k"])
 def test_independent_decoders_agree(orc, kind):
     """C oracle and the vectorised numpy decoder agree bit for bit on random
     blocks (Q4_K with arbitrary fp16 d/dmin bit patterns, not just the
@@ -167,7 +168,8 @@ def test_independent_decoders_agree(orc, kind):
     rng = _rng(4)
     rows, k = 400, 256 * 1  # 400 Q4_K blocks; more for the smaller formats
     k = {"q4_k": 256 * 250, "q8_0": 32 * 250, "tq1_g128": 128 * 250, "q4_0": 32 * 250,
-         "q5_0": 32 * 250, "q5_1": 32 * 250, "q6_k": 256 * 250}[kind]
+         "q5_0": 32 * 250, "q5_1": 32 * 250, "q6_k": 256 * 250, "q2_k": 256 * 250,
+         "q3_k": 256 * 250, "q5_k": 256 * 250}[kind]
     w = synth.weight_blocks(kind, rng, rows, k)
     if kind == "q4_k":
         # also cover arbitrary finite fp16 d/dmin (exponents across the range)
@@ -369,6 +371,144 @@ def test_lut23_split_identity():
         assert (p * 57) >> 9 == p // 9
 
 
+# ------------------------------------------------------------------ GGUF Q2_K / Q3_K / Q5_K
+# The rest of the [MID] page's K-quant table.  Pins as for Q6_K: blocks packed
+# from chosen fields, raw-byte probes of the layout read in words (which byte
+# and bit each weight, scale and min comes from), and the numpy decoder.
+def test_q2k_blocks_from_fields(orc):
+    """Q2_K from chosen 2-bit quants, 4-bit scales and mins: weight e is
+    d * sc[e // 16] * q - dmin * mn[e // 16]."""
+    rng = _rng(62)
+    nb = 40
+    q = rng.integers(0, 4, size=(nb, 256))
+    sc = rng.integers(0, 16, size=(nb, 16))
+    mn = rng.integers(0, 16, size=(nb, 16))
+    d16 = rng.uniform(-0.5, 0.5, nb).astype(np.float16)
+    dm16 = rng.uniform(-0.5, 0.5, nb).astype(np.float16)
+    got = orc.dequant("q2_k", npd.q2k_pack(q, sc, mn, d16, dm16), nb, 256)
+    d, dm = d16.astype(np.float64)[:, None], dm16.astype(np.float64)[:, None]
+    want = d * np.repeat(sc, 16, axis=1) * q - dm * np.repeat(mn, 16, axis=1)
+    assert np.array_equal(got, want)
+
+
+def test_q2k_layout_bytes(orc):
+    """Raw bytes: scale byte j's low nibble scales weights 16j..16j+15 and its
+    high nibble is their min; bits 2u..2u+1 of qs byte 32h + l are weight
+    128h + 32u + l; d and dmin are the last four bytes."""
+    blk = np.zeros((1, 84), np.uint8)
+    blk[0, 80:82] = np.array([1.0], np.float16).view(np.uint8)
+    blk[0, 82:84] = np.array([0.5], np.float16).view(np.uint8)
+    assert np.array_equal(orc.dequant("q2_k", blk, 1, 256)[0], np.zeros(256))
+    for j in range(16):
+        b = blk.copy()
+        b[0, j] = 0x30  # min 3, scale 0
+        want = np.zeros(256)
+        want[16 * j:16 * j + 16] = -1.5
+        assert np.array_equal(orc.dequant("q2_k", b, 1, 256)[0], want)
+    for e in range(256):
+        h, u, l = e // 128, (e % 128) // 32, e % 32
+        b = blk.copy()
+        b[0, 0:16] = 0x05  # every scale 5, min 0
+        b[0, 16 + 32 * h + l] = 2 << (2 * u)
+        got = orc.dequant("q2_k", b, 1, 256)[0]
+        assert np.flatnonzero(got).tolist() == [e] and got[e] == 10.0
+
+
+def test_q3k_blocks_from_fields(orc):
+    """Q3_K from chosen quants in -4..3 and 6-bit scales in -32..31: weight e
+    is d * sc[e // 16] * q."""
+    rng = _rng(63)
+    nb = 40
+    q = rng.integers(-4, 4, size=(nb, 256))
+    sc = rng.integers(-32, 32, size=(nb, 16))
+    d16 = rng.uniform(-0.5, 0.5, nb).astype(np.float16)
+    got = orc.dequant("q3_k", npd.q3k_pack(q, sc, d16), nb, 256)
+    want = d16.astype(np.float64)[:, None] * np.repeat(sc, 16, axis=1) * q
+    assert np.array_equal(got, want)
+
+
+def test_q3k_scale_bytes(orc):
+    """Raw scale bytes (offset 96): the low nibble of byte i is the low four
+    bits of scale i (i < 8), its high nibble those of scale i + 8; bit pair p
+    of byte 8 + r is the top of scale 4p + r; stored values are offset by 32.
+    Every quant is -4 (all quant bits clear) and d = 1."""
+    blk = np.zeros((1, 110), np.uint8)
+    blk[0, 108:110] = np.array([1.0], np.float16).view(np.uint8)
+    # stored 0 everywhere: scale -32, weight 128
+    assert np.array_equal(orc.dequant("q3_k", blk, 1, 256)[0], np.full(256, 128.0))
+    for i in range(16):
+        for stored in (1, 9, 17, 33, 47, 63):
+            b = blk.copy()
+            lo, top = stored & 15, stored >> 4
+            if i < 8:
+                b[0, 96 + i] |= lo
+            else:
+                b[0, 96 + i - 8] |= lo << 4
+            b[0, 96 + 8 + i % 4] |= top << (2 * (i // 4))
+            want = np.full(256, 128.0)
+            want[16 * i:16 * i + 16] = -4.0 * (stored - 32)
+            assert np.array_equal(orc.dequant("q3_k", b, 1, 256)[0], want), (i, stored)
+            assert orc.q3k_scale(b[0, 96:108], i) == stored - 32
+
+
+def test_q3k_quant_bit_probes(orc):
+    """Raw quant bytes: bits 2u..2u+1 of qs byte 32 + 32h + l and bit 4h + u of
+    hmask byte l belong to weight 128h + 32u + l alone; the hmask bit adds 4."""
+    blk = np.zeros((1, 110), np.uint8)
+    # every scale 1 and d = 1 from the packer; quant bits cleared
+    blk[0, 96:110] = npd.q3k_pack(np.zeros((1, 256)), np.full((1, 16), 1),
+                                   np.array([1.0], np.float16))[0, 96:110]
+    base = orc.dequant("q3_k", blk, 1, 256)[0]
+    assert np.array_equal(base, np.full(256, -4.0))
+    for e in range(256):
+        h, u, l = e // 128, (e % 128) // 32, e % 32
+        b = blk.copy()
+        b[0, 32 + 32 * h + l] = 3 << (2 * u)
+        diff = orc.dequant("q3_k", b, 1, 256)[0] - base
+        assert np.flatnonzero(diff).tolist() == [e] and diff[e] == 3.0
+        b = blk.copy()
+        b[0, l] = 1 << (4 * h + u)
+        diff = orc.dequant("q3_k", b, 1, 256)[0] - base
+        assert np.flatnonzero(diff).tolist() == [e] and diff[e] == 4.0
+
+
+def test_q5k_blocks_from_fields(orc):
+    """Q5_K from chosen Q4_K scales and mins and 5-bit quants: weight e is
+    d * sc[e // 32] * q - dmin * m[e // 32]."""
+    rng = _rng(64)
+    nb = 40
+    q = rng.integers(0, 32, size=(nb, 256))
+    sc = rng.integers(0, 64, size=(nb, 8))
+    m = rng.integers(0, 64, size=(nb, 8))
+    d16 = rng.uniform(-0.5, 0.5, nb).astype(np.float16)
+    dm16 = rng.uniform(-0.5, 0.5, nb).astype(np.float16)
+    got = orc.dequant("q5_k", npd.q5k_pack(d16, dm16, sc, m, q), nb, 256)
+    d, dm = d16.astype(np.float64)[:, None], dm16.astype(np.float64)[:, None]
+    want = d * np.repeat(sc, 32, axis=1) * q - dm * np.repeat(m, 32, axis=1)
+    assert np.array_equal(got, want)
+
+
+def test_q5k_fifth_bit_and_layout(orc):
+    """Raw bytes: bit j of qh byte 16 + l adds 16 to weight 32j + l alone; the
+    nibbles sit at offset 48 in the Q4_K order; the scales at 4..15 are Q4_K's."""
+    head = npd.q4k_pack(np.array([1.0], np.float16), np.array([0.0], np.float16),
+                        np.ones((1, 8), np.int64), np.zeros((1, 8), np.int64),
+                        np.zeros((1, 256), np.int64))[0]
+    blk = np.zeros((1, 176), np.uint8)
+    blk[0, 0:16] = head[0:16]
+    assert np.array_equal(orc.dequant("q5_k", blk, 1, 256)[0], np.zeros(256))
+    for e in range(256):
+        j, l = e // 32, e % 32
+        b = blk.copy()
+        b[0, 16 + l] = 1 << j
+        got = orc.dequant("q5_k", b, 1, 256)[0]
+        assert np.flatnonzero(got).tolist() == [e] and got[e] == 16.0
+        b = blk.copy()
+        b[0, 48 + 32 * (j // 2) + l] = 7 << (4 * (j % 2))
+        got = orc.dequant("q5_k", b, 1, 256)[0]
+        assert np.flatnonzero(got).tolist() == [e] and got[e] == 7.0
+
+
 # ------------------------------------------------------------------ stored dequant
 @pytest.mark.parametrize("kind", ["q4_k", "q8_0", "tq1_g128"])
 @pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
@@ -391,7 +531,8 @@ def test_dequant_store_is_rounded_exact_value(orc, kind, dt):
 
 
 # ------------------------------------------------------------------ products
-@pytest.mark.parametrize("kind", ["q4_k", "q8_0", "tq1_g128", "q4_0", "q5_0", "q5_1", "q6_k"])
+@pytest.mark.parametrize("kind", ["q4_k", "q8_0", "tq1_g128", "q4_0", "q5_0", "q5_1", "q6_k",
+                                  "q2_k", "q3_k", "q5_k"])
 def test_qmm_one_hot_columns(orc, kind):
     """x = e_c gives y[., n] = w[n, c] exactly, for every c."""
     import synth
@@ -418,7 +559,8 @@ def test_qmm_integer_case(orc):
     assert np.array_equal(y[0], nib.reshape(n, -1).sum(axis=1).astype(np.float64))
 
 
-@pytest.mark.parametrize("kind", ["q4_k", "q8_0", "tq1_g128", "q4_0", "q5_0", "q5_1", "q6_k"])
+@pytest.mark.parametrize("kind", ["q4_k", "q8_0", "tq1_g128", "q4_0", "q5_0", "q5_1", "q6_k",
+                                  "q2_k", "q3_k", "q5_k"])
 @pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
 def test_qmm_brute_force_vs_numpy(orc, kind, dt):
     import synth
