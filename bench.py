@@ -9,6 +9,8 @@ workload:
   moe_c4    128 experts, Q4_K gate/up 2048x7168, down 7168x2048, top-8;
             fp16 x, fp32 h and output; 1 token (decode) and 256 tokens (seed 104)
   tq1_c5    TQ1_G128 17408x5120 and 5120x17408, fp16 x at batch 1 and M=512 (seed 105)
+  ggml_mv   the further GGUF blocks (Q4_0, Q5_0, Q5_1, Q6_K, Q2_K, Q3_K, Q5_K) in the
+            C2 GEMV shapes 14336x4096 and 4096x14336, fp16 x at batch 1, fp16 y (seed 106)
 
 The headline value is the Q4_K decode GEMV (the six qmv_c2 calls): weight
 bytes streamed per second.  Every call reads weights from HBM: weight-bound
@@ -41,7 +43,8 @@ BF16_PEAK_TFS = 2500.0
 GIB = 1 << 30
 # (workgroups, loads in flight per lane) of the streaming-read ceiling
 READ_SHAPES = ((1024, 4), (2048, 4), (4096, 2), (4096, 4), (1024, 8), (2048, 8), (4096, 8))
-STAGES = ("dequant", "qmv_c1", "qmv_c2", "qmm_c3", "moe_c4", "tq1_c5")
+STAGES = ("dequant", "qmv_c1", "qmv_c2", "qmm_c3", "moe_c4", "tq1_c5", "ggml_mv")
+GGML_KINDS = ("q4_0", "q5_0", "q5_1", "q6_k", "q2_k", "q3_k", "q5_k")
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
 
@@ -236,6 +239,25 @@ def main():
         extra_parts.append(Stage("tq1_c5_b1_noworkspace", calls_q, bq, fv,
                                  note="TQ1 GEMV batch 1, fp16 (kq_qmv, no workspace)"))
         stages.append(Stage("tq1_c5_m512", calls_m, bm, fm, note="TQ1 qmm M=512, fp16 (kq_qmm_ws)"))
+
+    if "ggml_mv" in wanted:
+        rng = synth.rng_for(106)
+        for kind in GGML_KINDS:
+            calls, nbytes = [], 0
+            for n, k in ((14336, 4096), (4096, 14336)):
+                w = d8(synth.weight_blocks(kind, rng, n, k))
+                ws = copies(w, w.numel())
+                x = d16(synth.activations(rng, (1, k), "f16"), torch.float16)
+                y = torch.empty((1, n), dtype=torch.float16, device=dev)
+                part = [(lambda kind=kind, n=n, k=k, x=x, y=y, ws=ws:
+                         kq.kq_qmv(kind, nxt(ws), n, k, x, 1, y)) for _ in range(len(ws))]
+                pb = len(part) * (w.numel() + (k + n) * 2)
+                extra_parts.append(Stage(f"ggml_mv_{kind}_{n}x{k}_b1", part, pb,
+                                         len(part) * 2 * n * k, note=f"{kind} GEMV batch 1, fp16"))
+                calls += part
+                nbytes += pb
+            stages.append(Stage(f"ggml_mv_{kind}", calls, nbytes, 0,
+                                note=f"{kind} GEMV batch 1, fp16, both C2 shapes"))
 
     # Streaming-read ceiling: a plain 16-byte-load read of the same number of
     # bytes as one C2 / C5 weight matrix (libkq_hbmread.so), rotated over

@@ -21,7 +21,7 @@ kq_status fail(kq_status st, const std::string& msg) {
 
 int qk_of(int t) {
     switch (t) {
-    case KQ_Q4_K: case KQ_Q6_K: return 256;
+    case KQ_Q4_K: case KQ_Q6_K: case KQ_Q2_K: case KQ_Q3_K: case KQ_Q5_K: return 256;
     case KQ_TQ1_G128: return 128;
     case KQ_Q8_0: case KQ_Q4_0: case KQ_Q5_0: case KQ_Q5_1: return 32;
     default: return 0;
@@ -36,6 +36,9 @@ int bb_of(int t) {
     case KQ_Q5_0: return 22;
     case KQ_Q5_1: return 24;
     case KQ_Q6_K: return 210;
+    case KQ_Q2_K: return 84;
+    case KQ_Q3_K: return 110;
+    case KQ_Q5_K: return 176;
     default: return 0;
     }
 }

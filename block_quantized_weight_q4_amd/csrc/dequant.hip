@@ -11,7 +11,8 @@
 //   Q8_0: d*q is exact (<= 19 bits).
 //   TQ1:  (t-1)*s is exact.
 //   Q4_0 / Q5_0: d*(q-8), d*(q-16) are exact; Q5_1: d*q+m fused, one
-//         rounding; Q6_K: d*sc is exact, (d*sc)*(q-32) rounds once.
+//         rounding; Q6_K and Q3_K: d*sc and (d*sc)*q are exact; Q2_K and
+//         Q5_K: as Q4_K.
 // fp16/bf16 outputs then round that fp32 value to nearest even.
 #include "kq_device.h"
 #include "kq_internal.h"
@@ -131,7 +132,7 @@ __global__ __launch_bounds__(256) void dequant_tq1_kernel(const uint8_t* __restr
     Out8<DT>::store(out, b * 128 + 8 * part, v);
 }
 
-// GGUF Q4_0 / Q5_0 / Q5_1 / Q6_K: one thread per 32-weight chunk, decoded
+// GGUF Q4_0 / Q5_0 / Q5_1 / Q6_K / Q2_K / Q3_K / Q5_K: one thread per 32-weight chunk, decoded
 // by the shared chunk decoders (kq_device.h); the chunk's 32 outputs are
 // contiguous.  Rows are contiguous in both the blocks and the output, so
 // chunk g of the whole matrix is chunk g of one long row.
@@ -160,8 +161,9 @@ static hipError_t launch_chunk32_dt(int codec, const void* w, int64_t nchunks, v
     // chunks of one launch: a multiple of 8 (Q6_K super-blocks hold 8), and
     // fewer than 2^31 work-items
     const int64_t piece = (int64_t)1 << 30;
-    const int64_t bbytes = codec == Q4_0 ? 18 : codec == Q5_0 ? 22 : codec == Q5_1 ? 24 : 210;
-    const int64_t per = codec == Q6_K ? 8 : 1;  // chunks per block
+    const int64_t bbytes = codec == Q4_0 ? 18 : codec == Q5_0 ? 22 : codec == Q5_1 ? 24
+                         : codec == Q6_K ? 210 : codec == Q2_K ? 84 : codec == Q3_K ? 110 : 176;
+    const int64_t per = codec == Q4_0 || codec == Q5_0 || codec == Q5_1 ? 1 : 8;  // chunks per block
     for (int64_t c0 = 0; c0 < nchunks; c0 += piece) {
         const int64_t nc = nchunks - c0 < piece ? nchunks - c0 : piece;
         const uint8_t* wp = (const uint8_t*)w + c0 / per * bbytes;
@@ -171,7 +173,10 @@ static hipError_t launch_chunk32_dt(int codec, const void* w, int64_t nchunks, v
         case Q4_0: hipLaunchKernelGGL((dequant_chunk32_kernel<Q4_0, DT>), grid, block, 0, s, wp, op, nc); break;
         case Q5_0: hipLaunchKernelGGL((dequant_chunk32_kernel<Q5_0, DT>), grid, block, 0, s, wp, op, nc); break;
         case Q5_1: hipLaunchKernelGGL((dequant_chunk32_kernel<Q5_1, DT>), grid, block, 0, s, wp, op, nc); break;
-        default: hipLaunchKernelGGL((dequant_chunk32_kernel<Q6_K, DT>), grid, block, 0, s, wp, op, nc); break;
+        case Q6_K: hipLaunchKernelGGL((dequant_chunk32_kernel<Q6_K, DT>), grid, block, 0, s, wp, op, nc); break;
+        case Q2_K: hipLaunchKernelGGL((dequant_chunk32_kernel<Q2_K, DT>), grid, block, 0, s, wp, op, nc); break;
+        case Q3_K: hipLaunchKernelGGL((dequant_chunk32_kernel<Q3_K, DT>), grid, block, 0, s, wp, op, nc); break;
+        default: hipLaunchKernelGGL((dequant_chunk32_kernel<Q5_K, DT>), grid, block, 0, s, wp, op, nc); break;
         }
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;

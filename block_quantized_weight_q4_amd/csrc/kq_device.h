@@ -19,7 +19,7 @@ typedef float float16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-enum Codec { Q4_K = 0, Q8_0 = 1, TQ1 = 2, Q4_0 = 3, Q5_0 = 4, Q5_1 = 5, Q6_K = 6 };
+enum Codec { Q4_K = 0, Q8_0 = 1, TQ1 = 2, Q4_0 = 3, Q5_0 = 4, Q5_1 = 5, Q6_K = 6, Q2_K = 7, Q3_K = 8, Q5_K = 9 };
 enum DType { F32 = 0, F16 = 1, BF16 = 2 };
 
 template <int C> struct CodecInfo;
@@ -30,6 +30,9 @@ template <> struct CodecInfo<Q4_0> { static constexpr int QK = 32, BYTES = 18; }
 template <> struct CodecInfo<Q5_0> { static constexpr int QK = 32, BYTES = 22; };
 template <> struct CodecInfo<Q5_1> { static constexpr int QK = 32, BYTES = 24; };
 template <> struct CodecInfo<Q6_K> { static constexpr int QK = 256, BYTES = 210; };
+template <> struct CodecInfo<Q2_K> { static constexpr int QK = 256, BYTES = 84; };
+template <> struct CodecInfo<Q3_K> { static constexpr int QK = 256, BYTES = 110; };
+template <> struct CodecInfo<Q5_K> { static constexpr int QK = 256, BYTES = 176; };
 
 // ---------------------------------------------------------------- scalars
 __device__ __forceinline__ float half_bits_to_float(uint32_t bits16) {
@@ -270,6 +273,125 @@ template <> struct Chunk32<Q6_K> {
             }
         }
         xa = sb * 256 + 32 * p;
+        xb = xa + 16;
+    }
+};
+
+// The super-blocks Q2_K and Q3_K are, like Q6_K, two halves of four 32-weight
+// runs: chunk q is run u = q % 4 of half h = (q / 4) % 2 of super-block q / 8,
+// i.e. weights 32 (q % 8) .. + 31; weight l of the run takes bits 2u, 2u + 1
+// of quant byte 32h + l and the 16-weight scale 8h + 2u + l / 16.
+
+// Q2_K (84 bytes, 4-byte aligned): scale bytes[16] (low nibble scale, high
+// nibble min), qs[64], fp16 d, fp16 dmin; weight d sc q - dmin mn with
+// d sc and dmin mn exact and one fused rounding.
+template <> struct Chunk32<Q2_K> {
+    static __device__ __forceinline__ void decode(const uint8_t* row, int64_t q, float (&w)[32],
+                                                  int64_t& xa, int64_t& xb) {
+        const int64_t sb = q >> 3;
+        const int p = (int)q & 7, h = p >> 2, u = p & 3;
+        const uint8_t* blk = row + sb * 84;
+        const uint32_t dd = *(const uint32_t*)(blk + 80);
+        const float d = half_bits_to_float(dd & 0xffffu), dmin = half_bits_to_float(dd >> 16);
+        const uint32_t scw = *(const uint16_t*)(blk + 8 * h + 2 * u);
+        const uint32_t* qs = (const uint32_t*)(blk + 16 + 32 * h);
+        float sc[2], mn[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const uint32_t b = (scw >> (8 * i)) & 0xffu;
+            sc[i] = d * (float)(b & 15u);
+            mn[i] = dmin * (float)(b >> 4);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t word = qs[i] >> (2 * u);  // bytes 4i .. 4i + 3 of the run
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int l = 4 * i + e;
+                const float qv = (float)((word >> (8 * e)) & 3u);
+                w[l] = __builtin_fmaf(sc[l >> 4], qv, -mn[l >> 4]);
+            }
+        }
+        xa = sb * 256 + 32 * p;
+        xb = xa + 16;
+    }
+};
+
+// Q3_K (110 bytes, 2-byte aligned): hmask[32], qs[64], 12 scale bytes, fp16
+// d.  The third quant bit of weight l of run (h, u) is bit 4h + u of hmask[l]
+// (clear: the quant is 4 lower); quants lie in -4..3.  Scale i (stored + 32)
+// has its low four bits in the low nibble of scale byte i (i < 8) or the high
+// nibble of byte i - 8, and its top two bits at 2 (i / 4) in byte 8 + i % 4.
+// The run's two scales 8h + 2u, 8h + 2u + 1 therefore sit in the 16-bit
+// words at scale bytes 2u (nibble 4h) and 8 + 2 (u % 2) (bit 2 (2h + u / 2)).
+// Weight (d sc) q: both products exact.
+template <> struct Chunk32<Q3_K> {
+    static __device__ __forceinline__ void decode(const uint8_t* row, int64_t q, float (&w)[32],
+                                                  int64_t& xa, int64_t& xb) {
+        const int64_t sb = q >> 3;
+        const int p = (int)q & 7, h = p >> 2, u = p & 3;
+        const uint8_t* blk = row + sb * 110;
+        const float d = half_bits_to_float(*(const uint16_t*)(blk + 108));
+        const uint32_t lw = *(const uint16_t*)(blk + 96 + 2 * u);
+        const uint32_t tw = *(const uint16_t*)(blk + 104 + 2 * (u & 1));
+        const int tsh = 2 * (2 * h + (u >> 1));
+        float sc[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int lo = (int)((lw >> (8 * i + 4 * h)) & 15u);
+            const int top = (int)((tw >> (8 * i + tsh)) & 3u);
+            sc[i] = d * (float)((lo | (top << 4)) - 32);
+        }
+        const uint16_t* hm = (const uint16_t*)blk;
+        const uint16_t* qs = (const uint16_t*)(blk + 32 + 32 * h);
+        const int hsh = 4 * h + u;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const uint32_t qw = qs[i], hw = hm[i];  // bytes 2i, 2i + 1 of the run
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int l = 2 * i + e;
+                const int low = (int)((qw >> (8 * e + 2 * u)) & 3u);
+                const int third = (int)((hw >> (8 * e + hsh)) & 1u);
+                w[l] = sc[l >> 4] * (float)(low + 4 * third - 4);
+            }
+        }
+        xa = sb * 256 + 32 * p;
+        xb = xa + 16;
+    }
+};
+
+// Q5_K (176 bytes, 16-byte aligned): the 16-byte Q4_K head (fp16 d, dmin,
+// packed 6-bit scales and mins), qh[32], qs[128] in the Q4_K nibble order.
+// Chunk q is sub-block j = q % 8 of super-block q / 8: weight l takes nibble
+// j % 2 of qs[32 (j / 2) + l] and bit j of qh[l] as its fifth bit; weight
+// d sc q - dmin m with one fused rounding, as Q4_K.
+template <> struct Chunk32<Q5_K> {
+    static __device__ __forceinline__ void decode(const uint8_t* row, int64_t q, float (&w)[32],
+                                                  int64_t& xa, int64_t& xb) {
+        const int64_t sb = q >> 3;
+        const int j = (int)q & 7;
+        const uint8_t* blk = row + sb * 176;
+        const u32x4 hd = *(const u32x4*)blk;
+        int sc, m;
+        q4k_scale_min(hd, j, sc, m);
+        const float s = q4k_d(hd) * (float)sc, mn = q4k_dmin(hd) * (float)m;
+        const u32x4* qh = (const u32x4*)(blk + 16);
+        const u32x4* qs = (const u32x4*)(blk + 48 + 32 * (j >> 1));
+        const int nsh = 4 * (j & 1);
+#pragma unroll
+        for (int v = 0; v < 2; ++v) {
+            const u32x4 hv = qh[v], qv = qs[v];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int l = 16 * v + i;
+                const uint32_t qb = (qv[i >> 2] >> (8 * (i & 3))) & 0xffu;
+                const uint32_t hb = (hv[i >> 2] >> (8 * (i & 3))) & 0xffu;
+                const uint32_t qq = ((qb >> nsh) & 15u) | (((hb >> j) & 1u) << 4);
+                w[l] = __builtin_fmaf(s, (float)qq, -mn);
+            }
+        }
+        xa = sb * 256 + 32 * j;
         xb = xa + 16;
     }
 };

@@ -134,6 +134,9 @@ template <> struct Chunk<Q4_0> : Chunk32<Q4_0> {};
 template <> struct Chunk<Q5_0> : Chunk32<Q5_0> {};
 template <> struct Chunk<Q5_1> : Chunk32<Q5_1> {};
 template <> struct Chunk<Q6_K> : Chunk32<Q6_K> {};
+template <> struct Chunk<Q2_K> : Chunk32<Q2_K> {};
+template <> struct Chunk<Q3_K> : Chunk32<Q3_K> {};
+template <> struct Chunk<Q5_K> : Chunk32<Q5_K> {};
 
 __device__ __forceinline__ void store_any(void* y, int64_t i, int dt, float v) {
     if (dt == F32) store_out<F32>(y, i, v);
@@ -289,6 +292,9 @@ hipError_t launch_skinny(int codec, int x_dt, bool glu, const SkinnyArgs& a, int
     case Q5_0: glu ? launch_x<Q5_0, true>(x_dt, a, mb, grid, s) : launch_x<Q5_0, false>(x_dt, a, mb, grid, s); break;
     case Q5_1: glu ? launch_x<Q5_1, true>(x_dt, a, mb, grid, s) : launch_x<Q5_1, false>(x_dt, a, mb, grid, s); break;
     case Q6_K: glu ? launch_x<Q6_K, true>(x_dt, a, mb, grid, s) : launch_x<Q6_K, false>(x_dt, a, mb, grid, s); break;
+    case Q2_K: glu ? launch_x<Q2_K, true>(x_dt, a, mb, grid, s) : launch_x<Q2_K, false>(x_dt, a, mb, grid, s); break;
+    case Q3_K: glu ? launch_x<Q3_K, true>(x_dt, a, mb, grid, s) : launch_x<Q3_K, false>(x_dt, a, mb, grid, s); break;
+    case Q5_K: glu ? launch_x<Q5_K, true>(x_dt, a, mb, grid, s) : launch_x<Q5_K, false>(x_dt, a, mb, grid, s); break;
     default: glu ? launch_x<TQ1, true>(x_dt, a, mb, grid, s) : launch_x<TQ1, false>(x_dt, a, mb, grid, s); break;
     }
     return hipGetLastError();

@@ -26,7 +26,8 @@ __all__ = [
     "ACT_SILU_LIMIT", "MOE_TILE_ROWS",
 ]
 
-TYPES = {"q4_k": 0, "q8_0": 1, "tq1_g128": 2, "q4_0": 3, "q5_0": 4, "q5_1": 5, "q6_k": 6}
+TYPES = {"q4_k": 0, "q8_0": 1, "tq1_g128": 2, "q4_0": 3, "q5_0": 4, "q5_1": 5, "q6_k": 6,
+         "q2_k": 7, "q3_k": 8, "q5_k": 9}
 _DT = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 LAYOUT_SHARED, LAYOUT_SLOTTED = 0, 1
 REUSE_SCHEDULE = 0x100  # OR into the layout of a mixed kq_qmm_id: keep the workspace schedule

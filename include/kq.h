@@ -31,9 +31,9 @@
  *                weights are produced, not by these kernels.
  *
  * The further GGUF blocks that mlx-native "quantized_matmul_id_ggml.rs"
- * dispatches (GgmlType::Q4_0, Q5_0, Q5_1 and Q6_K in its mv_id / mm_id kernel
- * tables).  The page names them without printing a layout; these are the
- * GGUF layouts:
+ * dispatches (GgmlType::Q4_0, Q5_0, Q5_1, Q6_K, Q2_K, Q3_K and Q5_K in its
+ * mv_id / mm_id kernel tables).  The page names them without printing a
+ * layout; these are the GGUF layouts:
  *   KQ_Q4_0      32 weights in 18 bytes: fp16 d, 16 bytes of nibbles (low
  *                nibble of byte i is weight i, high nibble weight i + 16);
  *                w = d * (q - 8).
@@ -48,7 +48,23 @@
  *                or high nibble of ql[64h + 32(u % 2) + l], bits 2u..2u+1 of
  *                qh[32h + l] and scales[8h + 2u + l / 16];
  *                w = d * scale * (q - 32).
- * These four are decoded and multiplied (kq_dequantize, the products and the
+ *   KQ_Q2_K      256 weights in 84 bytes: 16 scale bytes (low nibble scale,
+ *                high nibble min), qs[64], fp16 d, fp16 dmin.  Weight
+ *                128h + 32u + l takes bits 2u..2u+1 of qs[32h + l] and scale
+ *                byte 8h + 2u + l / 16; w = d * scale * q - dmin * min.
+ *   KQ_Q3_K      256 weights in 110 bytes: hmask[32], qs[64], 12 bytes of
+ *                packed 6-bit scales, fp16 d.  Weight 128h + 32u + l takes
+ *                bits 2u..2u+1 of qs[32h + l] plus 4 times bit 4h + u of
+ *                hmask[l], minus 4, and scale i = 8h + 2u + l / 16, whose low
+ *                four bits are the low nibble of scale byte i (i < 8) or the
+ *                high nibble of byte i - 8, and whose top two bits are bits
+ *                2(i / 4)..2(i / 4)+1 of byte 8 + i % 4, stored plus 32;
+ *                w = d * scale * q.
+ *   KQ_Q5_K      256 weights in 176 bytes: fp16 d, fp16 dmin, the 12 scale
+ *                and min bytes of Q4_K, qh[32], qs[128] in the Q4_K nibble
+ *                order; weight 32j + l adds 16 times bit j of qh[l] to its
+ *                Q4_K nibble; w = d * sc_j * q - dmin * m_j.
+ * These seven are decoded and multiplied (kq_dequantize, the products and the
  * expert-routed forms) but not encoded (kq_quantize -> KQ_ERR_UNSUPPORTED);
  * their products run on the vector units (no matrix-core kernel is built for
  * them), for every m.
@@ -73,7 +89,10 @@ typedef enum kq_type {
     KQ_Q4_0 = 3,
     KQ_Q5_0 = 4,
     KQ_Q5_1 = 5,
-    KQ_Q6_K = 6
+    KQ_Q6_K = 6,
+    KQ_Q2_K = 7,
+    KQ_Q3_K = 8,
+    KQ_Q5_K = 9
 } kq_type;
 
 typedef enum kq_dtype { KQ_F32 = 0, KQ_F16 = 1, KQ_BF16 = 2 } kq_dtype;
@@ -173,8 +192,8 @@ kq_status kq_dequantize(kq_type t, const void* w, int64_t rows, int64_t k, void*
  * sub-blocks use levels 0 and 15 and whose largest sc and m are 63) encodes
  * back to its own bytes.
  * Errors: rows or k <= 0, k % QK != 0, null or misaligned pointers, out
- * overlapping an input -> KQ_ERR_INVALID_ARG; Q4_0, Q5_0, Q5_1 and Q6_K ->
- * KQ_ERR_UNSUPPORTED (no encoder is built for them).
+ * overlapping an input -> KQ_ERR_INVALID_ARG; the GGUF blocks other than Q4_K
+ * and Q8_0 -> KQ_ERR_UNSUPPORTED (no encoder is built for them).
  */
 kq_status kq_quantize(kq_type t, const void* w, kq_dtype w_dt, int64_t rows, int64_t k,
                       const float* imatrix, void* out, void* stream);

@@ -96,13 +96,14 @@ def test_block_geometry(kq):
     assert kq.kq_row_bytes("tq1_g128", 5120) == 40 * 28
     assert kq.kq_row_bytes("q4_k", 100) == -1
     assert kq.kq_row_bytes("q4_k", 0) == -1
-    assert kq.lib().kq_qk(7) == 0
+    assert kq.lib().kq_qk(10) == 0
 
 
 def test_ggml_block_geometry(kq):
     """The further GGUF blocks: QK and block bytes of the GGUF layouts, and
     their row strides."""
-    for kind, qk, bb in (("q4_0", 32, 18), ("q5_0", 32, 22), ("q5_1", 32, 24), ("q6_k", 256, 210)):
+    for kind, qk, bb in (("q4_0", 32, 18), ("q5_0", 32, 22), ("q5_1", 32, 24), ("q6_k", 256, 210),
+                         ("q2_k", 256, 84), ("q3_k", 256, 110), ("q5_k", 256, 176)):
         assert (kq.kq_qk(kind), kq.kq_block_bytes(kind)) == (qk, bb), kind
         assert kq.kq_row_bytes(kind, 4096) == 4096 // qk * bb, kind
     assert kq.kq_row_bytes("q6_k", 4096 + 32) == -1
@@ -113,14 +114,14 @@ def test_ggml_codecs_take_no_scratch_and_no_encoder(kq):
     any shape; kq_quantize rejects them before touching memory."""
     import torch
 
-    for kind in ("q4_0", "q5_0", "q5_1", "q6_k"):
+    for kind in ("q4_0", "q5_0", "q5_1", "q6_k", "q2_k", "q3_k", "q5_k"):
         for m, dt in ((1, torch.float16), (16, torch.bfloat16), (512, torch.float16),
                       (2048, torch.bfloat16)):
             assert kq.kq_qmm_workspace_bytes(kind, 512, 4096, m, dt) == 0, (kind, m)
     L = kq.lib()
     P = C.c_void_p
     base = 1 << 40
-    for t in (3, 4, 5, 6):
+    for t in (3, 4, 5, 6, 7, 8, 9):
         assert L.kq_quantize(t, P(base), 0, 4, 256, None, P(base + (1 << 30)), None) == 2
         assert kq.kq_last_error() == "no encoder for this weight type"
 
@@ -160,7 +161,7 @@ def test_validation_rejects_before_launch(kq):
     assert _call_qmv(L, **{**ok, "w": 0}) == 1            # null
     assert _call_qmv(L, **{**ok, "x": base + (1 << 30) + 2}) == 1  # misaligned
     assert _call_qmv(L, **{**ok, "y": base + 16}) == 1    # y overlaps w
-    assert _call_qmv(L, **{**ok, "t": 9}) == 2            # unknown type
+    assert _call_qmv(L, **{**ok, "t": 10}) == 2           # unknown type
     assert _call_qmv(L, **{**ok, "xdt": 7}) == 2          # unknown dtype
     assert kq.kq_last_error() == "unknown dtype"
     big = dict(w=base, x=base + (1 << 36), y=base + (2 << 36))

@@ -1,8 +1,9 @@
-"""GPU parity of the further GGUF blocks (Q4_0, Q5_0, Q5_1, Q6_K) against the
-CPU oracle, through the C ABI, over every entry point that takes them.
+"""GPU parity of the further GGUF blocks (Q4_0, Q5_0, Q5_1, Q6_K, Q2_K, Q3_K,
+Q5_K) against the CPU oracle, through the C ABI, over every entry point that
+takes them.
 
-mlx-native "quantized_matmul_id_ggml.rs" dispatches these four types
-(GgmlType::Q4_0, Q5_0, Q5_1, Q6_K) to its mv_id / mm_id kernels.  Here they
+mlx-native "quantized_matmul_id_ggml.rs" dispatches these types
+(GgmlType::Q4_0 ... Q5_K) to its mv_id / mm_id kernels.  Here they
 decode chunk by chunk on the vector units for every product shape, so the
 weights enter the products as exact fp32 values: dequantization is compared
 bit for bit, products with |gpu - ref| <= tau * sum|w*x| as for the other
@@ -21,8 +22,14 @@ from tests.gpu_util import TAU, bits, check_tol, device, empty, to_dev, to_f64
 
 pytestmark = pytest.mark.gpu
 
-KINDS = ["q4_0", "q5_0", "q5_1", "q6_k"]
-QK = {"q4_0": 32, "q5_0": 32, "q5_1": 32, "q6_k": 256}
+KINDS = ["q4_0", "q5_0", "q5_1", "q6_k", "q2_k", "q3_k", "q5_k"]
+QK = {"q4_0": 32, "q5_0": 32, "q5_1": 32, "q6_k": 256, "q2_k": 256, "q3_k": 256, "q5_k": 256}
+
+
+def _k(kind, blocks32):
+    """A row length of about blocks32 32-weight blocks (whole super-blocks of
+    the 256-weight codecs)."""
+    return 32 * blocks32 if QK[kind] == 32 else 256 * max(1, blocks32 // 8)
 
 
 @pytest.fixture(scope="module")
@@ -81,11 +88,9 @@ def _run(kq, fn, kind, w, n, k, x, x_dt, m, y_dt):
 @pytest.mark.parametrize("m", [1, 4, 16])
 @pytest.mark.parametrize("n,nblk", [(67, 6), (130, 150)])
 def test_qmv(kq, kind, x_dt, m, n, nblk):
-    # 150 blocks of 32 (or 19 super-blocks of Q6_K, 152 chunks): each lane
+    # 150 blocks of 32 (or 18 super-blocks of 256, 144 chunks): each lane
     # of a wave takes two or three chunks, the last pass ragged
-    if kind == "q6_k":
-        nblk = max(1, nblk * 32 // 256)
-    k = QK[kind] * nblk
+    k = _k(kind, nblk)
     rng = synth.rng_for(5100 + m + n)
     w = synth.weight_blocks(kind, rng, n, k)
     x = synth.activations(rng, (m, k), x_dt)
@@ -104,7 +109,7 @@ def test_qmv(kq, kind, x_dt, m, n, nblk):
 def test_qmm(kq, kind, x_dt, m, fn):
     """m > 16: tiles of 16 activation rows plus a ragged one, through the
     three prefill entry points (none of which takes scratch here)."""
-    n, k = 75, QK[kind] * (9 if kind == "q6_k" else 70)
+    n, k = 75, _k(kind, 72)
     rng = synth.rng_for(5200 + m)
     w = synth.weight_blocks(kind, rng, n, k)
     x = synth.activations(rng, (m, k), x_dt)
@@ -119,7 +124,7 @@ def test_one_hot_columns_exact(kq, kind):
     """x = e_c returns column c of the decoded weights exactly, for every c,
     in the decode (m <= 16) and the prefill (m = k) forms and with fp32 and
     fp16 activations: the weights are never rounded below fp32."""
-    n, k = 40, QK[kind] * (2 if kind == "q6_k" else 8)
+    n, k = 40, _k(kind, 16)
     w = synth.weight_blocks(kind, synth.rng_for(5300), n, k)
     W = oracle.dequant(kind, w, n, k).astype(np.float32)
     for fn, m, x_dt in (("kq_qmv", 16, "f32"), ("kq_qmm", k, "f32"), ("kq_qmm", k, "f16")):
@@ -140,7 +145,7 @@ def test_one_hot_columns_exact(kq, kind):
 @pytest.mark.parametrize("mixed", [False, True])
 @pytest.mark.parametrize("E,T,top_k", [(8, 1, 8), (8, 5, 3), (4, 70, 4)])
 def test_qmm_id(kq, kind, x_dt, layout, mixed, E, T, top_k):
-    n, k = 96, QK[kind] * (2 if kind == "q6_k" else 12)
+    n, k = 96, _k(kind, 16)
     rng = synth.rng_for(5400 + T)
     w = synth.weight_blocks(kind, rng, E * n, k)
     stride = n * synth.row_bytes(kind, k)
@@ -181,7 +186,7 @@ def _glu_bound_ok(h, ref, tau, act, limit):
 @pytest.mark.parametrize("act", [0, 1])
 def test_moe_glu(kq, kind, x_dt, T, act):
     E, n, top_k = 6, 80, 3
-    k = QK[kind] * (2 if kind == "q6_k" else 10)
+    k = _k(kind, 16)
     rng = synth.rng_for(5500 + T)
     gate = synth.weight_blocks(kind, rng, E * n, k)
     up = synth.weight_blocks(kind, rng, E * n, k)
@@ -203,7 +208,7 @@ def test_moe_glu(kq, kind, x_dt, T, act):
 def test_moe_glu_ex_shexp_silu_limit(kq, kind, T):
     """silu_limit and a shared expert in the last slot (kq_moe_glu_ex)."""
     E, n, top_k, limit = 6, 80, 3, 5.0
-    k = QK[kind] * (2 if kind == "q6_k" else 10)
+    k = _k(kind, 16)
     rng = synth.rng_for(5600 + T)
     gate = synth.weight_blocks(kind, rng, E * n, k)
     up = synth.weight_blocks(kind, rng, E * n, k)
@@ -228,7 +233,7 @@ def test_moe_glu_ex_shexp_silu_limit(kq, kind, T):
 @pytest.mark.parametrize("T", [1, 5, 40])
 def test_qmm_id_mix_shexp(kq, kind, x_dt, T):
     E, top_k, n = 6, 3, 72
-    k = QK[kind] * (2 if kind == "q6_k" else 10)
+    k = _k(kind, 16)
     rng = synth.rng_for(5700 + T)
     w = synth.weight_blocks(kind, rng, E * n, k)
     wsh = synth.weight_blocks(kind, rng, n, k)
