@@ -21,7 +21,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libkq.so")
 READ_LIB = os.path.join(PKG, "libkq_hbmread.so")
 READ_SOURCES = ["hbm_read.hip"]
-SOURCES = ["api.hip", "dequant.hip", "skinny.hip", "mmv2.hip", "mmv3.hip", "gemm.hip", "moe.hip", "moe_dec.hip", "moe_mm.hip", "tq1mv.hip", "quantize.hip"]
+SOURCES = ["api.hip", "dequant.hip", "skinny.hip", "mmv2.hip", "mmv3.hip", "gemm.hip", "moe.hip", "moe_dec.hip", "moe_mm.hip", "tq1mv.hip", "quantize.hip", "cmv.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -1,0 +1,261 @@
+// cmv.hip -- decode GEMV (one fp16 activation row) for the further GGUF
+// codecs Q4_0, Q5_0, Q5_1, Q6_K, Q2_K, Q3_K and Q5_K (kq_qmv, m = 1).
+//
+// mlx-kquant "bindings.cpp": quantized_matmul in the decode regime; the
+// codecs are the GGUF blocks that mlx-native "quantized_matmul_id_ggml.rs"
+// dispatches (its mv_id kernel table), laid out as include/kq.h states.
+//
+// A workgroup owns 16 weight rows.  Their bytes stream through LDS in
+// chunks of whole 16-byte-aligned units of blocks (coalesced global->LDS
+// copies, double buffered); the activation row is copied into LDS once.
+// Each lane takes one 32-weight chunk of R rows at a time: it decodes each
+// row's chunk to exact fp16 integer pairs with an affine scale per 16
+// weights (pair32.h) and multiplies them with the shared activations on
+// v_dot2_f32_f16, so one activation read serves R rows.  Lanes of a wave
+// that share a row are summed by lane shuffles, waves through LDS.
+#include "kq_device.h"
+#include "kq_internal.h"
+#include "lds_dma.h"
+#include "pair32.h"
+
+namespace kq {
+
+namespace {
+
+// The smallest run of whole blocks whose bytes are a multiple of 16 (so
+// every chunk of a 16-byte-aligned row starts 16-byte aligned): bytes and
+// weights.
+template <int C> struct Unit;
+template <> struct Unit<Q4_0> { static constexpr int BYTES = 144, W = 256; };   // 8 blocks
+template <> struct Unit<Q5_0> { static constexpr int BYTES = 176, W = 256; };   // 8 blocks
+template <> struct Unit<Q5_1> { static constexpr int BYTES = 192, W = 256; };   // 8 blocks
+template <> struct Unit<Q6_K> { static constexpr int BYTES = 1680, W = 2048; }; // 8 super-blocks
+template <> struct Unit<Q2_K> { static constexpr int BYTES = 336, W = 1024; };  // 4 super-blocks
+template <> struct Unit<Q3_K> { static constexpr int BYTES = 880, W = 2048; };  // 8 super-blocks
+template <> struct Unit<Q5_K> { static constexpr int BYTES = 176, W = 256; };   // 1 super-block
+
+// W waves; CU units per chunk; R rows per lane task
+template <int C, int W_, int CU_, int R_>
+struct CmvCfg {
+    static constexpr int W = W_, CU = CU_, R = R_;
+    static constexpr int CHB = CU * Unit<C>::BYTES;      // chunk bytes of one row
+    static constexpr int CHQ = CU * Unit<C>::W / 32;     // 32-weight chunks of one row per chunk
+    // 16-byte pieces per LDS row: the chunk, one piece of padding (read past
+    // by the realigning dword reads), and one more if that count is even, so
+    // that the 16 rows of a workgroup start on 16 different bank groups
+    static constexpr int ROW_PIECES = (CHB / 16 + 1) | 1;
+    static constexpr int WBUF = 16 * ROW_PIECES * 16;    // bytes of one chunk buffer
+    static constexpr int NBUF = 2;
+    static constexpr int RG = 16 / R;                    // row groups
+    static constexpr int TASKS = RG * CHQ;               // lane tasks per chunk
+    static_assert(Unit<C>::BYTES % 16 == 0, "units are whole 16-byte pieces");
+    static_assert(16 % R == 0 && 64 % RG == 0, "row groups tile a wave");
+    static size_t lds_bytes(int64_t k) { return (size_t)NBUF * WBUF + (size_t)k * 2 + (size_t)W * 16 * 4; }
+};
+
+}  // namespace
+
+template <int C, int W, int CU, int R>
+__global__ __launch_bounds__(64 * W) void cmv_kernel(const uint8_t* __restrict__ w, int64_t n, int64_t k,
+                                                     const uint16_t* __restrict__ x, void* __restrict__ y,
+                                                     int y_dt) {
+    using Cfg = CmvCfg<C, W, CU, R>;
+    constexpr int kRowPieces = Cfg::ROW_PIECES, kWBuf = Cfg::WBUF, kNBuf = Cfg::NBUF, kRG = Cfg::RG;
+    constexpr int NPIECE = 16 * kRowPieces;
+    constexpr int WLOADS = (NPIECE + 63) / 64;
+    constexpr int WL_PER_WAVE = (WLOADS + W - 1) / W;
+    extern __shared__ __align__(16) uint8_t smem[];
+    uint8_t* wbuf = smem;                                           // [kNBuf][kWBuf]
+    uint16_t* xs = (uint16_t*)(smem + kNBuf * kWBuf);               // [k]
+    float* red = (float*)(smem + kNBuf * kWBuf + (size_t)k * 2);    // [W][16]
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t n0 = (int64_t)blockIdx.x * 16;
+    const int64_t row_bytes = k / Unit<C>::W * Unit<C>::BYTES;
+    const int nchunks = (int)(row_bytes / Cfg::CHB);                // whole chunks (k is a multiple of the chunk)
+
+    // ---- the activation row into LDS (16-byte copies; k * 2 is a multiple of 16)
+    // (lanes past the row's end issue nothing: a copy lands at 16 * lane
+    // past its base, whatever the source)
+    const int xpieces = (int)(k / 8);
+    for (int p0 = 64 * wave; p0 < xpieces; p0 += 64 * W) {
+        const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr((const uint8_t*)xs + 16 * (int64_t)p0));
+        if (p0 + lane < xpieces) dma16(x + 8 * (int64_t)(p0 + lane), dst);
+    }
+    // ---- weight pieces of this lane: LDS piece p = 64 i + lane is piece
+    // p % kRowPieces of row p / kRowPieces (pieces past the chunk are padding)
+    const uint8_t* wbase = w + n0 * row_bytes;
+    uint32_t woff[WL_PER_WAVE];
+    bool wact[WL_PER_WAVE];
+#pragma unroll
+    for (int j = 0; j < WL_PER_WAVE; ++j) {
+        const int i = wave + W * j;
+        const int p = 64 * i + lane;
+        const int r = p / kRowPieces, q = p - r * kRowPieces;
+        int64_t nr = n0 + r;
+        if (nr >= n) nr = n - 1;
+        wact[j] = i < WLOADS && r < 16 && q < Cfg::CHB / 16;
+        woff[j] = (uint32_t)((nr - n0) * row_bytes) + 16u * (uint32_t)q;
+    }
+    int wave_loads = 0;
+#pragma unroll
+    for (int j = 0; j < WL_PER_WAVE; ++j) wave_loads += (wave + W * j < WLOADS) ? 1 : 0;
+    auto issue = [&](int chunk) {
+        uint8_t* dst = wbuf + (chunk % kNBuf) * kWBuf;
+        const uint8_t* src = wbase + (int64_t)chunk * Cfg::CHB;
+#pragma unroll
+        for (int j = 0; j < WL_PER_WAVE; ++j) {
+            const int i = wave + W * j;
+            if (i < WLOADS) {
+                // padding pieces and pieces past the 16 rows are not copied
+                // (every load instruction still has live lanes: each group of
+                // 64 pieces holds pieces of a row)
+                const uint32_t dl = __builtin_amdgcn_readfirstlane(lds_addr(dst + 1024 * i));
+                if (wact[j]) dma16(src + woff[j], dl);
+            }
+        }
+    };
+
+    float acc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = 0.f;
+    const int rg = lane % kRG;  // this lane's row group: rows rg + kRG * j
+    for (int c = 0; c < kNBuf - 1 && c < nchunks; ++c) issue(c);
+    for (int c = 0; c < nchunks; ++c) {
+        const int later = (nchunks - 1 < c + kNBuf - 2 ? nchunks - 1 : c + kNBuf - 2) - c;
+        // the activation copies were issued before every weight chunk
+        wait_loads_le(later * wave_loads);
+        __syncthreads();
+        if (c + kNBuf - 1 < nchunks) issue(c + kNBuf - 1);
+        const uint8_t* B = wbuf + (c % kNBuf) * kWBuf;
+        const int64_t kbase = (int64_t)c * (Cfg::CHQ * 32);
+        for (int t = lane + 64 * wave; t < Cfg::TASKS; t += 64 * W) {
+            const int cq = t / kRG;
+            uint32_t p[R][16];
+            float A[R][2], Bv[R][2];
+            int64_t xa = 0, xb = 0;
+#pragma unroll
+            for (int j = 0; j < R; ++j)
+                Pair32<C>::template decode<true>(B + (rg + kRG * j) * (kRowPieces * 16), cq, p[j], A[j], Bv[j],
+                                                 xa, xb);
+            uint32_t xw[16];
+            const u32x4* xp = (const u32x4*)(xs + kbase + xa);
+            const u32x4* xq = (const u32x4*)(xs + kbase + xb);
+            const u32x4 x0 = xp[0], x1 = xp[1], x2 = xq[0], x3 = xq[1];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) xw[e] = x0[e], xw[4 + e] = x1[e], xw[8 + e] = x2[e], xw[12 + e] = x3[e];
+            float t0 = 0.f, t1 = 0.f;
+            if (Pair32<C>::has_b) {
+                t0 = sum16(xw);
+                t1 = sum16(xw + 8);
+            }
+#pragma unroll
+            for (int j = 0; j < R; ++j) {
+                float s = A[j][0] * dot16(p[j], xw);
+                s = __builtin_fmaf(A[j][1], dot16(p[j] + 8, xw + 8), s);
+                if (Pair32<C>::has_b) {
+                    s = __builtin_fmaf(Bv[j][0], t0, s);
+                    s = __builtin_fmaf(Bv[j][1], t1, s);
+                }
+                acc[j] += s;
+            }
+        }
+    }
+
+    // ---- lanes rg, rg + kRG, ... of every wave hold rows rg + kRG j
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+#pragma unroll
+        for (int o = kRG; o < 64; o <<= 1)
+            acc[j] += __shfl_xor(acc[j], o, 64);
+    }
+    if (lane < kRG) {
+#pragma unroll
+        for (int j = 0; j < R; ++j) red[wave * 16 + rg + kRG * j] = acc[j];
+    }
+    __syncthreads();
+    if (wave == 0 && lane < 16) {
+        float v = 0.f;
+        for (int ww = 0; ww < W; ++ww) v += red[ww * 16 + lane];
+        const int64_t o = n0 + lane;
+        if (o < n) {
+            if (y_dt == F32) store_out<F32>(y, o, v);
+            else if (y_dt == F16) store_out<F16>(y, o, v);
+            else store_out<BF16>(y, o, v);
+        }
+    }
+}
+
+// Launch shapes (measured on the 14336x4096 and 4096x14336 GEMVs): rows of
+// fewer than 8192 weights take four waves, two rows per lane task; longer
+// rows, whose few workgroups leave compute units short of waves, take more
+// waves and longer chunks.
+template <int C, bool LONG> struct CmvPick;
+template <> struct CmvPick<Q4_0, false> { using Cfg = CmvCfg<Q4_0, 4, 4, 2>; };
+template <> struct CmvPick<Q5_0, false> { using Cfg = CmvCfg<Q5_0, 4, 4, 2>; };
+template <> struct CmvPick<Q5_1, false> { using Cfg = CmvCfg<Q5_1, 4, 4, 2>; };
+template <> struct CmvPick<Q5_K, false> { using Cfg = CmvCfg<Q5_K, 8, 4, 1>; };
+template <> struct CmvPick<Q2_K, false> { using Cfg = CmvCfg<Q2_K, 8, 2, 2>; };
+template <> struct CmvPick<Q6_K, false> { using Cfg = CmvCfg<Q6_K, 8, 1, 1>; };
+template <> struct CmvPick<Q3_K, false> { using Cfg = CmvCfg<Q3_K, 8, 2, 2>; };
+template <> struct CmvPick<Q4_0, true> { using Cfg = CmvCfg<Q4_0, 16, 8, 1>; };
+template <> struct CmvPick<Q5_0, true> { using Cfg = CmvCfg<Q5_0, 16, 8, 1>; };
+template <> struct CmvPick<Q5_1, true> { using Cfg = CmvCfg<Q5_1, 16, 8, 1>; };
+template <> struct CmvPick<Q5_K, true> { using Cfg = CmvCfg<Q5_K, 16, 8, 1>; };
+template <> struct CmvPick<Q2_K, true> { using Cfg = CmvCfg<Q2_K, 8, 2, 2>; };
+template <> struct CmvPick<Q6_K, true> { using Cfg = CmvCfg<Q6_K, 8, 1, 1>; };
+template <> struct CmvPick<Q3_K, true> { using Cfg = CmvCfg<Q3_K, 8, 1, 1>; };
+
+constexpr int64_t kLongRow = 8192;
+
+template <int C, bool LONG>
+static bool fits_cfg(int64_t k) {
+    using Cfg = typename CmvPick<C, LONG>::Cfg;
+    return k % (Cfg::CHQ * 32) == 0 && Cfg::lds_bytes(k) <= 160 * 1024;
+}
+template <int C>
+static bool fits_c(int64_t k) {
+    return k >= kLongRow ? fits_cfg<C, true>(k) : fits_cfg<C, false>(k);
+}
+
+bool cmv_fits(int codec, int64_t k) {
+    switch (codec) {
+    case Q4_0: return fits_c<Q4_0>(k);
+    case Q5_0: return fits_c<Q5_0>(k);
+    case Q5_1: return fits_c<Q5_1>(k);
+    case Q6_K: return fits_c<Q6_K>(k);
+    case Q2_K: return fits_c<Q2_K>(k);
+    case Q3_K: return fits_c<Q3_K>(k);
+    case Q5_K: return fits_c<Q5_K>(k);
+    default: return false;
+    }
+}
+
+template <int C, bool LONG>
+static hipError_t launch_cfg(const uint8_t* w, int64_t n, int64_t k, const uint16_t* x, void* y, int y_dt,
+                             hipStream_t s) {
+    using Cfg = typename CmvPick<C, LONG>::Cfg;
+    constexpr auto kern = cmv_kernel<C, Cfg::W, Cfg::CU, Cfg::R>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)((n + 15) / 16)), dim3(64 * Cfg::W), Cfg::lds_bytes(k), s, w, n, k,
+                       x, y, y_dt);
+    return hipGetLastError();
+}
+template <int C>
+static hipError_t launch_c(const uint8_t* w, int64_t n, int64_t k, const uint16_t* x, void* y, int y_dt,
+                           hipStream_t s) {
+    return k >= kLongRow ? launch_cfg<C, true>(w, n, k, x, y, y_dt, s) : launch_cfg<C, false>(w, n, k, x, y, y_dt, s);
+}
+
+hipError_t launch_cmv(int codec, const uint8_t* w, int64_t n, int64_t k, const uint16_t* x, void* y,
+                      int y_dt, hipStream_t s) {
+    switch (codec) {
+    case Q4_0: return launch_c<Q4_0>(w, n, k, x, y, y_dt, s);
+    case Q5_0: return launch_c<Q5_0>(w, n, k, x, y, y_dt, s);
+    case Q5_1: return launch_c<Q5_1>(w, n, k, x, y, y_dt, s);
+    case Q6_K: return launch_c<Q6_K>(w, n, k, x, y, y_dt, s);
+    case Q2_K: return launch_c<Q2_K>(w, n, k, x, y, y_dt, s);
+    case Q3_K: return launch_c<Q3_K>(w, n, k, x, y, y_dt, s);
+    default: return launch_c<Q5_K>(w, n, k, x, y, y_dt, s);
+    }
+}
+
+}  // namespace kq

@@ -104,6 +104,11 @@ int tq1_mv_pieces(int64_t n, int64_t k, int* pnb);
 hipError_t launch_tq1_mv(const uint8_t* w, int64_t n, int64_t k, const uint16_t* x, void* y,
                          int y_dt, hipStream_t s, int pnb = 0, float* part = nullptr);
 // y[i] = sum over pieces p in order of part[p * count + i], stored as y_dt
+// decode GEMV of one fp16 activation row for the further GGUF codecs
+// (cmv.hip): rows a whole number of its chunks long, LDS permitting
+bool cmv_fits(int codec, int64_t k);
+hipError_t launch_cmv(int codec, const uint8_t* w, int64_t n, int64_t k, const uint16_t* x, void* y,
+                      int y_dt, hipStream_t s);
 hipError_t launch_splitk_reduce(const float* part, int pieces, int64_t count, void* y, int y_dt,
                                 hipStream_t s);
 // Prefill GEMM (gemm.hip).

@@ -1,0 +1,240 @@
+// pair32.h -- the further GGUF codecs (Q4_0, Q5_0, Q5_1, Q6_K, Q2_K, Q3_K,
+// Q5_K) decoded for fp16 activations: exact fp16 integer pairs and an
+// affine scale per 16 weights, multiplied on v_dot2_f32_f16.  The block
+// layouts are those of include/kq.h (the GGUF layouts of the codecs that
+// mlx-native "quantized_matmul_id_ggml.rs" dispatches).
+#pragma once
+#include "kq_device.h"
+
+namespace kq {
+
+// For fp16 activations the further GGUF codecs skip fp32 weights: chunk q
+// decodes to 16 fp16 pairs p[] of exact small integers (p[0..7]: weights
+// 0..15, paired with activations [xa, xa+16); p[8..15]: weights 16..31 with
+// [xb, xb+16)) and, per half h of 16 weights, w = A[h] * v + B[h].  The dot
+// products run on v_dot2_f32_f16 (fp16 products are exact in fp32, sums in
+// fp32), then sum w x = A * sum v x + B * sum x.  An integer v is formed as
+// the fp16 1024 + v (the byte v under the exponent pattern 0x64) minus the
+// offset, exactly.
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+
+template <int C> struct Pair32 { static constexpr bool ok = false, has_b = false; };
+
+// bytes b0..b3 of t (each < 256) as two fp16 pairs (1024 + b0, 1024 + b1),
+// (1024 + b2, 1024 + b3), minus `off` in each lane
+__device__ __forceinline__ void bytes_to_pairs(uint32_t t, h2_t off, uint32_t& p01, uint32_t& p23) {
+    p01 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2_t, __builtin_amdgcn_perm(0x64646464u, t, 0x04010400u)) - off);
+    p23 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2_t, __builtin_amdgcn_perm(0x64646464u, t, 0x04030402u)) - off);
+}
+__device__ __forceinline__ h2_t h2(float v) { return h2_t{(_Float16)v, (_Float16)v}; }
+// N consecutive little-endian dwords from a 2-byte-aligned address.  From
+// global memory: 16-bit loads, which the compiler may merge (the vector
+// memory path takes unaligned addresses).  From LDS (LDS = true): N + 1
+// aligned dword reads realigned by v_alignbyte; the one extra dword must be
+// readable (the LDS rows of the decode kernels end in a padding piece).
+template <bool LDS, int N>
+__device__ __forceinline__ void words(const uint8_t* p, uint32_t (&v)[N]) {
+    if constexpr (LDS) {
+        const uint32_t sh = (uint32_t)(uintptr_t)p & 3u;
+        const uint32_t* b = (const uint32_t*)(p - sh);
+        uint32_t t[N + 1];
+#pragma unroll
+        for (int i = 0; i <= N; ++i) t[i] = b[i];
+#pragma unroll
+        for (int i = 0; i < N; ++i) v[i] = __builtin_amdgcn_alignbyte(t[i + 1], t[i], sh);
+    } else {
+        const uint16_t* q = (const uint16_t*)p;
+#pragma unroll
+        for (int i = 0; i < N; ++i) v[i] = (uint32_t)q[2 * i] | ((uint32_t)q[2 * i + 1] << 16);
+    }
+}
+// bits 0..3 of t moved to bits 0, 8, 16, 24 (the four copies t << 7i do not
+// overlap, so the product carries nothing)
+__device__ __forceinline__ uint32_t spread4(uint32_t t) { return (t * 0x00204081u) & 0x01010101u; }
+
+// Q4_0 / Q5_0 / Q5_1: v = q - 8 / q - 16 / q (A = d; Q5_1: B = m)
+template <int C> struct PairLegacy {
+    static constexpr bool ok = true, has_b = C == Q5_1;
+    template <bool LDS = false>
+    static __device__ __forceinline__ void decode(const uint8_t* row, int64_t q, uint32_t (&p)[16],
+                                                  float (&A)[2], float (&B)[2], int64_t& xa, int64_t& xb) {
+        constexpr int BB = C == Q4_0 ? 18 : C == Q5_0 ? 22 : 24;
+        const uint8_t* blk = row + q * BB;
+        // Q4_0: d, qs[16]; Q5_0: d, qh, qs[16]; Q5_1: d, m, qh, qs[16]
+        constexpr int NW = C == Q4_0 ? 4 : 5;
+        uint32_t wv[NW];
+        words<LDS>(blk + (C == Q5_1 ? 4 : 2), wv);
+        const float d = half_bits_to_float(*(const uint16_t*)blk);
+        A[0] = A[1] = d;
+        B[0] = B[1] = C == Q5_1 ? half_bits_to_float(*(const uint16_t*)(blk + 2)) : 0.f;
+        const uint32_t qh = C == Q4_0 ? 0u : wv[0];
+        const h2_t off = h2(C == Q4_0 ? 1032.f : C == Q5_0 ? 1040.f : 1024.f);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t qd = wv[NW - 4 + i];  // quant bytes 4i .. 4i + 3
+            uint32_t lo = qd & 0x0f0f0f0fu, hi = (qd >> 4) & 0x0f0f0f0fu;
+            if (C != Q4_0) {
+                lo |= spread4((qh >> (4 * i)) & 15u) << 4;
+                hi |= spread4((qh >> (16 + 4 * i)) & 15u) << 4;
+            }
+            bytes_to_pairs(lo, off, p[2 * i], p[2 * i + 1]);
+            bytes_to_pairs(hi, off, p[8 + 2 * i], p[8 + 2 * i + 1]);
+        }
+        xa = q * 32;
+        xb = xa + 16;
+    }
+};
+template <> struct Pair32<Q4_0> : PairLegacy<Q4_0> {};
+template <> struct Pair32<Q5_0> : PairLegacy<Q5_0> {};
+template <> struct Pair32<Q5_1> : PairLegacy<Q5_1> {};
+
+// Q6_K: v = q - 32, A = d * scale of each 16 weights
+template <> struct Pair32<Q6_K> {
+    static constexpr bool ok = true, has_b = false;
+    template <bool LDS = false>
+    static __device__ __forceinline__ void decode(const uint8_t* row, int64_t q, uint32_t (&p)[16],
+                                                  float (&A)[2], float (&B)[2], int64_t& xa, int64_t& xb) {
+        const int64_t sb = q >> 3;
+        const int r = (int)q & 7, h = r >> 2, u = r & 3;
+        const uint8_t* blk = row + sb * 210;
+        uint32_t lw[8], hw[8];
+        words<LDS>(blk + 64 * h + 32 * (u & 1), lw);
+        words<LDS>(blk + 128 + 32 * h, hw);
+        const float d = half_bits_to_float(*(const uint16_t*)(blk + 208));
+        const uint32_t scw = *(const uint16_t*)(blk + 192 + 8 * h + 2 * u);
+        A[0] = d * (float)(int8_t)(scw & 0xffu);
+        A[1] = d * (float)(int8_t)(scw >> 8);
+        B[0] = B[1] = 0.f;
+        const int lsh = 4 * (u >> 1), hsh = 2 * u;
+        const h2_t off = h2(1056.f);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t v = ((lw[i] >> lsh) & 0x0f0f0f0fu) | (((hw[i] >> hsh) & 0x03030303u) << 4);
+            bytes_to_pairs(v, off, p[2 * i], p[2 * i + 1]);
+        }
+        xa = sb * 256 + 32 * r;
+        xb = xa + 16;
+    }
+};
+
+// Q2_K: v = q, A = d * scale, B = -dmin * min of each 16 weights (blocks are
+// 4-byte aligned)
+template <> struct Pair32<Q2_K> {
+    static constexpr bool ok = true, has_b = true;
+    template <bool LDS = false>
+    static __device__ __forceinline__ void decode(const uint8_t* row, int64_t q, uint32_t (&p)[16],
+                                                  float (&A)[2], float (&B)[2], int64_t& xa, int64_t& xb) {
+        const int64_t sb = q >> 3;
+        const int r = (int)q & 7, h = r >> 2, u = r & 3;
+        const uint8_t* blk = row + sb * 84;
+        const uint32_t dd = *(const uint32_t*)(blk + 80);
+        const float d = half_bits_to_float(dd & 0xffffu), dmin = half_bits_to_float(dd >> 16);
+        const uint32_t scw = *(const uint16_t*)(blk + 8 * h + 2 * u);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const uint32_t b = (scw >> (8 * i)) & 0xffu;
+            A[i] = d * (float)(b & 15u);
+            B[i] = -(dmin * (float)(b >> 4));
+        }
+        const uint32_t* qs = (const uint32_t*)(blk + 16 + 32 * h);
+        const h2_t off = h2(1024.f);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) bytes_to_pairs((qs[i] >> (2 * u)) & 0x03030303u, off, p[2 * i], p[2 * i + 1]);
+        xa = sb * 256 + 32 * r;
+        xb = xa + 16;
+    }
+};
+
+// Q3_K: v = q in -4..3, A = d * scale of each 16 weights (scale bytes as in
+// the chunk decoder)
+template <> struct Pair32<Q3_K> {
+    static constexpr bool ok = true, has_b = false;
+    template <bool LDS = false>
+    static __device__ __forceinline__ void decode(const uint8_t* row, int64_t q, uint32_t (&p)[16],
+                                                  float (&A)[2], float (&B)[2], int64_t& xa, int64_t& xb) {
+        const int64_t sb = q >> 3;
+        const int r = (int)q & 7, h = r >> 2, u = r & 3;
+        const uint8_t* blk = row + sb * 110;
+        const float d = half_bits_to_float(*(const uint16_t*)(blk + 108));
+        const uint32_t lw = *(const uint16_t*)(blk + 96 + 2 * u);
+        const uint32_t tw = *(const uint16_t*)(blk + 104 + 2 * (u & 1));
+        const int tsh = 2 * (2 * h + (u >> 1));
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int lo = (int)((lw >> (8 * i + 4 * h)) & 15u);
+            const int top = (int)((tw >> (8 * i + tsh)) & 3u);
+            A[i] = d * (float)((lo | (top << 4)) - 32);
+        }
+        B[0] = B[1] = 0.f;
+        uint32_t hm[8], qs[8];
+        words<LDS>(blk, hm);
+        words<LDS>(blk + 32 + 32 * h, qs);
+        const int hsh = 4 * h + u;
+        const h2_t off = h2(1028.f);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t v = ((qs[i] >> (2 * u)) & 0x03030303u) | (((hm[i] >> hsh) & 0x01010101u) << 2);
+            bytes_to_pairs(v, off, p[2 * i], p[2 * i + 1]);
+        }
+        xa = sb * 256 + 32 * r;
+        xb = xa + 16;
+    }
+};
+
+// Q5_K: v = q in 0..31, A = d * sc, B = -dmin * m of the sub-block (blocks
+// are 16-byte aligned)
+template <> struct Pair32<Q5_K> {
+    static constexpr bool ok = true, has_b = true;
+    template <bool LDS = false>
+    static __device__ __forceinline__ void decode(const uint8_t* row, int64_t q, uint32_t (&p)[16],
+                                                  float (&A)[2], float (&B)[2], int64_t& xa, int64_t& xb) {
+        const int64_t sb = q >> 3;
+        const int j = (int)q & 7;
+        const uint8_t* blk = row + sb * 176;
+        const u32x4 hd = *(const u32x4*)blk;
+        int sc, m;
+        q4k_scale_min(hd, j, sc, m);
+        A[0] = A[1] = q4k_d(hd) * (float)sc;
+        B[0] = B[1] = -(q4k_dmin(hd) * (float)m);
+        const u32x4* qh = (const u32x4*)(blk + 16);
+        const u32x4* qs = (const u32x4*)(blk + 48 + 32 * (j >> 1));
+        const int nsh = 4 * (j & 1);
+        const h2_t off = h2(1024.f);
+#pragma unroll
+        for (int v = 0; v < 2; ++v) {
+            const u32x4 hv = qh[v], qv = qs[v];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t t = ((qv[i] >> nsh) & 0x0f0f0f0fu) | (((hv[i] >> j) & 0x01010101u) << 4);
+                bytes_to_pairs(t, off, p[8 * v + 2 * i], p[8 * v + 2 * i + 1]);
+            }
+        }
+        xa = sb * 256 + 32 * j;
+        xb = xa + 16;
+    }
+};
+
+// sum over 16 weights of v * x (p: 8 pairs, xw: 8 fp16 activation pairs)
+__device__ __forceinline__ float dot16(const uint32_t* p, const uint32_t* xw) {
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        s = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, p[e]), __builtin_bit_cast(h2_t, xw[e]), s, false);
+    return s;
+}
+__device__ __forceinline__ float sum16(const uint32_t* xw) {
+    const h2_t one = h2(1.f);
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s = __builtin_amdgcn_fdot2(one, __builtin_bit_cast(h2_t, xw[e]), s, false);
+    return s;
+}
+// the 16 fp16 activations at x[i .. i + 16) as 8 pairs
+__device__ __forceinline__ void load_x_pairs(const void* x, int64_t i, uint32_t* xw) {
+    const u32x4* p = (const u32x4*)((const uint16_t*)x + i);
+    const u32x4 a = p[0], b = p[1];
+    xw[0] = a[0], xw[1] = a[1], xw[2] = a[2], xw[3] = a[3];
+    xw[4] = b[0], xw[5] = b[1], xw[6] = b[2], xw[7] = b[3];
+}
+
+}  // namespace kq

@@ -12,6 +12,7 @@
 // end.  Accumulation is fp32.
 #include "kq_device.h"
 #include "kq_internal.h"
+#include "pair32.h"
 
 namespace kq {
 
@@ -187,6 +188,42 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs a) {
 #pragma unroll
         for (int i = 0; i < MB; ++i) acc[i] = 0.f, acc2[i] = 0.f;
 
+        if constexpr (XDT == F16 && Pair32<C>::ok) {
+            for (int64_t q = lane; q < nchunks; q += 64) {
+                uint32_t p[16], p2[16];
+                float A[2], B[2], A2[2], B2[2];
+                int64_t xa, xb;
+                Pair32<C>::decode(wrow, q, p, A, B, xa, xb);
+                if (GLU) Pair32<C>::decode(wrow2, q, p2, A2, B2, xa, xb);
+#pragma unroll
+                for (int i = 0; i < MB; ++i) {
+                    if (i < cnt) {
+                        uint32_t xw[16];
+                        load_x_pairs(a.x, xrow[i] * a.x_row + xa, xw);
+                        load_x_pairs(a.x, xrow[i] * a.x_row + xb, xw + 8);
+                        float s = A[0] * dot16(p, xw);
+                        s = __builtin_fmaf(A[1], dot16(p + 8, xw + 8), s);
+                        float t0 = 0.f, t1 = 0.f;
+                        if (Pair32<C>::has_b) {
+                            t0 = sum16(xw);
+                            t1 = sum16(xw + 8);
+                            s = __builtin_fmaf(B[0], t0, s);
+                            s = __builtin_fmaf(B[1], t1, s);
+                        }
+                        acc[i] += s;
+                        if (GLU) {
+                            float s2 = A2[0] * dot16(p2, xw);
+                            s2 = __builtin_fmaf(A2[1], dot16(p2 + 8, xw + 8), s2);
+                            if (Pair32<C>::has_b) {
+                                s2 = __builtin_fmaf(B2[0], t0, s2);
+                                s2 = __builtin_fmaf(B2[1], t1, s2);
+                            }
+                            acc2[i] += s2;
+                        }
+                    }
+                }
+            }
+        } else
         for (int64_t q = lane; q < nchunks; q += 64) {
             float w[32], w2[32];
             int64_t xa, xb;
@@ -275,6 +312,9 @@ hipError_t launch_skinny(int codec, int x_dt, bool glu, const SkinnyArgs& a, int
     // TQ1 decode GEMV of one fp16 activation row: table-decoded MFMA operands
     if (codec == TQ1 && x_dt == F16 && !a.ws && !glu && a.m == 1 && tq1_mv_fits(a.k))
         return launch_tq1_mv(a.w, a.n, a.k, (const uint16_t*)a.x, a.y, a.y_dt, s);
+    // the further GGUF codecs, one fp16 activation row: weights through LDS
+    if (codec >= Q4_0 && x_dt == F16 && !a.ws && !glu && a.m == 1 && cmv_fits(codec, a.k))
+        return launch_cmv(codec, a.w, a.n, a.k, (const uint16_t*)a.x, a.y, a.y_dt, s);
     int mb;
     int64_t tiles;
     if (a.ws) {

@@ -103,6 +103,57 @@ def test_qmv(kq, kind, x_dt, m, n, nblk):
 
 
 @pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("n,k", [(16, 2048), (45, 4096), (300, 6144), (33, 14336), (1, 2048)])
+def test_qmv_one_row_lds_kernel(kq, kind, n, k):
+    """One fp16 activation row with rows a whole number of the LDS kernel's
+    chunks (1024 or 2048 weights): several chunks, ragged row tiles, every
+    output dtype; and a second call gives the same bits."""
+    rng = synth.rng_for(5170 + n)
+    w = synth.weight_blocks(kind, rng, n, k)
+    x = synth.activations(rng, (1, k), "f16")
+    ref, s = oracle.qmm(kind, w, n, k, x, "f16", 1)
+    for y_dt in ("f32", "f16", "bf16"):
+        _say("qmv one row", kind, n, k, y_dt)
+        got = _run(kq, "kq_qmv", kind, w, n, k, x, "f16", 1, y_dt)
+        check_tol(got, ref, s, TAU["f16"], f"qmv one row {kind} {n}x{k} y={y_dt}",
+                  out_dt=y_dt if y_dt != "f32" else None)
+        assert np.array_equal(got, _run(kq, "kq_qmm_ws", kind, w, n, k, x, "f16", 1, y_dt))
+
+
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("n,k", [(14336, 4096), (4096, 14336)])
+def test_qmv_one_row_full_size_sampled(kq, kind, n, k):
+    """The C2 GEMV shapes as the benchmark times them (batch 1, fp16 x and
+    y), checked on 256 sampled outputs the oracle computes one by one."""
+    rng = synth.rng_for(5180)
+    w = synth.weight_blocks(kind, rng, n, k)
+    x = synth.activations(rng, (1, k), "f16")
+    _say("qmv full sampled", kind, n, k)
+    got = _run(kq, "kq_qmv", kind, w, n, k, x, "f16", 1, "f16")
+    pn = np.unique(np.concatenate([rng.integers(0, n, 250), [0, 15, 16, n - 1]]))
+    pm = np.zeros_like(pn)
+    ref, s = oracle.qmm_points(kind, w, n, k, x, "f16", 1, pm, pn)
+    check_tol(got[0, pn], ref, s, TAU["f16"], f"qmv full {kind} {n}x{k}", out_dt="f16")
+
+
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("m", [1, 3, 8])
+@pytest.mark.parametrize("scale", [2.0**-20, 1.0, 6.0e4])
+def test_qmv_activation_range(kq, kind, m, scale):
+    """fp16 activations from subnormals to near the fp16 maximum through the
+    fp16 pair products (v_dot2_f32_f16): still within the bound."""
+    n, k = 96, _k(kind, 128)
+    rng = synth.rng_for(5150 + m)
+    w = synth.weight_blocks(kind, rng, n, k)
+    xf = rng.uniform(-1.0, 1.0, size=(m, k)).astype(np.float32) * np.float32(scale)
+    x = xf.astype(np.float16).view(np.uint16)
+    _say("qmv range", kind, m, scale)
+    got = _run(kq, "kq_qmv", kind, w, n, k, x, "f16", m, "f32")
+    ref, s = oracle.qmm(kind, w, n, k, x, "f16", m)
+    check_tol(got, ref, s, TAU["f16"], f"qmv {kind} m={m} x scale {scale}")
+
+
+@pytest.mark.parametrize("kind", KINDS)
 @pytest.mark.parametrize("x_dt", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("m", [17, 40, 130])
 @pytest.mark.parametrize("fn", ["kq_qmm", "kq_qmm_ws", "kq_qmm_noalloc"])
