@@ -208,6 +208,23 @@ def test_qmv_tq1_split_k(kq, n, nblk):
         assert np.array_equal(got, again)
 
 
+@pytest.mark.parametrize("fn", ["kq_qmv", "kq_qmm_ws"])
+@pytest.mark.parametrize("scale", [2.0**-20, 6.0e4])
+def test_qmv_tq1_activation_range(kq, fn, scale):
+    """The TQ1 GEMV of one fp16 row, whole and split into K pieces (300 rows:
+    two pieces of 20 blocks), with activations from fp16 subnormals to near
+    the fp16 maximum."""
+    n, k = 300, 128 * 40
+    rng = _rng(2950)
+    w = synth.weight_blocks("tq1_g128", rng, n, k)
+    xf = rng.uniform(-1.0, 1.0, size=(1, k)).astype(np.float32) * np.float32(scale)
+    x = xf.astype(np.float16).view(np.uint16)
+    _say("qmv tq1 range", fn, scale)
+    got = _run(kq, fn, "tq1_g128", w, n, k, x, "f16", 1, "f32")
+    ref, s = oracle.qmm("tq1_g128", w, n, k, x, "f16", 1)
+    check_tol(got, ref, s, TAU["f16"], f"qmv tq1 {fn} x scale {scale}")
+
+
 @pytest.mark.parametrize("kind", KINDS)
 @pytest.mark.parametrize("m", [14, 15, 16])
 def test_qmv_long_rows_many_activations(kq, kind, m):
