@@ -9,8 +9,8 @@ workload:
   moe_c4    128 experts, Q4_K gate/up 2048x7168, down 7168x2048, top-8;
             fp16 x, fp32 h and output; 1 token (decode) and 256 tokens (seed 104)
   tq1_c5    TQ1_G128 17408x5120 and 5120x17408, fp16 x at batch 1 and M=512 (seed 105)
-  ggml_mv   the further GGUF blocks (Q4_0, Q5_0, Q5_1, Q6_K, Q2_K, Q3_K, Q5_K) in the
-            C2 GEMV shapes 14336x4096 and 4096x14336, fp16 x at batch 1, fp16 y (seed 106)
+  ggml_mv   Q8_0 and the further GGUF blocks (Q4_0, Q5_0, Q5_1, Q6_K, Q2_K, Q3_K, Q5_K)
+            in the C2 GEMV shapes 14336x4096 and 4096x14336, fp16 x at batch 1, fp16 y (seed 106)
 
 The headline value is the Q4_K decode GEMV (the six qmv_c2 calls): weight
 bytes streamed per second.  Every call reads weights from HBM: weight-bound
@@ -44,7 +44,7 @@ GIB = 1 << 30
 # (workgroups, loads in flight per lane) of the streaming-read ceiling
 READ_SHAPES = ((1024, 4), (2048, 4), (4096, 2), (4096, 4), (1024, 8), (2048, 8), (4096, 8))
 STAGES = ("dequant", "qmv_c1", "qmv_c2", "qmm_c3", "moe_c4", "tq1_c5", "ggml_mv")
-GGML_KINDS = ("q4_0", "q5_0", "q5_1", "q6_k", "q2_k", "q3_k", "q5_k")
+GGML_KINDS = ("q8_0", "q4_0", "q5_0", "q5_1", "q6_k", "q2_k", "q3_k", "q5_k")
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
 

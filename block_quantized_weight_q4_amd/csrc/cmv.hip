@@ -1,5 +1,5 @@
-// cmv.hip -- decode GEMV (one fp16 activation row) for the further GGUF
-// codecs Q4_0, Q5_0, Q5_1, Q6_K, Q2_K, Q3_K and Q5_K (kq_qmv, m = 1).
+// cmv.hip -- decode GEMV (one fp16 activation row) for Q8_0 and the further
+// GGUF codecs Q4_0, Q5_0, Q5_1, Q6_K, Q2_K, Q3_K and Q5_K (kq_qmv, m = 1).
 //
 // mlx-kquant "bindings.cpp": quantized_matmul in the decode regime; the
 // codecs are the GGUF blocks that mlx-native "quantized_matmul_id_ggml.rs"
@@ -26,6 +26,7 @@ namespace {
 // every chunk of a 16-byte-aligned row starts 16-byte aligned): bytes and
 // weights.
 template <int C> struct Unit;
+template <> struct Unit<Q8_0> { static constexpr int BYTES = 272, W = 256; };   // 8 blocks
 template <> struct Unit<Q4_0> { static constexpr int BYTES = 144, W = 256; };   // 8 blocks
 template <> struct Unit<Q5_0> { static constexpr int BYTES = 176, W = 256; };   // 8 blocks
 template <> struct Unit<Q5_1> { static constexpr int BYTES = 192, W = 256; };   // 8 blocks
@@ -190,6 +191,8 @@ __global__ __launch_bounds__(64 * W) void cmv_kernel(const uint8_t* __restrict__
 // rows, whose few workgroups leave compute units short of waves, take more
 // waves and longer chunks.
 template <int C, bool LONG> struct CmvPick;
+template <> struct CmvPick<Q8_0, false> { using Cfg = CmvCfg<Q8_0, 4, 4, 2>; };
+template <> struct CmvPick<Q8_0, true> { using Cfg = CmvCfg<Q8_0, 16, 8, 1>; };
 template <> struct CmvPick<Q4_0, false> { using Cfg = CmvCfg<Q4_0, 4, 4, 2>; };
 template <> struct CmvPick<Q5_0, false> { using Cfg = CmvCfg<Q5_0, 4, 4, 2>; };
 template <> struct CmvPick<Q5_1, false> { using Cfg = CmvCfg<Q5_1, 4, 4, 2>; };
@@ -219,6 +222,7 @@ static bool fits_c(int64_t k) {
 
 bool cmv_fits(int codec, int64_t k) {
     switch (codec) {
+    case Q8_0: return fits_c<Q8_0>(k);
     case Q4_0: return fits_c<Q4_0>(k);
     case Q5_0: return fits_c<Q5_0>(k);
     case Q5_1: return fits_c<Q5_1>(k);
@@ -248,6 +252,7 @@ static hipError_t launch_c(const uint8_t* w, int64_t n, int64_t k, const uint16_
 hipError_t launch_cmv(int codec, const uint8_t* w, int64_t n, int64_t k, const uint16_t* x, void* y,
                       int y_dt, hipStream_t s) {
     switch (codec) {
+    case Q8_0: return launch_c<Q8_0>(w, n, k, x, y, y_dt, s);
     case Q4_0: return launch_c<Q4_0>(w, n, k, x, y, y_dt, s);
     case Q5_0: return launch_c<Q5_0>(w, n, k, x, y, y_dt, s);
     case Q5_1: return launch_c<Q5_1>(w, n, k, x, y, y_dt, s);

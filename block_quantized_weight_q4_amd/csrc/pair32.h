@@ -1,5 +1,5 @@
-// pair32.h -- the further GGUF codecs (Q4_0, Q5_0, Q5_1, Q6_K, Q2_K, Q3_K,
-// Q5_K) decoded for fp16 activations: exact fp16 integer pairs and an
+// pair32.h -- Q8_0 and the further GGUF codecs (Q4_0, Q5_0, Q5_1, Q6_K, Q2_K,
+// Q3_K, Q5_K) decoded for fp16 activations: exact fp16 integer pairs and an
 // affine scale per 16 weights, multiplied on v_dot2_f32_f16.  The block
 // layouts are those of include/kq.h (the GGUF layouts of the codecs that
 // mlx-native "quantized_matmul_id_ggml.rs" dispatches).
@@ -87,6 +87,26 @@ template <int C> struct PairLegacy {
 template <> struct Pair32<Q4_0> : PairLegacy<Q4_0> {};
 template <> struct Pair32<Q5_0> : PairLegacy<Q5_0> {};
 template <> struct Pair32<Q5_1> : PairLegacy<Q5_1> {};
+
+// Q8_0 (34-byte blocks, 2-byte aligned): v = q (int8; q + 128 under the
+// exponent pattern, then minus 1152), A = d
+template <> struct Pair32<Q8_0> {
+    static constexpr bool ok = true, has_b = false;
+    template <bool LDS = false>
+    static __device__ __forceinline__ void decode(const uint8_t* row, int64_t q, uint32_t (&p)[16],
+                                                  float (&A)[2], float (&B)[2], int64_t& xa, int64_t& xb) {
+        const uint8_t* blk = row + q * 34;
+        uint32_t qw[8];
+        words<LDS>(blk + 2, qw);
+        A[0] = A[1] = half_bits_to_float(*(const uint16_t*)blk);
+        B[0] = B[1] = 0.f;
+        const h2_t off = h2(1152.f);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) bytes_to_pairs(qw[i] ^ 0x80808080u, off, p[2 * i], p[2 * i + 1]);
+        xa = q * 32;
+        xb = xa + 16;
+    }
+};
 
 // Q6_K: v = q - 32, A = d * scale of each 16 weights
 template <> struct Pair32<Q6_K> {

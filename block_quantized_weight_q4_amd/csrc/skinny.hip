@@ -312,8 +312,9 @@ hipError_t launch_skinny(int codec, int x_dt, bool glu, const SkinnyArgs& a, int
     // TQ1 decode GEMV of one fp16 activation row: table-decoded MFMA operands
     if (codec == TQ1 && x_dt == F16 && !a.ws && !glu && a.m == 1 && tq1_mv_fits(a.k))
         return launch_tq1_mv(a.w, a.n, a.k, (const uint16_t*)a.x, a.y, a.y_dt, s);
-    // the further GGUF codecs, one fp16 activation row: weights through LDS
-    if (codec >= Q4_0 && x_dt == F16 && !a.ws && !glu && a.m == 1 && cmv_fits(codec, a.k))
+    // Q8_0 and the further GGUF codecs, one fp16 activation row: weights
+    // through LDS
+    if ((codec >= Q4_0 || codec == Q8_0) && x_dt == F16 && !a.ws && !glu && a.m == 1 && cmv_fits(codec, a.k))
         return launch_cmv(codec, a.w, a.n, a.k, (const uint16_t*)a.x, a.y, a.y_dt, s);
     int mb;
     int64_t tiles;

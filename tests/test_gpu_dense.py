@@ -208,6 +208,24 @@ def test_qmv_tq1_split_k(kq, n, nblk):
         assert np.array_equal(got, again)
 
 
+@pytest.mark.parametrize("n,k", [(16, 2048), (45, 4096), (300, 6144), (33, 14336), (1, 2048)])
+def test_qmv_q8_0_one_row(kq, n, k):
+    """Q8_0, one fp16 activation row, rows a whole number of the LDS GEMV's
+    chunks: every output dtype against the oracle, with q = -128 planted (a
+    byte the encoder never writes, still decoded exactly)."""
+    rng = _rng(2960 + n)
+    w = synth.weight_blocks("q8_0", rng, n, k)
+    blocks = w.reshape(-1, 34)
+    blocks[::7, 2 + 5] = 0x80
+    x = synth.activations(rng, (1, k), "f16")
+    ref, s = oracle.qmm("q8_0", w, n, k, x, "f16", 1)
+    for y_dt in ("f32", "f16", "bf16"):
+        _say("qmv q8_0 one row", n, k, y_dt)
+        got = _run(kq, "kq_qmv", "q8_0", w, n, k, x, "f16", 1, y_dt)
+        check_tol(got, ref, s, TAU["f16"], f"qmv q8_0 one row {n}x{k} y={y_dt}",
+                  out_dt=y_dt if y_dt != "f32" else None)
+
+
 @pytest.mark.parametrize("fn", ["kq_qmv", "kq_qmm_ws"])
 @pytest.mark.parametrize("scale", [2.0**-20, 6.0e4])
 def test_qmv_tq1_activation_range(kq, fn, scale):
