@@ -120,6 +120,21 @@ def test_qmv_one_row_lds_kernel(kq, kind, n, k):
         assert np.array_equal(got, _run(kq, "kq_qmm_ws", kind, w, n, k, x, "f16", 1, y_dt))
 
 
+@pytest.mark.parametrize("kind,k", [("q4_0", 61440), ("q6_k", 51200), ("q8_0", 45056), ("q2_k", 69632)])
+def test_qmv_one_row_longest_rows(kq, kind, k):
+    """Rows near the longest the one-row LDS kernel stages (the activation
+    row and two chunk buffers fill most of the 160 KB of LDS)."""
+    n = 5
+    rng = synth.rng_for(5190)
+    w = synth.weight_blocks(kind, rng, n, k)
+    x = synth.activations(rng, (1, k), "f16")
+    _say("qmv longest rows", kind, k)
+    got = _run(kq, "kq_qmv", kind, w, n, k, x, "f16", 1, "f32")
+    ref, s = oracle.qmm(kind, w, n, k, x, "f16", 1)
+    check_tol(got, ref, s, TAU["f16"], f"qmv longest {kind} k={k}")
+    assert np.array_equal(got, _run(kq, "kq_qmm_noalloc", kind, w, n, k, x, "f16", 1, "f32"))
+
+
 @pytest.mark.parametrize("kind", KINDS)
 @pytest.mark.parametrize("n,k", [(14336, 4096), (4096, 14336)])
 def test_qmv_one_row_full_size_sampled(kq, kind, n, k):
