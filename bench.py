@@ -10,7 +10,8 @@ workload:
             fp16 x, fp32 h and output; 1 token (decode) and 256 tokens (seed 104)
   tq1_c5    TQ1_G128 17408x5120 and 5120x17408, fp16 x at batch 1 and M=512 (seed 105)
   ggml_mv   Q8_0 and the further GGUF blocks (Q4_0, Q5_0, Q5_1, Q6_K, Q2_K, Q3_K, Q5_K)
-            in the C2 GEMV shapes 14336x4096 and 4096x14336, fp16 x at batch 1, fp16 y (seed 106)
+            in the C2 GEMV shapes 14336x4096 and 4096x14336, fp16 x at batch 1, fp16 y, and the
+            further blocks' prefill GEMM in the C3 shape 14336x4096 at M=2048, bf16 x (seed 106)
 
 The headline value is the Q4_K decode GEMV (the six qmv_c2 calls): weight
 bytes streamed per second.  Every call reads weights from HBM: weight-bound
@@ -258,6 +259,20 @@ def main():
                 nbytes += pb
             stages.append(Stage(f"ggml_mv_{kind}", calls, nbytes, 0,
                                 note=f"{kind} GEMV batch 1, fp16, both C2 shapes"))
+            if kind == "q8_0":
+                continue  # (its prefill GEMM is timed by qmm_c3)
+            # the prefill GEMM in the largest C3 shape (bf16 x, kq_qmm_ws)
+            n, k, mm = 14336, 4096, 2048
+            w = d8(synth.weight_blocks(kind, rng, n, k))
+            ws = copies(w, w.numel())
+            xm = d16(synth.activations(rng, (mm, k), "bf16"), torch.bfloat16)
+            y = torch.empty((mm, n), dtype=torch.bfloat16, device=dev)
+            sc = scratch(kind, n, k, mm, torch.bfloat16)
+            part = [(lambda kind=kind, ws=ws, xm=xm, y=y, sc=sc:
+                     kq.kq_qmm_ws(kind, nxt(ws), n, k, xm, mm, y, sc)) for _ in range(8)]
+            extra_parts.append(Stage(f"ggml_mm_{kind}_{n}x{k}_m{mm}", part,
+                                     len(part) * (w.numel() + mm * (k + n) * 2),
+                                     len(part) * 2 * mm * n * k, note=f"{kind} prefill GEMM, bf16 x (kq_qmm_ws)"))
 
     # Streaming-read ceiling: a plain 16-byte-load read of the same number of
     # bytes as one C2 / C5 weight matrix (libkq_hbmread.so), rotated over

@@ -42,9 +42,8 @@ int bb_of(int t) {
     default: return 0;
     }
 }
-// the codecs with matrix-core GEMM kernels (and encoders); the other GGUF
-// blocks run every product on the chunk-decoding vector kernel
-static bool mfma_codec(int t) { return t == KQ_Q4_K || t == KQ_Q8_0 || t == KQ_TQ1_G128; }
+// the codecs with an encoder (kq_quantize)
+static bool has_encoder(int t) { return t == KQ_Q4_K || t == KQ_Q8_0 || t == KQ_TQ1_G128; }
 int64_t elem_size(int dt) { return dt == KQ_F32 ? 4 : 2; }
 bool valid_dt(int dt) { return dt == KQ_F32 || dt == KQ_F16 || dt == KQ_BF16; }
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
@@ -181,7 +180,7 @@ kq_status kq_dequantize(kq_type t, const void* w, int64_t rows, int64_t k, void*
 kq_status kq_quantize(kq_type t, const void* w, kq_dtype w_dt, int64_t rows, int64_t k,
                       const float* imatrix, void* out, void* stream) {
     if (!qk_of(t)) return fail(KQ_ERR_UNSUPPORTED, "unknown weight type");
-    if (!mfma_codec(t)) return fail(KQ_ERR_UNSUPPORTED, "no encoder for this weight type");
+    if (!has_encoder(t)) return fail(KQ_ERR_UNSUPPORTED, "no encoder for this weight type");
     if (!valid_dt(w_dt)) return fail(KQ_ERR_UNSUPPORTED, "unknown dtype");
     if (imatrix && t != KQ_Q4_K)
         return fail(KQ_ERR_UNSUPPORTED, "an importance vector steers the Q4_K encoder only");
@@ -243,7 +242,7 @@ kq_status kq_qmm(kq_type t, const void* w, int64_t n, int64_t k, const void* x, 
     int64_t row_bytes;
     kq_status st = check_product(t, w, n, k, x, x_dt, m, y, y_dt, row_bytes);
     if (st) return st;
-    if (m <= 16 || x_dt == KQ_F32 || !mfma_codec(t))
+    if (m <= 16 || x_dt == KQ_F32)
         return dense_skinny(t, w, n, k, row_bytes, x, x_dt, m, y, y_dt, (hipStream_t)stream);
     return launched(kq::launch_gemm(t, x_dt, w, n, k, x, m, y, y_dt, nullptr, (hipStream_t)stream));
 }
@@ -253,9 +252,7 @@ kq_status kq_qmm(kq_type t, const void* w, int64_t n, int64_t k, const void* x, 
 // the TQ1 GEMV of one fp16 row splits K when its rows fill few workgroups,
 // with fp32 partials [pieces][n]; the other decode products and the fp32
 // path need no scratch.
-static bool qmm_uses_gemm(kq_type t, int64_t m, kq_dtype x_dt) {
-    return m > 16 && x_dt != KQ_F32 && mfma_codec(t);
-}
+static bool qmm_uses_gemm(kq_type, int64_t m, kq_dtype x_dt) { return m > 16 && x_dt != KQ_F32; }
 
 static int64_t decode_split_bytes(kq_type t, int64_t n, int64_t k, int64_t m, kq_dtype x_dt,
                                   int* pnb) {

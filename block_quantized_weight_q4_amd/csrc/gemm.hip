@@ -30,6 +30,7 @@
 //    fp32 path instead, so no legal input loses precision silently.
 #include "kq_device.h"
 #include "kq_internal.h"
+#include "pair32.h"
 
 namespace kq {
 
@@ -329,6 +330,220 @@ template <> struct WTile<TQ1> {
     }
 };
 
+// The further GGUF codecs (Q4_0, Q5_0, Q5_1, Q6_K, Q2_K, Q3_K, Q5_K; layouts
+// as in include/kq.h): half h of step s is the 32-weight chunk q = 2s + h of
+// the row, i.e. columns 32h .. 32h + 31 of the step.  fetch() takes the
+// chunk's fields into registers; decode() forms the 32 weights exactly in
+// fp32 (one rounding for the codecs with an offset: Q5_1, Q2_K, Q5_K) and
+// rounds each once to fp16; a weight that could reach 65520, or a NaN, sends
+// the tile to the exact path.  Chunk q of a 32-weight codec is block q; of a
+// 256-weight codec it is run q % 8 of super-block q / 8.
+template <int C> struct GRaw;
+template <int C> struct GChunk;
+
+template <> struct GRaw<Q4_0> { uint32_t d, qs[4]; };
+template <> struct GChunk<Q4_0> {
+    static __device__ __forceinline__ void fetch(const uint8_t* row, int64_t q, GRaw<Q4_0>& r) {
+        const uint8_t* blk = row + q * 18;
+        r.d = *(const uint16_t*)blk;
+        words<false>(blk + 2, r.qs);
+    }
+    static __device__ __forceinline__ void decode(const GRaw<Q4_0>& r, int64_t, float (&w)[32]) {
+        const float d = half_bits_to_float(r.d);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const uint32_t b = (r.qs[j >> 2] >> (8 * (j & 3))) & 0xffu;
+            w[j] = d * (float)((int)(b & 15u) - 8);
+            w[16 + j] = d * (float)((int)(b >> 4) - 8);
+        }
+    }
+};
+
+// Q5_0 and Q5_1: [qh, qs[4]] after d (and m)
+template <> struct GRaw<Q5_0> { uint32_t d, v[5]; };
+template <> struct GRaw<Q5_1> { uint32_t dm, v[5]; };
+template <int C> struct GChunkQ5 {
+    static __device__ __forceinline__ void fetch(const uint8_t* row, int64_t q, GRaw<C>& r) {
+        const uint8_t* blk = row + q * (C == Q5_0 ? 22 : 24);
+        if constexpr (C == Q5_0) {
+            r.d = *(const uint16_t*)blk;
+            words<false>(blk + 2, r.v);
+        } else {
+            r.dm = (uint32_t)((const uint16_t*)blk)[0] | ((uint32_t)((const uint16_t*)blk)[1] << 16);
+            words<false>(blk + 4, r.v);
+        }
+    }
+    static __device__ __forceinline__ void decode(const GRaw<C>& r, int64_t, float (&w)[32]) {
+        float d, m = 0.f;
+        if constexpr (C == Q5_0) d = half_bits_to_float(r.d);
+        else d = half_bits_to_float(r.dm & 0xffffu), m = half_bits_to_float(r.dm >> 16);
+        const uint32_t qh = r.v[0];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const uint32_t b = (r.v[1 + (j >> 2)] >> (8 * (j & 3))) & 0xffu;
+            const uint32_t q0 = (b & 15u) | (((qh >> j) & 1u) << 4);
+            const uint32_t q1 = (b >> 4) | (((qh >> (j + 16)) & 1u) << 4);
+            if constexpr (C == Q5_0) {
+                w[j] = d * (float)((int)q0 - 16);
+                w[16 + j] = d * (float)((int)q1 - 16);
+            } else {
+                w[j] = __builtin_fmaf(d, (float)q0, m);
+                w[16 + j] = __builtin_fmaf(d, (float)q1, m);
+            }
+        }
+    }
+};
+template <> struct GChunk<Q5_0> : GChunkQ5<Q5_0> {};
+template <> struct GChunk<Q5_1> : GChunkQ5<Q5_1> {};
+
+// Q6_K run (h, u): ql and qh bytes of the run, the run's two scales, d
+template <> struct GRaw<Q6_K> { uint32_t ql[8], qh[8], sc, d; };
+template <> struct GChunk<Q6_K> {
+    static __device__ __forceinline__ void fetch(const uint8_t* row, int64_t q, GRaw<Q6_K>& r) {
+        const int p = (int)q & 7, h = p >> 2, u = p & 3;
+        const uint8_t* blk = row + (q >> 3) * 210;
+        words<false>(blk + 64 * h + 32 * (u & 1), r.ql);
+        words<false>(blk + 128 + 32 * h, r.qh);
+        r.sc = *(const uint16_t*)(blk + 192 + 8 * h + 2 * u);
+        r.d = *(const uint16_t*)(blk + 208);
+    }
+    static __device__ __forceinline__ void decode(const GRaw<Q6_K>& r, int64_t q, float (&w)[32]) {
+        const int u = (int)q & 3;
+        const float d = half_bits_to_float(r.d);
+        const float s0 = d * (float)(int8_t)(r.sc & 0xffu), s1 = d * (float)(int8_t)(r.sc >> 8);
+        const int lsh = 4 * (u >> 1), hsh = 2 * u;
+#pragma unroll
+        for (int l = 0; l < 32; ++l) {
+            const uint32_t lo4 = (r.ql[l >> 2] >> (8 * (l & 3) + lsh)) & 15u;
+            const uint32_t hi2 = (r.qh[l >> 2] >> (8 * (l & 3) + hsh)) & 3u;
+            w[l] = (l < 16 ? s0 : s1) * (float)((int)(lo4 | (hi2 << 4)) - 32);
+        }
+    }
+};
+
+// Q2_K run (h, u): the half's quant bytes, the run's scale/min bytes, d and dmin
+template <> struct GRaw<Q2_K> { uint32_t qs[8], sc, dd; };
+template <> struct GChunk<Q2_K> {
+    static __device__ __forceinline__ void fetch(const uint8_t* row, int64_t q, GRaw<Q2_K>& r) {
+        const int p = (int)q & 7, h = p >> 2, u = p & 3;
+        const uint8_t* blk = row + (q >> 3) * 84;
+        words<false>(blk + 16 + 32 * h, r.qs);
+        r.sc = *(const uint16_t*)(blk + 8 * h + 2 * u);
+        r.dd = (uint32_t)((const uint16_t*)(blk + 80))[0] | ((uint32_t)((const uint16_t*)(blk + 80))[1] << 16);
+    }
+    static __device__ __forceinline__ void decode(const GRaw<Q2_K>& r, int64_t q, float (&w)[32]) {
+        const int u = (int)q & 3;
+        const float d = half_bits_to_float(r.dd & 0xffffu), dmin = half_bits_to_float(r.dd >> 16);
+        float sc[2], mn[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const uint32_t b = (r.sc >> (8 * i)) & 0xffu;
+            sc[i] = d * (float)(b & 15u);
+            mn[i] = dmin * (float)(b >> 4);
+        }
+#pragma unroll
+        for (int l = 0; l < 32; ++l) {
+            const float qv = (float)((r.qs[l >> 2] >> (8 * (l & 3) + 2 * u)) & 3u);
+            w[l] = __builtin_fmaf(sc[l >> 4], qv, -mn[l >> 4]);
+        }
+    }
+};
+
+// Q3_K run (h, u): hmask and the half's quant bytes, the two scale words, d
+template <> struct GRaw<Q3_K> { uint32_t hm[8], qs[8], lw, tw, d; };
+template <> struct GChunk<Q3_K> {
+    static __device__ __forceinline__ void fetch(const uint8_t* row, int64_t q, GRaw<Q3_K>& r) {
+        const int p = (int)q & 7, h = p >> 2, u = p & 3;
+        const uint8_t* blk = row + (q >> 3) * 110;
+        words<false>(blk, r.hm);
+        words<false>(blk + 32 + 32 * h, r.qs);
+        r.lw = *(const uint16_t*)(blk + 96 + 2 * u);
+        r.tw = *(const uint16_t*)(blk + 104 + 2 * (u & 1));
+        r.d = *(const uint16_t*)(blk + 108);
+    }
+    static __device__ __forceinline__ void decode(const GRaw<Q3_K>& r, int64_t q, float (&w)[32]) {
+        const int p = (int)q & 7, h = p >> 2, u = p & 3;
+        const float d = half_bits_to_float(r.d);
+        const int tsh = 2 * (2 * h + (u >> 1));
+        float sc[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int lo = (int)((r.lw >> (8 * i + 4 * h)) & 15u);
+            const int top = (int)((r.tw >> (8 * i + tsh)) & 3u);
+            sc[i] = d * (float)((lo | (top << 4)) - 32);
+        }
+        const int hsh = 4 * h + u;
+#pragma unroll
+        for (int l = 0; l < 32; ++l) {
+            const int low = (int)((r.qs[l >> 2] >> (8 * (l & 3) + 2 * u)) & 3u);
+            const int third = (int)((r.hm[l >> 2] >> (8 * (l & 3) + hsh)) & 1u);
+            w[l] = sc[l >> 4] * (float)(low + 4 * third - 4);
+        }
+    }
+};
+
+// Q5_K sub-block j: the 16-byte head, qh[32], the sub-block's 32 nibble bytes
+template <> struct GRaw<Q5_K> { u32x4 hd, qh0, qh1, qs0, qs1; };
+template <> struct GChunk<Q5_K> {
+    static __device__ __forceinline__ void fetch(const uint8_t* row, int64_t q, GRaw<Q5_K>& r) {
+        const int j = (int)q & 7;
+        const uint8_t* blk = row + (q >> 3) * 176;
+        r.hd = *(const u32x4*)blk;
+        r.qh0 = *(const u32x4*)(blk + 16);
+        r.qh1 = *(const u32x4*)(blk + 32);
+        r.qs0 = *(const u32x4*)(blk + 48 + 32 * (j >> 1));
+        r.qs1 = *(const u32x4*)(blk + 64 + 32 * (j >> 1));
+    }
+    static __device__ __forceinline__ void decode(const GRaw<Q5_K>& r, int64_t q, float (&w)[32]) {
+        const int j = (int)q & 7;
+        int sc, m;
+        q4k_scale_min(r.hd, j, sc, m);
+        const float s = q4k_d(r.hd) * (float)sc, mn = q4k_dmin(r.hd) * (float)m;
+        const int nsh = 4 * (j & 1);
+#pragma unroll
+        for (int l = 0; l < 32; ++l) {
+            const uint32_t qb = ((l < 16 ? r.qs0 : r.qs1)[(l & 15) >> 2] >> (8 * (l & 3))) & 0xffu;
+            const uint32_t hb = ((l < 16 ? r.qh0 : r.qh1)[(l & 15) >> 2] >> (8 * (l & 3))) & 0xffu;
+            const uint32_t qq = ((qb >> nsh) & 15u) | (((hb >> j) & 1u) << 4);
+            w[l] = __builtin_fmaf(s, (float)qq, -mn);
+        }
+    }
+};
+
+template <int C> struct WTileGguf {
+    using Raw = GRaw<C>;
+    using RawQ = GRaw<C>;  // (quarters are not used for these codecs)
+    static __device__ __forceinline__ void fetch(const uint8_t* row, int s, int h, Raw& r, bool) {
+        GChunk<C>::fetch(row, 2 * (int64_t)s + h, r);
+    }
+    static __device__ __forceinline__ void decode(const Raw& r, int s, int h, uint32_t (&lo)[8],
+                                                  uint32_t (&hi)[8], int& col_lo, int& col_hi,
+                                                  bool& big) {
+        float w[32];
+        GChunk<C>::decode(r, 2 * (int64_t)s + h, w);
+        bool ok = true;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) ok &= __builtin_fabsf(w[i]) < 65520.0f;  // false for NaN
+        big |= !ok;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            lo[i] = pack_h(w[2 * i], w[2 * i + 1]);
+            hi[i] = pack_h(w[16 + 2 * i], w[17 + 2 * i]);
+        }
+        col_lo = 32 * h;
+        col_hi = 32 * h + 16;
+    }
+};
+template <> struct WTile<Q4_0> : WTileGguf<Q4_0> {};
+template <> struct WTile<Q5_0> : WTileGguf<Q5_0> {};
+template <> struct WTile<Q5_1> : WTileGguf<Q5_1> {};
+template <> struct WTile<Q6_K> : WTileGguf<Q6_K> {};
+template <> struct WTile<Q2_K> : WTileGguf<Q2_K> {};
+template <> struct WTile<Q3_K> : WTileGguf<Q3_K> {};
+template <> struct WTile<Q5_K> : WTileGguf<Q5_K> {};
+
+constexpr bool is_gguf(int c) { return c >= Q4_0; }
+
 // The per-step weight registers: halves (Raw) or quarters (RawQ).
 template <bool Q, class WT> struct RawSel { using type = typename WT::Raw; };
 template <class WT> struct RawSel<true, WT> { using type = typename WT::RawQ; };
@@ -420,9 +635,12 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const GemmArgs a) {
     // (contiguous bytes), except for TQ1, whose decoding branches on the
     // part: there each wave holds one part, so it runs one branch (measured
     // faster for TQ1, slower for the others).
-    constexpr bool QM = 4 * BN == NT && (C != Q8_0 || BM <= 128);
+    constexpr bool QM = 4 * BN == NT && (C != Q8_0 || BM <= 128) && !is_gguf(C);
     constexpr int NPART = QM ? 4 : 2;
     constexpr bool kWaveParts = C == TQ1;
+    // codecs of 32-weight blocks: a row of an odd block count ends half way
+    // through its last step
+    constexpr bool HALF_TAIL = C == Q8_0 || C == Q4_0 || C == Q5_0 || C == Q5_1;
     const int wr = kWaveParts ? tid % BN : tid / NPART, wh = kWaveParts ? tid / BN : tid % NPART;
     const bool wrole = tid < NPART * BN;
     const int64_t wrow_idx = n0 + wr;
@@ -524,7 +742,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const GemmArgs a) {
                 // its scheduling measured faster.
                 const bool ok = gm < m && c0 < k;
                 const u32x4 v = *(const u32x4*)(x + (ok ? gm * k + c0 : 0));
-                R.xr[i] = (C != Q8_0 || ok) ? v : u32x4{0u, 0u, 0u, 0u};
+                R.xr[i] = (!HALF_TAIL || ok) ? v : u32x4{0u, 0u, 0u, 0u};
             } else {
                 R.xr[i] = (gm < m && c0 < k) ? *(const u32x4*)(x + gm * k + c0) : u32x4{0u, 0u, 0u, 0u};
             }
@@ -534,10 +752,10 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const GemmArgs a) {
             const int qf = (C == Q8_0 && (int64_t)(2 * s + (wh >> 1)) * 32 >= k) ? (wh & 1) : wh;
             WT::fetch_q(wrow, s, qf, R.raw, (row_bytes & 3) == 0);
         } else if (FULL) {
-            // a Q8_0 half past the row end reads the step's first block instead
-            const int hf = (C == Q8_0 && (int64_t)(2 * s + wh) * 32 >= k) ? 0 : wh;
+            // a half past the row end reads the step's first block instead
+            const int hf = (HALF_TAIL && (int64_t)(2 * s + wh) * 32 >= k) ? 0 : wh;
             WT::fetch(wrow, s, hf, R.raw, (row_bytes & 3) == 0);
-        } else if (wrole && ((C != Q8_0) || (int64_t)(2 * s + wh) * 32 < k)) {
+        } else if (wrole && (!HALF_TAIL || (int64_t)(2 * s + wh) * 32 < k)) {
             WT::fetch(wrow, s, wh, R.raw, (row_bytes & 3) == 0);
         }
     };
@@ -582,7 +800,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const GemmArgs a) {
             // columns that are not stored and are left as decoded, except
             // for Q8_0, which also zeroes a half past the row end (that one
             // would reach stored outputs)
-            const bool live = (C != Q8_0) || (wr_valid && (int64_t)(2 * s + wh) * 32 < k);
+            const bool live = !HALF_TAIL || (wr_valid && (int64_t)(2 * s + wh) * 32 < k);
             if (FULL) {
                 WT::decode(R.raw, s, wh, lo, hi, cl, ch, wbig);
 #pragma unroll
@@ -596,7 +814,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const GemmArgs a) {
 #pragma unroll
                 for (int i = 0; i < 8; ++i) lo[i] = hi[i] = 0u;
                 cl = C == Q4_K ? 16 * wh : 32 * wh;
-                ch = C == Q4_K ? 32 + 16 * wh : 32 * wh + 16;
+                ch = C == Q4_K ? 32 + 16 * wh : 32 * wh + 16;  // (Q8_0 and the GGUF codecs alike)
             }
             *(u32x4*)&Bs[wr * LDS_STRIDE + cl] = u32x4{lo[0], lo[1], lo[2], lo[3]};
             *(u32x4*)&Bs[wr * LDS_STRIDE + cl + 8] = u32x4{lo[4], lo[5], lo[6], lo[7]};
@@ -625,8 +843,11 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const GemmArgs a) {
     //    a step to land, and the decode runs under the remaining MFMAs);
     //  - Q8_0: one register set, fetching two steps ahead, and the decode
     //    after the last sub-step (the loads have a whole step to land).
-    constexpr int kAhead = C == Q8_0 ? 2 : 3;              // steps fetched ahead
-    constexpr int kStashKs = C == Q8_0 ? BK / 16 - 1 : 1;  // sub-step the decode follows
+    // (the further GGUF codecs, whose raw fields take up to 20 registers, use
+    // the one-set pipeline of Q8_0)
+    constexpr bool ONESET = C == Q8_0 || is_gguf(C);
+    constexpr int kAhead = ONESET ? 2 : 3;              // steps fetched ahead
+    constexpr int kStashKs = ONESET ? BK / 16 - 1 : 1;  // sub-step the decode follows
     auto step = [&](int s, Regs& R) {
         const int st = s & 1;
         u32x4 af[FM], bf[FN];
@@ -859,6 +1080,13 @@ static void launch_xm(int codec, const GemmArgs& a, const GemmPlan& p, hipStream
     switch (codec) {
     case Q4_K: launch_c<Q4_K, XM>(a, p, s); break;
     case Q8_0: launch_c<Q8_0, XM>(a, p, s); break;
+    case Q4_0: launch_c<Q4_0, XM>(a, p, s); break;
+    case Q5_0: launch_c<Q5_0, XM>(a, p, s); break;
+    case Q5_1: launch_c<Q5_1, XM>(a, p, s); break;
+    case Q6_K: launch_c<Q6_K, XM>(a, p, s); break;
+    case Q2_K: launch_c<Q2_K, XM>(a, p, s); break;
+    case Q3_K: launch_c<Q3_K, XM>(a, p, s); break;
+    case Q5_K: launch_c<Q5_K, XM>(a, p, s); break;
     default: launch_c<TQ1, XM>(a, p, s); break;
     }
 }

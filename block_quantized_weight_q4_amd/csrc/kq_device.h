@@ -396,6 +396,29 @@ template <> struct Chunk32<Q5_K> {
     }
 };
 
+// One weight of the further GGUF codecs, exactly (the exact fallback of the
+// prefill GEMM): its chunk decoded, the element picked.
+template <int C>
+__device__ __forceinline__ float weight_exact_chunk(const uint8_t* row, int64_t c) {
+    float w[32];
+    int64_t xa, xb;
+    Chunk32<C>::decode(row, c >> 5, w, xa, xb);
+    // element (c - xa) of w[0..15] or 16 + (c - xb): picked by selects, so
+    // that w stays in registers
+    const int i = c - xa < 16 ? (int)(c - xa) : 16 + (int)(c - xb);
+    float v = w[0];
+#pragma unroll
+    for (int j = 1; j < 32; ++j) v = i == j ? w[j] : v;
+    return v;
+}
+template <> __device__ __forceinline__ float weight_exact<Q4_0>(const uint8_t* row, int64_t c) { return weight_exact_chunk<Q4_0>(row, c); }
+template <> __device__ __forceinline__ float weight_exact<Q5_0>(const uint8_t* row, int64_t c) { return weight_exact_chunk<Q5_0>(row, c); }
+template <> __device__ __forceinline__ float weight_exact<Q5_1>(const uint8_t* row, int64_t c) { return weight_exact_chunk<Q5_1>(row, c); }
+template <> __device__ __forceinline__ float weight_exact<Q6_K>(const uint8_t* row, int64_t c) { return weight_exact_chunk<Q6_K>(row, c); }
+template <> __device__ __forceinline__ float weight_exact<Q2_K>(const uint8_t* row, int64_t c) { return weight_exact_chunk<Q2_K>(row, c); }
+template <> __device__ __forceinline__ float weight_exact<Q3_K>(const uint8_t* row, int64_t c) { return weight_exact_chunk<Q3_K>(row, c); }
+template <> __device__ __forceinline__ float weight_exact<Q5_K>(const uint8_t* row, int64_t c) { return weight_exact_chunk<Q5_K>(row, c); }
+
 // ---------------------------------------------------------------- wave helpers
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

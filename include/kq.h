@@ -65,9 +65,10 @@
  *                order; weight 32j + l adds 16 times bit j of qh[l] to its
  *                Q4_K nibble; w = d * sc_j * q - dmin * m_j.
  * These seven are decoded and multiplied (kq_dequantize, the products and the
- * expert-routed forms) but not encoded (kq_quantize -> KQ_ERR_UNSUPPORTED);
- * their products run on the vector units (no matrix-core kernel is built for
- * them), for every m.
+ * expert-routed forms) but not encoded (kq_quantize -> KQ_ERR_UNSUPPORTED).
+ * Their prefill products (kq_qmm, m > 16, fp16 or bf16 activations) run on
+ * the matrix-core GEMM with each weight rounded once to fp16, as for Q4_K and
+ * Q8_0; their decode and expert-routed products run on the vector units.
  *
  * All multi-byte fields are little-endian.  fp16 is IEEE binary16; bf16 is
  * the upper half of an IEEE binary32.

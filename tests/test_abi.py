@@ -109,15 +109,18 @@ def test_ggml_block_geometry(kq):
     assert kq.kq_row_bytes("q6_k", 4096 + 32) == -1
 
 
-def test_ggml_codecs_take_no_scratch_and_no_encoder(kq):
-    """Their products run on the vector kernel for every m: no workspace for
-    any shape; kq_quantize rejects them before touching memory."""
+def test_ggml_codecs_workspace_and_no_encoder(kq):
+    """Their decode products take no workspace; their prefill GEMM takes the
+    same workspace plan as Q4_K's (bf16 rows, split K for few tiles);
+    kq_quantize rejects them before touching memory."""
     import torch
 
     for kind in ("q4_0", "q5_0", "q5_1", "q6_k", "q2_k", "q3_k", "q5_k"):
-        for m, dt in ((1, torch.float16), (16, torch.bfloat16), (512, torch.float16),
-                      (2048, torch.bfloat16)):
+        for m, dt in ((1, torch.float16), (16, torch.bfloat16)):
             assert kq.kq_qmm_workspace_bytes(kind, 512, 4096, m, dt) == 0, (kind, m)
+        for m, dt in ((512, torch.float16), (2048, torch.bfloat16), (64, torch.float32)):
+            assert (kq.kq_qmm_workspace_bytes(kind, 512, 4096, m, dt)
+                    == kq.kq_qmm_workspace_bytes("q4_k", 512, 4096, m, dt)), (kind, m)
     L = kq.lib()
     P = C.c_void_p
     base = 1 << 40

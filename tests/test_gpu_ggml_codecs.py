@@ -74,8 +74,8 @@ def _run(kq, fn, kind, w, n, k, x, x_dt, m, y_dt):
     wd, xd = to_dev(w), to_dev(x, x_dt)
     y = empty((m, n), y_dt)
     if fn == "kq_qmm_ws":
-        assert kq.kq_qmm_workspace_bytes(kind, n, k, m, xd.dtype) == 0
-        ws = torch.empty(256, dtype=torch.uint8, device=xd.device)
+        nb = kq.kq_qmm_workspace_bytes(kind, n, k, m, xd.dtype)
+        ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=xd.device)
         kq.kq_qmm_ws(kind, wd, n, k, xd, m, y, ws)
     else:
         getattr(kq, fn)(kind, wd, n, k, xd, m, y)
@@ -173,8 +173,8 @@ def test_qmv_activation_range(kq, kind, m, scale):
 @pytest.mark.parametrize("m", [17, 40, 130])
 @pytest.mark.parametrize("fn", ["kq_qmm", "kq_qmm_ws", "kq_qmm_noalloc"])
 def test_qmm(kq, kind, x_dt, m, fn):
-    """m > 16: tiles of 16 activation rows plus a ragged one, through the
-    three prefill entry points (none of which takes scratch here)."""
+    """m > 16 through the three prefill entry points: the matrix-core GEMM for
+    fp16 and bf16 activations, the vector kernel for fp32."""
     n, k = 75, _k(kind, 72)
     rng = synth.rng_for(5200 + m)
     w = synth.weight_blocks(kind, rng, n, k)
@@ -187,13 +187,17 @@ def test_qmm(kq, kind, x_dt, m, fn):
 
 @pytest.mark.parametrize("kind", KINDS)
 def test_one_hot_columns_exact(kq, kind):
-    """x = e_c returns column c of the decoded weights exactly, for every c,
-    in the decode (m <= 16) and the prefill (m = k) forms and with fp32 and
-    fp16 activations: the weights are never rounded below fp32."""
+    """x = e_c returns column c of the decoded weights, for every c: exactly in
+    the decode forms (m <= 16, fp32 and fp16 activations) and the fp32 prefill
+    form, and as the weight rounded once to fp16 in the matrix-core prefill
+    (m = k, fp16 activations)."""
     n, k = 40, _k(kind, 16)
     w = synth.weight_blocks(kind, synth.rng_for(5300), n, k)
     W = oracle.dequant(kind, w, n, k).astype(np.float32)
-    for fn, m, x_dt in (("kq_qmv", 16, "f32"), ("kq_qmm", k, "f32"), ("kq_qmm", k, "f16")):
+    W16 = W.astype(np.float16).astype(np.float32)
+    for fn, m, x_dt in (("kq_qmv", 16, "f32"), ("kq_qmv", 16, "f16"), ("kq_qmm", k, "f32"),
+                        ("kq_qmm", k, "f16")):
+        ref = W16 if (fn == "kq_qmm" and x_dt == "f16") else W
         for c0 in range(0, k, m):
             mm = min(m, k - c0)
             x = np.zeros((mm, k), np.float32)
@@ -201,7 +205,46 @@ def test_one_hot_columns_exact(kq, kind):
             _say("one-hot", kind, fn, x_dt, c0)
             xa = x if x_dt == "f32" else x.astype(np.float16).view(np.uint16)
             got = _run(kq, fn, kind, w, n, k, xa, x_dt, mm, "f32")
-            assert np.array_equal(got, W[:, c0:c0 + mm].T), (fn, x_dt, c0)
+            assert np.array_equal(got, ref[:, c0:c0 + mm].T), (fn, x_dt, c0)
+
+
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("x_dt", ["f16", "bf16"])
+@pytest.mark.parametrize("m,n,nb32", [(300, 200, 33), (512, 384, 64), (65, 1000, 136)])
+@pytest.mark.parametrize("fn", ["kq_qmm", "kq_qmm_ws"])
+def test_qmm_gemm(kq, kind, x_dt, m, n, nb32, fn):
+    """The matrix-core prefill GEMM: several tiles with ragged edges; rows of
+    an odd count of 32-weight blocks for the 32-weight codecs (a half step at
+    the row end); K split over workgroups with a workspace (few tiles)."""
+    k = 32 * nb32 if QK[kind] == 32 else 256 * max(1, nb32 // 8)
+    rng = synth.rng_for(5250 + m)
+    w = synth.weight_blocks(kind, rng, n, k)
+    x = synth.activations(rng, (m, k), x_dt)
+    _say("qmm gemm", kind, x_dt, m, n, k, fn)
+    got = _run(kq, fn, kind, w, n, k, x, x_dt, m, "f32")
+    ref, s = oracle.qmm(kind, w, n, k, x, x_dt, m)
+    check_tol(got, ref, s, TAU[x_dt], f"gemm {fn} {kind} {x_dt} m={m} n={n} k={k}")
+
+
+@pytest.mark.parametrize("kind", KINDS)
+def test_qmm_gemm_large_weights_take_exact_path(kq, kind):
+    """Blocks whose weights reach past the fp16 range (d = 30000 on a third of
+    the rows) send their tiles to the exact fp32 path; the result still
+    matches the oracle (fp16 activations)."""
+    n, m = 96, 40
+    k = 32 * 24 if QK[kind] == 32 else 512
+    rng = synth.rng_for(5270)
+    w = synth.weight_blocks(kind, rng, n, k)
+    bb = synth.BLOCK_BYTES[kind]
+    blocks = w.reshape(n, -1, bb)
+    big = np.array([30000.0], np.float16).view(np.uint8)
+    off = {"q4_0": 0, "q5_0": 0, "q5_1": 0, "q6_k": 208, "q2_k": 80, "q3_k": 108, "q5_k": 0}[kind]
+    blocks[::3, :, off:off + 2] = big
+    x = synth.activations(rng, (m, k), "f16")
+    _say("qmm gemm exact path", kind)
+    got = _run(kq, "kq_qmm", kind, w, n, k, x, "f16", m, "f32")
+    ref, s = oracle.qmm(kind, w, n, k, x, "f16", m)
+    check_tol(got, ref, s, TAU["f16"], f"gemm exact path {kind}")
 
 
 # ---------------------------------------------------------------- expert-routed forms
