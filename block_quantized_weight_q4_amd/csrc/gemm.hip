@@ -510,6 +510,49 @@ template <> struct GChunk<Q5_K> {
     }
 };
 
+// Q4_0, Q5_0, Q5_1 straight to fp16 pairs: the integer v (q - 8, q - 16 or
+// q) is exact in fp16 (1024 + q under the exponent pattern, minus the
+// offset), and one packed fp16 multiply by d (or fma with d and m) forms each
+// weight exactly and rounds it once, as the fp32 form would.  A weight that
+// could reach 65520 (|d| times the largest |v|, plus |m|), or a NaN scale,
+// sends the tile to the exact path.
+template <int C>
+__device__ __forceinline__ void legacy_pairs(const GRaw<C>& r, uint32_t (&lo)[8], uint32_t (&hi)[8],
+                                             bool& big) {
+    uint32_t qh = 0, dbits, mbits = 0;
+    const uint32_t* qs;
+    if constexpr (C == Q4_0) {
+        dbits = r.d, qs = r.qs;
+    } else if constexpr (C == Q5_0) {
+        dbits = r.d, qh = r.v[0], qs = r.v + 1;
+    } else {
+        dbits = r.dm & 0xffffu, mbits = r.dm >> 16, qh = r.v[0], qs = r.v + 1;
+    }
+    const float d = half_bits_to_float(dbits), mf = half_bits_to_float(mbits);
+    constexpr float vmax = C == Q4_0 ? 8.0f : C == Q5_0 ? 16.0f : 31.0f;
+    big |= !f16_safe(__builtin_fabsf(d) * vmax + __builtin_fabsf(mf));
+    const h2_t off = h2(C == Q4_0 ? 1032.f : C == Q5_0 ? 1040.f : 1024.f);
+    const h2_t d2 = __builtin_bit_cast(h2_t, dbits | (dbits << 16));
+    const h2_t m2 = __builtin_bit_cast(h2_t, mbits | (mbits << 16));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        uint32_t l = qs[i] & 0x0f0f0f0fu, u = (qs[i] >> 4) & 0x0f0f0f0fu;
+        if constexpr (C != Q4_0) {
+            l |= spread4((qh >> (4 * i)) & 15u) << 4;
+            u |= spread4((qh >> (16 + 4 * i)) & 15u) << 4;
+        }
+        uint32_t v[4];
+        bytes_to_pairs(l, off, v[0], v[1]);
+        bytes_to_pairs(u, off, v[2], v[3]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const h2_t vv = __builtin_bit_cast(h2_t, v[j]);
+            v[j] = __builtin_bit_cast(uint32_t, C == Q5_1 ? __builtin_elementwise_fma(vv, d2, m2) : vv * d2);
+        }
+        lo[2 * i] = v[0], lo[2 * i + 1] = v[1], hi[2 * i] = v[2], hi[2 * i + 1] = v[3];
+    }
+}
+
 template <int C> struct WTileGguf {
     using Raw = GRaw<C>;
     using RawQ = GRaw<C>;  // (quarters are not used for these codecs)
@@ -519,16 +562,20 @@ template <int C> struct WTileGguf {
     static __device__ __forceinline__ void decode(const Raw& r, int s, int h, uint32_t (&lo)[8],
                                                   uint32_t (&hi)[8], int& col_lo, int& col_hi,
                                                   bool& big) {
-        float w[32];
-        GChunk<C>::decode(r, 2 * (int64_t)s + h, w);
-        bool ok = true;
+        if constexpr (C == Q4_0 || C == Q5_0 || C == Q5_1) {
+            legacy_pairs<C>(r, lo, hi, big);
+        } else {
+            float w[32];
+            GChunk<C>::decode(r, 2 * (int64_t)s + h, w);
+            bool ok = true;
 #pragma unroll
-        for (int i = 0; i < 32; ++i) ok &= __builtin_fabsf(w[i]) < 65520.0f;  // false for NaN
-        big |= !ok;
+            for (int i = 0; i < 32; ++i) ok &= __builtin_fabsf(w[i]) < 65520.0f;  // false for NaN
+            big |= !ok;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            lo[i] = pack_h(w[2 * i], w[2 * i + 1]);
-            hi[i] = pack_h(w[16 + 2 * i], w[17 + 2 * i]);
+            for (int i = 0; i < 8; ++i) {
+                lo[i] = pack_h(w[2 * i], w[2 * i + 1]);
+                hi[i] = pack_h(w[16 + 2 * i], w[17 + 2 * i]);
+            }
         }
         col_lo = 32 * h;
         col_hi = 32 * h + 16;

@@ -193,8 +193,9 @@ def test_one_hot_columns_exact(kq, kind):
     (m = k, fp16 activations)."""
     n, k = 40, _k(kind, 16)
     w = synth.weight_blocks(kind, synth.rng_for(5300), n, k)
-    W = oracle.dequant(kind, w, n, k).astype(np.float32)
-    W16 = W.astype(np.float16).astype(np.float32)
+    W64 = oracle.dequant(kind, w, n, k)
+    W = W64.astype(np.float32)
+    W16 = W64.astype(np.float16).astype(np.float32)  # one rounding of the exact weight
     for fn, m, x_dt in (("kq_qmv", 16, "f32"), ("kq_qmv", 16, "f16"), ("kq_qmm", k, "f32"),
                         ("kq_qmm", k, "f16")):
         ref = W16 if (fn == "kq_qmm" and x_dt == "f16") else W
