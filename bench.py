@@ -10,7 +10,8 @@ workload:
             fp16 x, fp32 h and output; 1 token (decode) and 256 tokens (seed 104)
   tq1_c5    TQ1_G128 17408x5120 and 5120x17408, fp16 x at batch 1 and M=512 (seed 105)
   ggml_mv   Q8_0 and the further GGUF blocks (Q4_0, Q5_0, Q5_1, Q6_K, Q2_K, Q3_K, Q5_K)
-            in the C2 GEMV shapes 14336x4096 and 4096x14336, fp16 x at batch 1, fp16 y, and the
+            in the C2 GEMV shapes 14336x4096 and 4096x14336, fp16 x at batch 1 (and batch 8 as
+            extra rows), fp16 y, and the
             further blocks' prefill GEMM in the C3 shape 14336x4096 at M=2048, bf16 x (seed 106)
 
 The headline value is the Q4_K decode GEMV (the six qmv_c2 calls): weight
@@ -257,6 +258,14 @@ def main():
                                          len(part) * 2 * n * k, note=f"{kind} GEMV batch 1, fp16"))
                 calls += part
                 nbytes += pb
+                # batch 8 (the matrix-core decode kernel)
+                x8 = d16(synth.activations(rng, (8, k), "f16"), torch.float16)
+                y8 = torch.empty((8, n), dtype=torch.float16, device=dev)
+                part8 = [(lambda kind=kind, n=n, k=k, x8=x8, y8=y8, ws=ws:
+                          kq.kq_qmv(kind, nxt(ws), n, k, x8, 8, y8)) for _ in range(len(ws))]
+                extra_parts.append(Stage(f"ggml_mv_{kind}_{n}x{k}_b8", part8,
+                                         len(part8) * (w.numel() + 8 * (k + n) * 2),
+                                         len(part8) * 2 * 8 * n * k, note=f"{kind} GEMV batch 8, fp16"))
             stages.append(Stage(f"ggml_mv_{kind}", calls, nbytes, 0,
                                 note=f"{kind} GEMV batch 1, fp16, both C2 shapes"))
             if kind == "q8_0":

@@ -186,6 +186,276 @@ __global__ __launch_bounds__(64 * W) void cmv_kernel(const uint8_t* __restrict__
     }
 }
 
+// rows of this many weights and more take the LONG launch shapes
+constexpr int64_t kLongRow = 8192;
+
+// ---------------------------------------------------------------- 2..16 activation rows
+// The same weight stream feeding the matrix cores: per 32-weight chunk two
+// v_mfma_f32_16x16x16_f16 (one per 16-weight half), the activation rows as
+// the A operand (rows past m read row 0 and are not stored) and the chunk's
+// weights of the 16 rows as B.  Activations are staged per chunk next to the
+// weights (8 or 16 rows).
+// - The 32-weight blocks (Q8_0, Q4_0, Q5_0, Q5_1) fold their fp16 scale into
+//   the weights (each weight rounded once to fp16, as in the prefill GEMM)
+//   and the matrix cores accumulate across chunks.  A block whose weights
+//   could overflow fp16 sends its wave to the exact form for that buffer.
+// - The K-quants (and that exact form) multiply the exact fp16 integers of
+//   Pair8; each half's fp32 result takes its weight row's scale A[h], and
+//   B[h] times the half's activation sum (an MFMA against ones) for the
+//   codecs with an offset.
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4_t mfma4(const u32x2& a, const u32x2& b, const float4_t& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(half4_t, a), __builtin_bit_cast(half4_t, b),
+                                                 c, 0, 0, 0);
+}
+
+// W waves, CU units per chunk, S chunk buffers, MR staged activation rows
+template <int C, int W_, int CU_, int S_, int MR_>
+struct CmmCfg {
+    static constexpr int W = W_, CU = CU_, S = S_, MR = MR_;
+    static constexpr int CHB = CU * Unit<C>::BYTES, CHQ = CU * Unit<C>::W / 32, CHW = CHQ * 32;
+    static constexpr int ROW_PIECES = (CHB / 16 + 1) | 1;
+    static constexpr int WBUF = 16 * ROW_PIECES * 16;
+    static constexpr int XSTRIDE = CHW * 2 + 16;                       // bytes per staged activation row
+    static constexpr int XBUF = MR * XSTRIDE;
+    static constexpr int BUF = WBUF + XBUF;                             // one stage: weights, activations
+    static_assert((CHW * 2) % 1024 == 0, "an activation row's chunk is whole 1 KB copies");
+    static constexpr size_t lds_bytes() { return S * (size_t)BUF; }
+    static_assert(S >= 2 && W * 64 * 16 <= S * BUF, "buffers, and the final reduction fits in them");
+};
+
+template <int C, int W, int CU, int S, int MR>
+__global__ __launch_bounds__(64 * W) void cmm_kernel(const uint8_t* __restrict__ w, int64_t n, int64_t k,
+                                                     const uint16_t* __restrict__ x, int m,
+                                                     void* __restrict__ y, int y_dt) {
+    using Cfg = CmmCfg<C, W, CU, S, MR>;
+    constexpr int kRowPieces = Cfg::ROW_PIECES, kBuf = Cfg::BUF, CHB = Cfg::CHB, CHQ = Cfg::CHQ;
+    constexpr int NPIECE = 16 * kRowPieces, WLOADS = (NPIECE + 63) / 64, WL_PER_WAVE = (WLOADS + W - 1) / W;
+    constexpr int XL_ROW = Cfg::CHW * 2 / 1024;                         // 1 KB copies per activation row
+    constexpr int PER = CHQ / W;                                        // 32-weight chunks per wave and buffer
+    static_assert(CHQ % W == 0, "the waves split a chunk buffer evenly");
+    extern __shared__ __align__(16) uint8_t smem[];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n_l = lane & 15, g = lane >> 4;
+    const int64_t n0 = (int64_t)blockIdx.x * 16;
+    const int64_t row_bytes = k / Unit<C>::W * Unit<C>::BYTES;
+    const int nchunks = (int)(row_bytes / CHB);
+    const uint8_t* wbase = w + n0 * row_bytes;
+    uint32_t woff[WL_PER_WAVE];
+    bool wact[WL_PER_WAVE];
+#pragma unroll
+    for (int j = 0; j < WL_PER_WAVE; ++j) {
+        const int i = wave + W * j, p = 64 * i + lane;
+        const int r = p / kRowPieces, q = p - r * kRowPieces;
+        int64_t nr = n0 + r;
+        if (nr >= n) nr = n - 1;
+        wact[j] = i < WLOADS && r < 16 && q < CHB / 16;
+        woff[j] = (uint32_t)((nr - n0) * row_bytes) + 16u * (uint32_t)q;
+    }
+    const int xl_total = m * XL_ROW;  // 1 KB activation copies per chunk
+    // loads this wave issues per chunk: its weight copies, its share of the
+    // activation copies
+    int wave_loads = 0;
+#pragma unroll
+    for (int j = 0; j < WL_PER_WAVE; ++j) wave_loads += (wave + W * j < WLOADS) ? 1 : 0;
+    wave_loads += xl_total > wave ? (xl_total - wave + W - 1) / W : 0;
+    auto issue = [&](int chunk) {
+        uint8_t* dst = smem + (chunk % S) * kBuf;
+        const uint8_t* src = wbase + (int64_t)chunk * CHB;
+#pragma unroll
+        for (int j = 0; j < WL_PER_WAVE; ++j) {
+            const int i = wave + W * j;
+            if (i < WLOADS) {
+                const uint32_t dl = __builtin_amdgcn_readfirstlane(lds_addr(dst + 1024 * i));
+                if (wact[j]) dma16(src + woff[j], dl);
+            }
+        }
+        for (int i = wave; i < xl_total; i += W) {
+            const int r = i / XL_ROW, c = i - r * XL_ROW;
+            const uint8_t* xs = (const uint8_t*)(x + (int64_t)r * k + (int64_t)chunk * Cfg::CHW) + 1024 * c;
+            dma16(xs + 16 * lane, __builtin_amdgcn_readfirstlane(
+                                      lds_addr(dst + Cfg::WBUF + r * Cfg::XSTRIDE + 1024 * c)));
+        }
+    };
+
+    float4_t acc = {0.f, 0.f, 0.f, 0.f};
+    const int xrow = n_l < m ? n_l : 0;
+    const u32x2 ones = u32x2{0x3c003c00u, 0x3c003c00u};
+    for (int c = 0; c < S - 1 && c < nchunks; ++c) issue(c);
+    for (int c = 0; c < nchunks; ++c) {
+        // chunks c + 1 .. c + S - 2 may stay in flight
+        const int later = nchunks - 1 - c < S - 2 ? nchunks - 1 - c : S - 2;
+        wait_loads_le(later * wave_loads);
+        __syncthreads();  // chunk c has landed everywhere; every wave is done with chunk c - 1
+        if (c + S - 1 < nchunks) issue(c + S - 1);
+        const uint8_t* B = smem + (c % S) * kBuf;
+        const uint8_t* wrow = B + n_l * (kRowPieces * 16);
+        const uint8_t* xr = B + Cfg::WBUF + xrow * Cfg::XSTRIDE;
+        // this wave's chunks: PER consecutive ones
+        u32x2 a[PER][2];
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int cq = wave * PER + i;
+            a[i][0] = *(const u32x2*)(xr + 2 * (32 * cq + 4 * g));
+            a[i][1] = *(const u32x2*)(xr + 2 * (32 * cq + 16 + 4 * g));
+        }
+        auto exact = [&](int i) {
+            // unscaled integers on the matrix cores, each 16-weight half's
+            // scale (and offset) applied to the fp32 results
+            const int cq = wave * PER + i;
+            u32x2 b0, b1;
+            float A[2], Bv[2];
+            Pair8<C>::decode(wrow, cq, g, b0, b1, A, Bv);
+            const float4_t z = {0.f, 0.f, 0.f, 0.f};
+            const float4_t c0 = mfma4(a[i][0], b0, z), c1 = mfma4(a[i][1], b1, z);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[v] = __builtin_fmaf(A[0], c0[v], __builtin_fmaf(A[1], c1[v], acc[v]));
+            if constexpr (Pair8<C>::has_b) {
+                const float4_t s0 = mfma4(a[i][0], ones, z), s1 = mfma4(a[i][1], ones, z);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc[v] = __builtin_fmaf(Bv[0], s0[v], __builtin_fmaf(Bv[1], s1[v], acc[v]));
+            }
+        };
+        if constexpr (Pair8<C>::foldable) {
+            // the weights rounded once to fp16, accumulated by the matrix
+            // cores; a wave holding a block whose weights could overflow fp16
+            // takes the exact form for this chunk buffer
+            u32x2 wv[PER][2];
+            bool ok = true;
+#pragma unroll
+            for (int i = 0; i < PER; ++i) ok &= Pair8<C>::fold(wrow, wave * PER + i, g, wv[i][0], wv[i][1]);
+            if (__builtin_amdgcn_ballot_w64(!ok) == 0) {
+#pragma unroll
+                for (int i = 0; i < PER; ++i) {
+                    acc = mfma4(a[i][0], wv[i][0], acc);
+                    acc = mfma4(a[i][1], wv[i][1], acc);
+                }
+            } else {
+                for (int i = 0; i < PER; ++i) exact(i);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < PER; ++i) exact(i);
+        }
+    }
+    __syncthreads();  // every wave is done with the last chunk and no load is in flight
+    float4_t* red = (float4_t*)smem;  // [W][64]
+    red[wave * 64 + lane] = acc;
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int ww = 1; ww < W; ++ww) {
+        const float4_t t = red[ww * 64 + lane];
+        acc[0] += t[0], acc[1] += t[1], acc[2] += t[2], acc[3] += t[3];
+    }
+    // lane holds activation rows 4g + v of weight row n_l
+    const int64_t o = n0 + n_l;
+    if (o >= n) return;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int r = 4 * g + v;
+        if (r >= m) continue;
+        if (y_dt == F32) store_out<F32>(y, r * n + o, acc[v]);
+        else if (y_dt == F16) store_out<F16>(y, r * n + o, acc[v]);
+        else store_out<BF16>(y, r * n + o, acc[v]);
+    }
+}
+
+// Launch shapes (waves, units per chunk), measured on the 14336x4096 and
+// 4096x14336 GEMVs at 2 and 8 rows; rows of 8192 and more take LONG.  Deeper
+// buffering (S > 2) measured slower: the kernel is bound by its instruction
+// stream, and more LDS per workgroup only cuts occupancy.
+template <int C, bool LONG> struct CmmPick { static constexpr int W = 8, CU = 4; };
+template <> struct CmmPick<Q8_0, false> { static constexpr int W = 4, CU = 2; };
+template <> struct CmmPick<Q5_K, true> { static constexpr int W = 8, CU = 8; };
+template <> struct CmmPick<Q2_K, false> { static constexpr int W = 8, CU = 1; };
+template <> struct CmmPick<Q2_K, true> { static constexpr int W = 8, CU = 2; };
+template <bool LONG> struct CmmPick<Q6_K, LONG> { static constexpr int W = 8, CU = 1; };
+template <bool LONG> struct CmmPick<Q3_K, LONG> { static constexpr int W = 8, CU = 1; };
+
+template <int C, bool LONG>
+using CmmCfg8 = CmmCfg<C, CmmPick<C, LONG>::W, CmmPick<C, LONG>::CU, 2, 8>;
+template <int C, bool LONG>
+using CmmCfg16 = CmmCfg<C, CmmPick<C, LONG>::W, CmmPick<C, LONG>::CU, 2, 16>;
+
+// the shape a row of k weights takes: 1 LONG, 0 the other, -1 none (k is
+// not a whole number of its chunks)
+template <int C>
+static int cmm_variant(int64_t k) {
+    static_assert(CmmCfg8<C, true>::lds_bytes() <= 160 * 1024 && CmmCfg8<C, false>::lds_bytes() <= 160 * 1024,
+                  "LDS budget");
+    if (k <= 0) return -1;
+    if (k >= kLongRow && k % CmmCfg8<C, true>::CHW == 0) return 1;
+    return k % CmmCfg8<C, false>::CHW == 0 ? 0 : -1;
+}
+template <int C>
+static bool cmm_fits_c(int64_t k) { return cmm_variant<C>(k) >= 0; }
+bool cmm_fits(int codec, int64_t k) {
+    switch (codec) {
+    case Q8_0: return cmm_fits_c<Q8_0>(k);
+    case Q4_0: return cmm_fits_c<Q4_0>(k);
+    case Q5_0: return cmm_fits_c<Q5_0>(k);
+    case Q5_1: return cmm_fits_c<Q5_1>(k);
+    case Q6_K: return cmm_fits_c<Q6_K>(k);
+    case Q2_K: return cmm_fits_c<Q2_K>(k);
+    case Q3_K: return cmm_fits_c<Q3_K>(k);
+    case Q5_K: return cmm_fits_c<Q5_K>(k);
+    default: return false;
+    }
+}
+
+template <typename Cfg, int C>
+static hipError_t cmm_go(const uint8_t* w, int64_t n, int64_t k, const uint16_t* x, int m, void* y, int y_dt,
+                         hipStream_t s) {
+    hipLaunchKernelGGL((cmm_kernel<C, Cfg::W, Cfg::CU, Cfg::S, Cfg::MR>), dim3((unsigned)((n + 15) / 16)),
+                       dim3(64 * Cfg::W), Cfg::lds_bytes(), s, w, n, k, x, m, y, y_dt);
+    return hipGetLastError();
+}
+
+template <int C, bool LONG>
+static hipError_t cmm_launch_c(const uint8_t* w, int64_t n, int64_t k, const uint16_t* x, int64_t m, void* y,
+                               int y_dt, hipStream_t s) {
+    using C8 = CmmCfg8<C, LONG>;
+    using C16 = CmmCfg16<C, LONG>;
+    if (m <= 8) return cmm_go<C8, C>(w, n, k, x, (int)m, y, y_dt, s);
+    // 9..16 rows: all of them in one pass where their buffers fit in LDS,
+    // else two passes of up to 8
+    if constexpr (C16::lds_bytes() <= 160 * 1024) {
+        return cmm_go<C16, C>(w, n, k, x, (int)m, y, y_dt, s);
+    } else {
+        const size_t ysz = y_dt == F32 ? 4 : 2;
+        const hipError_t e = cmm_go<C8, C>(w, n, k, x, 8, y, y_dt, s);
+        if (e != hipSuccess) return e;
+        return cmm_go<C8, C>(w, n, k, x + 8 * k, (int)m - 8, (uint8_t*)y + 8 * n * ysz, y_dt, s);
+    }
+}
+
+template <int C>
+static hipError_t cmm_launch_k(const uint8_t* w, int64_t n, int64_t k, const uint16_t* x, int64_t m, void* y,
+                               int y_dt, hipStream_t s) {
+    // 9..16 rows: a long row whose LONG shape cannot stage 16 rows takes the
+    // other shape where that one can (one pass over the weights, not two)
+    constexpr bool long16 = CmmCfg16<C, true>::lds_bytes() <= 160 * 1024;
+    constexpr bool short16 = CmmCfg16<C, false>::lds_bytes() <= 160 * 1024;
+    const bool one_pass_short = m > 8 && !long16 && short16 && k % CmmCfg16<C, false>::CHW == 0;
+    if (cmm_variant<C>(k) == 1 && !one_pass_short) return cmm_launch_c<C, true>(w, n, k, x, m, y, y_dt, s);
+    return cmm_launch_c<C, false>(w, n, k, x, m, y, y_dt, s);
+}
+
+hipError_t launch_cmm(int codec, const uint8_t* w, int64_t n, int64_t k, const uint16_t* x, int64_t m, void* y,
+                      int y_dt, hipStream_t s) {
+    switch (codec) {
+    case Q8_0: return cmm_launch_k<Q8_0>(w, n, k, x, m, y, y_dt, s);
+    case Q4_0: return cmm_launch_k<Q4_0>(w, n, k, x, m, y, y_dt, s);
+    case Q5_0: return cmm_launch_k<Q5_0>(w, n, k, x, m, y, y_dt, s);
+    case Q5_1: return cmm_launch_k<Q5_1>(w, n, k, x, m, y, y_dt, s);
+    case Q6_K: return cmm_launch_k<Q6_K>(w, n, k, x, m, y, y_dt, s);
+    case Q2_K: return cmm_launch_k<Q2_K>(w, n, k, x, m, y, y_dt, s);
+    case Q3_K: return cmm_launch_k<Q3_K>(w, n, k, x, m, y, y_dt, s);
+    default: return cmm_launch_k<Q5_K>(w, n, k, x, m, y, y_dt, s);
+    }
+}
+
 // Launch shapes (measured on the 14336x4096 and 4096x14336 GEMVs): rows of
 // fewer than 8192 weights take four waves, two rows per lane task; longer
 // rows, whose few workgroups leave compute units short of waves, take more
@@ -208,7 +478,6 @@ template <> struct CmvPick<Q2_K, true> { using Cfg = CmvCfg<Q2_K, 8, 2, 2>; };
 template <> struct CmvPick<Q6_K, true> { using Cfg = CmvCfg<Q6_K, 8, 1, 1>; };
 template <> struct CmvPick<Q3_K, true> { using Cfg = CmvCfg<Q3_K, 8, 1, 1>; };
 
-constexpr int64_t kLongRow = 8192;
 
 template <int C, bool LONG>
 static bool fits_cfg(int64_t k) {

@@ -234,6 +234,200 @@ template <> struct Pair32<Q5_K> {
     }
 };
 
+// ---------------------------------------------------------------- one lane's part of a chunk
+// Pair8<C>::decode(row, q, g, b0, b1, A, B): lane group g (0..3) of chunk q
+// of a row: the exact fp16 integers v of weights 4g .. 4g+3 (b0, two pairs,
+// first 16-weight half) and 16+4g .. 16+4g+3 (b1, second half), and the
+// half's affine scales w = A[h] v + B[h] -- the same values Pair32 gives for
+// those weights.  These are one 16x16x16 MFMA operand slice each.  Reads
+// realigned dwords from LDS.
+template <int C> struct Pair8;
+
+// four bytes (each < 256) as fp16 integers minus off: two pairs
+__device__ __forceinline__ u32x2 bytes_pairs2(uint32_t t, h2_t off) {
+    uint32_t a, b;
+    bytes_to_pairs(t, off, a, b);
+    return u32x2{a, b};
+}
+
+// The 32-weight blocks (one fp16 d, Q5_1 also an fp16 m) also fold the scale
+// in: fold() gives the eight weights as fp16, each d*v (Q5_1: d*v + m by one
+// fma) rounded once, and returns false when a weight of the block could reach
+// 65520 or d or m is not finite (then decode() gives the exact form).
+__device__ __forceinline__ uint32_t fold_pair(uint32_t v, h2_t d2, h2_t m2, bool with_m) {
+    const h2_t vv = __builtin_bit_cast(h2_t, v);
+    return __builtin_bit_cast(uint32_t, with_m ? __builtin_elementwise_fma(vv, d2, m2) : vv * d2);
+}
+__device__ __forceinline__ u32x2 fold_pairs(const u32x2& v, uint32_t dbits, uint32_t mbits, bool with_m) {
+    const h2_t d2 = __builtin_bit_cast(h2_t, dbits | (dbits << 16));
+    const h2_t m2 = __builtin_bit_cast(h2_t, mbits | (mbits << 16));
+    const uint32_t v0 = v.x, v1 = v.y;
+    return u32x2{fold_pair(v0, d2, m2, with_m), fold_pair(v1, d2, m2, with_m)};
+}
+
+template <> struct Pair8<Q8_0> {
+    static constexpr bool has_b = false, foldable = true;
+    static __device__ __forceinline__ void ints(const uint8_t* blk, int g, u32x2& b0, u32x2& b1) {
+        uint32_t w0[1], w1[1];
+        words<true>(blk + 2 + 4 * g, w0);
+        words<true>(blk + 18 + 4 * g, w1);
+        const h2_t off = h2(1152.f);
+        b0 = bytes_pairs2(w0[0] ^ 0x80808080u, off);
+        b1 = bytes_pairs2(w1[0] ^ 0x80808080u, off);
+    }
+    static __device__ __forceinline__ void decode(const uint8_t* row, int64_t q, int g, u32x2& b0, u32x2& b1,
+                                                  float (&A)[2], float (&B)[2]) {
+        const uint8_t* blk = row + q * 34;
+        ints(blk, g, b0, b1);
+        A[0] = A[1] = half_bits_to_float(*(const uint16_t*)blk);
+        B[0] = B[1] = 0.f;
+    }
+    static __device__ __forceinline__ bool fold(const uint8_t* row, int64_t q, int g, u32x2& w0, u32x2& w1) {
+        const uint8_t* blk = row + q * 34;
+        u32x2 b0, b1;
+        ints(blk, g, b0, b1);
+        const uint32_t db = *(const uint16_t*)blk;
+        w0 = fold_pairs(b0, db, 0u, false);
+        w1 = fold_pairs(b1, db, 0u, false);
+        return __builtin_fabsf(half_bits_to_float(db)) * 128.0f < 65520.0f;  // |v| <= 128; NaN fails
+    }
+};
+
+template <int C> struct Pair8Legacy {
+    static constexpr bool has_b = C == Q5_1, foldable = true;
+    static constexpr int BB = C == Q4_0 ? 18 : C == Q5_0 ? 22 : 24, QS = C == Q4_0 ? 2 : C == Q5_0 ? 6 : 8;
+    static __device__ __forceinline__ void ints(const uint8_t* blk, int g, u32x2& b0, u32x2& b1) {
+        uint32_t qd[1];
+        words<true>(blk + QS + 4 * g, qd);  // quant bytes 4g .. 4g + 3
+        uint32_t lo = qd[0] & 0x0f0f0f0fu, hi = (qd[0] >> 4) & 0x0f0f0f0fu;
+        if constexpr (C != Q4_0) {
+            uint32_t qh[1];
+            words<true>(blk + (C == Q5_0 ? 2 : 4), qh);
+            lo |= spread4((qh[0] >> (4 * g)) & 15u) << 4;
+            hi |= spread4((qh[0] >> (16 + 4 * g)) & 15u) << 4;
+        }
+        const h2_t off = h2(C == Q4_0 ? 1032.f : C == Q5_0 ? 1040.f : 1024.f);
+        b0 = bytes_pairs2(lo, off);
+        b1 = bytes_pairs2(hi, off);
+    }
+    static __device__ __forceinline__ void decode(const uint8_t* row, int64_t q, int g, u32x2& b0, u32x2& b1,
+                                                  float (&A)[2], float (&B)[2]) {
+        const uint8_t* blk = row + q * BB;
+        ints(blk, g, b0, b1);
+        A[0] = A[1] = half_bits_to_float(*(const uint16_t*)blk);
+        B[0] = B[1] = C == Q5_1 ? half_bits_to_float(*(const uint16_t*)(blk + 2)) : 0.f;
+    }
+    static __device__ __forceinline__ bool fold(const uint8_t* row, int64_t q, int g, u32x2& w0, u32x2& w1) {
+        const uint8_t* blk = row + q * BB;
+        u32x2 b0, b1;
+        ints(blk, g, b0, b1);
+        const uint32_t db = *(const uint16_t*)blk, mb = C == Q5_1 ? *(const uint16_t*)(blk + 2) : 0u;
+        w0 = fold_pairs(b0, db, mb, C == Q5_1);
+        w1 = fold_pairs(b1, db, mb, C == Q5_1);
+        constexpr float vmax = C == Q4_0 ? 8.0f : C == Q5_0 ? 16.0f : 31.0f;
+        return __builtin_fabsf(half_bits_to_float(db)) * vmax + __builtin_fabsf(half_bits_to_float(mb)) < 65520.0f;
+    }
+};
+template <> struct Pair8<Q4_0> : Pair8Legacy<Q4_0> {};
+template <> struct Pair8<Q5_0> : Pair8Legacy<Q5_0> {};
+template <> struct Pair8<Q5_1> : Pair8Legacy<Q5_1> {};
+
+template <> struct Pair8<Q6_K> {
+    static constexpr bool has_b = false, foldable = false;
+    static __device__ __forceinline__ void decode(const uint8_t* row, int64_t q, int g, u32x2& b0, u32x2& b1,
+                                                  float (&A)[2], float (&B)[2]) {
+        const int r = (int)q & 7, h = r >> 2, u = r & 3;
+        const uint8_t* blk = row + (q >> 3) * 210;
+        const uint8_t* ql = blk + 64 * h + 32 * (u & 1);
+        const uint8_t* qh = blk + 128 + 32 * h;
+        uint32_t l0[1], l1[1], h0[1], h1[1];
+        words<true>(ql + 4 * g, l0);
+        words<true>(ql + 16 + 4 * g, l1);
+        words<true>(qh + 4 * g, h0);
+        words<true>(qh + 16 + 4 * g, h1);
+        const float d = half_bits_to_float(*(const uint16_t*)(blk + 208));
+        const uint32_t scw = *(const uint16_t*)(blk + 192 + 8 * h + 2 * u);
+        A[0] = d * (float)(int8_t)(scw & 0xffu);
+        A[1] = d * (float)(int8_t)(scw >> 8);
+        B[0] = B[1] = 0.f;
+        const int lsh = 4 * (u >> 1), hsh = 2 * u;
+        const h2_t off = h2(1056.f);
+        b0 = bytes_pairs2(((l0[0] >> lsh) & 0x0f0f0f0fu) | (((h0[0] >> hsh) & 0x03030303u) << 4), off);
+        b1 = bytes_pairs2(((l1[0] >> lsh) & 0x0f0f0f0fu) | (((h1[0] >> hsh) & 0x03030303u) << 4), off);
+    }
+};
+
+template <> struct Pair8<Q2_K> {
+    static constexpr bool has_b = true, foldable = false;
+    static __device__ __forceinline__ void decode(const uint8_t* row, int64_t q, int g, u32x2& b0, u32x2& b1,
+                                                  float (&A)[2], float (&B)[2]) {
+        const int r = (int)q & 7, h = r >> 2, u = r & 3;
+        const uint8_t* blk = row + (q >> 3) * 84;
+        const uint32_t* qs = (const uint32_t*)(blk + 16 + 32 * h);
+        const uint32_t dd = *(const uint32_t*)(blk + 80);
+        const float d = half_bits_to_float(dd & 0xffffu), dmin = half_bits_to_float(dd >> 16);
+        const uint32_t scw = *(const uint16_t*)(blk + 8 * h + 2 * u);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const uint32_t b = (scw >> (8 * i)) & 0xffu;
+            A[i] = d * (float)(b & 15u);
+            B[i] = -(dmin * (float)(b >> 4));
+        }
+        const h2_t off = h2(1024.f);
+        b0 = bytes_pairs2((qs[g] >> (2 * u)) & 0x03030303u, off);
+        b1 = bytes_pairs2((qs[4 + g] >> (2 * u)) & 0x03030303u, off);
+    }
+};
+
+template <> struct Pair8<Q3_K> {
+    static constexpr bool has_b = false, foldable = false;
+    static __device__ __forceinline__ void decode(const uint8_t* row, int64_t q, int g, u32x2& b0, u32x2& b1,
+                                                  float (&A)[2], float (&B)[2]) {
+        const int r = (int)q & 7, h = r >> 2, u = r & 3;
+        const uint8_t* blk = row + (q >> 3) * 110;
+        const float d = half_bits_to_float(*(const uint16_t*)(blk + 108));
+        const uint32_t lw = *(const uint16_t*)(blk + 96 + 2 * u);
+        const uint32_t tw = *(const uint16_t*)(blk + 104 + 2 * (u & 1));
+        const int tsh = 2 * (2 * h + (u >> 1));
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int lo = (int)((lw >> (8 * i + 4 * h)) & 15u);
+            const int top = (int)((tw >> (8 * i + tsh)) & 3u);
+            A[i] = d * (float)((lo | (top << 4)) - 32);
+        }
+        B[0] = B[1] = 0.f;
+        uint32_t m0[1], m1[1], s0[1], s1[1];
+        words<true>(blk + 4 * g, m0);
+        words<true>(blk + 16 + 4 * g, m1);
+        words<true>(blk + 32 + 32 * h + 4 * g, s0);
+        words<true>(blk + 32 + 32 * h + 16 + 4 * g, s1);
+        const int hsh = 4 * h + u;
+        const h2_t off = h2(1028.f);
+        b0 = bytes_pairs2(((s0[0] >> (2 * u)) & 0x03030303u) | (((m0[0] >> hsh) & 0x01010101u) << 2), off);
+        b1 = bytes_pairs2(((s1[0] >> (2 * u)) & 0x03030303u) | (((m1[0] >> hsh) & 0x01010101u) << 2), off);
+    }
+};
+
+template <> struct Pair8<Q5_K> {
+    static constexpr bool has_b = true, foldable = false;
+    static __device__ __forceinline__ void decode(const uint8_t* row, int64_t q, int g, u32x2& b0, u32x2& b1,
+                                                  float (&A)[2], float (&B)[2]) {
+        const int j = (int)q & 7;
+        const uint8_t* blk = row + (q >> 3) * 176;
+        const u32x4 hd = *(const u32x4*)blk;
+        int sc, m;
+        q4k_scale_min(hd, j, sc, m);
+        A[0] = A[1] = q4k_d(hd) * (float)sc;
+        B[0] = B[1] = -(q4k_dmin(hd) * (float)m);
+        const uint32_t* qh = (const uint32_t*)(blk + 16);
+        const uint32_t* qs = (const uint32_t*)(blk + 48 + 32 * (j >> 1));
+        const int nsh = 4 * (j & 1);
+        const h2_t off = h2(1024.f);
+        b0 = bytes_pairs2(((qs[g] >> nsh) & 0x0f0f0f0fu) | (((qh[g] >> j) & 0x01010101u) << 4), off);
+        b1 = bytes_pairs2(((qs[4 + g] >> nsh) & 0x0f0f0f0fu) | (((qh[4 + g] >> j) & 0x01010101u) << 4), off);
+    }
+};
+
 // sum over 16 weights of v * x (p: 8 pairs, xw: 8 fp16 activation pairs)
 __device__ __forceinline__ float dot16(const uint32_t* p, const uint32_t* xw) {
     float s = 0.f;

@@ -68,7 +68,12 @@
  * expert-routed forms) but not encoded (kq_quantize -> KQ_ERR_UNSUPPORTED).
  * Their prefill products (kq_qmm, m > 16, fp16 or bf16 activations) run on
  * the matrix-core GEMM with each weight rounded once to fp16, as for Q4_K and
- * Q8_0; their decode and expert-routed products run on the vector units.
+ * Q8_0.  Their decode products of 2..16 fp16 activation rows (rows a whole
+ * number of 1024 weights, 2048 for Q6_K and Q3_K) also run on the matrix
+ * cores: Q4_0, Q5_0, Q5_1 and Q8_0 with each weight rounded once to fp16
+ * (blocks whose weights could pass the fp16 range exactly), the K-quants with
+ * exact fp16 integers and their scales applied in fp32.  Their other decode
+ * and expert-routed products run on the vector units with exact weights.
  *
  * All multi-byte fields are little-endian.  fp16 is IEEE binary16; bf16 is
  * the upper half of an IEEE binary32.

@@ -151,6 +151,111 @@ def test_qmv_one_row_full_size_sampled(kq, kind, n, k):
     check_tol(got[0, pn], ref, s, TAU["f16"], f"qmv full {kind} {n}x{k}", out_dt="f16")
 
 
+@pytest.mark.parametrize("kind", KINDS + ["q8_0"])
+@pytest.mark.parametrize("m", [2, 5, 8, 9, 16])
+@pytest.mark.parametrize("n,k", [(45, 2048), (300, 6144), (40, 9216)])
+def test_qmv_batched_matrix_cores(kq, kind, m, n, k):
+    """2..16 fp16 activation rows with rows a whole number of the batched
+    kernel's chunks (9216: a long row that the long-row chunk of Q5_K and
+    Q2_K does not divide, and that Q6_K and Q3_K leave to the vector units):
+    the weight stream on the matrix
+    cores, 9..16 rows in one pass or two, ragged row tiles; every output
+    dtype, and the no-allocation entry gives the same bits."""
+    rng = synth.rng_for(5200 + 31 * m + n)
+    w = synth.weight_blocks(kind, rng, n, k)
+    if kind == "q8_0":
+        w.reshape(-1, 34)[::5, 2 + 9] = 0x80  # q = -128, never written by the encoder
+    x = synth.activations(rng, (m, k), "f16")
+    ref, s = oracle.qmm(kind, w, n, k, x, "f16", m)
+    for y_dt in ("f32", "f16", "bf16"):
+        _say("qmv batched", kind, m, n, k, y_dt)
+        got = _run(kq, "kq_qmv", kind, w, n, k, x, "f16", m, y_dt)
+        check_tol(got, ref, s, TAU["f16"], f"qmv batched {kind} m={m} {n}x{k} y={y_dt}",
+                  out_dt=y_dt if y_dt != "f32" else None)
+    assert np.array_equal(got, _run(kq, "kq_qmm_noalloc", kind, w, n, k, x, "f16", m, "bf16"))
+
+
+FOLDED = ("q4_0", "q5_0", "q5_1", "q8_0")  # one fp16 scale per 32 weights
+
+
+@pytest.mark.parametrize("kind", KINDS + ["q8_0"])
+@pytest.mark.parametrize("m", [5, 16])
+def test_qmv_batched_one_hot_columns(kq, kind, m):
+    """x = e_c through the batched matrix-core GEMV returns column c: the
+    weight rounded once to fp16 for the 32-weight blocks (their scale is
+    folded into the fp16 weights), the exact weight for the K-quants (their
+    scales are applied to fp32 results)."""
+    n, k = 40, 2048 if kind in ("q6_k", "q3_k") else 1024
+    w = synth.weight_blocks(kind, synth.rng_for(5310), n, k)
+    W64 = oracle.dequant(kind, w, n, k)
+    ref = (W64.astype(np.float16) if kind in FOLDED else W64).astype(np.float32)
+    for c0 in range(0, k, m):
+        mm = min(m, k - c0)
+        if mm < 2:
+            continue
+        x = np.zeros((mm, k), np.float16)
+        x[np.arange(mm), c0 + np.arange(mm)] = 1.0
+        _say("qmv batched one-hot", kind, m, c0)
+        got = _run(kq, "kq_qmv", kind, w, n, k, x.view(np.uint16), "f16", mm, "f32")
+        assert np.array_equal(got, ref[:, c0:c0 + mm].T), (kind, m, c0)
+
+
+@pytest.mark.parametrize("kind", KINDS + ["q8_0"])
+@pytest.mark.parametrize("m", [3, 16])
+def test_qmv_batched_large_scales_take_exact_path(kq, kind, m):
+    """Blocks with d = 30000 scattered over the matrix: a wave whose chunk
+    buffer holds one (its weights could pass the fp16 range when folded)
+    takes the exact form, the others the folded one; the result matches the
+    oracle."""
+    n, k = 96, 4096
+    rng = synth.rng_for(5320 + m)
+    w = synth.weight_blocks(kind, rng, n, k)
+    bb = synth.BLOCK_BYTES[kind]
+    blocks = w.reshape(n, -1, bb)
+    big = np.array([30000.0], np.float16).view(np.uint8)
+    off = {"q6_k": 208, "q2_k": 80, "q3_k": 108}.get(kind, 0)
+    blocks[::3, ::7, off:off + 2] = big
+    x = synth.activations(rng, (m, k), "f16")
+    _say("qmv batched exact path", kind, m)
+    got = _run(kq, "kq_qmv", kind, w, n, k, x, "f16", m, "f32")
+    ref, s = oracle.qmm(kind, w, n, k, x, "f16", m)
+    check_tol(got, ref, s, TAU["f16"], f"qmv batched exact path {kind} m={m}")
+
+
+@pytest.mark.parametrize("kind", KINDS + ["q8_0"])
+@pytest.mark.parametrize("n,k", [(14336, 4096), (4096, 14336)])
+@pytest.mark.parametrize("m", [8, 16])
+def test_qmv_batched_full_size_sampled(kq, kind, n, k, m):
+    """The C2 GEMV shapes at batch 8 and 16 as the benchmark times them (fp16
+    x and y), checked on sampled outputs the oracle computes one by one."""
+    rng = synth.rng_for(5210 + m)
+    w = synth.weight_blocks(kind, rng, n, k)
+    x = synth.activations(rng, (m, k), "f16")
+    _say("qmv batched full sampled", kind, n, k)
+    got = _run(kq, "kq_qmv", kind, w, n, k, x, "f16", m, "f16")
+    pn = np.concatenate([rng.integers(0, n, 120), [0, 15, 16, n - 1]])
+    pm = np.concatenate([rng.integers(0, m, 120), [0, m - 1, 3, 7]])
+    ref, s = oracle.qmm_points(kind, w, n, k, x, "f16", m, pm, pn)
+    check_tol(got[pm, pn], ref, s, TAU["f16"], f"qmv batched full {kind} {n}x{k}", out_dt="f16")
+
+
+@pytest.mark.parametrize("kind", KINDS + ["q8_0"])
+@pytest.mark.parametrize("m", [3, 8])
+@pytest.mark.parametrize("scale", [2.0**-20, 6.0e4])
+def test_qmv_batched_activation_range(kq, kind, m, scale):
+    """fp16 activations from subnormals to near the fp16 maximum through the
+    matrix-core products (exact fp16 products, fp32 sums): within the bound."""
+    n, k = 80, 4096
+    rng = synth.rng_for(5220 + m)
+    w = synth.weight_blocks(kind, rng, n, k)
+    xf = rng.uniform(-1.0, 1.0, size=(m, k)).astype(np.float32) * np.float32(scale)
+    x = xf.astype(np.float16).view(np.uint16)
+    _say("qmv batched range", kind, m, scale)
+    got = _run(kq, "kq_qmv", kind, w, n, k, x, "f16", m, "f32")
+    ref, s = oracle.qmm(kind, w, n, k, x, "f16", m)
+    check_tol(got, ref, s, TAU["f16"], f"qmv batched {kind} m={m} x scale {scale}")
+
+
 @pytest.mark.parametrize("kind", KINDS)
 @pytest.mark.parametrize("m", [1, 3, 8])
 @pytest.mark.parametrize("scale", [2.0**-20, 1.0, 6.0e4])
