@@ -362,97 +362,110 @@ __global__ __launch_bounds__(64 * W) void cmm_kernel(const uint8_t* __restrict__
 }
 
 // Launch shapes (waves, units per chunk), measured on the 14336x4096 and
-// 4096x14336 GEMVs at 2 and 8 rows; rows of 8192 and more take LONG.  Deeper
-// buffering (S > 2) measured slower: the kernel is bound by its instruction
-// stream, and more LDS per workgroup only cuts occupancy.
-template <int C, bool LONG> struct CmmPick { static constexpr int W = 8, CU = 4; };
-template <> struct CmmPick<Q8_0, false> { static constexpr int W = 4, CU = 2; };
-template <> struct CmmPick<Q5_K, true> { static constexpr int W = 8, CU = 8; };
-template <> struct CmmPick<Q2_K, false> { static constexpr int W = 8, CU = 1; };
-template <> struct CmmPick<Q2_K, true> { static constexpr int W = 8, CU = 2; };
-template <bool LONG> struct CmmPick<Q6_K, LONG> { static constexpr int W = 8, CU = 1; };
-template <bool LONG> struct CmmPick<Q3_K, LONG> { static constexpr int W = 8, CU = 1; };
+// 4096x14336 GEMVs at 2, 4, 8 and 16 rows; rows of 8192 and more take LONG
+// (256 workgroups on the 4096-row shape: sixteen waves each).  MR, the rows
+// the activation buffer holds, is the fewest of 2, 4, 8, 16 that take m:
+// smaller buffers let more workgroups share a compute unit (Q6_K at m = 2:
+// 22.1 -> 16.6 us).  Deeper buffering (S > 2) measured slower: more LDS per
+// workgroup only cuts occupancy.
+template <int C, bool LONG, int MR> struct CmmPick {
+    static constexpr int W = LONG ? 16 : MR == 16 ? 4 : 8;
+    static constexpr int CU = LONG ? (MR == 16 ? 4 : 8) : (MR == 16 ? 2 : 4);
+};
+template <bool LONG, int MR> struct CmmPick<Q8_0, LONG, MR> {
+    static constexpr int W = LONG ? 16 : 4, CU = LONG ? (MR == 16 ? 4 : 8) : 2;
+};
+template <bool LONG, int MR> struct CmmPick<Q5_K, LONG, MR> {
+    static constexpr int W = LONG || MR == 16 ? 16 : 8;
+    static constexpr int CU = LONG ? (MR == 16 ? 4 : 8) : MR == 16 ? 4 : MR == 8 ? 4 : 8;
+};
+template <bool LONG, int MR> struct CmmPick<Q2_K, LONG, MR> { static constexpr int W = LONG ? 16 : 8, CU = LONG ? 2 : 1; };
+template <bool LONG, int MR> struct CmmPick<Q6_K, LONG, MR> { static constexpr int W = LONG ? 16 : 8, CU = 1; };
+template <bool LONG, int MR> struct CmmPick<Q3_K, LONG, MR> { static constexpr int W = LONG ? 16 : 8, CU = 1; };
 
-template <int C, bool LONG>
-using CmmCfg8 = CmmCfg<C, CmmPick<C, LONG>::W, CmmPick<C, LONG>::CU, 2, 8>;
-template <int C, bool LONG>
-using CmmCfg16 = CmmCfg<C, CmmPick<C, LONG>::W, CmmPick<C, LONG>::CU, 2, 16>;
+template <int C, bool LONG, int MR>
+using CmmCfgR = CmmCfg<C, CmmPick<C, LONG, MR>::W, CmmPick<C, LONG, MR>::CU, 2, MR>;
 
-// the shape a row of k weights takes: 1 LONG, 0 the other, -1 none (k is
-// not a whole number of its chunks)
-template <int C>
-static int cmm_variant(int64_t k) {
-    static_assert(CmmCfg8<C, true>::lds_bytes() <= 160 * 1024 && CmmCfg8<C, false>::lds_bytes() <= 160 * 1024,
+// 16 staged rows fit in LDS for every codec but Q6_K, which takes 9..16 rows
+// in two passes of 8
+template <int C> constexpr bool kCmm16 = CmmCfgR<C, false, 16>::lds_bytes() <= 160 * 1024 &&
+                                         CmmCfgR<C, true, 16>::lds_bytes() <= 160 * 1024;
+
+template <int C, int MR>
+static int cmm_variant_mr(int64_t k) {
+    static_assert(CmmCfgR<C, true, MR>::lds_bytes() <= 160 * 1024 && CmmCfgR<C, false, MR>::lds_bytes() <= 160 * 1024,
                   "LDS budget");
     if (k <= 0) return -1;
-    if (k >= kLongRow && k % CmmCfg8<C, true>::CHW == 0) return 1;
-    return k % CmmCfg8<C, false>::CHW == 0 ? 0 : -1;
+    if (k >= kLongRow && k % CmmCfgR<C, true, MR>::CHW == 0) return 1;
+    return k % CmmCfgR<C, false, MR>::CHW == 0 ? 0 : -1;
 }
+// the shape a product of m rows of k weights takes: 1 LONG, 0 the other, -1
+// none (k is not a whole number of its chunks)
 template <int C>
-static bool cmm_fits_c(int64_t k) { return cmm_variant<C>(k) >= 0; }
-bool cmm_fits(int codec, int64_t k) {
+static int cmm_variant(int64_t k, int64_t m) {
+    if (m <= 2) return cmm_variant_mr<C, 2>(k);
+    if (m <= 4) return cmm_variant_mr<C, 4>(k);
+    if (m <= 8 || !kCmm16<C>) return cmm_variant_mr<C, 8>(k);
+    if constexpr (kCmm16<C>) return cmm_variant_mr<C, 16>(k);
+    return -1;
+}
+bool cmm_fits(int codec, int64_t k, int64_t m) {
+    if (m < 2 || m > 16) return false;
     switch (codec) {
-    case Q8_0: return cmm_fits_c<Q8_0>(k);
-    case Q4_0: return cmm_fits_c<Q4_0>(k);
-    case Q5_0: return cmm_fits_c<Q5_0>(k);
-    case Q5_1: return cmm_fits_c<Q5_1>(k);
-    case Q6_K: return cmm_fits_c<Q6_K>(k);
-    case Q2_K: return cmm_fits_c<Q2_K>(k);
-    case Q3_K: return cmm_fits_c<Q3_K>(k);
-    case Q5_K: return cmm_fits_c<Q5_K>(k);
+    case Q8_0: return cmm_variant<Q8_0>(k, m) >= 0;
+    case Q4_0: return cmm_variant<Q4_0>(k, m) >= 0;
+    case Q5_0: return cmm_variant<Q5_0>(k, m) >= 0;
+    case Q5_1: return cmm_variant<Q5_1>(k, m) >= 0;
+    case Q6_K: return cmm_variant<Q6_K>(k, m) >= 0;
+    case Q2_K: return cmm_variant<Q2_K>(k, m) >= 0;
+    case Q3_K: return cmm_variant<Q3_K>(k, m) >= 0;
+    case Q5_K: return cmm_variant<Q5_K>(k, m) >= 0;
     default: return false;
     }
 }
 
-template <typename Cfg, int C>
+template <int C, bool LONG, int MR>
 static hipError_t cmm_go(const uint8_t* w, int64_t n, int64_t k, const uint16_t* x, int m, void* y, int y_dt,
                          hipStream_t s) {
+    using Cfg = CmmCfgR<C, LONG, MR>;
     hipLaunchKernelGGL((cmm_kernel<C, Cfg::W, Cfg::CU, Cfg::S, Cfg::MR>), dim3((unsigned)((n + 15) / 16)),
                        dim3(64 * Cfg::W), Cfg::lds_bytes(), s, w, n, k, x, m, y, y_dt);
     return hipGetLastError();
 }
-
-template <int C, bool LONG>
-static hipError_t cmm_launch_c(const uint8_t* w, int64_t n, int64_t k, const uint16_t* x, int64_t m, void* y,
-                               int y_dt, hipStream_t s) {
-    using C8 = CmmCfg8<C, LONG>;
-    using C16 = CmmCfg16<C, LONG>;
-    if (m <= 8) return cmm_go<C8, C>(w, n, k, x, (int)m, y, y_dt, s);
-    // 9..16 rows: all of them in one pass where their buffers fit in LDS,
-    // else two passes of up to 8
-    if constexpr (C16::lds_bytes() <= 160 * 1024) {
-        return cmm_go<C16, C>(w, n, k, x, (int)m, y, y_dt, s);
-    } else {
-        const size_t ysz = y_dt == F32 ? 4 : 2;
-        const hipError_t e = cmm_go<C8, C>(w, n, k, x, 8, y, y_dt, s);
-        if (e != hipSuccess) return e;
-        return cmm_go<C8, C>(w, n, k, x + 8 * k, (int)m - 8, (uint8_t*)y + 8 * n * ysz, y_dt, s);
-    }
+template <int C, int MR>
+static hipError_t cmm_go_k(const uint8_t* w, int64_t n, int64_t k, const uint16_t* x, int m, void* y, int y_dt,
+                           hipStream_t s) {
+    if (cmm_variant_mr<C, MR>(k) == 1) return cmm_go<C, true, MR>(w, n, k, x, m, y, y_dt, s);
+    return cmm_go<C, false, MR>(w, n, k, x, m, y, y_dt, s);
 }
 
 template <int C>
-static hipError_t cmm_launch_k(const uint8_t* w, int64_t n, int64_t k, const uint16_t* x, int64_t m, void* y,
+static hipError_t cmm_launch_c(const uint8_t* w, int64_t n, int64_t k, const uint16_t* x, int64_t m, void* y,
                                int y_dt, hipStream_t s) {
-    // 9..16 rows: a long row whose LONG shape cannot stage 16 rows takes the
-    // other shape where that one can (one pass over the weights, not two)
-    constexpr bool long16 = CmmCfg16<C, true>::lds_bytes() <= 160 * 1024;
-    constexpr bool short16 = CmmCfg16<C, false>::lds_bytes() <= 160 * 1024;
-    const bool one_pass_short = m > 8 && !long16 && short16 && k % CmmCfg16<C, false>::CHW == 0;
-    if (cmm_variant<C>(k) == 1 && !one_pass_short) return cmm_launch_c<C, true>(w, n, k, x, m, y, y_dt, s);
-    return cmm_launch_c<C, false>(w, n, k, x, m, y, y_dt, s);
+    if (m <= 2) return cmm_go_k<C, 2>(w, n, k, x, (int)m, y, y_dt, s);
+    if (m <= 4) return cmm_go_k<C, 4>(w, n, k, x, (int)m, y, y_dt, s);
+    if (m <= 8) return cmm_go_k<C, 8>(w, n, k, x, (int)m, y, y_dt, s);
+    if constexpr (kCmm16<C>) {
+        return cmm_go_k<C, 16>(w, n, k, x, (int)m, y, y_dt, s);
+    } else {
+        const size_t ysz = y_dt == F32 ? 4 : 2;
+        const hipError_t e = cmm_go_k<C, 8>(w, n, k, x, 8, y, y_dt, s);
+        if (e != hipSuccess) return e;
+        return cmm_go_k<C, 8>(w, n, k, x + 8 * k, (int)m - 8, (uint8_t*)y + 8 * n * ysz, y_dt, s);
+    }
 }
 
 hipError_t launch_cmm(int codec, const uint8_t* w, int64_t n, int64_t k, const uint16_t* x, int64_t m, void* y,
                       int y_dt, hipStream_t s) {
     switch (codec) {
-    case Q8_0: return cmm_launch_k<Q8_0>(w, n, k, x, m, y, y_dt, s);
-    case Q4_0: return cmm_launch_k<Q4_0>(w, n, k, x, m, y, y_dt, s);
-    case Q5_0: return cmm_launch_k<Q5_0>(w, n, k, x, m, y, y_dt, s);
-    case Q5_1: return cmm_launch_k<Q5_1>(w, n, k, x, m, y, y_dt, s);
-    case Q6_K: return cmm_launch_k<Q6_K>(w, n, k, x, m, y, y_dt, s);
-    case Q2_K: return cmm_launch_k<Q2_K>(w, n, k, x, m, y, y_dt, s);
-    case Q3_K: return cmm_launch_k<Q3_K>(w, n, k, x, m, y, y_dt, s);
-    default: return cmm_launch_k<Q5_K>(w, n, k, x, m, y, y_dt, s);
+    case Q8_0: return cmm_launch_c<Q8_0>(w, n, k, x, m, y, y_dt, s);
+    case Q4_0: return cmm_launch_c<Q4_0>(w, n, k, x, m, y, y_dt, s);
+    case Q5_0: return cmm_launch_c<Q5_0>(w, n, k, x, m, y, y_dt, s);
+    case Q5_1: return cmm_launch_c<Q5_1>(w, n, k, x, m, y, y_dt, s);
+    case Q6_K: return cmm_launch_c<Q6_K>(w, n, k, x, m, y, y_dt, s);
+    case Q2_K: return cmm_launch_c<Q2_K>(w, n, k, x, m, y, y_dt, s);
+    case Q3_K: return cmm_launch_c<Q3_K>(w, n, k, x, m, y, y_dt, s);
+    default: return cmm_launch_c<Q5_K>(w, n, k, x, m, y, y_dt, s);
     }
 }
 

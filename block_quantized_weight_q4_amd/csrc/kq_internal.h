@@ -110,7 +110,7 @@ bool cmv_fits(int codec, int64_t k);
 hipError_t launch_cmv(int codec, const uint8_t* w, int64_t n, int64_t k, const uint16_t* x, void* y,
                       int y_dt, hipStream_t s);
 // ... and of 2..16 fp16 activation rows on the matrix cores (passes of 8 rows)
-bool cmm_fits(int codec, int64_t k);
+bool cmm_fits(int codec, int64_t k, int64_t m);
 hipError_t launch_cmm(int codec, const uint8_t* w, int64_t n, int64_t k, const uint16_t* x, int64_t m, void* y,
                       int y_dt, hipStream_t s);
 hipError_t launch_splitk_reduce(const float* part, int pieces, int64_t count, void* y, int y_dt,

@@ -318,7 +318,7 @@ hipError_t launch_skinny(int codec, int x_dt, bool glu, const SkinnyArgs& a, int
         return launch_cmv(codec, a.w, a.n, a.k, (const uint16_t*)a.x, a.y, a.y_dt, s);
     // ... and 2..16 rows (dense, the rows contiguous) on the matrix cores
     if ((codec >= Q4_0 || codec == Q8_0) && x_dt == F16 && !a.ws && !glu && a.m >= 2 && a.m <= 16 &&
-        a.x_row == a.k && a.y_row == a.n && cmm_fits(codec, a.k))
+        a.x_row == a.k && a.y_row == a.n && cmm_fits(codec, a.k, a.m))
         return launch_cmm(codec, a.w, a.n, a.k, (const uint16_t*)a.x, a.m, a.y, a.y_dt, s);
     int mb;
     int64_t tiles;
