@@ -293,10 +293,12 @@ def test_qmm(kq, kind, x_dt, m, fn):
 @pytest.mark.parametrize("kind", KINDS)
 def test_one_hot_columns_exact(kq, kind):
     """x = e_c returns column c of the decoded weights, for every c: exactly in
-    the decode forms (m <= 16, fp32 and fp16 activations) and the fp32 prefill
-    form, and as the weight rounded once to fp16 in the matrix-core prefill
-    (m = k, fp16 activations)."""
-    n, k = 40, _k(kind, 16)
+    the vector-unit decode forms (m <= 16, fp32 and fp16 activations; 17
+    blocks of 32 are no whole number of the batched matrix-core kernel's
+    chunks, whose one-hot test is test_qmv_batched_one_hot_columns) and the
+    fp32 prefill form, and as the weight rounded once to fp16 in the
+    matrix-core prefill (m = k, fp16 activations)."""
+    n, k = 40, _k(kind, 17)
     w = synth.weight_blocks(kind, synth.rng_for(5300), n, k)
     W64 = oracle.dequant(kind, w, n, k)
     W = W64.astype(np.float32)
