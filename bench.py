@@ -13,6 +13,8 @@ workload:
             in the C2 GEMV shapes 14336x4096 and 4096x14336, fp16 x at batch 1 (and batch 8 as
             extra rows), fp16 y, and the
             further blocks' prefill GEMM in the C3 shape 14336x4096 at M=2048, bf16 x (seed 106)
+  ggml_moe  one-token MoE layers (gate/up + SwiGLU, down + weighted sum) with those blocks at
+            the C4 matrix shapes: 32 experts, top-8, fp16 x, fp32 h (seed 107)
 
 The headline value is the Q4_K decode GEMV (the six qmv_c2 calls): weight
 bytes streamed per second.  Every call reads weights from HBM: weight-bound
@@ -45,7 +47,7 @@ BF16_PEAK_TFS = 2500.0
 GIB = 1 << 30
 # (workgroups, loads in flight per lane) of the streaming-read ceiling
 READ_SHAPES = ((1024, 4), (2048, 4), (4096, 2), (4096, 4), (1024, 8), (2048, 8), (4096, 8))
-STAGES = ("dequant", "qmv_c1", "qmv_c2", "qmm_c3", "moe_c4", "tq1_c5", "ggml_mv")
+STAGES = ("dequant", "qmv_c1", "qmv_c2", "qmm_c3", "moe_c4", "tq1_c5", "ggml_mv", "ggml_moe")
 GGML_KINDS = ("q8_0", "q4_0", "q5_0", "q5_1", "q6_k", "q2_k", "q3_k", "q5_k")
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
@@ -282,6 +284,36 @@ def main():
             extra_parts.append(Stage(f"ggml_mm_{kind}_{n}x{k}_m{mm}", part,
                                      len(part) * (w.numel() + mm * (k + n) * 2),
                                      len(part) * 2 * mm * n * k, note=f"{kind} prefill GEMM, bf16 x (kq_qmm_ws)"))
+
+    if "ggml_moe" in wanted:
+        # one-token MoE layers (gate/up + SwiGLU, down + weighted sum) with
+        # Q8_0 and the further GGUF codecs at the C4 matrix shapes: 32 experts
+        # (their 0.5-1.5 GB exceed the 256 MB Infinity Cache), top-8, fp16 x,
+        # fp32 h, 64 tokens of distinct routings
+        rng = synth.rng_for(107)
+        E, H, F, top_k, T = 32, 7168, 2048, 8, 64
+        xg = d16(synth.activations(rng, (T, H), "f16"), torch.float16)
+        idg = torch.from_numpy(np.stack([rng.choice(E, top_k, replace=False) for _ in range(T)])
+                               .astype(np.int32)).to(dev)
+        scg = torch.from_numpy(rng.uniform(0.05, 1.0, size=(T, top_k)).astype(np.float32)).to(dev)
+        for kind in GGML_KINDS:
+            gs, ds = F * synth.row_bytes(kind, H), H * synth.row_bytes(kind, F)
+            g_w = d8(synth.weight_blocks(kind, rng, E * F, H))
+            u_w = d8(synth.weight_blocks(kind, rng, E * F, H))
+            dn_w = d8(synth.weight_blocks(kind, rng, E * H, F))
+            mws_g = torch.empty(kq.kq_moe_workspace_bytes(E, 1, top_k, H), dtype=torch.uint8, device=dev)
+            h_g = torch.empty((1, top_k, F), dtype=torch.float32, device=dev)
+            o_g = torch.empty((1, H), dtype=torch.float32, device=dev)
+
+            def layer1(t, kind=kind, g_w=g_w, u_w=u_w, dn_w=dn_w, gs=gs, ds=ds, mws_g=mws_g, h_g=h_g, o_g=o_g):
+                kq.kq_moe_glu(kind, g_w, u_w, E, F, H, gs, xg[t:t + 1], idg[t:t + 1], 1, top_k, h_g, mws_g)
+                kq.kq_qmm_id(kind, dn_w, E, H, F, ds, h_g, kq.LAYOUT_SLOTTED, idg[t:t + 1], 1, top_k,
+                             scg[t:t + 1], o_g, mws_g)
+
+            calls = [lambda t=t, layer1=layer1: layer1(t) for t in range(T)]
+            extra_parts.append(Stage(f"ggml_moe_{kind}_decode", calls, T * top_k * (2 * gs + ds),
+                                     T * top_k * 2 * 3 * F * H,
+                                     note=f"{kind} one-token MoE layer at the C4 shapes, 32 experts, top-8"))
 
     # Streaming-read ceiling: a plain 16-byte-load read of the same number of
     # bytes as one C2 / C5 weight matrix (libkq_hbmread.so), rotated over

@@ -505,6 +505,40 @@ static kq_status qmm_id_impl(kq_type t, const void* w, int64_t n_experts, int64_
         d.w_sh = (const uint8_t*)w_sh;
         return launched(kq::launch_down_mix1(d, x_dt == KQ_F32, s));
     }
+    // ... and for Q8_0 and the further GGUF codecs where their kernel takes k.
+    // fp32 rows are split into fp16 hi + lo once, into the workspace's slot
+    // buffer (unused by this form) where they fit, else by each workgroup.
+    const kq::MoeLayout L1 = kq::moe_layout(n_experts + shexp, 1, S, n);
+    const int64_t x_rows1 = x_layout == KQ_LAYOUT_SLOTTED ? S : 1;
+    const int mode1 = x_dt == KQ_F16 ? 0 : (x_rows1 * k * 4 <= L1.slot_bytes ? 1 : 2);
+    if (scores && n_tokens == 1 && (t == KQ_Q8_0 || t >= KQ_Q4_0) && (x_dt == KQ_F16 || x_dt == KQ_F32) &&
+        kq::down1_fits(t, k, S, mode1)) {
+        kq::DownMixArgs d{};
+        d.w = (const uint8_t*)w;
+        d.expert_stride = expert_stride;
+        d.row_bytes = row_bytes;
+        d.n = n;
+        d.k = k;
+        d.x = x;
+        d.slotted = x_layout == KQ_LAYOUT_SLOTTED;
+        d.ids = ids;
+        d.scores = scores;
+        d.n_experts = n_experts;
+        d.top_k = S;
+        d.y = y;
+        d.y_dt = y_dt;
+        d.shexp = shexp;
+        d.w_sh = (const uint8_t*)w_sh;
+        if (mode1 == 1) {
+            uint8_t* xsplit = (uint8_t*)workspace + L1.slot_off_bytes;
+            int32_t* xexp = (int32_t*)workspace + L1.xexp_off;
+            const hipError_t e = kq::launch_split_rows((const float*)x, x_rows1, k, xsplit, xexp, s);
+            if (e != hipSuccess) return launched(e);
+            d.x = xsplit;
+            d.xexp = xexp;
+        }
+        return launched(kq::launch_down1_gguf(t, d, mode1, s));
+    }
     const kq::MoeLayout L = kq::moe_layout(n_experts + shexp, n_tokens, S, scores ? n : 0);
     int32_t* ws = (int32_t*)workspace;
     // the unmixed form's rows with an invalid id are poisoned by the route;
@@ -600,7 +634,10 @@ static kq_status moe_glu_impl(kq_type t, const void* gate_w, const void* up_w, i
     // one token with fp16 activations: each grid row is one slot, whose
     // expert id is read directly (no schedule)
     const bool direct = n_tokens == 1 && t == KQ_Q4_K && x_dt == KQ_F16;
-    if (direct) {
+    // (Q8_0 and the further GGUF codecs, where their kernel takes k)
+    const bool direct_gguf = n_tokens == 1 && (t == KQ_Q8_0 || t >= KQ_Q4_0) && x_dt == KQ_F16 &&
+                             kq::glu1_fits(t, k);
+    if (direct || direct_gguf) {
         a.ids = ids;
         a.m = 1;
     } else {
@@ -633,6 +670,7 @@ static kq_status moe_glu_impl(kq_type t, const void* gate_w, const void* up_w, i
     a.act = act;
     a.limit = limit;
     if (direct) return launched(kq::launch_moe_glu1(a, s));
+    if (direct_gguf) return launched(kq::launch_glu1_gguf(t, a, s));
     return launched(kq::launch_skinny(t, x_dt, true, a, L.max_tiles, s));
 }
 

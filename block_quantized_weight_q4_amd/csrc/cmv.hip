@@ -545,4 +545,677 @@ hipError_t launch_cmv(int codec, const uint8_t* w, int64_t n, int64_t k, const u
     }
 }
 
+// ---------------------------------------------------------------- one token, expert-routed
+// The one-row kernel's weight stream for the single-token MoE forms, with
+// the expert ids read directly (no schedule), as moe_dec.hip does for Q4_K:
+// - cglu1_kernel (kq_moe_glu, fp16 activations): grid (row tile, slot); the
+//   slot expert's 16 gate rows and the same 16 up rows stream together (32
+//   LDS rows), and one lane task decodes a 32-weight chunk of gate row i and
+//   of up row i against one activation read.  h = act(gate, up) is formed
+//   before the single store; a slot with an invalid id gets NaN rows.
+// - cdown1_kernel (kq_qmm_id with scores): the down projection with the
+//   weighted sum over the token's slots fused in.  The slots' activation rows
+//   are staged once; the workgroup's 16 rows walk the slots' experts in slot
+//   order as one row of S*k weights, and each lane task's partial sum is
+//   scaled by its slot's router weight.  fp32 activations are split per slot
+//   row into fp16 hi + lo parts of the row scaled by a power of two (its
+//   largest magnitude in [2^14, 2^15): 22 significant bits), both on
+//   v_dot2_f32_f16.  A token with an invalid id gets NaN outputs.
+
+__device__ __forceinline__ void put_dt(void* y, int64_t i, int dt, float v) {
+    if (dt == F32) store_out<F32>(y, i, v);
+    else if (dt == F16) store_out<F16>(y, i, v);
+    else store_out<BF16>(y, i, v);
+}
+
+// 16 fp32 values times 2^ne as fp16 hi and lo pairs (hi + lo holds 22
+// significant bits of each); the exponent that puts a row's largest
+// magnitude in [2^14, 2^15) (0 for a zero or non-finite maximum)
+__device__ __forceinline__ void split16(const uint32_t (&v)[16], int ne, uint32_t (&hw)[8], uint32_t (&lw)[8]) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const float f0 = __builtin_ldexpf(__builtin_bit_cast(float, v[2 * q]), ne);
+        const float f1 = __builtin_ldexpf(__builtin_bit_cast(float, v[2 * q + 1]), ne);
+        const _Float16 h0 = (_Float16)f0, h1 = (_Float16)f1;
+        const _Float16 l0 = (_Float16)(f0 - (float)h0), l1 = (_Float16)(f1 - (float)h1);
+        hw[q] = __builtin_bit_cast(uint32_t, h2_t{h0, h1});
+        lw[q] = __builtin_bit_cast(uint32_t, h2_t{l0, l1});
+    }
+}
+__device__ __forceinline__ int split_exponent(float mx) {
+    int ex = 0;
+    if (mx > 0.f && mx <= 3.402823466e38f) {
+        __builtin_frexpf(mx, &ex);
+        ex -= 15;
+    }
+    return ex;
+}
+
+template <int C, int W, int CU>
+__global__ __launch_bounds__(64 * W) void cglu1_kernel(SkinnyArgs a) {
+    using Cfg = CmvCfg<C, W, CU, 2>;
+    constexpr int kRowPieces = Cfg::ROW_PIECES, kNBuf = 2, kWBuf = 2 * Cfg::WBUF;  // 32 LDS rows
+    constexpr int NPIECE = 32 * kRowPieces, WLOADS = (NPIECE + 63) / 64, WL_PER_WAVE = (WLOADS + W - 1) / W;
+    constexpr int TASKS = 16 * Cfg::CHQ;
+    extern __shared__ __align__(16) uint8_t smem[];
+    uint8_t* wbuf = smem;                                             // [kNBuf][32 rows]
+    uint16_t* xs = (uint16_t*)(smem + kNBuf * kWBuf);                 // [k]
+    float* red = (float*)(smem + kNBuf * kWBuf + (size_t)a.k * 2);    // [W][2][16]
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t n = a.n, k = a.k, n0 = (int64_t)blockIdx.x * 16, slot = blockIdx.y;
+    const uint32_t e = slot_expert(a.ids, slot, a.top_k, a.shexp, a.n_experts);
+    if ((int64_t)e >= a.n_experts + a.shexp) {
+        if (tid < 16 && n0 + tid < n) put_dt(a.y, slot * a.y_row + n0 + tid, a.y_dt, __builtin_nanf(""));
+        return;
+    }
+    const int64_t row_bytes = a.row_bytes;
+    const int nchunks = (int)(row_bytes / Cfg::CHB);
+    const uint8_t* wg = expert_base(a.w, a.w_sh, e, a.n_experts, a.expert_stride) + n0 * row_bytes;
+    const uint8_t* wu = expert_base(a.w2, a.w2_sh, e, a.n_experts, a.expert_stride) + n0 * row_bytes;
+
+    // ---- the token's activation row into LDS
+    const uint16_t* x = (const uint16_t*)a.x;
+    const int xpieces = (int)(k / 8);
+    for (int p0 = 64 * wave; p0 < xpieces; p0 += 64 * W) {
+        const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr((const uint8_t*)xs + 16 * (int64_t)p0));
+        if (p0 + lane < xpieces) dma16(x + 8 * (int64_t)(p0 + lane), dst);
+    }
+    // ---- weight pieces: LDS piece p = 64 i + lane is piece p % kRowPieces of
+    // LDS row p / kRowPieces (rows 0..15 gate, 16..31 up)
+    uint32_t woff[WL_PER_WAVE];
+    bool wact[WL_PER_WAVE], wup[WL_PER_WAVE];
+#pragma unroll
+    for (int j = 0; j < WL_PER_WAVE; ++j) {
+        const int i = wave + W * j;
+        const int p = 64 * i + lane;
+        const int r = p / kRowPieces, q = p - r * kRowPieces;
+        const int rr = r & 15;
+        int64_t nr = n0 + rr;
+        if (nr >= n) nr = n - 1;
+        wact[j] = i < WLOADS && r < 32 && q < Cfg::CHB / 16;
+        wup[j] = r >= 16;
+        woff[j] = (uint32_t)((nr - n0) * row_bytes) + 16u * (uint32_t)q;
+    }
+    int wave_loads = 0;
+#pragma unroll
+    for (int j = 0; j < WL_PER_WAVE; ++j) wave_loads += (wave + W * j < WLOADS) ? 1 : 0;
+    auto issue = [&](int chunk) {
+        uint8_t* dst = wbuf + (chunk % kNBuf) * kWBuf;
+        const int64_t cb = (int64_t)chunk * Cfg::CHB;
+#pragma unroll
+        for (int j = 0; j < WL_PER_WAVE; ++j) {
+            const int i = wave + W * j;
+            if (i < WLOADS) {
+                const uint32_t dl = __builtin_amdgcn_readfirstlane(lds_addr(dst + 1024 * i));
+                if (wact[j]) dma16((wup[j] ? wu : wg) + cb + woff[j], dl);
+            }
+        }
+    };
+
+    float acc[2] = {0.f, 0.f};  // gate, up
+    const int rg = lane & 15;   // this lane's row
+    for (int c = 0; c < kNBuf - 1 && c < nchunks; ++c) issue(c);
+    for (int c = 0; c < nchunks; ++c) {
+        const int later = (nchunks - 1 < c + kNBuf - 2 ? nchunks - 1 : c + kNBuf - 2) - c;
+        wait_loads_le(later * wave_loads);
+        __syncthreads();
+        if (c + kNBuf - 1 < nchunks) issue(c + kNBuf - 1);
+        const uint8_t* B = wbuf + (c % kNBuf) * kWBuf;
+        const int64_t kbase = (int64_t)c * (Cfg::CHQ * 32);
+        for (int t = lane + 64 * wave; t < TASKS; t += 64 * W) {
+            const int cq = t >> 4;
+            uint32_t pw[2][16];
+            float A[2][2], Bv[2][2];
+            int64_t xa = 0, xb = 0;
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                Pair32<C>::template decode<true>(B + (rg + 16 * j) * (kRowPieces * 16), cq, pw[j], A[j], Bv[j],
+                                                 xa, xb);
+            uint32_t xw[16];
+            const u32x4* xp = (const u32x4*)(xs + kbase + xa);
+            const u32x4* xq = (const u32x4*)(xs + kbase + xb);
+            const u32x4 x0 = xp[0], x1 = xp[1], x2 = xq[0], x3 = xq[1];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) xw[q] = x0[q], xw[4 + q] = x1[q], xw[8 + q] = x2[q], xw[12 + q] = x3[q];
+            float t0 = 0.f, t1 = 0.f;
+            if (Pair32<C>::has_b) {
+                t0 = sum16(xw);
+                t1 = sum16(xw + 8);
+            }
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                float sj = A[j][0] * dot16(pw[j], xw);
+                sj = __builtin_fmaf(A[j][1], dot16(pw[j] + 8, xw + 8), sj);
+                if (Pair32<C>::has_b) {
+                    sj = __builtin_fmaf(Bv[j][0], t0, sj);
+                    sj = __builtin_fmaf(Bv[j][1], t1, sj);
+                }
+                acc[j] += sj;
+            }
+        }
+    }
+    // ---- lanes rg, rg + 16, rg + 32, rg + 48 of every wave hold row rg
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        acc[j] += __shfl_xor(acc[j], 16, 64);
+        acc[j] += __shfl_xor(acc[j], 32, 64);
+    }
+    if (lane < 16) red[(wave * 2 + 0) * 16 + lane] = acc[0], red[(wave * 2 + 1) * 16 + lane] = acc[1];
+    __syncthreads();
+    if (wave == 0 && lane < 16) {
+        float gs = 0.f, us = 0.f;
+        for (int ww = 0; ww < W; ++ww) gs += red[(ww * 2 + 0) * 16 + lane], us += red[(ww * 2 + 1) * 16 + lane];
+        if (n0 + lane < n) put_dt(a.y, slot * a.y_row + n0 + lane, a.y_dt, glu_act(a.act, gs, us, a.limit));
+    }
+}
+
+template <int C, int W, int CU, int R, bool XF32>
+__global__ __launch_bounds__(64 * W) void cdown1_kernel(DownMixArgs d) {
+    using Cfg = CmvCfg<C, W, CU, R>;
+    constexpr int kRowPieces = Cfg::ROW_PIECES, kWBuf = Cfg::WBUF, kNBuf = 2, kRG = Cfg::RG;
+    constexpr int NPIECE = 16 * kRowPieces, WLOADS = (NPIECE + 63) / 64, WL_PER_WAVE = (WLOADS + W - 1) / W;
+    constexpr int ESZ = XF32 ? 4 : 2;  // staged bytes per activation
+    extern __shared__ __align__(16) uint8_t smem[];
+    const int S = (int)d.top_k;
+    const int64_t n = d.n, k = d.k, n0 = (int64_t)blockIdx.x * 16;
+    uint8_t* wbuf = smem;                                               // [kNBuf][kWBuf]
+    uint8_t* xs = smem + kNBuf * kWBuf;                                 // [S][k] staged activations
+    int32_t* xe = (int32_t*)(xs + (size_t)S * k * ESZ);                 // [S] row exponents (fp32)
+    float* red = (float*)(xe + 16);                                     // [W][16]
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+    // a token with an invalid expert id has NaN outputs
+    bool bad = false;
+    for (int r = 0; r < S; ++r)
+        bad |= (int64_t)slot_expert(d.ids, r, S, d.shexp, d.n_experts) >= d.n_experts + d.shexp;
+    if (bad) {
+        if (tid < 16 && n0 + tid < n) put_dt(d.y, n0 + tid, d.y_dt, __builtin_nanf(""));
+        return;
+    }
+    const int64_t row_bytes = d.row_bytes;
+    const int cps = (int)(row_bytes / Cfg::CHB);  // chunks per slot (k is a multiple of the chunk)
+    const int nchunks = S * cps;
+
+    // ---- the slots' activation rows into LDS (slot-major, ESZ bytes each)
+    {
+        const int64_t ppr = k * ESZ / 16;  // 16-byte pieces per row
+        const int64_t total = S * ppr;
+        const uint8_t* xb = (const uint8_t*)d.x;
+        for (int64_t p0 = 64 * wave; p0 < total; p0 += 64 * W) {
+            const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(xs + 16 * p0));
+            const int64_t p = p0 + lane;
+            if (p < total) {
+                const int64_t r = p / ppr, q = p - r * ppr;
+                dma16(xb + (d.slotted ? r * k * ESZ : 0) + 16 * q, dst);
+            }
+        }
+    }
+    // ---- weight pieces (as in cmv_kernel), from the expert of each chunk's slot
+    uint32_t woff[WL_PER_WAVE];
+    bool wact[WL_PER_WAVE];
+#pragma unroll
+    for (int j = 0; j < WL_PER_WAVE; ++j) {
+        const int i = wave + W * j;
+        const int p = 64 * i + lane;
+        const int r = p / kRowPieces, q = p - r * kRowPieces;
+        int64_t nr = n0 + r;
+        if (nr >= n) nr = n - 1;
+        wact[j] = i < WLOADS && r < 16 && q < Cfg::CHB / 16;
+        woff[j] = (uint32_t)((nr - n0) * row_bytes) + 16u * (uint32_t)q;
+    }
+    int wave_loads = 0;
+#pragma unroll
+    for (int j = 0; j < WL_PER_WAVE; ++j) wave_loads += (wave + W * j < WLOADS) ? 1 : 0;
+    auto issue = [&](int chunk) {
+        uint8_t* dst = wbuf + (chunk % kNBuf) * kWBuf;
+        const int r = chunk / cps, lc = chunk - r * cps;
+        const uint8_t* src = expert_base(d.w, d.w_sh, slot_expert(d.ids, r, S, d.shexp, d.n_experts), d.n_experts,
+                                         d.expert_stride) +
+                             n0 * row_bytes + (int64_t)lc * Cfg::CHB;
+#pragma unroll
+        for (int j = 0; j < WL_PER_WAVE; ++j) {
+            const int i = wave + W * j;
+            if (i < WLOADS) {
+                const uint32_t dl = __builtin_amdgcn_readfirstlane(lds_addr(dst + 1024 * i));
+                if (wact[j]) dma16(src + woff[j], dl);
+            }
+        }
+    };
+
+    float acc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = 0.f;
+    const int rg = lane % kRG;
+    for (int c = 0; c < kNBuf - 1 && c < nchunks; ++c) issue(c);
+    for (int c = 0; c < nchunks; ++c) {
+        const int later = (nchunks - 1 < c + kNBuf - 2 ? nchunks - 1 : c + kNBuf - 2) - c;
+        wait_loads_le(later * wave_loads);  // (the activation copies were issued before every weight chunk)
+        __syncthreads();
+        if (c + kNBuf - 1 < nchunks) issue(c + kNBuf - 1);
+        if (XF32 && c == 0) {
+            // each slot row's exponent, then its values scaled by 2^-e and
+            // split in place into fp16 hi and lo: every 16 floats (64 bytes)
+            // become 16 hi halves then 16 lo halves
+            for (int r = wave; r < S; r += W) {
+                const float* row = (const float*)xs + (int64_t)r * k;
+                float mx = 0.f;
+                for (int64_t i = lane; i < k; i += 64) mx = __builtin_fmaxf(mx, __builtin_fabsf(row[i]));
+#pragma unroll
+                for (int o = 32; o > 0; o >>= 1) mx = __builtin_fmaxf(mx, __shfl_xor(mx, o, 64));
+                if (lane == 0) xe[r] = split_exponent(mx);
+            }
+            __syncthreads();
+            for (int64_t gi = tid; gi < (int64_t)S * k / 16; gi += 64 * W) {
+                const int ne = -xe[(gi * 16) / k];
+                u32x4* g4 = (u32x4*)(xs + 64 * gi);
+                uint32_t v[16];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const u32x4 u = g4[q];
+                    v[4 * q] = u.x, v[4 * q + 1] = u.y, v[4 * q + 2] = u.z, v[4 * q + 3] = u.w;
+                }
+                uint32_t hw[8], lw[8];
+                split16(v, ne, hw, lw);
+                g4[0] = u32x4{hw[0], hw[1], hw[2], hw[3]};
+                g4[1] = u32x4{hw[4], hw[5], hw[6], hw[7]};
+                g4[2] = u32x4{lw[0], lw[1], lw[2], lw[3]};
+                g4[3] = u32x4{lw[4], lw[5], lw[6], lw[7]};
+            }
+            __syncthreads();
+        }
+        const uint8_t* B = wbuf + (c % kNBuf) * kWBuf;
+        const int r = c / cps;
+        const float sc = d.scores[r];
+        const int ex = XF32 ? xe[r] : 0;
+        const int64_t kbase = (int64_t)r * k + (int64_t)(c - r * cps) * (Cfg::CHQ * 32);
+        for (int t = lane + 64 * wave; t < Cfg::TASKS; t += 64 * W) {
+            const int cq = t / kRG;
+            uint32_t p[R][16];
+            float A[R][2], Bv[R][2];
+            int64_t xa = 0, xb = 0;
+#pragma unroll
+            for (int j = 0; j < R; ++j)
+                Pair32<C>::template decode<true>(B + (rg + kRG * j) * (kRowPieces * 16), cq, p[j], A[j], Bv[j],
+                                                 xa, xb);
+            if constexpr (!XF32) {
+                uint32_t xw[16];
+                const u32x4* xp = (const u32x4*)((const uint16_t*)xs + kbase + xa);
+                const u32x4* xq = (const u32x4*)((const uint16_t*)xs + kbase + xb);
+                const u32x4 x0 = xp[0], x1 = xp[1], x2 = xq[0], x3 = xq[1];
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    xw[q] = x0[q], xw[4 + q] = x1[q], xw[8 + q] = x2[q], xw[12 + q] = x3[q];
+                float t0 = 0.f, t1 = 0.f;
+                if (Pair32<C>::has_b) {
+                    t0 = sum16(xw);
+                    t1 = sum16(xw + 8);
+                }
+#pragma unroll
+                for (int j = 0; j < R; ++j) {
+                    float sj = A[j][0] * dot16(p[j], xw);
+                    sj = __builtin_fmaf(A[j][1], dot16(p[j] + 8, xw + 8), sj);
+                    if (Pair32<C>::has_b) {
+                        sj = __builtin_fmaf(Bv[j][0], t0, sj);
+                        sj = __builtin_fmaf(Bv[j][1], t1, sj);
+                    }
+                    acc[j] = __builtin_fmaf(sc, sj, acc[j]);
+                }
+            } else {
+                // 16-element groups at (kbase + xa) / 16 and (kbase + xb) / 16:
+                // 8 dwords of hi pairs, then 8 of lo pairs
+                const u32x4* ga = (const u32x4*)(xs + 4 * (kbase + xa));
+                const u32x4* gb = (const u32x4*)(xs + 4 * (kbase + xb));
+                uint32_t ha[8], la[8], hb[8], lb[8];
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    const u32x4 u0 = ga[q], u1 = ga[2 + q], u2 = gb[q], u3 = gb[2 + q];
+#pragma unroll
+                    for (int z = 0; z < 4; ++z)
+                        ha[4 * q + z] = u0[z], la[4 * q + z] = u1[z], hb[4 * q + z] = u2[z], lb[4 * q + z] = u3[z];
+                }
+                float t0 = 0.f, t1 = 0.f;
+                if (Pair32<C>::has_b) {
+                    t0 = sum16(ha) + sum16(la);
+                    t1 = sum16(hb) + sum16(lb);
+                }
+#pragma unroll
+                for (int j = 0; j < R; ++j) {
+                    float sj = A[j][0] * (dot16(p[j], ha) + dot16(p[j], la));
+                    sj = __builtin_fmaf(A[j][1], dot16(p[j] + 8, hb) + dot16(p[j] + 8, lb), sj);
+                    if (Pair32<C>::has_b) {
+                        sj = __builtin_fmaf(Bv[j][0], t0, sj);
+                        sj = __builtin_fmaf(Bv[j][1], t1, sj);
+                    }
+                    acc[j] += __builtin_ldexpf(sc * sj, ex);
+                }
+            }
+        }
+    }
+    // ---- lanes rg, rg + kRG, ... of every wave hold rows rg + kRG j
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+#pragma unroll
+        for (int o = kRG; o < 64; o <<= 1)
+            acc[j] += __shfl_xor(acc[j], o, 64);
+    }
+    if (lane < kRG) {
+#pragma unroll
+        for (int j = 0; j < R; ++j) red[wave * 16 + rg + kRG * j] = acc[j];
+    }
+    __syncthreads();
+    if (wave == 0 && lane < 16) {
+        float v = 0.f;
+        for (int ww = 0; ww < W; ++ww) v += red[ww * 16 + lane];
+        if (n0 + lane < n) put_dt(d.y, n0 + lane, d.y_dt, v);
+    }
+}
+
+// fp32 activation rows split once for every workgroup of cdown1s_kernel:
+// one workgroup per row
+__global__ __launch_bounds__(256) void split_rows_kernel(const float* __restrict__ x, int64_t k,
+                                                         uint8_t* __restrict__ out, int32_t* __restrict__ xexp) {
+    __shared__ float part[4];
+    __shared__ int ex_s;
+    const int64_t r = blockIdx.x;
+    const int tid = threadIdx.x;
+    const float* row = x + r * k;
+    float mx = 0.f;
+    for (int64_t c = tid; c < k; c += 256) mx = __builtin_fmaxf(mx, __builtin_fabsf(row[c]));
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mx = __builtin_fmaxf(mx, __shfl_xor(mx, o, 64));
+    if ((tid & 63) == 0) part[tid >> 6] = mx;
+    __syncthreads();
+    if (tid == 0) {
+        ex_s = split_exponent(__builtin_fmaxf(__builtin_fmaxf(part[0], part[1]), __builtin_fmaxf(part[2], part[3])));
+        xexp[r] = ex_s;
+    }
+    __syncthreads();
+    const int ne = -ex_s;
+    for (int64_t g = tid; g < k / 16; g += 256) {
+        const u32x4* src = (const u32x4*)(row + 16 * g);
+        uint32_t v[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const u32x4 u = src[q];
+            v[4 * q] = u.x, v[4 * q + 1] = u.y, v[4 * q + 2] = u.z, v[4 * q + 3] = u.w;
+        }
+        uint32_t hw[8], lw[8];
+        split16(v, ne, hw, lw);
+        u32x4* dst = (u32x4*)(out + 64 * (r * (k / 16) + g));
+        dst[0] = u32x4{hw[0], hw[1], hw[2], hw[3]};
+        dst[1] = u32x4{hw[4], hw[5], hw[6], hw[7]};
+        dst[2] = u32x4{lw[0], lw[1], lw[2], lw[3]};
+        dst[3] = u32x4{lw[4], lw[5], lw[6], lw[7]};
+    }
+}
+
+hipError_t launch_split_rows(const float* x, int64_t rows, int64_t k, uint8_t* out, int32_t* xexp, hipStream_t s) {
+    hipLaunchKernelGGL(split_rows_kernel, dim3((unsigned)rows), dim3(256), 0, s, x, k, out, xexp);
+    return hipGetLastError();
+}
+
+// The down projection with each chunk's activations staged beside its
+// weights (no staging of all slots up front): fp16 activations (PRE false)
+// or fp32 rows split by split_rows_kernel (PRE true: 64-byte groups of 16 hi
+// and 16 lo halves, the row's exponent in d.xexp).
+template <int C, int W, int CU, int R, bool PRE>
+__global__ __launch_bounds__(64 * W) void cdown1s_kernel(DownMixArgs d) {
+    using Cfg = CmvCfg<C, W, CU, R>;
+    constexpr int kRowPieces = Cfg::ROW_PIECES, kWBuf = Cfg::WBUF, kNBuf = 2, kRG = Cfg::RG;
+    constexpr int NPIECE = 16 * kRowPieces, WLOADS = (NPIECE + 63) / 64, WL_PER_WAVE = (WLOADS + W - 1) / W;
+    constexpr int ESZ = PRE ? 4 : 2;                  // staged bytes per activation
+    constexpr int XB = Cfg::CHQ * 32 * ESZ;           // activation bytes of one chunk
+    constexpr int XL = XB / 1024;                     // 1 KB copies of them
+    constexpr int BUF = kWBuf + XB;
+    static_assert(XB % 1024 == 0, "a chunk's activations are whole 1 KB copies");
+    extern __shared__ __align__(16) uint8_t smem[];
+    float* red = (float*)(smem + kNBuf * BUF);        // [W][16]
+    const int S = (int)d.top_k;
+    const int64_t n = d.n, k = d.k, n0 = (int64_t)blockIdx.x * 16;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+    // a token with an invalid expert id has NaN outputs
+    bool bad = false;
+    for (int r = 0; r < S; ++r)
+        bad |= (int64_t)slot_expert(d.ids, r, S, d.shexp, d.n_experts) >= d.n_experts + d.shexp;
+    if (bad) {
+        if (tid < 16 && n0 + tid < n) put_dt(d.y, n0 + tid, d.y_dt, __builtin_nanf(""));
+        return;
+    }
+    const int64_t row_bytes = d.row_bytes;
+    const int cps = (int)(row_bytes / Cfg::CHB);  // chunks per slot
+    const int nchunks = S * cps;
+    const uint8_t* xsrc = (const uint8_t*)d.x;
+
+    uint32_t woff[WL_PER_WAVE];
+    bool wact[WL_PER_WAVE];
+#pragma unroll
+    for (int j = 0; j < WL_PER_WAVE; ++j) {
+        const int i = wave + W * j;
+        const int p = 64 * i + lane;
+        const int r = p / kRowPieces, q = p - r * kRowPieces;
+        int64_t nr = n0 + r;
+        if (nr >= n) nr = n - 1;
+        wact[j] = i < WLOADS && r < 16 && q < Cfg::CHB / 16;
+        woff[j] = (uint32_t)((nr - n0) * row_bytes) + 16u * (uint32_t)q;
+    }
+    int wave_loads = 0;
+#pragma unroll
+    for (int j = 0; j < WL_PER_WAVE; ++j) wave_loads += (wave + W * j < WLOADS) ? 1 : 0;
+    wave_loads += XL > wave ? (XL - wave + W - 1) / W : 0;
+    auto issue = [&](int chunk) {
+        uint8_t* dst = smem + (chunk % kNBuf) * BUF;
+        const int r = chunk / cps, lc = chunk - r * cps;
+        const uint8_t* src = expert_base(d.w, d.w_sh, slot_expert(d.ids, r, S, d.shexp, d.n_experts), d.n_experts,
+                                         d.expert_stride) +
+                             n0 * row_bytes + (int64_t)lc * Cfg::CHB;
+#pragma unroll
+        for (int j = 0; j < WL_PER_WAVE; ++j) {
+            const int i = wave + W * j;
+            if (i < WLOADS) {
+                const uint32_t dl = __builtin_amdgcn_readfirstlane(lds_addr(dst + 1024 * i));
+                if (wact[j]) dma16(src + woff[j], dl);
+            }
+        }
+        const int64_t xr = d.slotted ? r : 0;
+        const uint8_t* xs = xsrc + (xr * k + (int64_t)lc * (Cfg::CHQ * 32)) * ESZ;
+        for (int i = wave; i < XL; i += W)
+            dma16(xs + 1024 * i + 16 * lane, __builtin_amdgcn_readfirstlane(lds_addr(dst + kWBuf + 1024 * i)));
+    };
+
+    float acc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = 0.f;
+    const int rg = lane % kRG;
+    for (int c = 0; c < kNBuf - 1 && c < nchunks; ++c) issue(c);
+    for (int c = 0; c < nchunks; ++c) {
+        const int later = (nchunks - 1 < c + kNBuf - 2 ? nchunks - 1 : c + kNBuf - 2) - c;
+        wait_loads_le(later * wave_loads);
+        __syncthreads();
+        if (c + kNBuf - 1 < nchunks) issue(c + kNBuf - 1);
+        const uint8_t* B = smem + (c % kNBuf) * BUF;
+        const uint8_t* X = B + kWBuf;
+        const int r = c / cps;
+        const float sc = d.scores[r];
+        const int ex = PRE ? d.xexp[d.slotted ? r : 0] : 0;
+        for (int t = lane + 64 * wave; t < Cfg::TASKS; t += 64 * W) {
+            const int cq = t / kRG;
+            uint32_t p[R][16];
+            float A[R][2], Bv[R][2];
+            int64_t xa = 0, xb = 0;
+#pragma unroll
+            for (int j = 0; j < R; ++j)
+                Pair32<C>::template decode<true>(B + (rg + kRG * j) * (kRowPieces * 16), cq, p[j], A[j], Bv[j],
+                                                 xa, xb);
+            if constexpr (!PRE) {
+                uint32_t xw[16];
+                const u32x4* xp = (const u32x4*)(X + 2 * xa);
+                const u32x4* xq = (const u32x4*)(X + 2 * xb);
+                const u32x4 x0 = xp[0], x1 = xp[1], x2 = xq[0], x3 = xq[1];
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    xw[q] = x0[q], xw[4 + q] = x1[q], xw[8 + q] = x2[q], xw[12 + q] = x3[q];
+                float t0 = 0.f, t1 = 0.f;
+                if (Pair32<C>::has_b) {
+                    t0 = sum16(xw);
+                    t1 = sum16(xw + 8);
+                }
+#pragma unroll
+                for (int j = 0; j < R; ++j) {
+                    float sj = A[j][0] * dot16(p[j], xw);
+                    sj = __builtin_fmaf(A[j][1], dot16(p[j] + 8, xw + 8), sj);
+                    if (Pair32<C>::has_b) {
+                        sj = __builtin_fmaf(Bv[j][0], t0, sj);
+                        sj = __builtin_fmaf(Bv[j][1], t1, sj);
+                    }
+                    acc[j] = __builtin_fmaf(sc, sj, acc[j]);
+                }
+            } else {
+                const u32x4* ga = (const u32x4*)(X + 4 * xa);
+                const u32x4* gb = (const u32x4*)(X + 4 * xb);
+                uint32_t ha[8], la[8], hb[8], lb[8];
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    const u32x4 u0 = ga[q], u1 = ga[2 + q], u2 = gb[q], u3 = gb[2 + q];
+#pragma unroll
+                    for (int z = 0; z < 4; ++z)
+                        ha[4 * q + z] = u0[z], la[4 * q + z] = u1[z], hb[4 * q + z] = u2[z], lb[4 * q + z] = u3[z];
+                }
+                float t0 = 0.f, t1 = 0.f;
+                if (Pair32<C>::has_b) {
+                    t0 = sum16(ha) + sum16(la);
+                    t1 = sum16(hb) + sum16(lb);
+                }
+#pragma unroll
+                for (int j = 0; j < R; ++j) {
+                    float sj = A[j][0] * (dot16(p[j], ha) + dot16(p[j], la));
+                    sj = __builtin_fmaf(A[j][1], dot16(p[j] + 8, hb) + dot16(p[j] + 8, lb), sj);
+                    if (Pair32<C>::has_b) {
+                        sj = __builtin_fmaf(Bv[j][0], t0, sj);
+                        sj = __builtin_fmaf(Bv[j][1], t1, sj);
+                    }
+                    acc[j] += __builtin_ldexpf(sc * sj, ex);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+#pragma unroll
+        for (int o = kRG; o < 64; o <<= 1)
+            acc[j] += __shfl_xor(acc[j], o, 64);
+    }
+    if (lane < kRG) {
+#pragma unroll
+        for (int j = 0; j < R; ++j) red[wave * 16 + rg + kRG * j] = acc[j];
+    }
+    __syncthreads();
+    if (wave == 0 && lane < 16) {
+        float v = 0.f;
+        for (int ww = 0; ww < W; ++ww) v += red[ww * 16 + lane];
+        if (n0 + lane < n) put_dt(d.y, n0 + lane, d.y_dt, v);
+    }
+}
+
+// Launch shapes of the single-token forms (the down projection's own table
+// is the same: smaller chunks, which would let two of its workgroups share a
+// compute unit, measured slower).
+template <int C> struct RoutedPick { static constexpr int W = 8, CU = 4; };
+template <> struct RoutedPick<Q2_K> { static constexpr int W = 8, CU = 1; };
+template <> struct RoutedPick<Q6_K> { static constexpr int W = 8, CU = 1; };
+template <> struct RoutedPick<Q3_K> { static constexpr int W = 8, CU = 1; };
+template <int C> struct DownPick : RoutedPick<C> {};
+
+template <int C>
+static size_t glu1_lds(int64_t k) {
+    using Cfg = CmvCfg<C, RoutedPick<C>::W, RoutedPick<C>::CU, 2>;
+    return (size_t)2 * 2 * Cfg::WBUF + (size_t)k * 2 + (size_t)RoutedPick<C>::W * 2 * 16 * 4;
+}
+template <int C>
+static size_t down1_lds(int64_t k, int64_t S, int mode) {
+    using Cfg = CmvCfg<C, DownPick<C>::W, DownPick<C>::CU, 2>;
+    if (mode == 2) return (size_t)2 * Cfg::WBUF + (size_t)S * k * 4 + 16 * 4 + (size_t)DownPick<C>::W * 16 * 4;
+    return (size_t)2 * (Cfg::WBUF + Cfg::CHQ * 32 * (mode == 1 ? 4 : 2)) + (size_t)DownPick<C>::W * 16 * 4;
+}
+
+template <int C>
+static bool glu1_fits_c(int64_t k) {
+    return k > 0 && k % ((int64_t)RoutedPick<C>::CU * Unit<C>::W) == 0 && glu1_lds<C>(k) <= 160 * 1024;
+}
+template <int C>
+static bool down1_fits_c(int64_t k, int64_t S, int mode) {
+    // (splitting inside the kernel: at most 16 slots, whose row exponents take 16 words)
+    return k > 0 && S >= 1 && (mode != 2 || S <= 16) && k % ((int64_t)DownPick<C>::CU * Unit<C>::W) == 0 &&
+           down1_lds<C>(k, S, mode) <= 160 * 1024;
+}
+bool glu1_fits(int codec, int64_t k) {
+    switch (codec) {
+    case Q8_0: return glu1_fits_c<Q8_0>(k);
+    case Q4_0: return glu1_fits_c<Q4_0>(k);
+    case Q5_0: return glu1_fits_c<Q5_0>(k);
+    case Q5_1: return glu1_fits_c<Q5_1>(k);
+    case Q6_K: return glu1_fits_c<Q6_K>(k);
+    case Q2_K: return glu1_fits_c<Q2_K>(k);
+    case Q3_K: return glu1_fits_c<Q3_K>(k);
+    case Q5_K: return glu1_fits_c<Q5_K>(k);
+    default: return false;
+    }
+}
+bool down1_fits(int codec, int64_t k, int64_t S, int mode) {
+    switch (codec) {
+    case Q8_0: return down1_fits_c<Q8_0>(k, S, mode);
+    case Q4_0: return down1_fits_c<Q4_0>(k, S, mode);
+    case Q5_0: return down1_fits_c<Q5_0>(k, S, mode);
+    case Q5_1: return down1_fits_c<Q5_1>(k, S, mode);
+    case Q6_K: return down1_fits_c<Q6_K>(k, S, mode);
+    case Q2_K: return down1_fits_c<Q2_K>(k, S, mode);
+    case Q3_K: return down1_fits_c<Q3_K>(k, S, mode);
+    case Q5_K: return down1_fits_c<Q5_K>(k, S, mode);
+    default: return false;
+    }
+}
+
+template <int C>
+static hipError_t glu1_c(const SkinnyArgs& a, hipStream_t s) {
+    constexpr int W = RoutedPick<C>::W, CU = RoutedPick<C>::CU;
+    hipLaunchKernelGGL((cglu1_kernel<C, W, CU>), dim3((unsigned)((a.n + 15) / 16), (unsigned)a.top_k), dim3(64 * W),
+                       glu1_lds<C>(a.k), s, a);
+    return hipGetLastError();
+}
+template <int C>
+static hipError_t down1_c(const DownMixArgs& d, int mode, hipStream_t s) {
+    constexpr int W = DownPick<C>::W, CU = DownPick<C>::CU;
+    const dim3 grid((unsigned)((d.n + 15) / 16));
+    const size_t lds = down1_lds<C>(d.k, d.top_k, mode);
+    if (mode == 2) hipLaunchKernelGGL((cdown1_kernel<C, W, CU, 2, true>), grid, dim3(64 * W), lds, s, d);
+    else if (mode == 1) hipLaunchKernelGGL((cdown1s_kernel<C, W, CU, 2, true>), grid, dim3(64 * W), lds, s, d);
+    else hipLaunchKernelGGL((cdown1s_kernel<C, W, CU, 2, false>), grid, dim3(64 * W), lds, s, d);
+    return hipGetLastError();
+}
+
+hipError_t launch_glu1_gguf(int codec, const SkinnyArgs& a, hipStream_t s) {
+    switch (codec) {
+    case Q8_0: return glu1_c<Q8_0>(a, s);
+    case Q4_0: return glu1_c<Q4_0>(a, s);
+    case Q5_0: return glu1_c<Q5_0>(a, s);
+    case Q5_1: return glu1_c<Q5_1>(a, s);
+    case Q6_K: return glu1_c<Q6_K>(a, s);
+    case Q2_K: return glu1_c<Q2_K>(a, s);
+    case Q3_K: return glu1_c<Q3_K>(a, s);
+    default: return glu1_c<Q5_K>(a, s);
+    }
+}
+hipError_t launch_down1_gguf(int codec, const DownMixArgs& d, int mode, hipStream_t s) {
+    switch (codec) {
+    case Q8_0: return down1_c<Q8_0>(d, mode, s);
+    case Q4_0: return down1_c<Q4_0>(d, mode, s);
+    case Q5_0: return down1_c<Q5_0>(d, mode, s);
+    case Q5_1: return down1_c<Q5_1>(d, mode, s);
+    case Q6_K: return down1_c<Q6_K>(d, mode, s);
+    case Q2_K: return down1_c<Q2_K>(d, mode, s);
+    case Q3_K: return down1_c<Q3_K>(d, mode, s);
+    default: return down1_c<Q5_K>(d, mode, s);
+    }
+}
+
 }  // namespace kq

@@ -76,8 +76,22 @@ struct DownMixArgs {
     int y_dt;
     int shexp;              // the last of top_k slots is the shared expert w_sh
     const uint8_t* w_sh;
+    const int32_t* xexp;    // x split by split_rows_kernel: each row's exponent (else null)
 };
 hipError_t launch_down_mix1(const DownMixArgs& a, bool x_f32, hipStream_t s);
+// ... and for Q8_0 and the further GGUF codecs (cmv.hip): the down projection
+// with the mix (fp16 or fp32 activations) and the gate/up form (fp16), where
+// k is a whole number of the kernels' chunks and their buffers fit in LDS
+// (mode 0: fp16 x; 1: fp32 x split beforehand by launch_split_rows; 2: fp32
+// x split inside the kernel)
+bool down1_fits(int codec, int64_t k, int64_t S, int mode);
+hipError_t launch_down1_gguf(int codec, const DownMixArgs& d, int mode, hipStream_t s);
+// fp32 rows -> per row: the exponent e (largest magnitude x 2^-e in
+// [2^14, 2^15)) and every 16 values as 16 fp16 hi then 16 fp16 lo parts of
+// x 2^-e (64 bytes)
+hipError_t launch_split_rows(const float* x, int64_t rows, int64_t k, uint8_t* out, int32_t* xexp, hipStream_t s);
+bool glu1_fits(int codec, int64_t k);
+hipError_t launch_glu1_gguf(int codec, const SkinnyArgs& a, hipStream_t s);
 // Single-token gate/up with SiLU, expert ids read directly (moe_dec.hip).
 hipError_t launch_moe_glu1(const SkinnyArgs& a, hipStream_t s);
 

@@ -72,8 +72,14 @@
  * number of 1024 weights, 2048 for Q6_K and Q3_K) also run on the matrix
  * cores: Q4_0, Q5_0, Q5_1 and Q8_0 with each weight rounded once to fp16
  * (blocks whose weights could pass the fp16 range exactly), the K-quants with
- * exact fp16 integers and their scales applied in fp32.  Their other decode
- * and expert-routed products run on the vector units with exact weights.
+ * exact fp16 integers and their scales applied in fp32.  Their single-token
+ * MoE forms (kq_moe_glu with fp16 activations, kq_qmm_id with scores and
+ * fp16 or fp32 activations; k a whole number of 1024 weights, 2048 for Q6_K
+ * and Q3_K) stream each slot's expert rows through LDS with exact fp16
+ * integer pairs on the vector units; fp32 activation rows are split into
+ * fp16 hi + lo (22 significant bits), once into the workspace's slot buffer
+ * when n_slots * k <= n_slots * n.  Their other decode and expert-routed
+ * products run on the vector units with exact weights.
  *
  * All multi-byte fields are little-endian.  fp16 is IEEE binary16; bf16 is
  * the upper half of an IEEE binary32.

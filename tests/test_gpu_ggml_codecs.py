@@ -466,3 +466,199 @@ def test_qmm_id_mix_shexp(kq, kind, x_dt, T):
     torch.cuda.synchronize()
     ref, s = oracle.qmm_id_mix_shexp(kind, w, E, n, k, stride, wsh, x, x_dt, ids, T, top_k, scores)
     check_tol(to_f64(y), ref, s, TAU[x_dt], f"mix shexp {kind} {x_dt} T={T}")
+
+
+# ---------------------------------------------------------------- one token, routed, LDS stream
+# One token with k a whole number of the single-token kernels' chunks (2048
+# weights serve every codec): the gate/up form with the activation fused and
+# the down projection with the weighted sum over slots, expert ids read
+# directly, each slot's expert rows streamed through LDS.
+ROUTED = KINDS + ["q8_0"]
+
+
+@pytest.mark.parametrize("kind", ROUTED)
+@pytest.mark.parametrize("act", [0, 1])
+def test_moe_glu_one_token_lds(kq, kind, act):
+    E, n, top_k, k = 6, 72, 3, 2048
+    rng = synth.rng_for(5800 + act)
+    gate = synth.weight_blocks(kind, rng, E * n, k)
+    up = synth.weight_blocks(kind, rng, E * n, k)
+    stride = n * synth.row_bytes(kind, k)
+    ids = _ids(rng, 1, E, top_k)
+    x = synth.activations(rng, (1, k), "f16")
+    _say("moe_glu one token", kind, act)
+    h = empty((1, top_k, n), "f32")
+    ws = _moe_ws(kq, E, 1, top_k)
+    kq.kq_moe_glu(kind, to_dev(gate), to_dev(up), E, n, k, stride, to_dev(x, "f16"), to_dev(ids), 1, top_k,
+                  h, ws, act)
+    torch.cuda.synchronize()
+    ref = oracle.moe_glu(kind, gate, up, E, n, k, stride, x, "f16", ids, 1, top_k, act)
+    assert _glu_bound_ok(to_f64(h), ref, TAU["f16"], act, 0.0), f"moe_glu one token {kind} act={act}"
+
+
+@pytest.mark.parametrize("kind", ROUTED)
+def test_moe_glu_ex_one_token_lds_shexp_silu_limit(kq, kind):
+    E, n, top_k, k, limit = 6, 72, 3, 2048, 5.0
+    rng = synth.rng_for(5810)
+    gate = synth.weight_blocks(kind, rng, E * n, k)
+    up = synth.weight_blocks(kind, rng, E * n, k)
+    sg = synth.weight_blocks(kind, rng, n, k)
+    su = synth.weight_blocks(kind, rng, n, k)
+    stride = n * synth.row_bytes(kind, k)
+    ids = _ids(rng, 1, E, top_k)
+    x = synth.activations(rng, (1, k), "f16")
+    _say("moe_glu_ex one token", kind)
+    h = empty((1, top_k + 1, n), "f32")
+    ws = _moe_ws(kq, E + 1, 1, top_k + 1)
+    kq.kq_moe_glu_ex(kind, to_dev(gate), to_dev(up), E, n, k, stride, to_dev(x, "f16"), to_dev(ids), 1, top_k,
+                     h, ws, 2, limit, to_dev(sg), to_dev(su))
+    torch.cuda.synchronize()
+    ref = oracle.moe_glu_ex(kind, gate, up, E, n, k, stride, x, "f16", ids, 1, top_k, 2, limit, sg, su)
+    assert _glu_bound_ok(to_f64(h), ref, TAU["f16"], 2, limit), f"glu_ex one token {kind}"
+
+
+@pytest.mark.parametrize("kind", ["q4_0", "q6_k", "q8_0"])
+def test_moe_glu_one_token_lds_invalid_id(kq, kind):
+    """A slot whose id is out of range gets NaN rows; the other slots are
+    computed."""
+    E, n, top_k, k = 6, 40, 3, 2048
+    rng = synth.rng_for(5820)
+    gate = synth.weight_blocks(kind, rng, E * n, k)
+    up = synth.weight_blocks(kind, rng, E * n, k)
+    stride = n * synth.row_bytes(kind, k)
+    ids = np.array([[2, E + 3, 0]], np.uint32)
+    x = synth.activations(rng, (1, k), "f16")
+    _say("moe_glu one token invalid", kind)
+    h = empty((1, top_k, n), "f32")
+    ws = _moe_ws(kq, E, 1, top_k)
+    kq.kq_moe_glu(kind, to_dev(gate), to_dev(up), E, n, k, stride, to_dev(x, "f16"), to_dev(ids), 1, top_k,
+                  h, ws, 0)
+    torch.cuda.synchronize()
+    got = to_f64(h)
+    assert np.isnan(got[0, 1]).all()
+    ok_ids = np.array([[2, 0, 0]], np.uint32)
+    ref = oracle.moe_glu(kind, gate, up, E, n, k, stride, x, "f16", ok_ids, 1, top_k, 0)
+    for slot in (0, 2):
+        sub = {key: ref[key][:, slot:slot + 1] for key in ("g", "u", "sg", "su", "h")}
+        assert _glu_bound_ok(got[:, slot:slot + 1], sub, TAU["f16"], 0, 0.0), f"{kind} slot {slot}"
+
+
+@pytest.mark.parametrize("kind", ROUTED)
+@pytest.mark.parametrize("x_dt", ["f16", "f32"])
+@pytest.mark.parametrize("layout", [0, 1])
+@pytest.mark.parametrize("n", [72, 2100])
+def test_qmm_id_mixed_one_token_lds(kq, kind, x_dt, layout, n):
+    """fp32 rows are split into fp16 hi + lo in the workspace's slot buffer
+    when top_k * n * 4 bytes hold them (n = 2100), else by each workgroup
+    (n = 72)."""
+    E, top_k, k = 6, 3, 2048
+    rng = synth.rng_for(5830 + layout + n)
+    w = synth.weight_blocks(kind, rng, E * n, k)
+    stride = n * synth.row_bytes(kind, k)
+    ids = _ids(rng, 1, E, top_k)
+    scores = rng.uniform(0.05, 1.0, size=(1, top_k)).astype(np.float32)
+    x = synth.activations(rng, (1 if layout == 0 else top_k, k), x_dt)
+    _say("qmm_id mixed one token", kind, x_dt, layout)
+    y = empty((1, n), "f32")
+    ws = _moe_ws(kq, E, 1, top_k, n)
+    kq.kq_qmm_id(kind, to_dev(w), E, n, k, stride, to_dev(x, x_dt), layout, to_dev(ids), 1, top_k,
+                 to_dev(scores), y, ws)
+    torch.cuda.synchronize()
+    ref, s = oracle.qmm_id(kind, w, E, n, k, stride, x, x_dt, layout == 1, ids, 1, top_k, scores)
+    check_tol(to_f64(y), ref, s, TAU[x_dt], f"qmm_id mixed one token {kind} {x_dt} layout {layout}")
+
+
+@pytest.mark.parametrize("kind", ROUTED)
+@pytest.mark.parametrize("x_dt", ["f16", "f32"])
+def test_qmm_id_mix_shexp_one_token_lds(kq, kind, x_dt):
+    E, top_k, n, k = 6, 3, 72, 2048
+    rng = synth.rng_for(5840)
+    w = synth.weight_blocks(kind, rng, E * n, k)
+    wsh = synth.weight_blocks(kind, rng, n, k)
+    stride = n * synth.row_bytes(kind, k)
+    ids = _ids(rng, 1, E, top_k)
+    x = synth.activations(rng, (top_k + 1, k), x_dt)
+    scores = rng.uniform(0.05, 1.0, size=(1, top_k + 1)).astype(np.float32)
+    _say("mix shexp one token", kind, x_dt)
+    y = empty((1, n), "f32")
+    ws = _moe_ws(kq, E + 1, 1, top_k + 1, n)
+    kq.kq_qmm_id_mix_shexp(kind, to_dev(w), E, n, k, stride, to_dev(wsh), to_dev(x, x_dt), to_dev(ids), 1,
+                           top_k, to_dev(scores), y, ws)
+    torch.cuda.synchronize()
+    ref, s = oracle.qmm_id_mix_shexp(kind, w, E, n, k, stride, wsh, x, x_dt, ids, 1, top_k, scores)
+    check_tol(to_f64(y), ref, s, TAU[x_dt], f"mix shexp one token {kind} {x_dt}")
+
+
+@pytest.mark.parametrize("kind", ["q4_0", "q5_1", "q6_k", "q2_k", "q8_0"])
+@pytest.mark.parametrize("n", [48, 2100])
+def test_qmm_id_mixed_one_token_lds_fp32_range(kq, kind, n):
+    """fp32 slot rows at very different magnitudes (1e-30, 1e-3, 1e5, and a
+    row of zeros): each row is split into fp16 hi + lo at its own power of
+    two (in the workgroups, and beforehand into the workspace), within
+    tau = 1e-5."""
+    E, top_k, k = 6, 4, 2048
+    rng = synth.rng_for(5850)
+    w = synth.weight_blocks(kind, rng, E * n, k)
+    stride = n * synth.row_bytes(kind, k)
+    ids = _ids(rng, 1, E, top_k)
+    scores = rng.uniform(0.05, 1.0, size=(1, top_k)).astype(np.float32)
+    x = rng.standard_normal((top_k, k)).astype(np.float32)
+    x *= np.array([[1e-30], [1e-3], [1e5], [0.0]], np.float32)
+    _say("qmm_id one token fp32 range", kind)
+    y = empty((1, n), "f32")
+    ws = _moe_ws(kq, E, 1, top_k, n)
+    kq.kq_qmm_id(kind, to_dev(w), E, n, k, stride, to_dev(x), 1, to_dev(ids), 1, top_k, to_dev(scores), y, ws)
+    torch.cuda.synchronize()
+    ref, s = oracle.qmm_id(kind, w, E, n, k, stride, x, "f32", True, ids, 1, top_k, scores)
+    check_tol(to_f64(y), ref, s, TAU["f32"], f"qmm_id one token fp32 range {kind}")
+
+
+@pytest.mark.parametrize("kind", ["q4_0", "q6_k", "q8_0"])
+@pytest.mark.parametrize("x_dt", ["f16", "f32"])
+@pytest.mark.parametrize("n", [40, 2100])
+def test_qmm_id_mixed_one_token_lds_invalid_id(kq, kind, x_dt, n):
+    """An out-of-range id makes the token's whole output NaN."""
+    E, top_k, k = 6, 3, 2048
+    rng = synth.rng_for(5860)
+    w = synth.weight_blocks(kind, rng, E * n, k)
+    stride = n * synth.row_bytes(kind, k)
+    ids = np.array([[1, 4, E]], np.uint32)
+    scores = np.full((1, top_k), 0.5, np.float32)
+    x = synth.activations(rng, (top_k, k), x_dt)
+    _say("qmm_id one token invalid", kind, x_dt)
+    y = empty((1, n), "f32")
+    ws = _moe_ws(kq, E, 1, top_k, n)
+    kq.kq_qmm_id(kind, to_dev(w), E, n, k, stride, to_dev(x, x_dt), 1, to_dev(ids), 1, top_k, to_dev(scores),
+                 y, ws)
+    torch.cuda.synchronize()
+    assert np.isnan(to_f64(y)).all()
+
+
+@pytest.mark.parametrize("kind", ["q4_0", "q8_0", "q6_k", "q5_k"])
+def test_moe_one_token_c4_shapes(kq, kind):
+    """One token through a whole layer at the C4 matrix shapes (8 experts,
+    top-8, gate/up 2048x7168, down 7168x2048, fp32 h): every output against
+    the oracle."""
+    E, top_k, H, F = 8, 8, 7168, 2048
+    rng = synth.rng_for(5870)
+    gate = synth.weight_blocks(kind, rng, E * F, H)
+    up = synth.weight_blocks(kind, rng, E * F, H)
+    down = synth.weight_blocks(kind, rng, E * H, F)
+    gs, ds = F * synth.row_bytes(kind, H), H * synth.row_bytes(kind, F)
+    ids = _ids(rng, 1, E, top_k)
+    scores = rng.uniform(0.05, 1.0, size=(1, top_k)).astype(np.float32)
+    x = synth.activations(rng, (1, H), "f16")
+    _say("moe one token C4 shapes", kind)
+    h = empty((1, top_k, F), "f32")
+    ws = _moe_ws(kq, E, 1, top_k, H)
+    kq.kq_moe_glu(kind, to_dev(gate), to_dev(up), E, F, H, gs, to_dev(x, "f16"), to_dev(ids), 1, top_k, h, ws)
+    out = empty((1, H), "f32")
+    kq.kq_qmm_id(kind, to_dev(down), E, H, F, ds, h, 1, to_dev(ids), 1, top_k, to_dev(scores), out, ws)
+    torch.cuda.synchronize()
+    ref = oracle.moe_glu(kind, gate, up, E, F, H, gs, x, "f16", ids, 1, top_k, 0)
+    hg = to_f64(h)
+    assert _glu_bound_ok(hg, ref, TAU["f16"], 0, 0.0), f"C4 glu {kind}"
+    # the down projection against the oracle on the h the GPU produced
+    hx = hg.astype(np.float32).reshape(top_k, F)
+    yref, s = oracle.qmm_id(kind, down, E, H, F, ds, hx, "f32", True, ids, 1, top_k, scores)
+    check_tol(to_f64(out), yref, s, TAU["f32"], f"C4 down {kind}")
