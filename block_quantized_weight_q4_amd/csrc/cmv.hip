@@ -34,33 +34,45 @@ template <> struct Unit<Q6_K> { static constexpr int BYTES = 1680, W = 2048; }; 
 template <> struct Unit<Q2_K> { static constexpr int BYTES = 336, W = 1024; };  // 4 super-blocks
 template <> struct Unit<Q3_K> { static constexpr int BYTES = 880, W = 2048; };  // 8 super-blocks
 template <> struct Unit<Q5_K> { static constexpr int BYTES = 176, W = 256; };   // 1 super-block
+// With 4-byte copies (PB = 4) a unit need only be a whole number of dwords:
+// Q6_K and Q3_K then stream rows of any whole number of 2 super-blocks.
+template <int C, int PB> struct UnitP : Unit<C> {};
+template <> struct UnitP<Q6_K, 4> { static constexpr int BYTES = 420, W = 512; };
+template <> struct UnitP<Q3_K, 4> { static constexpr int BYTES = 220, W = 512; };
+template <int PB>
+__device__ __forceinline__ void dma_piece(const void* src, uint32_t lds) {
+    if constexpr (PB == 16) dma16(src, lds);
+    else dma4(src, lds);
+}
 
-// W waves; CU units per chunk; R rows per lane task
-template <int C, int W_, int CU_, int R_>
+// W waves; CU units per chunk; R rows per lane task; PB bytes per copied
+// piece (16: global_load_lds_dwordx4, 4: global_load_lds_dword)
+template <int C, int W_, int CU_, int R_, int PB_ = 16>
 struct CmvCfg {
-    static constexpr int W = W_, CU = CU_, R = R_;
-    static constexpr int CHB = CU * Unit<C>::BYTES;      // chunk bytes of one row
-    static constexpr int CHQ = CU * Unit<C>::W / 32;     // 32-weight chunks of one row per chunk
-    // 16-byte pieces per LDS row: the chunk, one piece of padding (read past
-    // by the realigning dword reads), and one more if that count is even, so
-    // that the 16 rows of a workgroup start on 16 different bank groups
-    static constexpr int ROW_PIECES = (CHB / 16 + 1) | 1;
-    static constexpr int WBUF = 16 * ROW_PIECES * 16;    // bytes of one chunk buffer
+    static constexpr int W = W_, CU = CU_, R = R_, PB = PB_;
+    static constexpr int CHB = CU * UnitP<C, PB>::BYTES;      // chunk bytes of one row
+    static constexpr int CHQ = CU * UnitP<C, PB>::W / 32;     // 32-weight chunks of one row per chunk
+    // pieces per LDS row: the chunk, one piece of padding (read past by the
+    // realigning dword reads), and one more if that count is even, so that
+    // the 16 rows of a workgroup start on different bank groups
+    static constexpr int ROW_PIECES = (CHB / PB + 1) | 1;
+    static constexpr int ROW_BYTES = ROW_PIECES * PB;
+    static constexpr int WBUF = 16 * ROW_BYTES;               // bytes of one chunk buffer (16 rows)
     static constexpr int NBUF = 2;
-    static constexpr int RG = 16 / R;                    // row groups
-    static constexpr int TASKS = RG * CHQ;               // lane tasks per chunk
-    static_assert(Unit<C>::BYTES % 16 == 0, "units are whole 16-byte pieces");
+    static constexpr int RG = 16 / R;                         // row groups
+    static constexpr int TASKS = RG * CHQ;                    // lane tasks per chunk
+    static_assert(UnitP<C, PB>::BYTES % PB == 0, "units are whole pieces");
     static_assert(16 % R == 0 && 64 % RG == 0, "row groups tile a wave");
     static size_t lds_bytes(int64_t k) { return (size_t)NBUF * WBUF + (size_t)k * 2 + (size_t)W * 16 * 4; }
 };
 
 }  // namespace
 
-template <int C, int W, int CU, int R>
+template <int C, int W, int CU, int R, int PB = 16>
 __global__ __launch_bounds__(64 * W) void cmv_kernel(const uint8_t* __restrict__ w, int64_t n, int64_t k,
                                                      const uint16_t* __restrict__ x, void* __restrict__ y,
                                                      int y_dt) {
-    using Cfg = CmvCfg<C, W, CU, R>;
+    using Cfg = CmvCfg<C, W, CU, R, PB>;
     constexpr int kRowPieces = Cfg::ROW_PIECES, kWBuf = Cfg::WBUF, kNBuf = Cfg::NBUF, kRG = Cfg::RG;
     constexpr int NPIECE = 16 * kRowPieces;
     constexpr int WLOADS = (NPIECE + 63) / 64;
@@ -71,7 +83,7 @@ __global__ __launch_bounds__(64 * W) void cmv_kernel(const uint8_t* __restrict__
     float* red = (float*)(smem + kNBuf * kWBuf + (size_t)k * 2);    // [W][16]
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t n0 = (int64_t)blockIdx.x * 16;
-    const int64_t row_bytes = k / Unit<C>::W * Unit<C>::BYTES;
+    const int64_t row_bytes = k / UnitP<C, PB>::W * UnitP<C, PB>::BYTES;  // (k is a whole number of units)
     const int nchunks = (int)(row_bytes / Cfg::CHB);                // whole chunks (k is a multiple of the chunk)
 
     // ---- the activation row into LDS (16-byte copies; k * 2 is a multiple of 16)
@@ -94,8 +106,8 @@ __global__ __launch_bounds__(64 * W) void cmv_kernel(const uint8_t* __restrict__
         const int r = p / kRowPieces, q = p - r * kRowPieces;
         int64_t nr = n0 + r;
         if (nr >= n) nr = n - 1;
-        wact[j] = i < WLOADS && r < 16 && q < Cfg::CHB / 16;
-        woff[j] = (uint32_t)((nr - n0) * row_bytes) + 16u * (uint32_t)q;
+        wact[j] = i < WLOADS && r < 16 && q < Cfg::CHB / PB;
+        woff[j] = (uint32_t)((nr - n0) * row_bytes) + (uint32_t)PB * (uint32_t)q;
     }
     int wave_loads = 0;
 #pragma unroll
@@ -110,8 +122,8 @@ __global__ __launch_bounds__(64 * W) void cmv_kernel(const uint8_t* __restrict__
                 // padding pieces and pieces past the 16 rows are not copied
                 // (every load instruction still has live lanes: each group of
                 // 64 pieces holds pieces of a row)
-                const uint32_t dl = __builtin_amdgcn_readfirstlane(lds_addr(dst + 1024 * i));
-                if (wact[j]) dma16(src + woff[j], dl);
+                const uint32_t dl = __builtin_amdgcn_readfirstlane(lds_addr(dst + 64 * PB * i));
+                if (wact[j]) dma_piece<PB>(src + woff[j], dl);
             }
         }
     };
@@ -136,7 +148,7 @@ __global__ __launch_bounds__(64 * W) void cmv_kernel(const uint8_t* __restrict__
             int64_t xa = 0, xb = 0;
 #pragma unroll
             for (int j = 0; j < R; ++j)
-                Pair32<C>::template decode<true>(B + (rg + kRG * j) * (kRowPieces * 16), cq, p[j], A[j], Bv[j],
+                Pair32<C>::template decode<true>(B + (rg + kRG * j) * Cfg::ROW_BYTES, cq, p[j], A[j], Bv[j],
                                                  xa, xb);
             uint32_t xw[16];
             const u32x4* xp = (const u32x4*)(xs + kbase + xa);
@@ -497,9 +509,20 @@ static bool fits_cfg(int64_t k) {
     using Cfg = typename CmvPick<C, LONG>::Cfg;
     return k % (Cfg::CHQ * 32) == 0 && Cfg::lds_bytes(k) <= 160 * 1024;
 }
+// Q6_K and Q3_K rows that are no whole number of their 2048-weight units
+// stream by 4-byte copies in chunks of 1024 weights (or 512)
+template <int C> constexpr bool kDword = C == Q6_K || C == Q3_K;
+template <int C, int CU4> using CmvCfg4 = CmvCfg<C, 8, CU4, 1, 4>;
+
+template <int C>
+static bool fits16_c(int64_t k) {
+    return k >= kLongRow ? fits_cfg<C, true>(k) : fits_cfg<C, false>(k);
+}
 template <int C>
 static bool fits_c(int64_t k) {
-    return k >= kLongRow ? fits_cfg<C, true>(k) : fits_cfg<C, false>(k);
+    if (fits16_c<C>(k)) return true;
+    if constexpr (kDword<C>) return k > 0 && k % 512 == 0 && CmvCfg4<C, 1>::lds_bytes(k) <= 160 * 1024;
+    return false;
 }
 
 bool cmv_fits(int codec, int64_t k) {
@@ -525,9 +548,22 @@ static hipError_t launch_cfg(const uint8_t* w, int64_t n, int64_t k, const uint1
                        x, y, y_dt);
     return hipGetLastError();
 }
+template <int C, int CU4>
+static hipError_t launch_cfg4(const uint8_t* w, int64_t n, int64_t k, const uint16_t* x, void* y, int y_dt,
+                              hipStream_t s) {
+    using Cfg = CmvCfg4<C, CU4>;
+    constexpr auto kern = cmv_kernel<C, Cfg::W, Cfg::CU, Cfg::R, 4>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)((n + 15) / 16)), dim3(64 * Cfg::W), Cfg::lds_bytes(k), s, w, n, k,
+                       x, y, y_dt);
+    return hipGetLastError();
+}
 template <int C>
 static hipError_t launch_c(const uint8_t* w, int64_t n, int64_t k, const uint16_t* x, void* y, int y_dt,
                            hipStream_t s) {
+    if constexpr (kDword<C>) {
+        if (!fits16_c<C>(k))
+            return k % 1024 == 0 ? launch_cfg4<C, 2>(w, n, k, x, y, y_dt, s) : launch_cfg4<C, 1>(w, n, k, x, y, y_dt, s);
+    }
     return k >= kLongRow ? launch_cfg<C, true>(w, n, k, x, y, y_dt, s) : launch_cfg<C, false>(w, n, k, x, y, y_dt, s);
 }
 
@@ -591,9 +627,9 @@ __device__ __forceinline__ int split_exponent(float mx) {
     return ex;
 }
 
-template <int C, int W, int CU>
+template <int C, int W, int CU, int PB = 16>
 __global__ __launch_bounds__(64 * W) void cglu1_kernel(SkinnyArgs a) {
-    using Cfg = CmvCfg<C, W, CU, 2>;
+    using Cfg = CmvCfg<C, W, CU, 2, PB>;
     constexpr int kRowPieces = Cfg::ROW_PIECES, kNBuf = 2, kWBuf = 2 * Cfg::WBUF;  // 32 LDS rows
     constexpr int NPIECE = 32 * kRowPieces, WLOADS = (NPIECE + 63) / 64, WL_PER_WAVE = (WLOADS + W - 1) / W;
     constexpr int TASKS = 16 * Cfg::CHQ;
@@ -632,9 +668,9 @@ __global__ __launch_bounds__(64 * W) void cglu1_kernel(SkinnyArgs a) {
         const int rr = r & 15;
         int64_t nr = n0 + rr;
         if (nr >= n) nr = n - 1;
-        wact[j] = i < WLOADS && r < 32 && q < Cfg::CHB / 16;
+        wact[j] = i < WLOADS && r < 32 && q < Cfg::CHB / PB;
         wup[j] = r >= 16;
-        woff[j] = (uint32_t)((nr - n0) * row_bytes) + 16u * (uint32_t)q;
+        woff[j] = (uint32_t)((nr - n0) * row_bytes) + (uint32_t)PB * (uint32_t)q;
     }
     int wave_loads = 0;
 #pragma unroll
@@ -646,8 +682,8 @@ __global__ __launch_bounds__(64 * W) void cglu1_kernel(SkinnyArgs a) {
         for (int j = 0; j < WL_PER_WAVE; ++j) {
             const int i = wave + W * j;
             if (i < WLOADS) {
-                const uint32_t dl = __builtin_amdgcn_readfirstlane(lds_addr(dst + 1024 * i));
-                if (wact[j]) dma16((wup[j] ? wu : wg) + cb + woff[j], dl);
+                const uint32_t dl = __builtin_amdgcn_readfirstlane(lds_addr(dst + 64 * PB * i));
+                if (wact[j]) dma_piece<PB>((wup[j] ? wu : wg) + cb + woff[j], dl);
             }
         }
     };
@@ -669,7 +705,7 @@ __global__ __launch_bounds__(64 * W) void cglu1_kernel(SkinnyArgs a) {
             int64_t xa = 0, xb = 0;
 #pragma unroll
             for (int j = 0; j < 2; ++j)
-                Pair32<C>::template decode<true>(B + (rg + 16 * j) * (kRowPieces * 16), cq, pw[j], A[j], Bv[j],
+                Pair32<C>::template decode<true>(B + (rg + 16 * j) * Cfg::ROW_BYTES, cq, pw[j], A[j], Bv[j],
                                                  xa, xb);
             uint32_t xw[16];
             const u32x4* xp = (const u32x4*)(xs + kbase + xa);
@@ -958,9 +994,9 @@ hipError_t launch_split_rows(const float* x, int64_t rows, int64_t k, uint8_t* o
 // weights (no staging of all slots up front): fp16 activations (PRE false)
 // or fp32 rows split by split_rows_kernel (PRE true: 64-byte groups of 16 hi
 // and 16 lo halves, the row's exponent in d.xexp).
-template <int C, int W, int CU, int R, bool PRE>
+template <int C, int W, int CU, int R, bool PRE, int PB = 16>
 __global__ __launch_bounds__(64 * W) void cdown1s_kernel(DownMixArgs d) {
-    using Cfg = CmvCfg<C, W, CU, R>;
+    using Cfg = CmvCfg<C, W, CU, R, PB>;
     constexpr int kRowPieces = Cfg::ROW_PIECES, kWBuf = Cfg::WBUF, kNBuf = 2, kRG = Cfg::RG;
     constexpr int NPIECE = 16 * kRowPieces, WLOADS = (NPIECE + 63) / 64, WL_PER_WAVE = (WLOADS + W - 1) / W;
     constexpr int ESZ = PRE ? 4 : 2;                  // staged bytes per activation
@@ -996,8 +1032,8 @@ __global__ __launch_bounds__(64 * W) void cdown1s_kernel(DownMixArgs d) {
         const int r = p / kRowPieces, q = p - r * kRowPieces;
         int64_t nr = n0 + r;
         if (nr >= n) nr = n - 1;
-        wact[j] = i < WLOADS && r < 16 && q < Cfg::CHB / 16;
-        woff[j] = (uint32_t)((nr - n0) * row_bytes) + 16u * (uint32_t)q;
+        wact[j] = i < WLOADS && r < 16 && q < Cfg::CHB / PB;
+        woff[j] = (uint32_t)((nr - n0) * row_bytes) + (uint32_t)PB * (uint32_t)q;
     }
     int wave_loads = 0;
 #pragma unroll
@@ -1013,8 +1049,8 @@ __global__ __launch_bounds__(64 * W) void cdown1s_kernel(DownMixArgs d) {
         for (int j = 0; j < WL_PER_WAVE; ++j) {
             const int i = wave + W * j;
             if (i < WLOADS) {
-                const uint32_t dl = __builtin_amdgcn_readfirstlane(lds_addr(dst + 1024 * i));
-                if (wact[j]) dma16(src + woff[j], dl);
+                const uint32_t dl = __builtin_amdgcn_readfirstlane(lds_addr(dst + 64 * PB * i));
+                if (wact[j]) dma_piece<PB>(src + woff[j], dl);
             }
         }
         const int64_t xr = d.slotted ? r : 0;
@@ -1045,7 +1081,7 @@ __global__ __launch_bounds__(64 * W) void cdown1s_kernel(DownMixArgs d) {
             int64_t xa = 0, xb = 0;
 #pragma unroll
             for (int j = 0; j < R; ++j)
-                Pair32<C>::template decode<true>(B + (rg + kRG * j) * (kRowPieces * 16), cq, p[j], A[j], Bv[j],
+                Pair32<C>::template decode<true>(B + (rg + kRG * j) * Cfg::ROW_BYTES, cq, p[j], A[j], Bv[j],
                                                  xa, xb);
             if constexpr (!PRE) {
                 uint32_t xw[16];
@@ -1126,28 +1162,49 @@ template <> struct RoutedPick<Q6_K> { static constexpr int W = 8, CU = 1; };
 template <> struct RoutedPick<Q3_K> { static constexpr int W = 8, CU = 1; };
 template <int C> struct DownPick : RoutedPick<C> {};
 
-template <int C>
+// (Q6_K and Q3_K rows that are no whole number of 2048 weights: 4-byte
+// copies, chunks of 1024 weights or 512, as in the one-row GEMV)
+template <int C, int CU, int PB>
 static size_t glu1_lds(int64_t k) {
-    using Cfg = CmvCfg<C, RoutedPick<C>::W, RoutedPick<C>::CU, 2>;
+    using Cfg = CmvCfg<C, RoutedPick<C>::W, CU, 2, PB>;
     return (size_t)2 * 2 * Cfg::WBUF + (size_t)k * 2 + (size_t)RoutedPick<C>::W * 2 * 16 * 4;
 }
-template <int C>
+template <int C, int CU, int PB>
 static size_t down1_lds(int64_t k, int64_t S, int mode) {
-    using Cfg = CmvCfg<C, DownPick<C>::W, DownPick<C>::CU, 2>;
+    using Cfg = CmvCfg<C, DownPick<C>::W, CU, 2, PB>;
     if (mode == 2) return (size_t)2 * Cfg::WBUF + (size_t)S * k * 4 + 16 * 4 + (size_t)DownPick<C>::W * 16 * 4;
     return (size_t)2 * (Cfg::WBUF + Cfg::CHQ * 32 * (mode == 1 ? 4 : 2)) + (size_t)DownPick<C>::W * 16 * 4;
 }
-
+// the routed forms' variant for k: 16 (the table's shape), 42 or 41 (4-byte
+// copies, chunks of 2 or 1 units), 0 none
 template <int C>
-static bool glu1_fits_c(int64_t k) {
-    return k > 0 && k % ((int64_t)RoutedPick<C>::CU * Unit<C>::W) == 0 && glu1_lds<C>(k) <= 160 * 1024;
+static int glu1_variant(int64_t k) {
+    if (k <= 0) return 0;
+    if (k % ((int64_t)RoutedPick<C>::CU * Unit<C>::W) == 0 && glu1_lds<C, RoutedPick<C>::CU, 16>(k) <= 160 * 1024)
+        return 16;
+    if constexpr (kDword<C>) {
+        if (k % 1024 == 0 && glu1_lds<C, 2, 4>(k) <= 160 * 1024) return 42;
+        if (k % 512 == 0 && glu1_lds<C, 1, 4>(k) <= 160 * 1024) return 41;
+    }
+    return 0;
 }
 template <int C>
-static bool down1_fits_c(int64_t k, int64_t S, int mode) {
-    // (splitting inside the kernel: at most 16 slots, whose row exponents take 16 words)
-    return k > 0 && S >= 1 && (mode != 2 || S <= 16) && k % ((int64_t)DownPick<C>::CU * Unit<C>::W) == 0 &&
-           down1_lds<C>(k, S, mode) <= 160 * 1024;
+static int down1_variant(int64_t k, int64_t S, int mode) {
+    // (splitting inside the kernel: at most 16 slots, whose row exponents
+    // take 16 words; that form has 16-byte copies only)
+    if (k <= 0 || S < 1 || (mode == 2 && S > 16)) return 0;
+    if (k % ((int64_t)DownPick<C>::CU * Unit<C>::W) == 0 && down1_lds<C, DownPick<C>::CU, 16>(k, S, mode) <= 160 * 1024)
+        return 16;
+    if constexpr (kDword<C>) {
+        if (mode != 2 && k % 1024 == 0) return 42;
+        if (mode != 2 && k % 512 == 0) return 41;
+    }
+    return 0;
 }
+template <int C>
+static bool glu1_fits_c(int64_t k) { return glu1_variant<C>(k) != 0; }
+template <int C>
+static bool down1_fits_c(int64_t k, int64_t S, int mode) { return down1_variant<C>(k, S, mode) != 0; }
 bool glu1_fits(int codec, int64_t k) {
     switch (codec) {
     case Q8_0: return glu1_fits_c<Q8_0>(k);
@@ -1175,22 +1232,45 @@ bool down1_fits(int codec, int64_t k, int64_t S, int mode) {
     }
 }
 
+template <int C, int CU, int PB>
+static hipError_t glu1_go(const SkinnyArgs& a, hipStream_t s) {
+    constexpr int W = RoutedPick<C>::W;
+    hipLaunchKernelGGL((cglu1_kernel<C, W, CU, PB>), dim3((unsigned)((a.n + 15) / 16), (unsigned)a.top_k),
+                       dim3(64 * W), (glu1_lds<C, CU, PB>(a.k)), s, a);
+    return hipGetLastError();
+}
 template <int C>
 static hipError_t glu1_c(const SkinnyArgs& a, hipStream_t s) {
-    constexpr int W = RoutedPick<C>::W, CU = RoutedPick<C>::CU;
-    hipLaunchKernelGGL((cglu1_kernel<C, W, CU>), dim3((unsigned)((a.n + 15) / 16), (unsigned)a.top_k), dim3(64 * W),
-                       glu1_lds<C>(a.k), s, a);
+    const int v = glu1_variant<C>(a.k);
+    if constexpr (kDword<C>) {
+        if (v == 42) return glu1_go<C, 2, 4>(a, s);
+        if (v == 41) return glu1_go<C, 1, 4>(a, s);
+    }
+    return glu1_go<C, RoutedPick<C>::CU, 16>(a, s);
+}
+template <int C, int CU, int PB>
+static hipError_t down1_go(const DownMixArgs& d, int mode, hipStream_t s) {
+    constexpr int W = DownPick<C>::W;
+    const dim3 grid((unsigned)((d.n + 15) / 16));
+    const size_t lds = down1_lds<C, CU, PB>(d.k, d.top_k, mode);
+    if constexpr (PB == 16) {
+        if (mode == 2) {
+            hipLaunchKernelGGL((cdown1_kernel<C, W, CU, 2, true>), grid, dim3(64 * W), lds, s, d);
+            return hipGetLastError();
+        }
+    }
+    if (mode == 1) hipLaunchKernelGGL((cdown1s_kernel<C, W, CU, 2, true, PB>), grid, dim3(64 * W), lds, s, d);
+    else hipLaunchKernelGGL((cdown1s_kernel<C, W, CU, 2, false, PB>), grid, dim3(64 * W), lds, s, d);
     return hipGetLastError();
 }
 template <int C>
 static hipError_t down1_c(const DownMixArgs& d, int mode, hipStream_t s) {
-    constexpr int W = DownPick<C>::W, CU = DownPick<C>::CU;
-    const dim3 grid((unsigned)((d.n + 15) / 16));
-    const size_t lds = down1_lds<C>(d.k, d.top_k, mode);
-    if (mode == 2) hipLaunchKernelGGL((cdown1_kernel<C, W, CU, 2, true>), grid, dim3(64 * W), lds, s, d);
-    else if (mode == 1) hipLaunchKernelGGL((cdown1s_kernel<C, W, CU, 2, true>), grid, dim3(64 * W), lds, s, d);
-    else hipLaunchKernelGGL((cdown1s_kernel<C, W, CU, 2, false>), grid, dim3(64 * W), lds, s, d);
-    return hipGetLastError();
+    const int v = down1_variant<C>(d.k, d.top_k, mode);
+    if constexpr (kDword<C>) {
+        if (v == 42) return down1_go<C, 2, 4>(d, mode, s);
+        if (v == 41) return down1_go<C, 1, 4>(d, mode, s);
+    }
+    return down1_go<C, DownPick<C>::CU, 16>(d, mode, s);
 }
 
 hipError_t launch_glu1_gguf(int codec, const SkinnyArgs& a, hipStream_t s) {

@@ -19,6 +19,13 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
                  : "v"(src), "s"(lds)
                  : "memory", "m0");
 }
+// The same with 4 bytes per lane: lane l's dword lands at lds + 4*l.
+__device__ __forceinline__ void dma4(const void* src, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
+                 :
+                 : "v"(src), "s"(lds)
+                 : "memory", "m0");
+}
 __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
     return (uint32_t)(uintptr_t)(const lds_u8*)p;
 }

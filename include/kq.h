@@ -74,7 +74,7 @@
  * (blocks whose weights could pass the fp16 range exactly), the K-quants with
  * exact fp16 integers and their scales applied in fp32.  Their single-token
  * MoE forms (kq_moe_glu with fp16 activations, kq_qmm_id with scores and
- * fp16 or fp32 activations; k a whole number of 1024 weights, 2048 for Q6_K
+ * fp16 or fp32 activations; k a whole number of 1024 weights, 512 for Q6_K
  * and Q3_K) stream each slot's expert rows through LDS with exact fp16
  * integer pairs on the vector units; fp32 activation rows are split into
  * fp16 hi + lo (22 significant bits), once into the workspace's slot buffer

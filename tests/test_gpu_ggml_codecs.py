@@ -662,3 +662,64 @@ def test_moe_one_token_c4_shapes(kq, kind):
     hx = hg.astype(np.float32).reshape(top_k, F)
     yref, s = oracle.qmm_id(kind, down, E, H, F, ds, hx, "f32", True, ids, 1, top_k, scores)
     check_tol(to_f64(out), yref, s, TAU["f32"], f"C4 down {kind}")
+
+
+# ---------------------------------------------------------------- Q6_K / Q3_K by 4-byte copies
+# Rows that are no whole number of the 16-byte-copy unit (8 super-blocks)
+# stream by 4-byte copies in chunks of 1024 weights (k a multiple of 1024) or
+# 512: the one-row GEMV and the single-token MoE forms.
+@pytest.mark.parametrize("kind", ["q6_k", "q3_k"])
+@pytest.mark.parametrize("n,k", [(16, 512), (45, 1536), (300, 5120), (33, 7168), (70, 4608)])
+def test_qmv_one_row_dword_stream(kq, kind, n, k):
+    rng = synth.rng_for(5900 + n)
+    w = synth.weight_blocks(kind, rng, n, k)
+    x = synth.activations(rng, (1, k), "f16")
+    ref, s = oracle.qmm(kind, w, n, k, x, "f16", 1)
+    for y_dt in ("f32", "f16", "bf16"):
+        _say("qmv one row dword", kind, n, k, y_dt)
+        got = _run(kq, "kq_qmv", kind, w, n, k, x, "f16", 1, y_dt)
+        check_tol(got, ref, s, TAU["f16"], f"qmv one row dword {kind} {n}x{k} y={y_dt}",
+                  out_dt=y_dt if y_dt != "f32" else None)
+    assert np.array_equal(got, _run(kq, "kq_qmm_noalloc", kind, w, n, k, x, "f16", 1, "bf16"))
+
+
+@pytest.mark.parametrize("kind", ["q6_k", "q3_k"])
+@pytest.mark.parametrize("k", [7168, 2560])
+def test_moe_glu_one_token_dword_stream(kq, kind, k):
+    E, n, top_k = 6, 72, 3
+    rng = synth.rng_for(5910 + k)
+    gate = synth.weight_blocks(kind, rng, E * n, k)
+    up = synth.weight_blocks(kind, rng, E * n, k)
+    stride = n * synth.row_bytes(kind, k)
+    ids = _ids(rng, 1, E, top_k)
+    x = synth.activations(rng, (1, k), "f16")
+    _say("moe_glu one token dword", kind, k)
+    h = empty((1, top_k, n), "f32")
+    ws = _moe_ws(kq, E, 1, top_k)
+    kq.kq_moe_glu(kind, to_dev(gate), to_dev(up), E, n, k, stride, to_dev(x, "f16"), to_dev(ids), 1, top_k,
+                  h, ws, 0)
+    torch.cuda.synchronize()
+    ref = oracle.moe_glu(kind, gate, up, E, n, k, stride, x, "f16", ids, 1, top_k, 0)
+    assert _glu_bound_ok(to_f64(h), ref, TAU["f16"], 0, 0.0), f"moe_glu one token dword {kind} k={k}"
+
+
+@pytest.mark.parametrize("kind", ["q6_k", "q3_k"])
+@pytest.mark.parametrize("x_dt", ["f16", "f32"])
+@pytest.mark.parametrize("k", [3072, 1536])
+def test_qmm_id_mixed_one_token_dword_stream(kq, kind, x_dt, k):
+    """n = 3100 >= k: fp32 rows are split beforehand into the workspace."""
+    E, top_k, n = 6, 3, 3100
+    rng = synth.rng_for(5920 + k)
+    w = synth.weight_blocks(kind, rng, E * n, k)
+    stride = n * synth.row_bytes(kind, k)
+    ids = _ids(rng, 1, E, top_k)
+    scores = rng.uniform(0.05, 1.0, size=(1, top_k)).astype(np.float32)
+    x = synth.activations(rng, (top_k, k), x_dt)
+    _say("qmm_id mixed one token dword", kind, x_dt, k)
+    y = empty((1, n), "f32")
+    ws = _moe_ws(kq, E, 1, top_k, n)
+    kq.kq_qmm_id(kind, to_dev(w), E, n, k, stride, to_dev(x, x_dt), 1, to_dev(ids), 1, top_k, to_dev(scores),
+                 y, ws)
+    torch.cuda.synchronize()
+    ref, s = oracle.qmm_id(kind, w, E, n, k, stride, x, x_dt, True, ids, 1, top_k, scores)
+    check_tol(to_f64(y), ref, s, TAU[x_dt], f"qmm_id mixed one token dword {kind} {x_dt} k={k}")
