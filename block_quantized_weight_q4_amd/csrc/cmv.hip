@@ -39,6 +39,7 @@ template <> struct Unit<Q5_K> { static constexpr int BYTES = 176, W = 256; };   
 template <int C, int PB> struct UnitP : Unit<C> {};
 template <> struct UnitP<Q6_K, 4> { static constexpr int BYTES = 420, W = 512; };
 template <> struct UnitP<Q3_K, 4> { static constexpr int BYTES = 220, W = 512; };
+template <> struct UnitP<Q2_K, 4> { static constexpr int BYTES = 168, W = 512; };
 template <int PB>
 __device__ __forceinline__ void dma_piece(const void* src, uint32_t lds) {
     if constexpr (PB == 16) dma16(src, lds);
@@ -1295,6 +1296,308 @@ hipError_t launch_down1_gguf(int codec, const DownMixArgs& d, int mode, hipStrea
     case Q2_K: return down1_c<Q2_K>(d, mode, s);
     case Q3_K: return down1_c<Q3_K>(d, mode, s);
     default: return down1_c<Q5_K>(d, mode, s);
+    }
+}
+
+// ---------------------------------------------------------------- routed tiles
+// The expert-routed products over the schedule's tiles (one expert, up to 32
+// rows gathered through the permutation): kq_qmm_id and the gate/up form of
+// kq_moe_glu, for Q8_0 and the further GGUF codecs, as the batched decode
+// kernel above computes them.  A workgroup of eight waves takes one tile and
+// NT tiles of 16 weight rows (16 gate and 16 up rows each for the GLU), as
+// many as LDS holds: the tile's activation rows, staged once per chunk of K
+// beside the weights, feed all of them.  8 / NT waves share a row tile and
+// split each chunk's 32-weight groups, their sums combined through LDS.  K is walked in chunks of 512 weights (256 for fp32
+// activations where a codec's copy unit allows; 16-byte copies, or 4-byte
+// ones for Q2_K, Q6_K and Q3_K).  Each 32-weight chunk of a weight row is
+// decoded once and feeds the two 16-row MFMA groups of the tile: folded into
+// fp16 weights for the 32-weight blocks with fp16 activations (exact form for
+// a wave holding a block that could overflow fp16), exact integers with the
+// scales applied in fp32 otherwise (the K-quants, and fp32 activations, held
+// to tau = 1e-5).  fp32 activations: each row scaled by its power of two
+// (row_exp_kernel) and split per chunk into fp16 hi + lo halves, both through
+// the matrix cores, the result scaled back.
+template <int C> constexpr int kCrmPB = (C == Q6_K || C == Q3_K || C == Q2_K) ? 4 : 16;
+template <int C, int NT, bool GLU, bool XF32>
+struct CrmCfg {
+    static constexpr int PB = kCrmPB<C>;
+    using U = UnitP<C, PB>;
+    static constexpr int CHW = (XF32 && U::W <= 256) ? 256 : 512;
+    static constexpr int CU = CHW / U::W, CHB = CU * U::BYTES, CHQ = CHW / 32;
+    static constexpr int NM = GLU ? 2 : 1;
+    static constexpr int ROW_PIECES = (CHB / PB + 1) | 1, ROW_BYTES = ROW_PIECES * PB;
+    static constexpr int WROWS = 16 * NT * NM;                 // weight rows per workgroup
+    static constexpr int WBUF = (WROWS * ROW_BYTES + 15) / 16 * 16;
+    static constexpr int ESZ = XF32 ? 4 : 2;
+    static constexpr int XSTRIDE = CHW * ESZ + 16;              // bytes per staged activation row
+    static constexpr int XL_ROW = CHW * ESZ / 1024;             // 1 KB copies per row and chunk
+    static constexpr int BUF = WBUF + 32 * XSTRIDE;
+    static constexpr size_t LDS = 2 * (size_t)BUF > (size_t)8 * NM * 2 * 1024 ? 2 * (size_t)BUF : (size_t)8 * NM * 2 * 1024;
+    static_assert(CHW % U::W == 0 && U::BYTES % PB == 0 && XL_ROW >= 1, "whole units and copies per chunk");
+};
+// the widest workgroup whose buffers fit in LDS
+template <int C, bool GLU, bool XF32>
+constexpr int crm_nt() {
+    return CrmCfg<C, 8, GLU, XF32>::LDS <= 160 * 1024   ? 8
+           : CrmCfg<C, 4, GLU, XF32>::LDS <= 160 * 1024 ? 4
+           : CrmCfg<C, 2, GLU, XF32>::LDS <= 160 * 1024 ? 2
+                                                        : 1;
+}
+
+template <int C, int NT, bool GLU, bool XF32>
+__global__ __launch_bounds__(512) void crm_kernel(SkinnyArgs a) {
+    using Cfg = CrmCfg<C, NT, GLU, XF32>;
+    constexpr int W = 8, KS = W / NT;  // waves; waves per row tile
+    constexpr int PB = Cfg::PB, NM = Cfg::NM, CHB = Cfg::CHB, CHQ = Cfg::CHQ, CHW = Cfg::CHW;
+    constexpr int ROW_PIECES = Cfg::ROW_PIECES, ROW_BYTES = Cfg::ROW_BYTES, BUF = Cfg::BUF;
+    constexpr int NPIECE = Cfg::WROWS * ROW_PIECES, WLOADS = (NPIECE + 63) / 64, WL_PER_WAVE = (WLOADS + W - 1) / W;
+    extern __shared__ __align__(16) uint8_t smem[];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n_l = lane & 15, g = lane >> 4;
+    const int64_t n = a.n, k = a.k, nb = (int64_t)blockIdx.x * (16 * NT);
+    if ((int64_t)blockIdx.y >= (int64_t)a.ws[0]) return;
+    const int32_t* tile = a.ws + a.tiles_off + 3 * (int64_t)blockIdx.y;
+    const int64_t e = tile[0], row0 = tile[1];
+    const int nrows = tile[2];
+    const int32_t* perm = a.ws + a.perm_off;
+    const int32_t* xexp = a.ws + a.xexp_off;
+    const int64_t row_bytes = a.row_bytes;
+    const int nchunks = (int)(k / CHW);
+    const uint8_t* wb0 = expert_base(a.w, a.w_sh, e, a.n_experts, a.expert_stride) + nb * row_bytes;
+    const uint8_t* wb1 = GLU ? expert_base(a.w2, a.w2_sh, e, a.n_experts, a.expert_stride) + nb * row_bytes : wb0;
+    // the activation row of tile row r (rows past the tile read row 0 and are not stored)
+    auto xrow_of = [&](int r) -> int64_t {
+        const int64_t R = perm[row0 + (r < nrows ? r : 0)];
+        return a.shared_x ? R / a.top_k : R;
+    };
+
+    // LDS row q of a chunk buffer: matrix q / (16 NT), weight row nb + q % (16 NT)
+    uint32_t woff[WL_PER_WAVE];
+    bool wact[WL_PER_WAVE], wsec[WL_PER_WAVE];
+#pragma unroll
+    for (int j = 0; j < WL_PER_WAVE; ++j) {
+        const int i = wave + W * j;
+        const int p = 64 * i + lane;
+        const int r = p / ROW_PIECES, q = p - r * ROW_PIECES;
+        const int rr = r % (16 * NT);
+        int64_t nr = nb + rr;
+        if (nr >= n) nr = n - 1;
+        wact[j] = i < WLOADS && r < Cfg::WROWS && q < CHB / PB;
+        wsec[j] = r >= 16 * NT;
+        woff[j] = (uint32_t)((nr - nb) * row_bytes) + (uint32_t)PB * (uint32_t)q;
+    }
+    const int xl_total = nrows * Cfg::XL_ROW;
+    int wave_loads = 0;
+#pragma unroll
+    for (int j = 0; j < WL_PER_WAVE; ++j) wave_loads += (wave + W * j < WLOADS) ? 1 : 0;
+    wave_loads += xl_total > wave ? (xl_total - wave + W - 1) / W : 0;
+    const uint8_t* xsrc = (const uint8_t*)a.x;
+    auto issue = [&](int chunk) {
+        uint8_t* dst = smem + (chunk & 1) * BUF;
+        const int64_t cb = (int64_t)chunk * CHB;
+#pragma unroll
+        for (int j = 0; j < WL_PER_WAVE; ++j) {
+            const int i = wave + W * j;
+            if (i < WLOADS) {
+                const uint32_t dl = __builtin_amdgcn_readfirstlane(lds_addr(dst + 64 * PB * i));
+                if (wact[j]) dma_piece<PB>((wsec[j] ? wb1 : wb0) + cb + woff[j], dl);
+            }
+        }
+        for (int i = wave; i < xl_total; i += W) {
+            const int r = i / Cfg::XL_ROW, c = i - r * Cfg::XL_ROW;
+            const uint8_t* src = xsrc + (xrow_of(r) * k + (int64_t)chunk * CHW) * Cfg::ESZ + 1024 * c;
+            dma16(src + 16 * lane,
+                  __builtin_amdgcn_readfirstlane(lds_addr(dst + Cfg::WBUF + r * Cfg::XSTRIDE + 1024 * c)));
+        }
+    };
+
+    float4_t acc[NM][2];
+#pragma unroll
+    for (int m = 0; m < NM; ++m) acc[m][0] = acc[m][1] = float4_t{0.f, 0.f, 0.f, 0.f};
+    const u32x2 ones = u32x2{0x3c003c00u, 0x3c003c00u};
+    const float4_t z = {0.f, 0.f, 0.f, 0.f};
+    issue(0);
+    for (int c = 0; c < nchunks; ++c) {
+        wait_loads_le(0);
+        __syncthreads();  // chunk c has landed everywhere; every wave is done with chunk c - 1
+        if (c + 1 < nchunks) issue(c + 1);
+        const uint8_t* B = smem + (c & 1) * BUF;
+        uint8_t* X = smem + (c & 1) * BUF + Cfg::WBUF;
+        if constexpr (XF32) {
+            // each row's values times 2^-e, split in place: every 16 values
+            // (64 bytes) become 16 hi halves then 16 lo halves
+            for (int gi = tid; gi < nrows * (CHW / 16); gi += 64 * W) {
+                const int r = gi / (CHW / 16), grp = gi - r * (CHW / 16);
+                const int ne = -xexp[xrow_of(r)];
+                u32x4* g4 = (u32x4*)(X + r * Cfg::XSTRIDE + 64 * grp);
+                uint32_t v[16];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const u32x4 u = g4[q];
+                    v[4 * q] = u.x, v[4 * q + 1] = u.y, v[4 * q + 2] = u.z, v[4 * q + 3] = u.w;
+                }
+                uint32_t hw[8], lw[8];
+                split16(v, ne, hw, lw);
+                g4[0] = u32x4{hw[0], hw[1], hw[2], hw[3]};
+                g4[1] = u32x4{hw[4], hw[5], hw[6], hw[7]};
+                g4[2] = u32x4{lw[0], lw[1], lw[2], lw[3]};
+                g4[3] = u32x4{lw[4], lw[5], lw[6], lw[7]};
+            }
+            __syncthreads();
+        }
+        // this wave's weight rows: row tile wave % NT of each matrix, and its
+        // share wave / NT of the chunk's 32-weight groups
+        const int rt = wave % NT;
+        const uint8_t* wrow0 = B + (rt * 16 + n_l) * ROW_BYTES;
+        const uint8_t* wrow1 = B + ((NT + rt) * 16 + n_l) * ROW_BYTES;
+        for (int cq = wave / NT; cq < CHQ; cq += KS) {
+            // activation operands of the two row groups: [group][half][hi, lo]
+            u32x2 av[2][2][2];
+#pragma unroll
+            for (int G = 0; G < 2; ++G) {
+                const uint8_t* xr = X + (16 * G + n_l) * Cfg::XSTRIDE;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    if constexpr (XF32) {
+                        const uint8_t* gp = xr + 4 * (32 * cq + 16 * h);
+                        av[G][h][0] = *(const u32x2*)(gp + 8 * g);
+                        av[G][h][1] = *(const u32x2*)(gp + 32 + 8 * g);
+                    } else {
+                        av[G][h][0] = *(const u32x2*)(xr + 2 * (32 * cq + 16 * h + 4 * g));
+                    }
+                }
+            }
+            bool folded = false;
+            // (fp32 activations are held to tau = 1e-5: exact weights only)
+            if constexpr (Pair8<C>::foldable && PB == 16 && !XF32) {
+                u32x2 wv[NM][2];
+                bool ok = Pair8<C>::fold(wrow0, cq, g, wv[0][0], wv[0][1]);
+                if constexpr (GLU) ok &= Pair8<C>::fold(wrow1, cq, g, wv[NM - 1][0], wv[NM - 1][1]);
+                if (__builtin_amdgcn_ballot_w64(!ok) == 0) {
+                    folded = true;
+#pragma unroll
+                    for (int m = 0; m < NM; ++m)
+#pragma unroll
+                        for (int G = 0; G < 2; ++G)
+#pragma unroll
+                            for (int h = 0; h < 2; ++h) acc[m][G] = mfma4(av[G][h][0], wv[m][h], acc[m][G]);
+                }
+            }
+            if (!folded) {
+#pragma unroll
+                for (int m = 0; m < NM; ++m) {
+                    u32x2 b[2];
+                    float A[2], Bv[2];
+                    Pair8<C>::decode(m ? wrow1 : wrow0, cq, g, b[0], b[1], A, Bv);
+#pragma unroll
+                    for (int G = 0; G < 2; ++G) {
+                        float4_t ch[2], sh[2];
+#pragma unroll
+                        for (int h = 0; h < 2; ++h) {
+                            ch[h] = mfma4(av[G][h][0], b[h], z);
+                            if constexpr (XF32) ch[h] = mfma4(av[G][h][1], b[h], ch[h]);
+                            if constexpr (Pair8<C>::has_b) {
+                                sh[h] = mfma4(av[G][h][0], ones, z);
+                                if constexpr (XF32) sh[h] = mfma4(av[G][h][1], ones, sh[h]);
+                            }
+                        }
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            float t = __builtin_fmaf(A[0], ch[0][v], __builtin_fmaf(A[1], ch[1][v], acc[m][G][v]));
+                            if constexpr (Pair8<C>::has_b)
+                                t = __builtin_fmaf(Bv[0], sh[0][v], __builtin_fmaf(Bv[1], sh[1][v], t));
+                            acc[m][G][v] = t;
+                        }
+                    }
+                }
+            }
+        }
+    }
+    if constexpr (KS > 1) {
+        __syncthreads();  // every wave is done with the last chunk and no copy is in flight
+        float4_t* red = (float4_t*)smem;  // [KS][NT][NM][2][64]
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+            for (int G = 0; G < 2; ++G) red[((wave * NM + m) * 2 + G) * 64 + lane] = acc[m][G];
+        __syncthreads();
+        if (wave >= NT) return;
+        for (int ks = 1; ks < KS; ++ks)
+#pragma unroll
+            for (int m = 0; m < NM; ++m)
+#pragma unroll
+                for (int G = 0; G < 2; ++G) {
+                    const float4_t t = red[(((ks * NT + wave) * NM + m) * 2 + G) * 64 + lane];
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) acc[m][G][v] += t[v];
+                }
+    }
+    // lane holds tile rows 16 G + 4 g + v of weight row nb + 16 wave + n_l
+    const int64_t col = nb + 16 * wave + n_l;
+    if (col >= n) return;
+#pragma unroll
+    for (int G = 0; G < 2; ++G)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int r = 16 * G + 4 * g + v;
+            if (r >= nrows) continue;
+            const int64_t R = perm[row0 + r];
+            float gv = acc[0][G][v], uv = acc[NM - 1][G][v];
+            if constexpr (XF32) {
+                const int ex = xexp[a.shared_x ? R / a.top_k : R];
+                gv = __builtin_ldexpf(gv, ex);
+                uv = __builtin_ldexpf(uv, ex);
+            }
+            put_dt(a.y, R * a.y_row + col, a.y_dt, GLU ? glu_act(a.act, gv, uv, a.limit) : gv);
+        }
+}
+
+template <int C, bool GLU, bool XF32>
+static bool crm_fits_g(int64_t k) {
+    using Cfg = CrmCfg<C, crm_nt<C, GLU, XF32>(), GLU, XF32>;
+    return k > 0 && k % Cfg::CHW == 0 && Cfg::LDS <= 160 * 1024;
+}
+template <int C>
+static bool crm_fits_c(int64_t k, bool glu, bool xf32) {
+    if (glu) return xf32 ? crm_fits_g<C, true, true>(k) : crm_fits_g<C, true, false>(k);
+    return xf32 ? crm_fits_g<C, false, true>(k) : crm_fits_g<C, false, false>(k);
+}
+bool crm_fits(int codec, int64_t k, bool glu, bool xf32) {
+    switch (codec) {
+    case Q8_0: return crm_fits_c<Q8_0>(k, glu, xf32);
+    case Q4_0: return crm_fits_c<Q4_0>(k, glu, xf32);
+    case Q5_0: return crm_fits_c<Q5_0>(k, glu, xf32);
+    case Q5_1: return crm_fits_c<Q5_1>(k, glu, xf32);
+    case Q6_K: return crm_fits_c<Q6_K>(k, glu, xf32);
+    case Q2_K: return crm_fits_c<Q2_K>(k, glu, xf32);
+    case Q3_K: return crm_fits_c<Q3_K>(k, glu, xf32);
+    case Q5_K: return crm_fits_c<Q5_K>(k, glu, xf32);
+    default: return false;
+    }
+}
+template <int C, bool GLU, bool XF32>
+static hipError_t crm_go(const SkinnyArgs& a, int64_t grid_tiles, hipStream_t s) {
+    constexpr int NT = crm_nt<C, GLU, XF32>();
+    hipLaunchKernelGGL((crm_kernel<C, NT, GLU, XF32>),
+                       dim3((unsigned)((a.n + 16 * NT - 1) / (16 * NT)), (unsigned)grid_tiles), dim3(512),
+                       (CrmCfg<C, NT, GLU, XF32>::LDS), s, a);
+    return hipGetLastError();
+}
+template <int C>
+static hipError_t crm_c(bool glu, bool xf32, const SkinnyArgs& a, int64_t grid_tiles, hipStream_t s) {
+    if (glu) return xf32 ? crm_go<C, true, true>(a, grid_tiles, s) : crm_go<C, true, false>(a, grid_tiles, s);
+    return xf32 ? crm_go<C, false, true>(a, grid_tiles, s) : crm_go<C, false, false>(a, grid_tiles, s);
+}
+hipError_t launch_crm(int codec, bool glu, bool xf32, const SkinnyArgs& a, int64_t grid_tiles, hipStream_t s) {
+    switch (codec) {
+    case Q8_0: return crm_c<Q8_0>(glu, xf32, a, grid_tiles, s);
+    case Q4_0: return crm_c<Q4_0>(glu, xf32, a, grid_tiles, s);
+    case Q5_0: return crm_c<Q5_0>(glu, xf32, a, grid_tiles, s);
+    case Q5_1: return crm_c<Q5_1>(glu, xf32, a, grid_tiles, s);
+    case Q6_K: return crm_c<Q6_K>(glu, xf32, a, grid_tiles, s);
+    case Q2_K: return crm_c<Q2_K>(glu, xf32, a, grid_tiles, s);
+    case Q3_K: return crm_c<Q3_K>(glu, xf32, a, grid_tiles, s);
+    default: return crm_c<Q5_K>(glu, xf32, a, grid_tiles, s);
     }
 }
 

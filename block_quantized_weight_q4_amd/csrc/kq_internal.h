@@ -92,6 +92,10 @@ hipError_t launch_down1_gguf(int codec, const DownMixArgs& d, int mode, hipStrea
 hipError_t launch_split_rows(const float* x, int64_t rows, int64_t k, uint8_t* out, int32_t* xexp, hipStream_t s);
 bool glu1_fits(int codec, int64_t k);
 hipError_t launch_glu1_gguf(int codec, const SkinnyArgs& a, hipStream_t s);
+// ... and their routed products over schedule tiles on the matrix cores
+// (cmv.hip); fp32 activations need the row exponents of launch_row_exp
+bool crm_fits(int codec, int64_t k, bool glu, bool xf32);
+hipError_t launch_crm(int codec, bool glu, bool xf32, const SkinnyArgs& a, int64_t grid_tiles, hipStream_t s);
 // Single-token gate/up with SiLU, expert ids read directly (moe_dec.hip).
 hipError_t launch_moe_glu1(const SkinnyArgs& a, hipStream_t s);
 

@@ -301,6 +301,18 @@ hipError_t launch_skinny(int codec, int x_dt, bool glu, const SkinnyArgs& a, int
         }
         return launch_moe_mm(glu, x_dt, b, grid_tiles, s);
     }
+    // Q8_0 and the further GGUF codecs over a schedule: routed tiles on the
+    // matrix cores (cmv.hip)
+    if ((codec >= Q4_0 || codec == Q8_0) && a.ws && (x_dt == F16 || x_dt == F32) &&
+        crm_fits(codec, a.k, glu, x_dt == F32)) {
+        if (x_dt == F32) {
+            const int64_t x_rows = a.shared_x ? a.rows_cap / a.top_k : a.rows_cap;
+            const hipError_t e = launch_row_exp((const float*)a.x, x_rows, a.k,
+                                                const_cast<int32_t*>(a.ws) + a.xexp_off, s);
+            if (e != hipSuccess) return e;
+        }
+        return launch_crm(codec, glu, x_dt == F32, a, grid_tiles, s);
+    }
     // up to four dense fp16 activation rows: unscaled nibbles on the matrix
     // cores, scales applied to the fp32 sub-block sums (mmv3.hip)
     if (codec == Q4_K && x_dt == F16 && !a.ws && !glu && a.m == 1 && mmv3_fits(a.k))

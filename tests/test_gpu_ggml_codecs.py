@@ -723,3 +723,84 @@ def test_qmm_id_mixed_one_token_dword_stream(kq, kind, x_dt, k):
     torch.cuda.synchronize()
     ref, s = oracle.qmm_id(kind, w, E, n, k, stride, x, x_dt, True, ids, 1, top_k, scores)
     check_tol(to_f64(y), ref, s, TAU[x_dt], f"qmm_id mixed one token dword {kind} {x_dt} k={k}")
+
+
+# ---------------------------------------------------------------- routed tiles on the matrix cores
+# Routings over a schedule (more than one token), k a whole number of 512
+# weights: the tile kernel (up to 32 gathered rows per tile, ragged tiles).
+@pytest.mark.parametrize("kind", ROUTED)
+@pytest.mark.parametrize("x_dt", ["f16", "f32"])
+@pytest.mark.parametrize("act", [0, 1])
+def test_moe_glu_routed_tiles(kq, kind, x_dt, act):
+    E, n, top_k, T, k = 8, 200, 4, 24, 1536
+    rng = synth.rng_for(5950 + act)
+    gate = synth.weight_blocks(kind, rng, E * n, k)
+    up = synth.weight_blocks(kind, rng, E * n, k)
+    stride = n * synth.row_bytes(kind, k)
+    ids = _ids(rng, T, E, top_k)
+    x = synth.activations(rng, (T, k), x_dt)
+    _say("moe_glu routed tiles", kind, x_dt, act)
+    h = empty((T, top_k, n), "f32")
+    ws = _moe_ws(kq, E, T, top_k)
+    kq.kq_moe_glu(kind, to_dev(gate), to_dev(up), E, n, k, stride, to_dev(x, x_dt), to_dev(ids), T, top_k, h, ws,
+                  act)
+    torch.cuda.synchronize()
+    ref = oracle.moe_glu(kind, gate, up, E, n, k, stride, x, x_dt, ids, T, top_k, act)
+    assert _glu_bound_ok(to_f64(h), ref, TAU[x_dt], act, 0.0), f"moe_glu routed {kind} {x_dt} act={act}"
+
+
+@pytest.mark.parametrize("kind", ROUTED)
+@pytest.mark.parametrize("x_dt", ["f16", "f32"])
+@pytest.mark.parametrize("layout", [0, 1])
+@pytest.mark.parametrize("mixed", [False, True])
+def test_qmm_id_routed_tiles(kq, kind, x_dt, layout, mixed):
+    """Four experts and 70 tokens of top-4: about 70 rows per expert, tiles
+    of 32, 32 and a ragged one."""
+    E, top_k, T, n, k = 4, 4, 70, 136, 1024
+    rng = synth.rng_for(5960 + layout)
+    w = synth.weight_blocks(kind, rng, E * n, k)
+    stride = n * synth.row_bytes(kind, k)
+    ids = _ids(rng, T, E, top_k)
+    scores = rng.uniform(0.05, 1.0, size=(T, top_k)).astype(np.float32)
+    x = synth.activations(rng, (T if layout == 0 else T * top_k, k), x_dt)
+    _say("qmm_id routed tiles", kind, x_dt, layout, mixed)
+    y = empty((T if mixed else T * top_k, n), "f32")
+    ws = _moe_ws(kq, E, T, top_k, n if mixed else 0)
+    kq.kq_qmm_id(kind, to_dev(w), E, n, k, stride, to_dev(x, x_dt), layout, to_dev(ids), T, top_k,
+                 to_dev(scores) if mixed else None, y, ws)
+    torch.cuda.synchronize()
+    ref, s = oracle.qmm_id(kind, w, E, n, k, stride, x, x_dt, layout == 1, ids, T, top_k,
+                           scores if mixed else None)
+    check_tol(to_f64(y), ref, s, TAU[x_dt], f"qmm_id routed {kind} {x_dt} layout {layout} mixed {mixed}")
+
+
+@pytest.mark.parametrize("kind", ["q4_0", "q8_0", "q6_k", "q2_k"])
+def test_moe_prefill_c4_shapes_sampled_tokens(kq, kind):
+    """A 256-token layer at the C4 matrix shapes (32 experts, top-8, fp16 x,
+    fp32 h) with the schedule reused by the down projection, as the benchmark
+    times it; tokens 0, 97 and 255 against the oracle."""
+    E, top_k, H, F, T = 32, 8, 7168, 2048, 256
+    rng = synth.rng_for(5970)
+    gate = synth.weight_blocks(kind, rng, E * F, H)
+    up = synth.weight_blocks(kind, rng, E * F, H)
+    down = synth.weight_blocks(kind, rng, E * H, F)
+    gs, ds = F * synth.row_bytes(kind, H), H * synth.row_bytes(kind, F)
+    ids = _ids(rng, T, E, top_k)
+    scores = rng.uniform(0.05, 1.0, size=(T, top_k)).astype(np.float32)
+    x = synth.activations(rng, (T, H), "f16")
+    _say("moe prefill C4 shapes", kind)
+    h = empty((T, top_k, F), "f32")
+    out = empty((T, H), "f32")
+    ws = _moe_ws(kq, E, T, top_k, H)
+    idd = to_dev(ids)
+    kq.kq_moe_glu(kind, to_dev(gate), to_dev(up), E, F, H, gs, to_dev(x, "f16"), idd, T, top_k, h, ws)
+    kq.kq_qmm_id(kind, to_dev(down), E, H, F, ds, h, kq.LAYOUT_SLOTTED | kq.REUSE_SCHEDULE, idd, T, top_k,
+                 to_dev(scores), out, ws)
+    torch.cuda.synchronize()
+    hg, og = to_f64(h), to_f64(out)
+    for t in (0, 97, 255):
+        ref = oracle.moe_glu(kind, gate, up, E, F, H, gs, x[t:t + 1], "f16", ids[t:t + 1], 1, top_k, 0)
+        assert _glu_bound_ok(hg[t:t + 1], ref, TAU["f16"], 0, 0.0), f"prefill glu {kind} token {t}"
+        hx = hg[t].astype(np.float32)
+        yref, s = oracle.qmm_id(kind, down, E, H, F, ds, hx, "f32", True, ids[t:t + 1], 1, top_k, scores[t:t + 1])
+        check_tol(og[t:t + 1], yref, s, TAU["f32"], f"prefill down {kind} token {t}")
