@@ -13,8 +13,8 @@ workload:
             in the C2 GEMV shapes 14336x4096 and 4096x14336, fp16 x at batch 1 (and batch 8 as
             extra rows), fp16 y, and the
             further blocks' prefill GEMM in the C3 shape 14336x4096 at M=2048, bf16 x (seed 106)
-  ggml_moe  one-token MoE layers (gate/up + SwiGLU, down + weighted sum) with those blocks at
-            the C4 matrix shapes: 32 experts, top-8, fp16 x, fp32 h (seed 107)
+  ggml_moe  one-token and 256-token MoE layers (gate/up + SwiGLU, down + weighted sum) with
+            those blocks at the C4 matrix shapes: 32 experts, top-8, fp16 x, fp32 h (seed 107)
 
 The headline value is the Q4_K decode GEMV (the six qmv_c2 calls): weight
 bytes streamed per second.  Every call reads weights from HBM: weight-bound
@@ -296,6 +296,11 @@ def main():
         idg = torch.from_numpy(np.stack([rng.choice(E, top_k, replace=False) for _ in range(T)])
                                .astype(np.int32)).to(dev)
         scg = torch.from_numpy(rng.uniform(0.05, 1.0, size=(T, top_k)).astype(np.float32)).to(dev)
+        TP = 256
+        xp = d16(synth.activations(rng, (TP, H), "f16"), torch.float16)
+        idp = torch.from_numpy(np.stack([rng.choice(E, top_k, replace=False) for _ in range(TP)])
+                               .astype(np.int32)).to(dev)
+        scp = torch.from_numpy(rng.uniform(0.05, 1.0, size=(TP, top_k)).astype(np.float32)).to(dev)
         for kind in GGML_KINDS:
             gs, ds = F * synth.row_bytes(kind, H), H * synth.row_bytes(kind, F)
             g_w = d8(synth.weight_blocks(kind, rng, E * F, H))
@@ -314,6 +319,19 @@ def main():
             extra_parts.append(Stage(f"ggml_moe_{kind}_decode", calls, T * top_k * (2 * gs + ds),
                                      T * top_k * 2 * 3 * F * H,
                                      note=f"{kind} one-token MoE layer at the C4 shapes, 32 experts, top-8"))
+            # the 256-token layer over the schedule (the down projection reuses it)
+            mws_p = torch.empty(kq.kq_moe_workspace_bytes(E, TP, top_k, H), dtype=torch.uint8, device=dev)
+            h_p = torch.empty((TP, top_k, F), dtype=torch.float32, device=dev)
+            o_p = torch.empty((TP, H), dtype=torch.float32, device=dev)
+
+            def layerp(kind=kind, g_w=g_w, u_w=u_w, dn_w=dn_w, gs=gs, ds=ds, mws_p=mws_p, h_p=h_p, o_p=o_p):
+                kq.kq_moe_glu(kind, g_w, u_w, E, F, H, gs, xp, idp, TP, top_k, h_p, mws_p)
+                kq.kq_qmm_id(kind, dn_w, E, H, F, ds, h_p, kq.LAYOUT_SLOTTED | kq.REUSE_SCHEDULE, idp, TP, top_k,
+                             scp, o_p, mws_p)
+
+            extra_parts.append(Stage(f"ggml_moe_{kind}_prefill", [layerp] * 2, 2 * E * (2 * gs + ds),
+                                     2 * TP * top_k * 2 * 3 * F * H,
+                                     note=f"{kind} 256-token MoE layer at the C4 shapes, 32 experts, top-8"))
 
     # Streaming-read ceiling: a plain 16-byte-load read of the same number of
     # bytes as one C2 / C5 weight matrix (libkq_hbmread.so), rotated over

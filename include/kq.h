@@ -78,8 +78,12 @@
  * and Q3_K) stream each slot's expert rows through LDS with exact fp16
  * integer pairs on the vector units; fp32 activation rows are split into
  * fp16 hi + lo (22 significant bits), once into the workspace's slot buffer
- * when n_slots * k <= n_slots * n.  Their other decode and expert-routed
- * products run on the vector units with exact weights.
+ * when n_slots * k <= n_slots * n.  Their expert-routed products over a
+ * schedule (more than one token; k a whole number of 512 weights) run on the
+ * matrix cores per schedule tile, as the batched decode products (fp32
+ * activations with exact weights and fp16 hi + lo rows).  Their other
+ * decode and expert-routed products run on the vector units with exact
+ * weights.
  *
  * All multi-byte fields are little-endian.  fp16 is IEEE binary16; bf16 is
  * the upper half of an IEEE binary32.
