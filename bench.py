@@ -279,7 +279,7 @@ def main():
             xm = d16(synth.activations(rng, (mm, k), "bf16"), torch.bfloat16)
             y = torch.empty((mm, n), dtype=torch.bfloat16, device=dev)
             sc = scratch(kind, n, k, mm, torch.bfloat16)
-            part = [(lambda kind=kind, ws=ws, xm=xm, y=y, sc=sc:
+            part = [(lambda kind=kind, n=n, k=k, mm=mm, ws=ws, xm=xm, y=y, sc=sc:
                      kq.kq_qmm_ws(kind, nxt(ws), n, k, xm, mm, y, sc)) for _ in range(8)]
             extra_parts.append(Stage(f"ggml_mm_{kind}_{n}x{k}_m{mm}", part,
                                      len(part) * (w.numel() + mm * (k + n) * 2),
@@ -310,7 +310,8 @@ def main():
             h_g = torch.empty((1, top_k, F), dtype=torch.float32, device=dev)
             o_g = torch.empty((1, H), dtype=torch.float32, device=dev)
 
-            def layer1(t, kind=kind, g_w=g_w, u_w=u_w, dn_w=dn_w, gs=gs, ds=ds, mws_g=mws_g, h_g=h_g, o_g=o_g):
+            def layer1(t, kind=kind, g_w=g_w, u_w=u_w, dn_w=dn_w, gs=gs, ds=ds, mws_g=mws_g, h_g=h_g, o_g=o_g,
+                       E=E, H=H, F=F, top_k=top_k, xg=xg, idg=idg, scg=scg):
                 kq.kq_moe_glu(kind, g_w, u_w, E, F, H, gs, xg[t:t + 1], idg[t:t + 1], 1, top_k, h_g, mws_g)
                 kq.kq_qmm_id(kind, dn_w, E, H, F, ds, h_g, kq.LAYOUT_SLOTTED, idg[t:t + 1], 1, top_k,
                              scg[t:t + 1], o_g, mws_g)
@@ -324,7 +325,8 @@ def main():
             h_p = torch.empty((TP, top_k, F), dtype=torch.float32, device=dev)
             o_p = torch.empty((TP, H), dtype=torch.float32, device=dev)
 
-            def layerp(kind=kind, g_w=g_w, u_w=u_w, dn_w=dn_w, gs=gs, ds=ds, mws_p=mws_p, h_p=h_p, o_p=o_p):
+            def layerp(kind=kind, g_w=g_w, u_w=u_w, dn_w=dn_w, gs=gs, ds=ds, mws_p=mws_p, h_p=h_p, o_p=o_p,
+                       E=E, H=H, F=F, top_k=top_k, TP=TP, xp=xp, idp=idp, scp=scp):
                 kq.kq_moe_glu(kind, g_w, u_w, E, F, H, gs, xp, idp, TP, top_k, h_p, mws_p)
                 kq.kq_qmm_id(kind, dn_w, E, H, F, ds, h_p, kq.LAYOUT_SLOTTED | kq.REUSE_SCHEDULE, idp, TP, top_k,
                              scp, o_p, mws_p)
