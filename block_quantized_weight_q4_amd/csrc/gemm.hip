@@ -979,8 +979,17 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
                                                             int splits, int64_t mn,
                                                             void* __restrict__ y, int y_dt) {
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < mn; i += (int64_t)gridDim.x * 256) {
+        // the partials are fetched eight at a time, all in flight together,
+        // and added in piece order
         float acc = part[i];
-        for (int z = 1; z < splits; ++z) acc += part[(int64_t)z * mn + i];
+        for (int z0 = 1; z0 < splits; z0 += 8) {
+            float v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = z0 + u < splits ? part[(int64_t)(z0 + u) * mn + i] : 0.f;
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (z0 + u < splits) acc += v[u];
+        }
         if (y_dt == F32) store_out<F32>(y, i, acc);
         else if (y_dt == F16) store_out<F16>(y, i, acc);
         else store_out<BF16>(y, i, acc);
